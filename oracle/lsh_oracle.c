@@ -1,0 +1,341 @@
+/*
+ * lsh_oracle.c -- the plain fp64 CPU oracle. TEST INFRASTRUCTURE only: see
+ * lsh_oracle.h for who may call it, the page sources ([TT], [DT]) and layouts.
+ *
+ * Every step is written the slow, literal way, one query at a time, in the
+ * order the pages give the method. OpenMP only splits independent
+ * (batch, head, round) segments or positions across threads; nothing is
+ * blocked, fused or reordered inside a step.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include "lsh_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+int lsh_oracle_check(const lsh_oracle_config* c) {
+  if (!c) return -1;
+  if (c->batch < 1 || c->heads < 1 || c->seq_len < 1 || c->head_dim < 1) return -2;
+  if (c->n_rounds < 1 || c->chunk_len < 1 || c->seq_len % c->chunk_len != 0) return -3;
+  if (c->n_buckets < 1 || (c->n_buckets > 1 && c->n_buckets % 2 != 0)) return -4;
+  if (c->causal != 0 && c->causal != 1) return -5;
+  return 0;
+}
+
+static size_t seg_count(const lsh_oracle_config* c) {
+  return (size_t)c->batch * c->heads * c->n_rounds;
+}
+
+/* ---------------------------------------------------------------------------
+ * Hash, [TT] section LSH: R has size [d, b/2]; h(x) is the index of the
+ * largest entry of the length-b vector [xR; -xR]. Several rounds use
+ * independent R ([TT] multi-round LSH); R is shared by every batch and head
+ * (the figure caption of [TT] LSH attention notes that R is shared).
+ * Readings where the page is silent:
+ *   - ties: the lowest index wins (exact ties only happen for x = 0 and on
+ *     sets of measure zero);
+ *   - n_buckets == 1: [d, b/2] is empty, every position is in bucket 0 and its
+ *     margin is +inf.
+ * margin = largest minus second-largest entry of [xR; -xR]; it measures how
+ * close a bucket decision is to a tie.
+ * ------------------------------------------------------------------------- */
+int lsh_oracle_hash(const lsh_oracle_config* c, const double* qk, const double* rot,
+                    int32_t* buckets, double* margin) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const int64_t L = c->seq_len, d = c->head_dim, nb = c->n_buckets, R = c->n_rounds;
+  const int64_t half = nb / 2;
+  const int64_t nseg = (int64_t)seg_count(c);
+  if (nb > 1 && !rot) return -6;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(nb > 1 ? nb : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t seg = 0; seg < nseg; ++seg) {
+      const int64_t bh = seg / R, r = seg % R;
+      const double* x_bh = qk + bh * L * d;
+      for (int64_t i = 0; i < L; ++i) {
+        const size_t out_idx = (size_t)(seg * L + i);
+        if (nb == 1) {
+          buckets[out_idx] = 0;
+          if (margin) margin[out_idx] = INFINITY;
+          continue;
+        }
+        const double* x = x_bh + i * d;
+        const double* Rr = rot + r * d * half;
+        /* projection xR: p_k = sum_t x_t R[t][k]; then z = [p; -p] */
+        for (int64_t k = 0; k < half; ++k) {
+          double p = 0.0;
+          for (int64_t t = 0; t < d; ++t) p += x[t] * Rr[t * half + k];
+          z[k] = p;
+          z[k + half] = -p;
+        }
+        int64_t best = 0;
+        for (int64_t k = 1; k < nb; ++k)
+          if (z[k] > z[best]) best = k;
+        double second = -INFINITY;
+        for (int64_t k = 0; k < nb; ++k)
+          if (k != best && z[k] > second) second = z[k];
+        buckets[out_idx] = (int32_t)best;
+        if (margin) margin[out_idx] = z[best] - second;
+      }
+    }
+    free(z);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Sort, [TT] section LSH attention: order positions by bucket, ascending, and
+ * inside a bucket by position. Written as a counting sort over bucket ids that
+ * visits positions in increasing order, which keeps equal buckets in position
+ * order. perm[s] = position held by sorted slot s; inv[perm[s]] = s.
+ * ------------------------------------------------------------------------- */
+int lsh_oracle_sort(const lsh_oracle_config* c, const int32_t* buckets, int32_t* perm,
+                    int32_t* inv) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const int64_t L = c->seq_len, nb = c->n_buckets;
+  const int64_t nseg = (int64_t)seg_count(c);
+  int bad = 0;
+#pragma omp parallel
+  {
+    int64_t* start = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nb + 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t seg = 0; seg < nseg; ++seg) {
+      const int32_t* bk = buckets + seg * L;
+      int32_t* pm = perm + seg * L;
+      for (int64_t b = 0; b <= nb; ++b) start[b] = 0;
+      int local_bad = 0;
+      for (int64_t i = 0; i < L; ++i) {
+        if (bk[i] < 0 || bk[i] >= nb) { local_bad = 1; break; }
+        start[bk[i] + 1] += 1;
+      }
+      if (local_bad) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      for (int64_t b = 0; b < nb; ++b) start[b + 1] += start[b];
+      for (int64_t i = 0; i < L; ++i) pm[start[bk[i]]++] = (int32_t)i;
+      if (inv) {
+        int32_t* iv = inv + seg * L;
+        for (int64_t s = 0; s < L; ++s) iv[pm[s]] = (int32_t)s;
+      }
+    }
+    free(start);
+  }
+  return bad ? -7 : 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * One query of one round.
+ * [TT] LSH attention: the sorted sequence is cut into chunks of m and a query
+ * attends inside its chunk; [DT] 2.1 adds the neighbouring chunk. Reading
+ * taken: the window of a query in chunk c is chunk c plus chunk c-1 (chunk 0
+ * has no look-back; no wrap-around; rounds are sorted and chunked separately).
+ * Keys are unit-normalised ([DT] 2.1); a zero key stays zero. Queries are not
+ * normalised. Logit s_ij = (q_i . khat_j) / sqrt(d) ([DT] scaled softmax).
+ * Causal: keys at a later original position are dropped.
+ * Self-mask ([TT] shared-QK self-mask): the query's own key is dropped when
+ * anything else is left. When nothing else is left, the query attends to
+ * itself only: o = v_i and the round's logsumexp is the constant
+ * LSH_ORACLE_SELF_LOGIT, which gives that round zero weight in the combine
+ * step whenever another round has a real window.
+ * Masked keys are excluded from the softmax (the page's multiplicative mask
+ * notation is read as exclusion).
+ * ------------------------------------------------------------------------- */
+static void unit_key(const double* k, int64_t d, double* khat) {
+  double ss = 0.0;
+  for (int64_t t = 0; t < d; ++t) ss += k[t] * k[t];
+  const double nrm = sqrt(ss);
+  for (int64_t t = 0; t < d; ++t) khat[t] = (nrm > 0.0) ? k[t] / nrm : 0.0;
+}
+
+/* qk_bh, v_bh: [L, d] of one (b, h); pm: perm of one round; s: the query slot.
+ * Writes o_row [d] and returns the round's logsumexp. Scratch: khat [d],
+ * logit [2m], key [2m]. */
+static double attend_one(const lsh_oracle_config* c, const double* qk_bh, const double* v_bh,
+                         const int32_t* pm, int64_t s, double* o_row, double* khat,
+                         double* logit, int64_t* key) {
+  const int64_t d = c->head_dim, m = c->chunk_len;
+  const int64_t i = pm[s];
+  const int64_t chunk = s / m;
+  const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;
+  const int64_t last = (chunk + 1) * m;
+  const double* q = qk_bh + i * d;
+  const double scale = 1.0 / sqrt((double)d);
+  int64_t n = 0;
+  for (int64_t t = first; t < last; ++t) {
+    const int64_t j = pm[t];
+    if (j == i) continue;                 /* self-mask */
+    if (c->causal && j > i) continue;     /* causal mask on original positions */
+    unit_key(qk_bh + j * d, d, khat);
+    double dot = 0.0;
+    for (int64_t u = 0; u < d; ++u) dot += q[u] * khat[u];
+    logit[n] = dot * scale;
+    key[n] = j;
+    ++n;
+  }
+  if (n == 0) {
+    for (int64_t u = 0; u < d; ++u) o_row[u] = v_bh[i * d + u];
+    return LSH_ORACLE_SELF_LOGIT;
+  }
+  double mx = -INFINITY;
+  for (int64_t a = 0; a < n; ++a) mx = logit[a] > mx ? logit[a] : mx;
+  double sum = 0.0;
+  for (int64_t a = 0; a < n; ++a) sum += exp(logit[a] - mx);
+  const double lse = mx + log(sum);
+  for (int64_t u = 0; u < d; ++u) o_row[u] = 0.0;
+  for (int64_t a = 0; a < n; ++a) {
+    const double w = exp(logit[a] - lse);
+    const double* vj = v_bh + key[a] * d;
+    for (int64_t u = 0; u < d; ++u) o_row[u] += w * vj[u];
+  }
+  return lse;
+}
+
+int lsh_oracle_attend(const lsh_oracle_config* c, const double* qk, const double* v,
+                      const int32_t* perm, double* o, double* lse) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
+  const int64_t nseg = (int64_t)seg_count(c);
+#pragma omp parallel
+  {
+    double* khat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t seg = 0; seg < nseg; ++seg) {
+      const int64_t bh = seg / R;
+      const int32_t* pm = perm + seg * L;
+      for (int64_t s = 0; s < L; ++s) {
+        const int64_t i = pm[s];
+        /* unsort: results are stored at the original position i */
+        double l = attend_one(c, qk + bh * L * d, v + bh * L * d, pm, s,
+                              o + (seg * L + i) * d, khat, logit, key);
+        lse[seg * L + i] = l;
+      }
+    }
+    free(khat);
+    free(logit);
+    free(key);
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Combination of rounds. [TT] multi-round LSH defers the details to the
+ * original paper; reading taken: each round r yields o_r(i) and its logsumexp
+ * lse_r(i); the rounds are combined with weights softmax over r of lse_r(i):
+ *   w_r(i) = exp(lse_r(i) - M) / sum_r' exp(lse_r'(i) - M),  M = max_r lse_r(i),
+ *   out(i) = sum_r w_r(i) o_r(i).
+ * This equals one softmax over the multiset union of the rounds' windows
+ * (a key seen in two rounds counts twice).
+ * ------------------------------------------------------------------------- */
+static void combine_one(int64_t R, int64_t d, const double* o_r0, int64_t o_stride,
+                        const double* lse_r0, int64_t lse_stride, double* out_row) {
+  double mx = -INFINITY;
+  for (int64_t r = 0; r < R; ++r) mx = lse_r0[r * lse_stride] > mx ? lse_r0[r * lse_stride] : mx;
+  double sum = 0.0;
+  for (int64_t r = 0; r < R; ++r) sum += exp(lse_r0[r * lse_stride] - mx);
+  for (int64_t u = 0; u < d; ++u) out_row[u] = 0.0;
+  for (int64_t r = 0; r < R; ++r) {
+    const double w = exp(lse_r0[r * lse_stride] - mx) / sum;
+    const double* orow = o_r0 + r * o_stride;
+    for (int64_t u = 0; u < d; ++u) out_row[u] += w * orow[u];
+  }
+}
+
+int lsh_oracle_combine(const lsh_oracle_config* c, const double* o, const double* lse,
+                       double* out) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds;
+  const int64_t nbh = (int64_t)c->batch * c->heads;
+#pragma omp parallel for schedule(static)
+  for (int64_t p = 0; p < nbh * L; ++p) {
+    const int64_t bh = p / L, i = p % L;
+    combine_one(R, d, o + (bh * R * L + i) * d, L * d, lse + bh * R * L + i, L,
+                out + p * d);
+  }
+  return 0;
+}
+
+int lsh_oracle_forward(const lsh_oracle_config* c, const double* qk, const double* v,
+                       const double* rot, const int32_t* buckets_override, double* out,
+                       double* lse, int32_t* buckets, int32_t* perm, double* margin) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const size_t nsl = seg_count(c) * (size_t)c->seq_len;
+  const size_t d = (size_t)c->head_dim;
+  int32_t* bk = buckets ? buckets : (int32_t*)malloc(sizeof(int32_t) * nsl);
+  int32_t* pm = perm ? perm : (int32_t*)malloc(sizeof(int32_t) * nsl);
+  double* ls = lse ? lse : (double*)malloc(sizeof(double) * nsl);
+  double* o = (double*)malloc(sizeof(double) * nsl * d);
+  if (!bk || !pm || !ls || !o) { rc = -8; goto done; }
+  if (rot || c->n_buckets == 1) {
+    rc = lsh_oracle_hash(c, qk, rot, bk, margin);
+    if (rc) goto done;
+  }
+  if (buckets_override) memcpy(bk, buckets_override, sizeof(int32_t) * nsl);
+  else if (!rot && c->n_buckets > 1) { rc = -6; goto done; }
+  rc = lsh_oracle_sort(c, bk, pm, NULL);
+  if (rc) goto done;
+  rc = lsh_oracle_attend(c, qk, v, pm, o, ls);
+  if (rc) goto done;
+  rc = lsh_oracle_combine(c, o, ls, out);
+done:
+  if (!buckets) free(bk);
+  if (!perm) free(pm);
+  if (!lse) free(ls);
+  free(o);
+  return rc;
+}
+
+int lsh_oracle_attend_rows(const lsh_oracle_config* c, const double* qk, const double* v,
+                           const int32_t* perm, int64_t n_rows, const int64_t* rows,
+                           double* out_rows, double* lse_rows) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
+  const int64_t nbh = (int64_t)c->batch * c->heads;
+  const int64_t nseg = nbh * R;
+  for (int64_t k = 0; k < n_rows; ++k)
+    if (rows[k] < 0 || rows[k] >= nbh * L) return -9;
+  int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nseg * L));
+  if (!inv) return -8;
+#pragma omp parallel for schedule(static)
+  for (int64_t seg = 0; seg < nseg; ++seg)
+    for (int64_t s = 0; s < L; ++s) inv[seg * L + perm[seg * L + s]] = (int32_t)s;
+#pragma omp parallel
+  {
+    double* khat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+    double* o = (double*)malloc(sizeof(double) * (size_t)(R * d));
+    double* l = (double*)malloc(sizeof(double) * (size_t)R);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t k = 0; k < n_rows; ++k) {
+      const int64_t bh = rows[k] / L, i = rows[k] % L;
+      for (int64_t r = 0; r < R; ++r) {
+        const int64_t seg = bh * R + r;
+        const int64_t s = inv[seg * L + i];
+        l[r] = attend_one(c, qk + bh * L * d, v + bh * L * d, perm + seg * L, s, o + r * d,
+                          khat, logit, key);
+        if (lse_rows) lse_rows[k * R + r] = l[r];
+      }
+      combine_one(R, d, o, d, l, 1, out_rows + k * d);
+    }
+    free(khat);
+    free(logit);
+    free(key);
+    free(o);
+    free(l);
+  }
+  free(inv);
+  return 0;
+}

@@ -1,0 +1,88 @@
+/*
+ * lsh_oracle.h -- plain, slow fp64 CPU definition of Reformer shared-QK LSH
+ * self-attention (forward).
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
+ * baseline may load or call this library. The product path (the HIP library
+ * and its Python binding) never links, imports or calls it, and it shares no
+ * code, header, constant or helper with that path.
+ *
+ * Sources for each step (the pages are web summaries of the Reformer paper):
+ *   [TT] Reformer summary, p2.ttnews.xyz/a/5dd41cfcdc9b5e51a0429126
+ *        sections: LSH (hash of a vector with a random matrix R of size
+ *        [dimension, b/2], h(x) = argmax of the concatenation [xR; -xR]);
+ *        LSH attention (sort by bucket, then by position inside a bucket; cut
+ *        the sorted sequence into groups of m and attend inside them);
+ *        multi-round LSH (several independent hash functions);
+ *        self-mask for shared QK (no attention to oneself unless nothing else
+ *        can be attended to).
+ *   [DT] Reformer overview, www.dtcms.com/a/488796.html, section 2.1
+ *        "key steps": unit-normalised keys, multiple projection rounds, each
+ *        query also looks at the neighbouring group; "math" paragraph: the
+ *        scaled softmax with 1/sqrt(d_k) and a mask.
+ * Where the pages leave a step open, the reading taken is stated at the step
+ * in lsh_oracle.c.
+ *
+ * Layouts (row-major, contiguous):
+ *   qk, v, out        [B, H, L, d]            float64
+ *   rotations         [n_rounds, d, n_buckets/2] float64 (unused when n_buckets == 1)
+ *   buckets, perm, inv [B, H, n_rounds, L]    int32
+ *   margin            [B, H, n_rounds, L]     float64 (largest minus second-largest of
+ *                                              the concatenated projection)
+ *   o                 [B, H, n_rounds, L, d]  float64, indexed by ORIGINAL position
+ *   lse               [B, H, n_rounds, L]     float64, indexed by original position
+ * perm maps a sorted slot to the position it holds; inv is its inverse.
+ * All functions return 0 on success and a negative value on a bad config.
+ */
+#ifndef LSH_ORACLE_H
+#define LSH_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int32_t batch, heads, seq_len, head_dim;
+  int32_t n_buckets;  /* 1, or even >= 2 */
+  int32_t n_rounds;   /* >= 1 */
+  int32_t chunk_len;  /* >= 1, divides seq_len */
+  int32_t causal;     /* 0 or 1 */
+} lsh_oracle_config;
+
+/* Logit given to a query's own key; also the logsumexp of a round in which the
+ * query can attend to nothing but itself. */
+#define LSH_ORACLE_SELF_LOGIT (-1.0e5)
+
+int lsh_oracle_check(const lsh_oracle_config* cfg);
+
+int lsh_oracle_hash(const lsh_oracle_config* cfg, const double* qk, const double* rotations,
+                    int32_t* buckets, double* margin);
+
+int lsh_oracle_sort(const lsh_oracle_config* cfg, const int32_t* buckets, int32_t* perm,
+                    int32_t* inv);
+
+int lsh_oracle_attend(const lsh_oracle_config* cfg, const double* qk, const double* v,
+                      const int32_t* perm, double* o, double* lse);
+
+int lsh_oracle_combine(const lsh_oracle_config* cfg, const double* o, const double* lse,
+                       double* out);
+
+/* Whole forward. buckets_override (nullable) replaces the hash step's buckets;
+ * margin is still computed from the projections when rotations are given. */
+int lsh_oracle_forward(const lsh_oracle_config* cfg, const double* qk, const double* v,
+                       const double* rotations, const int32_t* buckets_override,
+                       double* out, double* lse, int32_t* buckets, int32_t* perm,
+                       double* margin);
+
+/* Output rows for a sample of (b, h, i), given every round's perm:
+ * rows[k] = (b * H + h) * L + i; out_rows [n_rows, d]; lse_rows [n_rows, n_rounds]. */
+int lsh_oracle_attend_rows(const lsh_oracle_config* cfg, const double* qk, const double* v,
+                           const int32_t* perm, int64_t n_rows, const int64_t* rows,
+                           double* out_rows, double* lse_rows);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,90 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a private copy of lsh_oracle.c (on the CPU,
+in a temporary directory), builds it, and checks that at least one pin fails.
+"""
+import pytest
+
+import oracle
+
+import test_oracle_pins as pins
+
+# (name, original text, planted mistake); a list replaces several places at once.
+# Every planted mistake keeps all memory accesses in bounds.
+MUTATIONS = [
+    ("scale dropped", "logit[n] = dot * scale;", "logit[n] = dot;"),
+    ("R transposed", "Rr[t * half + k]", "Rr[k * d + t]"),
+    ("negated half dropped", "z[k + half] = -p;", "z[k + half] = p;"),
+    ("ties to highest index", "if (z[k] > z[best]) best = k;", "if (z[k] >= z[best]) best = k;"),
+    ("margin not a difference", "margin[out_idx] = z[best] - second;",
+     "margin[out_idx] = z[best];"),
+    ("no look-back", "const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;",
+     "const int64_t first = chunk * m;"),
+    ("look-ahead instead of look-back",
+     "const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;\n  const int64_t last = (chunk + 1) * m;",
+     "const int64_t first = chunk * m;\n"
+     "  const int64_t last = (chunk + 2) * m < c->seq_len ? (chunk + 2) * m : c->seq_len;"),
+    ("keys not normalised", "khat[t] = (nrm > 0.0) ? k[t] / nrm : 0.0;", "khat[t] = k[t];"),
+    ("causal reversed", "if (c->causal && j > i) continue;", "if (c->causal && j < i) continue;"),
+    ("self not masked", "if (j == i) continue;", "if (0) continue;"),
+    ("self-only lse zero", "return LSH_ORACLE_SELF_LOGIT;", "return 0.0;"),
+    ("lse without max", "const double lse = mx + log(sum);", "const double lse = log(sum);"),
+    ("rounds averaged", "const double w = exp(lse_r0[r * lse_stride] - mx) / sum;",
+     "const double w = 1.0 / (double)R;"),
+    ("unstable sort", "for (int64_t i = 0; i < L; ++i) pm[start[bk[i]]++] = (int32_t)i;",
+     "for (int64_t i = L - 1; i >= 0; --i) pm[start[bk[i]]++] = (int32_t)i;"),
+    ("buckets in descending order",
+     ["start[bk[i] + 1] += 1;", "pm[start[bk[i]]++] = (int32_t)i;"],
+     ["start[nb - bk[i]] += 1;", "pm[start[nb - 1 - bk[i]]++] = (int32_t)i;"]),
+]
+
+
+def _pin_calls():
+    o = oracle
+    return [
+        lambda: pins.test_hash_hand_worked_examples(o),
+        lambda: pins.test_hash_signed_permutation_closed_form(o),
+        lambda: pins.test_hash_rescale_invariance(o),
+        lambda: pins.test_hash_antipodal(o),
+        lambda: pins.test_sort_is_the_stable_bucket_order(o, 4, False),
+        lambda: pins.test_sort_is_the_stable_bucket_order(o, 64, True),
+        lambda: pins.test_windows_hand_enumerated(o, False),
+        lambda: pins.test_windows_hand_enumerated(o, True),
+        lambda: pins.test_single_chunk_equals_full_attention(o, 1, 1, True),
+        lambda: pins.test_single_chunk_equals_full_attention(o, 8, 3, False),
+        lambda: pins.test_dense_mask_and_multiset_union(o, True),
+        lambda: pins.test_identical_rounds_collapse(o),
+        lambda: pins.test_self_only_rows_return_their_value(o),
+    ]
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(tmp_path, name, orig, bad):
+    src = oracle.source_text()
+    origs = orig if isinstance(orig, list) else [orig]
+    bads = bad if isinstance(bad, list) else [bad]
+    for o, b in zip(origs, bads):
+        assert src.count(o) == 1, f"mutation anchor not found once: {o!r}"
+        src = src.replace(o, b)
+    lib = oracle.compile_source(src, str(tmp_path / "liblsh_oracle_mut.so"))
+    oracle.use_library(lib)
+    failures = 0
+    try:
+        for call in _pin_calls():
+            try:
+                call()
+            except (AssertionError, ValueError, IndexError):
+                failures += 1
+    finally:
+        oracle.use_library(None)
+    assert failures > 0, f"no pin caught: {name}"
+
+
+def test_unmutated_copy_passes_every_pin(tmp_path):
+    lib = oracle.compile_source(oracle.source_text(), str(tmp_path / "liblsh_oracle_copy.so"))
+    oracle.use_library(lib)
+    try:
+        for call in _pin_calls():
+            call()
+    finally:
+        oracle.use_library(None)
