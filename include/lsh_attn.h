@@ -1,0 +1,135 @@
+/*
+ * lsh_attn.h -- C ABI of the MI355X (gfx950) Reformer shared-QK LSH
+ * self-attention forward pass.
+ *
+ * What one forward computes (the Reformer summary at p2.ttnews.xyz, sections
+ * on LSH, LSH attention, multi-round LSH and the shared-QK self-mask; the
+ * overview at www.dtcms.com/a/488796.html, section 2.1):
+ *   1. hash: for every position i and round r, bucket = argmax([x R_r; -x R_r])
+ *      where x is the shared query/key vector and R_r a [d, n_buckets/2]
+ *      rotation; lowest index on exact ties;
+ *   2. sort: positions ordered by (bucket, position) per (batch, head, round);
+ *   3. gather: qk and v rows in sorted order;
+ *   4. chunked attention: the sorted sequence is cut into chunks of chunk_len;
+ *      a query attends to its chunk and the previous one (none before chunk 0),
+ *      with unit-normalised keys, logits (q . k/|k|) / sqrt(d), an optional
+ *      causal mask on original positions, and a self-mask: its own key gets
+ *      logit -1e5, so it is used only when nothing else is attendable. Each
+ *      round yields an output row o_r(i) and its logsumexp lse_r(i);
+ *   5. unsort and combine: out(i) = sum_r softmax_r(lse_r(i)) o_r(i).
+ *
+ * Conventions for every entry point:
+ *   - tensor arguments are DEVICE pointers on the current HIP device,
+ *     contiguous, row-major, and owned by the caller; the library never frees
+ *     or retains them past the call;
+ *   - the config and handle pointers are HOST pointers;
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream); all device work is enqueued on it and the call returns without
+ *     waiting for the device;
+ *   - every function returns a lsh_attn_status_t; nothing is thrown across
+ *     the ABI. lsh_attn_strerror() maps a status to a static string.
+ */
+#ifndef LSH_ATTN_H
+#define LSH_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lsh_attn_s* lsh_attn_t;
+
+typedef enum {
+  LSH_ATTN_FP32 = 0,
+  LSH_ATTN_BF16 = 1
+} lsh_attn_dtype_t;
+
+typedef enum {
+  LSH_ATTN_OK = 0,
+  LSH_ATTN_ERR_INVALID_ARG = 1,   /* null required pointer, bad sizes, bad flag */
+  LSH_ATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, dtype) */
+  LSH_ATTN_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed in create */
+  LSH_ATTN_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} lsh_attn_status_t;
+
+/* Flags (bit set in lsh_attn_config_t.flags). */
+enum {
+  /* Run the gather as its own kernel that writes sorted copies of qk and v
+   * (workspace grows by 2 * n_rounds * |qk|). By default the chunk-attention
+   * kernel reads rows through the permutation itself. Results are identical. */
+  LSH_ATTN_FLAG_SEPARATE_GATHER = 1
+};
+
+typedef struct {
+  int32_t batch, heads, seq_len, head_dim; /* qk, v, out: [batch, heads, seq_len, head_dim] */
+  int32_t n_buckets;  /* 1 (hash skipped: every position in bucket 0), or even in [2, 65536] */
+  int32_t n_rounds;   /* >= 1 independent hash rounds */
+  int32_t chunk_len;  /* >= 1 and divides seq_len; 64 is the tuned value */
+  int32_t causal;     /* 0 or 1 */
+  int32_t dtype;      /* lsh_attn_dtype_t of qk and v */
+  int32_t out_dtype;  /* lsh_attn_dtype_t of out; arithmetic is fp32 (fp64 for hash ties) */
+  int32_t flags;      /* LSH_ATTN_FLAG_* */
+} lsh_attn_config_t;
+
+/*
+ * Create a handle for one problem shape. Validates the config and allocates
+ * the device workspace on the current device (hipMalloc): bucket ids, the
+ * permutation, per-round outputs and logsumexps, sort histograms, and (with
+ * LSH_ATTN_FLAG_SEPARATE_GATHER) the sorted copies. The handle owns it.
+ * Errors: INVALID_ARG for a null pointer, non-positive sizes,
+ * seq_len % chunk_len != 0, an odd n_buckets > 1, n_buckets > 65536,
+ * n_buckets * 2^ceil(log2(seq_len)) > 2^32, causal not 0/1, unknown flags;
+ * UNSUPPORTED for head_dim not in {64, 128}, chunk_len != 64, or a dtype
+ * outside the enum; OUT_OF_MEMORY if the workspace cannot be allocated.
+ * On error *handle is set to NULL and nothing is left allocated.
+ */
+int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle);
+
+/*
+ * Enqueue one forward pass on `stream`.
+ *   qk        [B, H, L, d]          dtype     shared query/key vectors (read only)
+ *   v         [B, H, L, d]          dtype     values (read only)
+ *   rotations [n_rounds, d, n_buckets/2] fp32 random rotations (read only);
+ *                                          may be NULL only when n_buckets == 1
+ *   out       [B, H, L, d]          out_dtype combined output (written)
+ *   lse       [B, H, n_rounds, L]   fp32, nullable: per-round logsumexp at each
+ *                                          ORIGINAL position (-1e5 for a round in
+ *                                          which the position saw only itself)
+ *   buckets   [B, H, n_rounds, L]   int32, nullable: bucket ids
+ *   perm      [B, H, n_rounds, L]   int32, nullable: sorted slot -> position
+ * Inputs must not alias outputs. NaN/Inf inputs give undefined results (not
+ * checked). One forward at a time per handle: the workspace is reused, so
+ * two forwards of one handle must be ordered on the device (same stream).
+ * Performs no allocation and no host/device synchronisation.
+ * Errors: INVALID_ARG for a null handle or required pointer; HIP when a launch
+ * fails (hipGetLastError after the launches).
+ */
+int lsh_attn_forward(lsh_attn_t handle, const void* qk, const void* v, const float* rotations,
+                     void* out, float* lse, int32_t* buckets, int32_t* perm, void* stream);
+
+/*
+ * Counters of the last forward (waits for the handle's last stream):
+ *   n_exact_rescored: hash decisions the bulk projection could not certify and
+ *   that were settled by recomputing the candidates in fp64.
+ * Errors: INVALID_ARG for null pointers; HIP if the copy fails.
+ */
+typedef struct {
+  int64_t n_exact_rescored;
+  int64_t n_full_fallback;
+} lsh_attn_stats_t;
+int lsh_attn_get_stats(lsh_attn_t handle, lsh_attn_stats_t* stats);
+
+/* Bytes of device workspace the handle holds. INVALID_ARG for null pointers. */
+int lsh_attn_workspace_bytes(lsh_attn_t handle, int64_t* bytes);
+
+/* Free the workspace (synchronises the device first). NULL is accepted. */
+int lsh_attn_destroy(lsh_attn_t handle);
+
+/* Static, never-NULL description of a status code. */
+const char* lsh_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSH_ATTN_H */

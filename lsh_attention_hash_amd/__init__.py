@@ -1,0 +1,201 @@
+"""MI355X-native Reformer shared-QK LSH self-attention (forward).
+
+Thin Python binding of the C ABI in include/lsh_attn.h. This module only
+marshals arguments: it checks devices, dtypes, shapes and contiguity, allocates
+outputs with torch on the current device, and passes raw pointers and torch's
+current HIP stream to liblsh_attn.so. Every step of the computation runs in the
+library's HIP kernels. There is no CPU fallback: if the library is not built or
+cannot be loaded, use of this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["LSHAttention", "load_library", "library_path", "LSHAttnError", "EXPORTED_SYMBOLS",
+           "FLAG_SEPARATE_GATHER"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "_lib", "liblsh_attn.so")
+
+FP32, BF16 = 0, 1
+FLAG_SEPARATE_GATHER = 1
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP"}
+
+# Every function declared in include/lsh_attn.h.
+EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats",
+                    "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror")
+
+
+class LSHAttnError(RuntimeError):
+    def __init__(self, status: int, where: str, lib=None):
+        msg = lib.lsh_attn_strerror(status).decode() if lib is not None else ""
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len", "causal",
+        "dtype", "out_dtype", "flags")]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("n_exact_rescored", ctypes.c_int64), ("n_full_fallback", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load liblsh_attn.so (raises if it is missing: build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m lsh_attention_hash_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.lsh_attn_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
+    lib.lsh_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P]
+    lib.lsh_attn_get_stats.argtypes = [P, ctypes.POINTER(Stats)]
+    lib.lsh_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.lsh_attn_destroy.argtypes = [P]
+    lib.lsh_attn_strerror.argtypes = [I]
+    lib.lsh_attn_strerror.restype = ctypes.c_char_p
+    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats",
+              "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
+        getattr(lib, n).restype = I
+    _lib = lib
+    return lib
+
+
+def _dtype_code(dt) -> int:
+    if dt in (torch.bfloat16, "bf16", BF16):
+        return BF16
+    if dt in (torch.float32, "fp32", FP32):
+        return FP32
+    raise ValueError(f"unsupported dtype {dt!r}")
+
+
+_TORCH = {BF16: torch.bfloat16, FP32: torch.float32}
+
+
+def make_config(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len=64,
+                causal=False, dtype=torch.bfloat16, out_dtype=None, flags=0) -> Config:
+    dc = _dtype_code(dtype)
+    oc = dc if out_dtype is None else _dtype_code(out_dtype)
+    return Config(int(batch), int(heads), int(seq_len), int(head_dim), int(n_buckets),
+                  int(n_rounds), int(chunk_len), int(causal), dc, oc, int(flags))
+
+
+class LSHAttention:
+    """One problem shape bound to a library handle (and its device workspace).
+
+    Call with qk, v [B, H, L, d] (dtype) and rotations [n_rounds, d, n_buckets/2]
+    float32, all contiguous on the handle's device. Returns out [B, H, L, d]
+    (out_dtype), or (out, extras) when any return_* flag is set, with extras
+    holding lse [B, H, R, L] float32, buckets and perm [B, H, R, L] int32.
+    """
+
+    def __init__(self, batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len=64,
+                 causal=False, dtype=torch.bfloat16, out_dtype=None, separate_gather=False,
+                 device=None):
+        self.lib = load_library()
+        self.cfg = make_config(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len,
+                               causal, dtype, out_dtype,
+                               FLAG_SEPARATE_GATHER if separate_gather else 0)
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None
+                                   else torch.device(device).index or 0)
+        self.handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            rc = self.lib.lsh_attn_create(ctypes.byref(self.cfg), ctypes.byref(self.handle))
+        if rc != 0:
+            self.handle = ctypes.c_void_p()
+            raise LSHAttnError(rc, "lsh_attn_create", self.lib)
+
+    @property
+    def dtype(self):
+        return _TORCH[self.cfg.dtype]
+
+    @property
+    def out_dtype(self):
+        return _TORCH[self.cfg.out_dtype]
+
+    def _check(self, name, t, shape, dtype):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device != self.device:
+            raise ValueError(f"{name} is on {t.device}, expected {self.device}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def __call__(self, qk, v, rotations, out=None, return_lse=False, return_buckets=False,
+                 return_perm=False, stream=None):
+        c = self.cfg
+        shp = (c.batch, c.heads, c.seq_len, c.head_dim)
+        self._check("qk", qk, shp, self.dtype)
+        self._check("v", v, shp, self.dtype)
+        if c.n_buckets > 1:
+            self._check("rotations", rotations, (c.n_rounds, c.head_dim, c.n_buckets // 2),
+                        torch.float32)
+        elif rotations is not None:
+            raise ValueError("rotations must be None when n_buckets == 1")
+        if out is None:
+            out = torch.empty(shp, dtype=self.out_dtype, device=self.device)
+        else:
+            self._check("out", out, shp, self.out_dtype)
+        per_round = (c.batch, c.heads, c.n_rounds, c.seq_len)
+        lse = torch.empty(per_round, dtype=torch.float32, device=self.device) if return_lse else None
+        bk = torch.empty(per_round, dtype=torch.int32, device=self.device) if return_buckets else None
+        pm = torch.empty(per_round, dtype=torch.int32, device=self.device) if return_perm else None
+        s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        with torch.cuda.device(self.device):
+            rc = self.lib.lsh_attn_forward(self.handle, ptr(qk), ptr(v), ptr(rotations), ptr(out),
+                                           ptr(lse), ptr(bk), ptr(pm), ctypes.c_void_p(s))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_forward", self.lib)
+        if return_lse or return_buckets or return_perm:
+            return out, {"lse": lse, "buckets": bk, "perm": pm}
+        return out
+
+    def stats(self) -> dict:
+        st = Stats()
+        rc = self.lib.lsh_attn_get_stats(self.handle, ctypes.byref(st))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_get_stats", self.lib)
+        return {"n_exact_rescored": st.n_exact_rescored, "n_full_fallback": st.n_full_fallback}
+
+    def workspace_bytes(self) -> int:
+        b = ctypes.c_int64()
+        rc = self.lib.lsh_attn_workspace_bytes(self.handle, ctypes.byref(b))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_workspace_bytes", self.lib)
+        return int(b.value)
+
+    def close(self):
+        if self.handle:
+            rc = self.lib.lsh_attn_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+            if rc != 0:
+                raise LSHAttnError(rc, "lsh_attn_destroy", self.lib)
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                self.lib.lsh_attn_destroy(self.handle)
+                self.handle = ctypes.c_void_p()
+        except Exception:
+            pass

@@ -1,0 +1,58 @@
+// internal.h -- shared declarations of the HIP library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsh_attn.h"
+
+namespace lsh {
+
+// Value of the logit a query gives its own key, and the logsumexp of a round
+// in which it sees nothing else. Exactly representable in fp32.
+constexpr float kSelfLogit = -1.0e5f;
+
+// One wave is 64 lanes on CDNA.
+constexpr int kWave = 64;
+
+// Elements of one (segment, tile) in the sort's histogram and scatter phases.
+constexpr int kSortTile = 1024;
+
+struct Problem {
+  int B, H, L, d, nb, R, m, causal, dtype, out_dtype, flags;
+  int64_t nbh() const { return (int64_t)B * H; }
+  int64_t nseg() const { return nbh() * R; }           // (batch, head, round) segments
+  int64_t n_token_heads() const { return nbh() * L; }
+  int64_t n_rows() const { return nseg() * L; }        // (segment, position) pairs
+  int half() const { return nb / 2; }
+  int sort_tiles() const { return (L + kSortTile - 1) / kSortTile; }
+};
+
+// Device workspace owned by a handle. Per-round arrays are [seg, L(, d)] with
+// seg = (b * H + h) * R + r, i.e. the [B, H, R, L] layout of the ABI.
+struct Workspace {
+  uint16_t* buckets = nullptr;     // [seg, L]
+  int32_t* perm = nullptr;         // [seg, L] sorted slot -> position
+  float* o = nullptr;              // [seg, L, d] per-round outputs at original positions
+  float* lse = nullptr;            // [seg, L]
+  uint32_t* sort_counts = nullptr; // [seg, nb, tiles] counts, then exclusive offsets
+  void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
+  void* v_sorted = nullptr;        // [seg, L, d]
+  unsigned long long* stats = nullptr;  // [2] exact rescored, full fallback
+};
+
+// Kernel launchers (each defined next to its kernels). All enqueue on `s` and
+// return hipGetLastError().
+hipError_t launch_hash(const Problem& p, const void* qk, const float* rot, uint16_t* buckets,
+                       int32_t* buckets_out, unsigned long long* stats, hipStream_t s);
+hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,
+                       int32_t* perm, hipStream_t s);
+hipError_t launch_gather(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+                         void* qk_sorted, void* v_sorted, hipStream_t s);
+hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const void* qk_sorted,
+                         const void* v_sorted, const int32_t* perm, float* o, float* lse,
+                         hipStream_t s);
+hipError_t launch_combine(const Problem& p, const float* o, const float* lse, void* out,
+                          hipStream_t s);
+
+}  // namespace lsh

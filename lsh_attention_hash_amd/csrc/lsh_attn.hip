@@ -1,0 +1,189 @@
+// lsh_attn.hip -- host side of the C ABI declared in include/lsh_attn.h:
+// argument checks, the workspace, and the launch sequence
+//   hash -> sort -> (gather) -> chunked attention -> combine
+// on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "internal.h"
+#include "lsh_attn.h"
+
+struct lsh_attn_s {
+  lsh::Problem p;
+  lsh::Workspace ws;
+  int device = 0;
+  int64_t bytes = 0;
+  hipStream_t last_stream = nullptr;
+};
+
+namespace {
+
+__global__ void k_zero_u64(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+int validate(const lsh_attn_config_t* c) {
+  if (!c) return LSH_ATTN_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->heads < 1 || c->seq_len < 1 || c->head_dim < 1)
+    return LSH_ATTN_ERR_INVALID_ARG;
+  if (c->seq_len > (1 << 24)) return LSH_ATTN_ERR_INVALID_ARG;
+  if (c->n_rounds < 1 || c->chunk_len < 1 || c->seq_len % c->chunk_len != 0)
+    return LSH_ATTN_ERR_INVALID_ARG;
+  if (c->n_buckets < 1 || c->n_buckets > 65536 || (c->n_buckets > 1 && c->n_buckets % 2 != 0))
+    return LSH_ATTN_ERR_INVALID_ARG;
+  if (c->causal != 0 && c->causal != 1) return LSH_ATTN_ERR_INVALID_ARG;
+  if ((c->flags & ~LSH_ATTN_FLAG_SEPARATE_GATHER) != 0) return LSH_ATTN_ERR_INVALID_ARG;
+  if (c->dtype != LSH_ATTN_FP32 && c->dtype != LSH_ATTN_BF16) return LSH_ATTN_ERR_UNSUPPORTED;
+  if (c->out_dtype != LSH_ATTN_FP32 && c->out_dtype != LSH_ATTN_BF16)
+    return LSH_ATTN_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return LSH_ATTN_ERR_UNSUPPORTED;
+  if (c->chunk_len > 256) return LSH_ATTN_ERR_UNSUPPORTED;
+  return LSH_ATTN_OK;
+}
+
+void free_ws(lsh::Workspace& w) {
+  hipFree(w.buckets);
+  hipFree(w.perm);
+  hipFree(w.o);
+  hipFree(w.lse);
+  hipFree(w.sort_counts);
+  hipFree(w.qk_sorted);
+  hipFree(w.v_sorted);
+  hipFree(w.stats);
+  w = lsh::Workspace{};
+}
+
+template <typename T>
+bool alloc(T** ptr, int64_t bytes, int64_t& total) {
+  void* q = nullptr;
+  if (hipMalloc(&q, (size_t)(bytes > 0 ? bytes : 1)) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed allocation
+    return false;
+  }
+  *ptr = (T*)q;
+  total += bytes;
+  return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
+  if (!handle) return LSH_ATTN_ERR_INVALID_ARG;
+  *handle = nullptr;
+  const int rc = validate(cfg);
+  if (rc != LSH_ATTN_OK) return rc;
+  lsh_attn_s* h = new (std::nothrow) lsh_attn_s();
+  if (!h) return LSH_ATTN_ERR_OUT_OF_MEMORY;
+  h->p = lsh::Problem{cfg->batch,  cfg->heads,   cfg->seq_len, cfg->head_dim,
+                      cfg->n_buckets, cfg->n_rounds, cfg->chunk_len, cfg->causal,
+                      cfg->dtype,  cfg->out_dtype, cfg->flags};
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return LSH_ATTN_ERR_HIP;
+  }
+  const lsh::Problem& p = h->p;
+  const int64_t rows = p.n_rows();
+  const int esize = p.dtype == LSH_ATTN_BF16 ? 2 : 4;
+  lsh::Workspace& w = h->ws;
+  int64_t& t = h->bytes;
+  bool ok = alloc(&w.buckets, rows * 2, t) && alloc(&w.perm, rows * 4, t) &&
+            alloc(&w.o, rows * p.d * 4, t) && alloc(&w.lse, rows * 4, t) &&
+            alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
+            alloc(&w.stats, 2 * 8, t);
+  if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
+    ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
+  if (!ok) {
+    free_ws(w);
+    delete h;
+    return LSH_ATTN_ERR_OUT_OF_MEMORY;
+  }
+  *handle = h;
+  return LSH_ATTN_OK;
+}
+
+int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* rotations,
+                     void* out, float* lse, int32_t* buckets, int32_t* perm, void* stream) {
+  if (!h || !qk || !v || !out) return LSH_ATTN_ERR_INVALID_ARG;
+  const lsh::Problem& p = h->p;
+  if (p.nb > 1 && !rotations) return LSH_ATTN_ERR_INVALID_ARG;
+  if (!aligned16(qk) || !aligned16(v) || !aligned16(out)) return LSH_ATTN_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return LSH_ATTN_ERR_INVALID_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  lsh::Workspace& w = h->ws;
+  int32_t* pm = perm ? perm : w.perm;
+  float* ls = lse ? lse : w.lse;
+  hipError_t e = hipSuccess;
+  hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, w.stats, 2);
+  if (e == hipSuccess) e = lsh::launch_hash(p, qk, rotations, w.buckets, buckets, w.stats, s);
+  if (e == hipSuccess) e = lsh::launch_sort(p, w.buckets, w.sort_counts, pm, s);
+  const bool separate = (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER) != 0;
+  if (e == hipSuccess && separate)
+    e = lsh::launch_gather(p, qk, v, pm, w.qk_sorted, w.v_sorted, s);
+  if (e == hipSuccess)
+    e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
+                           separate ? w.v_sorted : nullptr, pm, w.o, ls, s);
+  if (e == hipSuccess) e = lsh::launch_combine(p, w.o, ls, out, s);
+  if (e == hipSuccess) e = hipGetLastError();
+  return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
+}
+
+int lsh_attn_get_stats(lsh_attn_t h, lsh_attn_stats_t* stats) {
+  if (!h || !stats) return LSH_ATTN_ERR_INVALID_ARG;
+  unsigned long long host[2] = {0, 0};
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess ||
+      hipMemcpy(host, h->ws.stats, sizeof(host), hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return LSH_ATTN_ERR_HIP;
+  }
+  stats->n_exact_rescored = (int64_t)host[0];
+  stats->n_full_fallback = (int64_t)host[1];
+  return LSH_ATTN_OK;
+}
+
+int lsh_attn_workspace_bytes(lsh_attn_t h, int64_t* bytes) {
+  if (!h || !bytes) return LSH_ATTN_ERR_INVALID_ARG;
+  *bytes = h->bytes;
+  return LSH_ATTN_OK;
+}
+
+int lsh_attn_destroy(lsh_attn_t h) {
+  if (!h) return LSH_ATTN_OK;
+  int prev = -1;
+  const bool switched = hipGetDevice(&prev) == hipSuccess && prev != h->device &&
+                        hipSetDevice(h->device) == hipSuccess;
+  const hipError_t e = hipDeviceSynchronize();
+  free_ws(h->ws);
+  if (switched) hipSetDevice(prev);
+  delete h;
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return LSH_ATTN_ERR_HIP;
+  }
+  return LSH_ATTN_OK;
+}
+
+const char* lsh_attn_strerror(int status) {
+  switch (status) {
+    case LSH_ATTN_OK: return "ok";
+    case LSH_ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case LSH_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LSH_ATTN_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case LSH_ATTN_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,166 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on seeded inputs.
+
+Small cases are compared element by element over every output; the full-size
+workloads are compared on every bucket of a few heads, on the whole
+permutation (the oracle's stable sort of the GPU's bucket ids), and on a few
+thousand sampled output rows. Each case prints what it is before it runs.
+"""
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import lsh_attention_hash_amd as lat
+from parity import (check_buckets, check_outputs_full, check_outputs_rows, check_perm,
+                    make_op, run_gpu, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lat.load_library()
+
+
+def W(name, **kw):
+    return workloads.get(name).with_(**kw)
+
+
+SMALL = [
+    # several sort tiles with a ragged tail (L = 64 * 37), ragged hash tiles
+    W("c4k", batch=1, heads=2, seq_len=2368, n_buckets=96, n_rounds=3, causal=True),
+    W("c4k", batch=2, heads=1, seq_len=2368, n_buckets=96, n_rounds=3, causal=False),
+    W("c4k", batch=1, heads=3, seq_len=1024, n_buckets=2, n_rounds=2, causal=True),
+    W("c4k", batch=1, heads=2, seq_len=1024, n_buckets=6, n_rounds=1, causal=False),
+    W("text64k", batch=1, heads=2, seq_len=1536, n_buckets=64, n_rounds=2, causal=True),
+    W("text64k", batch=1, heads=1, seq_len=4096, n_buckets=128, n_rounds=1, causal=False),
+    W("skewed", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=2),
+    W("image12k", batch=2, heads=2, seq_len=768, n_buckets=12, n_rounds=4),
+    W("c4k", batch=1, heads=1, seq_len=64, n_buckets=4, n_rounds=2, causal=True),   # one chunk
+    W("c4k", batch=1, heads=2, seq_len=512, n_buckets=1024, n_rounds=1, causal=False),  # nb > L
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-B{w.batch}H{w.heads}L{w.seq_len}"
+                         f"d{w.head_dim}nb{w.n_buckets}R{w.n_rounds}{'c' if w.causal else 'n'}")
+def test_small_full_parity(w):
+    _say(f"[small] {w}")
+    inp = workloads.make_inputs(w)
+    gpu = run_gpu(w, inp)
+    n, ties, tie_mis = check_buckets(w, inp, gpu["buckets"])
+    check_perm(w, gpu["buckets"], gpu["perm"])
+    err, lerr = check_outputs_full(w, inp, gpu)
+    _say(f"  buckets {n} ties {ties} tie-mismatch {tie_mis} out err {err:.3g} lse err {lerr:.3g}")
+
+
+def test_tiny_fp32_full_parity():
+    w = workloads.get("tiny")
+    _say(f"[tiny] {w}")
+    inp = workloads.make_inputs(w)
+    gpu = run_gpu(w, inp)
+    check_buckets(w, inp, gpu["buckets"])
+    check_perm(w, gpu["buckets"], gpu["perm"])
+    err, lerr = check_outputs_full(w, inp, gpu)
+    assert err <= 1e-5
+    _say(f"  out err {err:.3g} lse err {lerr:.3g}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_one_bucket_one_chunk_is_full_attention(causal, d):
+    """n_buckets = 1 and one chunk covering the sequence: the path reduces to
+    full shared-QK softmax attention with the self-mask."""
+    w = W("c4k", batch=2, heads=2, seq_len=128, head_dim=d, n_buckets=1, n_rounds=2,
+          chunk_len=128, causal=causal)
+    _say(f"[nb=1] {w}")
+    inp = workloads.make_inputs(w)
+    gpu = run_gpu(w, inp)
+    assert np.all(gpu["buckets"] == 0)
+    np.testing.assert_array_equal(gpu["perm"], np.broadcast_to(np.arange(w.seq_len),
+                                                               gpu["perm"].shape))
+    check_outputs_full(w, inp, gpu)
+
+
+def test_out_dtype_fp32_and_separate_gather():
+    w = W("c4k", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=2, causal=True)
+    _say(f"[out fp32 / separate gather] {w}")
+    inp = workloads.make_inputs(w)
+    a = run_gpu(w, inp, out_dtype=torch.float32)
+    check_outputs_full(w, inp, a)
+    b = run_gpu(w, inp, out_dtype=torch.float32, separate_gather=True)
+    for k in ("out", "lse", "buckets", "perm"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_deterministic():
+    w = W("skewed", batch=1, heads=2, seq_len=4096, n_buckets=64, n_rounds=4)
+    _say(f"[determinism] {w}")
+    inp = workloads.make_inputs(w)
+    op = make_op(w)
+    qk, v, rot = to_device(inp)
+    o1, e1 = op(qk, v, rot, return_lse=True, return_perm=True)
+    o2, e2 = op(qk, v, rot, return_lse=True, return_perm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(e1["lse"], e2["lse"]) and torch.equal(e1["perm"], e2["perm"])
+
+
+def test_zero_vectors_and_constant_rows():
+    """Zero qk rows: every projection is 0 (bucket 0 by the lowest-index rule,
+    margin 0 so it counts as a tie) and a zero key has logit 0."""
+    w = W("c4k", batch=1, heads=1, seq_len=512, n_buckets=16, n_rounds=2, causal=True)
+    _say(f"[zero rows] {w}")
+    inp = workloads.make_inputs(w)
+    inp.qk[0, 0, ::7] = 0.0
+    inp.qk_bits[0, 0, ::7] = 0
+    gpu = run_gpu(w, inp)
+    assert np.all(gpu["buckets"][0, 0, :, ::7] == 0)
+    check_buckets(w, inp, gpu["buckets"])
+    check_outputs_full(w, inp, gpu)
+
+
+FULL = ["c4k", "text64k", "image12k", "skewed"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_parity(name):
+    w = workloads.get(name)
+    _say(f"[full] {w}")
+    inp = workloads.make_inputs(w)
+    gpu = run_gpu(w, inp)
+    check_perm(w, gpu["buckets"], gpu["perm"])
+    sel = [(0, 0), (w.batch - 1, w.heads - 1)]
+    n, ties, tie_mis = check_buckets(w, inp, gpu["buckets"], bh_sel=sel)
+    err, lerr = check_outputs_rows(w, inp, gpu, n_rows=1024)
+    _say(f"  buckets checked {n} ties {ties} tie-mismatch {tie_mis} out err {err:.3g} "
+         f"lse err {lerr:.3g} stats {gpu['stats']}")
+
+
+def test_forward_rejects_null_and_misaligned_pointers():
+    w = W("c4k", batch=1, heads=1, seq_len=256, n_buckets=8, n_rounds=1)
+    op = make_op(w)
+    inp = workloads.make_inputs(w)
+    qk, v, rot = to_device(inp)
+    out = torch.empty_like(qk)
+    lib = op.lib
+    P = ctypes.c_void_p
+    s = P(torch.cuda.current_stream().cuda_stream)
+    assert lib.lsh_attn_forward(op.handle, None, P(v.data_ptr()), P(rot.data_ptr()),
+                                P(out.data_ptr()), None, None, None, s) == 1
+    assert lib.lsh_attn_forward(op.handle, P(qk.data_ptr()), P(v.data_ptr()), None,
+                                P(out.data_ptr()), None, None, None, s) == 1
+    assert lib.lsh_attn_forward(op.handle, P(qk.data_ptr() + 2), P(v.data_ptr()),
+                                P(rot.data_ptr()), P(out.data_ptr()), None, None, None, s) == 1
+    assert op.workspace_bytes() > 0
+    op.close()
