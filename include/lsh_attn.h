@@ -77,11 +77,11 @@ typedef struct {
  * the device workspace on the current device (hipMalloc): bucket ids, the
  * permutation, per-round outputs and logsumexps, sort histograms, and (with
  * LSH_ATTN_FLAG_SEPARATE_GATHER) the sorted copies. The handle owns it.
- * Errors: INVALID_ARG for a null pointer, non-positive sizes,
+ * Errors: INVALID_ARG for a null pointer, non-positive sizes, seq_len > 2^24,
  * seq_len % chunk_len != 0, an odd n_buckets > 1, n_buckets > 65536,
- * n_buckets * 2^ceil(log2(seq_len)) > 2^32, causal not 0/1, unknown flags;
- * UNSUPPORTED for head_dim not in {64, 128}, chunk_len != 64, or a dtype
- * outside the enum; OUT_OF_MEMORY if the workspace cannot be allocated.
+ * causal not 0/1, unknown flags; UNSUPPORTED for head_dim not in {64, 128},
+ * chunk_len > 256, or a dtype outside the enum; OUT_OF_MEMORY if the
+ * workspace cannot be allocated; HIP if no device is current.
  * On error *handle is set to NULL and nothing is left allocated.
  */
 int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle);
@@ -98,11 +98,12 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle);
  *                                          which the position saw only itself)
  *   buckets   [B, H, n_rounds, L]   int32, nullable: bucket ids
  *   perm      [B, H, n_rounds, L]   int32, nullable: sorted slot -> position
- * Inputs must not alias outputs. NaN/Inf inputs give undefined results (not
- * checked). One forward at a time per handle: the workspace is reused, so
+ * qk, v and out must be 16-byte aligned. Inputs must not alias outputs.
+ * NaN/Inf inputs give undefined results (not checked). One forward at a time per handle: the workspace is reused, so
  * two forwards of one handle must be ordered on the device (same stream).
  * Performs no allocation and no host/device synchronisation.
- * Errors: INVALID_ARG for a null handle or required pointer; HIP when a launch
+ * Errors: INVALID_ARG for a null handle or required pointer, a misaligned
+ * pointer, or a current device other than the handle's; HIP when a launch
  * fails (hipGetLastError after the launches).
  */
 int lsh_attn_forward(lsh_attn_t handle, const void* qk, const void* v, const float* rotations,
@@ -119,6 +120,27 @@ typedef struct {
   int64_t n_full_fallback;
 } lsh_attn_stats_t;
 int lsh_attn_get_stats(lsh_attn_t handle, lsh_attn_stats_t* stats);
+
+/*
+ * Per-stage device timing, for diagnostics and the benchmark. When enabled,
+ * each forward records a HIP event on its stream before the first stage and
+ * after every stage, for at most `capacity` forwards (later forwards are not
+ * timed). Events are created here (host call, no device memory).
+ * Stages: 0 hash, 1 sort, 2 gather (0 ms unless separate), 3 chunk attention,
+ * 4 combine.
+ * Errors: INVALID_ARG for a null handle or capacity < 0 (0 disables);
+ * HIP if events cannot be created.
+ */
+#define LSH_ATTN_N_STAGES 5
+int lsh_attn_set_timing(lsh_attn_t handle, int capacity);
+
+/*
+ * Sum of each stage's elapsed milliseconds over the timed forwards since the
+ * last call (waits for their events), and how many forwards that was; then
+ * starts a new accumulation. ms has LSH_ATTN_N_STAGES entries (host memory).
+ * Errors: INVALID_ARG for null pointers or timing not enabled; HIP on event errors.
+ */
+int lsh_attn_get_timing(lsh_attn_t handle, double* ms, int64_t* n_forwards);
 
 /* Bytes of device workspace the handle holds. INVALID_ARG for null pointers. */
 int lsh_attn_workspace_bytes(lsh_attn_t handle, int64_t* bytes);

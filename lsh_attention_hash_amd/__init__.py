@@ -27,7 +27,10 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "H
 
 # Every function declared in include/lsh_attn.h.
 EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats",
-                    "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror")
+                    "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_workspace_bytes",
+                    "lsh_attn_destroy", "lsh_attn_strerror")
+N_STAGES = 5
+STAGES = ("hash", "sort", "gather", "attend", "combine")
 
 
 class LSHAttnError(RuntimeError):
@@ -67,11 +70,14 @@ def load_library():
     lib.lsh_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_get_stats.argtypes = [P, ctypes.POINTER(Stats)]
     lib.lsh_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.lsh_attn_set_timing.argtypes = [P, I]
+    lib.lsh_attn_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64)]
     lib.lsh_attn_destroy.argtypes = [P]
     lib.lsh_attn_strerror.argtypes = [I]
     lib.lsh_attn_strerror.restype = ctypes.c_char_p
-    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats",
-              "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
+    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats", "lsh_attn_set_timing",
+              "lsh_attn_get_timing", "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
         getattr(lib, n).restype = I
     _lib = lib
     return lib
@@ -177,6 +183,21 @@ class LSHAttention:
         if rc != 0:
             raise LSHAttnError(rc, "lsh_attn_get_stats", self.lib)
         return {"n_exact_rescored": st.n_exact_rescored, "n_full_fallback": st.n_full_fallback}
+
+    def set_timing(self, capacity: int) -> None:
+        """Record per-stage HIP events for the next `capacity` forwards (0 disables)."""
+        rc = self.lib.lsh_attn_set_timing(self.handle, int(capacity))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_set_timing", self.lib)
+
+    def get_timing(self):
+        """(dict stage -> summed ms, number of timed forwards); resets the sums."""
+        ms = (ctypes.c_double * N_STAGES)()
+        n = ctypes.c_int64()
+        rc = self.lib.lsh_attn_get_timing(self.handle, ms, ctypes.byref(n))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_get_timing", self.lib)
+        return {k: float(ms[j]) for j, k in enumerate(STAGES)}, int(n.value)
 
     def workspace_bytes(self) -> int:
         b = ctypes.c_int64()

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <new>
+#include <vector>
 
 #include "internal.h"
 #include "lsh_attn.h"
@@ -17,6 +18,11 @@ struct lsh_attn_s {
   int device = 0;
   int64_t bytes = 0;
   hipStream_t last_stream = nullptr;
+  // stage timing: events[k * (N_STAGES + 1) + j] marks the start of stage j of
+  // timed forward k (j = N_STAGES marks the end of the last stage)
+  std::vector<hipEvent_t> events;
+  int timing_capacity = 0;
+  int timed = 0;
 };
 
 namespace {
@@ -122,20 +128,32 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   }
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
+  const bool timing = h->timed < h->timing_capacity;
+  hipEvent_t* ev = timing ? &h->events[(size_t)h->timed * (LSH_ATTN_N_STAGES + 1)] : nullptr;
+  if (timing) ++h->timed;
+  auto mark = [&](int j) {
+    if (ev) hipEventRecord(ev[j], s);
+  };
   lsh::Workspace& w = h->ws;
   int32_t* pm = perm ? perm : w.perm;
   float* ls = lse ? lse : w.lse;
   hipError_t e = hipSuccess;
   hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, w.stats, 2);
+  mark(0);
   if (e == hipSuccess) e = lsh::launch_hash(p, qk, rotations, w.buckets, buckets, w.stats, s);
+  mark(1);
   if (e == hipSuccess) e = lsh::launch_sort(p, w.buckets, w.sort_counts, pm, s);
+  mark(2);
   const bool separate = (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER) != 0;
   if (e == hipSuccess && separate)
     e = lsh::launch_gather(p, qk, v, pm, w.qk_sorted, w.v_sorted, s);
+  mark(3);
   if (e == hipSuccess)
     e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
                            separate ? w.v_sorted : nullptr, pm, w.o, ls, s);
+  mark(4);
   if (e == hipSuccess) e = lsh::launch_combine(p, w.o, ls, out, s);
+  mark(5);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
 }
@@ -153,6 +171,58 @@ int lsh_attn_get_stats(lsh_attn_t h, lsh_attn_stats_t* stats) {
   return LSH_ATTN_OK;
 }
 
+static void destroy_events(lsh_attn_s* h) {
+  for (hipEvent_t e : h->events) hipEventDestroy(e);
+  h->events.clear();
+  h->timing_capacity = 0;
+  h->timed = 0;
+}
+
+int lsh_attn_set_timing(lsh_attn_t h, int capacity) {
+  if (!h || capacity < 0) return LSH_ATTN_ERR_INVALID_ARG;
+  if (!h->events.empty() && hipStreamSynchronize(h->last_stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return LSH_ATTN_ERR_HIP;
+  }
+  destroy_events(h);
+  const size_t n = (size_t)capacity * (LSH_ATTN_N_STAGES + 1);
+  h->events.reserve(n);
+  for (size_t k = 0; k < n; ++k) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      destroy_events(h);
+      return LSH_ATTN_ERR_HIP;
+    }
+    h->events.push_back(e);
+  }
+  h->timing_capacity = capacity;
+  return LSH_ATTN_OK;
+}
+
+int lsh_attn_get_timing(lsh_attn_t h, double* ms, int64_t* n_forwards) {
+  if (!h || !ms || !n_forwards || h->timing_capacity == 0) return LSH_ATTN_ERR_INVALID_ARG;
+  for (int j = 0; j < LSH_ATTN_N_STAGES; ++j) ms[j] = 0.0;
+  for (int k = 0; k < h->timed; ++k) {
+    hipEvent_t* ev = &h->events[(size_t)k * (LSH_ATTN_N_STAGES + 1)];
+    if (hipEventSynchronize(ev[LSH_ATTN_N_STAGES]) != hipSuccess) {
+      (void)hipGetLastError();
+      return LSH_ATTN_ERR_HIP;
+    }
+    for (int j = 0; j < LSH_ATTN_N_STAGES; ++j) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, ev[j], ev[j + 1]) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSH_ATTN_ERR_HIP;
+      }
+      ms[j] += t;
+    }
+  }
+  *n_forwards = h->timed;
+  h->timed = 0;
+  return LSH_ATTN_OK;
+}
+
 int lsh_attn_workspace_bytes(lsh_attn_t h, int64_t* bytes) {
   if (!h || !bytes) return LSH_ATTN_ERR_INVALID_ARG;
   *bytes = h->bytes;
@@ -165,6 +235,7 @@ int lsh_attn_destroy(lsh_attn_t h) {
   const bool switched = hipGetDevice(&prev) == hipSuccess && prev != h->device &&
                         hipSetDevice(h->device) == hipSuccess;
   const hipError_t e = hipDeviceSynchronize();
+  destroy_events(h);
   free_ws(h->ws);
   if (switched) hipSetDevice(prev);
   delete h;
