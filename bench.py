@@ -67,7 +67,7 @@ KERNEL_BOUND = {
     "hash": ("fp64", "fp64_vector_TFLOPs"),     # exact fp64 projection
     "sort": ("hbm", "hbm_GBps"),
     "gather": ("hbm", "hbm_GBps"),
-    "attend": ("alu", "fp32_vector_TFLOPs"),    # fp32 vector online softmax
+    "attend": ("mfma", "mfma_bf16_TFLOPs"),     # bf16 MFMA QK^T and PV
     "combine": ("hbm", "hbm_GBps"),
 }
 
@@ -134,6 +134,7 @@ def main():
     ap.add_argument("--workload", default="text64k")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--separate-gather", action="store_true")
+    ap.add_argument("--fp32-round-outputs", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: as many as rounds fit the cores)")
@@ -169,7 +170,8 @@ def main():
     tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
     op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
                           w.chunk_len, w.causal, dtype=tdt[w.dtype], out_dtype=tdt[out_dtype],
-                          separate_gather=args.separate_gather)
+                          separate_gather=args.separate_gather,
+                          fp32_round_outputs=args.fp32_round_outputs)
     out = torch.empty((w.batch, w.heads, w.seq_len, w.head_dim), dtype=tdt[out_dtype],
                       device=dev)
     stream = torch.cuda.current_stream()
@@ -236,7 +238,8 @@ def main():
                    "qk_v_dtype": w.dtype, "out_dtype": out_dtype,
                    "inputs": f"{w.kind} seeded (qk {1000 + w.seed_base}, v {2000 + w.seed_base},"
                              f" R {3000 + w.seed_base})",
-                   "separate_gather": bool(args.separate_gather)},
+                   "separate_gather": bool(args.separate_gather),
+                   "round_outputs": "fp32" if args.fp32_round_outputs else "fp16"},
         "roofline": rl,
         "stages": per_stage,
         "token_heads_per_s": round(w.batch * w.heads * w.seq_len / (ms * 1e-3), 1),

@@ -58,7 +58,12 @@ enum {
   /* Run the gather as its own kernel that writes sorted copies of qk and v
    * (workspace grows by 2 * n_rounds * |qk|). By default the chunk-attention
    * kernel reads rows through the permutation itself. Results are identical. */
-  LSH_ATTN_FLAG_SEPARATE_GATHER = 1
+  LSH_ATTN_FLAG_SEPARATE_GATHER = 1,
+  /* Keep the per-round outputs in fp32 between the attention and the combine
+   * step. By default the matrix-core path (bf16 inputs) keeps them in fp16,
+   * which halves that traffic; fp16 saturates at +-65504, so inputs whose v
+   * exceeds that magnitude need this flag. */
+  LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2
 };
 
 typedef struct {

@@ -23,6 +23,7 @@ _LIB_PATH = os.path.join(_PKG, "_lib", "liblsh_attn.so")
 
 FP32, BF16 = 0, 1
 FLAG_SEPARATE_GATHER = 1
+FLAG_FP32_ROUND_OUTPUTS = 2
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP"}
 
 # Every function declared in include/lsh_attn.h.
@@ -113,11 +114,12 @@ class LSHAttention:
 
     def __init__(self, batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len=64,
                  causal=False, dtype=torch.bfloat16, out_dtype=None, separate_gather=False,
-                 device=None):
+                 fp32_round_outputs=False, device=None):
         self.lib = load_library()
+        flags = (FLAG_SEPARATE_GATHER if separate_gather else 0) | (
+            FLAG_FP32_ROUND_OUTPUTS if fp32_round_outputs else 0)
         self.cfg = make_config(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len,
-                               causal, dtype, out_dtype,
-                               FLAG_SEPARATE_GATHER if separate_gather else 0)
+                               causal, dtype, out_dtype, flags)
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None
                                    else torch.device(device).index or 0)
         self.handle = ctypes.c_void_p()

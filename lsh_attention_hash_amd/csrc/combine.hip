@@ -14,8 +14,11 @@
 namespace lsh {
 namespace {
 
-template <typename OutT>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o,
+__device__ __forceinline__ float ld_f32(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f32(const _Float16* p) { return (float)*p; }
+
+template <typename OutT, typename OT>
+__global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
                                                  const float* __restrict__ lse,
                                                  OutT* __restrict__ out, int L, int R, int d,
                                                  int64_t n_rows) {
@@ -35,26 +38,32 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ o,
       float acc = 0.f;
       for (int r = 0; r < R; ++r) {
         const float w = __expf(lr[(int64_t)r * L] - mx) * inv_sum;
-        acc += w * o[((bh * R + r) * L + i) * d + u];
+        acc += w * ld_f32(o + ((bh * R + r) * L + i) * d + u);
       }
       out[row * d + u] = from_f32<OutT>(acc);
     }
   }
 }
 
-}  // namespace
-
-hipError_t launch_combine(const Problem& p, const float* o, const float* lse, void* out,
-                          hipStream_t s) {
+template <typename OT>
+void launch_t(const Problem& p, const OT* o, const float* lse, void* out, hipStream_t s) {
   const int64_t n = p.n_token_heads();
   const int64_t want = (n + 3) / 4;
   const unsigned blocks = (unsigned)(want < 131072 ? want : 131072);
   if (p.out_dtype == LSH_ATTN_BF16)
-    hipLaunchKernelGGL(k_combine<bf16_t>, dim3(blocks), dim3(256), 0, s, o, lse,
+    hipLaunchKernelGGL((k_combine<bf16_t, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
                        (bf16_t*)out, p.L, p.R, p.d, n);
   else
-    hipLaunchKernelGGL(k_combine<float>, dim3(blocks), dim3(256), 0, s, o, lse, (float*)out,
-                       p.L, p.R, p.d, n);
+    hipLaunchKernelGGL((k_combine<float, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
+                       (float*)out, p.L, p.R, p.d, n);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
+                          void* out, hipStream_t s) {
+  if (o_half) launch_t<_Float16>(p, (const _Float16*)o, lse, out, s);
+  else launch_t<float>(p, (const float*)o, lse, out, s);
   return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ struct Problem {
 struct Workspace {
   uint16_t* buckets = nullptr;     // [seg, L]
   int32_t* perm = nullptr;         // [seg, L] sorted slot -> position
-  float* o = nullptr;              // [seg, L, d] per-round outputs at original positions
+  void* o = nullptr;               // [seg, L, d] per-round outputs at original positions
+                                   // (fp16, or fp32 with the fp32 flag / plain kernel)
   float* lse = nullptr;            // [seg, L]
   uint32_t* sort_counts = nullptr; // [seg, nb, tiles] counts, then exclusive offsets
   void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
@@ -52,7 +53,19 @@ hipError_t launch_gather(const Problem& p, const void* qk, const void* v, const 
 hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const void* qk_sorted,
                          const void* v_sorted, const int32_t* perm, float* o, float* lse,
                          hipStream_t s);
-hipError_t launch_combine(const Problem& p, const float* o, const float* lse, void* out,
-                          hipStream_t s);
+bool attend_mfma_supported(const Problem& p);
+template <typename OT>
+hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
+                              const void* qk_sorted, const void* v_sorted, const int32_t* perm,
+                              OT* o, float* lse, hipStream_t s);
+// o is fp16 when o_half, else fp32
+hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
+                          void* out, hipStream_t s);
+
+// Per-round outputs are kept in fp16 on the matrix-core path unless the
+// caller asks for fp32.
+inline bool round_outputs_half(const Problem& p) {
+  return attend_mfma_supported(p) && !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
+}
 
 }  // namespace lsh

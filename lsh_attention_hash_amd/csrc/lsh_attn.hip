@@ -41,7 +41,8 @@ int validate(const lsh_attn_config_t* c) {
   if (c->n_buckets < 1 || c->n_buckets > 65536 || (c->n_buckets > 1 && c->n_buckets % 2 != 0))
     return LSH_ATTN_ERR_INVALID_ARG;
   if (c->causal != 0 && c->causal != 1) return LSH_ATTN_ERR_INVALID_ARG;
-  if ((c->flags & ~LSH_ATTN_FLAG_SEPARATE_GATHER) != 0) return LSH_ATTN_ERR_INVALID_ARG;
+  if ((c->flags & ~(LSH_ATTN_FLAG_SEPARATE_GATHER | LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS)) != 0)
+    return LSH_ATTN_ERR_INVALID_ARG;
   if (c->dtype != LSH_ATTN_FP32 && c->dtype != LSH_ATTN_BF16) return LSH_ATTN_ERR_UNSUPPORTED;
   if (c->out_dtype != LSH_ATTN_FP32 && c->out_dtype != LSH_ATTN_BF16)
     return LSH_ATTN_ERR_UNSUPPORTED;
@@ -101,7 +102,8 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   lsh::Workspace& w = h->ws;
   int64_t& t = h->bytes;
   bool ok = alloc(&w.buckets, rows * 2, t) && alloc(&w.perm, rows * 4, t) &&
-            alloc(&w.o, rows * p.d * 4, t) && alloc(&w.lse, rows * 4, t) &&
+            alloc(&w.o, rows * p.d * (lsh::round_outputs_half(p) ? 2 : 4), t) &&
+            alloc(&w.lse, rows * 4, t) &&
             alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
             alloc(&w.stats, 2 * 8, t);
   if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
@@ -150,9 +152,9 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   mark(3);
   if (e == hipSuccess)
     e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
-                           separate ? w.v_sorted : nullptr, pm, w.o, ls, s);
+                           separate ? w.v_sorted : nullptr, pm, (float*)w.o, ls, s);
   mark(4);
-  if (e == hipSuccess) e = lsh::launch_combine(p, w.o, ls, out, s);
+  if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, out, s);
   mark(5);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;

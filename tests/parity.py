@@ -37,15 +37,17 @@ def to_device(inp: workloads.Inputs, device="cuda"):
     return qk, v, rot
 
 
-def make_op(w: workloads.Workload, out_dtype=None, separate_gather=False):
+def make_op(w: workloads.Workload, out_dtype=None, separate_gather=False,
+            fp32_round_outputs=False):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     return lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
                             w.chunk_len, w.causal, dtype=dt, out_dtype=out_dtype,
-                            separate_gather=separate_gather)
+                            separate_gather=separate_gather,
+                            fp32_round_outputs=fp32_round_outputs)
 
 
-def run_gpu(w, inp, out_dtype=None, separate_gather=False):
-    op = make_op(w, out_dtype, separate_gather)
+def run_gpu(w, inp, out_dtype=None, separate_gather=False, fp32_round_outputs=False):
+    op = make_op(w, out_dtype, separate_gather, fp32_round_outputs)
     qk, v, rot = to_device(inp)
     out, ex = op(qk, v, rot, return_lse=True, return_buckets=True, return_perm=True)
     torch.cuda.synchronize()

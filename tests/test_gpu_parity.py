@@ -103,6 +103,20 @@ def test_out_dtype_fp32_and_separate_gather():
         np.testing.assert_array_equal(a[k], b[k])
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_round_outputs(causal):
+    """Per-round outputs kept in fp32 instead of fp16: both within tolerance."""
+    w = W("text64k", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=3, causal=causal)
+    _say(f"[fp32 round outputs] {w}")
+    inp = workloads.make_inputs(w)
+    a = run_gpu(w, inp, out_dtype=torch.float32, fp32_round_outputs=True)
+    e32, _ = check_outputs_full(w, inp, a)
+    b = run_gpu(w, inp, out_dtype=torch.float32)
+    e16, _ = check_outputs_full(w, inp, b)
+    np.testing.assert_array_equal(a["lse"], b["lse"])
+    _say(f"  out err fp32 round outputs {e32:.3g}, fp16 {e16:.3g}")
+
+
 def test_deterministic():
     w = W("skewed", batch=1, heads=2, seq_len=4096, n_buckets=64, n_rounds=4)
     _say(f"[determinism] {w}")
