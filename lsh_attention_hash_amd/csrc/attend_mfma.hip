@@ -384,9 +384,9 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
   static bool configured = false;
   if (!configured) {
     // allow the dynamic LDS size above the 64 KiB default
-    hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, true>,
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, true>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
-    hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, false>,
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
     configured = true;
   }

@@ -76,9 +76,8 @@ __global__ void k_fill_bucket0(uint16_t* __restrict__ buckets, int32_t* __restri
 
 }  // namespace
 
-hipError_t launch_hash(const Problem& p, const void* qk, const float* rot, uint16_t* buckets,
-                       int32_t* buckets_out, unsigned long long* stats, hipStream_t s) {
-  (void)stats;
+hipError_t launch_hash_exact(const Problem& p, const void* qk, const float* rot,
+                             uint16_t* buckets, int32_t* buckets_out, hipStream_t s) {
   const int64_t n = p.n_rows();
   if (p.nb == 1) {
     const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;

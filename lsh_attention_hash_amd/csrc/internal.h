@@ -28,6 +28,15 @@ struct Problem {
   int sort_tiles() const { return (L + kSortTile - 1) / kSortTile; }
 };
 
+// Scratch of the matrix-core hash (hash_mfma.hip).
+struct HashScratch {
+  _Float16* rh = nullptr;     // [R, half_pad, d] fp16 rotations, transposed, zero-padded
+  float* rt = nullptr;        // [R, half, d] fp32 rotations, transposed (exact re-scoring)
+  unsigned* bounds = nullptr; // [R][4] norm bounds (float bits), then 2 queue counters
+  void* queue_a = nullptr;    // [R * N] two-candidate re-score entries (16 B)
+  void* queue_b = nullptr;    // [R * N] all-column re-score entries (8 B)
+};
+
 // Device workspace owned by a handle. Per-round arrays are [seg, L(, d)] with
 // seg = (b * H + h) * R + r, i.e. the [B, H, R, L] layout of the ABI.
 struct Workspace {
@@ -40,12 +49,20 @@ struct Workspace {
   void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
   void* v_sorted = nullptr;        // [seg, L, d]
   unsigned long long* stats = nullptr;  // [2] exact rescored, full fallback
+  HashScratch hash;                     // matrix-core hash only
 };
 
 // Kernel launchers (each defined next to its kernels). All enqueue on `s` and
 // return hipGetLastError().
-hipError_t launch_hash(const Problem& p, const void* qk, const float* rot, uint16_t* buckets,
-                       int32_t* buckets_out, unsigned long long* stats, hipStream_t s);
+// exact fp64 hash of every row (fp32 inputs, or shapes the matrix-core hash
+// does not cover)
+hipError_t launch_hash_exact(const Problem& p, const void* qk, const float* rot,
+                             uint16_t* buckets, int32_t* buckets_out, hipStream_t s);
+int hash_half_pad(const Problem& p);
+bool hash_mfma_supported(const Problem& p);
+hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
+                            uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
+                            hipStream_t s);
 hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,
                        int32_t* perm, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const void* qk, const void* v, const int32_t* perm,

@@ -60,6 +60,11 @@ void free_ws(lsh::Workspace& w) {
   hipFree(w.qk_sorted);
   hipFree(w.v_sorted);
   hipFree(w.stats);
+  hipFree(w.hash.rh);
+  hipFree(w.hash.rt);
+  hipFree(w.hash.bounds);
+  hipFree(w.hash.queue_a);
+  hipFree(w.hash.queue_b);
   w = lsh::Workspace{};
 }
 
@@ -106,6 +111,13 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
             alloc(&w.lse, rows * 4, t) &&
             alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
             alloc(&w.stats, 2 * 8, t);
+  if (ok && lsh::hash_mfma_supported(p)) {
+    const int64_t hp = lsh::hash_half_pad(p);
+    ok = alloc(&w.hash.rh, (int64_t)p.R * hp * p.d * 2, t) &&
+         alloc(&w.hash.rt, (int64_t)p.R * p.half() * p.d * 4, t) &&
+         alloc(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4, t) &&
+         alloc(&w.hash.queue_a, rows * 16, t) && alloc(&w.hash.queue_b, rows * 8, t);
+  }
   if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
     ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
   if (!ok) {
@@ -142,7 +154,12 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   hipError_t e = hipSuccess;
   hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, w.stats, 2);
   mark(0);
-  if (e == hipSuccess) e = lsh::launch_hash(p, qk, rotations, w.buckets, buckets, w.stats, s);
+  if (e == hipSuccess) {
+    if (lsh::hash_mfma_supported(p))
+      e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, s);
+    else
+      e = lsh::launch_hash_exact(p, qk, rotations, w.buckets, buckets, s);
+  }
   mark(1);
   if (e == hipSuccess) e = lsh::launch_sort(p, w.buckets, w.sort_counts, pm, s);
   mark(2);
