@@ -38,13 +38,15 @@ def esize(dt: str) -> int:
     return 2 if dt == "bf16" else 4
 
 
-def algorithmic_units(w, out_dtype: str):
+def algorithmic_units(w, out_dtype: str, round_bytes: int = 2):
     """Per-launch algorithmic work of each stage's kernel (what the method
     must compute or move, not what an implementation happens to move).
-    N = B*H*L token-heads, R rounds, d head dim, nb buckets, m chunk length."""
+    N = B*H*L token-heads, R rounds, d head dim, nb buckets, m chunk length;
+    round_bytes = bytes per element of the per-round outputs kept between the
+    attention and the combine (2 for fp16, 4 with the fp32 option)."""
     N = w.batch * w.heads * w.seq_len
     R, d, nb, m = w.n_rounds, w.head_dim, w.n_buckets, w.chunk_len
-    e, eo = esize(w.dtype), esize(out_dtype)
+    e, eo, ro = esize(w.dtype), esize(out_dtype), round_bytes
     return {
         # projection x.R for every token-head and round: nb/2 MACs of length d
         "hash": {"flops": N * R * d * nb, "bytes": N * d * e + N * R * 2},
@@ -55,16 +57,16 @@ def algorithmic_units(w, out_dtype: str):
         # QK^T and PV over the 2m-key window of every query-round; rows read
         # through the permutation, per-round output row and lse written
         "attend": {"flops": N * R * 4 * d * 2 * m,
-                   "bytes": N * R * (2 * d * e + 4 + d * 4 + 4)},
+                   "bytes": N * R * (2 * d * e + 4 + d * ro + 4)},
         # R per-round rows and lse read, one output row written
-        "combine": {"bytes": N * R * (d * 4 + 4) + N * d * eo},
+        "combine": {"bytes": N * R * (d * ro + 4) + N * d * eo},
     }
 
 
 # How each stage's kernel is bound in the current implementation, and the peak
 # it is measured against.
 KERNEL_BOUND = {
-    "hash": ("fp64", "fp64_vector_TFLOPs"),     # exact fp64 projection
+    "hash": ("mfma", "mfma_fp16_TFLOPs"),       # fp16 MFMA projection (+ rare fp64 re-score)
     "sort": ("hbm", "hbm_GBps"),
     "gather": ("hbm", "hbm_GBps"),
     "attend": ("mfma", "mfma_bf16_TFLOPs"),     # bf16 MFMA QK^T and PV
@@ -196,7 +198,8 @@ def main():
     stage_avg = {k: v_ / max(n_timed, 1) for k, v_ in stage_ms.items()}
     stats = op.stats()
 
-    units = algorithmic_units(w, out_dtype)
+    fp16_rounds = w.dtype == "bf16" and w.chunk_len == 64 and not args.fp32_round_outputs
+    units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4)
     if not args.separate_gather:
         stage_avg.pop("gather")   # rows are read through the permutation inside attend
     dominant = max(stage_avg, key=stage_avg.get)
@@ -239,7 +242,7 @@ def main():
                    "inputs": f"{w.kind} seeded (qk {1000 + w.seed_base}, v {2000 + w.seed_base},"
                              f" R {3000 + w.seed_base})",
                    "separate_gather": bool(args.separate_gather),
-                   "round_outputs": "fp32" if args.fp32_round_outputs else "fp16"},
+                   "round_outputs": "fp16" if fp16_rounds else "fp32"},
         "roofline": rl,
         "stages": per_stage,
         "token_heads_per_s": round(w.batch * w.heads * w.seq_len / (ms * 1e-3), 1),

@@ -12,14 +12,17 @@
 //   Kt : qk rows of the previous and current chunk, row-major (+16 B pad);
 //        they are the keys and, for the current chunk, the queries (shared QK);
 //   Vq : v rows stored as groups of 4 keys x d dims x 4 (8 bytes per dim), so
-//        that one 8-byte LDS read yields 4 consecutive keys of one dim, the
-//        B-operand layout of the P.V product;
+//        that one 8-byte LDS read yields 4 consecutive keys of one dim;
 //   per key: log2(e)/(sqrt(d) |k|), original position, and log2(e) |k|/sqrt(d).
 // The previous chunk stays in LDS, so every chunk is loaded once per walk.
+// Loads run two chunks ahead of the compute: the permutation entries of chunk
+// c+3 and the rows of chunk c+2 are in flight while chunk c is computed, so no
+// row load waits for its own index load.
 //
-// Per wave (32 queries = 2 blocks of 16), v_mfma_f32_16x16x32_bf16:
-//   S^T[key, query] = K Q^T over the 128-key window (64 for chunk 0);
-//   lane l holds query l%16 of each block and keys 16kb + 4(l/16) + 0..3.
+// Per wave (32 queries), v_mfma_f32_32x32x16_bf16:
+//   S^T[key, query] = K Q^T over the 128-key window (64 for chunk 0), 4
+//   blocks of 32 keys; lane l holds query l%32 and keys
+//   32kb + 8(v/4) + 4(l/32) + v%4, v = 0..15, of every block.
 // Softmax in log2 units, p = exp2(s * scale_key - m_query). The shift m is the
 // Cauchy-Schwarz bound |q| log2(e)/sqrt(d) >= every logit of the query (keys are
 // unit vectors), so no max pass is needed; if a bound exceeds 60 (a query norm
@@ -27,9 +30,12 @@
 // exp2 never under- or overflows. Masked keys (causal: later original position;
 // self) get p = 0. A query whose p are all 0 saw nothing but itself: its output
 // is v_i and its logsumexp -1e5, as in the definition.
-// P.V: the P block of the A operand comes straight from the S^T accumulators
-// (their key order is the order of the A operand's k index), the B operand
-// from Vq. An extra MFMA against a block of ones yields the row sums of the
+// O^T = V^T P^T: the B operand (P^T) comes straight from the S^T accumulators,
+// with the k index of each 16-key step ordered as the accumulator registers
+// (v = 8e..8e+7 of block kb), and the A operand (V^T) from two 8-byte Vq reads
+// in the same key order. In the output, lane l holds 4 consecutive dims of
+// query l%32 per register group, so each store writes 8 (fp16) or 16 (fp32)
+// contiguous bytes. An MFMA against a block of ones gives the row sums of the
 // bf16-rounded P, so numerator and denominator use the same weights; the
 // logsumexp takes the fp32 sum of the unrounded p.
 #include "dtype.h"
@@ -39,7 +45,7 @@ namespace lsh {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kChunk = 64;
 constexpr int kThreads = 128;  // 2 waves
@@ -50,7 +56,8 @@ constexpr float kBoundLimit = 60.0f;
 template <int D>
 struct Lds {
   static constexpr int kRow = D * 2 + 16;     // bytes per staged qk row
-  static constexpr int kQuad = D * 8 + 32;    // bytes per group of 4 v rows
+  static constexpr int kQuad = D * 8 + 128;   // bytes per group of 4 v rows (+128: the two
+                                              // lane halves of a read hit disjoint banks)
   static constexpr int kKt = 0;
   static constexpr int kVq = kKt + 2 * kChunk * kRow;
   static constexpr int kScale = kVq + 2 * (kChunk / 4) * kQuad;
@@ -63,37 +70,86 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo).bits | ((uint32_t)f32_to_bf16(hi).bits << 16);
 }
 
-template <typename OT>
-__device__ __forceinline__ void store_o(OT* p, float x);
-template <>
-__device__ __forceinline__ void store_o<float>(float* p, float x) { *p = x; }
-template <>
-__device__ __forceinline__ void store_o<_Float16>(_Float16* p, float x) {
-  x = fminf(fmaxf(x, -65504.0f), 65504.0f);
-  *p = (_Float16)x;
+// 4 consecutive outputs
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
+__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
+  typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+  f16x4_t v = {(_Float16)sat16(a), (_Float16)sat16(b), (_Float16)sat16(c), (_Float16)sat16(d)};
+  *(f16x4_t*)p = v;
 }
 
-// Stage chunk `c` of segment `seg` into LDS slot `sl`.
+// Thread t loads half t%2 of qk row t/2 and, for piece pp, 8 dims of the 4 v
+// rows of group (t + 128 pp) / (D/8).
 template <int D>
-__device__ __forceinline__ void load_chunk(unsigned char* lds, int sl, int c, const uint4* qk_rows,
-                                           const uint4* v_rows, const int32_t* pm, int64_t row0,
-                                           bool sorted, int64_t sorted_row0) {
-  using Lay = Lds<D>;
+struct ChunkRegs {
+  static constexpr int kPieces = D * 2 / 16;  // uint4 per row
+  static constexpr int kSegs = D / 8;         // 8-dim pieces per row
+  static constexpr int kPer = kSegs * 16 / kThreads;
+  uint4 qk[kPieces / 2];
+  uint4 v[kPer][4];
+  int pos;
+};
+
+// permutation entries (original positions) a chunk's loads need
+template <int D>
+struct PermRegs {
+  int pos;
+  int vpos[ChunkRegs<D>::kPer][4];
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_perm(PermRegs<D>& pr, int c, const int32_t* pm) {
+  using CR = ChunkRegs<D>;
   const int t = threadIdx.x;
-  constexpr int kPieces = D * 2 / 16;  // uint4 per row
-  // qk rows: thread t takes row t/2, half t%2
+  pr.pos = pm[c * kChunk + (t >> 1)];
+#pragma unroll
+  for (int pp = 0; pp < CR::kPer; ++pp) {
+    const int qd = (t + pp * kThreads) / CR::kSegs;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pr.vpos[pp][k] = pm[c * kChunk + qd * 4 + k];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& pr, int c,
+                                           const uint4* qk_rows, const uint4* v_rows,
+                                           int64_t row0, bool sorted, int64_t sorted_row0) {
+  using CR = ChunkRegs<D>;
+  const int t = threadIdx.x;
   {
     const int r = t >> 1, half = t & 1;
-    const int pos = pm[c * kChunk + r];
-    const uint4* src = sorted ? qk_rows + (sorted_row0 + c * kChunk + r) * kPieces
-                              : qk_rows + (row0 + pos) * kPieces;
-    uint4 x[kPieces / 2];
+    cr.pos = pr.pos;
+    const uint4* src = sorted ? qk_rows + (sorted_row0 + c * kChunk + r) * CR::kPieces
+                              : qk_rows + (row0 + pr.pos) * CR::kPieces;
 #pragma unroll
-    for (int k = 0; k < kPieces / 2; ++k) x[k] = src[half * (kPieces / 2) + k];
+    for (int k = 0; k < CR::kPieces / 2; ++k) cr.qk[k] = src[half * (CR::kPieces / 2) + k];
+  }
+#pragma unroll
+  for (int pp = 0; pp < CR::kPer; ++pp) {
+    const int id = t + pp * kThreads;
+    const int qd = id / CR::kSegs, sg = id % CR::kSegs;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t row = sorted ? sorted_row0 + c * kChunk + qd * 4 + k : row0 + pr.vpos[pp][k];
+      cr.v[pp][k] = v_rows[row * CR::kPieces + sg];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const ChunkRegs<D>& cr) {
+  using Lay = Lds<D>;
+  using CR = ChunkRegs<D>;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 1, half = t & 1;
     float nn = 0.f;
 #pragma unroll
-    for (int k = 0; k < kPieces / 2; ++k) {
-      const uint32_t w[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+    for (int k = 0; k < CR::kPieces / 2; ++k) {
+      const uint32_t w[4] = {cr.qk[k].x, cr.qk[k].y, cr.qk[k].z, cr.qk[k].w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float a = __uint_as_float(w[u] << 16), b = __uint_as_float(w[u] & 0xFFFF0000u);
@@ -102,43 +158,32 @@ __device__ __forceinline__ void load_chunk(unsigned char* lds, int sl, int c, co
       }
     }
     nn += __shfl_xor(nn, 1);
-    uint4* dst = (uint4*)(lds + Lay::kKt + (sl * kChunk + r) * Lay::kRow) + half * (kPieces / 2);
+    uint4* dst = (uint4*)(lds + Lay::kKt + (sl * kChunk + r) * Lay::kRow) + half * (CR::kPieces / 2);
 #pragma unroll
-    for (int k = 0; k < kPieces / 2; ++k) dst[k] = x[k];
+    for (int k = 0; k < CR::kPieces / 2; ++k) dst[k] = cr.qk[k];
     if (half == 0) {
       const float nrm = sqrtf(nn);
       const float sc = kLog2e / sqrtf((float)D);
       ((float*)(lds + Lay::kScale))[sl * kChunk + r] = nn > 0.f ? sc / nrm : 0.f;
-      ((int*)(lds + Lay::kPos))[sl * kChunk + r] = pos;
+      ((int*)(lds + Lay::kPos))[sl * kChunk + r] = cr.pos;
       ((float*)(lds + Lay::kBound))[sl * kChunk + r] = sc * nrm;
     }
   }
   // v rows, 4 keys x 8 dims per piece, stored as [quad][dim][4 keys]
-  {
-    constexpr int kSegs = D / 8;                      // 8-dim pieces per row
-    constexpr int kPer = kSegs * 16 / kThreads;       // pieces per thread (1 or 2)
 #pragma unroll
-    for (int pp = 0; pp < kPer; ++pp) {
-      const int id = t + pp * kThreads;
-      const int qd = id / kSegs, sg = id % kSegs;
-      uint4 x[4];
+  for (int pp = 0; pp < CR::kPer; ++pp) {
+    const int id = t + pp * kThreads;
+    const int qd = id / CR::kSegs, sg = id % CR::kSegs;
+    uint2* dst = (uint2*)(lds + Lay::kVq + (sl * (kChunk / 4) + qd) * Lay::kQuad) + sg * 8;
+    const uint32_t w0[4] = {cr.v[pp][0].x, cr.v[pp][0].y, cr.v[pp][0].z, cr.v[pp][0].w};
+    const uint32_t w1[4] = {cr.v[pp][1].x, cr.v[pp][1].y, cr.v[pp][1].z, cr.v[pp][1].w};
+    const uint32_t w2[4] = {cr.v[pp][2].x, cr.v[pp][2].y, cr.v[pp][2].z, cr.v[pp][2].w};
+    const uint32_t w3[4] = {cr.v[pp][3].x, cr.v[pp][3].y, cr.v[pp][3].z, cr.v[pp][3].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int slot = c * kChunk + qd * 4 + k;
-        const int64_t row = sorted ? sorted_row0 + slot : row0 + pm[slot];
-        x[k] = v_rows[row * kPieces + sg];
-      }
-      uint2* dst = (uint2*)(lds + Lay::kVq + (sl * (kChunk / 4) + qd) * Lay::kQuad) + sg * 8;
-      const uint32_t w0[4] = {x[0].x, x[0].y, x[0].z, x[0].w};
-      const uint32_t w1[4] = {x[1].x, x[1].y, x[1].z, x[1].w};
-      const uint32_t w2[4] = {x[2].x, x[2].y, x[2].z, x[2].w};
-      const uint32_t w3[4] = {x[3].x, x[3].y, x[3].z, x[3].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dst[2 * u] = make_uint2((w0[u] & 0xFFFFu) | (w1[u] << 16), (w2[u] & 0xFFFFu) | (w3[u] << 16));
-        dst[2 * u + 1] = make_uint2((w0[u] >> 16) | (w1[u] & 0xFFFF0000u),
-                                    (w2[u] >> 16) | (w3[u] & 0xFFFF0000u));
-      }
+    for (int u = 0; u < 4; ++u) {
+      dst[2 * u] = make_uint2((w0[u] & 0xFFFFu) | (w1[u] << 16), (w2[u] & 0xFFFFu) | (w3[u] << 16));
+      dst[2 * u + 1] = make_uint2((w0[u] >> 16) | (w1[u] & 0xFFFF0000u),
+                                  (w2[u] >> 16) | (w3[u] & 0xFFFF0000u));
     }
   }
 }
@@ -150,6 +195,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     const int32_t* __restrict__ perm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
     int nseg, int chunks_per_wg) {
   using Lay = Lds<D>;
+  constexpr int KS = D / 16;       // 16-dim K-steps of QK^T
+  constexpr int MB = D / 32;       // 32-dim blocks of the output
   extern __shared__ __align__(16) unsigned char lds[];
   const int nchunks = L / kChunk;
   const int64_t seg = blockIdx.x % (unsigned)nseg;
@@ -167,182 +214,185 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int g = lane >> 4;     // lane group 0..3
-  const int li = lane & 15;    // column within a 16-block
+  const int h = lane >> 5;     // lane half
+  const int lq = lane & 31;    // query (column) of this lane within the wave's 32
 
-  if (c0 > 0) load_chunk<D>(lds, (c0 - 1) & 1, c0 - 1, qk_rows, v_rows, pm, row0, sorted, srow0);
-  load_chunk<D>(lds, c0 & 1, c0, qk_rows, v_rows, pm, row0, sorted, srow0);
+  ChunkRegs<D> cr;
+  PermRegs<D> pr;
+  if (c0 > 0) {
+    fetch_perm<D>(pr, c0 - 1, pm);
+    fetch_rows<D>(cr, pr, c0 - 1, qk_rows, v_rows, row0, sorted, srow0);
+    stage_chunk<D>(lds, (c0 - 1) & 1, cr);
+  }
+  fetch_perm<D>(pr, c0, pm);
+  fetch_rows<D>(cr, pr, c0, qk_rows, v_rows, row0, sorted, srow0);
+  stage_chunk<D>(lds, c0 & 1, cr);
+  if (c0 + 1 < c1) {
+    fetch_perm<D>(pr, c0 + 1, pm);
+    fetch_rows<D>(cr, pr, c0 + 1, qk_rows, v_rows, row0, sorted, srow0);
+  }
+  if (c0 + 2 < c1) fetch_perm<D>(pr, c0 + 2, pm);
   __syncthreads();
 
   const float* kscale = (const float*)(lds + Lay::kScale);
   const int* kpos = (const int*)(lds + Lay::kPos);
   const float* kbound = (const float*)(lds + Lay::kBound);
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+  const uint32_t ones_u[4] = {one2, one2, one2, one2};
+  const bf16x8_t ones = *(const bf16x8_t*)ones_u;
 
   for (int c = c0; c < c1; ++c) {
     const int cur = c & 1, prv = cur ^ 1;
-    const int kb0 = c > 0 ? 0 : 4;  // chunk 0 has no previous chunk
-    // queries of this wave: 32w + 16qb + li
-    bf16x8_t qf[2][D / 32];
-    float mq[2];
-    int posq[2];
+    const int kb0 = c > 0 ? 0 : 2;  // chunk 0 has no previous chunk
+    const int q = 32 * w + lq;      // this lane's query row in the chunk
+    float mq = kbound[cur * kChunk + q];
+    const int posq = kpos[cur * kChunk + q];
+    // S^T = K Q^T; K index of each step: dims h*D/2 + 8ks + 0..7 in both operands
+    bf16x8_t qf[KS];
+    {
+      const unsigned char* row = lds + Lay::kKt + (cur * kChunk + q) * Lay::kRow + h * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = 32 * w + 16 * qb + li;
-      const unsigned char* row = lds + Lay::kKt + (cur * kChunk + q) * Lay::kRow;
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) qf[qb][ks] = *(const bf16x8_t*)(row + (ks * 32 + 8 * g) * 2);
-      mq[qb] = kbound[cur * kChunk + q];
-      posq[qb] = kpos[cur * kChunk + q];
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(row + ks * 16);
     }
-    // S^T = K Q^T
-    floatx4_t s[8][2];
+    floatx16_t sacc[4];
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = floatx16_t{};
       if (kb < kb0) continue;
-      const int sl = kb < 4 ? prv : cur;
-      const unsigned char* row = lds + Lay::kKt + (sl * kChunk + (kb & 3) * 16 + li) * Lay::kRow;
+      const int sl = kb < 2 ? prv : cur;
+      const unsigned char* row = lds + Lay::kKt + (sl * kChunk + (kb & 1) * 32 + lq) * Lay::kRow + h * D;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const bf16x8_t a = *(const bf16x8_t*)(row + (ks * 32 + 8 * g) * 2);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][ks], s[kb][qb], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = *(const bf16x8_t*)(row + ks * 16);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // softmax weights in log2 units
-    const bool slow = __ballot(mq[0] > kBoundLimit || mq[1] > kBoundLimit) != 0ull;
-    // key kb*16 + 4g + vv is masked for query block qb: absent (chunk 0 has no
-    // previous chunk), the query itself, or (causal) a later original position
-    auto masked = [&](int kb, int qb, int vv, int kp) -> bool {
+    // key kb*32 + 8(v/4) + 4h + v%4 is masked: absent (chunk 0 has no previous
+    // chunk), the query itself, or (causal) a later original position
+    auto masked = [&](int kb, int v, int kp) -> bool {
       if (kb < kb0) return true;
-      const bool self = (kb == 4 + 2 * w + qb) && (4 * g + vv == li);
-      return self || (CAUSAL && kp > posq[qb]);
+      const bool self = (kb == 2 + w) && (8 * (v >> 2) + 4 * h + (v & 3) == lq);
+      return self || (CAUSAL && kp > posq);
     };
+    const bool slow = __ballot(mq > kBoundLimit) != 0ull;
     if (slow) {
-      float mx[2] = {-INFINITY, -INFINITY};
+      float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const int sl = kb < 4 ? prv : cur;
-        const float4 sc = *(const float4*)(kscale + sl * kChunk + (kb & 3) * 16 + 4 * g);
-        const int4 kp = *(const int4*)(kpos + sl * kChunk + (kb & 3) * 16 + 4 * g);
+      for (int kb = 0; kb < 4; ++kb) {
+        const int sl = kb < 2 ? prv : cur;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int key = (kb & 1) * 32 + 8 * a4 + 4 * h;
+          const float4 sc = *(const float4*)(kscale + sl * kChunk + key);
+          const int4 kp = *(const int4*)(kpos + sl * kChunk + key);
+          const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+          const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (!masked(kb, 4 * a4 + b, kpv[b])) mx = fmaxf(mx, sacc[kb][4 * a4 + b] * scv[b]);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mq = mx == -INFINITY ? 0.f : mx;
+    }
+    // p in bf16 as the B operand of O^T: step (kb, e) takes v = 8e..8e+7
+    bf16x8_t pf[4][2];
+    float rowsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int sl = kb < 2 ? prv : cur;
+      float p[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int key = (kb & 1) * 32 + 8 * a4 + 4 * h;
+        const float4 sc = *(const float4*)(kscale + sl * kChunk + key);
+        const int4 kp = *(const int4*)(kpos + sl * kChunk + key);
         const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
         const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int vv = 0; vv < 4; ++vv)
-            if (!masked(kb, qb, vv, kpv[vv])) mx[qb] = fmaxf(mx[qb], s[kb][qb][vv] * scv[vv]);
+        for (int b = 0; b < 4; ++b) {
+          const int vv = 4 * a4 + b;
+          const float x = fmaf(sacc[kb][vv], scv[b], -mq);
+          p[vv] = masked(kb, vv, kpv[b]) ? 0.f : __builtin_amdgcn_exp2f(x);
+          rowsum += p[vv];
+        }
       }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float m = fmaxf(mx[qb], __shfl_xor(mx[qb], 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        mq[qb] = m == -INFINITY ? 0.f : m;
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t u[4] = {pack_bf16x2(p[8 * e + 0], p[8 * e + 1]),
+                               pack_bf16x2(p[8 * e + 2], p[8 * e + 3]),
+                               pack_bf16x2(p[8 * e + 4], p[8 * e + 5]),
+                               pack_bf16x2(p[8 * e + 6], p[8 * e + 7])};
+        pf[kb][e] = *(const bf16x8_t*)u;
       }
     }
-    bf16x8_t pf[2][4];
-    float rowsum[2] = {0.f, 0.f};  // fp32 sum of p, for the logsumexp
+    rowsum += __shfl_xor(rowsum, 32);
+    // O^T = V^T P^T (+ row sums against ones)
+    floatx16_t oacc[MB];
+    floatx16_t lacc = floatx16_t{};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float p[2][8];
+    for (int mb = 0; mb < MB; ++mb) oacc[mb] = floatx16_t{};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kb = 2 * t + h;
-        const int sl = kb < 4 ? prv : cur;
-        const float4 sc = *(const float4*)(kscale + sl * kChunk + (kb & 3) * 16 + 4 * g);
-        const int4 kp = *(const int4*)(kpos + sl * kChunk + (kb & 3) * 16 + 4 * g);
-        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-        const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb < kb0) continue;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+      for (int e = 0; e < 2; ++e) {
+        // keys 32kb + 16e + 4h + 0..3 and 32kb + 16e + 8 + 4h + 0..3 (window order)
+        const int qa = 8 * kb + 4 * e + h, qc = qa + 2;
+        const unsigned char* va =
+            lds + Lay::kVq + ((qa < 16 ? prv : cur) * (kChunk / 4) + (qa & 15)) * Lay::kQuad;
+        const unsigned char* vc =
+            lds + Lay::kVq + ((qc < 16 ? prv : cur) * (kChunk / 4) + (qc & 15)) * Lay::kQuad;
 #pragma unroll
-          for (int vv = 0; vv < 4; ++vv) {
-            const float x = fmaf(s[kb][qb][vv], scv[vv], -mq[qb]);
-            p[qb][4 * h + vv] = masked(kb, qb, vv, kpv[vv]) ? 0.f : __builtin_amdgcn_exp2f(x);
-            rowsum[qb] += p[qb][4 * h + vv];
+        for (int mb = 0; mb < MB; ++mb) {
+          const int dim = mb * 32 + lq;
+          const uint2 lo = *(const uint2*)(va + dim * 8);
+          const uint2 hi = *(const uint2*)(vc + dim * 8);
+          const uint32_t u[4] = {lo.x, lo.y, hi.x, hi.y};
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)u, pf[kb][e],
+                                                              oacc[mb], 0, 0, 0);
+        }
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[kb][e], lacc, 0, 0, 0);
+      }
+    }
+    // The next chunk, whose rows were loaded during this compute, is staged
+    // before this chunk's outputs are stored: a wait on those loads then does
+    // not also wait on the stores (one counter tracks both).
+    __syncthreads();  // every wave is done with slot prv
+    if (c + 1 < c1) stage_chunk<D>(lds, prv, cr);
+    // normalise and scatter to the query's original position
+    {
+      const float l = lacc[0];
+      OT* orow = o + (seg * L + posq) * D;
+      if (l > 0.f) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            store4(orow + mb * 32 + 8 * a4 + 4 * h, oacc[mb][4 * a4] * inv,
+                   oacc[mb][4 * a4 + 1] * inv, oacc[mb][4 * a4 + 2] * inv,
+                   oacc[mb][4 * a4 + 3] * inv);
+      } else {
+        const uint16_t* vr = v_raw + (row0 + posq) * D;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = mb * 32 + 8 * a4 + 4 * h;
+            store4(orow + d0, __uint_as_float((uint32_t)vr[d0] << 16),
+                   __uint_as_float((uint32_t)vr[d0 + 1] << 16),
+                   __uint_as_float((uint32_t)vr[d0 + 2] << 16),
+                   __uint_as_float((uint32_t)vr[d0 + 3] << 16));
           }
       }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const uint32_t u[4] = {pack_bf16x2(p[qb][0], p[qb][1]), pack_bf16x2(p[qb][2], p[qb][3]),
-                               pack_bf16x2(p[qb][4], p[qb][5]), pack_bf16x2(p[qb][6], p[qb][7])};
-        pf[qb][t] = *(const bf16x8_t*)u;
-      }
+      if (h == 0) lse[seg * L + posq] = l > 0.f ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
     }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      rowsum[qb] += __shfl_xor(rowsum[qb], 16);
-      rowsum[qb] += __shfl_xor(rowsum[qb], 32);
+    if (c + 2 < c1) {
+      fetch_rows<D>(cr, pr, c + 2, qk_rows, v_rows, row0, sorted, srow0);
+      if (c + 3 < c1) fetch_perm<D>(pr, c + 3, pm);
     }
-    // O = P V, plus row sums against a block of ones
-    floatx4_t acc[D / 16][2];
-    floatx4_t lsum[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      lsum[qb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) acc[nt][qb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
-    const uint32_t ones_u[4] = {one2, one2, one2, one2};
-    const bf16x8_t ones = *(const bf16x8_t*)ones_u;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if (2 * t < kb0) continue;
-      // keys 32t + 4g + 0..3 (quad 8t + g) and 32t + 16 + 4g + 0..3 (quad 8t + 4 + g)
-      const int qa = 8 * t + g, qc = 8 * t + 4 + g;
-      const unsigned char* va =
-          lds + Lay::kVq + ((qa < 16 ? prv : cur) * (kChunk / 4) + (qa & 15)) * Lay::kQuad;
-      const unsigned char* vc =
-          lds + Lay::kVq + ((qc < 16 ? prv : cur) * (kChunk / 4) + (qc & 15)) * Lay::kQuad;
-#pragma unroll
-      for (int nt = 0; nt < D / 16; ++nt) {
-        const int dim = nt * 16 + li;
-        const uint2 lo = *(const uint2*)(va + dim * 8);
-        const uint2 hi = *(const uint2*)(vc + dim * 8);
-        const uint32_t u[4] = {lo.x, lo.y, hi.x, hi.y};
-        const bf16x8_t b = *(const bf16x8_t*)u;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          acc[nt][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[qb][t], b, acc[nt][qb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[qb][t], ones, lsum[qb], 0, 0, 0);
-    }
-    // normalise and scatter to original positions; lse per query
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int vv = 0; vv < 4; ++vv) {
-        const int q = 32 * w + 16 * qb + 4 * g + vv;   // query row of this output element
-        const int pos = kpos[cur * kChunk + q];
-        const float l = lsum[qb][vv];
-        const float m = __shfl(mq[qb], 4 * g + vv);
-        const float lx = __shfl(rowsum[qb], 4 * g + vv);
-        OT* orow = o + (seg * L + pos) * D;
-        if (l > 0.f) {
-          const float inv = 1.0f / l;
-#pragma unroll
-          for (int nt = 0; nt < D / 16; ++nt) store_o<OT>(orow + nt * 16 + li, acc[nt][qb][vv] * inv);
-        } else {
-          const uint16_t* vr = v_raw + (row0 + pos) * D;
-#pragma unroll
-          for (int nt = 0; nt < D / 16; ++nt)
-            store_o<OT>(orow + nt * 16 + li, __uint_as_float((uint32_t)vr[nt * 16 + li] << 16));
-        }
-        if (li == vv) lse[seg * L + pos] = l > 0.f ? (m + __log2f(lx)) * kLn2 : kSelfLogit;
-      }
-    }
-    __syncthreads();  // every wave is done with slot prv
-    if (c + 1 < c1) {
-      load_chunk<D>(lds, prv, c + 1, qk_rows, v_rows, pm, row0, sorted, srow0);
-      __syncthreads();
-    }
+    __syncthreads();
   }
 }
 

@@ -14,18 +14,42 @@
 namespace lsh {
 namespace {
 
-__device__ __forceinline__ float ld_f32(const float* p) { return *p; }
-__device__ __forceinline__ float ld_f32(const _Float16* p) { return (float)*p; }
+// 8 consecutive per-round outputs as floats
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void load8(const _Float16* p, float* x) {
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  const f16x8_t a = *(const f16x8_t*)p;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+  *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+  *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float* x) {
+  uint32_t u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    u[j] = (uint32_t)f32_to_bf16(x[2 * j]).bits | ((uint32_t)f32_to_bf16(x[2 * j + 1]).bits << 16);
+  *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
+}
 
-template <typename OutT, typename OT>
+// Each lane owns 8 consecutive dims of one row; D/8 lanes cover a row.
+template <int D, typename OutT, typename OT>
 __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
                                                  const float* __restrict__ lse,
-                                                 OutT* __restrict__ out, int L, int R, int d,
+                                                 OutT* __restrict__ out, int L, int R,
                                                  int64_t n_rows) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
-  for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-       row < n_rows; row += waves) {
+  constexpr int kLpr = D / 8;             // lanes per row
+  constexpr int kRpb = 256 / kLpr;        // rows per block
+  const int sub = threadIdx.x % kLpr;
+  const int64_t stride = (int64_t)gridDim.x * kRpb;
+  for (int64_t row = (int64_t)blockIdx.x * kRpb + threadIdx.x / kLpr; row < n_rows;
+       row += stride) {
     const int64_t bh = row / L;
     const int64_t i = row - bh * L;
     const float* lr = lse + bh * R * L + i;
@@ -34,36 +58,43 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
     float sum = 0.f;
     for (int r = 0; r < R; ++r) sum += __expf(lr[(int64_t)r * L] - mx);
     const float inv_sum = 1.0f / sum;
-    for (int u = lane; u < d; u += kWave) {
-      float acc = 0.f;
-      for (int r = 0; r < R; ++r) {
-        const float w = __expf(lr[(int64_t)r * L] - mx) * inv_sum;
-        acc += w * ld_f32(o + ((bh * R + r) * L + i) * d + u);
-      }
-      out[row * d + u] = from_f32<OutT>(acc);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < R; ++r) {
+      const float w = __expf(lr[(int64_t)r * L] - mx) * inv_sum;
+      float x[8];
+      load8(o + ((bh * R + r) * L + i) * D + sub * 8, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[j], acc[j]);
     }
+    store8(out + row * D + sub * 8, acc);
   }
 }
 
-template <typename OT>
+template <int D, typename OT>
 void launch_t(const Problem& p, const OT* o, const float* lse, void* out, hipStream_t s) {
   const int64_t n = p.n_token_heads();
-  const int64_t want = (n + 3) / 4;
-  const unsigned blocks = (unsigned)(want < 131072 ? want : 131072);
+  const int64_t rpb = 256 / (D / 8);
+  const int64_t want = (n + rpb - 1) / rpb;
+  const unsigned blocks = (unsigned)(want < 262144 ? want : 262144);
   if (p.out_dtype == LSH_ATTN_BF16)
-    hipLaunchKernelGGL((k_combine<bf16_t, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
-                       (bf16_t*)out, p.L, p.R, p.d, n);
+    hipLaunchKernelGGL((k_combine<D, bf16_t, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
+                       (bf16_t*)out, p.L, p.R, n);
   else
-    hipLaunchKernelGGL((k_combine<float, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
-                       (float*)out, p.L, p.R, p.d, n);
+    hipLaunchKernelGGL((k_combine<D, float, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
+                       (float*)out, p.L, p.R, n);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
                           void* out, hipStream_t s) {
-  if (o_half) launch_t<_Float16>(p, (const _Float16*)o, lse, out, s);
-  else launch_t<float>(p, (const float*)o, lse, out, s);
+  if (p.d == 64) {
+    if (o_half) launch_t<64, _Float16>(p, (const _Float16*)o, lse, out, s);
+    else launch_t<64, float>(p, (const float*)o, lse, out, s);
+  } else {
+    if (o_half) launch_t<128, _Float16>(p, (const _Float16*)o, lse, out, s);
+    else launch_t<128, float>(p, (const float*)o, lse, out, s);
+  }
   return hipGetLastError();
 }
 

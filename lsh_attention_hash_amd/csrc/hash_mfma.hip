@@ -43,7 +43,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 512;     // 8 waves
+constexpr int kThreads = 256;     // 4 waves, one per SIMD; each wave pipelines its own work
 constexpr int kTokWave = 64;      // 2 sets of 32 tokens per wave
 constexpr int kTokWG = kThreads / 64 * kTokWave;
 constexpr float kF16Max = 65504.0f;
@@ -57,36 +57,67 @@ __device__ __forceinline__ float f16_round(float x) {
 // upper bound of a non-negative double as float
 __device__ __forceinline__ float up_f32(double x) { return (float)(x * (1.0 + 1e-6)) + 1e-30f; }
 
-// One block of 64 threads per (round, padded column).
-__global__ __launch_bounds__(64) void k_hash_prep(const float* __restrict__ rot,
-                                                  _Float16* __restrict__ rh,
-                                                  float* __restrict__ rt,
-                                                  unsigned* __restrict__ bounds, int d, int half,
-                                                  int half_pad) {
-  const int k = blockIdx.x % (unsigned)half_pad;
-  const int r = blockIdx.x / (unsigned)half_pad;
-  const int t = threadIdx.x;
+// One block of 256 threads per (round, 32-column tile): 8 groups of 32
+// threads read R row by row (coalesced over columns), the tile is transposed
+// in LDS and written out as rows of d.
+constexpr int kPrepMaxD = 128;
+__global__ __launch_bounds__(256) void k_hash_prep(const float* __restrict__ rot,
+                                                   _Float16* __restrict__ rh,
+                                                   float* __restrict__ rt,
+                                                   unsigned* __restrict__ bounds, int d, int half,
+                                                   int half_pad) {
+  __shared__ __align__(16) _Float16 th[32][kPrepMaxD + 8];
+  __shared__ __align__(16) float tx[32][kPrepMaxD + 4];
+  __shared__ double red[3][8][33];
+  const int ntiles = half_pad / 32;
+  const int kt = blockIdx.x % (unsigned)ntiles;
+  const int r = blockIdx.x / (unsigned)ntiles;
+  const int col = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int k = kt * 32 + col;
   double sh = 0.0, slo = 0.0, sr = 0.0;
-  for (int u = t; u < d; u += 64) {
+  for (int u = grp; u < d; u += 8) {
     const float x = k < half ? rot[((int64_t)r * d + u) * half + k] : 0.f;
     const float h = f16_round(x);
-    rh[((int64_t)r * half_pad + k) * d + u] = (_Float16)h;
-    if (k < half) rt[((int64_t)r * half + k) * d + u] = x;
+    th[col][u] = (_Float16)h;
+    tx[col][u] = x;
     const double hd = h, xd = x;
     sh += hd * hd;
     slo += (xd - hd) * (xd - hd);
     sr += xd * xd;
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    sh += __shfl_xor(sh, off);
-    slo += __shfl_xor(slo, off);
-    sr += __shfl_xor(sr, off);
+  red[0][grp][col] = sh;
+  red[1][grp][col] = slo;
+  red[2][grp][col] = sr;
+  __syncthreads();
+  const int pieces_h = d / 8, pieces_x = d / 4;
+  for (int idx = threadIdx.x; idx < 32 * pieces_h; idx += 256) {
+    const int row = idx / pieces_h, c = idx % pieces_h;
+    *(uint4*)(rh + ((int64_t)r * half_pad + kt * 32 + row) * d + c * 8) = *(const uint4*)&th[row][c * 8];
   }
-  if (t == 0) {
-    // non-negative floats order like their bit patterns
-    atomicMax(bounds + r * 4 + 0, __float_as_uint(up_f32(sqrt(sh))));
-    atomicMax(bounds + r * 4 + 1, __float_as_uint(up_f32(sqrt(slo))));
-    atomicMax(bounds + r * 4 + 2, __float_as_uint(up_f32(sqrt(sr))));
+  for (int idx = threadIdx.x; idx < 32 * pieces_x; idx += 256) {
+    const int row = idx / pieces_x, c = idx % pieces_x;
+    if (kt * 32 + row < half)
+      *(uint4*)(rt + ((int64_t)r * half + kt * 32 + row) * d + c * 4) = *(const uint4*)&tx[row][c * 4];
+  }
+  if (grp == 0) {
+    double a = 0.0, b = 0.0, c = 0.0;
+    for (int g2 = 0; g2 < 8; ++g2) {
+      a += red[0][g2][col];
+      b += red[1][g2][col];
+      c += red[2][g2][col];
+    }
+    float fa = up_f32(sqrt(a)), fb = up_f32(sqrt(b)), fc = up_f32(sqrt(c));
+    for (int off = 16; off > 0; off >>= 1) {
+      fa = fmaxf(fa, __shfl_xor(fa, off));
+      fb = fmaxf(fb, __shfl_xor(fb, off));
+      fc = fmaxf(fc, __shfl_xor(fc, off));
+    }
+    if (col == 0) {
+      // non-negative floats order like their bit patterns
+      atomicMax(bounds + r * 4 + 0, __float_as_uint(fa));
+      atomicMax(bounds + r * 4 + 1, __float_as_uint(fb));
+      atomicMax(bounds + r * 4 + 2, __float_as_uint(fc));
+    }
   }
 }
 
@@ -94,11 +125,15 @@ __global__ void k_zero_u32(unsigned* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
-// keep the three largest of (t1 >= t2 >= t3) and key
-__device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, uint32_t key) {
-  const uint32_t n1 = max(t1, key);
-  const uint32_t n2 = max(t2, min(t1, key));  // median of (t1, t2, key), t1 >= t2
-  const uint32_t n3 = max(t3, min(t2, key));
+// Keep the three largest of (t1 >= t2 >= t3) and key. Keys have a clear sign
+// bit and finite magnitude bits, so as floats they order exactly like their
+// bit patterns, and v_max_f32 / v_med3_f32 return one of their inputs; keys
+// below 2^-126 (rows whose projections are all ~0) may be flushed, and such
+// rows are never certified (their top value is ~0).
+__device__ __forceinline__ void top3(float& t1, float& t2, float& t3, float key) {
+  const float n1 = fmaxf(t1, key);
+  const float n2 = __builtin_amdgcn_fmed3f(t1, t2, key);
+  const float n3 = __builtin_amdgcn_fmed3f(t2, t3, key);
   t1 = n1;
   t2 = n2;
   t3 = n3;
@@ -108,12 +143,19 @@ struct QA {  // two-candidate re-score
   uint32_t row_lo, row_hi, k1, k2;
 };
 
+// Persistent: workgroup w serves round r and token tiles j = grp, grp + G/R, ...
+// (tiles of kTokWG consecutive token-heads). Its rotation R_r stays in LDS for
+// the whole walk. w -> (xcd = w % 8, k = w / 8, r = k % R, grp = xcd + 8 (k / R)):
+// the R workgroups that read the same token tile differ only in r and run on
+// the same XCD, so the tile is fetched from HBM once and the other rounds find
+// it in that XCD's L2.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const uint16_t* __restrict__ qk, const _Float16* __restrict__ rh,
     const unsigned* __restrict__ bounds_u, uint16_t* __restrict__ buckets,
     int32_t* __restrict__ buckets_out, QA* __restrict__ qa, uint2* __restrict__ qb,
-    unsigned* __restrict__ qcount, int64_t N, int L, int R, int half, int half_pad, int ib) {
+    unsigned* __restrict__ qcount, int64_t N, int L, int R, int half, int half_pad, int ib,
+    int n_tok_tiles) {
   constexpr int KS = D / 16;           // K-steps of 16
   constexpr int ROWB = 2 * D + 16;     // LDS bytes per rotation column
   extern __shared__ __align__(16) unsigned char lds[];
@@ -121,88 +163,124 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   const int w = threadIdx.x >> 6;
   const int hf = lane >> 5;            // which half of the dims this lane feeds
   const int tl = lane & 31;            // token within a set
-  const int64_t tok0 = (int64_t)blockIdx.x * kTokWG + w * kTokWave;
   const uint32_t imask = (1u << ib) - 1u;
   const uint32_t vmask = 0x7FFFFFFFu & ~imask;
   const float gamma = (float)(D + 2) * 1.1920928955078125e-07f;
 
-  // x in fp16 as the B operand: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
-  // of token tl, K-step ks covering dims hf*D/2 + 8ks + 0..7 (the K order of
-  // both operands is permuted the same way, which leaves the product as is)
-  f16x8_t bx[2][KS];
-  float nx[2], nres[2];
+  const int xcd = blockIdx.x & 7;
+  const int kk = blockIdx.x >> 3;
+  const int r = kk % R;
+  const int grp = xcd + 8 * (kk / R);
+  const int ngrp = gridDim.x / R;      // gridDim.x is a multiple of 8 R
+
+  // rotation of round r -> LDS, 8 loads in flight per thread
+  {
+    const uint4* g = (const uint4*)(rh + (int64_t)r * half_pad * D);
+    const int total = half_pad * (D / 8);
+    for (int base = threadIdx.x; base < total; base += kThreads * 8) {
+      uint4 tmp[8];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int64_t n = tok0 + s * 32 + tl;
-    const bool valid = n < N;
-    const uint4* src = (const uint4*)(qk + (valid ? n : 0) * D) + hf * KS;
-    float a = 0.f, b = 0.f;
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * kThreads;
+        tmp[u] = g[idx < total ? idx : 0];
+      }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 raw = valid ? src[ks] : make_uint4(0, 0, 0, 0);
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = __uint_as_float(wv[j] << 16), x1 = __uint_as_float(wv[j] & 0xFFFF0000u);
-        const float h0 = f16_round(x0), h1 = f16_round(x1);
-        bx[s][ks][2 * j] = (_Float16)h0;
-        bx[s][ks][2 * j + 1] = (_Float16)h1;
-        a = fmaf(h0, h0, fmaf(h1, h1, a));
-        b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
+      for (int u = 0; u < 8; ++u) {
+        const int idx = base + u * kThreads;
+        if (idx < total) *(uint4*)(lds + (idx / (D / 8)) * ROWB + (idx % (D / 8)) * 16) = tmp[u];
       }
     }
-    a += __shfl_xor(a, 32);
-    b += __shfl_xor(b, 32);
-    nx[s] = sqrtf(a) * (1.0f + 1e-5f);
-    nres[s] = sqrtf(b) * (1.0f + 1e-5f);
   }
-
+  __syncthreads();
+  const float rh_max = __uint_as_float(bounds_u[r * 4 + 0]);
+  const float lo_max = __uint_as_float(bounds_u[r * 4 + 1]);
+  const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
   const int ntiles = half_pad / 32;
-  for (int r = 0; r < R; ++r) {
-    __syncthreads();
-    {
-      const uint4* g = (const uint4*)(rh + (int64_t)r * half_pad * D);
-      for (int idx = threadIdx.x; idx < half_pad * (D / 8); idx += kThreads) {
-        const int row = idx / (D / 8), c = idx % (D / 8);
-        *(uint4*)(lds + row * ROWB + c * 16) = g[idx];
-      }
-    }
-    __syncthreads();
-    const float rh_max = __uint_as_float(bounds_u[r * 4 + 0]);
-    const float lo_max = __uint_as_float(bounds_u[r * 4 + 1]);
-    const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
 
-    uint32_t t1[2] = {0u, 0u}, t2[2] = {0u, 0u}, t3[2] = {0u, 0u};
-    for (int kt = 0; kt < ntiles; ++kt) {
-      floatx16_t acc[2];
+  // raw bf16 x of a token tile: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
+  // of token tl of each set; the next tile is loaded while this one runs
+  uint4 raw[2][KS];
+  auto fetch = [&](int j) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+      const int64_t n = (int64_t)j * kTokWG + w * kTokWave + s * 32 + tl;
+      const uint4* src = (const uint4*)(qk + (n < N ? n : 0) * D) + hf * KS;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[s][v] = 0.f;
-      const unsigned char* arow = lds + (kt * 32 + tl) * ROWB + hf * D;
+      for (int ks = 0; ks < KS; ++ks) raw[s][ks] = n < N ? src[ks] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (grp < n_tok_tiles) fetch(grp);
+  for (int j = grp; j < n_tok_tiles; j += ngrp) {
+    const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
+    // x in fp16 as the B operand, K-step ks covering dims hf*D/2 + 8ks + 0..7
+    // (the K order of both operands is permuted the same way, which leaves
+    // the product as is)
+    f16x8_t bx[2][KS];
+    float nx[2], nres[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float a = 0.f, b = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const f16x8_t a = *(const f16x8_t*)(arow + ks * 16);
+        const uint32_t wv[4] = {raw[s][ks].x, raw[s][ks].y, raw[s][ks].z, raw[s][ks].w};
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bx[s][ks], acc[s], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
+          const float h0 = f16_round(x0), h1 = f16_round(x1);
+          bx[s][ks][2 * q] = (_Float16)h0;
+          bx[s][ks][2 * q + 1] = (_Float16)h1;
+          a = fmaf(h0, h0, fmaf(h1, h1, a));
+          b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
+        }
       }
-      // C layout: lane holds token tl and columns kt*32 + 8(v/4) + 4 hf + v%4
+      a += __shfl_xor(a, 32);
+      b += __shfl_xor(b, 32);
+      nx[s] = sqrtf(a) * (1.0f + 1e-5f);
+      nres[s] = sqrtf(b) * (1.0f + 1e-5f);
+    }
+    if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
+
+    float t1[2] = {0.f, 0.f}, t2[2] = {0.f, 0.f}, t3[2] = {0.f, 0.f};
+    // Set 0's keys are folded while set 1's MFMAs run and the other way
+    // round, so the matrix cores and the vector ALU work at the same time.
+    floatx16_t acc[2];
+    f16x8_t at[KS];  // the rotation tile, shared by both sets
+    auto load_tile = [&](int kt) {
+      const unsigned char* arow = lds + (kt * 32 + tl) * ROWB + hf * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) at[ks] = *(const f16x8_t*)(arow + ks * 16);
+    };
+    auto set_mfma = [&](int s) {
+      const floatx16_t zero = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(at[ks], bx[s][ks], ks == 0 ? zero : acc[s],
+                                                         0, 0, 0);
+    };
+    // C layout: lane holds token tl and columns kt*32 + 8(v/4) + 4 hf + v%4
+    auto fold = [&](int kt, int s) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const uint32_t k = (uint32_t)(kt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3));
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint32_t key = (__float_as_uint(acc[s][v]) & vmask) | k;
-          top3(t1[s], t2[s], t3[s], key);
-        }
+        const float key = __uint_as_float((__float_as_uint(acc[s][v]) & vmask) | k);
+        top3(t1[s], t2[s], t3[s], key);
       }
+    };
+    load_tile(0);
+    set_mfma(0);
+    set_mfma(1);
+    for (int kt = 0; kt < ntiles; ++kt) {
+      if (kt + 1 < ntiles) load_tile(kt + 1);
+      fold(kt, 0);
+      if (kt + 1 < ntiles) set_mfma(0);
+      fold(kt, 1);
+      if (kt + 1 < ntiles) set_mfma(1);
     }
     // merge the two lane halves (same tokens, other columns)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32),
-                     o3 = __shfl_xor(t3[s], 32);
+      const float o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32),
+                  o3 = __shfl_xor(t3[s], 32);
       top3(t1[s], t2[s], t3[s], o1);
       top3(t1[s], t2[s], t3[s], o2);
       top3(t1[s], t2[s], t3[s], o3);
@@ -211,16 +289,16 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     float part[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t k1 = t1[s] & imask;
+      const uint32_t k1 = __float_as_uint(t1[s]) & imask;
       const unsigned char* row = lds + k1 * ROWB + hf * D;
       float acc = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const f16x8_t a = *(const f16x8_t*)(row + ks * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x2_t pa = {a[2 * j], a[2 * j + 1]};
-          const f16x2_t pb = {bx[s][ks][2 * j], bx[s][ks][2 * j + 1]};
+        for (int q = 0; q < 4; ++q) {
+          const f16x2_t pa = {a[2 * q], a[2 * q + 1]};
+          const f16x2_t pb = {bx[s][ks][2 * q], bx[s][ks][2 * q + 1]};
           acc = __builtin_amdgcn_fdot2(pa, pb, acc, false);
         }
       }
@@ -231,12 +309,11 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const float recv = __shfl_xor(send, 32);
     const float pk1 = (hf ? part[1] : part[0]) + recv;
 
-    const int s = hf;
-    const int64_t n = tok0 + s * 32 + tl;
+    const int64_t n = tok0 + hf * 32 + tl;
     if (n < N) {
-      const uint32_t a1 = hf ? t1[1] : t1[0];
-      const uint32_t a2 = hf ? t2[1] : t2[0];
-      const uint32_t a3 = hf ? t3[1] : t3[0];
+      const uint32_t a1 = __float_as_uint(hf ? t1[1] : t1[0]);
+      const uint32_t a2 = __float_as_uint(hf ? t2[1] : t2[0]);
+      const uint32_t a3 = __float_as_uint(hf ? t3[1] : t3[0]);
       const float d1 = __uint_as_float(a1 & vmask);
       const float d2 = __uint_as_float(a2 & vmask);
       const float d3 = __uint_as_float(a3 & vmask);
@@ -270,63 +347,108 @@ __device__ __forceinline__ void take_better(double& v, int& k, double ov, int ok
   }
 }
 
-// fp64 projection of row x on column k, t = 0..d-1 in order
-template <typename T>
-__device__ __forceinline__ double proj64(const T* x, const float* rtk, int d) {
-  double p = 0.0;
-  for (int t = 0; t < d; ++t) p += (double)to_f32(x[t]) * (double)rtk[t];
-  return p;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_hash_fallback(const T* __restrict__ qk,
+// Queue A: per block iteration 64 entries are staged in LDS (their x rows and
+// both candidate columns, coalesced 16-byte loads); then thread 2e + c sums
+// candidate c of entry e in fp64, t = 0..d-1 in order, and the pair compares.
+// Queue B: one wave per entry, lanes over columns (rare).
+constexpr int kQaBatch = 64;
+template <int D>
+__global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restrict__ qk,
                                                        const float* __restrict__ rt,
                                                        const QA* __restrict__ qa,
                                                        const uint2* __restrict__ qb,
                                                        const unsigned* __restrict__ qcount,
                                                        uint16_t* __restrict__ buckets,
                                                        int32_t* __restrict__ buckets_out, int L,
-                                                       int d, int half, int R) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
-  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
-  // queue A: 32 entries per wave, one lane per candidate
+                                                       int half, int R) {
+  constexpr int XROW = D + 2;      // bf16 elements per staged x row (pad: bank spread)
+  constexpr int CROW = D + 1;      // floats per staged column
+  __shared__ __align__(16) uint16_t xs[kQaBatch][XROW];
+  __shared__ __align__(16) float cs[2 * kQaBatch][CROW];
+  __shared__ int64_t rows[kQaBatch];
+  __shared__ int kk[2 * kQaBatch];
+  const int tid = threadIdx.x;
   const int64_t na = qcount[0];
-  for (int64_t e0 = wave * 32; e0 < na; e0 += waves * 32) {
-    const int64_t e = e0 + lane / 2;
-    double best = -DBL_MAX;
-    int bidx = INT_MAX;
-    int64_t row = 0;
-    if (e < na) {
-      const QA q = qa[e];
-      row = (int64_t)q.row_lo | ((int64_t)q.row_hi << 32);
-      const int k = (lane & 1) ? (int)q.k2 : (int)q.k1;
-      const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
-      const int r = (int)(seg - bh * R);
-      const double p = proj64(qk + (bh * L + i) * d, rt + ((int64_t)r * half + k) * d, d);
-      take_better(best, bidx, p, k);
-      take_better(best, bidx, -p, k + half);
+  for (int64_t e0 = (int64_t)blockIdx.x * kQaBatch; e0 < na; e0 += (int64_t)gridDim.x * kQaBatch) {
+    const int n_here = (int)(na - e0 < kQaBatch ? na - e0 : kQaBatch);
+    if (tid < kQaBatch) {
+      int64_t row = -1;
+      int k1 = 0, k2 = 0;
+      if (tid < n_here) {
+        const QA q = qa[e0 + tid];
+        row = (int64_t)q.row_lo | ((int64_t)q.row_hi << 32);
+        k1 = (int)q.k1;
+        k2 = (int)q.k2;
+      }
+      rows[tid] = row;
+      kk[2 * tid] = k1;
+      kk[2 * tid + 1] = k2;
     }
-    const double ob = __shfl_xor(best, 1);
-    const int ok = __shfl_xor(bidx, 1);
-    take_better(best, bidx, ob, ok);
-    if (e < na && (lane & 1) == 0) {
-      buckets[row] = (uint16_t)bidx;
-      if (buckets_out) buckets_out[row] = bidx;
+    __syncthreads();
+    // x rows: D/8 pieces of 8 bf16 each (4 bytes per pair of elements)
+    for (int idx = tid; idx < kQaBatch * (D / 8); idx += 256) {
+      const int e = idx / (D / 8), c = idx % (D / 8);
+      const int64_t row = rows[e];
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row >= 0) {
+        const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
+        v = *(const uint4*)(qk + (bh * L + i) * D + c * 8);
+      }
+      uint32_t* dst = (uint32_t*)&xs[e][c * 8];
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
     }
+    // candidate columns: D/4 pieces of 4 floats
+    for (int idx = tid; idx < 2 * kQaBatch * (D / 4); idx += 256) {
+      const int j = idx / (D / 4), c = idx % (D / 4);
+      const int64_t row = rows[j / 2];
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row >= 0) {
+        const int64_t seg = row / L, bh = seg / R;
+        const int r = (int)(seg - bh * R);
+        v = *(const float4*)(rt + ((int64_t)r * half + kk[j]) * D + c * 4);
+      }
+      cs[j][c * 4 + 0] = v.x; cs[j][c * 4 + 1] = v.y; cs[j][c * 4 + 2] = v.z; cs[j][c * 4 + 3] = v.w;
+    }
+    __syncthreads();
+    if (tid < 2 * kQaBatch) {
+      const int e = tid >> 1;
+      double best = -DBL_MAX;
+      int bidx = INT_MAX;
+      if (rows[e] >= 0) {
+        double p = 0.0;
+        for (int t = 0; t < D; ++t)
+          p += (double)__uint_as_float((uint32_t)xs[e][t] << 16) * (double)cs[tid][t];
+        const int k = kk[tid];
+        take_better(best, bidx, p, k);
+        take_better(best, bidx, -p, k + half);
+      }
+      const double ob = __shfl_xor(best, 1);
+      const int ok = __shfl_xor(bidx, 1);
+      take_better(best, bidx, ob, ok);
+      if (rows[e] >= 0 && (tid & 1) == 0) {
+        buckets[rows[e]] = (uint16_t)bidx;
+        if (buckets_out) buckets_out[rows[e]] = bidx;
+      }
+    }
+    __syncthreads();
   }
-  // queue B: one wave per entry, lanes over columns
+  // queue B
+  const int lane = tid & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + tid / 64;
+  const int64_t waves = (int64_t)gridDim.x * 4;
   const int64_t nb_ = qcount[1];
   for (int64_t e = wave; e < nb_; e += waves) {
     const uint2 q = qb[e];
     const int64_t row = (int64_t)q.x | ((int64_t)q.y << 32);
     const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
     const int r = (int)(seg - bh * R);
-    const T* x = qk + (bh * L + i) * d;
+    const uint16_t* x = qk + (bh * L + i) * D;
     double best = -DBL_MAX;
     int bidx = INT_MAX;
     for (int k = lane; k < half; k += 64) {
-      const double p = proj64(x, rt + ((int64_t)r * half + k) * d, d);
+      const float* col = rt + ((int64_t)r * half + k) * D;
+      double p = 0.0;
+      for (int t = 0; t < D; ++t) p += (double)__uint_as_float((uint32_t)x[t] << 16) * (double)col[t];
       take_better(best, bidx, p, k);
       take_better(best, bidx, -p, k + half);
     }
@@ -379,34 +501,44 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, hs.bounds, 4 * p.R + 2);
   unsigned* qcount = hs.bounds + 4 * p.R;
-  hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * hp)), dim3(64), 0, s, rot, hs.rh, hs.rt,
-                     hs.bounds, p.d, half, hp);
+  hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * (hp / 32))), dim3(256), 0, s, rot, hs.rh,
+                     hs.rt, hs.bounds, p.d, half, hp);
   const int64_t N = p.n_token_heads();
-  const unsigned grid = (unsigned)((N + kTokWG - 1) / kTokWG);
-  if (p.d == 128) {
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute((const void*)k_hash_mfma<128>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-      attr = true;
-    }
-    hipLaunchKernelGGL(k_hash_mfma<128>, dim3(grid), dim3(kThreads), lds_bytes<128>(hp), s,
-                       (const uint16_t*)qk, hs.rh, hs.bounds, buckets, buckets_out,
-                       (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib);
-  } else {
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute((const void*)k_hash_mfma<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          150 * 1024);
-      attr = true;
-    }
-    hipLaunchKernelGGL(k_hash_mfma<64>, dim3(grid), dim3(kThreads), lds_bytes<64>(hp), s,
-                       (const uint16_t*)qk, hs.rh, hs.bounds, buckets, buckets_out,
-                       (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib);
+  const int n_tok_tiles = (int)((N + kTokWG - 1) / kTokWG);
+  // persistent grid: as many resident workgroups as fit, a multiple of 8 R
+  const int lds = p.d == 128 ? lds_bytes<128>(hp) : lds_bytes<64>(hp);
+  const void* fn = p.d == 128 ? (const void*)k_hash_mfma<128> : (const void*)k_hash_mfma<64>;
+  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+  int per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess ||
+      per_cu < 1) {
+    (void)hipGetLastError();
+    per_cu = 1;
   }
-  hipLaunchKernelGGL(k_hash_fallback<bf16_t>, dim3(1024), dim3(256), 0, s, (const bf16_t*)qk,
-                     hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
-                     buckets_out, p.L, p.d, half, p.R);
+  const int unit = 8 * p.R;
+  int64_t grid = (int64_t)hs.n_cu * per_cu;
+  grid = (grid / unit) * unit;
+  if (grid < unit) grid = unit;
+  const int64_t max_grid = (int64_t)unit * ((n_tok_tiles + 7) / 8);
+  if (grid > max_grid) grid = max_grid;
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_hash_mfma<128>, dim3((unsigned)grid), dim3(kThreads), lds, s,
+                       (const uint16_t*)qk, hs.rh, hs.bounds, buckets, buckets_out,
+                       (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
+                       n_tok_tiles);
+  else
+    hipLaunchKernelGGL(k_hash_mfma<64>, dim3((unsigned)grid), dim3(kThreads), lds, s,
+                       (const uint16_t*)qk, hs.rh, hs.bounds, buckets, buckets_out,
+                       (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
+                       n_tok_tiles);
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_hash_fallback<128>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
+                       hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
+                       buckets_out, p.L, half, p.R);
+  else
+    hipLaunchKernelGGL(k_hash_fallback<64>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
+                       hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
+                       buckets_out, p.L, half, p.R);
   hipLaunchKernelGGL(k_hash_stats, dim3(1), dim3(64), 0, s, qcount, stats);
   return hipGetLastError();
 }

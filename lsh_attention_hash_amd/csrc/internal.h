@@ -35,6 +35,7 @@ struct HashScratch {
   unsigned* bounds = nullptr; // [R][4] norm bounds (float bits), then 2 queue counters
   void* queue_a = nullptr;    // [R * N] two-candidate re-score entries (16 B)
   void* queue_b = nullptr;    // [R * N] all-column re-score entries (8 B)
+  int n_cu = 0;               // compute units of the handle's device
 };
 
 // Device workspace owned by a handle. Per-round arrays are [seg, L(, d)] with
@@ -45,7 +46,7 @@ struct Workspace {
   void* o = nullptr;               // [seg, L, d] per-round outputs at original positions
                                    // (fp16, or fp32 with the fp32 flag / plain kernel)
   float* lse = nullptr;            // [seg, L]
-  uint32_t* sort_counts = nullptr; // [seg, nb, tiles] counts, then exclusive offsets
+  uint32_t* sort_counts = nullptr; // [seg, tiles, nb] counts, then first output slots
   void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
   void* v_sorted = nullptr;        // [seg, L, d]
   unsigned long long* stats = nullptr;  // [2] exact rescored, full fallback

@@ -113,6 +113,12 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
             alloc(&w.stats, 2 * 8, t);
   if (ok && lsh::hash_mfma_supported(p)) {
     const int64_t hp = lsh::hash_half_pad(p);
+    if (hipDeviceGetAttribute(&w.hash.n_cu, hipDeviceAttributeMultiprocessorCount, h->device) !=
+            hipSuccess ||
+        w.hash.n_cu < 1) {
+      (void)hipGetLastError();
+      w.hash.n_cu = 1;
+    }
     ok = alloc(&w.hash.rh, (int64_t)p.R * hp * p.d * 2, t) &&
          alloc(&w.hash.rt, (int64_t)p.R * p.half() * p.d * 4, t) &&
          alloc(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4, t) &&

@@ -7,14 +7,15 @@
 // the position bits is needed.
 //
 // Three phases over tiles of kSortTile positions (one wave per tile):
-//   count:   counts[seg][b][tile] = how many positions of the tile are in b;
-//   scan:    exclusive prefix over the bucket-major [b][tile] array, giving
-//            the first output slot of each (bucket, tile);
-//   scatter: every position gets slot = offset[b][tile] + (number of earlier
-//            positions of the same tile in b), computed with wave ballots
-//            over the bucket bits (lanes holding equal ids find each other).
-// Buckets are handled in LDS windows of kLdsBins ids, so any n_buckets up to
-// 65536 works with a fixed LDS footprint.
+//   count:   counts[seg][tile][b] = how many positions of the tile are in b;
+//   scan:    offsets[seg][tile][b] = sum of all counts of buckets < b plus the
+//            counts of bucket b in earlier tiles: the first output slot of the
+//            tile's positions in bucket b;
+//   scatter: every position gets slot = offset + (number of earlier positions
+//            of the same tile in b), computed with wave ballots over the
+//            bucket bits (lanes holding equal ids find each other).
+// Buckets are handled in LDS windows of at most kLdsBins ids, so any
+// n_buckets up to 65536 works with a bounded LDS footprint.
 #include "internal.h"
 
 namespace lsh {
@@ -36,16 +37,17 @@ __device__ __forceinline__ uint64_t match_peers(uint32_t key, bool active, int n
 __global__ __launch_bounds__(64) void k_sort_count(const uint16_t* __restrict__ buckets,
                                                    uint32_t* __restrict__ counts, int L, int nb,
                                                    int tiles, int nbits) {
-  __shared__ uint32_t cnt[kLdsBins];
+  extern __shared__ uint32_t cnt[];
   const int tile = (int)(blockIdx.x % (unsigned)tiles);
   const int64_t seg = blockIdx.x / (unsigned)tiles;
   const int lane = threadIdx.x;
   const uint16_t* bk = buckets + seg * L;
-  uint32_t* cs = counts + seg * (int64_t)nb * tiles;
+  uint32_t* cs = counts + (seg * tiles + tile) * (int64_t)nb;
   const int begin = tile * kSortTile;
   const int end = min(L, begin + kSortTile);
-  for (int base = 0; base < nb; base += kLdsBins) {
-    const int span = min(kLdsBins, nb - base);
+  const int window = min(nb, kLdsBins);
+  for (int base = 0; base < nb; base += window) {
+    const int span = min(window, nb - base);
     for (int b = lane; b < span; b += kWave) cnt[b] = 0;
     __syncthreads();
     for (int e0 = begin; e0 < end; e0 += kWave) {
@@ -56,34 +58,45 @@ __global__ __launch_bounds__(64) void k_sort_count(const uint16_t* __restrict__ 
       if (in && lane == __builtin_ctzll(peers)) cnt[b - base] += (uint32_t)__popcll(peers);
     }
     __syncthreads();
-    for (int b = lane; b < span; b += kWave) cs[(int64_t)(base + b) * tiles + tile] = cnt[b];
+    for (int b = lane; b < span; b += kWave) cs[base + b] = cnt[b];
     __syncthreads();
   }
 }
 
-// One block per segment: exclusive prefix sum of n counts, in place.
-__global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ counts, int64_t n) {
+// One block per segment. Buckets are taken 1024 at a time, one per thread:
+// first the running count over tiles (the tile's offset inside its bucket),
+// then a block-wide exclusive scan of the bucket totals gives the bucket's
+// first slot, which is added to every tile of the bucket.
+__global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ counts, int nb,
+                                                    int tiles) {
   __shared__ uint32_t part[1024];
   const int tid = threadIdx.x;
-  uint32_t* c = counts + (int64_t)blockIdx.x * n;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t b0 = tid * per;
-  const int64_t b1 = b0 + per < n ? b0 + per : n;
-  uint32_t sum = 0;
-  for (int64_t k = b0; k < b1; ++k) sum += c[k];
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t add = tid >= off ? part[tid - off] : 0u;
+  uint32_t* c = counts + (int64_t)blockIdx.x * nb * tiles;
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < nb; b0 += 1024) {
+    const int b = b0 + tid;
+    uint32_t run = 0;
+    if (b < nb) {
+      for (int t = 0; t < tiles; ++t) {
+        uint32_t* p = c + (int64_t)t * nb + b;
+        const uint32_t x = *p;
+        *p = run;
+        run += x;
+      }
+    }
+    part[tid] = run;
     __syncthreads();
-    part[tid] += add;
+    for (int off = 1; off < 1024; off <<= 1) {
+      const uint32_t add = tid >= off ? part[tid - off] : 0u;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    const uint32_t base = carry + part[tid] - run;  // exclusive
+    if (b < nb)
+      for (int t = 0; t < tiles; ++t) c[(int64_t)t * nb + b] += base;
+    carry += part[1023];
     __syncthreads();
-  }
-  uint32_t run = tid ? part[tid - 1] : 0u;
-  for (int64_t k = b0; k < b1; ++k) {
-    const uint32_t x = c[k];
-    c[k] = run;
-    run += x;
   }
 }
 
@@ -91,19 +104,20 @@ __global__ __launch_bounds__(64) void k_sort_scatter(const uint16_t* __restrict_
                                                      const uint32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm, int L, int nb,
                                                      int tiles, int nbits) {
-  __shared__ uint32_t next[kLdsBins];
+  extern __shared__ uint32_t next[];
   const int tile = (int)(blockIdx.x % (unsigned)tiles);
   const int64_t seg = blockIdx.x / (unsigned)tiles;
   const int lane = threadIdx.x;
   const uint16_t* bk = buckets + seg * L;
-  const uint32_t* os = offsets + seg * (int64_t)nb * tiles;
+  const uint32_t* os = offsets + (seg * tiles + tile) * (int64_t)nb;
   int32_t* pm = perm + seg * L;
   const int begin = tile * kSortTile;
   const int end = min(L, begin + kSortTile);
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int base = 0; base < nb; base += kLdsBins) {
-    const int span = min(kLdsBins, nb - base);
-    for (int b = lane; b < span; b += kWave) next[b] = os[(int64_t)(base + b) * tiles + tile];
+  const int window = min(nb, kLdsBins);
+  for (int base = 0; base < nb; base += window) {
+    const int span = min(window, nb - base);
+    for (int b = lane; b < span; b += kWave) next[b] = os[base + b];
     __syncthreads();
     for (int e0 = begin; e0 < end; e0 += kWave) {
       const int e = e0 + lane;
@@ -129,12 +143,13 @@ hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* coun
   int nbits = 0;
   while ((1 << nbits) < p.nb) ++nbits;
   const dim3 grid((unsigned)(tiles * p.nseg()));
-  hipLaunchKernelGGL(k_sort_count, grid, dim3(kWave), 0, s, buckets, counts, p.L, p.nb, tiles,
+  const size_t lds = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins) * 4;
+  hipLaunchKernelGGL(k_sort_count, grid, dim3(kWave), lds, s, buckets, counts, p.L, p.nb, tiles,
                      nbits);
-  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)p.nseg()), dim3(1024), 0, s, counts,
-                     (int64_t)p.nb * tiles);
-  hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kWave), 0, s, buckets, counts, perm, p.L, p.nb,
-                     tiles, nbits);
+  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)p.nseg()), dim3(1024), 0, s, counts, p.nb,
+                     tiles);
+  hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kWave), lds, s, buckets, counts, perm, p.L,
+                     p.nb, tiles, nbits);
   return hipGetLastError();
 }
 
