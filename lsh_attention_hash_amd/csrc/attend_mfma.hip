@@ -23,7 +23,8 @@
 //   S^T[key, query] = K Q^T over the 128-key window (64 for chunk 0), 4
 //   blocks of 32 keys; lane l holds query l%32 and keys
 //   32kb + 8(v/4) + 4(l/32) + v%4, v = 0..15, of every block.
-// Softmax in log2 units, p = exp2(s * scale_key - m_query). The shift m is the
+// Softmax in log2 units, p = exp2(s * scale_key - m_query), masked keys
+// entering exp2 as -inf (no branches). The shift m is the
 // Cauchy-Schwarz bound |q| log2(e)/sqrt(d) >= every logit of the query (keys are
 // unit vectors), so no max pass is needed; if a bound exceeds 60 (a query norm
 // far outside the usual range) the wave takes the true row max instead, so
@@ -65,10 +66,6 @@ struct Lds {
   static constexpr int kBound = kPos + 2 * kChunk * 4;
   static constexpr int kBytes = kBound + 2 * kChunk * 4;
 };
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo).bits | ((uint32_t)f32_to_bf16(hi).bits << 16);
-}
 
 // 4 consecutive outputs
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
@@ -113,10 +110,11 @@ __device__ __forceinline__ void fetch_perm(PermRegs<D>& pr, int c, const int32_t
   }
 }
 
-template <int D>
+template <int D, bool SORTED>
 __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& pr, int c,
                                            const uint4* qk_rows, const uint4* v_rows,
-                                           int64_t row0, bool sorted, int64_t sorted_row0) {
+                                           int64_t row0, int64_t sorted_row0) {
+  constexpr bool sorted = SORTED;
   using CR = ChunkRegs<D>;
   const int t = threadIdx.x;
   {
@@ -188,7 +186,7 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
   }
 }
 
-template <int D, typename OT, bool CAUSAL>
+template <int D, typename OT, bool CAUSAL, bool SORTED>
 __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
     const uint4* __restrict__ v_s, const uint16_t* __restrict__ v_raw,
@@ -208,9 +206,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   const int32_t* pm = perm + seg * L;
   const int64_t row0 = bh * L;           // first row of this (b, h) in qk / v
   const int64_t srow0 = seg * L;         // first row of this segment in the sorted copies
-  const bool sorted = qk_s != nullptr;
-  const uint4* qk_rows = sorted ? qk_s : qk;
-  const uint4* v_rows = sorted ? v_s : v;
+  const uint4* qk_rows = SORTED ? qk_s : qk;
+  const uint4* v_rows = SORTED ? v_s : v;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -221,15 +218,15 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   PermRegs<D> pr;
   if (c0 > 0) {
     fetch_perm<D>(pr, c0 - 1, pm);
-    fetch_rows<D>(cr, pr, c0 - 1, qk_rows, v_rows, row0, sorted, srow0);
+    fetch_rows<D, SORTED>(cr, pr, c0 - 1, qk_rows, v_rows, row0, srow0);
     stage_chunk<D>(lds, (c0 - 1) & 1, cr);
   }
   fetch_perm<D>(pr, c0, pm);
-  fetch_rows<D>(cr, pr, c0, qk_rows, v_rows, row0, sorted, srow0);
+  fetch_rows<D, SORTED>(cr, pr, c0, qk_rows, v_rows, row0, srow0);
   stage_chunk<D>(lds, c0 & 1, cr);
   if (c0 + 1 < c1) {
     fetch_perm<D>(pr, c0 + 1, pm);
-    fetch_rows<D>(cr, pr, c0 + 1, qk_rows, v_rows, row0, sorted, srow0);
+    fetch_rows<D, SORTED>(cr, pr, c0 + 1, qk_rows, v_rows, row0, srow0);
   }
   if (c0 + 2 < c1) fetch_perm<D>(pr, c0 + 2, pm);
   __syncthreads();
@@ -267,12 +264,12 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // key kb*32 + 8(v/4) + 4h + v%4 is masked: absent (chunk 0 has no previous
-    // chunk), the query itself, or (causal) a later original position
-    auto masked = [&](int kb, int v, int kp) -> bool {
-      if (kb < kb0) return true;
-      const bool self = (kb == 2 + w) && (8 * (v >> 2) + 4 * h + (v & 3) == lq);
-      return self || (CAUSAL && kp > posq);
+    // A key is masked when it is absent (chunk 0 has no previous chunk), the
+    // query itself, or (causal) at a later original position. Positions are
+    // unique within a segment, so "itself" is pos_j == pos_q and the causal
+    // and self masks together are pos_j >= pos_q.
+    auto masked = [&](bool absent, int kp) -> bool {
+      return absent || (CAUSAL ? kp >= posq : kp == posq);
     };
     const bool slow = __ballot(mq > kBoundLimit) != 0ull;
     if (slow) {
@@ -280,6 +277,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int sl = kb < 2 ? prv : cur;
+        const bool absent = kb < kb0;
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const int key = (kb & 1) * 32 + 8 * a4 + 4 * h;
@@ -288,8 +286,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
           const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
           const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (!masked(kb, 4 * a4 + b, kpv[b])) mx = fmaxf(mx, sacc[kb][4 * a4 + b] * scv[b]);
+          for (int b = 0; b < 4; ++b) {
+            const float x = sacc[kb][4 * a4 + b] * scv[b];
+            mx = fmaxf(mx, masked(absent, kpv[b]) ? -INFINITY : x);
+          }
         }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -301,6 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int sl = kb < 2 ? prv : cur;
+      const bool absent = kb < kb0;
       float p[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -313,17 +314,16 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
         for (int b = 0; b < 4; ++b) {
           const int vv = 4 * a4 + b;
           const float x = fmaf(sacc[kb][vv], scv[b], -mq);
-          p[vv] = masked(kb, vv, kpv[b]) ? 0.f : __builtin_amdgcn_exp2f(x);
+          p[vv] = __builtin_amdgcn_exp2f(masked(absent, kpv[b]) ? -INFINITY : x);
           rowsum += p[vv];
         }
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t u[4] = {pack_bf16x2(p[8 * e + 0], p[8 * e + 1]),
-                               pack_bf16x2(p[8 * e + 2], p[8 * e + 3]),
-                               pack_bf16x2(p[8 * e + 4], p[8 * e + 5]),
-                               pack_bf16x2(p[8 * e + 6], p[8 * e + 7])};
-        pf[kb][e] = *(const bf16x8_t*)u;
+        bf16x8_t t;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = (__bf16)p[8 * e + j];
+        pf[kb][e] = t;
       }
     }
     rowsum += __shfl_xor(rowsum, 32);
@@ -389,14 +389,14 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       if (h == 0) lse[seg * L + posq] = l > 0.f ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
     }
     if (c + 2 < c1) {
-      fetch_rows<D>(cr, pr, c + 2, qk_rows, v_rows, row0, sorted, srow0);
+      fetch_rows<D, SORTED>(cr, pr, c + 2, qk_rows, v_rows, row0, srow0);
       if (c + 3 < c1) fetch_perm<D>(pr, c + 3, pm);
     }
     __syncthreads();
   }
 }
 
-template <int D, typename OT, bool CAUSAL>
+template <int D, typename OT, bool CAUSAL, bool SORTED>
 void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_s,
                 const void* v_s, const int32_t* perm, OT* o, float* lse, hipStream_t s) {
   const int nchunks = p.L / kChunk;
@@ -408,7 +408,7 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
   const int per = (int)((nchunks + ranges - 1) / ranges);
   ranges = (nchunks + per - 1) / per;
   const size_t shmem = Lds<D>::kBytes;
-  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL>), dim3((unsigned)(nseg * ranges)),
+  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED>), dim3((unsigned)(nseg * ranges)),
                      dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
                      (const uint4*)qk_s, (const uint4*)v_s, (const uint16_t*)v, perm, o, lse, p.L,
                      p.R, (int)nseg, per);
@@ -417,8 +417,14 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
 template <int D, typename OT>
 void launch_d(const Problem& p, const void* qk, const void* v, const void* qk_s, const void* v_s,
               const int32_t* perm, OT* o, float* lse, hipStream_t s) {
-  if (p.causal) launch_one<D, OT, true>(p, qk, v, qk_s, v_s, perm, o, lse, s);
-  else launch_one<D, OT, false>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+  const bool sorted = qk_s != nullptr;
+  if (p.causal) {
+    if (sorted) launch_one<D, OT, true, true>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+    else launch_one<D, OT, true, false>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+  } else {
+    if (sorted) launch_one<D, OT, false, true>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+    else launch_one<D, OT, false, false>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+  }
 }
 
 }  // namespace
@@ -434,10 +440,14 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
   static bool configured = false;
   if (!configured) {
     // allow the dynamic LDS size above the 64 KiB default
-    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, true>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
-    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, false>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, true, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, false, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, true, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, false, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
     configured = true;
   }
   if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, o, lse, s);
