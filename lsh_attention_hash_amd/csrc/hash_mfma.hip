@@ -13,7 +13,9 @@
 //     32; per round the kernel records upper bounds of max_k |Rh_k|,
 //     max_k |R_k - Rh_k| and max_k |R_k| (2-norms over d, computed in fp64).
 //     A transposed fp32 copy [r][k][d] serves the exact re-scoring.
-//  2. main: x (bf16) is rounded to fp16 the same way; v_mfma_f32_32x32x16_f16
+//  2. main: x (bf16) is rounded to fp16 the same way (once per forward, in a
+//     streaming pre-pass that also records |x16| and |x - x16| per row);
+//     v_mfma_f32_32x32x16_f16
 //     gives p~ = x16 . Rh_k with exact products and fp32 sums. For every
 //     column the kernel forms a key (bits of |p~| with the low ib mantissa bits
 //     replaced by k) and keeps the three largest keys per row (max / med3).
@@ -139,6 +141,42 @@ __device__ __forceinline__ void top3(float& t1, float& t2, float& t3, float key)
   t3 = n3;
 }
 
+// x -> fp16 (clamped to +-65504, |x| < 2^-14 flushed to 0), once per forward
+// for every round; with the upper bounds of |x16| and |x - x16| per row that
+// the certificate needs. D/8 consecutive lanes share a row.
+template <int D>
+__global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
+                                                  uint4* __restrict__ x16,
+                                                  float2* __restrict__ xnorm, int64_t N) {
+  constexpr int kLpr = D / 8;
+  const int sub = threadIdx.x % kLpr;
+  const int64_t stride = (int64_t)gridDim.x * (256 / kLpr);
+  for (int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr; row < N;
+       row += stride) {
+    const uint4 raw = qk[row * kLpr + sub];
+    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t out[4];
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
+      const float h0 = f16_round(x0), h1 = f16_round(x1);
+      const _Float16 e0 = (_Float16)h0, e1 = (_Float16)h1;
+      out[q] = (uint32_t)__builtin_bit_cast(uint16_t, e0) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+      a = fmaf(h0, h0, fmaf(h1, h1, a));
+      b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
+    }
+    x16[row * kLpr + sub] = make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+    for (int off = 1; off < kLpr; off <<= 1) {
+      a += __shfl_xor(a, off);
+      b += __shfl_xor(b, off);
+    }
+    if (sub == 0) xnorm[row] = make_float2(sqrtf(a) * (1.0f + 1e-5f), sqrtf(b) * (1.0f + 1e-5f));
+  }
+}
+
 struct QA {  // two-candidate re-score
   uint32_t row_lo, row_hi, k1, k2;
 };
@@ -151,7 +189,8 @@ struct QA {  // two-candidate re-score
 // it in that XCD's L2.
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_hash_mfma(
-    const uint16_t* __restrict__ qk, const _Float16* __restrict__ rh,
+    const uint16_t* __restrict__ x16, const float2* __restrict__ xnorm,
+    const _Float16* __restrict__ rh,
     const unsigned* __restrict__ bounds_u, uint16_t* __restrict__ buckets,
     int32_t* __restrict__ buckets_out, QA* __restrict__ qa, uint2* __restrict__ qb,
     unsigned* __restrict__ qcount, int64_t N, int L, int R, int half, int half_pad, int ib,
@@ -197,46 +236,37 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
   const int ntiles = half_pad / 32;
 
-  // raw bf16 x of a token tile: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
-  // of token tl of each set; the next tile is loaded while this one runs
-  uint4 raw[2][KS];
+  // x in fp16 as the B operand: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
+  // of token tl of each set, K-step ks covering dims hf*D/2 + 8ks + 0..7 (the
+  // K order of both operands is permuted the same way, which leaves the
+  // product as is). The next token tile is loaded while this one runs.
+  f16x8_t bn[2][KS];
+  float2 nn[2];
   auto fetch = [&](int j) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int64_t n = (int64_t)j * kTokWG + w * kTokWave + s * 32 + tl;
-      const uint4* src = (const uint4*)(qk + (n < N ? n : 0) * D) + hf * KS;
+      const int64_t nc = n < N ? n : 0;
+      const uint4* src = (const uint4*)(x16 + nc * D) + hf * KS;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) raw[s][ks] = n < N ? src[ks] : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 u = src[ks];
+        bn[s][ks] = __builtin_bit_cast(f16x8_t, u);
+      }
+      nn[s] = xnorm[nc];
     }
   };
   if (grp < n_tok_tiles) fetch(grp);
   for (int j = grp; j < n_tok_tiles; j += ngrp) {
     const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
-    // x in fp16 as the B operand, K-step ks covering dims hf*D/2 + 8ks + 0..7
-    // (the K order of both operands is permuted the same way, which leaves
-    // the product as is)
     f16x8_t bx[2][KS];
     float nx[2], nres[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      float a = 0.f, b = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t wv[4] = {raw[s][ks].x, raw[s][ks].y, raw[s][ks].z, raw[s][ks].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
-          const float h0 = f16_round(x0), h1 = f16_round(x1);
-          bx[s][ks][2 * q] = (_Float16)h0;
-          bx[s][ks][2 * q + 1] = (_Float16)h1;
-          a = fmaf(h0, h0, fmaf(h1, h1, a));
-          b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
-        }
-      }
-      a += __shfl_xor(a, 32);
-      b += __shfl_xor(b, 32);
-      nx[s] = sqrtf(a) * (1.0f + 1e-5f);
-      nres[s] = sqrtf(b) * (1.0f + 1e-5f);
+      for (int ks = 0; ks < KS; ++ks) bx[s][ks] = bn[s][ks];
+      nx[s] = nn[s].x;
+      nres[s] = nn[s].y;
     }
     if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
 
@@ -521,14 +551,27 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   if (grid < unit) grid = unit;
   const int64_t max_grid = (int64_t)unit * ((n_tok_tiles + 7) / 8);
   if (grid > max_grid) grid = max_grid;
+  {
+    const int64_t rpb = 256 / (p.d / 8);
+    const int64_t want = (N + rpb - 1) / rpb;
+    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+    if (p.d == 128)
+      hipLaunchKernelGGL(k_hash_x16<128>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
+                         (uint4*)hs.x16, (float2*)hs.xnorm, N);
+    else
+      hipLaunchKernelGGL(k_hash_x16<64>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
+                         (uint4*)hs.x16, (float2*)hs.xnorm, N);
+  }
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_mfma<128>, dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       (const uint16_t*)qk, hs.rh, hs.bounds, buckets, buckets_out,
+                       (const uint16_t*)hs.x16, (const float2*)hs.xnorm, hs.rh, hs.bounds,
+                       buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);
   else
     hipLaunchKernelGGL(k_hash_mfma<64>, dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       (const uint16_t*)qk, hs.rh, hs.bounds, buckets, buckets_out,
+                       (const uint16_t*)hs.x16, (const float2*)hs.xnorm, hs.rh, hs.bounds,
+                       buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);
   if (p.d == 128)

@@ -35,6 +35,8 @@ struct HashScratch {
   unsigned* bounds = nullptr; // [R][4] norm bounds (float bits), then 2 queue counters
   void* queue_a = nullptr;    // [R * N] two-candidate re-score entries (16 B)
   void* queue_b = nullptr;    // [R * N] all-column re-score entries (8 B)
+  void* x16 = nullptr;        // [N, d] fp16 copy of qk
+  void* xnorm = nullptr;      // [N] float2 bounds of |x16| and |x - x16|
   int n_cu = 0;               // compute units of the handle's device
 };
 

@@ -65,6 +65,8 @@ void free_ws(lsh::Workspace& w) {
   hipFree(w.hash.bounds);
   hipFree(w.hash.queue_a);
   hipFree(w.hash.queue_b);
+  hipFree(w.hash.x16);
+  hipFree(w.hash.xnorm);
   w = lsh::Workspace{};
 }
 
@@ -122,7 +124,9 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
     ok = alloc(&w.hash.rh, (int64_t)p.R * hp * p.d * 2, t) &&
          alloc(&w.hash.rt, (int64_t)p.R * p.half() * p.d * 4, t) &&
          alloc(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4, t) &&
-         alloc(&w.hash.queue_a, rows * 16, t) && alloc(&w.hash.queue_b, rows * 8, t);
+         alloc(&w.hash.queue_a, rows * 16, t) && alloc(&w.hash.queue_b, rows * 8, t) &&
+         alloc(&w.hash.x16, p.n_token_heads() * p.d * 2, t) &&
+         alloc(&w.hash.xnorm, p.n_token_heads() * 8, t);
   }
   if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
     ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
