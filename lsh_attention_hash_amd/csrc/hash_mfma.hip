@@ -129,16 +129,19 @@ __global__ void k_zero_u32(unsigned* p, int n) {
 
 // Keep the three largest of (t1 >= t2 >= t3) and key. Keys have a clear sign
 // bit and finite magnitude bits, so as floats they order exactly like their
-// bit patterns, and v_max_f32 / v_med3_f32 return one of their inputs; keys
-// below 2^-126 (rows whose projections are all ~0) may be flushed, and such
+// bit patterns: the max is an unsigned integer max (no NaN canonicalisation
+// on the way), and v_med3_f32 returns one of its inputs; keys below 2^-126
+// (rows whose projections are all ~0) may be flushed by the med3, and such
 // rows are never certified (their top value is ~0).
-__device__ __forceinline__ void top3(float& t1, float& t2, float& t3, float key) {
-  const float n1 = fmaxf(t1, key);
-  const float n2 = __builtin_amdgcn_fmed3f(t1, t2, key);
-  const float n3 = __builtin_amdgcn_fmed3f(t2, t3, key);
+__device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, uint32_t key) {
+  const uint32_t n1 = t1 > key ? t1 : key;
+  const float n2 = __builtin_amdgcn_fmed3f(__uint_as_float(t1), __uint_as_float(t2),
+                                           __uint_as_float(key));
+  const float n3 = __builtin_amdgcn_fmed3f(__uint_as_float(t2), __uint_as_float(t3),
+                                           __uint_as_float(key));
   t1 = n1;
-  t2 = n2;
-  t3 = n3;
+  t2 = __float_as_uint(n2);
+  t3 = __float_as_uint(n3);
 }
 
 // x -> fp16 (clamped to +-65504, |x| < 2^-14 flushed to 0), once per forward
@@ -204,6 +207,10 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   const int tl = lane & 31;            // token within a set
   const uint32_t imask = (1u << ib) - 1u;
   const uint32_t vmask = 0x7FFFFFFFu & ~imask;
+  // the key mask in a vector register: the key's index part is uniform and
+  // takes the one scalar operand v_and_or_b32 may have
+  uint32_t vmask_v;
+  asm("v_mov_b32 %0, %1" : "=v"(vmask_v) : "s"(vmask));
   const float gamma = (float)(D + 2) * 1.1920928955078125e-07f;
 
   const int xcd = blockIdx.x & 7;
@@ -270,9 +277,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     }
     if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
 
-    float t1[2] = {0.f, 0.f}, t2[2] = {0.f, 0.f}, t3[2] = {0.f, 0.f};
-    // Set 0's keys are folded while set 1's MFMAs run and the other way
-    // round, so the matrix cores and the vector ALU work at the same time.
+    uint32_t t1[2] = {0u, 0u}, t2[2] = {0u, 0u}, t3[2] = {0u, 0u};
     floatx16_t acc[2];
     f16x8_t at[KS];  // the rotation tile, shared by both sets
     auto load_tile = [&](int kt) {
@@ -287,29 +292,57 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(at[ks], bx[s][ks], ks == 0 ? zero : acc[s],
                                                          0, 0, 0);
     };
-    // C layout: lane holds token tl and columns kt*32 + 8(v/4) + 4 hf + v%4
-    auto fold = [&](int kt, int s) {
+    // C layout: lane holds token tl and columns kt*32 + 8(v/4) + 4 hf + v%4.
+    // The index field gets kt*32 + 8(v/4) + v%4 (uniform across the wave); bit
+    // 2 (the lane half) is added when the halves merge. Within one lane the
+    // order of keys is the same with or without that bit.
+    auto fold = [&](int kt, const floatx16_t& c, int s) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const uint32_t k = (uint32_t)(kt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3));
-        const float key = __uint_as_float((__float_as_uint(acc[s][v]) & vmask) | k);
-        top3(t1[s], t2[s], t3[s], key);
+        const uint32_t k = (uint32_t)(kt * 32 + 8 * (v >> 2) + (v & 3));
+        top3(t1[s], t2[s], t3[s], (__float_as_uint(c[v]) & vmask_v) | k);
       }
     };
+    // Each set's keys of tile kt are folded while the other set's MFMAs of
+    // tile kt + 1 run: the accumulators are copied out first, and the group
+    // barriers interleave one MFMA with the vector work that hides it.
     load_tile(0);
     set_mfma(0);
     set_mfma(1);
-    for (int kt = 0; kt < ntiles; ++kt) {
-      if (kt + 1 < ntiles) load_tile(kt + 1);
-      fold(kt, 0);
-      if (kt + 1 < ntiles) set_mfma(0);
-      fold(kt, 1);
-      if (kt + 1 < ntiles) set_mfma(1);
+    int kt = 0;
+    for (; kt + 1 < ntiles; ++kt) {
+      load_tile(kt + 1);
+      const floatx16_t c0 = acc[0];
+      set_mfma(0);
+      fold(kt, c0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // rotation tile reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const floatx16_t c1 = acc[1];
+      set_mfma(1);
+      fold(kt, c1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    fold(kt, acc[0], 0);
+    fold(kt, acc[1], 1);
     // merge the two lane halves (same tokens, other columns)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const float o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32),
+      t1[s] |= (uint32_t)(hf << 2);
+      t2[s] |= (uint32_t)(hf << 2);
+      t3[s] |= (uint32_t)(hf << 2);
+      const uint32_t o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32),
                   o3 = __shfl_xor(t3[s], 32);
       top3(t1[s], t2[s], t3[s], o1);
       top3(t1[s], t2[s], t3[s], o2);
@@ -319,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     float part[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint32_t k1 = __float_as_uint(t1[s]) & imask;
+      const uint32_t k1 = t1[s] & imask;
       const unsigned char* row = lds + k1 * ROWB + hf * D;
       float acc = 0.f;
 #pragma unroll
@@ -341,9 +374,9 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
 
     const int64_t n = tok0 + hf * 32 + tl;
     if (n < N) {
-      const uint32_t a1 = __float_as_uint(hf ? t1[1] : t1[0]);
-      const uint32_t a2 = __float_as_uint(hf ? t2[1] : t2[0]);
-      const uint32_t a3 = __float_as_uint(hf ? t3[1] : t3[0]);
+      const uint32_t a1 = hf ? t1[1] : t1[0];
+      const uint32_t a2 = hf ? t2[1] : t2[0];
+      const uint32_t a3 = hf ? t3[1] : t3[0];
       const float d1 = __uint_as_float(a1 & vmask);
       const float d2 = __uint_as_float(a2 & vmask);
       const float d3 = __uint_as_float(a3 & vmask);
