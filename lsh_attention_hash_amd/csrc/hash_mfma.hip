@@ -410,13 +410,21 @@ __device__ __forceinline__ void take_better(double& v, int& k, double ov, int ok
   }
 }
 
-// Queue A: per block iteration 64 entries are staged in LDS (their x rows and
-// both candidate columns, coalesced 16-byte loads); then thread 2e + c sums
-// candidate c of entry e in fp64, t = 0..d-1 in order, and the pair compares.
-// Queue B: one wave per entry, lanes over columns (rare).
-constexpr int kQaBatch = 64;
+// Exact re-scoring of the rows the certificate could not settle, as the
+// plain fp64 dot product with the sum over t = 0..d-1 in order (each product
+// of a bf16 and an fp32 is exact in fp64), so the chosen bucket is the one the
+// fp64 definition gives, tie rule included.
+//  * queue B (all columns; rare): one wave per entry, lanes over columns,
+//    reading the rotation in its own [r][t][k] layout (coalesced over k) and
+//    x_t broadcast from the lane that loaded it. Waves take entries first.
+//  * queue A (two candidates): one thread per (entry, candidate), the x row
+//    and the candidate's column read straight from memory; the two threads of
+//    an entry are neighbouring lanes and compare through a lane swap.
+constexpr int kQbCols = 8;  // independent column sums per lane in queue B
+constexpr int kQbT = 8;     // rows of t whose loads are in flight together
 template <int D>
 __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restrict__ qk,
+                                                       const float* __restrict__ rot,
                                                        const float* __restrict__ rt,
                                                        const QA* __restrict__ qa,
                                                        const uint2* __restrict__ qb,
@@ -424,104 +432,113 @@ __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restric
                                                        uint16_t* __restrict__ buckets,
                                                        int32_t* __restrict__ buckets_out, int L,
                                                        int half, int R) {
-  constexpr int XROW = D + 2;      // bf16 elements per staged x row (pad: bank spread)
-  constexpr int CROW = D + 1;      // floats per staged column
-  __shared__ __align__(16) uint16_t xs[kQaBatch][XROW];
-  __shared__ __align__(16) float cs[2 * kQaBatch][CROW];
-  __shared__ int64_t rows[kQaBatch];
-  __shared__ int kk[2 * kQaBatch];
   const int tid = threadIdx.x;
-  const int64_t na = qcount[0];
-  for (int64_t e0 = (int64_t)blockIdx.x * kQaBatch; e0 < na; e0 += (int64_t)gridDim.x * kQaBatch) {
-    const int n_here = (int)(na - e0 < kQaBatch ? na - e0 : kQaBatch);
-    if (tid < kQaBatch) {
-      int64_t row = -1;
-      int k1 = 0, k2 = 0;
-      if (tid < n_here) {
-        const QA q = qa[e0 + tid];
-        row = (int64_t)q.row_lo | ((int64_t)q.row_hi << 32);
-        k1 = (int)q.k1;
-        k2 = (int)q.k2;
-      }
-      rows[tid] = row;
-      kk[2 * tid] = k1;
-      kk[2 * tid + 1] = k2;
-    }
-    __syncthreads();
-    // x rows: D/8 pieces of 8 bf16 each (4 bytes per pair of elements)
-    for (int idx = tid; idx < kQaBatch * (D / 8); idx += 256) {
-      const int e = idx / (D / 8), c = idx % (D / 8);
-      const int64_t row = rows[e];
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row >= 0) {
-        const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
-        v = *(const uint4*)(qk + (bh * L + i) * D + c * 8);
-      }
-      uint32_t* dst = (uint32_t*)&xs[e][c * 8];
-      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-    }
-    // candidate columns: D/4 pieces of 4 floats
-    for (int idx = tid; idx < 2 * kQaBatch * (D / 4); idx += 256) {
-      const int j = idx / (D / 4), c = idx % (D / 4);
-      const int64_t row = rows[j / 2];
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row >= 0) {
-        const int64_t seg = row / L, bh = seg / R;
-        const int r = (int)(seg - bh * R);
-        v = *(const float4*)(rt + ((int64_t)r * half + kk[j]) * D + c * 4);
-      }
-      cs[j][c * 4 + 0] = v.x; cs[j][c * 4 + 1] = v.y; cs[j][c * 4 + 2] = v.z; cs[j][c * 4 + 3] = v.w;
-    }
-    __syncthreads();
-    if (tid < 2 * kQaBatch) {
-      const int e = tid >> 1;
+  const int lane = tid & 63;
+  // queue B
+  {
+    const int64_t wave = (int64_t)blockIdx.x * 4 + tid / 64;
+    const int64_t waves = (int64_t)gridDim.x * 4;
+    const int64_t nq = qcount[1];
+    for (int64_t e = wave; e < nq; e += waves) {
+      const uint2 q = qb[e];
+      const int64_t row = (int64_t)q.x | ((int64_t)q.y << 32);
+      const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
+      const int r = (int)(seg - bh * R);
+      const uint16_t* x = qk + (bh * L + i) * D;
+      float xv[D / 64];
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) xv[u] = __uint_as_float((uint32_t)x[u * 64 + lane] << 16);
+      const float* rr = rot + (int64_t)r * D * half;
       double best = -DBL_MAX;
       int bidx = INT_MAX;
-      if (rows[e] >= 0) {
-        double p = 0.0;
-        for (int t = 0; t < D; ++t)
-          p += (double)__uint_as_float((uint32_t)xs[e][t] << 16) * (double)cs[tid][t];
-        const int k = kk[tid];
-        take_better(best, bidx, p, k);
-        take_better(best, bidx, -p, k + half);
+      for (int k0 = 0; k0 < half; k0 += 64 * kQbCols) {
+        double p[kQbCols];
+        int kc[kQbCols];
+#pragma unroll
+        for (int c = 0; c < kQbCols; ++c) {
+          p[c] = 0.0;
+          const int k = k0 + c * 64 + lane;
+          kc[c] = k < half ? k : 0;
+        }
+        // kQbT rows of t at a time, all their loads issued before the sums
+        for (int t0 = 0; t0 < D; t0 += kQbT) {
+          float cv[kQbT][kQbCols];
+#pragma unroll
+          for (int tt = 0; tt < kQbT; ++tt) {
+            const float* rrow = rr + (int64_t)(t0 + tt) * half;
+#pragma unroll
+            for (int c = 0; c < kQbCols; ++c) cv[tt][c] = rrow[kc[c]];
+          }
+#pragma unroll
+          for (int tt = 0; tt < kQbT; ++tt) {
+            const int t = t0 + tt;
+            const double xt = (double)__uint_as_float(
+                __builtin_amdgcn_readlane(__float_as_uint(xv[t / 64]), t & 63));
+#pragma unroll
+            for (int c = 0; c < kQbCols; ++c) p[c] += xt * (double)cv[tt][c];
+          }
+          __builtin_amdgcn_sched_group_barrier(0x020, kQbT * kQbCols, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int c = 0; c < kQbCols; ++c) {
+          const int k = k0 + c * 64 + lane;
+          if (k < half) {
+            take_better(best, bidx, p[c], k);
+            take_better(best, bidx, -p[c], k + half);
+          }
+        }
       }
-      const double ob = __shfl_xor(best, 1);
-      const int ok = __shfl_xor(bidx, 1);
-      take_better(best, bidx, ob, ok);
-      if (rows[e] >= 0 && (tid & 1) == 0) {
-        buckets[rows[e]] = (uint16_t)bidx;
-        if (buckets_out) buckets_out[rows[e]] = bidx;
+      for (int off = 32; off > 0; off >>= 1) {
+        const double ob = __shfl_xor(best, off);
+        const int ok = __shfl_xor(bidx, off);
+        take_better(best, bidx, ob, ok);
+      }
+      if (bidx < 0 || bidx >= 2 * half) bidx = 0;  // NaN input: keep the id in range
+      if (lane == 0) {
+        buckets[row] = (uint16_t)bidx;
+        if (buckets_out) buckets_out[row] = bidx;
       }
     }
-    __syncthreads();
   }
-  // queue B
-  const int lane = tid & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + tid / 64;
-  const int64_t waves = (int64_t)gridDim.x * 4;
-  const int64_t nb_ = qcount[1];
-  for (int64_t e = wave; e < nb_; e += waves) {
-    const uint2 q = qb[e];
-    const int64_t row = (int64_t)q.x | ((int64_t)q.y << 32);
+  // queue A
+  const int64_t na2 = 2 * (int64_t)qcount[0];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + tid; g < na2; g += stride) {
+    const QA q = qa[g >> 1];
+    const int64_t row = (int64_t)q.row_lo | ((int64_t)q.row_hi << 32);
+    const int k = (int)((g & 1) ? q.k2 : q.k1);
     const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
     const int r = (int)(seg - bh * R);
-    const uint16_t* x = qk + (bh * L + i) * D;
+    const uint4* xp = (const uint4*)(qk + (bh * L + i) * D);
+    const float4* cp = (const float4*)(rt + ((int64_t)r * half + k) * D);
+    uint4 xr[D / 8];
+    float4 cr[D / 4];
+#pragma unroll
+    for (int u = 0; u < D / 8; ++u) xr[u] = xp[u];
+#pragma unroll
+    for (int u = 0; u < D / 4; ++u) cr[u] = cp[u];
+    double p = 0.0;
+#pragma unroll
+    for (int u = 0; u < D / 8; ++u) {
+      const uint32_t wv[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+      const float cv[8] = {cr[2 * u].x, cr[2 * u].y, cr[2 * u].z, cr[2 * u].w,
+                           cr[2 * u + 1].x, cr[2 * u + 1].y, cr[2 * u + 1].z, cr[2 * u + 1].w};
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        p += (double)__uint_as_float(wv[qd] << 16) * (double)cv[2 * qd];
+        p += (double)__uint_as_float(wv[qd] & 0xFFFF0000u) * (double)cv[2 * qd + 1];
+      }
+    }
     double best = -DBL_MAX;
     int bidx = INT_MAX;
-    for (int k = lane; k < half; k += 64) {
-      const float* col = rt + ((int64_t)r * half + k) * D;
-      double p = 0.0;
-      for (int t = 0; t < D; ++t) p += (double)__uint_as_float((uint32_t)x[t] << 16) * (double)col[t];
-      take_better(best, bidx, p, k);
-      take_better(best, bidx, -p, k + half);
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-      const double ob = __shfl_xor(best, off);
-      const int ok = __shfl_xor(bidx, off);
-      take_better(best, bidx, ob, ok);
-    }
-    if (bidx < 0 || bidx >= 2 * half) bidx = 0;  // NaN input: keep the id in range
-    if (lane == 0) {
+    take_better(best, bidx, p, k);
+    take_better(best, bidx, -p, k + half);
+    const double ob = __shfl_xor(best, 1);
+    const int ok = __shfl_xor(bidx, 1);
+    take_better(best, bidx, ob, ok);
+    if ((g & 1) == 0) {
       buckets[row] = (uint16_t)bidx;
       if (buckets_out) buckets_out[row] = bidx;
     }
@@ -609,11 +626,11 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
                        n_tok_tiles);
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_fallback<128>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
-                       hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
+                       rot, hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
                        buckets_out, p.L, half, p.R);
   else
     hipLaunchKernelGGL(k_hash_fallback<64>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
-                       hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
+                       rot, hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
                        buckets_out, p.L, half, p.R);
   hipLaunchKernelGGL(k_hash_stats, dim3(1), dim3(64), 0, s, qcount, stats);
   return hipGetLastError();
