@@ -29,8 +29,9 @@
 // unit vectors), so no max pass is needed; if a bound exceeds 60 (a query norm
 // far outside the usual range) the wave takes the true row max instead, so
 // exp2 never under- or overflows. Masked keys (causal: later original position;
-// self) get p = 0. A query whose p are all 0 saw nothing but itself: its output
-// is v_i and its logsumexp -1e5, as in the definition.
+// self) get p = 0. A query whose p are all 0 saw nothing but itself: its
+// logsumexp is -1e5, as in the definition, and its output for the round (v_i)
+// is not written here; the round combination reads v_i for such rounds.
 // O^T = V^T P^T: the B operand (P^T) comes straight from the S^T accumulators,
 // with the k index of each 16-key step ordered as the accumulator registers
 // (v = 8e..8e+7 of block kb), and the A operand (V^T) from two 8-byte Vq reads
@@ -67,15 +68,35 @@ struct Lds {
   static constexpr int kBytes = kBound + 2 * kChunk * 4;
 };
 
-// 4 consecutive outputs
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-  *(float4*)p = make_float4(a, b, c, d);
-}
+// 4 consecutive outputs packed into 32-bit words (fp16: 2 words, fp32: 4)
+template <typename OT>
+struct Pack4 {
+  static constexpr int kWords = 4 * (int)sizeof(OT) / 4;
+};
 __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
-__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
-  typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-  f16x4_t v = {(_Float16)sat16(a), (_Float16)sat16(b), (_Float16)sat16(c), (_Float16)sat16(d)};
-  *(f16x4_t*)p = v;
+__device__ __forceinline__ void pack4(float a, float b, float c, float d, uint32_t* w, float*) {
+  w[0] = __float_as_uint(a); w[1] = __float_as_uint(b);
+  w[2] = __float_as_uint(c); w[3] = __float_as_uint(d);
+}
+__device__ __forceinline__ void pack4(float a, float b, float c, float d, uint32_t* w, _Float16*) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t lo = {(_Float16)sat16(a), (_Float16)sat16(b)};
+  const f16x2_t hi = {(_Float16)sat16(c), (_Float16)sat16(d)};
+  w[0] = __builtin_bit_cast(uint32_t, lo);
+  w[1] = __builtin_bit_cast(uint32_t, hi);
+}
+// 8 consecutive outputs from two packed groups of 4
+template <typename OT>
+__device__ __forceinline__ void store8(OT* p, const uint32_t* lo, const uint32_t* hi) {
+  constexpr int W = Pack4<OT>::kWords;
+  uint32_t u[2 * W];
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    u[i] = lo[i];
+    u[W + i] = hi[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * W; i += 4) *(uint4*)((uint32_t*)p + i) = make_uint4(u[i], u[i + 1], u[i + 2], u[i + 3]);
 }
 
 // Thread t loads half t%2 of qk row t/2 and, for piece pp, 8 dims of the 4 v
@@ -110,31 +131,39 @@ __device__ __forceinline__ void fetch_perm(PermRegs<D>& pr, int c, const int32_t
   }
 }
 
+// Rows are addressed as a wave-uniform base (the segment's first row) plus a
+// 32-bit byte offset per lane, every offset computed before the first load,
+// so no load waits for an earlier one to release its address registers.
 template <int D, bool SORTED>
 __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& pr, int c,
                                            const uint4* qk_rows, const uint4* v_rows,
                                            int64_t row0, int64_t sorted_row0) {
   constexpr bool sorted = SORTED;
   using CR = ChunkRegs<D>;
+  constexpr uint32_t kRowBytes = D * 2;
   const int t = threadIdx.x;
-  {
-    const int r = t >> 1, half = t & 1;
-    cr.pos = pr.pos;
-    const uint4* src = sorted ? qk_rows + (sorted_row0 + c * kChunk + r) * CR::kPieces
-                              : qk_rows + (row0 + pr.pos) * CR::kPieces;
-#pragma unroll
-    for (int k = 0; k < CR::kPieces / 2; ++k) cr.qk[k] = src[half * (CR::kPieces / 2) + k];
-  }
+  const int64_t base_row = sorted ? sorted_row0 + c * kChunk : row0;
+  const unsigned char* qb = (const unsigned char*)(qk_rows + base_row * CR::kPieces);
+  const unsigned char* vb = (const unsigned char*)(v_rows + base_row * CR::kPieces);
+  const int r = t >> 1, half = t & 1;
+  const uint32_t qoff = (uint32_t)(sorted ? r : pr.pos) * kRowBytes + half * (kRowBytes / 2);
+  uint32_t voff[CR::kPer][4];
 #pragma unroll
   for (int pp = 0; pp < CR::kPer; ++pp) {
     const int id = t + pp * kThreads;
     const int qd = id / CR::kSegs, sg = id % CR::kSegs;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t row = sorted ? sorted_row0 + c * kChunk + qd * 4 + k : row0 + pr.vpos[pp][k];
-      cr.v[pp][k] = v_rows[row * CR::kPieces + sg];
-    }
+    for (int k = 0; k < 4; ++k)
+      voff[pp][k] = (uint32_t)(sorted ? qd * 4 + k : pr.vpos[pp][k]) * kRowBytes + sg * 16;
   }
+  cr.pos = pr.pos;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < CR::kPieces / 2; ++k) cr.qk[k] = *(const uint4*)(qb + qoff + k * 16);
+#pragma unroll
+  for (int pp = 0; pp < CR::kPer; ++pp)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cr.v[pp][k] = *(const uint4*)(vb + voff[pp][k]);
 }
 
 template <int D>
@@ -189,7 +218,7 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
 template <int D, typename OT, bool CAUSAL, bool SORTED>
 __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
-    const uint4* __restrict__ v_s, const uint16_t* __restrict__ v_raw,
+    const uint4* __restrict__ v_s,
     const int32_t* __restrict__ perm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
     int nseg, int chunks_per_wg) {
   using Lay = Lds<D>;
@@ -360,37 +389,58 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     // not also wait on the stores (one counter tracks both).
     __syncthreads();  // every wave is done with slot prv
     if (c + 1 < c1) stage_chunk<D>(lds, prv, cr);
-    // normalise and scatter to the query's original position
+    // Normalise and scatter to the query's original position. Lane half h
+    // holds dims 8a + 4h + 0..3 (a = 0..3) of each 32-dim block; one swap of
+    // the lanes' upper and lower halves gives lane half h dims 16j + 8h + 0..7
+    // (j = 0, 1), so each store writes 8 contiguous outputs. Every packed
+    // output sits in its own register before the first store.
+    constexpr int W = Pack4<OT>::kWords;
+    const float l = lacc[0];
+    const bool seen = l > 0.f;  // both lanes of a query agree
+    uint32_t lo[MB][2][W], hi[MB][2][W];
     {
-      const float l = lacc[0];
-      OT* orow = o + (seg * L + posq) * D;
-      if (l > 0.f) {
-        const float inv = 1.0f / l;
+      const float inv = seen ? 1.0f / l : 0.f;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        uint32_t wa[4][W];
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4)
-            store4(orow + mb * 32 + 8 * a4 + 4 * h, oacc[mb][4 * a4] * inv,
-                   oacc[mb][4 * a4 + 1] * inv, oacc[mb][4 * a4 + 2] * inv,
-                   oacc[mb][4 * a4 + 3] * inv);
-      } else {
-        const uint16_t* vr = v_raw + (row0 + posq) * D;
+        for (int a4 = 0; a4 < 4; ++a4)
+          pack4(oacc[mb][4 * a4] * inv, oacc[mb][4 * a4 + 1] * inv, oacc[mb][4 * a4 + 2] * inv,
+                oacc[mb][4 * a4 + 3] * inv, wa[a4], (OT*)nullptr);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int j = 0; j < 2; ++j) {
+          // upper lanes send group 2j, lower lanes send group 2j + 1
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int d0 = mb * 32 + 8 * a4 + 4 * h;
-            store4(orow + d0, __uint_as_float((uint32_t)vr[d0] << 16),
-                   __uint_as_float((uint32_t)vr[d0 + 1] << 16),
-                   __uint_as_float((uint32_t)vr[d0 + 2] << 16),
-                   __uint_as_float((uint32_t)vr[d0 + 3] << 16));
+          for (int i = 0; i < W; ++i) {
+            const auto r = __builtin_amdgcn_permlane32_swap(wa[2 * j][i], wa[2 * j + 1][i],
+                                                            false, false);
+            lo[mb][j][i] = h ? r[0] : wa[2 * j][i];
+            hi[mb][j][i] = h ? wa[2 * j + 1][i] : r[1];
           }
+        }
       }
-      if (h == 0) lse[seg * L + posq] = l > 0.f ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
     }
+    // The loads of chunk c + 2 (and the permutation of c + 3) go out before
+    // this chunk's stores: loads and stores share one completion counter, and
+    // a wait for the permutation entries would otherwise also wait for the
+    // stores just issued.
     if (c + 2 < c1) {
       fetch_rows<D, SORTED>(cr, pr, c + 2, qk_rows, v_rows, row0, srow0);
       if (c + 3 < c1) fetch_perm<D>(pr, c + 3, pm);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // A query that saw only itself (l == 0) has no row here: its output for
+    // this round is v_i, which the round combination takes from v directly
+    // (the logsumexp -1e5 marks the round).
+    {
+      OT* orow = o + (seg * L + posq) * D;
+      if (seen) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) store8(orow + mb * 32 + 16 * j + 8 * h, lo[mb][j], hi[mb][j]);
+      }
+      if (h == 0) lse[seg * L + posq] = seen ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
     }
     __syncthreads();
   }
@@ -410,7 +460,7 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
   const size_t shmem = Lds<D>::kBytes;
   hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED>), dim3((unsigned)(nseg * ranges)),
                      dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
-                     (const uint4*)qk_s, (const uint4*)v_s, (const uint16_t*)v, perm, o, lse, p.L,
+                     (const uint4*)qk_s, (const uint4*)v_s, perm, o, lse, p.L,
                      p.R, (int)nseg, per);
 }
 

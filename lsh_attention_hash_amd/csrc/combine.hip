@@ -7,7 +7,10 @@
 //   out(i) = sum_r w_r o_r(i),
 // which equals one softmax over the multiset union of all rounds' windows.
 // The per-round rows are already at original positions (the attention kernel
-// scatters them), so this kernel streams them in order.
+// scatters them), so this kernel streams them in order. A round whose
+// logsumexp is the self-only value -1e5 has output v_i by definition; that row
+// is taken from v (the attention kernel need not write it), selected rather
+// than weighted so that nothing else in the slot can leak in.
 #include "dtype.h"
 #include "internal.h"
 
@@ -26,6 +29,15 @@ __device__ __forceinline__ void load8(const _Float16* p, float* x) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
 }
+__device__ __forceinline__ void load8(const bf16_t* p, float* x) {
+  const uint4 a = *(const uint4*)p;
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(w[j] << 16);
+    x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
 __device__ __forceinline__ void store8(float* p, const float* x) {
   *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
   *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
@@ -39,9 +51,10 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* x) {
 }
 
 // Each lane owns 8 consecutive dims of one row; D/8 lanes cover a row.
-template <int D, typename OutT, typename OT>
+template <int D, typename OutT, typename OT, typename VT>
 __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
                                                  const float* __restrict__ lse,
+                                                 const VT* __restrict__ v,
                                                  OutT* __restrict__ out, int L, int R,
                                                  int64_t n_rows) {
   constexpr int kLpr = D / 8;             // lanes per row
@@ -59,41 +72,60 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
     for (int r = 0; r < R; ++r) sum += __expf(lr[(int64_t)r * L] - mx);
     const float inv_sum = 1.0f / sum;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wself = 0.f;  // total weight of the self-only rounds
     for (int r = 0; r < R; ++r) {
-      const float w = __expf(lr[(int64_t)r * L] - mx) * inv_sum;
+      const float lv = lr[(int64_t)r * L];
+      const float w = __expf(lv - mx) * inv_sum;
+      const bool self_only = lv == kSelfLogit;
       float x[8];
       load8(o + ((bh * R + r) * L + i) * D + sub * 8, x);
+      wself += self_only ? w : 0.f;
+      const float wo = self_only ? 0.f : w;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, x[j], acc[j]);
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wo, self_only ? 0.f : x[j], acc[j]);
+    }
+    if (wself > 0.f) {
+      float x[8];
+      load8(v + row * D + sub * 8, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wself, x[j], acc[j]);
     }
     store8(out + row * D + sub * 8, acc);
   }
 }
 
-template <int D, typename OT>
-void launch_t(const Problem& p, const OT* o, const float* lse, void* out, hipStream_t s) {
+template <int D, typename OT, typename VT>
+void launch_t(const Problem& p, const OT* o, const float* lse, const VT* v, void* out,
+              hipStream_t s) {
   const int64_t n = p.n_token_heads();
   const int64_t rpb = 256 / (D / 8);
   const int64_t want = (n + rpb - 1) / rpb;
   const unsigned blocks = (unsigned)(want < 262144 ? want : 262144);
   if (p.out_dtype == LSH_ATTN_BF16)
-    hipLaunchKernelGGL((k_combine<D, bf16_t, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
+    hipLaunchKernelGGL((k_combine<D, bf16_t, OT, VT>), dim3(blocks), dim3(256), 0, s, o, lse, v,
                        (bf16_t*)out, p.L, p.R, n);
   else
-    hipLaunchKernelGGL((k_combine<D, float, OT>), dim3(blocks), dim3(256), 0, s, o, lse,
+    hipLaunchKernelGGL((k_combine<D, float, OT, VT>), dim3(blocks), dim3(256), 0, s, o, lse, v,
                        (float*)out, p.L, p.R, n);
+}
+
+template <int D, typename OT>
+void launch_v(const Problem& p, const OT* o, const float* lse, const void* v, void* out,
+              hipStream_t s) {
+  if (p.dtype == LSH_ATTN_BF16) launch_t<D, OT, bf16_t>(p, o, lse, (const bf16_t*)v, out, s);
+  else launch_t<D, OT, float>(p, o, lse, (const float*)v, out, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
-                          void* out, hipStream_t s) {
+                          const void* v, void* out, hipStream_t s) {
   if (p.d == 64) {
-    if (o_half) launch_t<64, _Float16>(p, (const _Float16*)o, lse, out, s);
-    else launch_t<64, float>(p, (const float*)o, lse, out, s);
+    if (o_half) launch_v<64, _Float16>(p, (const _Float16*)o, lse, v, out, s);
+    else launch_v<64, float>(p, (const float*)o, lse, v, out, s);
   } else {
-    if (o_half) launch_t<128, _Float16>(p, (const _Float16*)o, lse, out, s);
-    else launch_t<128, float>(p, (const float*)o, lse, out, s);
+    if (o_half) launch_v<128, _Float16>(p, (const _Float16*)o, lse, v, out, s);
+    else launch_v<128, float>(p, (const float*)o, lse, v, out, s);
   }
   return hipGetLastError();
 }

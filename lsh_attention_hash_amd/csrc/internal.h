@@ -78,9 +78,10 @@ template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
                               OT* o, float* lse, hipStream_t s);
-// o is fp16 when o_half, else fp32
+// o is fp16 when o_half, else fp32; v (the input values) supplies the rows of
+// rounds in which a query saw only itself
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
-                          void* out, hipStream_t s);
+                          const void* v, void* out, hipStream_t s);
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.

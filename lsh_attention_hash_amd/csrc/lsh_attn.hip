@@ -181,7 +181,7 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
     e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
                            separate ? w.v_sorted : nullptr, pm, (float*)w.o, ls, s);
   mark(4);
-  if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, out, s);
+  if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, s);
   mark(5);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
