@@ -38,18 +38,29 @@ def esize(dt: str) -> int:
     return 2 if dt == "bf16" else 4
 
 
-def algorithmic_units(w, out_dtype: str, round_bytes: int = 2):
-    """Per-launch algorithmic work of each stage's kernel (what the method
-    must compute or move, not what an implementation happens to move).
+def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None):
+    """Per-launch algorithmic work of each stage (what the method must compute
+    or move, not what an implementation happens to move).
     N = B*H*L token-heads, R rounds, d head dim, nb buckets, m chunk length;
     round_bytes = bytes per element of the per-round outputs kept between the
-    attention and the combine (2 for fp16, 4 with the fp32 option)."""
+    attention and the combine (2 for fp16, 4 with the fp32 option); stats =
+    the re-scoring counts of the forward (rows re-scored on two columns, rows
+    re-scored on all columns)."""
     N = w.batch * w.heads * w.seq_len
     R, d, nb, m = w.n_rounds, w.head_dim, w.n_buckets, w.chunk_len
     e, eo, ro = esize(w.dtype), esize(out_dtype), round_bytes
+    half = max(nb // 2, 1)
+    n_a = (stats or {}).get("n_exact_rescored", 0)
+    n_b = (stats or {}).get("n_full_fallback", 0)
     return {
-        # projection x.R for every token-head and round: nb/2 MACs of length d
-        "hash": {"flops": N * R * d * nb, "bytes": N * d * e + N * R * 2},
+        # fp16 copy of qk and its two norm bounds; rotation copies (fp16, fp32)
+        "hash_prep": {"bytes": N * d * e + N * d * 2 + N * 8 + R * d * half * (4 + 2 + 4)},
+        # projection x.R for every token-head and round: nb/2 MACs of length d;
+        # reads the fp16 rows and norm bounds once, writes the bucket ids
+        "hash": {"flops": N * R * d * nb, "bytes": N * d * 2 + N * 8 + N * R * 2},
+        # exact fp64 dot products of the re-scored rows
+        "hash_rescore": {"flops64": 2 * d * (2 * n_a + half * n_b),
+                         "bytes": (n_a + n_b) * d * e + 2 * n_a * d * 4},
         # read bucket ids twice (count, scatter), write the permutation
         "sort": {"bytes": N * R * (2 + 2 + 4)},
         # read two rows, write two rows per (round, slot), plus the perm read
@@ -63,30 +74,52 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2):
     }
 
 
-# How each stage's kernel is bound in the current implementation, and the peak
-# it is measured against.
-KERNEL_BOUND = {
-    "hash": ("mfma", "mfma_fp16_TFLOPs"),       # fp16 MFMA projection (+ rare fp64 re-score)
-    "sort": ("hbm", "hbm_GBps"),
-    "gather": ("hbm", "hbm_GBps"),
-    "attend": ("mfma", "mfma_bf16_TFLOPs"),     # bf16 MFMA QK^T and PV
-    "combine": ("hbm", "hbm_GBps"),
-}
+# The matrix-core peak each stage's contraction runs at (fp16 projection,
+# bf16 attention); HBM for the rest; fp64 vector for the exact re-scoring.
+MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs"}
+
+
+def stage_bound(stage: str, u: dict):
+    """The resource that bounds a stage at its algorithmic work: the larger of
+    flops / matrix peak and bytes / HBM peak."""
+    if "flops64" in u:
+        return "alu", "fp64_vector_TFLOPs"
+    if "flops" in u:
+        t_f = u["flops"] / (PEAK[MFMA_PEAK[stage]] * 1e12)
+        t_b = u["bytes"] / (PEAK["hbm_GBps"] * 1e9)
+        if t_f >= t_b:
+            return "mfma", MFMA_PEAK[stage]
+    return "hbm", "hbm_GBps"
 
 
 def roofline(stage: str, units: dict, ms: float, traffic=None):
-    bound, peak_key = KERNEL_BOUND[stage]
     u = units[stage]
+    bound, peak_key = stage_bound(stage, u)
     if peak_key == "hbm_GBps":
         achieved = u["bytes"] / (ms * 1e-3) / 1e9
         unit = "GB/s"
+    elif peak_key == "fp64_vector_TFLOPs":
+        achieved = u["flops64"] / (ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
     else:
         achieved = u["flops"] / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
     peak = PEAK[peak_key]
-    return {"kernel": stage, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 5), "traffic": traffic,
-            "algorithmic_bytes": u.get("bytes"), "algorithmic_flops": u.get("flops")}
+    return {"kernel": STAGE_KERNEL.get(stage, stage), "stage": stage, "bound": bound,
+            "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5), "traffic": traffic,
+            "algorithmic_bytes": u.get("bytes"),
+            "algorithmic_flops": u.get("flops", u.get("flops64"))}
+
+
+# Stages that are exactly one kernel launch (name as rocprofv3 reports it),
+# and the source files each stage's kernels are built from.
+STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine"}
+STAGE_SOURCES = {
+    "hash_prep": ["hash_mfma.hip"], "hash": ["hash_mfma.hip", "hash.hip"],
+    "hash_rescore": ["hash_mfma.hip"], "sort": ["sort.hip"], "gather": ["gather.hip"],
+    "attend": ["attend_mfma.hip", "attend.hip"], "combine": ["combine.hip"],
+}
 
 
 def cpu_baseline(w, inp, heads: int):
@@ -142,7 +175,16 @@ def main():
                     help="heads in the oracle sample (0: as many as rounds fit the cores)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed region, copy this many MiB device to device "
+                         "(the reference kernel for scaling FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: read two rocprofv3 --pmc output folders (FETCH_SIZE, "
+                         "WRITE_SIZE) of a run with --calib-copy-mib and write --traffic-json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -198,11 +240,22 @@ def main():
     stage_avg = {k: v_ / max(n_timed, 1) for k, v_ in stage_ms.items()}
     stats = op.stats()
 
+    if args.calib_copy_mib > 0:
+        nbytes = args.calib_copy_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     fp16_rounds = w.dtype == "bf16" and w.chunk_len == 64 and not args.fp32_round_outputs
-    units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4)
+    units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4, stats)
     if not args.separate_gather:
         stage_avg.pop("gather")   # rows are read through the permutation inside attend
-    dominant = max(stage_avg, key=stage_avg.get)
+    # the dominant kernel: the slowest stage that is one kernel launch
+    single = {k: v_ for k, v_ in stage_avg.items() if k in STAGE_KERNEL}
+    dominant = max(single, key=single.get)
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
@@ -257,14 +310,74 @@ def main():
 
 
 def kernel_source_hash(stage: str) -> str:
-    """Hash of the source file of a stage's kernel; counter-derived traffic is
-    only reported while the kernel source is unchanged."""
+    """Hash of the source files of a stage's kernels (and the shared headers);
+    counter-derived traffic is only reported while they are unchanged."""
     import hashlib
-    fname = {"hash": "hash.hip", "sort": "sort.hip", "gather": "gather.hip",
-             "attend": "attend.hip", "combine": "combine.hip"}[stage]
-    path = os.path.join(ROOT, "lsh_attention_hash_amd", "csrc", fname)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for fname in STAGE_SOURCES[stage] + ["internal.h", "dtype.h"]:
+        with open(os.path.join(ROOT, "lsh_attention_hash_amd", "csrc", fname), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_dispatches(folder: str, counter: str):
+    """(kernel name, value) of one counter for every dispatch in a rocprofv3
+    --pmc output folder (csv)."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(args):
+    """HBM bytes per launch of the single-kernel stages from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for the calibration copy of known size (--calib-copy-mib of the profiled
+    run: each copy dispatch reads and writes exactly that many bytes)."""
+    import statistics
+    fetch = _pmc_dispatches(args.write_traffic[0], "FETCH_SIZE")
+    write = _pmc_dispatches(args.write_traffic[1], "WRITE_SIZE")
+    if args.calib_copy_mib <= 0:
+        raise SystemExit("--write-traffic needs --calib-copy-mib of the profiled run")
+    known_kib = float(args.calib_copy_mib * 1024)
+
+    def calib(rows):
+        # copy dispatches of the calibration size (other copies in the run are small)
+        vals = [v for k, v in rows if "copy" in k.lower() and v >= known_kib / 8]
+        if not vals:
+            raise SystemExit("calibration copy dispatches not found in the counters")
+        return "copy", known_kib / statistics.median(vals)
+
+    def mean_of(rows, kname):
+        vals = [v for k, v in rows if kname in k]
+        return sum(vals) / len(vals) if vals else None
+
+    cf_name, cf = calib(fetch)
+    cw_name, cw = calib(write)
+    out = {}
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            out = json.load(f)
+    entry = out.setdefault(args.workload, {})
+    for stage, kname in STAGE_KERNEL.items():
+        f_kib, w_kib = mean_of(fetch, kname), mean_of(write, kname)
+        if f_kib is None or w_kib is None:
+            continue
+        entry[stage] = {
+            "bytes_per_launch": round(f_kib * 1024 * cf + w_kib * 1024 * cw),
+            "fetch_kib": round(f_kib, 1), "write_kib": round(w_kib, 1),
+            "fetch_scale": round(cf, 4), "write_scale": round(cw, 4),
+            "calibration": f"{args.calib_copy_mib} MiB device copy (__amd_rocclr_copyBuffer)",
+            "source_hash": kernel_source_hash(stage),
+        }
+    with open(args.traffic_json, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(entry, indent=1))
 
 
 if __name__ == "__main__":

@@ -131,12 +131,14 @@ int lsh_attn_get_stats(lsh_attn_t handle, lsh_attn_stats_t* stats);
  * each forward records a HIP event on its stream before the first stage and
  * after every stage, for at most `capacity` forwards (later forwards are not
  * timed). Events are created here (host call, no device memory).
- * Stages: 0 hash, 1 sort, 2 gather (0 ms unless separate), 3 chunk attention,
- * 4 combine.
+ * Stages: 0 hash preparation (rotation copies, fp16 copy of qk; 0 ms on the
+ * exact fp64 path), 1 hash projection (the matrix-core kernel, or the exact
+ * kernel), 2 exact re-scoring of unsettled rows (0 ms on the exact path),
+ * 3 sort, 4 gather (0 ms unless separate), 5 chunk attention, 6 combine.
  * Errors: INVALID_ARG for a null handle or capacity < 0 (0 disables);
  * HIP if events cannot be created.
  */
-#define LSH_ATTN_N_STAGES 5
+#define LSH_ATTN_N_STAGES 7
 int lsh_attn_set_timing(lsh_attn_t handle, int capacity);
 
 /*

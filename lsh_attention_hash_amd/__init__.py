@@ -30,8 +30,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "H
 EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats",
                     "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_workspace_bytes",
                     "lsh_attn_destroy", "lsh_attn_strerror")
-N_STAGES = 5
-STAGES = ("hash", "sort", "gather", "attend", "combine")
+N_STAGES = 7
+STAGES = ("hash_prep", "hash", "hash_rescore", "sort", "gather", "attend", "combine")
 
 
 class LSHAttnError(RuntimeError):

@@ -575,7 +575,7 @@ bool hash_mfma_supported(const Problem& p) {
 
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
-                            hipStream_t s) {
+                            hipStream_t s, hipEvent_t after_prep, hipEvent_t after_main) {
   const int half = p.half();
   const int hp = hash_half_pad(p);
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
@@ -612,6 +612,7 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
       hipLaunchKernelGGL(k_hash_x16<64>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
                          (uint4*)hs.x16, (float2*)hs.xnorm, N);
   }
+  if (after_prep) (void)hipEventRecord(after_prep, s);
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_mfma<128>, dim3((unsigned)grid), dim3(kThreads), lds, s,
                        (const uint16_t*)hs.x16, (const float2*)hs.xnorm, hs.rh, hs.bounds,
@@ -624,6 +625,7 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
                        buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);
+  if (after_main) (void)hipEventRecord(after_main, s);
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_fallback<128>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
                        rot, hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,

@@ -63,9 +63,11 @@ hipError_t launch_hash_exact(const Problem& p, const void* qk, const float* rot,
                              uint16_t* buckets, int32_t* buckets_out, hipStream_t s);
 int hash_half_pad(const Problem& p);
 bool hash_mfma_supported(const Problem& p);
+// after_prep / after_main (may be null) are recorded once the preparation
+// kernels and the projection kernel are enqueued
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
-                            hipStream_t s);
+                            hipStream_t s, hipEvent_t after_prep, hipEvent_t after_main);
 hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,
                        int32_t* perm, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const void* qk, const void* v, const int32_t* perm,

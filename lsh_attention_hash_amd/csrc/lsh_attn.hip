@@ -165,24 +165,28 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, w.stats, 2);
   mark(0);
   if (e == hipSuccess) {
-    if (lsh::hash_mfma_supported(p))
-      e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, s);
-    else
+    if (lsh::hash_mfma_supported(p)) {
+      e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, s,
+                                ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
+    } else {
+      mark(1);
       e = lsh::launch_hash_exact(p, qk, rotations, w.buckets, buckets, s);
+      mark(2);
+    }
   }
-  mark(1);
+  mark(3);
   if (e == hipSuccess) e = lsh::launch_sort(p, w.buckets, w.sort_counts, pm, s);
-  mark(2);
+  mark(4);
   const bool separate = (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER) != 0;
   if (e == hipSuccess && separate)
     e = lsh::launch_gather(p, qk, v, pm, w.qk_sorted, w.v_sorted, s);
-  mark(3);
+  mark(5);
   if (e == hipSuccess)
     e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
                            separate ? w.v_sorted : nullptr, pm, (float*)w.o, ls, s);
-  mark(4);
+  mark(6);
   if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, s);
-  mark(5);
+  mark(7);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
 }
