@@ -11,6 +11,8 @@
 // logsumexp is the self-only value -1e5 has output v_i by definition; that row
 // is taken from v (the attention kernel need not write it), selected rather
 // than weighted so that nothing else in the slot can leak in.
+#include <type_traits>
+
 #include "dtype.h"
 #include "internal.h"
 
@@ -50,8 +52,10 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* x) {
   *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
 }
 
-// Each lane owns 8 consecutive dims of one row; D/8 lanes cover a row.
-template <int D, typename OutT, typename OT, typename VT>
+// Each lane owns 8 consecutive dims of one row; D/8 lanes cover a row. Rounds
+// are taken kG at a time (kG = R when R is 1, 2, 4 or 8; else 4 with a guard),
+// all their loads issued before any use.
+template <int D, typename OutT, typename OT, typename VT, int kG>
 __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
                                                  const float* __restrict__ lse,
                                                  const VT* __restrict__ v,
@@ -66,30 +70,45 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
     const int64_t bh = row / L;
     const int64_t i = row - bh * L;
     const float* lr = lse + bh * R * L + i;
+    const OT* orow = o + (bh * R * L + i) * D + sub * 8;
     float mx = -INFINITY;
-    for (int r = 0; r < R; ++r) mx = fmaxf(mx, lr[(int64_t)r * L]);
-    float sum = 0.f;
-    for (int r = 0; r < R; ++r) sum += __expf(lr[(int64_t)r * L] - mx);
-    const float inv_sum = 1.0f / sum;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float wself = 0.f;  // total weight of the self-only rounds
-    for (int r = 0; r < R; ++r) {
-      const float lv = lr[(int64_t)r * L];
-      const float w = __expf(lv - mx) * inv_sum;
-      const bool self_only = lv == kSelfLogit;
-      float x[8];
-      load8(o + ((bh * R + r) * L + i) * D + sub * 8, x);
-      wself += self_only ? w : 0.f;
-      const float wo = self_only ? 0.f : w;
+    for (int r0 = 0; r0 < R; r0 += kG) {
+      float lv[kG];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wo, self_only ? 0.f : x[j], acc[j]);
+      for (int u = 0; u < kG; ++u) lv[u] = r0 + u < R ? lr[(int64_t)(r0 + u) * L] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kG; ++u) mx = fmaxf(mx, lv[u]);
     }
+    float sum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float wself = 0.f;  // weight of the self-only rounds
+    for (int r0 = 0; r0 < R; r0 += kG) {
+      float lv[kG], x[kG][8];
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const bool in = r0 + u < R;
+        lv[u] = in ? lr[(int64_t)(r0 + u) * L] : -INFINITY;
+        if (in) load8(orow + (int64_t)(r0 + u) * L * D, x[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const float w = __expf(lv[u] - mx);  // 0 for rounds past R
+        const bool self_only = lv[u] == kSelfLogit;
+        sum += w;
+        wself += self_only ? w : 0.f;
+        const float wo = self_only || r0 + u >= R ? 0.f : w;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wo, wo != 0.f ? x[u][j] : 0.f, acc[j]);
+      }
+    }
+    const float inv_sum = 1.0f / sum;
     if (wself > 0.f) {
       float x[8];
       load8(v + row * D + sub * 8, x);
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = fmaf(wself, x[j], acc[j]);
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= inv_sum;
     store8(out + row * D + sub * 8, acc);
   }
 }
@@ -101,12 +120,21 @@ void launch_t(const Problem& p, const OT* o, const float* lse, const VT* v, void
   const int64_t rpb = 256 / (D / 8);
   const int64_t want = (n + rpb - 1) / rpb;
   const unsigned blocks = (unsigned)(want < 262144 ? want : 262144);
-  if (p.out_dtype == LSH_ATTN_BF16)
-    hipLaunchKernelGGL((k_combine<D, bf16_t, OT, VT>), dim3(blocks), dim3(256), 0, s, o, lse, v,
-                       (bf16_t*)out, p.L, p.R, n);
-  else
-    hipLaunchKernelGGL((k_combine<D, float, OT, VT>), dim3(blocks), dim3(256), 0, s, o, lse, v,
-                       (float*)out, p.L, p.R, n);
+  auto go = [&](auto g) {
+    constexpr int G = decltype(g)::value;
+    if (p.out_dtype == LSH_ATTN_BF16)
+      hipLaunchKernelGGL((k_combine<D, bf16_t, OT, VT, G>), dim3(blocks), dim3(256), 0, s, o, lse,
+                         v, (bf16_t*)out, p.L, p.R, n);
+    else
+      hipLaunchKernelGGL((k_combine<D, float, OT, VT, G>), dim3(blocks), dim3(256), 0, s, o, lse,
+                         v, (float*)out, p.L, p.R, n);
+  };
+  switch (p.R) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 8: go(std::integral_constant<int, 8>{}); break;
+    default: go(std::integral_constant<int, 4>{}); break;
+  }
 }
 
 template <int D, typename OT>

@@ -123,10 +123,6 @@ __global__ __launch_bounds__(256) void k_hash_prep(const float* __restrict__ rot
   }
 }
 
-__global__ void k_zero_u32(unsigned* p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
-}
-
 // Keep the three largest of (t1 >= t2 >= t3) and key. Keys have a clear sign
 // bit and finite magnitude bits, so as floats they order exactly like their
 // bit patterns: the max is an unsigned integer max (no NaN canonicalisation
@@ -147,11 +143,16 @@ __device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, u
 // x -> fp16 (clamped to +-65504, |x| < 2^-14 flushed to 0), once per forward
 // for every round; with the upper bounds of |x16| and |x - x16| per row that
 // the certificate needs. D/8 consecutive lanes share a row.
+// Block 0 also clears the norm bounds and queue counters of this forward
+// (the rotation preparation, launched next, accumulates into them).
 template <int D>
 __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
                                                   uint4* __restrict__ x16,
-                                                  float2* __restrict__ xnorm, int64_t N) {
+                                                  float2* __restrict__ xnorm, int64_t N,
+                                                  unsigned* __restrict__ clear, int n_clear) {
   constexpr int kLpr = D / 8;
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_clear; i += 256) clear[i] = 0u;
   const int sub = threadIdx.x % kLpr;
   const int64_t stride = (int64_t)gridDim.x * (256 / kLpr);
   for (int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr; row < N;
@@ -414,14 +415,16 @@ __device__ __forceinline__ void take_better(double& v, int& k, double ov, int ok
 // plain fp64 dot product with the sum over t = 0..d-1 in order (each product
 // of a bf16 and an fp32 is exact in fp64), so the chosen bucket is the one the
 // fp64 definition gives, tie rule included.
-//  * queue B (all columns; rare): one wave per entry, lanes over columns,
-//    reading the rotation in its own [r][t][k] layout (coalesced over k) and
-//    x_t broadcast from the lane that loaded it. Waves take entries first.
+//  * queue B (all columns; rare): one workgroup per row, threads over
+//    columns, reading the rotation in its own [r][t][k] layout (coalesced
+//    over k) in batches of kQbT rows of t, x_t broadcast from the lane that
+//    loaded it; the workgroup's best (value, column) is reduced through LDS.
+//    Workgroups take these rows first.
 //  * queue A (two candidates): one thread per (entry, candidate), the x row
 //    and the candidate's column read straight from memory; the two threads of
 //    an entry are neighbouring lanes and compare through a lane swap.
-constexpr int kQbCols = 8;  // independent column sums per lane in queue B
-constexpr int kQbT = 8;     // rows of t whose loads are in flight together
+// Thread 0 of workgroup 0 also reports the queue sizes.
+constexpr int kQbT = 32;  // rows of t whose loads are in flight together (x2 columns)
 template <int D>
 __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restrict__ qk,
                                                        const float* __restrict__ rot,
@@ -430,77 +433,82 @@ __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restric
                                                        const uint2* __restrict__ qb,
                                                        const unsigned* __restrict__ qcount,
                                                        uint16_t* __restrict__ buckets,
-                                                       int32_t* __restrict__ buckets_out, int L,
-                                                       int half, int R) {
+                                                       int32_t* __restrict__ buckets_out,
+                                                       unsigned long long* __restrict__ stats,
+                                                       int L, int half, int R) {
+  __shared__ double red_v[4];
+  __shared__ int red_k[4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int wv = tid >> 6;
+  if (blockIdx.x == 0 && tid == 0) {
+    stats[0] = qcount[0];
+    stats[1] = qcount[1];
+  }
   // queue B
-  {
-    const int64_t wave = (int64_t)blockIdx.x * 4 + tid / 64;
-    const int64_t waves = (int64_t)gridDim.x * 4;
-    const int64_t nq = qcount[1];
-    for (int64_t e = wave; e < nq; e += waves) {
-      const uint2 q = qb[e];
-      const int64_t row = (int64_t)q.x | ((int64_t)q.y << 32);
-      const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
-      const int r = (int)(seg - bh * R);
-      const uint16_t* x = qk + (bh * L + i) * D;
-      float xv[D / 64];
+  const int64_t nq = qcount[1];
+  for (int64_t e = blockIdx.x; e < nq; e += gridDim.x) {
+    const uint2 q = qb[e];
+    const int64_t row = (int64_t)q.x | ((int64_t)q.y << 32);
+    const int64_t seg = row / L, i = row - seg * L, bh = seg / R;
+    const int r = (int)(seg - bh * R);
+    const uint16_t* x = qk + (bh * L + i) * D;
+    float xv[D / 64];
 #pragma unroll
-      for (int u = 0; u < D / 64; ++u) xv[u] = __uint_as_float((uint32_t)x[u * 64 + lane] << 16);
-      const float* rr = rot + (int64_t)r * D * half;
-      double best = -DBL_MAX;
-      int bidx = INT_MAX;
-      for (int k0 = 0; k0 < half; k0 += 64 * kQbCols) {
-        double p[kQbCols];
-        int kc[kQbCols];
+    for (int u = 0; u < D / 64; ++u) xv[u] = __uint_as_float((uint32_t)x[u * 64 + lane] << 16);
+    const float* rr = rot + (int64_t)r * D * half;
+    double best = -DBL_MAX;
+    int bidx = INT_MAX;
+    for (int k0 = 0; k0 < half; k0 += 512) {
+      const int ka = k0 + tid, kb = k0 + 256 + tid;
+      const int kca = ka < half ? ka : 0, kcb = kb < half ? kb : 0;
+      double pa = 0.0, pb = 0.0;
+      for (int t0 = 0; t0 < D; t0 += kQbT) {
+        float ca[kQbT], cb[kQbT];
 #pragma unroll
-        for (int c = 0; c < kQbCols; ++c) {
-          p[c] = 0.0;
-          const int k = k0 + c * 64 + lane;
-          kc[c] = k < half ? k : 0;
-        }
-        // kQbT rows of t at a time, all their loads issued before the sums
-        for (int t0 = 0; t0 < D; t0 += kQbT) {
-          float cv[kQbT][kQbCols];
-#pragma unroll
-          for (int tt = 0; tt < kQbT; ++tt) {
-            const float* rrow = rr + (int64_t)(t0 + tt) * half;
-#pragma unroll
-            for (int c = 0; c < kQbCols; ++c) cv[tt][c] = rrow[kc[c]];
-          }
-#pragma unroll
-          for (int tt = 0; tt < kQbT; ++tt) {
-            const int t = t0 + tt;
-            const double xt = (double)__uint_as_float(
-                __builtin_amdgcn_readlane(__float_as_uint(xv[t / 64]), t & 63));
-#pragma unroll
-            for (int c = 0; c < kQbCols; ++c) p[c] += xt * (double)cv[tt][c];
-          }
-          __builtin_amdgcn_sched_group_barrier(0x020, kQbT * kQbCols, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int tt = 0; tt < kQbT; ++tt) {
+          const float* rrow = rr + (int64_t)(t0 + tt) * half;
+          ca[tt] = rrow[kca];
+          cb[tt] = rrow[kcb];
         }
 #pragma unroll
-        for (int c = 0; c < kQbCols; ++c) {
-          const int k = k0 + c * 64 + lane;
-          if (k < half) {
-            take_better(best, bidx, p[c], k);
-            take_better(best, bidx, -p[c], k + half);
-          }
+        for (int tt = 0; tt < kQbT; ++tt) {
+          const int t = t0 + tt;
+          const double xt = (double)__uint_as_float(
+              __builtin_amdgcn_readlane(__float_as_uint(xv[t / 64]), t & 63));
+          pa += xt * (double)ca[tt];
+          pb += xt * (double)cb[tt];
         }
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * kQbT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 1000, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      for (int off = 32; off > 0; off >>= 1) {
-        const double ob = __shfl_xor(best, off);
-        const int ok = __shfl_xor(bidx, off);
-        take_better(best, bidx, ob, ok);
+      if (ka < half) {
+        take_better(best, bidx, pa, ka);
+        take_better(best, bidx, -pa, ka + half);
       }
-      if (bidx < 0 || bidx >= 2 * half) bidx = 0;  // NaN input: keep the id in range
-      if (lane == 0) {
-        buckets[row] = (uint16_t)bidx;
-        if (buckets_out) buckets_out[row] = bidx;
+      if (kb < half) {
+        take_better(best, bidx, pb, kb);
+        take_better(best, bidx, -pb, kb + half);
       }
     }
+    for (int off = 32; off > 0; off >>= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int ok = __shfl_xor(bidx, off);
+      take_better(best, bidx, ob, ok);
+    }
+    if (lane == 0) {
+      red_v[wv] = best;
+      red_k[wv] = bidx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int u = 1; u < 4; ++u) take_better(best, bidx, red_v[u], red_k[u]);
+      if (bidx < 0 || bidx >= 2 * half) bidx = 0;  // NaN input: keep the id in range
+      buckets[row] = (uint16_t)bidx;
+      if (buckets_out) buckets_out[row] = bidx;
+    }
+    __syncthreads();
   }
   // queue A
   const int64_t na2 = 2 * (int64_t)qcount[0];
@@ -522,13 +530,13 @@ __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restric
     double p = 0.0;
 #pragma unroll
     for (int u = 0; u < D / 8; ++u) {
-      const uint32_t wv[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+      const uint32_t wq[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
       const float cv[8] = {cr[2 * u].x, cr[2 * u].y, cr[2 * u].z, cr[2 * u].w,
                            cr[2 * u + 1].x, cr[2 * u + 1].y, cr[2 * u + 1].z, cr[2 * u + 1].w};
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        p += (double)__uint_as_float(wv[qd] << 16) * (double)cv[2 * qd];
-        p += (double)__uint_as_float(wv[qd] & 0xFFFF0000u) * (double)cv[2 * qd + 1];
+        p += (double)__uint_as_float(wq[qd] << 16) * (double)cv[2 * qd];
+        p += (double)__uint_as_float(wq[qd] & 0xFFFF0000u) * (double)cv[2 * qd + 1];
       }
     }
     double best = -DBL_MAX;
@@ -542,14 +550,6 @@ __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restric
       buckets[row] = (uint16_t)bidx;
       if (buckets_out) buckets_out[row] = bidx;
     }
-  }
-}
-
-__global__ void k_hash_stats(const unsigned* __restrict__ qcount,
-                             unsigned long long* __restrict__ stats) {
-  if (threadIdx.x == 0) {
-    stats[0] = qcount[0];
-    stats[1] = qcount[1];
   }
 }
 
@@ -579,10 +579,7 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   const int half = p.half();
   const int hp = hash_half_pad(p);
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
-  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, hs.bounds, 4 * p.R + 2);
   unsigned* qcount = hs.bounds + 4 * p.R;
-  hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * (hp / 32))), dim3(256), 0, s, rot, hs.rh,
-                     hs.rt, hs.bounds, p.d, half, hp);
   const int64_t N = p.n_token_heads();
   const int n_tok_tiles = (int)((N + kTokWG - 1) / kTokWG);
   // persistent grid: as many resident workgroups as fit, a multiple of 8 R
@@ -607,11 +604,13 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
     if (p.d == 128)
       hipLaunchKernelGGL(k_hash_x16<128>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (uint4*)hs.x16, (float2*)hs.xnorm, N);
+                         (uint4*)hs.x16, (float2*)hs.xnorm, N, hs.bounds, 4 * p.R + 2);
     else
       hipLaunchKernelGGL(k_hash_x16<64>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (uint4*)hs.x16, (float2*)hs.xnorm, N);
+                         (uint4*)hs.x16, (float2*)hs.xnorm, N, hs.bounds, 4 * p.R + 2);
   }
+  hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * (hp / 32))), dim3(256), 0, s, rot, hs.rh,
+                     hs.rt, hs.bounds, p.d, half, hp);
   if (after_prep) (void)hipEventRecord(after_prep, s);
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_mfma<128>, dim3((unsigned)grid), dim3(kThreads), lds, s,
@@ -629,12 +628,11 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_fallback<128>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
                        rot, hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
-                       buckets_out, p.L, half, p.R);
+                       buckets_out, stats, p.L, half, p.R);
   else
     hipLaunchKernelGGL(k_hash_fallback<64>, dim3(1024), dim3(256), 0, s, (const uint16_t*)qk,
                        rot, hs.rt, (const QA*)hs.queue_a, (const uint2*)hs.queue_b, qcount, buckets,
-                       buckets_out, p.L, half, p.R);
-  hipLaunchKernelGGL(k_hash_stats, dim3(1), dim3(64), 0, s, qcount, stats);
+                       buckets_out, stats, p.L, half, p.R);
   return hipGetLastError();
 }
 

@@ -162,10 +162,12 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   int32_t* pm = perm ? perm : w.perm;
   float* ls = lse ? lse : w.lse;
   hipError_t e = hipSuccess;
-  hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, w.stats, 2);
+  const bool mfma_hash = lsh::hash_mfma_supported(p);
+  // the matrix-core hash reports its own re-scoring counts
+  if (!mfma_hash) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, w.stats, 2);
   mark(0);
   if (e == hipSuccess) {
-    if (lsh::hash_mfma_supported(p)) {
+    if (mfma_hash) {
       e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, s,
                                 ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
     } else {
