@@ -249,6 +249,15 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     fetch_perm<D>(pr, c0 - 1, pm);
     fetch_rows<D, SORTED>(cr, pr, c0 - 1, qk_rows, v_rows, row0, srow0);
     stage_chunk<D>(lds, (c0 - 1) & 1, cr);
+  } else {
+    // Chunk 0 has no previous chunk: its slot holds zero keys and values, so
+    // the window's first 64 logits are finite (0) and contribute nothing once
+    // masked as absent; the loops then need no branch for chunk 0.
+    uint4* kt = (uint4*)(lds + Lay::kKt + kChunk * Lay::kRow);        // slot 1
+    for (int i = threadIdx.x; i < kChunk * Lay::kRow / 16; i += kThreads) kt[i] = uint4{};
+    uint4* vq = (uint4*)(lds + Lay::kVq + (kChunk / 4) * Lay::kQuad);  // slot 1
+    for (int i = threadIdx.x; i < (kChunk / 4) * Lay::kQuad / 16; i += kThreads) vq[i] = uint4{};
+    if (threadIdx.x < kChunk) ((float*)(lds + Lay::kScale))[kChunk + threadIdx.x] = 0.f;
   }
   fetch_perm<D>(pr, c0, pm);
   fetch_rows<D, SORTED>(cr, pr, c0, qk_rows, v_rows, row0, srow0);
@@ -267,6 +276,8 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   const uint32_t ones_u[4] = {one2, one2, one2, one2};
   const bf16x8_t ones = *(const bf16x8_t*)ones_u;
 
+  constexpr int W = Pack4<OT>::kWords;
+
   for (int c = c0; c < c1; ++c) {
     const int cur = c & 1, prv = cur ^ 1;
     const int kb0 = c > 0 ? 0 : 2;  // chunk 0 has no previous chunk
@@ -280,19 +291,20 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(row + ks * 16);
     }
-    floatx16_t sacc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = floatx16_t{};
-      if (kb < kb0) continue;
+    // S^T of key block kb (32 keys: window keys 32kb .. 32kb + 31)
+    auto qk_block = [&](int kb) -> floatx16_t {
       const int sl = kb < 2 ? prv : cur;
-      const unsigned char* row = lds + Lay::kKt + (sl * kChunk + (kb & 1) * 32 + lq) * Lay::kRow + h * D;
+      const unsigned char* row =
+          lds + Lay::kKt + (sl * kChunk + (kb & 1) * 32 + lq) * Lay::kRow + h * D;
+      floatx16_t acc;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t a = *(const bf16x8_t*)(row + ks * 16);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? floatx16_t{} : acc,
+                                                       0, 0, 0);
       }
-    }
+      return acc;
+    };
     // A key is masked when it is absent (chunk 0 has no previous chunk), the
     // query itself, or (causal) at a later original position. Positions are
     // unique within a segment, so "itself" is pos_j == pos_q and the causal
@@ -300,11 +312,14 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     auto masked = [&](bool absent, int kp) -> bool {
       return absent || (CAUSAL ? kp >= posq : kp == posq);
     };
-    const bool slow = __ballot(mq > kBoundLimit) != 0ull;
-    if (slow) {
+    // If a bound is far above the logits it bounds, shift by the true row
+    // max instead (an extra QK^T pass; the bound depends only on the query,
+    // so the choice is known before any product).
+    if (__ballot(mq > kBoundLimit) != 0ull) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        const floatx16_t sb = qk_block(kb);
         const int sl = kb < 2 ? prv : cur;
         const bool absent = kb < kb0;
 #pragma unroll
@@ -316,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
           const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const float x = sacc[kb][4 * a4 + b] * scv[b];
+            const float x = sb[4 * a4 + b] * scv[b];
             mx = fmaxf(mx, masked(absent, kpv[b]) ? -INFINITY : x);
           }
         }
@@ -324,14 +339,13 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       mq = mx == -INFINITY ? 0.f : mx;
     }
-    // p in bf16 as the B operand of O^T: step (kb, e) takes v = 8e..8e+7
-    bf16x8_t pf[4][2];
+    // p of key block kb in bf16 as the B operand of O^T: step e takes the
+    // accumulator registers v = 8e..8e+7
     float rowsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    auto soft_block = [&](int kb, const floatx16_t& sb, bf16x8_t* pf) {
       const int sl = kb < 2 ? prv : cur;
       const bool absent = kb < kb0;
-      float p[16];
+      float pv[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int key = (kb & 1) * 32 + 8 * a4 + 4 * h;
@@ -342,28 +356,25 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const int vv = 4 * a4 + b;
-          const float x = fmaf(sacc[kb][vv], scv[b], -mq);
-          p[vv] = __builtin_amdgcn_exp2f(masked(absent, kpv[b]) ? -INFINITY : x);
-          rowsum += p[vv];
+          const float x = fmaf(sb[vv], scv[b], -mq);
+          pv[vv] = __builtin_amdgcn_exp2f(masked(absent, kpv[b]) ? -INFINITY : x);
+          rowsum += pv[vv];
         }
       }
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         bf16x8_t t;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = (__bf16)p[8 * e + j];
-        pf[kb][e] = t;
+        for (int j = 0; j < 8; ++j) t[j] = (__bf16)pv[8 * e + j];
+        pf[e] = t;
       }
-    }
-    rowsum += __shfl_xor(rowsum, 32);
-    // O^T = V^T P^T (+ row sums against ones)
+    };
+    // O^T += V^T P^T over key block kb (+ row sums against ones)
     floatx16_t oacc[MB];
     floatx16_t lacc = floatx16_t{};
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) oacc[mb] = floatx16_t{};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb < kb0) continue;
+    auto pv_block = [&](int kb, const bf16x8_t* pf) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         // keys 32kb + 16e + 4h + 0..3 and 32kb + 16e + 8 + 4h + 0..3 (window order)
@@ -378,12 +389,31 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
           const uint2 lo = *(const uint2*)(va + dim * 8);
           const uint2 hi = *(const uint2*)(vc + dim * 8);
           const uint32_t u[4] = {lo.x, lo.y, hi.x, hi.y};
-          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)u, pf[kb][e],
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_t*)u, pf[e],
                                                               oacc[mb], 0, 0, 0);
         }
-        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[kb][e], lacc, 0, 0, 0);
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[e], lacc, 0, 0, 0);
       }
+    };
+    // Software pipeline over the four key blocks: the QK^T MFMAs of block
+    // kb + 1 and the PV MFMAs of block kb - 1 run while the vector unit does
+    // the softmax of block kb.
+    {
+      bf16x8_t pfa[2], pfb[2];
+      floatx16_t s0 = qk_block(0);
+      floatx16_t s1 = qk_block(1);
+      soft_block(0, s0, pfa);
+      floatx16_t s2 = qk_block(2);
+      soft_block(1, s1, pfb);
+      pv_block(0, pfa);
+      floatx16_t s3 = qk_block(3);
+      soft_block(2, s2, pfa);
+      pv_block(1, pfb);
+      soft_block(3, s3, pfb);
+      pv_block(2, pfa);
+      pv_block(3, pfb);
     }
+    rowsum += __shfl_xor(rowsum, 32);
     // The next chunk, whose rows were loaded during this compute, is staged
     // before this chunk's outputs are stored: a wait on those loads then does
     // not also wait on the stores (one counter tracks both).
@@ -394,7 +424,6 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     // the lanes' upper and lower halves gives lane half h dims 16j + 8h + 0..7
     // (j = 0, 1), so each store writes 8 contiguous outputs. Every packed
     // output sits in its own register before the first store.
-    constexpr int W = Pack4<OT>::kWords;
     const float l = lacc[0];
     const bool seen = l > 0.f;  // both lanes of a query agree
     uint32_t lo[MB][2][W], hi[MB][2][W];
