@@ -15,9 +15,11 @@
 //        that one 8-byte LDS read yields 4 consecutive keys of one dim;
 //   per key: log2(e)/(sqrt(d) |k|), original position, and log2(e) |k|/sqrt(d).
 // The previous chunk stays in LDS, so every chunk is loaded once per walk.
-// Loads run two chunks ahead of the compute: the permutation entries of chunk
-// c+3 and the rows of chunk c+2 are in flight while chunk c is computed, so no
-// row load waits for its own index load.
+// The rows of chunk c+1 are loaded while chunk c is computed, addressed by
+// its positions that the previous step staged in LDS; the positions of chunk
+// c+2 are loaded at the same time. Both are waited for only when chunk c+1
+// is staged, after the compute, so no wait at the top of a step involves
+// memory (loads and stores share one completion counter).
 //
 // Per wave (32 queries), v_mfma_f32_32x32x16_bf16:
 //   S^T[key, query] = K Q^T over the 128-key window (64 for chunk 0), 4
@@ -65,7 +67,8 @@ struct Lds {
   static constexpr int kScale = kVq + 2 * (kChunk / 4) * kQuad;
   static constexpr int kPos = kScale + 2 * kChunk * 4;
   static constexpr int kBound = kPos + 2 * kChunk * 4;
-  static constexpr int kBytes = kBound + 2 * kChunk * 4;
+  static constexpr int kPermNext = kBound + 2 * kChunk * 4;  // positions of the next chunk
+  static constexpr int kBytes = kPermNext + kChunk * 4;
 };
 
 // 4 consecutive outputs packed into 32-bit words (fp16: 2 words, fp32: 4)
@@ -118,16 +121,20 @@ struct PermRegs {
   int vpos[ChunkRegs<D>::kPer][4];
 };
 
+// The entries come from the chunk's 64 positions staged in LDS.
 template <int D>
-__device__ __forceinline__ void fetch_perm(PermRegs<D>& pr, int c, const int32_t* pm) {
+__device__ __forceinline__ void read_perm(PermRegs<D>& pr, const int* pn) {
   using CR = ChunkRegs<D>;
   const int t = threadIdx.x;
-  pr.pos = pm[c * kChunk + (t >> 1)];
+  pr.pos = pn[t >> 1];
 #pragma unroll
   for (int pp = 0; pp < CR::kPer; ++pp) {
     const int qd = (t + pp * kThreads) / CR::kSegs;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pr.vpos[pp][k] = pm[c * kChunk + qd * 4 + k];
+    const int4 q4 = *(const int4*)(pn + qd * 4);
+    pr.vpos[pp][0] = q4.x;
+    pr.vpos[pp][1] = q4.y;
+    pr.vpos[pp][2] = q4.z;
+    pr.vpos[pp][3] = q4.w;
   }
 }
 
@@ -245,10 +252,18 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 
   ChunkRegs<D> cr;
   PermRegs<D> pr;
+  int* pn = (int*)(lds + Lay::kPermNext);
+  // positions of chunk c into LDS (threads 0..63), for the prologue
+  auto perm_to_lds = [&](int c) {
+    if (threadIdx.x < kChunk) pn[threadIdx.x] = pm[c * kChunk + threadIdx.x];
+  };
   if (c0 > 0) {
-    fetch_perm<D>(pr, c0 - 1, pm);
+    perm_to_lds(c0 - 1);
+    __syncthreads();
+    read_perm<D>(pr, pn);
     fetch_rows<D, SORTED>(cr, pr, c0 - 1, qk_rows, v_rows, row0, srow0);
     stage_chunk<D>(lds, (c0 - 1) & 1, cr);
+    __syncthreads();
   } else {
     // Chunk 0 has no previous chunk: its slot holds zero keys and values, so
     // the window's first 64 logits are finite (0) and contribute nothing once
@@ -259,15 +274,15 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     for (int i = threadIdx.x; i < (kChunk / 4) * Lay::kQuad / 16; i += kThreads) vq[i] = uint4{};
     if (threadIdx.x < kChunk) ((float*)(lds + Lay::kScale))[kChunk + threadIdx.x] = 0.f;
   }
-  fetch_perm<D>(pr, c0, pm);
+  perm_to_lds(c0);
+  __syncthreads();
+  read_perm<D>(pr, pn);
   fetch_rows<D, SORTED>(cr, pr, c0, qk_rows, v_rows, row0, srow0);
   stage_chunk<D>(lds, c0 & 1, cr);
-  if (c0 + 1 < c1) {
-    fetch_perm<D>(pr, c0 + 1, pm);
-    fetch_rows<D, SORTED>(cr, pr, c0 + 1, qk_rows, v_rows, row0, srow0);
-  }
-  if (c0 + 2 < c1) fetch_perm<D>(pr, c0 + 2, pm);
   __syncthreads();
+  if (c0 + 1 < c1) perm_to_lds(c0 + 1);
+  __syncthreads();
+  int pnext = 0;  // a position of chunk c + 2, in flight to LDS
 
   const float* kscale = (const float*)(lds + Lay::kScale);
   const int* kpos = (const int*)(lds + Lay::kPos);
@@ -279,6 +294,14 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   constexpr int W = Pack4<OT>::kWords;
 
   for (int c = c0; c < c1; ++c) {
+    // Rows of chunk c + 1 (positions from LDS) and the positions of chunk
+    // c + 2 are loaded while this chunk is computed; they are waited for only
+    // when chunk c + 1 is staged, after the compute.
+    if (c + 1 < c1) {
+      read_perm<D>(pr, pn);
+      fetch_rows<D, SORTED>(cr, pr, c + 1, qk_rows, v_rows, row0, srow0);
+      if (c + 2 < c1 && threadIdx.x < kChunk) pnext = pm[(c + 2) * kChunk + threadIdx.x];
+    }
     const int cur = c & 1, prv = cur ^ 1;
     const int kb0 = c > 0 ? 0 : 2;  // chunk 0 has no previous chunk
     const int q = 32 * w + lq;      // this lane's query row in the chunk
@@ -418,7 +441,10 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     // before this chunk's outputs are stored: a wait on those loads then does
     // not also wait on the stores (one counter tracks both).
     __syncthreads();  // every wave is done with slot prv
-    if (c + 1 < c1) stage_chunk<D>(lds, prv, cr);
+    if (c + 1 < c1) {
+      stage_chunk<D>(lds, prv, cr);
+      if (c + 2 < c1 && threadIdx.x < kChunk) pn[threadIdx.x] = pnext;
+    }
     // Normalise and scatter to the query's original position. Lane half h
     // holds dims 8a + 4h + 0..3 (a = 0..3) of each 32-dim block; one swap of
     // the lanes' upper and lower halves gives lane half h dims 16j + 8h + 0..7
@@ -449,15 +475,6 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
         }
       }
     }
-    // The loads of chunk c + 2 (and the permutation of c + 3) go out before
-    // this chunk's stores: loads and stores share one completion counter, and
-    // a wait for the permutation entries would otherwise also wait for the
-    // stores just issued.
-    if (c + 2 < c1) {
-      fetch_rows<D, SORTED>(cr, pr, c + 2, qk_rows, v_rows, row0, srow0);
-      if (c + 3 < c1) fetch_perm<D>(pr, c + 3, pm);
-    }
-    __builtin_amdgcn_sched_barrier(0);
     // A query that saw only itself (l == 0) has no row here: its output for
     // this round is v_i, which the round combination takes from v directly
     // (the logsumexp -1e5 marks the round).
