@@ -184,6 +184,11 @@ __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
 struct QA {  // two-candidate re-score
   uint32_t row_lo, row_hi, k1, k2;
 };
+// Re-score entries are first appended to a workgroup queue in LDS (LDS atomics
+// answer in tens of cycles) and moved to the global queues, one global atomic
+// per queue, when the workgroup ends; only a full LDS queue appends globally.
+constexpr int kQaLds = 256, kQbLds = 64;
+constexpr int kQueueLdsBytes = kQaLds * 16 + kQbLds * 8 + 16;
 
 // Persistent: workgroup w serves round r and token tiles j = grp, grp + G/R, ...
 // (tiles of kTokWG consecutive token-heads). Its rotation R_r stays in LDS for
@@ -214,6 +219,10 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   asm("v_mov_b32 %0, %1" : "=v"(vmask_v) : "s"(vmask));
   const float gamma = (float)(D + 2) * 1.1920928955078125e-07f;
 
+  QA* qa_l = (QA*)(lds + half_pad * ROWB);
+  uint2* qb_l = (uint2*)(lds + half_pad * ROWB + kQaLds * 16);
+  unsigned* qn_l = (unsigned*)(lds + half_pad * ROWB + kQaLds * 16 + kQbLds * 8);
+  if (threadIdx.x < 2) qn_l[threadIdx.x] = 0u;
   const int xcd = blockIdx.x & 7;
   const int kk = blockIdx.x >> 3;
   const int r = kk % R;
@@ -374,6 +383,10 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const float pk1 = (hf ? part[1] : part[0]) + recv;
 
     const int64_t n = tok0 + hf * 32 + tl;
+    // head and position of the wave's first token (wave-uniform)
+    const int64_t tok0u = __builtin_amdgcn_readfirstlane((int)(tok0 & 0xffffffff)) |
+                          ((int64_t)__builtin_amdgcn_readfirstlane((int)(tok0 >> 32)) << 32);
+    const int64_t bh0 = tok0u / L, i0 = tok0u - bh0 * L;
     if (n < N) {
       const uint32_t a1 = hf ? t1[1] : t1[0];
       const uint32_t a2 = hf ? t2[1] : t2[0];
@@ -384,8 +397,11 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       const float ex = (gamma * rh_max + lo_max) * (hf ? nx[1] : nx[0]) +
                        r_max * (hf ? nres[1] : nres[0]);
       const float thr = 2.0f * (ex + ldexpf(d1, ib - 22));
-      const int64_t bh = n / L;
-      const int64_t i = n - bh * L;
+      int64_t bh = bh0, i = i0 + hf * 32 + tl;
+      while (i >= L) {  // at most once when L >= 64
+        i -= L;
+        ++bh;
+      }
       const int64_t row = (bh * R + r) * L + i;
       const uint32_t k1 = a1 & imask;
       if (d1 - d2 > thr && k1 < (uint32_t)half) {
@@ -393,14 +409,29 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         buckets[row] = (uint16_t)bk;
         if (buckets_out) buckets_out[row] = bk;
       } else if (d1 - d3 > thr && k1 < (uint32_t)half && (a2 & imask) < (uint32_t)half) {
-        const unsigned e = atomicAdd(qcount + 0, 1u);
-        qa[e] = QA{(uint32_t)row, (uint32_t)(row >> 32), k1, a2 & imask};
+        const QA entry{(uint32_t)row, (uint32_t)(row >> 32), k1, a2 & imask};
+        const unsigned e = atomicAdd(qn_l + 0, 1u);
+        if (e < (unsigned)kQaLds) qa_l[e] = entry;
+        else qa[atomicAdd(qcount + 0, 1u)] = entry;
       } else {
-        const unsigned e = atomicAdd(qcount + 1, 1u);
-        qb[e] = make_uint2((uint32_t)row, (uint32_t)(row >> 32));
+        const uint2 entry = make_uint2((uint32_t)row, (uint32_t)(row >> 32));
+        const unsigned e = atomicAdd(qn_l + 1, 1u);
+        if (e < (unsigned)kQbLds) qb_l[e] = entry;
+        else qb[atomicAdd(qcount + 1, 1u)] = entry;
       }
     }
   }
+  // move the workgroup's queued entries to the global queues
+  __syncthreads();
+  unsigned* base_l = qn_l + 2;
+  const unsigned na = min(qn_l[0], (unsigned)kQaLds), nb = min(qn_l[1], (unsigned)kQbLds);
+  if (threadIdx.x == 0) {
+    base_l[0] = na ? atomicAdd(qcount + 0, na) : 0u;
+    base_l[1] = nb ? atomicAdd(qcount + 1, nb) : 0u;
+  }
+  __syncthreads();
+  for (unsigned e = threadIdx.x; e < na; e += kThreads) qa[base_l[0] + e] = qa_l[e];
+  for (unsigned e = threadIdx.x; e < nb; e += kThreads) qb[base_l[1] + e] = qb_l[e];
 }
 
 // Better of two (value, index) candidates under "largest value, lowest index".
@@ -554,7 +585,7 @@ __global__ __launch_bounds__(256) void k_hash_fallback(const uint16_t* __restric
 }
 
 template <int D>
-constexpr int lds_bytes(int half_pad) { return half_pad * (2 * D + 16); }
+constexpr int lds_bytes(int half_pad) { return half_pad * (2 * D + 16) + kQueueLdsBytes; }
 
 int ceil_log2(int x) {
   int b = 0;
