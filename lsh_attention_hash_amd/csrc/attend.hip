@@ -85,13 +85,13 @@ void launch_simple(const Problem& p, const void* qk, const void* v, const void* 
 }  // namespace
 
 hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const void* qk_sorted,
-                         const void* v_sorted, const int32_t* perm, float* o, float* lse,
-                         hipStream_t s) {
+                         const void* v_sorted, const int32_t* perm, const float* knorm, float* o,
+                         float* lse, hipStream_t s) {
   if (attend_mfma_supported(p)) {
     if (round_outputs_half(p))
-      return launch_attend_mfma<_Float16>(p, qk, v, qk_sorted, v_sorted, perm, (_Float16*)o, lse,
-                                          s);
-    return launch_attend_mfma<float>(p, qk, v, qk_sorted, v_sorted, perm, o, lse, s);
+      return launch_attend_mfma<_Float16>(p, qk, v, qk_sorted, v_sorted, perm, knorm,
+                                          (_Float16*)o, lse, s);
+    return launch_attend_mfma<float>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
   }
   const bool bf = p.dtype == LSH_ATTN_BF16;
   if (p.d == 64) {

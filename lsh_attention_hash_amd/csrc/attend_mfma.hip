@@ -112,6 +112,7 @@ struct ChunkRegs {
   uint4 qk[kPieces / 2];
   uint4 v[kPer][4];
   int pos;
+  float n2;  // squared norm of qk row t/2
 };
 
 // permutation entries (original positions) a chunk's loads need
@@ -144,7 +145,8 @@ __device__ __forceinline__ void read_perm(PermRegs<D>& pr, const int* pn) {
 template <int D, bool SORTED>
 __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& pr, int c,
                                            const uint4* qk_rows, const uint4* v_rows,
-                                           int64_t row0, int64_t sorted_row0) {
+                                           const float* knorm, int64_t row0,
+                                           int64_t sorted_row0) {
   constexpr bool sorted = SORTED;
   using CR = ChunkRegs<D>;
   constexpr uint32_t kRowBytes = D * 2;
@@ -165,6 +167,7 @@ __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& 
   }
   cr.pos = pr.pos;
   __builtin_amdgcn_sched_barrier(0);
+  cr.n2 = knorm[row0 + pr.pos];
 #pragma unroll
   for (int k = 0; k < CR::kPieces / 2; ++k) cr.qk[k] = *(const uint4*)(qb + qoff + k * 16);
 #pragma unroll
@@ -180,21 +183,16 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
   const int t = threadIdx.x;
   {
     const int r = t >> 1, half = t & 1;
-    float nn = 0.f;
+    const float nn = cr.n2;
+    uint4* dst = (uint4*)(lds + Lay::kKt + (sl * kChunk + r) * Lay::kRow) + half * (CR::kPieces / 2);
+    // (each piece passes through a register-only asm statement, so the copy
+    // cannot become a memcpy from a stack copy of the registers)
 #pragma unroll
     for (int k = 0; k < CR::kPieces / 2; ++k) {
-      const uint32_t w[4] = {cr.qk[k].x, cr.qk[k].y, cr.qk[k].z, cr.qk[k].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float a = __uint_as_float(w[u] << 16), b = __uint_as_float(w[u] & 0xFFFF0000u);
-        nn = fmaf(a, a, nn);
-        nn = fmaf(b, b, nn);
-      }
+      uint4 x = cr.qk[k];
+      asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+      dst[k] = x;
     }
-    nn += __shfl_xor(nn, 1);
-    uint4* dst = (uint4*)(lds + Lay::kKt + (sl * kChunk + r) * Lay::kRow) + half * (CR::kPieces / 2);
-#pragma unroll
-    for (int k = 0; k < CR::kPieces / 2; ++k) dst[k] = cr.qk[k];
     if (half == 0) {
       const float nrm = sqrtf(nn);
       const float sc = kLog2e / sqrtf((float)D);
@@ -222,11 +220,14 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
   }
 }
 
+// LDS (the two chunks of K and V) allows one wave per SIMD at d = 128, so the
+// register budget is the whole file; say so, or the compiler aims for two
+// waves and spills.
 template <int D, typename OT, bool CAUSAL, bool SORTED>
-__global__ __launch_bounds__(kThreads) void k_attend_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attend_mfma(
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
-    const uint4* __restrict__ v_s,
-    const int32_t* __restrict__ perm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
+    const uint4* __restrict__ v_s, const int32_t* __restrict__ perm,
+    const float* __restrict__ knorm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
     int nseg, int chunks_per_wg) {
   using Lay = Lds<D>;
   constexpr int KS = D / 16;       // 16-dim K-steps of QK^T
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     perm_to_lds(c0 - 1);
     __syncthreads();
     read_perm<D>(pr, pn);
-    fetch_rows<D, SORTED>(cr, pr, c0 - 1, qk_rows, v_rows, row0, srow0);
+    fetch_rows<D, SORTED>(cr, pr, c0 - 1, qk_rows, v_rows, knorm, row0, srow0);
     stage_chunk<D>(lds, (c0 - 1) & 1, cr);
     __syncthreads();
   } else {
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
   perm_to_lds(c0);
   __syncthreads();
   read_perm<D>(pr, pn);
-  fetch_rows<D, SORTED>(cr, pr, c0, qk_rows, v_rows, row0, srow0);
+  fetch_rows<D, SORTED>(cr, pr, c0, qk_rows, v_rows, knorm, row0, srow0);
   stage_chunk<D>(lds, c0 & 1, cr);
   __syncthreads();
   if (c0 + 1 < c1) perm_to_lds(c0 + 1);
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
     // when chunk c + 1 is staged, after the compute.
     if (c + 1 < c1) {
       read_perm<D>(pr, pn);
-      fetch_rows<D, SORTED>(cr, pr, c + 1, qk_rows, v_rows, row0, srow0);
+      fetch_rows<D, SORTED>(cr, pr, c + 1, qk_rows, v_rows, knorm, row0, srow0);
       if (c + 2 < c1 && threadIdx.x < kChunk) pnext = pm[(c + 2) * kChunk + threadIdx.x];
     }
     const int cur = c & 1, prv = cur ^ 1;
@@ -429,6 +430,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
       floatx16_t s2 = qk_block(2);
       soft_block(1, s1, pfb);
       pv_block(0, pfa);
+
       floatx16_t s3 = qk_block(3);
       soft_block(2, s2, pfa);
       pv_block(1, pfb);
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void k_attend_mfma(
 
 template <int D, typename OT, bool CAUSAL, bool SORTED>
 void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_s,
-                const void* v_s, const int32_t* perm, OT* o, float* lse, hipStream_t s) {
+                const void* v_s, const int32_t* perm, const float* knorm, OT* o, float* lse, hipStream_t s) {
   const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
   const int64_t target = 1024;
@@ -506,20 +508,20 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
   const size_t shmem = Lds<D>::kBytes;
   hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED>), dim3((unsigned)(nseg * ranges)),
                      dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
-                     (const uint4*)qk_s, (const uint4*)v_s, perm, o, lse, p.L,
+                     (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse, p.L,
                      p.R, (int)nseg, per);
 }
 
 template <int D, typename OT>
 void launch_d(const Problem& p, const void* qk, const void* v, const void* qk_s, const void* v_s,
-              const int32_t* perm, OT* o, float* lse, hipStream_t s) {
+              const int32_t* perm, const float* knorm, OT* o, float* lse, hipStream_t s) {
   const bool sorted = qk_s != nullptr;
   if (p.causal) {
-    if (sorted) launch_one<D, OT, true, true>(p, qk, v, qk_s, v_s, perm, o, lse, s);
-    else launch_one<D, OT, true, false>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+    if (sorted) launch_one<D, OT, true, true>(p, qk, v, qk_s, v_s, perm, knorm, o, lse, s);
+    else launch_one<D, OT, true, false>(p, qk, v, qk_s, v_s, perm, knorm, o, lse, s);
   } else {
-    if (sorted) launch_one<D, OT, false, true>(p, qk, v, qk_s, v_s, perm, o, lse, s);
-    else launch_one<D, OT, false, false>(p, qk, v, qk_s, v_s, perm, o, lse, s);
+    if (sorted) launch_one<D, OT, false, true>(p, qk, v, qk_s, v_s, perm, knorm, o, lse, s);
+    else launch_one<D, OT, false, false>(p, qk, v, qk_s, v_s, perm, knorm, o, lse, s);
   }
 }
 
@@ -532,7 +534,7 @@ bool attend_mfma_supported(const Problem& p) {
 template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
-                              OT* o, float* lse, hipStream_t s) {
+                              const float* knorm, OT* o, float* lse, hipStream_t s) {
   static bool configured = false;
   if (!configured) {
     // allow the dynamic LDS size above the 64 KiB default
@@ -546,16 +548,16 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
     configured = true;
   }
-  if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, o, lse, s);
-  else launch_d<128, OT>(p, qk, v, qk_sorted, v_sorted, perm, o, lse, s);
+  if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
+  else launch_d<128, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
   return hipGetLastError();
 }
 
 template hipError_t launch_attend_mfma<float>(const Problem&, const void*, const void*, const void*,
-                                              const void*, const int32_t*, float*, float*,
-                                              hipStream_t);
+                                              const void*, const int32_t*, const float*, float*,
+                                              float*, hipStream_t);
 template hipError_t launch_attend_mfma<_Float16>(const Problem&, const void*, const void*,
                                                  const void*, const void*, const int32_t*,
-                                                 _Float16*, float*, hipStream_t);
+                                                 const float*, _Float16*, float*, hipStream_t);
 
 }  // namespace lsh

@@ -142,16 +142,19 @@ __device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, u
 
 // x -> fp16 (clamped to +-65504, |x| < 2^-14 flushed to 0), once per forward
 // for every round; with the upper bounds of |x16| and |x - x16| per row that
-// the certificate needs. D/8 consecutive lanes share a row.
+// the certificate needs, and the squared norm of the bf16 row (fp32), which
+// the attention turns into its key scale. D/8 consecutive lanes share a row.
 // Block 0 also clears the norm bounds and queue counters of this forward
 // (the rotation preparation, launched next, accumulates into them).
-template <int D>
+// With kX16 = false only the squared norms are produced.
+template <int D, bool kX16>
 __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
                                                   uint4* __restrict__ x16,
-                                                  float2* __restrict__ xnorm, int64_t N,
+                                                  float2* __restrict__ xnorm,
+                                                  float* __restrict__ knorm, int64_t N,
                                                   unsigned* __restrict__ clear, int n_clear) {
   constexpr int kLpr = D / 8;
-  if (blockIdx.x == 0)
+  if (kX16 && blockIdx.x == 0)
     for (int i = threadIdx.x; i < n_clear; i += 256) clear[i] = 0u;
   const int sub = threadIdx.x % kLpr;
   const int64_t stride = (int64_t)gridDim.x * (256 / kLpr);
@@ -160,24 +163,33 @@ __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
     const uint4 raw = qk[row * kLpr + sub];
     const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
     uint32_t out[4];
-    float a = 0.f, b = 0.f;
+    float a = 0.f, b = 0.f, c = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
-      const float h0 = f16_round(x0), h1 = f16_round(x1);
-      const _Float16 e0 = (_Float16)h0, e1 = (_Float16)h1;
-      out[q] = (uint32_t)__builtin_bit_cast(uint16_t, e0) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
-      a = fmaf(h0, h0, fmaf(h1, h1, a));
-      b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
+      c = fmaf(x0, x0, fmaf(x1, x1, c));
+      if (kX16) {
+        const float h0 = f16_round(x0), h1 = f16_round(x1);
+        const _Float16 e0 = (_Float16)h0, e1 = (_Float16)h1;
+        out[q] = (uint32_t)__builtin_bit_cast(uint16_t, e0) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+        a = fmaf(h0, h0, fmaf(h1, h1, a));
+        b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
+      }
     }
-    x16[row * kLpr + sub] = make_uint4(out[0], out[1], out[2], out[3]);
+    if (kX16) x16[row * kLpr + sub] = make_uint4(out[0], out[1], out[2], out[3]);
 #pragma unroll
     for (int off = 1; off < kLpr; off <<= 1) {
-      a += __shfl_xor(a, off);
-      b += __shfl_xor(b, off);
+      c += __shfl_xor(c, off);
+      if (kX16) {
+        a += __shfl_xor(a, off);
+        b += __shfl_xor(b, off);
+      }
     }
-    if (sub == 0) xnorm[row] = make_float2(sqrtf(a) * (1.0f + 1e-5f), sqrtf(b) * (1.0f + 1e-5f));
+    if (sub == 0) {
+      if (knorm) knorm[row] = c;
+      if (kX16) xnorm[row] = make_float2(sqrtf(a) * (1.0f + 1e-5f), sqrtf(b) * (1.0f + 1e-5f));
+    }
   }
 }
 
@@ -597,6 +609,20 @@ int ceil_log2(int x) {
 
 int hash_half_pad(const Problem& p) { return ((p.half() + 31) / 32) * 32; }
 
+hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipStream_t s) {
+  const int64_t N = p.n_token_heads();
+  const int64_t rpb = 256 / (p.d / 8);
+  const int64_t want = (N + rpb - 1) / rpb;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  if (p.d == 128)
+    hipLaunchKernelGGL((k_hash_x16<128, false>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
+                       nullptr, nullptr, knorm, N, nullptr, 0);
+  else
+    hipLaunchKernelGGL((k_hash_x16<64, false>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
+                       nullptr, nullptr, knorm, N, nullptr, 0);
+  return hipGetLastError();
+}
+
 bool hash_mfma_supported(const Problem& p) {
   if (p.dtype != LSH_ATTN_BF16 || p.nb < 2 || (p.d != 64 && p.d != 128)) return false;
   const int hp = hash_half_pad(p);
@@ -606,7 +632,8 @@ bool hash_mfma_supported(const Problem& p) {
 
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
-                            hipStream_t s, hipEvent_t after_prep, hipEvent_t after_main) {
+                            float* knorm, hipStream_t s, hipEvent_t after_prep,
+                            hipEvent_t after_main) {
   const int half = p.half();
   const int hp = hash_half_pad(p);
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
@@ -634,11 +661,11 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
     const int64_t want = (N + rpb - 1) / rpb;
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
     if (p.d == 128)
-      hipLaunchKernelGGL(k_hash_x16<128>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (uint4*)hs.x16, (float2*)hs.xnorm, N, hs.bounds, 4 * p.R + 2);
+      hipLaunchKernelGGL((k_hash_x16<128, true>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
+                         (uint4*)hs.x16, (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
     else
-      hipLaunchKernelGGL(k_hash_x16<64>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (uint4*)hs.x16, (float2*)hs.xnorm, N, hs.bounds, 4 * p.R + 2);
+      hipLaunchKernelGGL((k_hash_x16<64, true>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
+                         (uint4*)hs.x16, (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
   }
   hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * (hp / 32))), dim3(256), 0, s, rot, hs.rh,
                      hs.rt, hs.bounds, p.d, half, hp);

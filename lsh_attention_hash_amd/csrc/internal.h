@@ -52,6 +52,7 @@ struct Workspace {
   void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
   void* v_sorted = nullptr;        // [seg, L, d]
   unsigned long long* stats = nullptr;  // [2] exact rescored, full fallback
+  float* knorm = nullptr;          // [B*H*L] squared qk row norms (matrix-core attention)
   HashScratch hash;                     // matrix-core hash only
 };
 
@@ -65,21 +66,26 @@ int hash_half_pad(const Problem& p);
 bool hash_mfma_supported(const Problem& p);
 // after_prep / after_main (may be null) are recorded once the preparation
 // kernels and the projection kernel are enqueued
+// knorm (may be null): receives the squared norm of every qk row (bf16
+// inputs, d = 64 or 128), which the matrix-core attention uses
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
-                            hipStream_t s, hipEvent_t after_prep, hipEvent_t after_main);
+                            float* knorm, hipStream_t s, hipEvent_t after_prep,
+                            hipEvent_t after_main);
+// squared norms of the qk rows alone (when the matrix-core hash does not run)
+hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipStream_t s);
 hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,
                        int32_t* perm, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                          void* qk_sorted, void* v_sorted, hipStream_t s);
 hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const void* qk_sorted,
-                         const void* v_sorted, const int32_t* perm, float* o, float* lse,
-                         hipStream_t s);
+                         const void* v_sorted, const int32_t* perm, const float* knorm, float* o,
+                         float* lse, hipStream_t s);
 bool attend_mfma_supported(const Problem& p);
 template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
-                              OT* o, float* lse, hipStream_t s);
+                              const float* knorm, OT* o, float* lse, hipStream_t s);
 // o is fp16 when o_half, else fp32; v (the input values) supplies the rows of
 // rounds in which a query saw only itself
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,

@@ -60,6 +60,7 @@ void free_ws(lsh::Workspace& w) {
   hipFree(w.qk_sorted);
   hipFree(w.v_sorted);
   hipFree(w.stats);
+  hipFree(w.knorm);
   hipFree(w.hash.rh);
   hipFree(w.hash.rt);
   hipFree(w.hash.bounds);
@@ -113,6 +114,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
             alloc(&w.lse, rows * 4, t) &&
             alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
             alloc(&w.stats, 2 * 8, t);
+  if (ok && lsh::attend_mfma_supported(p)) ok = alloc(&w.knorm, p.n_token_heads() * 4, t);
   if (ok && lsh::hash_mfma_supported(p)) {
     const int64_t hp = lsh::hash_half_pad(p);
     if (hipDeviceGetAttribute(&w.hash.n_cu, hipDeviceAttributeMultiprocessorCount, h->device) !=
@@ -168,9 +170,10 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   mark(0);
   if (e == hipSuccess) {
     if (mfma_hash) {
-      e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, s,
+      e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, w.knorm, s,
                                 ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
     } else {
+      if (w.knorm) e = lsh::launch_key_norms(p, qk, w.knorm, s);
       mark(1);
       e = lsh::launch_hash_exact(p, qk, rotations, w.buckets, buckets, s);
       mark(2);
@@ -185,7 +188,7 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   mark(5);
   if (e == hipSuccess)
     e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
-                           separate ? w.v_sorted : nullptr, pm, (float*)w.o, ls, s);
+                           separate ? w.v_sorted : nullptr, pm, w.knorm, (float*)w.o, ls, s);
   mark(6);
   if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, s);
   mark(7);
