@@ -6,14 +6,19 @@
 // bucket id alone yields exactly the (bucket, position) order; no pass over
 // the position bits is needed.
 //
-// Three phases over tiles of kSortTile positions (one wave per tile):
-//   count:   counts[seg][tile][b] = how many positions of the tile are in b;
+// Three phases over tiles of kSortTile positions (one 4-wave workgroup per
+// tile; wave w owns the tile's positions 256w .. 256w + 255):
+//   count:   counts[seg][tile][b] = how many positions of the tile are in b
+//            (LDS atomic adds; the order of the adds does not matter);
 //   scan:    offsets[seg][tile][b] = sum of all counts of buckets < b plus the
 //            counts of bucket b in earlier tiles: the first output slot of the
 //            tile's positions in bucket b;
-//   scatter: every position gets slot = offset + (number of earlier positions
-//            of the same tile in b), computed with wave ballots over the
-//            bucket bits (lanes holding equal ids find each other).
+//   scatter: each wave first counts its own positions per bucket; a prefix
+//            over the waves turns the tile offset into per-wave offsets; then
+//            every position gets slot = its wave's offset + (number of earlier
+//            positions of the same wave in b), found with wave ballots over
+//            the bucket bits (lanes holding equal ids find each other), 64
+//            positions at a time in position order.
 // Buckets are handled in LDS windows of at most kLdsBins ids, so any
 // n_buckets up to 65536 works with a bounded LDS footprint.
 #include "internal.h"
@@ -21,7 +26,11 @@
 namespace lsh {
 namespace {
 
-constexpr int kLdsBins = 8192;
+constexpr int kLdsBins = 2048;
+constexpr int kSortThreads = 256;
+constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kPerThread = kSortTile / kSortThreads;  // positions per thread
+static_assert(kPerThread * kSortThreads == kSortTile, "tile covered by the workgroup");
 
 // Mask of active lanes whose key equals this lane's key.
 __device__ __forceinline__ uint64_t match_peers(uint32_t key, bool active, int nbits) {
@@ -34,57 +43,70 @@ __device__ __forceinline__ uint64_t match_peers(uint32_t key, bool active, int n
   return peers;
 }
 
-__global__ __launch_bounds__(64) void k_sort_count(const uint16_t* __restrict__ buckets,
-                                                   uint32_t* __restrict__ counts, int L, int nb,
-                                                   int tiles, int nbits) {
+// Thread (w, lane) takes positions begin + 256w + 64k + lane, k = 0..3: in
+// position order per wave, one coalesced 128-byte read per wave and k.
+__device__ __forceinline__ void load_tile(const uint16_t* bk, int begin, int end, uint32_t* b,
+                                          int* e) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int k = 0; k < kPerThread; ++k) {
+    e[k] = begin + kWave * (kPerThread * w + k) + lane;
+    b[k] = e[k] < end ? bk[e[k]] : 0u;
+  }
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint16_t* __restrict__ buckets,
+                                                             uint32_t* __restrict__ counts, int L,
+                                                             int nb, int tiles) {
   extern __shared__ uint32_t cnt[];
   const int tile = (int)(blockIdx.x % (unsigned)tiles);
   const int64_t seg = blockIdx.x / (unsigned)tiles;
-  const int lane = threadIdx.x;
-  const uint16_t* bk = buckets + seg * L;
+  const int tid = threadIdx.x;
   uint32_t* cs = counts + (seg * tiles + tile) * (int64_t)nb;
   const int begin = tile * kSortTile;
   const int end = min(L, begin + kSortTile);
+  uint32_t b[kPerThread];
+  int e[kPerThread];
+  load_tile(buckets + seg * L, begin, end, b, e);
   const int window = min(nb, kLdsBins);
   for (int base = 0; base < nb; base += window) {
     const int span = min(window, nb - base);
-    for (int b = lane; b < span; b += kWave) cnt[b] = 0;
+    for (int j = tid; j < span; j += kSortThreads) cnt[j] = 0;
     __syncthreads();
-    for (int e0 = begin; e0 < end; e0 += kWave) {
-      const int e = e0 + lane;
-      const uint32_t b = e < end ? bk[e] : 0u;
-      const bool in = e < end && (int)b >= base && (int)b < base + span;
-      const uint64_t peers = match_peers(b, in, nbits);
-      if (in && lane == __builtin_ctzll(peers)) cnt[b - base] += (uint32_t)__popcll(peers);
-    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+      if (e[k] < end && (int)b[k] >= base && (int)b[k] < base + span) atomicAdd(&cnt[b[k] - base], 1u);
     __syncthreads();
-    for (int b = lane; b < span; b += kWave) cs[base + b] = cnt[b];
+    for (int j = tid; j < span; j += kSortThreads) cs[base + j] = cnt[j];
     __syncthreads();
   }
 }
 
 // One block per segment. Buckets are taken 1024 at a time, one per thread:
-// first the running count over tiles (the tile's offset inside its bucket),
-// then a block-wide exclusive scan of the bucket totals gives the bucket's
-// first slot, which is added to every tile of the bucket.
+// first the bucket's total over the tiles, then a block-wide exclusive scan
+// of the totals gives the bucket's first slot, and a second pass over the
+// tiles replaces every count with the running slot. Counts are read 16 tiles
+// at a time, all loads of a batch issued before any use.
 __global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ counts, int nb,
                                                     int tiles) {
+  constexpr int kBatch = 16;
   __shared__ uint32_t part[1024];
   const int tid = threadIdx.x;
   uint32_t* c = counts + (int64_t)blockIdx.x * nb * tiles;
   uint32_t carry = 0;
   for (int b0 = 0; b0 < nb; b0 += 1024) {
     const int b = b0 + tid;
-    uint32_t run = 0;
+    uint32_t total = 0;
     if (b < nb) {
-      for (int t = 0; t < tiles; ++t) {
-        uint32_t* p = c + (int64_t)t * nb + b;
-        const uint32_t x = *p;
-        *p = run;
-        run += x;
+      for (int t0 = 0; t0 < tiles; t0 += kBatch) {
+        uint32_t x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb + b] : 0u;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) total += x[u];
       }
     }
-    part[tid] = run;
+    part[tid] = total;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
       const uint32_t add = tid >= off ? part[tid - off] : 0u;
@@ -92,44 +114,72 @@ __global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ count
       part[tid] += add;
       __syncthreads();
     }
-    const uint32_t base = carry + part[tid] - run;  // exclusive
-    if (b < nb)
-      for (int t = 0; t < tiles; ++t) c[(int64_t)t * nb + b] += base;
+    uint32_t run = carry + part[tid] - total;  // exclusive
+    if (b < nb) {
+      for (int t0 = 0; t0 < tiles; t0 += kBatch) {
+        uint32_t x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb + b] : 0u;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (t0 + u < tiles) c[(int64_t)(t0 + u) * nb + b] = run;
+          run += x[u];
+        }
+      }
+    }
     carry += part[1023];
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(64) void k_sort_scatter(const uint16_t* __restrict__ buckets,
-                                                     const uint32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ perm, int L, int nb,
-                                                     int tiles, int nbits) {
-  extern __shared__ uint32_t next[];
+__global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
+    const uint16_t* __restrict__ buckets, const uint32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int L, int nb, int tiles, int nbits) {
+  extern __shared__ uint32_t next[];  // [wave][window]
   const int tile = (int)(blockIdx.x % (unsigned)tiles);
   const int64_t seg = blockIdx.x / (unsigned)tiles;
-  const int lane = threadIdx.x;
-  const uint16_t* bk = buckets + seg * L;
+  const int tid = threadIdx.x;
+  const int w = tid / kWave, lane = tid % kWave;
   const uint32_t* os = offsets + (seg * tiles + tile) * (int64_t)nb;
   int32_t* pm = perm + seg * L;
   const int begin = tile * kSortTile;
   const int end = min(L, begin + kSortTile);
   const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t b[kPerThread];
+  int e[kPerThread];
+  load_tile(buckets + seg * L, begin, end, b, e);
   const int window = min(nb, kLdsBins);
   for (int base = 0; base < nb; base += window) {
     const int span = min(window, nb - base);
-    for (int b = lane; b < span; b += kWave) next[b] = os[base + b];
+    uint32_t* mine = next + w * span;
+    for (int j = tid; j < kSortWaves * span; j += kSortThreads) next[j] = 0;
     __syncthreads();
-    for (int e0 = begin; e0 < end; e0 += kWave) {
-      const int e = e0 + lane;
-      const uint32_t b = e < end ? bk[e] : 0u;
-      const bool in = e < end && (int)b >= base && (int)b < base + span;
-      const uint64_t peers = match_peers(b, in, nbits);
-      if (in) {
-        const uint32_t slot = next[b - base] + (uint32_t)__popcll(peers & below);
-        pm[slot] = e;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+      if (e[k] < end && (int)b[k] >= base && (int)b[k] < base + span)
+        atomicAdd(&mine[b[k] - base], 1u);
+    __syncthreads();
+    for (int j = tid; j < span; j += kSortThreads) {
+      uint32_t run = os[base + j];
+#pragma unroll
+      for (int ww = 0; ww < kSortWaves; ++ww) {
+        const uint32_t n = next[ww * span + j];
+        next[ww * span + j] = run;
+        run += n;
       }
-      // all lanes have read next[] above; the group's first lane advances it
-      if (in && lane == __builtin_ctzll(peers)) next[b - base] += (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const bool in = e[k] < end && (int)b[k] >= base && (int)b[k] < base + span;
+      const uint64_t peers = match_peers(b[k], in, nbits);
+      if (in) {
+        const uint32_t slot = mine[b[k] - base] + (uint32_t)__popcll(peers & below);
+        pm[slot] = e[k];
+      }
+      // all lanes have read the wave's counter above; the group's first lane
+      // advances it
+      if (in && lane == __builtin_ctzll(peers)) mine[b[k] - base] += (uint32_t)__popcll(peers);
     }
     __syncthreads();
   }
@@ -143,13 +193,13 @@ hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* coun
   int nbits = 0;
   while ((1 << nbits) < p.nb) ++nbits;
   const dim3 grid((unsigned)(tiles * p.nseg()));
-  const size_t lds = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins) * 4;
-  hipLaunchKernelGGL(k_sort_count, grid, dim3(kWave), lds, s, buckets, counts, p.L, p.nb, tiles,
-                     nbits);
+  const size_t window = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins);
+  hipLaunchKernelGGL(k_sort_count, grid, dim3(kSortThreads), window * 4, s, buckets, counts, p.L,
+                     p.nb, tiles);
   hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)p.nseg()), dim3(1024), 0, s, counts, p.nb,
                      tiles);
-  hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kWave), lds, s, buckets, counts, perm, p.L,
-                     p.nb, tiles, nbits);
+  hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kSortThreads), kSortWaves * window * 4, s,
+                     buckets, counts, perm, p.L, p.nb, tiles, nbits);
   return hipGetLastError();
 }
 
