@@ -76,26 +76,28 @@ struct Lds {
 __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
 
 // One chunk's rows in flight between the loads and the staging. Thread t
-// loads pieces kQ (t % kTpr) .. of qk row t / kTpr and, for t < kVUsers,
-// 8 dims (piece t % kSegs) of the 4 v rows of group t / kSegs.
+// loads 16 bytes (piece t % kSegs) of qk rows t / kSegs + kRowStep k and, for
+// t < kVUsers, of the 4 v rows of group t / kSegs: each load instruction of a
+// wave reads whole rows. Threads t < 64 also load the squared norm of row t.
 template <int D>
 struct ChunkRegs {
-  static constexpr int kPieces = D / 8;                    // uint4 per row
-  static constexpr int kSegs = D / 8;                      // 8-dim pieces per row
-  static constexpr int kQ = kChunk * kPieces / kThreads;   // qk pieces per thread
-  static constexpr int kTpr = kPieces / kQ;                // threads per qk row
+  static constexpr int kSegs = D / 8;                      // 16-byte pieces per row
+  static constexpr int kRowStep = kThreads / kSegs;        // rows per load instruction set
+  static constexpr int kQ = kChunk / kRowStep;             // qk rows per thread
   static constexpr int kVUsers = (kChunk / 4) * kSegs;     // (4-key group, piece) pairs
   static_assert(kVUsers <= kThreads, "one v group piece per thread");
+  static_assert(kQ * kRowStep == kChunk, "qk rows covered");
   uint4 qk[kQ];
   uint4 v[4];
-  int pos;
-  float n2;  // squared norm of qk row t / kTpr
+  int pos;   // original position of row t % 64
+  float n2;  // squared norm of qk row t (t < 64)
 };
 
 // permutation entries (original positions) a chunk's loads need
 template <int D>
 struct PermRegs {
   int pos;
+  int qpos[ChunkRegs<D>::kQ];
   int vpos[4];
 };
 
@@ -104,7 +106,9 @@ template <int D>
 __device__ __forceinline__ void read_perm(PermRegs<D>& pr, const int* pn) {
   using CR = ChunkRegs<D>;
   const int t = threadIdx.x;
-  pr.pos = pn[t / CR::kTpr];
+  pr.pos = pn[t % kChunk];
+#pragma unroll
+  for (int k = 0; k < CR::kQ; ++k) pr.qpos[k] = pn[t / CR::kSegs + CR::kRowStep * k];
   const int qd = (t < CR::kVUsers ? t : 0) / CR::kSegs;
   const int4 q4 = *(const int4*)(pn + qd * 4);
   pr.vpos[0] = q4.x;
@@ -125,20 +129,21 @@ __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& 
   constexpr uint32_t kRowBytes = D * 2;
   const int t = threadIdx.x;
   const int64_t base_row = SORTED ? sorted_row0 + c * kChunk : row0;
-  const unsigned char* qb = (const unsigned char*)(qk_rows + base_row * CR::kPieces);
-  const unsigned char* vb = (const unsigned char*)(v_rows + base_row * CR::kPieces);
-  const int r = t / CR::kTpr, qt = t % CR::kTpr;
-  const uint32_t qoff = (uint32_t)(SORTED ? r : pr.pos) * kRowBytes + qt * (CR::kQ * 16);
+  const unsigned char* qb = (const unsigned char*)(qk_rows + base_row * CR::kSegs);
+  const unsigned char* vb = (const unsigned char*)(v_rows + base_row * CR::kSegs);
   const int qd = t / CR::kSegs, sg = t % CR::kSegs;
-  uint32_t voff[4];
+  uint32_t qoff[CR::kQ], voff[4];
+#pragma unroll
+  for (int k = 0; k < CR::kQ; ++k)
+    qoff[k] = (uint32_t)(SORTED ? qd + CR::kRowStep * k : pr.qpos[k]) * kRowBytes + sg * 16;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     voff[k] = (uint32_t)(SORTED ? qd * 4 + k : pr.vpos[k]) * kRowBytes + sg * 16;
   cr.pos = pr.pos;
   __builtin_amdgcn_sched_barrier(0);
-  cr.n2 = knorm[row0 + pr.pos];
+  if (t < kChunk) cr.n2 = knorm[row0 + pr.pos];
 #pragma unroll
-  for (int k = 0; k < CR::kQ; ++k) cr.qk[k] = *(const uint4*)(qb + qoff + k * 16);
+  for (int k = 0; k < CR::kQ; ++k) cr.qk[k] = *(const uint4*)(qb + qoff[k]);
   if (t < CR::kVUsers) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) cr.v[k] = *(const uint4*)(vb + voff[k]);
@@ -151,23 +156,22 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
   using CR = ChunkRegs<D>;
   const int t = threadIdx.x;
   {
-    const int r = t / CR::kTpr, qt = t % CR::kTpr;
-    uint4* dst = (uint4*)(lds + Lay::kKt + (sl * kChunk + r) * Lay::kRow + qt * (CR::kQ * 16));
+    const int qd = t / CR::kSegs, sg = t % CR::kSegs;
     // (each piece passes through a register-only asm statement, so the copy
     // cannot become a memcpy from a stack copy of the registers)
 #pragma unroll
     for (int k = 0; k < CR::kQ; ++k) {
       uint4 x = cr.qk[k];
       asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
-      dst[k] = x;
+      *(uint4*)(lds + Lay::kKt + (sl * kChunk + qd + CR::kRowStep * k) * Lay::kRow + sg * 16) = x;
     }
-    if (qt == 0) {
+    if (t < kChunk) {
       const float nn = cr.n2;
       const float nrm = sqrtf(nn);
       const float sc = kLog2e / sqrtf((float)D);
-      ((float*)(lds + Lay::kScale))[sl * kChunk + r] = nn > 0.f ? sc / nrm : 0.f;
-      ((int*)(lds + Lay::kPos))[sl * kChunk + r] = cr.pos;
-      ((float*)(lds + Lay::kBound))[sl * kChunk + r] = sc * nrm;
+      ((float*)(lds + Lay::kScale))[sl * kChunk + t] = nn > 0.f ? sc / nrm : 0.f;
+      ((int*)(lds + Lay::kPos))[sl * kChunk + t] = cr.pos;
+      ((float*)(lds + Lay::kBound))[sl * kChunk + t] = sc * nrm;
     }
   }
   // v rows, 4 keys x 8 dims per piece, stored as [group][dim][4 keys]
@@ -187,15 +191,9 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
   }
 }
 
-// 4 consecutive outputs (fp16: saturated to the finite range)
+// 4 consecutive fp32 outputs
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *(float4*)p = make_float4(a, b, c, d);
-}
-__device__ __forceinline__ void store4(_Float16* p, float a, float b, float c, float d) {
-  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-  const f16x2_t lo = {(_Float16)sat16(a), (_Float16)sat16(b)};
-  const f16x2_t hi = {(_Float16)sat16(c), (_Float16)sat16(d)};
-  *(uint2*)p = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 // LDS allows two workgroups (8 waves) per CU at d = 128, so each wave may take
@@ -205,14 +203,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
     const uint4* __restrict__ v_s, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
-    int nseg, int chunks_per_wg) {
+    int nseg, int chunks_per_wg, int ranges, int group_segs) {
   using Lay = Lds<D>;
   constexpr int KS = D / 32;  // 32-dim K-steps of QK^T
   constexpr int DT = D / 16;  // 16-dim tiles of the output
   extern __shared__ __align__(16) unsigned char lds[];
   const int nchunks = L / kChunk;
-  const int64_t seg = blockIdx.x % (unsigned)nseg;
-  const int range = blockIdx.x / (unsigned)nseg;
+  // Blocks walk groups of group_segs segments (all rounds of a few heads),
+  // the segments of a group interleaved, so the workgroups in flight read
+  // the rows of few heads, which then stay in the memory-side cache for the
+  // other rounds.
+  const int group = blockIdx.x / (unsigned)(group_segs * ranges);
+  const int first = group * group_segs;
+  const int gn = min(group_segs, nseg - first);
+  const int inner = blockIdx.x - group * group_segs * ranges;
+  const int64_t seg = first + inner % gn;
+  const int range = inner / gn;
   const int c0 = range * chunks_per_wg;
   const int c1 = min(nchunks, c0 + chunks_per_wg);
   if (c0 >= c1) return;
@@ -386,17 +392,46 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     // normalise and scatter to the query's original position: lane holds dims
     // 16t + 4g + 0..3; a query that saw only itself stores nothing (the round
-    // combination takes v_i for it)
+    // combination takes v_i for it). The four lanes of a query agree on l.
     {
       const float l = lacc[0];
       const bool seen = l > 0.f;
-      if (seen) {
-        const float inv = 1.0f / l;
-        OT* orow = o + (seg * L + posq) * D + 4 * g;
+      const float inv = seen ? 1.0f / l : 0.f;
+      OT* orow = o + (seg * L + posq) * D;
+      if constexpr (sizeof(OT) == 2) {
+        // fp16: tiles t and t + 1 packed as 2 words per lane, then one swap of
+        // odd and even 16-lane rows leaves lane group g with 8 consecutive
+        // dims, 16(t + g%2) + 8(g/2) + 0..7, one 16-byte store per tile pair
+        uint32_t pk[DT][2];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          store4(orow + dt * 16, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
-                 oacc[dt][3] * inv);
+        for (int dt = 0; dt < DT; ++dt) {
+          typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+          const f16x2_t lo = {(_Float16)sat16(oacc[dt][0] * inv), (_Float16)sat16(oacc[dt][1] * inv)};
+          const f16x2_t hi = {(_Float16)sat16(oacc[dt][2] * inv), (_Float16)sat16(oacc[dt][3] * inv)};
+          pk[dt][0] = __builtin_bit_cast(uint32_t, lo);
+          pk[dt][1] = __builtin_bit_cast(uint32_t, hi);
+        }
+        uint4 st[DT / 2];
+#pragma unroll
+        for (int j = 0; j < DT / 2; ++j) {
+          const auto r0 = __builtin_amdgcn_permlane16_swap(pk[2 * j][0], pk[2 * j + 1][0], false, false);
+          const auto r1 = __builtin_amdgcn_permlane16_swap(pk[2 * j][1], pk[2 * j + 1][1], false, false);
+          // even g: words of tile 2j from lanes g, g + 1; odd g: tile 2j + 1
+          // from lanes g - 1, g
+          st[j] = make_uint4(r0[0], r1[0], r0[1], r1[1]);
+        }
+        if (seen) {
+#pragma unroll
+          for (int j = 0; j < DT / 2; ++j)
+            *(uint4*)(orow + 32 * j + 16 * (g & 1) + 8 * (g >> 1)) = st[j];
+        }
+      } else {
+        if (seen) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            store4(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv,
+                   oacc[dt][2] * inv, oacc[dt][3] * inv);
+        }
       }
       if (g == 0) lse[seg * L + posq] = seen ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
     }
@@ -404,22 +439,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+// Chunks per workgroup, and workgroups in flight the grid order is shaped for
+// (two per CU on 256 CUs).
+constexpr int kRangeChunks = 16;
+constexpr int kResidentBlocks = 512;
+
 template <int D, typename OT, bool CAUSAL, bool SORTED>
 void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_s,
                 const void* v_s, const int32_t* perm, const float* knorm, OT* o, float* lse, hipStream_t s) {
   const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
-  const int64_t target = 1024;
-  int64_t ranges = (target + nseg - 1) / nseg;
-  if (ranges > nchunks) ranges = nchunks;
-  if (ranges < 1) ranges = 1;
-  const int per = (int)((nchunks + ranges - 1) / ranges);
-  ranges = (nchunks + per - 1) / per;
+  const int per = nchunks < kRangeChunks ? nchunks : kRangeChunks;
+  const int ranges = (nchunks + per - 1) / per;
+  // whole heads (all their rounds) per group, enough to fill the resident set
+  int64_t heads = (kResidentBlocks + (int64_t)ranges * p.R - 1) / ((int64_t)ranges * p.R);
+  if (heads < 1) heads = 1;
+  int64_t group_segs = heads * p.R;
+  if (group_segs > nseg) group_segs = nseg;
   const size_t shmem = Lds<D>::kBytes;
   hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED>), dim3((unsigned)(nseg * ranges)),
                      dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
                      (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse, p.L,
-                     p.R, (int)nseg, per);
+                     p.R, (int)nseg, per, ranges, (int)group_segs);
 }
 
 template <int D, typename OT>
