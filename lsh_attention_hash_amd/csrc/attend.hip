@@ -23,7 +23,7 @@ template <int D, typename T>
 __global__ __launch_bounds__(256) void k_attend_simple(
     const T* __restrict__ qk, const T* __restrict__ v, const T* __restrict__ qk_s,
     const T* __restrict__ v_s, const int32_t* __restrict__ perm, float* __restrict__ o,
-    float* __restrict__ lse, int L, int m, int R, int causal) {
+    float* __restrict__ lse, int L, int m, int R, int causal, int64_t o_seg_rows) {
   if ((int)threadIdx.x >= m) return;
   const int nchunks = L / m;
   const int64_t seg = blockIdx.x / (unsigned)nchunks;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_attend_simple(
     for (int u = 0; u < D; ++u) acc[u] = acc[u] * corr + pj * to_f32(vrow[u]);
     mx = mnew;
   }
-  float* orow = o + (seg * L + i) * D;
+  float* orow = o + (seg * o_seg_rows + i) * D;
   const float inv_l = 1.0f / l;
 #pragma unroll
   for (int u = 0; u < D; ++u) orow[u] = acc[u] * inv_l;
@@ -79,7 +79,7 @@ void launch_simple(const Problem& p, const void* qk, const void* v, const void* 
   const int block = ((p.m + kWave - 1) / kWave) * kWave;
   hipLaunchKernelGGL((k_attend_simple<D, T>), grid, dim3(block), 0, s, (const T*)qk,
                      (const T*)v, (const T*)qk_s, (const T*)v_s, perm, o, lse, p.L, p.m, p.R,
-                     p.causal);
+                     p.causal, p.o_seg_rows());
 }
 
 }  // namespace

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
     const uint4* __restrict__ v_s, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
-    int nseg, int chunks_per_wg, int ranges, int group_segs) {
+    int nseg, int chunks_per_wg, int ranges, int group_segs, int64_t o_seg_rows) {
   using Lay = Lds<D>;
   constexpr int KS = D / 32;  // 32-dim K-steps of QK^T
   constexpr int DT = D / 16;  // 16-dim tiles of the output
@@ -391,13 +391,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       if (c + 2 < c1 && threadIdx.x < kChunk) pn[threadIdx.x] = pnext;
     }
     // normalise and scatter to the query's original position: lane holds dims
-    // 16t + 4g + 0..3; a query that saw only itself stores nothing (the round
-    // combination takes v_i for it). The four lanes of a query agree on l.
+    // 16t + 4g + 0..3. A query that saw only itself (l == 0) stores zeros (its
+    // accumulators are 0); the round combination takes v_i for it.
     {
       const float l = lacc[0];
       const bool seen = l > 0.f;
       const float inv = seen ? 1.0f / l : 0.f;
-      OT* orow = o + (seg * L + posq) * D;
+      OT* orow = o + (seg * o_seg_rows + posq) * D;
       if constexpr (sizeof(OT) == 2) {
         // fp16: tiles t and t + 1 packed as 2 words per lane, then one swap of
         // odd and even 16-lane rows leaves lane group g with 8 consecutive
@@ -420,18 +420,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           // from lanes g - 1, g
           st[j] = make_uint4(r0[0], r1[0], r0[1], r1[1]);
         }
-        if (seen) {
 #pragma unroll
-          for (int j = 0; j < DT / 2; ++j)
-            *(uint4*)(orow + 32 * j + 16 * (g & 1) + 8 * (g >> 1)) = st[j];
-        }
+        for (int j = 0; j < DT / 2; ++j)
+          *(uint4*)(orow + 32 * j + 16 * (g & 1) + 8 * (g >> 1)) = st[j];
       } else {
-        if (seen) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            store4(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv,
-                   oacc[dt][2] * inv, oacc[dt][3] * inv);
-        }
+        for (int dt = 0; dt < DT; ++dt)
+          store4(orow + dt * 16 + 4 * g, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
+                 oacc[dt][3] * inv);
       }
       if (g == 0) lse[seg * L + posq] = seen ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
     }
@@ -460,7 +456,7 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
   hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED>), dim3((unsigned)(nseg * ranges)),
                      dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
                      (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse, p.L,
-                     p.R, (int)nseg, per, ranges, (int)group_segs);
+                     p.R, (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows());
 }
 
 template <int D, typename OT>

@@ -9,8 +9,8 @@
 // The per-round rows are already at original positions (the attention kernel
 // scatters them), so this kernel streams them in order. A round whose
 // logsumexp is the self-only value -1e5 has output v_i by definition; that row
-// is taken from v (the attention kernel need not write it), selected rather
-// than weighted so that nothing else in the slot can leak in.
+// is taken from v, the round's own row (finite, zeros on the matrix-core path)
+// entering with weight 0.
 #include <type_traits>
 
 #include "dtype.h"
@@ -52,17 +52,20 @@ __device__ __forceinline__ void store8(bf16_t* p, const float* x) {
   *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
 }
 
-// Each lane owns 8 consecutive dims of one row; D/8 lanes cover a row. Rounds
-// are taken kG at a time (kG = R when R is 1, 2, 4 or 8; else 4 with a guard),
-// all their loads issued before any use.
-template <int D, typename OutT, typename OT, typename VT, int kG>
+// Each lane owns 8 consecutive dims of one row; D/8 lanes cover a row.
+// kR > 0: R == kR, every round's logsumexp and row loaded before any use.
+// kR == 0 (other round counts): rounds taken 4 at a time, a first pass over
+// the logsumexps for the max, then the rows.
+template <int D, typename OutT, typename OT, typename VT, int kR>
 __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
                                                  const float* __restrict__ lse,
                                                  const VT* __restrict__ v,
-                                                 OutT* __restrict__ out, int L, int R,
-                                                 int64_t n_rows) {
+                                                 OutT* __restrict__ out, int L, int R_rt,
+                                                 int64_t n_rows, int64_t o_seg_rows) {
   constexpr int kLpr = D / 8;             // lanes per row
   constexpr int kRpb = 256 / kLpr;        // rows per block
+  constexpr int kG = kR > 0 ? kR : 4;     // rounds per group
+  const int R = kR > 0 ? kR : R_rt;
   const int sub = threadIdx.x % kLpr;
   const int64_t stride = (int64_t)gridDim.x * kRpb;
   for (int64_t row = (int64_t)blockIdx.x * kRpb + threadIdx.x / kLpr; row < n_rows;
@@ -70,34 +73,49 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
     const int64_t bh = row / L;
     const int64_t i = row - bh * L;
     const float* lr = lse + bh * R * L + i;
-    const OT* orow = o + (bh * R * L + i) * D + sub * 8;
+    const OT* orow = o + (bh * R * o_seg_rows + i) * D + sub * 8;
     float mx = -INFINITY;
-    for (int r0 = 0; r0 < R; r0 += kG) {
-      float lv[kG];
-#pragma unroll
-      for (int u = 0; u < kG; ++u) lv[u] = r0 + u < R ? lr[(int64_t)(r0 + u) * L] : -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kG; ++u) mx = fmaxf(mx, lv[u]);
-    }
     float sum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wself = 0.f;  // weight of the self-only rounds
-    for (int r0 = 0; r0 < R; r0 += kG) {
-      float lv[kG], x[kG][8];
-#pragma unroll
-      for (int u = 0; u < kG; ++u) {
-        const bool in = r0 + u < R;
-        lv[u] = in ? lr[(int64_t)(r0 + u) * L] : -INFINITY;
-        if (in) load8(orow + (int64_t)(r0 + u) * L * D, x[u]);
-      }
+    // rounds r0 .. r0 + kG - 1 given their logsumexps and rows, mx final
+    auto accumulate = [&](int r0, const float* lv, float (*x)[8]) {
 #pragma unroll
       for (int u = 0; u < kG; ++u) {
         const float w = __expf(lv[u] - mx);  // 0 for rounds past R
         const bool self_only = lv[u] == kSelfLogit;
         sum += w;
         wself += self_only ? w : 0.f;
-        const float wo = self_only || r0 + u >= R ? 0.f : w;
+        const float wo = self_only ? 0.f : w;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wo, wo != 0.f ? x[u][j] : 0.f, acc[j]);
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wo, x[u][j], acc[j]);
+      }
+    };
+    if constexpr (kR > 0) {
+      float lv[kR], x[kR][8];
+#pragma unroll
+      for (int u = 0; u < kR; ++u) lv[u] = lr[(int64_t)u * L];
+#pragma unroll
+      for (int u = 0; u < kR; ++u) load8(orow + u * o_seg_rows * D, x[u]);
+#pragma unroll
+      for (int u = 0; u < kR; ++u) mx = fmaxf(mx, lv[u]);
+      accumulate(0, lv, x);
+    } else {
+      for (int r0 = 0; r0 < R; r0 += kG) {
+        float lv[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) lv[u] = r0 + u < R ? lr[(int64_t)(r0 + u) * L] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kG; ++u) mx = fmaxf(mx, lv[u]);
+      }
+      for (int r0 = 0; r0 < R; r0 += kG) {
+        float lv[kG], x[kG][8] = {};
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+          const bool in = r0 + u < R;
+          lv[u] = in ? lr[(int64_t)(r0 + u) * L] : -INFINITY;  // weight 0 past R
+          if (in) load8(orow + (r0 + u) * o_seg_rows * D, x[u]);
+        }
+        accumulate(r0, lv, x);
       }
     }
     const float inv_sum = 1.0f / sum;
@@ -124,16 +142,18 @@ void launch_t(const Problem& p, const OT* o, const float* lse, const VT* v, void
     constexpr int G = decltype(g)::value;
     if (p.out_dtype == LSH_ATTN_BF16)
       hipLaunchKernelGGL((k_combine<D, bf16_t, OT, VT, G>), dim3(blocks), dim3(256), 0, s, o, lse,
-                         v, (bf16_t*)out, p.L, p.R, n);
+                         v, (bf16_t*)out, p.L, p.R, n, p.o_seg_rows());
     else
       hipLaunchKernelGGL((k_combine<D, float, OT, VT, G>), dim3(blocks), dim3(256), 0, s, o, lse,
-                         v, (float*)out, p.L, p.R, n);
+                         v, (float*)out, p.L, p.R, n, p.o_seg_rows());
   };
   switch (p.R) {
     case 1: go(std::integral_constant<int, 1>{}); break;
     case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
     case 8: go(std::integral_constant<int, 8>{}); break;
-    default: go(std::integral_constant<int, 4>{}); break;
+    default: go(std::integral_constant<int, 0>{}); break;
   }
 }
 

@@ -18,12 +18,18 @@ constexpr int kWave = 64;
 // Elements of one (segment, tile) in the sort's histogram and scatter phases.
 constexpr int kSortTile = 1024;
 
+// Rows of padding after each segment's per-round outputs. With L a power of
+// two the rounds of one position would otherwise lie a power of two apart,
+// and the round combination's loads of them would meet in one DRAM bank.
+constexpr int kORowPad = 17;
+
 struct Problem {
   int B, H, L, d, nb, R, m, causal, dtype, out_dtype, flags;
   int64_t nbh() const { return (int64_t)B * H; }
   int64_t nseg() const { return nbh() * R; }           // (batch, head, round) segments
   int64_t n_token_heads() const { return nbh() * L; }
   int64_t n_rows() const { return nseg() * L; }        // (segment, position) pairs
+  int64_t o_seg_rows() const { return (int64_t)L + kORowPad; }  // o rows per segment
   int half() const { return nb / 2; }
   int sort_tiles() const { return (L + kSortTile - 1) / kSortTile; }
 };
@@ -45,7 +51,7 @@ struct HashScratch {
 struct Workspace {
   uint16_t* buckets = nullptr;     // [seg, L]
   int32_t* perm = nullptr;         // [seg, L] sorted slot -> position
-  void* o = nullptr;               // [seg, L, d] per-round outputs at original positions
+  void* o = nullptr;               // [seg, L + kORowPad, d] per-round outputs at original positions
                                    // (fp16, or fp32 with the fp32 flag / plain kernel)
   float* lse = nullptr;            // [seg, L]
   uint32_t* sort_counts = nullptr; // [seg, tiles, nb] counts, then first output slots

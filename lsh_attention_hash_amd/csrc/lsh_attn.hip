@@ -110,7 +110,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   lsh::Workspace& w = h->ws;
   int64_t& t = h->bytes;
   bool ok = alloc(&w.buckets, rows * 2, t) && alloc(&w.perm, rows * 4, t) &&
-            alloc(&w.o, rows * p.d * (lsh::round_outputs_half(p) ? 2 : 4), t) &&
+            alloc(&w.o, p.nseg() * p.o_seg_rows() * p.d * (lsh::round_outputs_half(p) ? 2 : 4), t) &&
             alloc(&w.lse, rows * 4, t) &&
             alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
             alloc(&w.stats, 2 * 8, t);

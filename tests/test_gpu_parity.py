@@ -49,6 +49,8 @@ SMALL = [
     W("image12k", batch=2, heads=2, seq_len=768, n_buckets=12, n_rounds=4),
     W("c4k", batch=1, heads=1, seq_len=64, n_buckets=4, n_rounds=2, causal=True),   # one chunk
     W("c4k", batch=1, heads=2, seq_len=512, n_buckets=1024, n_rounds=1, causal=False),  # nb > L
+    # a round count the combination has no specialisation for (groups of 4 + 1)
+    W("image12k", batch=1, heads=2, seq_len=1024, n_buckets=16, n_rounds=5, causal=True),
     # bucket ids beyond one LDS window of the sort's histograms
     W("c4k", batch=1, heads=1, seq_len=4096, n_buckets=8192, n_rounds=2, causal=True),
     W("c4k", batch=1, heads=1, seq_len=1024, n_buckets=65536, n_rounds=1, causal=False),  # max nb
