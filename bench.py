@@ -164,8 +164,8 @@ def cpu_baseline(w, inp, heads: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="text64k")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--separate-gather", action="store_true")

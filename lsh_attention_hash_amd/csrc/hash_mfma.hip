@@ -76,16 +76,27 @@ __global__ __launch_bounds__(256) void k_hash_prep(const float* __restrict__ rot
   const int r = blockIdx.x / (unsigned)ntiles;
   const int col = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int k = kt * 32 + col;
+  // every load issued before the first use
+  float xs[kPrepMaxD / 8];
+#pragma unroll
+  for (int i = 0; i < kPrepMaxD / 8; ++i) {
+    const int u = grp + 8 * i;
+    xs[i] = u < d && k < half ? rot[((int64_t)r * d + u) * half + k] : 0.f;
+  }
   double sh = 0.0, slo = 0.0, sr = 0.0;
-  for (int u = grp; u < d; u += 8) {
-    const float x = k < half ? rot[((int64_t)r * d + u) * half + k] : 0.f;
-    const float h = f16_round(x);
-    th[col][u] = (_Float16)h;
-    tx[col][u] = x;
-    const double hd = h, xd = x;
-    sh += hd * hd;
-    slo += (xd - hd) * (xd - hd);
-    sr += xd * xd;
+#pragma unroll
+  for (int i = 0; i < kPrepMaxD / 8; ++i) {
+    const int u = grp + 8 * i;
+    if (u < d) {
+      const float x = xs[i];
+      const float h = f16_round(x);
+      th[col][u] = (_Float16)h;
+      tx[col][u] = x;
+      const double hd = h, xd = x;
+      sh += hd * hd;
+      slo += (xd - hd) * (xd - hd);
+      sr += xd * xd;
+    }
   }
   red[0][grp][col] = sh;
   red[1][grp][col] = slo;

@@ -43,6 +43,23 @@ __device__ __forceinline__ uint64_t match_peers(uint32_t key, bool active, int n
   return peers;
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin. When the segments split
+// evenly, block b takes a tile of a segment s with s % 8 == b % 8, so all
+// tiles of a segment run on one XCD and the partial-line permutation writes
+// of neighbouring tiles meet in that XCD's L2 before they reach HBM.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void block_tile(int tiles, int64_t nseg, int64_t& seg, int& tile) {
+  const unsigned b = blockIdx.x;
+  if (nseg % kXcds == 0) {
+    const unsigned k = b / kXcds;
+    seg = (int64_t)(b % kXcds) + (int64_t)kXcds * (k / (unsigned)tiles);
+    tile = (int)(k % (unsigned)tiles);
+  } else {
+    seg = b / (unsigned)tiles;
+    tile = (int)(b % (unsigned)tiles);
+  }
+}
+
 // Thread (w, lane) takes positions begin + 256w + 64k + lane, k = 0..3: in
 // position order per wave, one coalesced 128-byte read per wave and k.
 __device__ __forceinline__ void load_tile(const uint16_t* bk, int begin, int end, uint32_t* b,
@@ -57,10 +74,11 @@ __device__ __forceinline__ void load_tile(const uint16_t* bk, int begin, int end
 
 __global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint16_t* __restrict__ buckets,
                                                              uint32_t* __restrict__ counts, int L,
-                                                             int nb, int tiles) {
+                                                             int nb, int tiles, int64_t nseg) {
   extern __shared__ uint32_t cnt[];
-  const int tile = (int)(blockIdx.x % (unsigned)tiles);
-  const int64_t seg = blockIdx.x / (unsigned)tiles;
+  int64_t seg;
+  int tile;
+  block_tile(tiles, nseg, seg, tile);
   const int tid = threadIdx.x;
   uint32_t* cs = counts + (seg * tiles + tile) * (int64_t)nb;
   const int begin = tile * kSortTile;
@@ -134,10 +152,11 @@ __global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ count
 
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const uint16_t* __restrict__ buckets, const uint32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int L, int nb, int tiles, int nbits) {
+    int32_t* __restrict__ perm, int L, int nb, int tiles, int nbits, int64_t nseg) {
   extern __shared__ uint32_t next[];  // [wave][window]
-  const int tile = (int)(blockIdx.x % (unsigned)tiles);
-  const int64_t seg = blockIdx.x / (unsigned)tiles;
+  int64_t seg;
+  int tile;
+  block_tile(tiles, nseg, seg, tile);
   const int tid = threadIdx.x;
   const int w = tid / kWave, lane = tid % kWave;
   const uint32_t* os = offsets + (seg * tiles + tile) * (int64_t)nb;
@@ -195,11 +214,11 @@ hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* coun
   const dim3 grid((unsigned)(tiles * p.nseg()));
   const size_t window = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins);
   hipLaunchKernelGGL(k_sort_count, grid, dim3(kSortThreads), window * 4, s, buckets, counts, p.L,
-                     p.nb, tiles);
+                     p.nb, tiles, p.nseg());
   hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)p.nseg()), dim3(1024), 0, s, counts, p.nb,
                      tiles);
   hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kSortThreads), kSortWaves * window * 4, s,
-                     buckets, counts, perm, p.L, p.nb, tiles, nbits);
+                     buckets, counts, perm, p.L, p.nb, tiles, nbits, p.nseg());
   return hipGetLastError();
 }
 
