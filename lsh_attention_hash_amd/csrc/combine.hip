@@ -19,18 +19,25 @@
 namespace lsh {
 namespace {
 
-// 8 consecutive per-round outputs as floats
+// 8 consecutive per-round outputs as floats. Each row is read exactly once,
+// so the loads are non-temporal (streamed past the caches).
 __device__ __forceinline__ void load8(const float* p, float* x) {
-  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const f32x4_t a = __builtin_nontemporal_load((const f32x4_t*)p);
+  const f32x4_t b = __builtin_nontemporal_load((const f32x4_t*)(p + 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a[j];
+    x[4 + j] = b[j];
+  }
 }
 __device__ __forceinline__ void load8(const _Float16* p, float* x) {
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-  const f16x8_t a = *(const f16x8_t*)p;
+  const f16x8_t a = __builtin_nontemporal_load((const f16x8_t*)p);
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
 }
+// 8 consecutive inputs (v) as floats
 __device__ __forceinline__ void load8(const bf16_t* p, float* x) {
   const uint4 a = *(const uint4*)p;
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -68,7 +75,10 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
   const int R = kR > 0 ? kR : R_rt;
   const int sub = threadIdx.x % kLpr;
   const int64_t stride = (int64_t)gridDim.x * kRpb;
-  for (int64_t row = (int64_t)blockIdx.x * kRpb + threadIdx.x / kLpr; row < n_rows;
+  // Blocks walk the rows from the end: the attention kernel finishes the last
+  // heads last, so their rows are read first, while they are most likely
+  // still in the memory-side cache.
+  for (int64_t row = (int64_t)(gridDim.x - 1 - blockIdx.x) * kRpb + threadIdx.x / kLpr; row < n_rows;
        row += stride) {
     const int64_t bh = row / L;
     const int64_t i = row - bh * L;

@@ -311,19 +311,17 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
 
     uint32_t t1[2] = {0u, 0u}, t2[2] = {0u, 0u}, t3[2] = {0u, 0u};
-    floatx16_t acc[2];
     f16x8_t at[KS];  // the rotation tile, shared by both sets
     auto load_tile = [&](int kt) {
       const unsigned char* arow = lds + (kt * 32 + tl) * ROWB + hf * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) at[ks] = *(const f16x8_t*)(arow + ks * 16);
     };
-    auto set_mfma = [&](int s) {
+    auto set_mfma = [&](floatx16_t& acc, int s) {
       const floatx16_t zero = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_f16(at[ks], bx[s][ks], ks == 0 ? zero : acc[s],
-                                                         0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(at[ks], bx[s][ks], ks == 0 ? zero : acc, 0, 0, 0);
     };
     // C layout: lane holds token tl and columns kt*32 + 8(v/4) + 4 hf + v%4.
     // The index field gets kt*32 + 8(v/4) + v%4 (uniform across the wave); bit
@@ -336,18 +334,14 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         top3(t1[s], t2[s], t3[s], (__float_as_uint(c[v]) & vmask_v) | k);
       }
     };
-    // Each set's keys of tile kt are folded while the other set's MFMAs of
-    // tile kt + 1 run: the accumulators are copied out first, and the group
-    // barriers interleave one MFMA with the vector work that hides it.
-    load_tile(0);
-    set_mfma(0);
-    set_mfma(1);
-    int kt = 0;
-    for (; kt + 1 < ntiles; ++kt) {
+    // Tiles alternate between two accumulator pairs: each set's keys of tile
+    // kt are folded from one pair while the MFMAs of tile kt + 1 fill the
+    // other, so the fold reads the MFMA results in place (no copies), and the
+    // group barriers interleave one MFMA with the vector work around it.
+    auto step = [&](int kt, floatx16_t (&cur)[2], floatx16_t (&nxt)[2]) {
       load_tile(kt + 1);
-      const floatx16_t c0 = acc[0];
-      set_mfma(0);
-      fold(kt, c0, 0);
+      set_mfma(nxt[0], 0);
+      fold(kt, cur[0], 0);
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // rotation tile reads
       __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
 #pragma unroll
@@ -356,9 +350,8 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const floatx16_t c1 = acc[1];
-      set_mfma(1);
-      fold(kt, c1, 1);
+      set_mfma(nxt[1], 1);
+      fold(kt, cur[1], 1);
       __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
@@ -366,9 +359,24 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+    };
+    floatx16_t even[2], odd[2];
+    load_tile(0);
+    set_mfma(even[0], 0);
+    set_mfma(even[1], 1);
+    int kt = 0;
+    for (; kt + 2 < ntiles; kt += 2) {
+      step(kt, even, odd);
+      step(kt + 1, odd, even);
     }
-    fold(kt, acc[0], 0);
-    fold(kt, acc[1], 1);
+    if (kt + 1 < ntiles) {
+      step(kt, even, odd);
+      fold(kt + 1, odd[0], 0);
+      fold(kt + 1, odd[1], 1);
+    } else {
+      fold(kt, even[0], 0);
+      fold(kt, even[1], 1);
+    }
     // merge the two lane halves (same tokens, other columns)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
