@@ -11,8 +11,11 @@
 // permutation (the gather is fused into the load) and staged in LDS:
 //   Kt : qk rows of the previous and current chunk, row-major (+16 B pad);
 //        they are the keys and, for the current chunk, the queries (shared QK);
-//   Vq : v rows stored as groups of 4 keys x d dims x 4 (8 bytes per dim), so
-//        that one 8-byte LDS read yields 4 consecutive keys of one dim;
+//   Vp : v rows stored by key pairs of 4-key groups (a, a + 4), a in
+//        {0..3, 8..11}: per dim 16 bytes, the 4 keys of group a then those of
+//        group a + 4, so one 16-byte LDS read is a whole A operand of PV (a
+//        16-byte pad after every 8 dims keeps the staging writes and the
+//        reads free of bank conflicts);
 //   per key: log2(e)/(sqrt(d) |k|), original position, and log2(e) |k|/sqrt(d).
 // The previous chunk stays in LDS, so every chunk is loaded once per walk.
 // The rows of chunk c+1 are loaded while chunk c is computed, addressed by
@@ -62,11 +65,11 @@ constexpr float kBoundLimit = 60.0f;
 template <int D>
 struct Lds {
   static constexpr int kRow = D * 2 + 16;     // bytes per staged qk row
-  static constexpr int kQuad = D * 8 + 128;   // bytes per group of 4 v rows (+128: the two
-                                              // lane halves of a read hit disjoint banks)
+  static constexpr int kBlk8 = 8 * 16 + 16;  // bytes per 8 dims of a key pair (+16 pad)
+  static constexpr int kPair = D / 8 * kBlk8;  // bytes per key pair (8 keys x d dims)
   static constexpr int kKt = 0;
-  static constexpr int kVq = kKt + 2 * kChunk * kRow;
-  static constexpr int kScale = kVq + 2 * (kChunk / 4) * kQuad;
+  static constexpr int kVp = kKt + 2 * kChunk * kRow;
+  static constexpr int kScale = kVp + 2 * (kChunk / 8) * kPair;
   static constexpr int kPos = kScale + 2 * kChunk * 4;
   static constexpr int kBound = kPos + 2 * kChunk * 4;
   static constexpr int kPermNext = kBound + 2 * kChunk * 4;  // positions of the next chunk
@@ -174,19 +177,23 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
       ((float*)(lds + Lay::kBound))[sl * kChunk + t] = sc * nrm;
     }
   }
-  // v rows, 4 keys x 8 dims per piece, stored as [group][dim][4 keys]
+  // v rows, 4 keys x 8 dims per piece: group qd is half (qd / 4) % 2 of key
+  // pair (qd % 4) + 4 (qd / 8), stored as [pair][dim][8 keys]
   if (t < CR::kVUsers) {
     const int qd = t / CR::kSegs, sg = t % CR::kSegs;
-    uint2* dst = (uint2*)(lds + Lay::kVq + (sl * (kChunk / 4) + qd) * Lay::kQuad) + sg * 8;
+    const int pair = (qd & 3) + 4 * (qd >> 3), half = (qd >> 2) & 1;
+    unsigned char* dst =
+        lds + Lay::kVp + (sl * (kChunk / 8) + pair) * Lay::kPair + sg * Lay::kBlk8 + half * 8;
     const uint32_t w0[4] = {cr.v[0].x, cr.v[0].y, cr.v[0].z, cr.v[0].w};
     const uint32_t w1[4] = {cr.v[1].x, cr.v[1].y, cr.v[1].z, cr.v[1].w};
     const uint32_t w2[4] = {cr.v[2].x, cr.v[2].y, cr.v[2].z, cr.v[2].w};
     const uint32_t w3[4] = {cr.v[3].x, cr.v[3].y, cr.v[3].z, cr.v[3].w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      dst[2 * u] = make_uint2((w0[u] & 0xFFFFu) | (w1[u] << 16), (w2[u] & 0xFFFFu) | (w3[u] << 16));
-      dst[2 * u + 1] = make_uint2((w0[u] >> 16) | (w1[u] & 0xFFFF0000u),
-                                  (w2[u] >> 16) | (w3[u] & 0xFFFF0000u));
+      *(uint2*)(dst + 32 * u) =
+          make_uint2((w0[u] & 0xFFFFu) | (w1[u] << 16), (w2[u] & 0xFFFFu) | (w3[u] << 16));
+      *(uint2*)(dst + 32 * u + 16) = make_uint2((w0[u] >> 16) | (w1[u] & 0xFFFF0000u),
+                                                (w2[u] >> 16) | (w3[u] & 0xFFFF0000u));
     }
   }
 }
@@ -251,8 +258,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // chunk 0 has no previous chunk: zero keys and values in its slot
     uint4* kt = (uint4*)(lds + Lay::kKt + kChunk * Lay::kRow);        // slot 1
     for (int i = threadIdx.x; i < kChunk * Lay::kRow / 16; i += kThreads) kt[i] = uint4{};
-    uint4* vq = (uint4*)(lds + Lay::kVq + (kChunk / 4) * Lay::kQuad);  // slot 1
-    for (int i = threadIdx.x; i < (kChunk / 4) * Lay::kQuad / 16; i += kThreads) vq[i] = uint4{};
+    uint4* vp = (uint4*)(lds + Lay::kVp + (kChunk / 8) * Lay::kPair);  // slot 1
+    for (int i = threadIdx.x; i < (kChunk / 8) * Lay::kPair / 16; i += kThreads) vp[i] = uint4{};
     if (threadIdx.x < kChunk) ((float*)(lds + Lay::kScale))[kChunk + threadIdx.x] = 0.f;
   }
   perm_to_lds(c0);
@@ -354,17 +361,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4_t{};
     auto pv_step = [&](int e, const bf16x8_t& pf) {
       const int sl = e < 2 ? prv : cur;
-      const int qa = 8 * (e & 1) + g, qc = qa + 4;
-      const unsigned char* va = lds + Lay::kVq + (sl * (kChunk / 4) + qa) * Lay::kQuad;
-      const unsigned char* vc = lds + Lay::kVq + (sl * (kChunk / 4) + qc) * Lay::kQuad;
+      // key pair g + 4 (e % 2): groups 8 (e % 2) + g and 8 (e % 2) + g + 4
+      const unsigned char* vp = lds + Lay::kVp + (sl * (kChunk / 8) + g + 4 * (e & 1)) * Lay::kPair +
+                                (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int dim = dt * 16 + lq;
-        const uint2 lo = *(const uint2*)(va + dim * 8);
-        const uint2 hi = *(const uint2*)(vc + dim * 8);
-        const uint32_t u[4] = {lo.x, lo.y, hi.x, hi.y};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)u, pf, oacc[dt],
-                                                            0, 0, 0);
+        const bf16x8_t a = *(const bf16x8_t*)(vp + dt * 2 * Lay::kBlk8);  // dim 16 dt + lq
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[dt], 0, 0, 0);
       }
       lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
     };
