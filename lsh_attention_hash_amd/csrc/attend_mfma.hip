@@ -308,8 +308,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       return acc;
     };
+    // (absent is uniform; a bitwise or keeps it from becoming a branch that
+    // splits the key reads)
     auto masked = [&](bool absent, int kp) -> bool {
-      return absent || (CAUSAL ? kp >= posq : kp == posq);
+      return absent | (CAUSAL ? kp >= posq : kp == posq);
     };
     if (__ballot(mq > kBoundLimit) != 0ull) {
       float mx = -INFINITY;
