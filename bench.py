@@ -310,13 +310,16 @@ def main():
 
 
 def kernel_source_hash(stage: str) -> str:
-    """Hash of the source files of a stage's kernels (and the shared headers);
-    counter-derived traffic is only reported while they are unchanged."""
+    """Hash of the source files of a stage's kernels, the shared headers and the
+    build script (compiler flags); counter-derived traffic is only reported
+    while they are unchanged."""
     import hashlib
     h = hashlib.sha256()
     for fname in STAGE_SOURCES[stage] + ["internal.h", "dtype.h"]:
         with open(os.path.join(ROOT, "lsh_attention_hash_amd", "csrc", fname), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(ROOT, "lsh_attention_hash_amd", "build.py"), "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
