@@ -48,6 +48,7 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;     // 4 waves, one per SIMD; each wave pipelines its own work
 constexpr int kTokWave = 64;      // 2 sets of 32 tokens per wave
 constexpr int kTokWG = kThreads / 64 * kTokWave;
+constexpr int kRotLoads = 32;     // rotation loads per thread in flight (32 x 16 B x 256 = 128 KB)
 constexpr float kF16Max = 65504.0f;
 constexpr float kF16MinNormal = 6.103515625e-05f;  // 2^-14
 
@@ -252,34 +253,11 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   const int grp = xcd + 8 * (kk / R);
   const int ngrp = gridDim.x / R;      // gridDim.x is a multiple of 8 R
 
-  // rotation of round r -> LDS, 8 loads in flight per thread
-  {
-    const uint4* g = (const uint4*)(rh + (int64_t)r * half_pad * D);
-    const int total = half_pad * (D / 8);
-    for (int base = threadIdx.x; base < total; base += kThreads * 8) {
-      uint4 tmp[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * kThreads;
-        tmp[u] = g[idx < total ? idx : 0];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int idx = base + u * kThreads;
-        if (idx < total) *(uint4*)(lds + (idx / (D / 8)) * ROWB + (idx % (D / 8)) * 16) = tmp[u];
-      }
-    }
-  }
-  __syncthreads();
-  const float rh_max = __uint_as_float(bounds_u[r * 4 + 0]);
-  const float lo_max = __uint_as_float(bounds_u[r * 4 + 1]);
-  const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
-  const int ntiles = half_pad / 32;
-
   // x in fp16 as the B operand: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
   // of token tl of each set, K-step ks covering dims hf*D/2 + 8ks + 0..7 (the
   // K order of both operands is permuted the same way, which leaves the
-  // product as is). The next token tile is loaded while this one runs.
+  // product as is). The next token tile is loaded while this one runs; the
+  // first one while the rotation is copied into LDS.
   f16x8_t bn[2][KS];
   float2 nn[2];
   auto fetch = [&](int j) {
@@ -297,6 +275,38 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     }
   };
   if (grp < n_tok_tiles) fetch(grp);
+
+  // rotation of round r -> LDS: every load of a thread in flight at once
+  // (kRotLoads of 16 bytes cover 128 KB over the workgroup), then the stores
+  {
+    const uint4* g = (const uint4*)(rh + (int64_t)r * half_pad * D);
+    const int total = half_pad * (D / 8);
+    for (int base = threadIdx.x; base < total; base += kThreads * kRotLoads) {
+      uint4 tmp[kRotLoads];
+#pragma unroll
+      for (int u = 0; u < kRotLoads; ++u) {
+        const int idx = base + u * kThreads;
+        tmp[u] = g[idx < total ? idx : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < kRotLoads; ++u) {
+        const int idx = base + u * kThreads;
+        if (idx < total) *(uint4*)(lds + (idx / (D / 8)) * ROWB + (idx % (D / 8)) * 16) = tmp[u];
+      }
+    }
+  }
+  __syncthreads();
+  const float rh_max = __uint_as_float(bounds_u[r * 4 + 0]);
+  const float lo_max = __uint_as_float(bounds_u[r * 4 + 1]);
+  const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
+  const int ntiles = half_pad / 32;
+
+  // head and position of the wave's first token (wave-uniform), advanced by
+  // the walk's stride at the end of every token tile: one division per walk
+  const int64_t tfirst = (int64_t)grp * kTokWG + __builtin_amdgcn_readfirstlane(w) * kTokWave;
+  const int64_t tstep = (int64_t)ngrp * kTokWG;
+  int64_t bh0 = tfirst / L, i0 = tfirst - (tfirst / L) * L;
+  const int64_t step_q = tstep / L, step_r = tstep - (tstep / L) * L;
   for (int j = grp; j < n_tok_tiles; j += ngrp) {
     const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
     f16x8_t bx[2][KS];
@@ -310,14 +320,21 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     }
     if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
 
+    // two independent top-3 lists per set (even and odd accumulator
+    // registers), merged once per token tile: half the dependency chain
     uint32_t t1[2] = {0u, 0u}, t2[2] = {0u, 0u}, t3[2] = {0u, 0u};
-    f16x8_t at[KS];  // the rotation tile, shared by both sets
-    auto load_tile = [&](int kt) {
-      const unsigned char* arow = lds + (kt * 32 + tl) * ROWB + hf * D;
+    uint32_t u1[2] = {0u, 0u}, u2[2] = {0u, 0u}, u3[2] = {0u, 0u};
+    // Rotation tiles (the A operand, shared by both sets) are read from LDS
+    // one step ahead: even tiles into at0, odd tiles into at1. A read past the
+    // last tile re-reads the last one (never used).
+    f16x8_t at0[KS], at1[KS];
+    auto load_tile = [&](int kt, f16x8_t (&at)[KS]) {
+      const int kc = kt < ntiles ? kt : ntiles - 1;
+      const unsigned char* arow = lds + (kc * 32 + tl) * ROWB + hf * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) at[ks] = *(const f16x8_t*)(arow + ks * 16);
     };
-    auto set_mfma = [&](floatx16_t& acc, int s) {
+    auto set_mfma = [&](floatx16_t& acc, int s, const f16x8_t (&at)[KS]) {
       const floatx16_t zero = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -331,16 +348,19 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const uint32_t k = (uint32_t)(kt * 32 + 8 * (v >> 2) + (v & 3));
-        top3(t1[s], t2[s], t3[s], (__float_as_uint(c[v]) & vmask_v) | k);
+        if (v & 1) top3(u1[s], u2[s], u3[s], (__float_as_uint(c[v]) & vmask_v) | k);
+        else top3(t1[s], t2[s], t3[s], (__float_as_uint(c[v]) & vmask_v) | k);
       }
     };
     // Tiles alternate between two accumulator pairs: each set's keys of tile
     // kt are folded from one pair while the MFMAs of tile kt + 1 fill the
-    // other, so the fold reads the MFMA results in place (no copies), and the
-    // group barriers interleave one MFMA with the vector work around it.
-    auto step = [&](int kt, floatx16_t (&cur)[2], floatx16_t (&nxt)[2]) {
-      load_tile(kt + 1);
-      set_mfma(nxt[0], 0);
+    // other, so the fold reads the MFMA results in place (no copies); the
+    // rotation tile kt + 2 is read meanwhile. The group barriers interleave
+    // one MFMA with the vector work around it.
+    auto step = [&](int kt, floatx16_t (&cur)[2], floatx16_t (&nxt)[2], const f16x8_t (&use)[KS],
+                    f16x8_t (&pre)[KS]) {
+      load_tile(kt + 2, pre);
+      set_mfma(nxt[0], 0, use);
       fold(kt, cur[0], 0);
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // rotation tile reads
       __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
@@ -350,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      set_mfma(nxt[1], 1);
+      set_mfma(nxt[1], 1, use);
       fold(kt, cur[1], 1);
       __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
 #pragma unroll
@@ -361,25 +381,30 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       __builtin_amdgcn_sched_barrier(0);
     };
     floatx16_t even[2], odd[2];
-    load_tile(0);
-    set_mfma(even[0], 0);
-    set_mfma(even[1], 1);
+    load_tile(0, at0);
+    load_tile(1, at1);
+    set_mfma(even[0], 0, at0);
+    set_mfma(even[1], 1, at0);
     int kt = 0;
     for (; kt + 2 < ntiles; kt += 2) {
-      step(kt, even, odd);
-      step(kt + 1, odd, even);
+      step(kt, even, odd, at1, at0);
+      step(kt + 1, odd, even, at0, at1);
     }
     if (kt + 1 < ntiles) {
-      step(kt, even, odd);
+      step(kt, even, odd, at1, at0);
       fold(kt + 1, odd[0], 0);
       fold(kt + 1, odd[1], 1);
     } else {
       fold(kt, even[0], 0);
       fold(kt, even[1], 1);
     }
-    // merge the two lane halves (same tokens, other columns)
+    // merge the odd list into the even one, then the two lane halves (same
+    // tokens, other columns)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      top3(t1[s], t2[s], t3[s], u1[s]);
+      top3(t1[s], t2[s], t3[s], u2[s]);
+      top3(t1[s], t2[s], t3[s], u3[s]);
       t1[s] |= (uint32_t)(hf << 2);
       t2[s] |= (uint32_t)(hf << 2);
       t3[s] |= (uint32_t)(hf << 2);
@@ -390,12 +415,13 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       top3(t1[s], t2[s], t3[s], o3);
     }
     // sign of p~ at each set's best column, partial over this lane's dims
+    // (four partial sums: any fp32 order is within the certificate's bound)
     float part[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint32_t k1 = t1[s] & imask;
       const unsigned char* row = lds + k1 * ROWB + hf * D;
-      float acc = 0.f;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const f16x8_t a = *(const f16x8_t*)(row + ks * 16);
@@ -403,10 +429,10 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         for (int q = 0; q < 4; ++q) {
           const f16x2_t pa = {a[2 * q], a[2 * q + 1]};
           const f16x2_t pb = {bx[s][ks][2 * q], bx[s][ks][2 * q + 1]};
-          acc = __builtin_amdgcn_fdot2(pa, pb, acc, false);
+          acc[q] = __builtin_amdgcn_fdot2(pa, pb, acc[q], false);
         }
       }
-      part[s] = acc;
+      part[s] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
     // this lane finishes set hf; the partner holds the other half of its dims
     const float send = hf ? part[0] : part[1];
@@ -414,10 +440,6 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const float pk1 = (hf ? part[1] : part[0]) + recv;
 
     const int64_t n = tok0 + hf * 32 + tl;
-    // head and position of the wave's first token (wave-uniform)
-    const int64_t tok0u = __builtin_amdgcn_readfirstlane((int)(tok0 & 0xffffffff)) |
-                          ((int64_t)__builtin_amdgcn_readfirstlane((int)(tok0 >> 32)) << 32);
-    const int64_t bh0 = tok0u / L, i0 = tok0u - bh0 * L;
     if (n < N) {
       const uint32_t a1 = hf ? t1[1] : t1[0];
       const uint32_t a2 = hf ? t2[1] : t2[0];
@@ -450,6 +472,12 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         if (e < (unsigned)kQbLds) qb_l[e] = entry;
         else qb[atomicAdd(qcount + 1, 1u)] = entry;
       }
+    }
+    bh0 += step_q;
+    i0 += step_r;
+    if (i0 >= L) {
+      i0 -= L;
+      ++bh0;
     }
   }
   // move the workgroup's queued entries to the global queues
