@@ -88,6 +88,7 @@ def _load():
             "lsh_oracle_combine": [C, P, P, P],
             "lsh_oracle_forward": [C, P, P, P, P, P, P, P, P, P],
             "lsh_oracle_attend_rows": [C, P, P, P, ctypes.c_int64, P, P, P],
+            "lsh_oracle_backward": [C, P, P, P, P, P, P],
         }.items():
             f = getattr(lib, name)
             f.argtypes = argt
@@ -187,3 +188,14 @@ def attend_rows(c: Config, qk, v, perm, rows):
                                         ctypes.c_int64(rows.size), _p(rows), _p(out), _p(lse)),
          "attend_rows")
     return out, lse
+
+
+def backward(c: Config, qk, v, perm, dout):
+    """Gradients (dqk, dv) [B, H, L, d] of a loss given dout = dL/dout, at the
+    permutations perm [B, H, R, L] of the forward (buckets held fixed)."""
+    qk, v, pm, do = _f64(qk), _f64(v), _i32(perm), _f64(dout)
+    dqk = np.empty((c.batch, c.heads, c.seq_len, c.head_dim), np.float64)
+    dv = np.empty_like(dqk)
+    _chk(_load().lsh_oracle_backward(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do), _p(dqk),
+                                     _p(dv)), "backward")
+    return dqk, dv

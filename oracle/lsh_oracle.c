@@ -154,12 +154,12 @@ static void unit_key(const double* k, int64_t d, double* khat) {
   for (int64_t t = 0; t < d; ++t) khat[t] = (nrm > 0.0) ? k[t] / nrm : 0.0;
 }
 
-/* qk_bh, v_bh: [L, d] of one (b, h); pm: perm of one round; s: the query slot.
- * Writes o_row [d] and returns the round's logsumexp. Scratch: khat [d],
- * logit [2m], key [2m]. */
-static double attend_one(const lsh_oracle_config* c, const double* qk_bh, const double* v_bh,
-                         const int32_t* pm, int64_t s, double* o_row, double* khat,
-                         double* logit, int64_t* key) {
+/* The attendable keys of the query at slot s of one round: its chunk and the
+ * previous one, without the query itself and (causal) later positions.
+ * qk_bh: [L, d] of one (b, h); pm: perm of the round. Writes the keys'
+ * positions key[n] and logits logit[n] (n returned). Scratch: khat [d]. */
+static int64_t window(const lsh_oracle_config* c, const double* qk_bh, const int32_t* pm,
+                      int64_t s, double* khat, double* logit, int64_t* key) {
   const int64_t d = c->head_dim, m = c->chunk_len;
   const int64_t i = pm[s];
   const int64_t chunk = s / m;
@@ -179,6 +179,18 @@ static double attend_one(const lsh_oracle_config* c, const double* qk_bh, const 
     key[n] = j;
     ++n;
   }
+  return n;
+}
+
+/* qk_bh, v_bh: [L, d] of one (b, h); pm: perm of one round; s: the query slot.
+ * Writes o_row [d] and returns the round's logsumexp. Scratch: khat [d],
+ * logit [2m], key [2m]. */
+static double attend_one(const lsh_oracle_config* c, const double* qk_bh, const double* v_bh,
+                         const int32_t* pm, int64_t s, double* o_row, double* khat,
+                         double* logit, int64_t* key) {
+  const int64_t d = c->head_dim;
+  const int64_t i = pm[s];
+  const int64_t n = window(c, qk_bh, pm, s, khat, logit, key);
   if (n == 0) {
     for (int64_t u = 0; u < d; ++u) o_row[u] = v_bh[i * d + u];
     return LSH_ORACLE_SELF_LOGIT;
@@ -293,6 +305,137 @@ done:
   if (!perm) free(pm);
   if (!lse) free(ls);
   free(o);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward: gradients of a loss with respect to qk and v, given dL/dout, at
+ * the buckets (hence permutations) of the forward. The hash is an argmax and
+ * the sort a permutation: both are piecewise constant, so no gradient flows
+ * through them. The chain rule is taken through the steps above in reverse:
+ *  combination (out = sum_r w_r o_r, w = softmax over rounds of lse):
+ *    dL/do_r(i)   = w_r(i) dout(i)
+ *    dL/dlse_r(i) = w_r(i) ((o_r(i) - out(i)) . dout(i))
+ *  one round, query i with attendable keys O (softmax P_j over O):
+ *    dL/dv_j     += P_j do_r(i)
+ *    dL/ds_ij     = P_j (do_r(i) . v_j - sum_k P_k do_r(i) . v_k) + P_j dlse_r(i)
+ *    with s_ij = (q_i . khat_j) / sqrt(d), q_i = qk_i, khat_j = qk_j / |qk_j|:
+ *    dL/dq_i     += dL/ds_ij khat_j / sqrt(d),   dL/dkhat_j += dL/ds_ij q_i / sqrt(d)
+ *  a query that could attend only to itself has o_r(i) = v_i:
+ *    dL/dv_i     += do_r(i)   (its logsumexp is a constant)
+ *  key normalisation (khat = k / |k|, khat := 0 for k = 0):
+ *    dL/dk_j      = (dkhat_j - khat_j (khat_j . dkhat_j)) / |k_j|
+ *  shared QK: dL/dqk_j = dL/dq_j + dL/dk_j.
+ * perm: every round's permutation [B, H, R, L]; dout, dqk, dv: [B, H, L, d].
+ * ------------------------------------------------------------------------- */
+int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const double* v,
+                        const int32_t* perm, const double* dout, double* dqk, double* dv) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
+  const int64_t nbh = (int64_t)c->batch * c->heads;
+  const size_t nsl = seg_count(c) * (size_t)L;
+  double* o = (double*)malloc(sizeof(double) * nsl * (size_t)d);
+  double* lse = (double*)malloc(sizeof(double) * nsl);
+  double* out = (double*)malloc(sizeof(double) * (size_t)(nbh * L * d));
+  double* dkhat = (double*)calloc((size_t)(nbh * L * d), sizeof(double));
+  if (!o || !lse || !out || !dkhat) { rc = -8; goto done; }
+  rc = lsh_oracle_attend(c, qk, v, perm, o, lse);
+  if (rc) goto done;
+  rc = lsh_oracle_combine(c, o, lse, out);
+  if (rc) goto done;
+  for (int64_t x = 0; x < nbh * L * d; ++x) { dqk[x] = 0.0; dv[x] = 0.0; }
+  /* one (b, h) per thread: every write of a (b, h) stays in its own rows */
+#pragma omp parallel
+  {
+    double* khat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
+    double* pj = (double*)malloc(sizeof(double) * (size_t)(2 * m));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(2 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+    double* dor = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < nbh; ++bh) {
+      const double* qk_bh = qk + bh * L * d;
+      const double* v_bh = v + bh * L * d;
+      for (int64_t r = 0; r < R; ++r) {
+        const int64_t seg = bh * R + r;
+        const int32_t* pm = perm + seg * L;
+        for (int64_t s = 0; s < L; ++s) {
+          const int64_t i = pm[s];
+          /* combination backward for (round r, position i) */
+          double mx = -INFINITY;
+          for (int64_t rr = 0; rr < R; ++rr) {
+            const double l = lse[(bh * R + rr) * L + i];
+            mx = l > mx ? l : mx;
+          }
+          double sum = 0.0;
+          for (int64_t rr = 0; rr < R; ++rr) sum += exp(lse[(bh * R + rr) * L + i] - mx);
+          const double w = exp(lse[seg * L + i] - mx) / sum;
+          const double* orow = o + (seg * L + i) * d;
+          const double* outrow = out + (bh * L + i) * d;
+          const double* drow = dout + (bh * L + i) * d;
+          double g = 0.0;
+          for (int64_t u = 0; u < d; ++u) {
+            dor[u] = w * drow[u];
+            g += (orow[u] - outrow[u]) * drow[u];
+          }
+          const double dlse = w * g;
+          /* the round's window, as in the forward */
+          const int64_t n = window(c, qk_bh, pm, s, khat, logit, key);
+          const double* q = qk_bh + i * d;
+          const double scale = 1.0 / sqrt((double)d);
+          if (n == 0) {
+            for (int64_t u = 0; u < d; ++u) dv[(bh * L + i) * d + u] += dor[u];
+            continue;
+          }
+          const double l = lse[seg * L + i];
+          double dsum = 0.0;
+          for (int64_t a = 0; a < n; ++a) {
+            pj[a] = exp(logit[a] - l);
+            double t = 0.0;
+            for (int64_t u = 0; u < d; ++u) t += dor[u] * v_bh[key[a] * d + u];
+            dp[a] = t;
+            dsum += pj[a] * t;
+          }
+          for (int64_t a = 0; a < n; ++a) {
+            const int64_t j = key[a];
+            const double ds = pj[a] * (dp[a] - dsum) + pj[a] * dlse;
+            unit_key(qk_bh + j * d, d, khat);
+            for (int64_t u = 0; u < d; ++u) {
+              dv[(bh * L + j) * d + u] += pj[a] * dor[u];
+              dqk[(bh * L + i) * d + u] += ds * khat[u] * scale;
+              dkhat[(bh * L + j) * d + u] += ds * q[u] * scale;
+            }
+          }
+        }
+      }
+      /* key normalisation */
+      for (int64_t j = 0; j < L; ++j) {
+        const double* k = qk_bh + j * d;
+        double ss = 0.0;
+        for (int64_t u = 0; u < d; ++u) ss += k[u] * k[u];
+        const double nrm = sqrt(ss);
+        if (nrm == 0.0) continue;
+        const double* dk = dkhat + (bh * L + j) * d;
+        double proj = 0.0;
+        for (int64_t u = 0; u < d; ++u) proj += (k[u] / nrm) * dk[u];
+        for (int64_t u = 0; u < d; ++u)
+          dqk[(bh * L + j) * d + u] += (dk[u] - (k[u] / nrm) * proj) / nrm;
+      }
+    }
+    free(khat);
+    free(logit);
+    free(pj);
+    free(dp);
+    free(key);
+    free(dor);
+  }
+done:
+  free(o);
+  free(lse);
+  free(out);
+  free(dkhat);
   return rc;
 }
 

@@ -1,6 +1,6 @@
 /*
  * lsh_oracle.h -- plain, slow fp64 CPU definition of Reformer shared-QK LSH
- * self-attention (forward).
+ * self-attention (forward, and its backward at fixed buckets).
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU
  * baseline may load or call this library. The product path (the HIP library
@@ -75,6 +75,11 @@ int lsh_oracle_forward(const lsh_oracle_config* cfg, const double* qk, const dou
                        const double* rotations, const int32_t* buckets_override,
                        double* out, double* lse, int32_t* buckets, int32_t* perm,
                        double* margin);
+
+/* Backward at fixed permutations: dqk, dv [B, H, L, d] from dout [B, H, L, d]
+ * (gradient of a loss with respect to out); perm [B, H, R, L] as from forward. */
+int lsh_oracle_backward(const lsh_oracle_config* cfg, const double* qk, const double* v,
+                        const int32_t* perm, const double* dout, double* dqk, double* dv);
 
 /* Output rows for a sample of (b, h, i), given every round's perm:
  * rows[k] = (b * H + h) * L + i; out_rows [n_rows, d]; lse_rows [n_rows, n_rounds]. */

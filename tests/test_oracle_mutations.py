@@ -7,6 +7,7 @@ import pytest
 
 import oracle
 
+import test_oracle_backward as bpins
 import test_oracle_pins as pins
 
 # (name, original text, planted mistake); a list replaces several places at once.
@@ -36,6 +37,21 @@ MUTATIONS = [
     ("buckets in descending order",
      ["start[bk[i] + 1] += 1;", "pm[start[bk[i]]++] = (int32_t)i;"],
      ["start[nb - bk[i]] += 1;", "pm[start[nb - 1 - bk[i]]++] = (int32_t)i;"]),
+    # backward
+    ("bwd: logsumexp term dropped", "const double ds = pj[a] * (dp[a] - dsum) + pj[a] * dlse;",
+     "const double ds = pj[a] * (dp[a] - dsum);"),
+    ("bwd: key normalisation Jacobian dropped",
+     "dqk[(bh * L + j) * d + u] += (dk[u] - (k[u] / nrm) * proj) / nrm;",
+     "dqk[(bh * L + j) * d + u] += dk[u] / nrm;"),
+    ("bwd: self-only value gradient dropped",
+     "for (int64_t u = 0; u < d; ++u) dv[(bh * L + i) * d + u] += dor[u];",
+     "for (int64_t u = 0; u < d; ++u) dv[(bh * L + i) * d + u] += 0.0 * dor[u];"),
+    ("bwd: round weight missing", "dor[u] = w * drow[u];", "dor[u] = drow[u];"),
+    ("bwd: logsumexp gradient against the round row only",
+     "g += (orow[u] - outrow[u]) * drow[u];", "g += orow[u] * drow[u];"),
+    ("bwd: key gradient from the key instead of the query",
+     "dkhat[(bh * L + j) * d + u] += ds * q[u] * scale;",
+     "dkhat[(bh * L + j) * d + u] += ds * khat[u] * scale;"),
 ]
 
 
@@ -55,6 +71,9 @@ def _pin_calls():
         lambda: pins.test_dense_mask_and_multiset_union(o, True),
         lambda: pins.test_identical_rounds_collapse(o),
         lambda: pins.test_self_only_rows_return_their_value(o),
+        lambda: bpins.test_backward_matches_finite_differences(o, False),
+        lambda: bpins.test_backward_matches_finite_differences(o, True),
+        lambda: bpins.test_backward_single_chunk_equals_dense_autograd(o, 3, True),
     ]
 
 
