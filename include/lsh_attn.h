@@ -63,7 +63,10 @@ enum {
    * step. By default the matrix-core path (bf16 inputs) keeps them in fp16,
    * which halves that traffic; fp16 saturates at +-65504, so inputs whose v
    * exceeds that magnitude need this flag. */
-  LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2
+  LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
+  /* Also allocate the workspace of lsh_attn_backward (fp32 per-round rows and
+   * gradients: about 4 * n_rounds * |qk| * 4 / esize bytes more). */
+  LSH_ATTN_FLAG_BACKWARD = 4
 };
 
 typedef struct {
@@ -113,6 +116,31 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle);
  */
 int lsh_attn_forward(lsh_attn_t handle, const void* qk, const void* v, const float* rotations,
                      void* out, float* lse, int32_t* buckets, int32_t* perm, void* stream);
+
+/*
+ * Enqueue the backward of a forward on `stream`: the gradients of a loss with
+ * respect to qk and v, given dout = dL/dout, at that forward's buckets (the
+ * hash is an argmax and the sort a permutation, both piecewise constant, so
+ * no gradient flows through them). The chain rule is taken through the
+ * round combination, the windowed softmax, the shared-QK logits and the key
+ * normalisation (Reformer summary at p2.ttnews.xyz, LSH attention and
+ * multi-round sections; overview at www.dtcms.com/a/488796.html, section
+ * 2.1). The per-round attention is recomputed from the permutation.
+ *   qk, v     [B, H, L, d]          dtype  (read only), as passed to the forward
+ *   perm      [B, H, n_rounds, L]   int32  (read only): the forward's perm output
+ *   dout      [B, H, L, d]          dtype  (read only)
+ *   dqk, dv   [B, H, L, d]          dtype  (written); must not alias the inputs
+ * Device pointers; qk, v, dout, dqk and dv 16-byte aligned. Uses the handle's
+ * backward workspace (LSH_ATTN_FLAG_BACKWARD at create) and the forward's key
+ * norm buffer, so a backward and a forward of one handle must be ordered on the
+ * device (same stream). Performs no allocation and no host/device
+ * synchronisation. Deterministic: every output element is written once.
+ * Errors: INVALID_ARG for a null handle or pointer, a misaligned pointer or a
+ * current device other than the handle's; UNSUPPORTED if the handle was
+ * created without LSH_ATTN_FLAG_BACKWARD; HIP when a launch fails.
+ */
+int lsh_attn_backward(lsh_attn_t handle, const void* qk, const void* v, const int32_t* perm,
+                      const void* dout, void* dqk, void* dv, void* stream);
 
 /*
  * Counters of the last forward (waits for the handle's last stream):

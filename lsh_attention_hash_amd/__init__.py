@@ -24,10 +24,12 @@ _LIB_PATH = os.path.join(_PKG, "_lib", "liblsh_attn.so")
 FP32, BF16 = 0, 1
 FLAG_SEPARATE_GATHER = 1
 FLAG_FP32_ROUND_OUTPUTS = 2
+FLAG_BACKWARD = 4
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP"}
 
 # Every function declared in include/lsh_attn.h.
-EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats",
+EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward",
+                    "lsh_attn_get_stats",
                     "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_workspace_bytes",
                     "lsh_attn_destroy", "lsh_attn_strerror")
 N_STAGES = 7
@@ -69,6 +71,7 @@ def load_library():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.lsh_attn_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
     lib.lsh_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P]
+    lib.lsh_attn_backward.argtypes = [P, P, P, P, P, P, P, P]
     lib.lsh_attn_get_stats.argtypes = [P, ctypes.POINTER(Stats)]
     lib.lsh_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.lsh_attn_set_timing.argtypes = [P, I]
@@ -77,7 +80,8 @@ def load_library():
     lib.lsh_attn_destroy.argtypes = [P]
     lib.lsh_attn_strerror.argtypes = [I]
     lib.lsh_attn_strerror.restype = ctypes.c_char_p
-    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_get_stats", "lsh_attn_set_timing",
+    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward", "lsh_attn_get_stats",
+              "lsh_attn_set_timing",
               "lsh_attn_get_timing", "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
         getattr(lib, n).restype = I
     _lib = lib
@@ -114,10 +118,11 @@ class LSHAttention:
 
     def __init__(self, batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len=64,
                  causal=False, dtype=torch.bfloat16, out_dtype=None, separate_gather=False,
-                 fp32_round_outputs=False, device=None):
+                 fp32_round_outputs=False, backward=False, device=None):
         self.lib = load_library()
         flags = (FLAG_SEPARATE_GATHER if separate_gather else 0) | (
-            FLAG_FP32_ROUND_OUTPUTS if fp32_round_outputs else 0)
+            FLAG_FP32_ROUND_OUTPUTS if fp32_round_outputs else 0) | (
+            FLAG_BACKWARD if backward else 0)
         self.cfg = make_config(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len,
                                causal, dtype, out_dtype, flags)
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None
@@ -178,6 +183,33 @@ class LSHAttention:
         if return_lse or return_buckets or return_perm:
             return out, {"lse": lse, "buckets": bk, "perm": pm}
         return out
+
+    def backward(self, qk, v, perm, dout, dqk=None, dv=None, stream=None):
+        """Gradients (dqk, dv) [B, H, L, d] (dtype) given dout = dL/dout, at the
+        permutations perm [B, H, R, L] int32 returned by the forward (call it
+        with return_perm=True). Needs backward=True at construction."""
+        c = self.cfg
+        shp = (c.batch, c.heads, c.seq_len, c.head_dim)
+        self._check("qk", qk, shp, self.dtype)
+        self._check("v", v, shp, self.dtype)
+        self._check("perm", perm, (c.batch, c.heads, c.n_rounds, c.seq_len), torch.int32)
+        self._check("dout", dout, shp, self.dtype)
+        if dqk is None:
+            dqk = torch.empty(shp, dtype=self.dtype, device=self.device)
+        else:
+            self._check("dqk", dqk, shp, self.dtype)
+        if dv is None:
+            dv = torch.empty(shp, dtype=self.dtype, device=self.device)
+        else:
+            self._check("dv", dv, shp, self.dtype)
+        s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        with torch.cuda.device(self.device):
+            rc = self.lib.lsh_attn_backward(self.handle, ptr(qk), ptr(v), ptr(perm), ptr(dout),
+                                            ptr(dqk), ptr(dv), ctypes.c_void_p(s))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_backward", self.lib)
+        return dqk, dv
 
     def stats(self) -> dict:
         st = Stats()

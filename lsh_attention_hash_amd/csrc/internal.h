@@ -62,6 +62,17 @@ struct Workspace {
   HashScratch hash;                     // matrix-core hash only
 };
 
+// Backward workspace (allocated with LSH_ATTN_FLAG_BACKWARD), fp32:
+struct BwdWorkspace {
+  float* o32 = nullptr;  // [seg, L + kORowPad, d] recomputed per-round rows
+  float* lse = nullptr;  // [seg, L] recomputed per-round logsumexps
+  float* w = nullptr;    // [seg, L] round weights of the combination
+  float* cq = nullptr;   // [B*H, L] dout . out
+  float* dq = nullptr;   // [seg, L, d] per-round dq at original positions
+  float* dk = nullptr;   // [seg, L, d] per-round d(unit key)
+  float* dv = nullptr;   // [seg, L, d] per-round dv
+};
+
 // Kernel launchers (each defined next to its kernels). All enqueue on `s` and
 // return hipGetLastError().
 // exact fp64 hash of every row (fp32 inputs, or shapes the matrix-core hash
@@ -96,6 +107,11 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
 // rounds in which a query saw only itself
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
                           const void* v, void* out, hipStream_t s);
+
+// gradients of qk and v given dout, at the permutations perm of a forward
+hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+                           const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
+                           hipStream_t s);
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.

@@ -15,6 +15,7 @@
 struct lsh_attn_s {
   lsh::Problem p;
   lsh::Workspace ws;
+  lsh::BwdWorkspace bw;
   int device = 0;
   int64_t bytes = 0;
   hipStream_t last_stream = nullptr;
@@ -41,7 +42,8 @@ int validate(const lsh_attn_config_t* c) {
   if (c->n_buckets < 1 || c->n_buckets > 65536 || (c->n_buckets > 1 && c->n_buckets % 2 != 0))
     return LSH_ATTN_ERR_INVALID_ARG;
   if (c->causal != 0 && c->causal != 1) return LSH_ATTN_ERR_INVALID_ARG;
-  if ((c->flags & ~(LSH_ATTN_FLAG_SEPARATE_GATHER | LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS)) != 0)
+  if ((c->flags & ~(LSH_ATTN_FLAG_SEPARATE_GATHER | LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS |
+                    LSH_ATTN_FLAG_BACKWARD)) != 0)
     return LSH_ATTN_ERR_INVALID_ARG;
   if (c->dtype != LSH_ATTN_FP32 && c->dtype != LSH_ATTN_BF16) return LSH_ATTN_ERR_UNSUPPORTED;
   if (c->out_dtype != LSH_ATTN_FP32 && c->out_dtype != LSH_ATTN_BF16)
@@ -69,6 +71,17 @@ void free_ws(lsh::Workspace& w) {
   hipFree(w.hash.x16);
   hipFree(w.hash.xnorm);
   w = lsh::Workspace{};
+}
+
+void free_bw(lsh::BwdWorkspace& b) {
+  hipFree(b.o32);
+  hipFree(b.lse);
+  hipFree(b.w);
+  hipFree(b.cq);
+  hipFree(b.dq);
+  hipFree(b.dk);
+  hipFree(b.dv);
+  b = lsh::BwdWorkspace{};
 }
 
 template <typename T>
@@ -132,7 +145,15 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   }
   if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
     ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
+  if (ok && (p.flags & LSH_ATTN_FLAG_BACKWARD)) {
+    lsh::BwdWorkspace& b = h->bw;
+    ok = alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t) && alloc(&b.lse, rows * 4, t) &&
+         alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
+         alloc(&b.dq, rows * p.d * 4, t) && alloc(&b.dk, rows * p.d * 4, t) &&
+         alloc(&b.dv, rows * p.d * 4, t);
+  }
   if (!ok) {
+    free_bw(h->bw);
     free_ws(w);
     delete h;
     return LSH_ATTN_ERR_OUT_OF_MEMORY;
@@ -192,6 +213,25 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   mark(6);
   if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, s);
   mark(7);
+  if (e == hipSuccess) e = hipGetLastError();
+  return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
+}
+
+int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
+                      const void* dout, void* dqk, void* dv, void* stream) {
+  if (!h || !qk || !v || !perm || !dout || !dqk || !dv) return LSH_ATTN_ERR_INVALID_ARG;
+  const lsh::Problem& p = h->p;
+  if (!(p.flags & LSH_ATTN_FLAG_BACKWARD)) return LSH_ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(qk) || !aligned16(v) || !aligned16(dout) || !aligned16(dqk) || !aligned16(dv))
+    return LSH_ATTN_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return LSH_ATTN_ERR_INVALID_ARG;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  hipError_t e = lsh::launch_backward(p, qk, v, perm, dout, dqk, dv, h->ws.knorm, h->bw, s);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
 }
@@ -274,6 +314,7 @@ int lsh_attn_destroy(lsh_attn_t h) {
                         hipSetDevice(h->device) == hipSuccess;
   const hipError_t e = hipDeviceSynchronize();
   destroy_events(h);
+  free_bw(h->bw);
   free_ws(h->ws);
   if (switched) hipSetDevice(prev);
   delete h;
