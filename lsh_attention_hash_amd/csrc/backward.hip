@@ -18,6 +18,9 @@
 // w_r(i) dout(i) to v_i. Key normalisation khat = k / |k| (0 for k = 0):
 //   dk_j = (dkhat_j - khat_j (khat_j . dkhat_j)) / |k_j|,  dqk = dq + dk.
 //
+// On the matrix-core path (bf16, chunk_len 64, d in {64, 128}) the dq and
+// (dkhat, dv) products run in backward_mfma.hip instead of the two kernels
+// below, with the same outputs.
 // Launches (one stream): the per-round attention is recomputed from the
 // forward's permutation (fp32 rows and logsumexps); per position, the round
 // weights and dout . out; per round, dq of every query and dkhat, dv of every
@@ -273,13 +276,16 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
 
 template <int D, typename T>
 void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-              const void* dout, void* dqk, void* dvo, BwdWorkspace& b, hipStream_t s) {
+              const void* dout, void* dqk, void* dvo, const float* knorm, BwdWorkspace& b,
+              hipStream_t s) {
   const int64_t rpb = 256 / (D / 8);
   const int64_t nt = p.n_token_heads(), nr = p.n_rows();
   const dim3 gt((unsigned)((nt + rpb - 1) / rpb)), gr((unsigned)((nr + rpb - 1) / rpb));
   hipLaunchKernelGGL((k_bwd_rows<D, T>), gt, dim3(256), 0, s, b.o32, b.lse, (const T*)v,
                      (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
-  if (p.causal) {
+  if (attend_mfma_supported(p)) {
+    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
+  } else if (p.causal) {
     hipLaunchKernelGGL((k_bwd_dq<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
@@ -311,11 +317,11 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
   if (e != hipSuccess) return e;
   const bool bf = p.dtype == LSH_ATTN_BF16;
   if (p.d == 64) {
-    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, b, s);
-    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, b, s);
+    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
+    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
   } else {
-    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, b, s);
-    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, b, s);
+    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
+    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
   }
   return hipGetLastError();
 }

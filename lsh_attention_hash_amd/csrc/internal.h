@@ -113,6 +113,11 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
                            const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
                            hipStream_t s);
 
+// the dq and (dkhat, dv) products on matrix cores (attend_mfma_supported shapes)
+hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
+                                const int32_t* perm, const void* dout, const float* knorm,
+                                BwdWorkspace& b, hipStream_t s);
+
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.
 inline bool round_outputs_half(const Problem& p) {
