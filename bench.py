@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Forward throughput of Reformer shared-QK LSH attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload text64k]
+    python bench.py [--steps K] [--warmup W] [--workload text64k] [--backward]
 
 One step is one whole forward (hash, sort, gather, chunked attention, unsort
 and combine) over one batch of seeded synthetic inputs already resident in
@@ -9,6 +9,11 @@ HBM. Prints ONE JSON line: tokens/s (batch * seq_len / seconds per forward),
 the roofline of the dominant kernel (per-stage HIP events recorded by the
 library on the launch stream during the timed region), and the fp64 oracle
 timed on the host cores over a bounded sample of the same workload.
+
+With --backward, one step is one backward (gradients of qk and v for a seeded
+dout, at the permutation of one forward of the same inputs), with the same
+line layout: tokens/s of backwards, the dominant backward kernel's roofline,
+and the oracle's backward on a bounded sample.
 """
 from __future__ import annotations
 
@@ -23,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "LSH-attn fwd tokens/sec at L=64K, 4 rounds; % MFMA / HBM roofline"
+METRIC_BWD = "LSH-attn bwd tokens/sec at L=64K, 4 rounds; % MFMA / HBM roofline"
 
 # MI355X published peaks
 PEAK = {
@@ -74,9 +80,41 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None):
     }
 
 
+def backward_units(w, out_dtype: str):
+    """Per-launch algorithmic work of each backward stage (matrix-core path:
+    bf16 inputs, fp32 per-round gradients). N token-heads, R rounds, d, m as
+    above; a round's window is 2m keys per query. Rows are read through the
+    permutation once per (round, slot); the per-round gradients are fp32 rows
+    at original positions."""
+    N = w.batch * w.heads * w.seq_len
+    R, d, m = w.n_rounds, w.head_dim, w.chunk_len
+    e, eo = esize(w.dtype), esize(out_dtype)
+    return {
+        # attention at the permutation (as the forward's) with dout read per
+        # query-round; per query-round lse and dout . o_r written; key norms
+        "recompute": {"flops": N * R * 4 * d * 2 * m,
+                      "bytes": N * R * (3 * d * e + 4 + 4 + 4) + N * (d * e + 4)},
+        # lse and dout . o_r per round, v and dout rows; round weights, dout . out
+        "rows": {"bytes": N * R * (4 + 4 + 4) + N * (2 * d * e + 4)},
+        # per query-round: S, dP and dQ over its 2m-key window; qk, v, dout
+        # rows, perm, lse, weight, dout . out, key norm read; fp32 dq row written
+        "dq": {"flops": N * R * 3 * 2 * d * 2 * m,
+               "bytes": N * R * (3 * d * e + 5 * 4 + d * 4)},
+        # per key-round: S, dP, dkhat and dv over the 2m queries that see it;
+        # the same reads, fp32 dkhat and dv rows written
+        "dkv": {"flops": N * R * 4 * 2 * d * 2 * m,
+                "bytes": N * R * (3 * d * e + 5 * 4 + 2 * d * 4)},
+        # R rounds of fp32 dq, dkhat, dv rows, lse and weight; qk and dout
+        # rows; dqk and dv written
+        "reduce": {"bytes": N * R * (3 * d * 4 + 8) + N * 2 * d * e + N * 2 * d * eo},
+    }
+
+
 # The matrix-core peak each stage's contraction runs at (fp16 projection,
 # bf16 attention); HBM for the rest; fp64 vector for the exact re-scoring.
-MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs"}
+MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs",
+             "recompute": "mfma_bf16_TFLOPs", "dq": "mfma_bf16_TFLOPs",
+             "dkv": "mfma_bf16_TFLOPs"}
 
 
 def stage_bound(stage: str, u: dict):
@@ -105,7 +143,8 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
         achieved = u["flops"] / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
     peak = PEAK[peak_key]
-    return {"kernel": STAGE_KERNEL.get(stage, stage), "stage": stage, "bound": bound,
+    return {"kernel": STAGE_KERNEL.get(stage, BWD_STAGE_KERNEL.get(stage, stage)),
+            "stage": stage, "bound": bound,
             "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 5), "traffic": traffic,
             "algorithmic_bytes": u.get("bytes"),
@@ -115,10 +154,14 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
 # Stages that are exactly one kernel launch (name as rocprofv3 reports it),
 # and the source files each stage's kernels are built from.
 STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine"}
+BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "dq": "k_bwd_dq_mfma", "dkv": "k_bwd_dkv_mfma",
+                    "reduce": "k_bwd_reduce"}
 STAGE_SOURCES = {
     "hash_prep": ["hash_mfma.hip"], "hash": ["hash_mfma.hip", "hash.hip"],
     "hash_rescore": ["hash_mfma.hip"], "sort": ["sort.hip"], "gather": ["gather.hip"],
     "attend": ["attend_mfma.hip", "attend.hip"], "combine": ["combine.hip"],
+    "recompute": ["attend_mfma.hip", "backward.hip"], "rows": ["backward.hip"],
+    "dq": ["backward_mfma.hip"], "dkv": ["backward_mfma.hip"], "reduce": ["backward.hip"],
 }
 
 
@@ -161,6 +204,150 @@ def cpu_baseline(w, inp, heads: int):
             "seconds": round(t, 3), "cpu_model": model, "threads_available": threads}
 
 
+def calibration_copy(mib: int, dev):
+    """After the timed region: copy `mib` MiB device to device three times (the
+    reference dispatch for scaling FETCH_SIZE / WRITE_SIZE)."""
+    if mib <= 0:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def cpu_baseline_backward(w, inp, heads: int):
+    """The fp64 oracle's backward as it stands, on batch 0 and the first
+    `heads` heads at full sequence length, all rounds, at the oracle forward's
+    permutation (not timed); scaled to tokens/s of the whole workload."""
+    import numpy as np
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    env_threads = os.environ.get("OMP_NUM_THREADS")
+    if env_threads:
+        threads = min(threads, int(env_threads))
+    sub = w.with_(batch=1, heads=heads)
+    c = oracle.config(sub)
+    qk = np.ascontiguousarray(inp.qk[:1, :heads], dtype=np.float64)
+    v = np.ascontiguousarray(inp.v[:1, :heads], dtype=np.float64)
+    rot = None if inp.rotations is None else inp.rotations.astype(np.float64)
+    dout = np.random.default_rng(5).standard_normal(qk.shape)
+    oracle.build(force=False)
+    perm = oracle.forward(c, qk, v, rot)["perm"]
+    t0 = time.perf_counter()
+    oracle.backward(c, qk, v, perm, dout)
+    t = time.perf_counter() - t0
+    frac = heads / (w.batch * w.heads)
+    return {"value": round(w.batch * w.seq_len * frac / t, 3), "unit": "tokens/s",
+            "cores": min(threads, heads), "kind": "oracle",
+            "sample": f"batch 0, heads 0..{heads - 1} of {w.heads}, full L={w.seq_len}, "
+                      f"all {w.n_rounds} rounds ({frac:.4f} of the workload), fp64 oracle "
+                      f"backward in {t:.2f} s (its forward's permutation made first, not "
+                      f"timed); OpenMP over (batch, head)",
+            "seconds": round(t, 3), "threads_available": threads}
+
+
+def main_backward(args, w, inp, op_kw):
+    """The --backward line (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import lsh_attention_hash_amd as lat
+
+    dev = torch.device("cuda", 0)
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}
+    if w.dtype == "bf16":
+        qk = torch.from_numpy(inp.qk_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        v = torch.from_numpy(inp.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        qk = torch.from_numpy(inp.qk).to(dev)
+        v = torch.from_numpy(inp.v).to(dev)
+    rot = None if inp.rotations is None else torch.from_numpy(inp.rotations).to(dev)
+    op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
+                          w.chunk_len, w.causal, dtype=tdt[w.dtype], backward=True, **op_kw)
+    _, ex = op(qk, v, rot, return_perm=True)
+    perm = ex["perm"]
+    g = torch.Generator(device="cpu").manual_seed(5)
+    dout = torch.randn((w.batch, w.heads, w.seq_len, w.head_dim), generator=g).to(
+        tdt[w.dtype]).to(dev)
+    dqk = torch.empty_like(qk)
+    dv = torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        op.backward(qk, v, perm, dout, dqk, dv)
+    torch.cuda.synchronize()
+    op.set_timing(args.steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        op.backward(qk, v, perm, dout, dqk, dv)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    stage_ms, n_timed = op.get_backward_timing()
+    stage_avg = {k: v_ / max(n_timed, 1) for k, v_ in stage_ms.items()}
+    op.close()
+    calibration_copy(args.calib_copy_mib, dev)
+
+    units = backward_units(w, w.dtype)
+    single = {k: v_ for k, v_ in stage_avg.items() if k in BWD_STAGE_KERNEL}
+    dominant = max(single, key=single.get)
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                entry = json.load(f).get(args.workload + ":backward", {}).get(dominant)
+            if entry and entry.get("source_hash") == kernel_source_hash(dominant):
+                traffic = entry.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    rl = roofline(dominant, units, stage_avg[dominant], traffic)
+    per_stage = {}
+    for k, t in stage_avg.items():
+        per_stage[k] = {"ms": round(t, 5)}
+        if t > 0:
+            r = roofline(k, units, t)
+            per_stage[k].update({"achieved": r["achieved"], "unit": r["unit"],
+                                 "frac": r["frac"], "bound": r["bound"]})
+    tokens = w.batch * w.seq_len
+    res = {
+        "metric": METRIC_BWD,
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "heads": w.heads,
+                   "seq_len": w.seq_len, "head_dim": w.head_dim, "n_buckets": w.n_buckets,
+                   "n_rounds": w.n_rounds, "chunk_len": w.chunk_len, "causal": w.causal,
+                   "qk_v_dtype": w.dtype,
+                   "inputs": f"{w.kind} seeded (qk {1000 + w.seed_base}, v {2000 + w.seed_base},"
+                             f" R {3000 + w.seed_base}); dout torch seed 5, standard normal",
+                   "per_round_gradients": "fp32"},
+        "roofline": rl,
+        "stages": per_stage,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        heads = args.cpu_heads or max(1, min(w.heads, len(os.sched_getaffinity(0)) // 4))
+        res["cpu_baseline"] = cpu_baseline_backward(w, inp, heads)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -170,6 +357,8 @@ def main():
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "fp32"])
     ap.add_argument("--separate-gather", action="store_true")
     ap.add_argument("--fp32-round-outputs", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward instead of the forward (its own JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: as many as rounds fit the cores)")
@@ -204,6 +393,10 @@ def main():
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.backward:
+        main_backward(args, w, inp, {"separate_gather": args.separate_gather,
+                                     "fp32_round_outputs": args.fp32_round_outputs})
+        return
     if w.dtype == "bf16":
         qk = torch.from_numpy(inp.qk_bits.view(np.int16)).to(dev).view(torch.bfloat16)
         v = torch.from_numpy(inp.v_bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -240,14 +433,7 @@ def main():
     stage_avg = {k: v_ / max(n_timed, 1) for k, v_ in stage_ms.items()}
     stats = op.stats()
 
-    if args.calib_copy_mib > 0:
-        nbytes = args.calib_copy_mib << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args.calib_copy_mib, dev)
 
     fp16_rounds = w.dtype == "bf16" and w.chunk_len == 64 and not args.fp32_round_outputs
     units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4, stats)
@@ -366,8 +552,9 @@ def write_traffic(args):
     if os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             out = json.load(f)
-    entry = out.setdefault(args.workload, {})
-    for stage, kname in STAGE_KERNEL.items():
+    key = args.workload + (":backward" if args.backward else "")
+    entry = out.setdefault(key, {})
+    for stage, kname in (BWD_STAGE_KERNEL if args.backward else STAGE_KERNEL).items():
         f_kib, w_kib = mean_of(fetch, kname), mean_of(write, kname)
         if f_kib is None or w_kib is None:
             continue

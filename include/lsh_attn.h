@@ -177,6 +177,21 @@ int lsh_attn_set_timing(lsh_attn_t handle, int capacity);
  */
 int lsh_attn_get_timing(lsh_attn_t handle, double* ms, int64_t* n_forwards);
 
+/*
+ * The same for lsh_attn_backward: with timing enabled (lsh_attn_set_timing,
+ * the same capacity, counted separately), each backward records an event
+ * before its first stage and after every stage. Stages: 0 recomputation of the
+ * per-round attention (key norms and the chunk attention at the given
+ * permutation), 1 per-position round weights and dout . out, 2 the per-round
+ * dq of every query, 3 the per-round dkhat and dv of every key, 4 the sum over
+ * rounds with the key normalisation. ms has LSH_ATTN_N_BWD_STAGES entries
+ * (host memory); n_backwards receives the number of timed backwards, and the
+ * accumulation restarts.
+ * Errors: INVALID_ARG for null pointers or timing not enabled; HIP on event errors.
+ */
+#define LSH_ATTN_N_BWD_STAGES 5
+int lsh_attn_get_backward_timing(lsh_attn_t handle, double* ms, int64_t* n_backwards);
+
 /* Bytes of device workspace the handle holds. INVALID_ARG for null pointers. */
 int lsh_attn_workspace_bytes(lsh_attn_t handle, int64_t* bytes);
 

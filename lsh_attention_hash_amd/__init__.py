@@ -30,10 +30,12 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "H
 # Every function declared in include/lsh_attn.h.
 EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward",
                     "lsh_attn_get_stats",
-                    "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_workspace_bytes",
-                    "lsh_attn_destroy", "lsh_attn_strerror")
+                    "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
+                    "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror")
 N_STAGES = 7
 STAGES = ("hash_prep", "hash", "hash_rescore", "sort", "gather", "attend", "combine")
+N_BWD_STAGES = 5
+BWD_STAGES = ("recompute", "rows", "dq", "dkv", "reduce")
 
 
 class LSHAttnError(RuntimeError):
@@ -77,12 +79,14 @@ def load_library():
     lib.lsh_attn_set_timing.argtypes = [P, I]
     lib.lsh_attn_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64)]
+    lib.lsh_attn_get_backward_timing.argtypes = [P, ctypes.POINTER(ctypes.c_double),
+                                                 ctypes.POINTER(ctypes.c_int64)]
     lib.lsh_attn_destroy.argtypes = [P]
     lib.lsh_attn_strerror.argtypes = [I]
     lib.lsh_attn_strerror.restype = ctypes.c_char_p
     for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward", "lsh_attn_get_stats",
-              "lsh_attn_set_timing",
-              "lsh_attn_get_timing", "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
+              "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
+              "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
         getattr(lib, n).restype = I
     _lib = lib
     return lib
@@ -232,6 +236,16 @@ class LSHAttention:
         if rc != 0:
             raise LSHAttnError(rc, "lsh_attn_get_timing", self.lib)
         return {k: float(ms[j]) for j, k in enumerate(STAGES)}, int(n.value)
+
+    def get_backward_timing(self):
+        """(dict backward stage -> summed ms, number of timed backwards); resets
+        the sums. Timing is enabled by set_timing (handles made with backward=True)."""
+        ms = (ctypes.c_double * N_BWD_STAGES)()
+        n = ctypes.c_int64()
+        rc = self.lib.lsh_attn_get_backward_timing(self.handle, ms, ctypes.byref(n))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_get_backward_timing", self.lib)
+        return {k: float(ms[j]) for j, k in enumerate(BWD_STAGES)}, int(n.value)
 
     def workspace_bytes(self) -> int:
         b = ctypes.c_int64()

@@ -47,6 +47,8 @@
 // or 16 (fp32) contiguous bytes. An MFMA against a block of ones gives the row
 // sums of the bf16-rounded P, so numerator and denominator use the same
 // weights; the logsumexp takes the fp32 sum of the unrounded p.
+#include <type_traits>
+
 #include "dtype.h"
 #include "internal.h"
 
@@ -205,12 +207,16 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 
 // LDS allows two workgroups (8 waves) per CU at d = 128, so each wave may take
 // half the register file; say so, or the compiler aims for more waves.
-template <int D, typename OT, bool CAUSAL, bool SORTED>
+// DOT (the backward's recomputation): instead of the round's rows, o receives
+// per query the scalar dout(i) . o_r(i) ([seg, L] fp32; 0 for a query that saw
+// only itself), dout being bf16 rows [B*H, L, D].
+template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attend_mfma(
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
     const uint4* __restrict__ v_s, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
-    int nseg, int chunks_per_wg, int ranges, int group_segs, int64_t o_seg_rows) {
+    int nseg, int chunks_per_wg, int ranges, int group_segs, int64_t o_seg_rows,
+    const unsigned char* __restrict__ dout) {
   using Lay = Lds<D>;
   constexpr int KS = D / 32;  // 32-dim K-steps of QK^T
   constexpr int DT = D / 16;  // 16-dim tiles of the output
@@ -290,6 +296,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int q = 16 * w + lq;
     float mq = kbound[cur * kChunk + q];
     const int posq = kpos[cur * kChunk + q];
+    // DOT: the query's dout, dims 16 dt + 4g + 0..3 (as the output tiles)
+    uint2 dz[DOT ? DT : 1];
+    if constexpr (DOT) {
+      const unsigned char* drow = dout + ((row0 + posq) * D + 4 * g) * 2;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dz[dt] = *(const uint2*)(drow + 32 * dt);
+    }
     bf16x8_t qf[KS];
     {
       const unsigned char* row = lds + Lay::kKt + (cur * kChunk + q) * Lay::kRow;
@@ -403,7 +416,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const bool seen = l > 0.f;
       const float inv = seen ? 1.0f / l : 0.f;
       OT* orow = o + (seg * o_seg_rows + posq) * D;
-      if constexpr (sizeof(OT) == 2) {
+      if constexpr (DOT) {
+        float d = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          d = fmaf(oacc[dt][0], __uint_as_float(dz[dt].x << 16), d);
+          d = fmaf(oacc[dt][1], __uint_as_float(dz[dt].x & 0xFFFF0000u), d);
+          d = fmaf(oacc[dt][2], __uint_as_float(dz[dt].y << 16), d);
+          d = fmaf(oacc[dt][3], __uint_as_float(dz[dt].y & 0xFFFF0000u), d);
+        }
+        d += __shfl_xor(d, 16);
+        d += __shfl_xor(d, 32);
+        if (g == 0) o[seg * L + posq] = d * inv;
+      } else if constexpr (sizeof(OT) == 2) {
         // fp16: tiles t and t + 1 packed as 2 words per lane, then one swap of
         // odd and even 16-lane rows leaves lane group g with 8 consecutive
         // dims, 16(t + g%2) + 8(g/2) + 0..7, one 16-byte store per tile pair
@@ -445,9 +470,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 constexpr int kRangeChunks = 16;
 constexpr int kResidentBlocks = 512;
 
-template <int D, typename OT, bool CAUSAL, bool SORTED>
+template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false>
 void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_s,
-                const void* v_s, const int32_t* perm, const float* knorm, OT* o, float* lse, hipStream_t s) {
+                const void* v_s, const int32_t* perm, const float* knorm, OT* o, float* lse,
+                hipStream_t s, const void* dout = nullptr) {
   const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
   const int per = nchunks < kRangeChunks ? nchunks : kRangeChunks;
@@ -458,10 +484,11 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
   int64_t group_segs = heads * p.R;
   if (group_segs > nseg) group_segs = nseg;
   const size_t shmem = Lds<D>::kBytes;
-  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED>), dim3((unsigned)(nseg * ranges)),
+  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED, DOT>), dim3((unsigned)(nseg * ranges)),
                      dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
                      (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse, p.L,
-                     p.R, (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows());
+                     p.R, (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows(),
+                     (const unsigned char*)dout);
 }
 
 template <int D, typename OT>
@@ -502,6 +529,31 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
   }
   if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
   else launch_d<128, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* v,
+                                  const int32_t* perm, const float* knorm, const void* dout,
+                                  float* od, float* lse, hipStream_t s) {
+  static bool configured = false;
+  if (!configured) {
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, float, true, false, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, float, false, false, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    configured = true;
+  }
+  auto go = [&](auto d) {
+    constexpr int D = decltype(d)::value;
+    if (p.causal)
+      launch_one<D, float, true, false, true>(p, qk, v, nullptr, nullptr, perm, knorm, od, lse, s,
+                                              dout);
+    else
+      launch_one<D, float, false, false, true>(p, qk, v, nullptr, nullptr, perm, knorm, od, lse,
+                                               s, dout);
+  };
+  if (p.d == 64) go(std::integral_constant<int, 64>{});
+  else go(std::integral_constant<int, 128>{});
   return hipGetLastError();
 }
 

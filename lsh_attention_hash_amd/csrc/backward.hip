@@ -22,8 +22,9 @@
 // (dkhat, dv) products run in backward_mfma.hip instead of the two kernels
 // below, with the same outputs.
 // Launches (one stream): the per-round attention is recomputed from the
-// forward's permutation (fp32 rows and logsumexps); per position, the round
-// weights and dout . out; per round, dq of every query and dkhat, dv of every
+// forward's permutation (fp32 rows and logsumexps; on the matrix-core path only
+// the logsumexps and dout . o_r per query); per position, the round weights
+// and dout . out; per round, dq of every query and dkhat, dv of every
 // key (each key is seen by the queries of its chunk and of the next one); then
 // the sum over rounds with the normalisation, in the caller's dtype. Every
 // output element is written by one thread: no atomics, deterministic.
@@ -120,6 +121,44 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const float* __restrict__ o,
   load8<T>(dout + row * D + sub * 8, dz);
   const float c = row_sum<kLpr>(dot8(dz, acc));
   if (sub == 0) cq[row] = c;
+}
+
+// As k_bwd_rows, from the per-round scalars od_r(i) = dout(i) . o_r(i) of the
+// matrix-core recomputation: dout . out = sum_r w_r od_r, with dout(i) . v_i for
+// a round in which the position saw only itself.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_bwd_rows_dot(const float* __restrict__ od,
+                                                      const float* __restrict__ lse,
+                                                      const T* __restrict__ v,
+                                                      const T* __restrict__ dout,
+                                                      float* __restrict__ w,
+                                                      float* __restrict__ cq, int L, int R,
+                                                      int64_t n_rows) {
+  constexpr int kLpr = D / 8;
+  const int sub = threadIdx.x % kLpr;
+  const int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
+  if (row >= n_rows) return;
+  const int64_t bh = row / L, i = row - bh * L;
+  float vi[8], dz[8];
+  load8<T>(v + row * D + sub * 8, vi);
+  load8<T>(dout + row * D + sub * 8, dz);
+  const float vd = row_sum<kLpr>(dot8(dz, vi));
+  if (sub != 0) return;
+  const float* lr = lse + bh * R * L + i;
+  const float* dr = od + bh * R * L + i;
+  float mx = -INFINITY;
+  for (int r = 0; r < R; ++r) mx = fmaxf(mx, lr[(int64_t)r * L]);
+  float sum = 0.f;
+  for (int r = 0; r < R; ++r) sum += __expf(lr[(int64_t)r * L] - mx);
+  const float inv = 1.0f / sum;
+  float c = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const float l = lr[(int64_t)r * L];
+    const float wr = __expf(l - mx) * inv;
+    w[(bh * R + r) * L + i] = wr;
+    c = fmaf(wr, l == kSelfLogit ? vd : dr[(int64_t)r * L], c);
+  }
+  cq[row] = c;
 }
 
 // dq of the query at slot s of segment seg (one D/8-lane row group per
@@ -277,51 +316,65 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
 template <int D, typename T>
 void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* perm,
               const void* dout, void* dqk, void* dvo, const float* knorm, BwdWorkspace& b,
-              hipStream_t s) {
+              hipStream_t s, const hipEvent_t* ev) {
+  auto mark = [&](int j) {
+    if (ev) (void)hipEventRecord(ev[j], s);
+  };
   const int64_t rpb = 256 / (D / 8);
   const int64_t nt = p.n_token_heads(), nr = p.n_rows();
   const dim3 gt((unsigned)((nt + rpb - 1) / rpb)), gr((unsigned)((nr + rpb - 1) / rpb));
-  hipLaunchKernelGGL((k_bwd_rows<D, T>), gt, dim3(256), 0, s, b.o32, b.lse, (const T*)v,
-                     (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
+  if (attend_mfma_supported(p))
+    hipLaunchKernelGGL((k_bwd_rows_dot<D, T>), gt, dim3(256), 0, s, b.od, b.lse, (const T*)v,
+                       (const T*)dout, b.w, b.cq, p.L, p.R, nt);
+  else
+    hipLaunchKernelGGL((k_bwd_rows<D, T>), gt, dim3(256), 0, s, b.o32, b.lse, (const T*)v,
+                       (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
+  mark(2);
   if (attend_mfma_supported(p)) {
-    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
+    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s, ev ? ev[3] : nullptr);
   } else if (p.causal) {
     hipLaunchKernelGGL((k_bwd_dq<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
+    mark(3);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr);
   } else {
     hipLaunchKernelGGL((k_bwd_dq<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
+    mark(3);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr);
   }
+  mark(4);
   hipLaunchKernelGGL((k_bwd_reduce<D, T>), gt, dim3(256), 0, s, (const T*)qk, (const T*)dout,
                      b.lse, b.w, b.dq, b.dk, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
+  mark(5);
 }
 
 }  // namespace
 
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                            const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
-                           hipStream_t s) {
+                           hipStream_t s, const hipEvent_t* ev) {
   // the per-round attention, recomputed from the permutation in fp32
   hipError_t e;
+  if (ev) (void)hipEventRecord(ev[0], s);
   if (attend_mfma_supported(p)) {
     e = launch_key_norms(p, qk, knorm, s);
     if (e == hipSuccess)
-      e = launch_attend_mfma<float>(p, qk, v, nullptr, nullptr, perm, knorm, b.o32, b.lse, s);
+      e = launch_attend_mfma_dot(p, qk, v, perm, knorm, dout, b.od, b.lse, s);
   } else {
     e = launch_attend(p, qk, v, nullptr, nullptr, perm, nullptr, b.o32, b.lse, s);
   }
   if (e != hipSuccess) return e;
+  if (ev) (void)hipEventRecord(ev[1], s);
   const bool bf = p.dtype == LSH_ATTN_BF16;
   if (p.d == 64) {
-    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
-    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
+    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
+    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
   } else {
-    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
-    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s);
+    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
+    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
   }
   return hipGetLastError();
 }

@@ -402,11 +402,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(
 
 template <int D, bool CAUSAL>
 void launch_d(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-              const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
+              const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s,
+              hipEvent_t after_dq) {
   const dim3 grid((unsigned)(p.nseg() * (p.L / kChunk)));
   hipLaunchKernelGGL((k_bwd_dq_mfma<D, CAUSAL>), grid, dim3(kThreads), DqLds<D>::kBytes, s,
                      (const unsigned char*)qk, (const unsigned char*)v,
                      (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, b.dq, p.L, p.R);
+  if (after_dq) (void)hipEventRecord(after_dq, s);
   hipLaunchKernelGGL((k_bwd_dkv_mfma<D, CAUSAL>), grid, dim3(kThreads), DkvLds<D>::kBytes, s,
                      (const unsigned char*)qk, (const unsigned char*)v,
                      (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, b.dk, b.dv, p.L,
@@ -429,7 +431,7 @@ void configure() {
 
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
-                                BwdWorkspace& b, hipStream_t s) {
+                                BwdWorkspace& b, hipStream_t s, hipEvent_t after_dq) {
   static bool configured = false;
   if (!configured) {
     configure<64>();
@@ -437,11 +439,11 @@ hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
     configured = true;
   }
   if (p.d == 64) {
-    if (p.causal) launch_d<64, true>(p, qk, v, perm, dout, knorm, b, s);
-    else launch_d<64, false>(p, qk, v, perm, dout, knorm, b, s);
+    if (p.causal) launch_d<64, true>(p, qk, v, perm, dout, knorm, b, s, after_dq);
+    else launch_d<64, false>(p, qk, v, perm, dout, knorm, b, s, after_dq);
   } else {
-    if (p.causal) launch_d<128, true>(p, qk, v, perm, dout, knorm, b, s);
-    else launch_d<128, false>(p, qk, v, perm, dout, knorm, b, s);
+    if (p.causal) launch_d<128, true>(p, qk, v, perm, dout, knorm, b, s, after_dq);
+    else launch_d<128, false>(p, qk, v, perm, dout, knorm, b, s, after_dq);
   }
   return hipGetLastError();
 }

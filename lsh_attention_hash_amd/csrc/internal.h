@@ -64,7 +64,8 @@ struct Workspace {
 
 // Backward workspace (allocated with LSH_ATTN_FLAG_BACKWARD), fp32:
 struct BwdWorkspace {
-  float* o32 = nullptr;  // [seg, L + kORowPad, d] recomputed per-round rows
+  float* o32 = nullptr;  // [seg, L + kORowPad, d] recomputed per-round rows (plain path)
+  float* od = nullptr;   // [seg, L] dout . o_r per query (matrix-core path)
   float* lse = nullptr;  // [seg, L] recomputed per-round logsumexps
   float* w = nullptr;    // [seg, L] round weights of the combination
   float* cq = nullptr;   // [B*H, L] dout . out
@@ -103,20 +104,27 @@ template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
                               const float* knorm, OT* o, float* lse, hipStream_t s);
+// the per-round attention of the backward: lse as above, and per query the
+// scalar dout . o_r in od [seg, L] instead of the rows
+hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* v,
+                                  const int32_t* perm, const float* knorm, const void* dout,
+                                  float* od, float* lse, hipStream_t s);
 // o is fp16 when o_half, else fp32; v (the input values) supplies the rows of
 // rounds in which a query saw only itself
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
                           const void* v, void* out, hipStream_t s);
 
 // gradients of qk and v given dout, at the permutations perm of a forward
+// ev (may be null): 6 events, recorded before the recomputation and after
+// each of its 5 stages (recomputation, rows, dq, dkhat/dv, reduction)
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                            const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
-                           hipStream_t s);
+                           hipStream_t s, const hipEvent_t* ev);
 
 // the dq and (dkhat, dv) products on matrix cores (attend_mfma_supported shapes)
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
-                                BwdWorkspace& b, hipStream_t s);
+                                BwdWorkspace& b, hipStream_t s, hipEvent_t after_dq);
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.

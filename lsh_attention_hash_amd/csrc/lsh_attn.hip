@@ -24,6 +24,9 @@ struct lsh_attn_s {
   std::vector<hipEvent_t> events;
   int timing_capacity = 0;
   int timed = 0;
+  // the same for backwards: bevents[k * (N_BWD_STAGES + 1) + j]
+  std::vector<hipEvent_t> bevents;
+  int btimed = 0;
 };
 
 namespace {
@@ -75,6 +78,7 @@ void free_ws(lsh::Workspace& w) {
 
 void free_bw(lsh::BwdWorkspace& b) {
   hipFree(b.o32);
+  hipFree(b.od);
   hipFree(b.lse);
   hipFree(b.w);
   hipFree(b.cq);
@@ -147,7 +151,9 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
     ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
   if (ok && (p.flags & LSH_ATTN_FLAG_BACKWARD)) {
     lsh::BwdWorkspace& b = h->bw;
-    ok = alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t) && alloc(&b.lse, rows * 4, t) &&
+    ok = (lsh::attend_mfma_supported(p) ? alloc(&b.od, rows * 4, t)
+                                        : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
+         alloc(&b.lse, rows * 4, t) &&
          alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
          alloc(&b.dq, rows * p.d * 4, t) && alloc(&b.dk, rows * p.d * 4, t) &&
          alloc(&b.dv, rows * p.d * 4, t);
@@ -231,7 +237,11 @@ int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t
   }
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
-  hipError_t e = lsh::launch_backward(p, qk, v, perm, dout, dqk, dv, h->ws.knorm, h->bw, s);
+  const bool timing = h->btimed < h->timing_capacity;
+  const hipEvent_t* ev =
+      timing ? &h->bevents[(size_t)h->btimed * (LSH_ATTN_N_BWD_STAGES + 1)] : nullptr;
+  if (timing) ++h->btimed;
+  hipError_t e = lsh::launch_backward(p, qk, v, perm, dout, dqk, dv, h->ws.knorm, h->bw, s, ev);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
 }
@@ -251,9 +261,48 @@ int lsh_attn_get_stats(lsh_attn_t h, lsh_attn_stats_t* stats) {
 
 static void destroy_events(lsh_attn_s* h) {
   for (hipEvent_t e : h->events) hipEventDestroy(e);
+  for (hipEvent_t e : h->bevents) hipEventDestroy(e);
   h->events.clear();
+  h->bevents.clear();
   h->timing_capacity = 0;
   h->timed = 0;
+  h->btimed = 0;
+}
+
+// capacity * per events into v (false if one cannot be created)
+static bool create_events(std::vector<hipEvent_t>& v, size_t n) {
+  v.reserve(n);
+  for (size_t k = 0; k < n; ++k) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    v.push_back(e);
+  }
+  return true;
+}
+
+// Sum over the first `count` timed calls of each of `stages` stage durations.
+static int sum_stage_times(const std::vector<hipEvent_t>& events, int count, int stages,
+                           double* ms) {
+  for (int j = 0; j < stages; ++j) ms[j] = 0.0;
+  for (int k = 0; k < count; ++k) {
+    const hipEvent_t* ev = &events[(size_t)k * (stages + 1)];
+    if (hipEventSynchronize(ev[stages]) != hipSuccess) {
+      (void)hipGetLastError();
+      return LSH_ATTN_ERR_HIP;
+    }
+    for (int j = 0; j < stages; ++j) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, ev[j], ev[j + 1]) != hipSuccess) {
+        (void)hipGetLastError();
+        return LSH_ATTN_ERR_HIP;
+      }
+      ms[j] += t;
+    }
+  }
+  return LSH_ATTN_OK;
 }
 
 int lsh_attn_set_timing(lsh_attn_t h, int capacity) {
@@ -263,16 +312,11 @@ int lsh_attn_set_timing(lsh_attn_t h, int capacity) {
     return LSH_ATTN_ERR_HIP;
   }
   destroy_events(h);
-  const size_t n = (size_t)capacity * (LSH_ATTN_N_STAGES + 1);
-  h->events.reserve(n);
-  for (size_t k = 0; k < n; ++k) {
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) {
-      (void)hipGetLastError();
-      destroy_events(h);
-      return LSH_ATTN_ERR_HIP;
-    }
-    h->events.push_back(e);
+  if (!create_events(h->events, (size_t)capacity * (LSH_ATTN_N_STAGES + 1)) ||
+      ((h->p.flags & LSH_ATTN_FLAG_BACKWARD) &&
+       !create_events(h->bevents, (size_t)capacity * (LSH_ATTN_N_BWD_STAGES + 1)))) {
+    destroy_events(h);
+    return LSH_ATTN_ERR_HIP;
   }
   h->timing_capacity = capacity;
   return LSH_ATTN_OK;
@@ -280,24 +324,19 @@ int lsh_attn_set_timing(lsh_attn_t h, int capacity) {
 
 int lsh_attn_get_timing(lsh_attn_t h, double* ms, int64_t* n_forwards) {
   if (!h || !ms || !n_forwards || h->timing_capacity == 0) return LSH_ATTN_ERR_INVALID_ARG;
-  for (int j = 0; j < LSH_ATTN_N_STAGES; ++j) ms[j] = 0.0;
-  for (int k = 0; k < h->timed; ++k) {
-    hipEvent_t* ev = &h->events[(size_t)k * (LSH_ATTN_N_STAGES + 1)];
-    if (hipEventSynchronize(ev[LSH_ATTN_N_STAGES]) != hipSuccess) {
-      (void)hipGetLastError();
-      return LSH_ATTN_ERR_HIP;
-    }
-    for (int j = 0; j < LSH_ATTN_N_STAGES; ++j) {
-      float t = 0.f;
-      if (hipEventElapsedTime(&t, ev[j], ev[j + 1]) != hipSuccess) {
-        (void)hipGetLastError();
-        return LSH_ATTN_ERR_HIP;
-      }
-      ms[j] += t;
-    }
-  }
+  const int rc = sum_stage_times(h->events, h->timed, LSH_ATTN_N_STAGES, ms);
+  if (rc != LSH_ATTN_OK) return rc;
   *n_forwards = h->timed;
   h->timed = 0;
+  return LSH_ATTN_OK;
+}
+
+int lsh_attn_get_backward_timing(lsh_attn_t h, double* ms, int64_t* n_backwards) {
+  if (!h || !ms || !n_backwards || h->timing_capacity == 0) return LSH_ATTN_ERR_INVALID_ARG;
+  const int rc = sum_stage_times(h->bevents, h->btimed, LSH_ATTN_N_BWD_STAGES, ms);
+  if (rc != LSH_ATTN_OK) return rc;
+  *n_backwards = h->btimed;
+  h->btimed = 0;
   return LSH_ATTN_OK;
 }
 
