@@ -96,25 +96,21 @@ def backward_units(w, out_dtype: str):
                       "bytes": N * R * (3 * d * e + 4 + 4 + 4) + N * (d * e + 4)},
         # lse and dout . o_r per round, v and dout rows; round weights, dout . out
         "rows": {"bytes": N * R * (4 + 4 + 4) + N * (2 * d * e + 4)},
-        # per query-round: S, dP and dQ over its 2m-key window; qk, v, dout
-        # rows, perm, lse, weight, dout . out, key norm read; fp32 dq row written
-        "dq": {"flops": N * R * 3 * 2 * d * 2 * m,
-               "bytes": N * R * (3 * d * e + 5 * 4 + d * 4)},
-        # per key-round: S, dP, dkhat and dv over the 2m queries that see it;
-        # the same reads, fp32 dkhat and dv rows written
-        "dkv": {"flops": N * R * 4 * 2 * d * 2 * m,
-                "bytes": N * R * (3 * d * e + 5 * 4 + 2 * d * 4)},
-        # R rounds of fp32 dq, dkhat, dv rows, lse and weight; qk and dout
-        # rows; dqk and dv written
-        "reduce": {"bytes": N * R * (3 * d * 4 + 8) + N * 2 * d * e + N * 2 * d * eo},
+        # per (round, slot), over the 2m-key window of each query: S, dP once,
+        # then dQ, dkhat and dv; qk, v, dout rows, perm, lse, weight,
+        # dout . out and key norm read once; fp32 dqk and dv rows written
+        "products": {"flops": N * R * 5 * 2 * d * 2 * m,
+                     "bytes": N * R * (3 * d * e + 5 * 4 + 2 * d * 4)},
+        # R rounds of fp32 dqk and dv rows, lse and weight; dout rows; dqk
+        # and dv written
+        "reduce": {"bytes": N * R * (2 * d * 4 + 8) + N * d * e + N * 2 * d * eo},
     }
 
 
 # The matrix-core peak each stage's contraction runs at (fp16 projection,
 # bf16 attention); HBM for the rest; fp64 vector for the exact re-scoring.
 MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs",
-             "recompute": "mfma_bf16_TFLOPs", "dq": "mfma_bf16_TFLOPs",
-             "dkv": "mfma_bf16_TFLOPs"}
+             "recompute": "mfma_bf16_TFLOPs", "products": "mfma_bf16_TFLOPs"}
 
 
 def stage_bound(stage: str, u: dict):
@@ -154,14 +150,14 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
 # Stages that are exactly one kernel launch (name as rocprofv3 reports it),
 # and the source files each stage's kernels are built from.
 STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine"}
-BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "dq": "k_bwd_dq_mfma", "dkv": "k_bwd_dkv_mfma",
-                    "reduce": "k_bwd_reduce"}
+BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "products": "k_bwd_fused_mfma",
+                    "reduce": "k_bwd_reduce_sum"}
 STAGE_SOURCES = {
     "hash_prep": ["hash_mfma.hip"], "hash": ["hash_mfma.hip", "hash.hip"],
     "hash_rescore": ["hash_mfma.hip"], "sort": ["sort.hip"], "gather": ["gather.hip"],
     "attend": ["attend_mfma.hip", "attend.hip"], "combine": ["combine.hip"],
     "recompute": ["attend_mfma.hip", "backward.hip"], "rows": ["backward.hip"],
-    "dq": ["backward_mfma.hip"], "dkv": ["backward_mfma.hip"], "reduce": ["backward.hip"],
+    "products": ["backward_mfma.hip"], "reduce": ["backward.hip"],
 }
 
 

@@ -183,13 +183,13 @@ int lsh_attn_get_timing(lsh_attn_t handle, double* ms, int64_t* n_forwards);
  * before its first stage and after every stage. Stages: 0 recomputation of the
  * per-round attention (key norms and the chunk attention at the given
  * permutation), 1 per-position round weights and dout . out, 2 the per-round
- * dq of every query, 3 the per-round dkhat and dv of every key, 4 the sum over
- * rounds with the key normalisation. ms has LSH_ATTN_N_BWD_STAGES entries
+ * gradient products (dq of every query, dkhat and dv of every key), 3 the sum
+ * over rounds. ms has LSH_ATTN_N_BWD_STAGES entries
  * (host memory); n_backwards receives the number of timed backwards, and the
  * accumulation restarts.
  * Errors: INVALID_ARG for null pointers or timing not enabled; HIP on event errors.
  */
-#define LSH_ATTN_N_BWD_STAGES 5
+#define LSH_ATTN_N_BWD_STAGES 4
 int lsh_attn_get_backward_timing(lsh_attn_t handle, double* ms, int64_t* n_backwards);
 
 /* Bytes of device workspace the handle holds. INVALID_ARG for null pointers. */

@@ -34,8 +34,8 @@ EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward",
                     "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror")
 N_STAGES = 7
 STAGES = ("hash_prep", "hash", "hash_rescore", "sort", "gather", "attend", "combine")
-N_BWD_STAGES = 5
-BWD_STAGES = ("recompute", "rows", "dq", "dkv", "reduce")
+N_BWD_STAGES = 4
+BWD_STAGES = ("recompute", "rows", "products", "reduce")
 
 
 class LSHAttnError(RuntimeError):

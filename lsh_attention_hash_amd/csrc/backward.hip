@@ -19,8 +19,9 @@
 //   dk_j = (dkhat_j - khat_j (khat_j . dkhat_j)) / |k_j|,  dqk = dq + dk.
 //
 // On the matrix-core path (bf16, chunk_len 64, d in {64, 128}) the dq and
-// (dkhat, dv) products run in backward_mfma.hip instead of the two kernels
-// below, with the same outputs.
+// (dkhat, dv) products run in one kernel of backward_mfma.hip instead of the
+// two below; it also applies the normalisation per round, so its reduction
+// (k_bwd_reduce_sum) only sums.
 // Launches (one stream): the per-round attention is recomputed from the
 // forward's permutation (fp32 rows and logsumexps; on the matrix-core path only
 // the logsumexps and dout . o_r per query); per position, the round weights
@@ -313,6 +314,49 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
   store8(dv + row * D + sub * 8, gv);
 }
 
+// The same on the matrix-core path, whose per-round rows already hold
+// dq + the normalised key gradient (dqk_r) and dv_r: sums over rounds plus the
+// self-only value terms. Each per-round row is read once (non-temporal).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ dout,
+                                                        const float* __restrict__ lse,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ dqkr,
+                                                        const float* __restrict__ dvr,
+                                                        T* __restrict__ dqk, T* __restrict__ dv,
+                                                        int L, int R, int64_t n_rows) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  constexpr int kLpr = D / 8;
+  const int sub = threadIdx.x % kLpr;
+  const int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
+  if (row >= n_rows) return;
+  const int64_t bh = row / L, j = row - bh * L;
+  float gq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wself = 0.f;
+  for (int r = 0; r < R; ++r) {
+    const int64_t sr = (bh * R + r) * L + j;
+    const f32x4_t* a = (const f32x4_t*)(dqkr + sr * D + sub * 8);
+    const f32x4_t* c = (const f32x4_t*)(dvr + sr * D + sub * 8);
+    const f32x4_t a0 = __builtin_nontemporal_load(a), a1 = __builtin_nontemporal_load(a + 1);
+    const f32x4_t c0 = __builtin_nontemporal_load(c), c1 = __builtin_nontemporal_load(c + 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      gq[u] += a0[u];
+      gq[4 + u] += a1[u];
+      gv[u] += c0[u];
+      gv[4 + u] += c1[u];
+    }
+    if (lse[sr] == kSelfLogit) wself += w[sr];
+  }
+  float dz[8];
+  load8<T>(dout + row * D + sub * 8, dz);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) gv[u] = fmaf(wself, dz[u], gv[u]);
+  store8(dqk + row * D + sub * 8, gq);
+  store8(dv + row * D + sub * 8, gv);
+}
+
 template <int D, typename T>
 void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* perm,
               const void* dout, void* dqk, void* dvo, const float* knorm, BwdWorkspace& b,
@@ -331,24 +375,28 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
                        (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
   mark(2);
   if (attend_mfma_supported(p)) {
-    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s, ev ? ev[3] : nullptr);
-  } else if (p.causal) {
+    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
+    mark(3);
+    hipLaunchKernelGGL((k_bwd_reduce_sum<D, T>), gt, dim3(256), 0, s, (const T*)dout, b.lse, b.w,
+                       b.dq, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
+    mark(4);
+    return;
+  }
+  if (p.causal) {
     hipLaunchKernelGGL((k_bwd_dq<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
-    mark(3);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr);
   } else {
     hipLaunchKernelGGL((k_bwd_dq<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
-    mark(3);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
                        (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr);
   }
-  mark(4);
+  mark(3);
   hipLaunchKernelGGL((k_bwd_reduce<D, T>), gt, dim3(256), 0, s, (const T*)qk, (const T*)dout,
                      b.lse, b.w, b.dq, b.dk, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
-  mark(5);
+  mark(4);
 }
 
 }  // namespace

@@ -1,26 +1,17 @@
-// backward_mfma.hip -- the backward's dq and (dkhat, dv) products on gfx950
-// matrix cores (bf16 inputs, chunk_len 64, d in {64, 128}); same definition and
-// outputs as k_bwd_dq / k_bwd_dkv in backward.hip (see there for the chain
-// rule), computed per chunk with v_mfma_f32_16x16x32_bf16.
+// backward_mfma.hip -- the backward's per-round gradient products on gfx950
+// matrix cores (bf16 inputs, chunk_len 64, d in {64, 128}); same definition as
+// k_bwd_dq / k_bwd_dkv in backward.hip (see there for the chain rule), computed
+// per chunk with v_mfma_f32_16x16x32_bf16, one kernel for dq, dkhat and dv.
 //
-// dq: one workgroup per (segment, query chunk c), 4 waves x 16 queries. The
-//   window (chunks c-1 and c) is staged in LDS: qk rows row-major (Kt) and by
-//   pairs of 4-key groups (Kp: per dim the 4 keys of group a then of group
-//   a + 4, as the forward stages v), v rows row-major (Vt). Per wave:
-//     S^T  = K Q^T       (A = Kt rows, B = the queries' rows)
-//     dP^T = V dO^T      (A = Vt rows, B = the queries' dout rows)
-//     dS^T = w_q P (dP - dout.out) / (sqrt(d) |k|)    (registers)
-//     dQ^T = K^T dS^T    (A = Kp, B = dS^T of two 16-key blocks, in the
-//                         key order of the forward's P V product)
-// dkv: one workgroup per (segment, key chunk c), 4 waves x 16 keys; the
-//   queries that see the chunk are those of chunks c and c + 1, staged one
-//   chunk at a time (qk and dout rows, row-major and by pairs of groups).
-//   Per wave and 16-query block:
-//     S  = Q K^T, dP = dO V^T   (A = query rows, B = the wave's key rows)
-//     wP = w_q P, dS = wP (dP - dout.out)
-//   then over 32-query steps:
-//     dV^T    += dO^T (wP)      (A = dout by pairs of query groups)
-//     dkhat^T += Q^T dS / sqrt(d)
+// Operand layouts in LDS: qk and v rows row-major (one 16-byte piece per lane
+// and K-step of a product over dims), and qk and dout rows by pairs of 4-row
+// groups (per dim the 4 rows of group a, then of group a + 4, the layout of
+// the forward's P V product), which give a product over rows its A operand.
+// Per wave and 16-row block:
+//   S^T  = K Q^T,  dP^T = V dO^T                 (a query block, its 128 keys)
+//   dS^T = w_q P (dP - dout.out) / (sqrt(d) |k|)   -> dQ^T = K^T dS^T
+//   S    = Q K^T,  dP   = dO V^T                 (a key block, the chunk's queries)
+//   wP = w_q P, dS = wP (dP - dout.out)          -> dV^T += dO^T wP, dkhat^T += Q^T dS
 // Rows are written at original positions, once: no atomics, deterministic.
 #include "dtype.h"
 #include "internal.h"
@@ -107,167 +98,73 @@ __device__ __forceinline__ void zero_lds(unsigned char* p, int bytes) {
 }
 
 // -------------------------------------------------------------------------
+// Fused: one workgroup per (segment, range of consecutive chunks), 4 waves,
+// walking the range one query chunk c at a time with the keys of chunks c - 1
+// and c staged (slots alternate with the chunk's parity). Wave w owns query
+// block w and key block w (rows 16w .. 16w + 15) of every chunk:
+//   query block w of c: S^T, dP^T over the 128 keys, dS^T, dQ^T
+//   key block w of c - 1 and of c: S, dP over the 64 queries of c, then
+//     dV^T += dO^T (wP), dkhat^T += Q^T dS
+// The keys of chunk c - 1 have then seen every query (those of c - 1 in the
+// previous step, those of c now), so their rows are final: the wave holds
+// dq and dkhat of the same 16 positions (the rows of block w of chunk c - 1),
+// applies the key normalisation's Jacobian per round,
+//   dqk_r = dq_r + (dkhat_r - khat (khat . dkhat_r)) / |k|,
+// and writes dqk_r and dv_r once (fp32, original positions). A range's last
+// step takes the queries of the chunk after it for its last keys only; the
+// next range computes their dq. The next chunk's rows are loaded into
+// registers at the start of each step and staged after it.
 template <int D>
-struct DqLds {
+struct FLds {
   using L = BLay<D>;
-  static constexpr int kKt = 0;                         // [2][64 rows]
-  static constexpr int kVt = kKt + 2 * L::kRM;
-  static constexpr int kKp = kVt + 2 * L::kRM;          // [2][8 pairs]
-  static constexpr int kScale = kKp + 2 * L::kPM;       // [2][64] log2(e) / (sqrt(d) |k|)
-  static constexpr int kPos = kScale + 2 * kChunk * 4;  // [2][64]
-  static constexpr int kBytes = kPos + 2 * kChunk * 4;
+  static constexpr int kKt = 0;                           // [2 slots][64] qk rows
+  static constexpr int kVt = kKt + 2 * L::kRM;            // [2][64] v rows
+  static constexpr int kKp = kVt + 2 * L::kRM;            // [2] qk rows by group pairs
+  static constexpr int kDt = kKp + 2 * L::kPM;            // dout rows of the query chunk
+  static constexpr int kDp = kDt + L::kRM;                // the same by group pairs
+  static constexpr int kKScale = kDp + L::kPM;            // [2][64] log2(e) / (sqrt(d) |k|)
+  static constexpr int kKPos = kKScale + 2 * kChunk * 4;  // [2][64] original positions
+  static constexpr int kQLse = kKPos + 2 * kChunk * 4;    // [64] lse * log2(e) of the queries
+  static constexpr int kQW = kQLse + kChunk * 4;          // [64] round weight
+  static constexpr int kQC = kQW + kChunk * 4;            // [64] dout . out
+  static constexpr int kPn = kQC + kChunk * 4;            // [64] positions of the next chunk
+  static constexpr int kBytes = kPn + kChunk * 4;
 };
 
+// one chunk's rows and scalars between their loads and the staging
+struct FRegs {
+  uint4 k[4], v[4], d[4];
+  int pos;
+  float n2, lse, w, c;
+};
+
+// Chunks per workgroup, and workgroups in flight the grid order is shaped for.
+constexpr int kFusedRange = 16;
+constexpr int kFusedResident = 256;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void k_bwd_dq_mfma(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void k_bwd_fused_mfma(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const unsigned char* __restrict__ dout, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
-    const float* __restrict__ cq, float* __restrict__ dq, int L, int R) {
+    const float* __restrict__ cq, float* __restrict__ dqk_r, float* __restrict__ dv_r, int L,
+    int R, int nseg, int chunks_per_wg, int ranges, int group_segs) {
   using Lay = BLay<D>;
-  using M = DqLds<D>;
+  using M = FLds<D>;
   constexpr int KS = D / 32, DT = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
   const int nchunks = L / kChunk;
-  const int64_t seg = blockIdx.x / (unsigned)nchunks;
-  const int c = (int)(blockIdx.x - seg * nchunks);
-  const int64_t bh = seg / R;
-  const int64_t row0 = bh * L;
-  const int32_t* pm = perm + seg * L;
-  const unsigned char* qkb = qk + row0 * D * 2;
-  const unsigned char* vb = v + row0 * D * 2;
-  int* pn = (int*)(lds + M::kPos);  // positions (slot 0: chunk c - 1, slot 1: chunk c)
-  float* kscale = (float*)(lds + M::kScale);
-  const int t = threadIdx.x;
-  if (t < kChunk) pn[kChunk + t] = pm[c * kChunk + t];
-  else if (t < 2 * kChunk) pn[t - kChunk] = c > 0 ? pm[(c - 1) * kChunk + t - kChunk] : 0;
-  __syncthreads();
-  {
-    uint4 kr[2][4], vr[2][4];
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      load_group<D>(kr[sl], qkb, pn + sl * kChunk);
-      load_group<D>(vr[sl], vb, pn + sl * kChunk);
-    }
-    float n2 = 0.f;
-    if (t < 2 * kChunk) n2 = knorm[row0 + pn[t]];
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      if (sl == 0 && c == 0) continue;
-      store_rm<D>(lds + M::kKt + sl * Lay::kRM, kr[sl]);
-      store_pair<D>(lds + M::kKp + sl * Lay::kPM, kr[sl]);
-      store_rm<D>(lds + M::kVt + sl * Lay::kRM, vr[sl]);
-    }
-    if (t < 2 * kChunk) {
-      const float sc = kLog2e / sqrtf((float)D);
-      kscale[t] = (n2 > 0.f && (t >= kChunk || c > 0)) ? sc / sqrtf(n2) : 0.f;
-    }
-    if (c == 0) {  // no previous chunk: zero keys and values in slot 0
-      zero_lds(lds + M::kKt, Lay::kRM);
-      zero_lds(lds + M::kVt, Lay::kRM);
-      zero_lds(lds + M::kKp, Lay::kPM);
-    }
-  }
-  __syncthreads();
-
-  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  const int q = 16 * w + lq;
-  const int posq = pn[kChunk + q];
-  const int64_t sq = seg * L + posq;
-  const float lse2 = lse[sq] * kLog2e;
-  const float wq = wr[sq], cqv = cq[row0 + posq];
-  const int kb0 = c > 0 ? 0 : 4;  // chunk 0: the first four 16-key blocks are absent
-  bf16x8_t qf[KS], df[KS];
-  {
-    const unsigned char* qrow = lds + M::kKt + (kChunk + q) * Lay::kRow;
-    const unsigned char* drow = dout + (row0 + posq) * D * 2;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = *(const bf16x8_t*)(qrow + (32 * ks + 8 * g) * 2);
-      df[ks] = *(const bf16x8_t*)(drow + (32 * ks + 8 * g) * 2);
-    }
-  }
-  floatx4_t acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = floatx4_t{};
-  const float inv_log2e = 1.0f / kLog2e;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    bf16x8_t dsf;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int kb = 2 * e + half;
-      const int sl = kb < 4 ? 0 : 1;
-      const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + ((kb & 3) * 16 + lq) * Lay::kRow;
-      const unsigned char* vrow = lds + M::kVt + sl * Lay::kRM + ((kb & 3) * 16 + lq) * Lay::kRow;
-      floatx4_t s = {}, dp = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)(krow + (32 * ks + 8 * g) * 2),
-                                                     qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)(vrow + (32 * ks + 8 * g) * 2),
-                                                      df[ks], dp, 0, 0, 0);
-      }
-      const int key = (kb & 3) * 16 + 4 * g;
-      const float4 sc = *(const float4*)(kscale + sl * kChunk + key);
-      const int4 kp = *(const int4*)(pn + sl * kChunk + key);
-      const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-      const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
-      const bool absent = kb < kb0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const bool masked = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq);
-        const float p = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], scv[b], -lse2));
-        dsf[4 * half + b] = (__bf16)(wq * p * (dp[b] - cqv) * scv[b] * inv_log2e);
-      }
-    }
-    const int sl = e < 2 ? 0 : 1;
-    const unsigned char* kp = lds + M::kKp + sl * Lay::kPM + (g + 4 * (e & 1)) * Lay::kPair +
-                              (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          *(const bf16x8_t*)(kp + dt * 2 * Lay::kBlk8), dsf, acc[dt], 0, 0, 0);
-  }
-  // lane holds dims 16 dt + 4g + 0..3 of query q
-  float* orow = dq + sq * D + 4 * g;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *(float4*)(orow + 16 * dt) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-}
-
-// -------------------------------------------------------------------------
-template <int D>
-struct DkvLds {
-  using L = BLay<D>;
-  static constexpr int kKt = 0;                       // keys of chunk c
-  static constexpr int kVt = kKt + L::kRM;
-  static constexpr int kQt = kVt + L::kRM;            // queries of the staged chunk
-  static constexpr int kDt = kQt + L::kRM;            // their dout rows
-  static constexpr int kQp = kDt + L::kRM;
-  static constexpr int kDp = kQp + L::kPM;
-  static constexpr int kKScale = kDp + L::kPM;        // [64]
-  static constexpr int kKPos = kKScale + kChunk * 4;  // [64]
-  static constexpr int kQPos = kKPos + kChunk * 4;    // [64]
-  static constexpr int kQLse = kQPos + kChunk * 4;    // [64] lse * log2(e)
-  static constexpr int kQW = kQLse + kChunk * 4;      // [64] round weight
-  static constexpr int kQC = kQW + kChunk * 4;        // [64] dout . out
-  static constexpr int kBytes = kQC + kChunk * 4;
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(
-    const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
-    const unsigned char* __restrict__ dout, const int32_t* __restrict__ perm,
-    const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
-    const float* __restrict__ cq, float* __restrict__ dk, float* __restrict__ dv, int L, int R) {
-  using Lay = BLay<D>;
-  using M = DkvLds<D>;
-  constexpr int KS = D / 32, DT = D / 16;
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int nchunks = L / kChunk;
-  const int64_t seg = blockIdx.x / (unsigned)nchunks;
-  const int c = (int)(blockIdx.x - seg * nchunks);
+  // groups of group_segs segments (all rounds of a few heads), interleaved
+  const int group = blockIdx.x / (unsigned)(group_segs * ranges);
+  const int first = group * group_segs;
+  const int gn = min(group_segs, nseg - first);
+  const int inner = blockIdx.x - group * group_segs * ranges;
+  const int64_t seg = first + inner % gn;
+  const int range = inner / gn;
+  const int c0 = range * chunks_per_wg;
+  const int c1 = min(nchunks, c0 + chunks_per_wg);
+  if (c0 >= c1) return;
+  const int cend = c1 < nchunks ? c1 : c1 - 1;  // last step (c1: its queries for keys c1 - 1)
   const int64_t bh = seg / R;
   const int64_t row0 = bh * L;
   const int32_t* pm = perm + seg * L;
@@ -276,69 +173,91 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(
   const unsigned char* db = dout + row0 * D * 2;
   float* kscale = (float*)(lds + M::kKScale);
   int* kpos = (int*)(lds + M::kKPos);
-  int* qpos = (int*)(lds + M::kQPos);
   float* qlse = (float*)(lds + M::kQLse);
   float* qw = (float*)(lds + M::kQW);
   float* qc = (float*)(lds + M::kQC);
+  int* pn = (int*)(lds + M::kPn);
   const int t = threadIdx.x;
-  // the keys: chunk c
-  if (t < kChunk) kpos[t] = pm[c * kChunk + t];
-  __syncthreads();
-  {
-    uint4 kr[4], vr[4];
-    load_group<D>(kr, qkb, kpos);
-    load_group<D>(vr, vb, kpos);
-    float n2 = 0.f;
-    if (t < kChunk) n2 = knorm[row0 + kpos[t]];
-    store_rm<D>(lds + M::kKt, kr);
-    store_rm<D>(lds + M::kVt, vr);
-    if (t < kChunk) kscale[t] = n2 > 0.f ? kLog2e / sqrtf((float)D) / sqrtf(n2) : 0.f;
-  }
-  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  const int key = 16 * w + lq;  // this lane's key (B operand column) in the chunk
-  floatx4_t dka[DT], dva[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dka[dt] = floatx4_t{};
-    dva[dt] = floatx4_t{};
-  }
-  for (int h = 0; h < 2; ++h) {
-    const int cq_idx = c + h;
-    if (cq_idx >= nchunks) break;
-    __syncthreads();  // the previous query chunk is no longer read
-    if (t < kChunk) qpos[t] = pm[cq_idx * kChunk + t];
-    __syncthreads();
-    {
-      uint4 qr[4], dr[4];
-      load_group<D>(qr, qkb, qpos);
-      load_group<D>(dr, db, qpos);
-      float l = 0.f, wv = 0.f, cv = 0.f;
-      if (t < kChunk) {
-        const int64_t sq = seg * L + qpos[t];
-        l = lse[sq];
-        wv = wr[sq];
-        cv = cq[row0 + qpos[t]];
-      }
-      store_rm<D>(lds + M::kQt, qr);
-      store_pair<D>(lds + M::kQp, qr);
-      store_rm<D>(lds + M::kDt, dr);
-      store_pair<D>(lds + M::kDp, dr);
-      if (t < kChunk) {
-        qlse[t] = l * kLog2e;
-        qw[t] = wv;
-        qc[t] = cv;
+  const float sc = kLog2e / sqrtf((float)D);
+
+  auto fetch = [&](FRegs& r, bool queries) {
+    load_group<D>(r.k, qkb, pn);
+    load_group<D>(r.v, vb, pn);
+    if (queries) load_group<D>(r.d, db, pn);
+    if (t < kChunk) {
+      r.pos = pn[t];
+      r.n2 = knorm[row0 + r.pos];
+      if (queries) {
+        r.lse = lse[seg * L + r.pos];
+        r.w = wr[seg * L + r.pos];
+        r.c = cq[row0 + r.pos];
       }
     }
+  };
+  auto stage = [&](const FRegs& r, int sl, bool queries) {
+    store_rm<D>(lds + M::kKt + sl * Lay::kRM, r.k);
+    store_pair<D>(lds + M::kKp + sl * Lay::kPM, r.k);
+    store_rm<D>(lds + M::kVt + sl * Lay::kRM, r.v);
+    if (queries) {
+      store_rm<D>(lds + M::kDt, r.d);
+      store_pair<D>(lds + M::kDp, r.d);
+    }
+    if (t < kChunk) {
+      kscale[sl * kChunk + t] = r.n2 > 0.f ? sc / sqrtf(r.n2) : 0.f;
+      kpos[sl * kChunk + t] = r.pos;
+      if (queries) {
+        qlse[t] = r.lse * kLog2e;
+        qw[t] = r.w;
+        qc[t] = r.c;
+      }
+    }
+  };
+
+  FRegs r;
+  if (c0 > 0) {  // the keys of chunk c0 - 1, for the dq of chunk c0
+    if (t < kChunk) pn[t] = pm[(c0 - 1) * kChunk + t];
     __syncthreads();
-    const float ksc = kscale[key];
-    const int kp = kpos[key];
-    const unsigned char* krow = lds + M::kKt + key * Lay::kRow;
-    const unsigned char* vrow = lds + M::kVt + key * Lay::kRow;
+    fetch(r, false);
+    stage(r, (c0 - 1) & 1, false);
+    __syncthreads();
+  } else {  // chunk 0 has no previous chunk: zero keys and values in slot 1
+    zero_lds(lds + M::kKt + Lay::kRM, Lay::kRM);
+    zero_lds(lds + M::kVt + Lay::kRM, Lay::kRM);
+    zero_lds(lds + M::kKp + Lay::kPM, Lay::kPM);
+    if (t < kChunk) {
+      kscale[kChunk + t] = 0.f;
+      kpos[kChunk + t] = 0;
+    }
+  }
+  if (t < kChunk) pn[t] = pm[c0 * kChunk + t];
+  __syncthreads();
+  fetch(r, true);
+  stage(r, c0 & 1, true);
+  __syncthreads();
+  if (c0 + 1 <= cend && t < kChunk) pn[t] = pm[(c0 + 1) * kChunk + t];
+  __syncthreads();
+
+  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
+  const int blk = 16 * w + lq;  // this lane's query / key row in a chunk
+  const float inv_log2e = 1.0f / kLog2e;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  floatx4_t dqa[DT], dka[DT], dva[DT];
+
+  // key block w of slot sl against the 64 queries of slot cur: S = Q K^T and
+  // dP = dO V^T per 16-query block, then dV^T and dkhat^T (unscaled) summed
+  // into dka / dva over 32-query steps
+  auto keys_step = [&](int sl, int cur) {
+    const float ksc = kscale[sl * kChunk + blk];
+    const int kp = kpos[sl * kChunk + blk];
     bf16x8_t kf[KS], vf[KS];
+    {
+      const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + blk * Lay::kRow;
+      const unsigned char* vrow = lds + M::kVt + sl * Lay::kRM + blk * Lay::kRow;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = *(const bf16x8_t*)(krow + (32 * ks + 8 * g) * 2);
-      vf[ks] = *(const bf16x8_t*)(vrow + (32 * ks + 8 * g) * 2);
+      for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = *(const bf16x8_t*)(krow + (32 * ks + 8 * g) * 2);
+        vf[ks] = *(const bf16x8_t*)(vrow + (32 * ks + 8 * g) * 2);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -346,19 +265,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int qb = 2 * e + half;
-        const unsigned char* qrow = lds + M::kQt + (qb * 16 + lq) * Lay::kRow;
+        const unsigned char* qrow = lds + M::kKt + cur * Lay::kRM + (qb * 16 + lq) * Lay::kRow;
         const unsigned char* drow = lds + M::kDt + (qb * 16 + lq) * Lay::kRow;
         floatx4_t s = {}, dp = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8_t*)(qrow + (32 * ks + 8 * g) * 2),
-                                                       kf[ks], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *(const bf16x8_t*)(qrow + (32 * ks + 8 * g) * 2), kf[ks], s, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               *(const bf16x8_t*)(drow + (32 * ks + 8 * g) * 2), vf[ks], dp, 0, 0, 0);
         }
         // lane holds queries qb*16 + 4g + 0..3 and this lane's key
         const int q0 = qb * 16 + 4 * g;
-        const int4 qp = *(const int4*)(qpos + q0);
+        const int4 qp = *(const int4*)(kpos + cur * kChunk + q0);
         const float4 ql = *(const float4*)(qlse + q0);
         const float4 qwv = *(const float4*)(qw + q0);
         const float4 qcv = *(const float4*)(qc + q0);
@@ -377,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(
       }
       const int off = (g + 4 * e) * Lay::kPair + (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
       const unsigned char* dpair = lds + M::kDp + off;
-      const unsigned char* qpair = lds + M::kQp + off;
+      const unsigned char* qpair = lds + M::kKp + cur * Lay::kPM + off;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -386,52 +305,159 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkv_mfma(
             *(const bf16x8_t*)(qpair + dt * 2 * Lay::kBlk8), dsf, dka[dt], 0, 0, 0);
       }
     }
-  }
-  // lane holds dims 16 dt + 4g + 0..3 of this lane's key
-  const float scale = 1.0f / sqrtf((float)D);
-  const int64_t sk = seg * L + kpos[key];
-  float* krow_o = dk + sk * D + 4 * g;
-  float* vrow_o = dv + sk * D + 4 * g;
+  };
+
+  // dq of query block w of slot cur (chunk c) over keys of slots prv and cur
+  auto query_step = [&](int c, int cur, int prv) {
+    const int posq = kpos[cur * kChunk + blk];
+    const float lse2 = qlse[blk], wq = qw[blk], cqv = qc[blk];
+    const int kb0 = c > 0 ? 0 : 4;  // chunk 0: the first four 16-key blocks are absent
+    bf16x8_t qf[KS], df[KS];
+    {
+      const unsigned char* qrow = lds + M::kKt + cur * Lay::kRM + blk * Lay::kRow;
+      const unsigned char* drow = lds + M::kDt + blk * Lay::kRow;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    *(float4*)(krow_o + 16 * dt) = make_float4(dka[dt][0] * scale, dka[dt][1] * scale,
-                                               dka[dt][2] * scale, dka[dt][3] * scale);
-    *(float4*)(vrow_o + 16 * dt) = make_float4(dva[dt][0], dva[dt][1], dva[dt][2], dva[dt][3]);
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = *(const bf16x8_t*)(qrow + (32 * ks + 8 * g) * 2);
+        df[ks] = *(const bf16x8_t*)(drow + (32 * ks + 8 * g) * 2);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dqa[dt] = floatx4_t{};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bf16x8_t dsf;
+      const int sl = e < 2 ? prv : cur;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kb = 2 * e + half;
+        const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + ((kb & 3) * 16 + lq) * Lay::kRow;
+        const unsigned char* vrow = lds + M::kVt + sl * Lay::kRM + ((kb & 3) * 16 + lq) * Lay::kRow;
+        floatx4_t s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *(const bf16x8_t*)(krow + (32 * ks + 8 * g) * 2), qf[ks], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *(const bf16x8_t*)(vrow + (32 * ks + 8 * g) * 2), df[ks], dp, 0, 0, 0);
+        }
+        const int key = (kb & 3) * 16 + 4 * g;
+        const float4 scv4 = *(const float4*)(kscale + sl * kChunk + key);
+        const int4 kp4 = *(const int4*)(kpos + sl * kChunk + key);
+        const float scv[4] = {scv4.x, scv4.y, scv4.z, scv4.w};
+        const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
+        const bool absent = kb < kb0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bool masked = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq);
+          const float p = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], scv[b], -lse2));
+          dsf[4 * half + b] = (__bf16)(wq * p * (dp[b] - cqv) * scv[b] * inv_log2e);
+        }
+      }
+      const unsigned char* kp = lds + M::kKp + sl * Lay::kPM + (g + 4 * (e & 1)) * Lay::kPair +
+                                (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dqa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8_t*)(kp + dt * 2 * Lay::kBlk8), dsf, dqa[dt], 0, 0, 0);
+    }
+  };
+
+  // rows 16w .. 16w + 15 of the chunk in slot sl are final: lane holds dims
+  // 16 dt + 4g + 0..3 of row blk in dqa, dka, dva
+  auto finish = [&](int sl) {
+    const int pos = kpos[sl * kChunk + blk];
+    const float rn = kscale[sl * kChunk + blk] * (sqrtf((float)D) * inv_log2e);  // 1 / |k|, 0 for k = 0
+    const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + blk * Lay::kRow + 8 * g;
+    float kv[DT][4];
+    float proj = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint2 x = *(const uint2*)(krow + 32 * dt);
+      kv[dt][0] = __uint_as_float(x.x << 16);
+      kv[dt][1] = __uint_as_float(x.x & 0xFFFF0000u);
+      kv[dt][2] = __uint_as_float(x.y << 16);
+      kv[dt][3] = __uint_as_float(x.y & 0xFFFF0000u);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) proj = fmaf(kv[dt][b], dka[dt][b], proj);
+    }
+    proj += __shfl_xor(proj, 16);
+    proj += __shfl_xor(proj, 32);
+    proj *= rn * inv_sqrt_d;  // khat . dkhat
+    float* qo = dqk_r + (seg * L + pos) * D + 4 * g;
+    float* vo = dv_r + (seg * L + pos) * D + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      float o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        o[b] = dqa[dt][b] + (dka[dt][b] * inv_sqrt_d - kv[dt][b] * rn * proj) * rn;
+      *(float4*)(qo + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
+      *(float4*)(vo + 16 * dt) = make_float4(dva[dt][0], dva[dt][1], dva[dt][2], dva[dt][3]);
+    }
+  };
+
+  int pnext = 0;
+  for (int c = c0; c <= cend; ++c) {
+    const bool more = c + 1 <= cend;
+    if (more) {
+      fetch(r, true);
+      if (c + 2 <= cend && t < kChunk) pnext = pm[(c + 2) * kChunk + t];
+    }
+    const int cur = c & 1, prv = cur ^ 1;
+    if (c > c0) {  // the last queries of the keys of chunk c - 1
+      keys_step(prv, cur);
+      finish(prv);
+    }
+    if (c < c1) {
+      query_step(c, cur, prv);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dka[dt] = floatx4_t{};
+        dva[dt] = floatx4_t{};
+      }
+      keys_step(cur, cur);
+    }
+    __syncthreads();  // slot prv and the query chunk are no longer read
+    if (more) {
+      stage(r, prv, true);
+      if (c + 2 <= cend && t < kChunk) pn[t] = pnext;
+    }
+    __syncthreads();
   }
+  if (c1 == nchunks) finish((c1 - 1) & 1);  // the last chunk's keys see no later queries
 }
 
 template <int D, bool CAUSAL>
-void launch_d(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-              const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s,
-              hipEvent_t after_dq) {
-  const dim3 grid((unsigned)(p.nseg() * (p.L / kChunk)));
-  hipLaunchKernelGGL((k_bwd_dq_mfma<D, CAUSAL>), grid, dim3(kThreads), DqLds<D>::kBytes, s,
-                     (const unsigned char*)qk, (const unsigned char*)v,
-                     (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, b.dq, p.L, p.R);
-  if (after_dq) (void)hipEventRecord(after_dq, s);
-  hipLaunchKernelGGL((k_bwd_dkv_mfma<D, CAUSAL>), grid, dim3(kThreads), DkvLds<D>::kBytes, s,
-                     (const unsigned char*)qk, (const unsigned char*)v,
-                     (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, b.dk, b.dv, p.L,
-                     p.R);
+void launch_fused(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+                  const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
+  const int nchunks = p.L / kChunk;
+  const int64_t nseg = p.nseg();
+  const int per = nchunks < kFusedRange ? nchunks : kFusedRange;
+  const int ranges = (nchunks + per - 1) / per;
+  int64_t heads = (kFusedResident + (int64_t)ranges * p.R - 1) / ((int64_t)ranges * p.R);
+  if (heads < 1) heads = 1;
+  int64_t group_segs = heads * p.R;
+  if (group_segs > nseg) group_segs = nseg;
+  hipLaunchKernelGGL((k_bwd_fused_mfma<D, CAUSAL>), dim3((unsigned)(nseg * ranges)),
+                     dim3(kThreads), FLds<D>::kBytes, s, (const unsigned char*)qk,
+                     (const unsigned char*)v, (const unsigned char*)dout, perm, knorm, b.lse,
+                     b.w, b.cq, b.dq, b.dv, p.L, p.R, (int)nseg, per, ranges, (int)group_segs);
 }
 
 template <int D>
 void configure() {
-  (void)hipFuncSetAttribute((const void*)k_bwd_dq_mfma<D, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DqLds<D>::kBytes);
-  (void)hipFuncSetAttribute((const void*)k_bwd_dq_mfma<D, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DqLds<D>::kBytes);
-  (void)hipFuncSetAttribute((const void*)k_bwd_dkv_mfma<D, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DkvLds<D>::kBytes);
-  (void)hipFuncSetAttribute((const void*)k_bwd_dkv_mfma<D, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, DkvLds<D>::kBytes);
+  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, FLds<D>::kBytes);
+  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, FLds<D>::kBytes);
 }
 
 }  // namespace
 
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
-                                BwdWorkspace& b, hipStream_t s, hipEvent_t after_dq) {
+                                BwdWorkspace& b, hipStream_t s) {
   static bool configured = false;
   if (!configured) {
     configure<64>();
@@ -439,11 +465,11 @@ hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
     configured = true;
   }
   if (p.d == 64) {
-    if (p.causal) launch_d<64, true>(p, qk, v, perm, dout, knorm, b, s, after_dq);
-    else launch_d<64, false>(p, qk, v, perm, dout, knorm, b, s, after_dq);
+    if (p.causal) launch_fused<64, true>(p, qk, v, perm, dout, knorm, b, s);
+    else launch_fused<64, false>(p, qk, v, perm, dout, knorm, b, s);
   } else {
-    if (p.causal) launch_d<128, true>(p, qk, v, perm, dout, knorm, b, s, after_dq);
-    else launch_d<128, false>(p, qk, v, perm, dout, knorm, b, s, after_dq);
+    if (p.causal) launch_fused<128, true>(p, qk, v, perm, dout, knorm, b, s);
+    else launch_fused<128, false>(p, qk, v, perm, dout, knorm, b, s);
   }
   return hipGetLastError();
 }

@@ -69,8 +69,9 @@ struct BwdWorkspace {
   float* lse = nullptr;  // [seg, L] recomputed per-round logsumexps
   float* w = nullptr;    // [seg, L] round weights of the combination
   float* cq = nullptr;   // [B*H, L] dout . out
-  float* dq = nullptr;   // [seg, L, d] per-round dq at original positions
-  float* dk = nullptr;   // [seg, L, d] per-round d(unit key)
+  float* dq = nullptr;   // [seg, L, d] per-round dq at original positions (matrix-core
+                         // path: dq plus the normalised key gradient, dqk per round)
+  float* dk = nullptr;   // [seg, L, d] per-round d(unit key) (plain path)
   float* dv = nullptr;   // [seg, L, d] per-round dv
 };
 
@@ -115,16 +116,17 @@ hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const fl
                           const void* v, void* out, hipStream_t s);
 
 // gradients of qk and v given dout, at the permutations perm of a forward
-// ev (may be null): 6 events, recorded before the recomputation and after
-// each of its 5 stages (recomputation, rows, dq, dkhat/dv, reduction)
+// ev (may be null): 5 events, recorded before the recomputation and after
+// each of its 4 stages (recomputation, rows, gradient products, reduction)
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                            const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
                            hipStream_t s, const hipEvent_t* ev);
 
-// the dq and (dkhat, dv) products on matrix cores (attend_mfma_supported shapes)
+// the per-round gradient products on matrix cores (attend_mfma_supported
+// shapes): b.dq receives dqk per round (dq and the normalised dkhat), b.dv dv
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
-                                BwdWorkspace& b, hipStream_t s, hipEvent_t after_dq);
+                                BwdWorkspace& b, hipStream_t s);
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.

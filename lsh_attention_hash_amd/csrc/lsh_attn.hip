@@ -155,7 +155,8 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
                                         : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
          alloc(&b.lse, rows * 4, t) &&
          alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
-         alloc(&b.dq, rows * p.d * 4, t) && alloc(&b.dk, rows * p.d * 4, t) &&
+         alloc(&b.dq, rows * p.d * 4, t) &&
+         (lsh::attend_mfma_supported(p) || alloc(&b.dk, rows * p.d * 4, t)) &&
          alloc(&b.dv, rows * p.d * 4, t);
   }
   if (!ok) {

@@ -69,6 +69,9 @@ BWD = [
     W("text64k", batch=1, heads=1, seq_len=1024, n_buckets=16, n_rounds=1, causal=False),
     W("skewed", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=2),
     W("c4k", batch=1, heads=1, seq_len=64, n_buckets=4, n_rounds=2, causal=True),  # one chunk
+    # 20 chunks: a full range of 16 and a short last one
+    W("text64k", batch=1, heads=2, seq_len=1280, n_buckets=16, n_rounds=3, causal=False),
+    W("image12k", batch=2, heads=1, seq_len=3072, n_buckets=32, n_rounds=2),
 ]
 
 
@@ -130,3 +133,35 @@ def test_backward_deterministic():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     finally:
         op.close()
+
+
+def test_backward_full_size_sampled_heads():
+    """Text-64K at full size, in the bench's configuration; the oracle's
+    backward is computed for two of the (batch, head) pairs (each pair's
+    gradients depend only on its own rows) at the GPU forward's permutation."""
+    w = workloads.get("text64k")
+    _say(f"[backward full size] {w}")
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    qk, v, rot = to_device(inp, dev)
+    op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
+                          w.chunk_len, w.causal, backward=True)
+    try:
+        _, ex = op(qk, v, rot, return_perm=True)
+        dout_t, dout = _dout(w, 4242)
+        dqk, dv = op.backward(qk, v, ex["perm"], dout_t.to(dev))
+        torch.cuda.synchronize()
+        perm = ex["perm"].cpu().numpy().reshape(w.batch, w.heads, w.n_rounds, w.seq_len)
+        dqk = dqk.to(torch.float64).cpu().numpy()
+        dv = dv.to(torch.float64).cpu().numpy()
+    finally:
+        op.close()
+    heads = [0, w.heads - 1]
+    sub = w.with_(batch=1, heads=len(heads))
+    c = oracle.config(sub)
+    rq, rv = oracle.backward(c, np.ascontiguousarray(inp.qk[:1, heads]),
+                             np.ascontiguousarray(inp.v[:1, heads]),
+                             np.ascontiguousarray(perm[:1, heads]),
+                             np.ascontiguousarray(dout[:1, heads]))
+    _check("dqk", dqk[:1, heads], rq, True)
+    _check("dv", dv[:1, heads], rv, True)
