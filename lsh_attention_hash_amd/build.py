@@ -35,6 +35,7 @@ CFLAGS = [
 # place instead of copying each one out of the accumulation registers.
 EXTRA_FLAGS = {
     "hash_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "backward_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -123,10 +123,11 @@ struct FLds {
   static constexpr int kDt = kKp + 2 * L::kPM;            // dout rows of the query chunk
   static constexpr int kDp = kDt + L::kRM;                // the same by group pairs
   static constexpr int kKScale = kDp + L::kPM;            // [2][64] log2(e) / (sqrt(d) |k|)
-  static constexpr int kKPos = kKScale + 2 * kChunk * 4;  // [2][64] original positions
-  static constexpr int kQLse = kKPos + 2 * kChunk * 4;    // [64] lse * log2(e) of the queries
-  static constexpr int kQW = kQLse + kChunk * 4;          // [64] round weight
-  static constexpr int kQC = kQW + kChunk * 4;            // [64] dout . out
+  static constexpr int kKScaleDs = kKScale + 2 * kChunk * 4;  // [2][64] 1 / (sqrt(d) |k|)
+  static constexpr int kKPos = kKScaleDs + 2 * kChunk * 4;  // [2][64] original positions
+  // [64] per query: lse log2(e) - log2(w), so that exp2(s - it) is w P
+  static constexpr int kQLse = kKPos + 2 * kChunk * 4;
+  static constexpr int kQC = kQLse + kChunk * 4;          // [64] dout . out
   static constexpr int kPn = kQC + kChunk * 4;            // [64] positions of the next chunk
   static constexpr int kBytes = kPn + kChunk * 4;
 };
@@ -172,13 +173,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   const unsigned char* vb = v + row0 * D * 2;
   const unsigned char* db = dout + row0 * D * 2;
   float* kscale = (float*)(lds + M::kKScale);
+  float* kscale_ds = (float*)(lds + M::kKScaleDs);
   int* kpos = (int*)(lds + M::kKPos);
   float* qlse = (float*)(lds + M::kQLse);
-  float* qw = (float*)(lds + M::kQW);
   float* qc = (float*)(lds + M::kQC);
   int* pn = (int*)(lds + M::kPn);
   const int t = threadIdx.x;
   const float sc = kLog2e / sqrtf((float)D);
+  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
   auto fetch = [&](FRegs& r, bool queries) {
     load_group<D>(r.k, qkb, pn);
@@ -203,11 +205,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       store_pair<D>(lds + M::kDp, r.d);
     }
     if (t < kChunk) {
-      kscale[sl * kChunk + t] = r.n2 > 0.f ? sc / sqrtf(r.n2) : 0.f;
+      const float rn = r.n2 > 0.f ? 1.0f / sqrtf(r.n2) : 0.f;
+      kscale[sl * kChunk + t] = sc * rn;
+      kscale_ds[sl * kChunk + t] = rn * inv_sqrt_d;
       kpos[sl * kChunk + t] = r.pos;
       if (queries) {
-        qlse[t] = r.lse * kLog2e;
-        qw[t] = r.w;
+        // a zero weight gives +inf here and P = 0 below
+        qlse[t] = r.lse * kLog2e - __log2f(r.w);
         qc[t] = r.c;
       }
     }
@@ -226,6 +230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     zero_lds(lds + M::kKp + Lay::kPM, Lay::kPM);
     if (t < kChunk) {
       kscale[kChunk + t] = 0.f;
+      kscale_ds[kChunk + t] = 0.f;
       kpos[kChunk + t] = 0;
     }
   }
@@ -239,8 +244,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
   const int blk = 16 * w + lq;  // this lane's query / key row in a chunk
-  const float inv_log2e = 1.0f / kLog2e;
-  const float inv_sqrt_d = 1.0f / sqrtf((float)D);
   floatx4_t dqa[DT], dka[DT], dva[DT];
 
   // key block w of slot sl against the 64 queries of slot cur: S = Q K^T and
@@ -279,17 +282,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
         const int q0 = qb * 16 + 4 * g;
         const int4 qp = *(const int4*)(kpos + cur * kChunk + q0);
         const float4 ql = *(const float4*)(qlse + q0);
-        const float4 qwv = *(const float4*)(qw + q0);
         const float4 qcv = *(const float4*)(qc + q0);
         const int qpv[4] = {qp.x, qp.y, qp.z, qp.w};
         const float qlv[4] = {ql.x, ql.y, ql.z, ql.w};
-        const float qww[4] = {qwv.x, qwv.y, qwv.z, qwv.w};
         const float qcc[4] = {qcv.x, qcv.y, qcv.z, qcv.w};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const bool masked = CAUSAL ? kp >= qpv[b] : kp == qpv[b];
-          const float p = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], ksc, -qlv[b]));
-          const float wp = qww[b] * p;
+          const float wp = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], ksc, -qlv[b]));
           wpf[4 * half + b] = (__bf16)wp;
           dsf[4 * half + b] = (__bf16)(wp * (dp[b] - qcc[b]));
         }
@@ -308,9 +308,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   };
 
   // dq of query block w of slot cur (chunk c) over keys of slots prv and cur
-  auto query_step = [&](int c, int cur, int prv) {
+  auto query_step = [&](int c, int cur, int prv, floatx4_t* dq) {
     const int posq = kpos[cur * kChunk + blk];
-    const float lse2 = qlse[blk], wq = qw[blk], cqv = qc[blk];
+    const float lse2 = qlse[blk], cqv = qc[blk];
     const int kb0 = c > 0 ? 0 : 4;  // chunk 0: the first four 16-key blocks are absent
     bf16x8_t qf[KS], df[KS];
     {
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       }
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dqa[dt] = floatx4_t{};
+    for (int dt = 0; dt < DT; ++dt) dq[dt] = floatx4_t{};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       bf16x8_t dsf;
@@ -343,23 +343,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
         }
         const int key = (kb & 3) * 16 + 4 * g;
         const float4 scv4 = *(const float4*)(kscale + sl * kChunk + key);
+        const float4 sdv4 = *(const float4*)(kscale_ds + sl * kChunk + key);
         const int4 kp4 = *(const int4*)(kpos + sl * kChunk + key);
         const float scv[4] = {scv4.x, scv4.y, scv4.z, scv4.w};
+        const float sdv[4] = {sdv4.x, sdv4.y, sdv4.z, sdv4.w};
         const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
         const bool absent = kb < kb0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const bool masked = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq);
-          const float p = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], scv[b], -lse2));
-          dsf[4 * half + b] = (__bf16)(wq * p * (dp[b] - cqv) * scv[b] * inv_log2e);
+          const float wp = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], scv[b], -lse2));
+          dsf[4 * half + b] = (__bf16)(wp * (dp[b] - cqv) * sdv[b]);
         }
       }
       const unsigned char* kp = lds + M::kKp + sl * Lay::kPM + (g + 4 * (e & 1)) * Lay::kPair +
                                 (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        dqa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *(const bf16x8_t*)(kp + dt * 2 * Lay::kBlk8), dsf, dqa[dt], 0, 0, 0);
+        dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8_t*)(kp + dt * 2 * Lay::kBlk8), dsf, dq[dt], 0, 0, 0);
     }
   };
 
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   // 16 dt + 4g + 0..3 of row blk in dqa, dka, dva
   auto finish = [&](int sl) {
     const int pos = kpos[sl * kChunk + blk];
-    const float rn = kscale[sl * kChunk + blk] * (sqrtf((float)D) * inv_log2e);  // 1 / |k|, 0 for k = 0
+    const float rn = kscale_ds[sl * kChunk + blk] * sqrtf((float)D);  // 1 / |k|, 0 for k = 0
     const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + blk * Lay::kRow + 8 * g;
     float kv[DT][4];
     float proj = 0.f;
@@ -410,7 +412,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       finish(prv);
     }
     if (c < c1) {
-      query_step(c, cur, prv);
+      query_step(c, cur, prv, dqa);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         dka[dt] = floatx4_t{};
