@@ -64,8 +64,9 @@ enum {
    * which halves that traffic; fp16 saturates at +-65504, so inputs whose v
    * exceeds that magnitude need this flag. */
   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
-  /* Also allocate the workspace of lsh_attn_backward (fp32 per-round rows and
-   * gradients: about 4 * n_rounds * |qk| * 4 / esize bytes more). */
+  /* Also allocate the workspace of lsh_attn_backward: per position and round,
+   * 2 fp32 rows of head_dim on the matrix-core path (bf16, chunk_len 64, head_dim
+   * 64 or 128) or 4 on the other shapes, plus 12 bytes; 4 bytes per position. */
   LSH_ATTN_FLAG_BACKWARD = 4
 };
 
