@@ -208,8 +208,9 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 // LDS allows two workgroups (8 waves) per CU at d = 128, so each wave may take
 // half the register file; say so, or the compiler aims for more waves.
 // DOT (the backward's recomputation): instead of the round's rows, o receives
-// per query the scalar dout(i) . o_r(i) ([seg, L] fp32; 0 for a query that saw
-// only itself), dout being bf16 rows [B*H, L, D].
+// per query the scalar dout(i) . o_r(i) ([seg, L] fp32; dout(i) . v_i for a
+// query that saw only itself, whose output is v_i), dout being bf16 rows
+// [B*H, L, D].
 template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attend_mfma(
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
@@ -425,9 +426,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
           d = fmaf(oacc[dt][2], __uint_as_float(dz[dt].y << 16), d);
           d = fmaf(oacc[dt][3], __uint_as_float(dz[dt].y & 0xFFFF0000u), d);
         }
+        d *= inv;
+        if (!seen) {  // the round's output is v_i itself
+          const unsigned char* vrow = (const unsigned char*)v + ((row0 + posq) * D + 4 * g) * 2;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint2 x = *(const uint2*)(vrow + 32 * dt);
+            d = fmaf(__uint_as_float(x.x << 16), __uint_as_float(dz[dt].x << 16), d);
+            d = fmaf(__uint_as_float(x.x & 0xFFFF0000u), __uint_as_float(dz[dt].x & 0xFFFF0000u), d);
+            d = fmaf(__uint_as_float(x.y << 16), __uint_as_float(dz[dt].y << 16), d);
+            d = fmaf(__uint_as_float(x.y & 0xFFFF0000u), __uint_as_float(dz[dt].y & 0xFFFF0000u), d);
+          }
+        }
         d += __shfl_xor(d, 16);
         d += __shfl_xor(d, 32);
-        if (g == 0) o[seg * L + posq] = d * inv;
+        if (g == 0) o[seg * L + posq] = d;
       } else if constexpr (sizeof(OT) == 2) {
         // fp16: tiles t and t + 1 packed as 2 words per lane, then one swap of
         // odd and even 16-lane rows leaves lane group g with 8 consecutive

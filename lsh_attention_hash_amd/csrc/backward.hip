@@ -29,6 +29,8 @@
 // key (each key is seen by the queries of its chunk and of the next one); then
 // the sum over rounds with the normalisation, in the caller's dtype. Every
 // output element is written by one thread: no atomics, deterministic.
+#include <type_traits>
+
 #include "dtype.h"
 #include "internal.h"
 
@@ -125,26 +127,18 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const float* __restrict__ o,
 }
 
 // As k_bwd_rows, from the per-round scalars od_r(i) = dout(i) . o_r(i) of the
-// matrix-core recomputation: dout . out = sum_r w_r od_r, with dout(i) . v_i for
-// a round in which the position saw only itself.
-template <int D, typename T>
+// matrix-core recomputation (dout(i) . v_i for a round in which the position
+// saw only itself): dout . out = sum_r w_r od_r. Also the summed weight of the
+// self-only rounds per position, wself [B*H, L]. One thread per position.
 __global__ __launch_bounds__(256) void k_bwd_rows_dot(const float* __restrict__ od,
                                                       const float* __restrict__ lse,
-                                                      const T* __restrict__ v,
-                                                      const T* __restrict__ dout,
                                                       float* __restrict__ w,
-                                                      float* __restrict__ cq, int L, int R,
+                                                      float* __restrict__ cq,
+                                                      float* __restrict__ wself, int L, int R,
                                                       int64_t n_rows) {
-  constexpr int kLpr = D / 8;
-  const int sub = threadIdx.x % kLpr;
-  const int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (row >= n_rows) return;
   const int64_t bh = row / L, i = row - bh * L;
-  float vi[8], dz[8];
-  load8<T>(v + row * D + sub * 8, vi);
-  load8<T>(dout + row * D + sub * 8, dz);
-  const float vd = row_sum<kLpr>(dot8(dz, vi));
-  if (sub != 0) return;
   const float* lr = lse + bh * R * L + i;
   const float* dr = od + bh * R * L + i;
   float mx = -INFINITY;
@@ -152,14 +146,16 @@ __global__ __launch_bounds__(256) void k_bwd_rows_dot(const float* __restrict__ 
   float sum = 0.f;
   for (int r = 0; r < R; ++r) sum += __expf(lr[(int64_t)r * L] - mx);
   const float inv = 1.0f / sum;
-  float c = 0.f;
+  float c = 0.f, ws = 0.f;
   for (int r = 0; r < R; ++r) {
     const float l = lr[(int64_t)r * L];
     const float wr = __expf(l - mx) * inv;
     w[(bh * R + r) * L + i] = wr;
-    c = fmaf(wr, l == kSelfLogit ? vd : dr[(int64_t)r * L], c);
+    c = fmaf(wr, dr[(int64_t)r * L], c);
+    ws += l == kSelfLogit ? wr : 0.f;
   }
   cq[row] = c;
+  wself[row] = ws;
 }
 
 // dq of the query at slot s of segment seg (one D/8-lane row group per
@@ -316,43 +312,56 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
 
 // The same on the matrix-core path, whose per-round rows already hold
 // dq + the normalised key gradient (dqk_r) and dv_r: sums over rounds plus the
-// self-only value terms. Each per-round row is read once (non-temporal).
-template <int D, typename T>
+// self-only value term wself dout. kR > 0: R == kR and every load is issued
+// before the sums; kR == 0: any R. Each per-round row is read once
+// (non-temporal); blocks take the rows from the end, which the product kernel
+// wrote last.
+template <int D, typename T, int kR>
 __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ dout,
-                                                        const float* __restrict__ lse,
-                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ wself,
                                                         const float* __restrict__ dqkr,
                                                         const float* __restrict__ dvr,
                                                         T* __restrict__ dqk, T* __restrict__ dv,
-                                                        int L, int R, int64_t n_rows) {
+                                                        int L, int R_rt, int64_t n_rows) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   constexpr int kLpr = D / 8;
+  constexpr int kG = kR > 0 ? kR : 1;
+  const int R = kR > 0 ? kR : R_rt;
   const int sub = threadIdx.x % kLpr;
-  const int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
+  const int64_t row = (int64_t)(gridDim.x - 1 - blockIdx.x) * (256 / kLpr) + threadIdx.x / kLpr;
   if (row >= n_rows) return;
   const int64_t bh = row / L, j = row - bh * L;
   float gq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wself = 0.f;
-  for (int r = 0; r < R; ++r) {
-    const int64_t sr = (bh * R + r) * L + j;
-    const f32x4_t* a = (const f32x4_t*)(dqkr + sr * D + sub * 8);
-    const f32x4_t* c = (const f32x4_t*)(dvr + sr * D + sub * 8);
-    const f32x4_t a0 = __builtin_nontemporal_load(a), a1 = __builtin_nontemporal_load(a + 1);
-    const f32x4_t c0 = __builtin_nontemporal_load(c), c1 = __builtin_nontemporal_load(c + 1);
+  const float ws = wself[row];
+  for (int r0 = 0; r0 < R; r0 += kG) {
+    f32x4_t a[kG][2], c[kG][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      gq[u] += a0[u];
-      gq[4 + u] += a1[u];
-      gv[u] += c0[u];
-      gv[4 + u] += c1[u];
+    for (int u = 0; u < kG; ++u) {
+      const int64_t sr = (bh * R + r0 + u) * L + j;
+      const f32x4_t* pa = (const f32x4_t*)(dqkr + sr * D + sub * 8);
+      const f32x4_t* pc = (const f32x4_t*)(dvr + sr * D + sub * 8);
+      a[u][0] = __builtin_nontemporal_load(pa);
+      a[u][1] = __builtin_nontemporal_load(pa + 1);
+      c[u][0] = __builtin_nontemporal_load(pc);
+      c[u][1] = __builtin_nontemporal_load(pc + 1);
     }
-    if (lse[sr] == kSelfLogit) wself += w[sr];
-  }
-  float dz[8];
-  load8<T>(dout + row * D + sub * 8, dz);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) gv[u] = fmaf(wself, dz[u], gv[u]);
+    for (int u = 0; u < kG; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        gq[k] += a[u][0][k];
+        gq[4 + k] += a[u][1][k];
+        gv[k] += c[u][0][k];
+        gv[4 + k] += c[u][1][k];
+      }
+  }
+  if (ws > 0.f) {
+    float dz[8];
+    load8<T>(dout + row * D + sub * 8, dz);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) gv[u] = fmaf(ws, dz[u], gv[u]);
+  }
   store8(dqk + row * D + sub * 8, gq);
   store8(dv + row * D + sub * 8, gv);
 }
@@ -368,8 +377,8 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
   const int64_t nt = p.n_token_heads(), nr = p.n_rows();
   const dim3 gt((unsigned)((nt + rpb - 1) / rpb)), gr((unsigned)((nr + rpb - 1) / rpb));
   if (attend_mfma_supported(p))
-    hipLaunchKernelGGL((k_bwd_rows_dot<D, T>), gt, dim3(256), 0, s, b.od, b.lse, (const T*)v,
-                       (const T*)dout, b.w, b.cq, p.L, p.R, nt);
+    hipLaunchKernelGGL(k_bwd_rows_dot, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, b.od,
+                       b.lse, b.w, b.cq, b.wself, p.L, p.R, nt);
   else
     hipLaunchKernelGGL((k_bwd_rows<D, T>), gt, dim3(256), 0, s, b.o32, b.lse, (const T*)v,
                        (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
@@ -377,8 +386,19 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
   if (attend_mfma_supported(p)) {
     (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
     mark(3);
-    hipLaunchKernelGGL((k_bwd_reduce_sum<D, T>), gt, dim3(256), 0, s, (const T*)dout, b.lse, b.w,
-                       b.dq, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
+    auto go = [&](auto r) {
+      constexpr int kR = decltype(r)::value;
+      hipLaunchKernelGGL((k_bwd_reduce_sum<D, T, kR>), gt, dim3(256), 0, s, (const T*)dout,
+                         b.wself, b.dq, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
+    };
+    switch (p.R) {
+      case 1: go(std::integral_constant<int, 1>{}); break;
+      case 2: go(std::integral_constant<int, 2>{}); break;
+      case 3: go(std::integral_constant<int, 3>{}); break;
+      case 4: go(std::integral_constant<int, 4>{}); break;
+      case 8: go(std::integral_constant<int, 8>{}); break;
+      default: go(std::integral_constant<int, 0>{}); break;
+    }
     mark(4);
     return;
   }

@@ -69,6 +69,7 @@ struct BwdWorkspace {
   float* lse = nullptr;  // [seg, L] recomputed per-round logsumexps
   float* w = nullptr;    // [seg, L] round weights of the combination
   float* cq = nullptr;   // [B*H, L] dout . out
+  float* wself = nullptr;  // [B*H, L] summed weight of the self-only rounds (matrix-core path)
   float* dq = nullptr;   // [seg, L, d] per-round dq at original positions (matrix-core
                          // path: dq plus the normalised key gradient, dqk per round)
   float* dk = nullptr;   // [seg, L, d] per-round d(unit key) (plain path)

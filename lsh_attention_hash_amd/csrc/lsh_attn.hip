@@ -82,6 +82,7 @@ void free_bw(lsh::BwdWorkspace& b) {
   hipFree(b.lse);
   hipFree(b.w);
   hipFree(b.cq);
+  hipFree(b.wself);
   hipFree(b.dq);
   hipFree(b.dk);
   hipFree(b.dv);
@@ -155,6 +156,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
                                         : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
          alloc(&b.lse, rows * 4, t) &&
          alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
+         alloc(&b.wself, p.n_token_heads() * 4, t) &&
          alloc(&b.dq, rows * p.d * 4, t) &&
          (lsh::attend_mfma_supported(p) || alloc(&b.dk, rows * p.d * 4, t)) &&
          alloc(&b.dv, rows * p.d * 4, t);

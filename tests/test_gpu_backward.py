@@ -72,6 +72,8 @@ BWD = [
     # 20 chunks: a full range of 16 and a short last one
     W("text64k", batch=1, heads=2, seq_len=1280, n_buckets=16, n_rounds=3, causal=False),
     W("image12k", batch=2, heads=1, seq_len=3072, n_buckets=32, n_rounds=2),
+    # a round count without a specialised reduction
+    W("image12k", batch=1, heads=1, seq_len=1024, n_buckets=16, n_rounds=5),
 ]
 
 
