@@ -307,6 +307,84 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     }
   };
 
+  // keys_step for key block w of both slots at once (chunk c - 1 into dka /
+  // dva, chunk c into dkc / dvc): the query-row operands and the pair
+  // operands of the products are read once for both
+  auto keys_step2 = [&](int cur, floatx4_t* dkc, floatx4_t* dvc) {
+    const int prv = cur ^ 1;
+    const int sls[2] = {prv, cur};
+    float ksc[2];
+    int kp[2];
+    bf16x8_t kf[2][KS], vf[2][KS];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ksc[j] = kscale[sls[j] * kChunk + blk];
+      kp[j] = kpos[sls[j] * kChunk + blk];
+      const unsigned char* krow = lds + M::kKt + sls[j] * Lay::kRM + blk * Lay::kRow;
+      const unsigned char* vrow = lds + M::kVt + sls[j] * Lay::kRM + blk * Lay::kRow;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kf[j][ks] = *(const bf16x8_t*)(krow + (32 * ks + 8 * g) * 2);
+        vf[j][ks] = *(const bf16x8_t*)(vrow + (32 * ks + 8 * g) * 2);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      bf16x8_t wpf[2], dsf[2];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int qb = 2 * e + half;
+        const unsigned char* qrow = lds + M::kKt + cur * Lay::kRM + (qb * 16 + lq) * Lay::kRow;
+        const unsigned char* drow = lds + M::kDt + (qb * 16 + lq) * Lay::kRow;
+        bf16x8_t aq[KS], ad[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          aq[ks] = *(const bf16x8_t*)(qrow + (32 * ks + 8 * g) * 2);
+          ad[ks] = *(const bf16x8_t*)(drow + (32 * ks + 8 * g) * 2);
+        }
+        floatx4_t sv[2], dp[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          sv[j] = floatx4_t{};
+          dp[j] = floatx4_t{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            sv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], kf[j][ks], sv[j], 0, 0, 0);
+            dp[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad[ks], vf[j][ks], dp[j], 0, 0, 0);
+          }
+        }
+        const int q0 = qb * 16 + 4 * g;
+        const int4 qp = *(const int4*)(kpos + cur * kChunk + q0);
+        const float4 ql = *(const float4*)(qlse + q0);
+        const float4 qcv = *(const float4*)(qc + q0);
+        const int qpv[4] = {qp.x, qp.y, qp.z, qp.w};
+        const float qlv[4] = {ql.x, ql.y, ql.z, ql.w};
+        const float qcc[4] = {qcv.x, qcv.y, qcv.z, qcv.w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const bool masked = CAUSAL ? kp[j] >= qpv[b] : kp[j] == qpv[b];
+            const float wp = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(sv[j][b], ksc[j], -qlv[b]));
+            wpf[j][4 * half + b] = (__bf16)wp;
+            dsf[j][4 * half + b] = (__bf16)(wp * (dp[j][b] - qcc[b]));
+          }
+      }
+      const int off = (g + 4 * e) * Lay::kPair + (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
+      const unsigned char* dpair = lds + M::kDp + off;
+      const unsigned char* qpair = lds + M::kKp + cur * Lay::kPM + off;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8_t a_d = *(const bf16x8_t*)(dpair + dt * 2 * Lay::kBlk8);
+        const bf16x8_t a_q = *(const bf16x8_t*)(qpair + dt * 2 * Lay::kBlk8);
+        dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_d, wpf[0], dva[dt], 0, 0, 0);
+        dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_q, dsf[0], dka[dt], 0, 0, 0);
+        dvc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_d, wpf[1], dvc[dt], 0, 0, 0);
+        dkc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_q, dsf[1], dkc[dt], 0, 0, 0);
+      }
+    }
+  };
+
   // dq of query block w of slot cur (chunk c) over keys of slots prv and cur
   auto query_step = [&](int c, int cur, int prv, floatx4_t* dq) {
     const int posq = kpos[cur * kChunk + blk];
@@ -407,18 +485,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       if (c + 2 <= cend && t < kChunk) pnext = pm[(c + 2) * kChunk + t];
     }
     const int cur = c & 1, prv = cur ^ 1;
-    if (c > c0) {  // the last queries of the keys of chunk c - 1
-      keys_step(prv, cur);
+    // (at d = 64 two workgroups share a CU, and the registers of the joint
+    // step would not fit their half of the file: separate steps there)
+    if (D == 128 && c > c0 && c < c1) {
+      // key blocks of chunks c - 1 (their last queries) and c (their first)
+      floatx4_t dkc[DT], dvc[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dkc[dt] = floatx4_t{};
+        dvc[dt] = floatx4_t{};
+      }
+      keys_step2(cur, dkc, dvc);
       finish(prv);
-    }
-    if (c < c1) {
       query_step(c, cur, prv, dqa);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        dka[dt] = floatx4_t{};
-        dva[dt] = floatx4_t{};
+        dka[dt] = dkc[dt];
+        dva[dt] = dvc[dt];
       }
-      keys_step(cur, cur);
+    } else {
+      if (c > c0) {  // the last queries of the keys of chunk c - 1
+        keys_step(prv, cur);
+        finish(prv);
+      }
+      if (c < c1) {
+        query_step(c, cur, prv, dqa);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dka[dt] = floatx4_t{};
+          dva[dt] = floatx4_t{};
+        }
+        keys_step(cur, cur);
+      }
     }
     __syncthreads();  // slot prv and the query chunk are no longer read
     if (more) {
