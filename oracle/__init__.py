@@ -40,7 +40,14 @@ def build(force: bool = True) -> str:
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len",
-        "causal")]
+        "causal", "variant")]
+
+
+# variant bits (lsh_oracle.h): readings the pages also allow; 0 is the default
+LOOK_AHEAD = 1
+SAME_BUCKET = 2
+NORM_QUERIES = 4
+DEDUP = 8
 
 
 _lib = None
@@ -84,10 +91,10 @@ def _load():
             "lsh_oracle_check": [C],
             "lsh_oracle_hash": [C, P, P, P, P],
             "lsh_oracle_sort": [C, P, P, P],
-            "lsh_oracle_attend": [C, P, P, P, P, P],
+            "lsh_oracle_attend": [C, P, P, P, P, P, P],
             "lsh_oracle_combine": [C, P, P, P],
             "lsh_oracle_forward": [C, P, P, P, P, P, P, P, P, P],
-            "lsh_oracle_attend_rows": [C, P, P, P, ctypes.c_int64, P, P, P],
+            "lsh_oracle_attend_rows": [C, P, P, P, P, ctypes.c_int64, P, P, P],
             "lsh_oracle_backward": [C, P, P, P, P, P, P],
         }.items():
             f = getattr(lib, name)
@@ -100,11 +107,12 @@ def _load():
 def config(w=None, **kw) -> Config:
     """Config from a workloads.Workload (or any object with the same fields) and/or keywords."""
     names = ("batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len",
-             "causal")
-    vals = {}
+             "causal", "variant")
+    vals = {"variant": 0}
     if w is not None:
         for n in names:
-            vals[n] = int(getattr(w, n))
+            if hasattr(w, n):
+                vals[n] = int(getattr(w, n))
     vals.update({k: int(v) for k, v in kw.items()})
     return Config(**{n: vals[n] for n in names})
 
@@ -148,13 +156,14 @@ def sort(c: Config, buckets):
     return pm, iv
 
 
-def attend(c: Config, qk, v, perm):
-    """Per-round outputs o [B, H, R, L, d] and logsumexp [B, H, R, L], original order."""
-    qk, v, pm = _f64(qk), _f64(v), _i32(perm)
+def attend(c: Config, qk, v, perm, buckets=None):
+    """Per-round outputs o [B, H, R, L, d] and logsumexp [B, H, R, L], original order.
+    buckets [B, H, R, L] is needed with the SAME_BUCKET variant."""
+    qk, v, pm, bk = _f64(qk), _f64(v), _i32(perm), _i32(buckets)
     o = np.empty(_shapes(c) + (c.head_dim,), np.float64)
     lse = np.empty(_shapes(c), np.float64)
-    _chk(_load().lsh_oracle_attend(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(o), _p(lse)),
-         "attend")
+    _chk(_load().lsh_oracle_attend(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(bk), _p(o),
+                                   _p(lse)), "attend")
     return o, lse
 
 
@@ -178,13 +187,14 @@ def forward(c: Config, qk, v, rotations, buckets_override: Optional[np.ndarray] 
     return {"out": out, "lse": lse, "buckets": bk, "perm": pm, "margin": mg}
 
 
-def attend_rows(c: Config, qk, v, perm, rows):
-    """Combined output rows [n, d] and per-round lse [n, R] for rows = (b*H+h)*L+i."""
-    qk, v, pm = _f64(qk), _f64(v), _i32(perm)
+def attend_rows(c: Config, qk, v, perm, rows, buckets=None):
+    """Combined output rows [n, d] and per-round lse [n, R] for rows = (b*H+h)*L+i
+    (buckets as for attend)."""
+    qk, v, pm, bk = _f64(qk), _f64(v), _i32(perm), _i32(buckets)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     out = np.empty((rows.size, c.head_dim), np.float64)
     lse = np.empty((rows.size, c.n_rounds), np.float64)
-    _chk(_load().lsh_oracle_attend_rows(ctypes.byref(c), _p(qk), _p(v), _p(pm),
+    _chk(_load().lsh_oracle_attend_rows(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(bk),
                                         ctypes.c_int64(rows.size), _p(rows), _p(out), _p(lse)),
          "attend_rows")
     return out, lse

@@ -21,6 +21,7 @@ int lsh_oracle_check(const lsh_oracle_config* c) {
   if (c->n_rounds < 1 || c->chunk_len < 1 || c->seq_len % c->chunk_len != 0) return -3;
   if (c->n_buckets < 1 || (c->n_buckets > 1 && c->n_buckets % 2 != 0)) return -4;
   if (c->causal != 0 && c->causal != 1) return -5;
+  if (c->variant < 0 || c->variant > 15) return -11;
   return 0;
 }
 
@@ -155,23 +156,33 @@ static void unit_key(const double* k, int64_t d, double* khat) {
 }
 
 /* The attendable keys of the query at slot s of one round: its chunk and the
- * previous one, without the query itself and (causal) later positions.
- * qk_bh: [L, d] of one (b, h); pm: perm of the round. Writes the keys'
- * positions key[n] and logits logit[n] (n returned). Scratch: khat [d]. */
+ * previous one (LOOK_AHEAD: and the next one), without the query itself,
+ * (causal) later positions and (SAME_BUCKET) keys of other buckets.
+ * qk_bh: [L, d] of one (b, h); pm: perm of the round; bk: the round's buckets
+ * at original positions (read with SAME_BUCKET only). Writes the keys'
+ * positions key[n] and logits logit[n] (n returned, at most 3m). Scratch:
+ * khat [d], qhat [d]. */
 static int64_t window(const lsh_oracle_config* c, const double* qk_bh, const int32_t* pm,
-                      int64_t s, double* khat, double* logit, int64_t* key) {
-  const int64_t d = c->head_dim, m = c->chunk_len;
+                      const int32_t* bk, int64_t s, double* khat, double* qhat, double* logit,
+                      int64_t* key) {
+  const int64_t d = c->head_dim, m = c->chunk_len, L = c->seq_len;
   const int64_t i = pm[s];
   const int64_t chunk = s / m;
   const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;
-  const int64_t last = (chunk + 1) * m;
+  int64_t last = (chunk + 1) * m;
+  if ((c->variant & LSH_ORACLE_LOOK_AHEAD) && last < L) last += m;
   const double* q = qk_bh + i * d;
+  if (c->variant & LSH_ORACLE_NORM_QUERIES) {
+    unit_key(q, d, qhat);
+    q = qhat;
+  }
   const double scale = 1.0 / sqrt((double)d);
   int64_t n = 0;
   for (int64_t t = first; t < last; ++t) {
     const int64_t j = pm[t];
     if (j == i) continue;                 /* self-mask */
     if (c->causal && j > i) continue;     /* causal mask on original positions */
+    if ((c->variant & LSH_ORACLE_SAME_BUCKET) && bk[j] != bk[i]) continue;
     unit_key(qk_bh + j * d, d, khat);
     double dot = 0.0;
     for (int64_t u = 0; u < d; ++u) dot += q[u] * khat[u];
@@ -182,15 +193,40 @@ static int64_t window(const lsh_oracle_config* c, const double* qk_bh, const int
   return n;
 }
 
-/* qk_bh, v_bh: [L, d] of one (b, h); pm: perm of one round; s: the query slot.
- * Writes o_row [d] and returns the round's logsumexp. Scratch: khat [d],
- * logit [2m], key [2m]. */
+/* DEDUP: the number of rounds in whose window key j is attendable for query
+ * i (self and causal masks do not depend on the round and hold already).
+ * inv_bh, bk_bh: [R, L] of one (b, h). */
+static int64_t rounds_sharing(const lsh_oracle_config* c, const int32_t* inv_bh,
+                              const int32_t* bk_bh, int64_t i, int64_t j) {
+  const int64_t L = c->seq_len, m = c->chunk_len, R = c->n_rounds;
+  int64_t n = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t ci = inv_bh[r * L + i] / m, cj = inv_bh[r * L + j] / m;
+    int in = cj == ci || cj == ci - 1;
+    if (c->variant & LSH_ORACLE_LOOK_AHEAD) in = in || cj == ci + 1;
+    if ((c->variant & LSH_ORACLE_SAME_BUCKET) && bk_bh[r * L + j] != bk_bh[r * L + i]) in = 0;
+    n += in;
+  }
+  return n;
+}
+
+/* qk_bh, v_bh: [L, d] of one (b, h); round r; s: the query slot; pm_bh,
+ * inv_bh, bk_bh: [R, L] of the (b, h) (inv_bh read with DEDUP, bk_bh with
+ * SAME_BUCKET). Writes o_row [d] and returns the round's logsumexp. With
+ * DEDUP each logit is lowered by log N_ij. Scratch: khat, qhat [d], logit,
+ * key [3m]. */
 static double attend_one(const lsh_oracle_config* c, const double* qk_bh, const double* v_bh,
-                         const int32_t* pm, int64_t s, double* o_row, double* khat,
+                         const int32_t* pm_bh, const int32_t* inv_bh, const int32_t* bk_bh,
+                         int64_t r, int64_t s, double* o_row, double* khat, double* qhat,
                          double* logit, int64_t* key) {
-  const int64_t d = c->head_dim;
+  const int64_t d = c->head_dim, L = c->seq_len;
+  const int32_t* pm = pm_bh + r * L;
   const int64_t i = pm[s];
-  const int64_t n = window(c, qk_bh, pm, s, khat, logit, key);
+  const int64_t n = window(c, qk_bh, pm, bk_bh ? bk_bh + r * L : NULL, s, khat, qhat, logit,
+                           key);
+  if (c->variant & LSH_ORACLE_DEDUP)
+    for (int64_t a = 0; a < n; ++a)
+      logit[a] -= log((double)rounds_sharing(c, inv_bh, bk_bh, i, key[a]));
   if (n == 0) {
     for (int64_t u = 0; u < d; ++u) o_row[u] = v_bh[i * d + u];
     return LSH_ORACLE_SELF_LOGIT;
@@ -209,34 +245,137 @@ static double attend_one(const lsh_oracle_config* c, const double* qk_bh, const 
   return lse;
 }
 
+/* inv [nseg, L] of perm: the slot of each position, per (b, h, round) */
+static int32_t* inverse_perm(const lsh_oracle_config* c, const int32_t* perm) {
+  const int64_t L = c->seq_len, nseg = (int64_t)seg_count(c);
+  int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nseg * L));
+  if (!inv) return NULL;
+#pragma omp parallel for schedule(static)
+  for (int64_t seg = 0; seg < nseg; ++seg)
+    for (int64_t s = 0; s < L; ++s) inv[seg * L + perm[seg * L + s]] = (int32_t)s;
+  return inv;
+}
+
 int lsh_oracle_attend(const lsh_oracle_config* c, const double* qk, const double* v,
-                      const int32_t* perm, double* o, double* lse) {
+                      const int32_t* perm, const int32_t* buckets, double* o, double* lse) {
   int rc = lsh_oracle_check(c);
   if (rc) return rc;
+  if ((c->variant & LSH_ORACLE_SAME_BUCKET) && !buckets) return -12;
   const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
   const int64_t nseg = (int64_t)seg_count(c);
+  int32_t* inv = NULL;
+  if (c->variant & LSH_ORACLE_DEDUP) {
+    inv = inverse_perm(c, perm);
+    if (!inv) return -8;
+  }
 #pragma omp parallel
   {
     double* khat = (double*)malloc(sizeof(double) * (size_t)d);
-    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
-    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+    double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(3 * m));
 #pragma omp for schedule(dynamic, 1)
     for (int64_t seg = 0; seg < nseg; ++seg) {
-      const int64_t bh = seg / R;
+      const int64_t bh = seg / R, r = seg % R;
       const int32_t* pm = perm + seg * L;
       for (int64_t s = 0; s < L; ++s) {
         const int64_t i = pm[s];
         /* unsort: results are stored at the original position i */
-        double l = attend_one(c, qk + bh * L * d, v + bh * L * d, pm, s,
-                              o + (seg * L + i) * d, khat, logit, key);
+        double l = attend_one(c, qk + bh * L * d, v + bh * L * d, perm + bh * R * L,
+                              inv ? inv + bh * R * L : NULL,
+                              buckets ? buckets + bh * R * L : NULL, r, s,
+                              o + (seg * L + i) * d, khat, qhat, logit, key);
         lse[seg * L + i] = l;
       }
     }
     free(khat);
+    free(qhat);
     free(logit);
     free(key);
   }
+  free(inv);
   return 0;
+}
+
+/* DEDUP, from the definition: the query at position i attends once to every
+ * key that any round makes attendable for it (the union of the rounds' key
+ * sets); if the union is empty it attends to itself only (out = v_i).
+ * stamp [L]: scratch marking the keys already taken, with the value mark.
+ * Scratch: ukey, ulogit [R * 3m] and window()'s. */
+static void union_one(const lsh_oracle_config* c, const double* qk_bh, const double* v_bh,
+                      const int32_t* pm_bh, const int32_t* inv_bh, const int32_t* bk_bh,
+                      int64_t i, double* out_row, int64_t* stamp, int64_t mark, double* khat,
+                      double* qhat, double* logit, int64_t* key, double* ulogit,
+                      int64_t* ukey) {
+  const int64_t d = c->head_dim, L = c->seq_len, R = c->n_rounds;
+  int64_t nu = 0;
+  for (int64_t r = 0; r < R; ++r) {
+    const int64_t n = window(c, qk_bh, pm_bh + r * L, bk_bh ? bk_bh + r * L : NULL,
+                             inv_bh[r * L + i], khat, qhat, logit, key);
+    for (int64_t a = 0; a < n; ++a) {
+      if (stamp[key[a]] == mark) continue;
+      stamp[key[a]] = mark;
+      ukey[nu] = key[a];
+      ulogit[nu] = logit[a];
+      ++nu;
+    }
+  }
+  if (nu == 0) {
+    for (int64_t u = 0; u < d; ++u) out_row[u] = v_bh[i * d + u];
+    return;
+  }
+  double mx = -INFINITY;
+  for (int64_t a = 0; a < nu; ++a) mx = ulogit[a] > mx ? ulogit[a] : mx;
+  double sum = 0.0;
+  for (int64_t a = 0; a < nu; ++a) sum += exp(ulogit[a] - mx);
+  for (int64_t u = 0; u < d; ++u) out_row[u] = 0.0;
+  for (int64_t a = 0; a < nu; ++a) {
+    const double w = exp(ulogit[a] - mx) / sum;
+    for (int64_t u = 0; u < d; ++u) out_row[u] += w * v_bh[ukey[a] * d + u];
+  }
+}
+
+/* union_one for every position, or for the listed rows (rows[k] = bh * L + i;
+ * all positions when rows is NULL) into out [n, d] */
+static int union_rows(const lsh_oracle_config* c, const double* qk, const double* v,
+                      const int32_t* perm, const int32_t* inv, const int32_t* buckets,
+                      int64_t n_rows, const int64_t* rows, double* out) {
+  const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* khat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(3 * m));
+    double* ulogit = (double*)malloc(sizeof(double) * (size_t)(R * 3 * m));
+    int64_t* ukey = (int64_t*)malloc(sizeof(int64_t) * (size_t)(R * 3 * m));
+    int64_t* stamp = (int64_t*)malloc(sizeof(int64_t) * (size_t)L);
+    const int ok = khat && qhat && logit && key && ulogit && ukey && stamp;
+    if (!ok) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+      for (int64_t j = 0; j < L; ++j) stamp[j] = -1;
+    }
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t k = 0; k < n_rows; ++k) {
+      if (!ok) continue;
+      const int64_t row = rows ? rows[k] : k;
+      const int64_t bh = row / L, i = row % L;
+      union_one(c, qk + bh * L * d, v + bh * L * d, perm + bh * R * L, inv + bh * R * L,
+                buckets ? buckets + bh * R * L : NULL, i, out + k * d, stamp, row, khat, qhat,
+                logit, key, ulogit, ukey);
+    }
+    free(khat);
+    free(qhat);
+    free(logit);
+    free(key);
+    free(ulogit);
+    free(ukey);
+    free(stamp);
+  }
+  return bad ? -8 : 0;
 }
 
 /* ---------------------------------------------------------------------------
@@ -297,9 +436,17 @@ int lsh_oracle_forward(const lsh_oracle_config* c, const double* qk, const doubl
   else if (!rot && c->n_buckets > 1) { rc = -6; goto done; }
   rc = lsh_oracle_sort(c, bk, pm, NULL);
   if (rc) goto done;
-  rc = lsh_oracle_attend(c, qk, v, pm, o, ls);
+  rc = lsh_oracle_attend(c, qk, v, pm, bk, o, ls);
   if (rc) goto done;
-  rc = lsh_oracle_combine(c, o, ls, out);
+  if (c->variant & LSH_ORACLE_DEDUP) {
+    int32_t* inv = inverse_perm(c, pm);
+    if (!inv) { rc = -8; goto done; }
+    rc = union_rows(c, qk, v, pm, inv, bk, (int64_t)c->batch * c->heads * c->seq_len, NULL,
+                    out);
+    free(inv);
+  } else {
+    rc = lsh_oracle_combine(c, o, ls, out);
+  }
 done:
   if (!buckets) free(bk);
   if (!perm) free(pm);
@@ -332,6 +479,7 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
                         const int32_t* perm, const double* dout, double* dqk, double* dv) {
   int rc = lsh_oracle_check(c);
   if (rc) return rc;
+  if (c->variant != 0) return -10;
   const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
   const int64_t nbh = (int64_t)c->batch * c->heads;
   const size_t nsl = seg_count(c) * (size_t)L;
@@ -340,7 +488,7 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
   double* out = (double*)malloc(sizeof(double) * (size_t)(nbh * L * d));
   double* dkhat = (double*)calloc((size_t)(nbh * L * d), sizeof(double));
   if (!o || !lse || !out || !dkhat) { rc = -8; goto done; }
-  rc = lsh_oracle_attend(c, qk, v, perm, o, lse);
+  rc = lsh_oracle_attend(c, qk, v, perm, NULL, o, lse);
   if (rc) goto done;
   rc = lsh_oracle_combine(c, o, lse, out);
   if (rc) goto done;
@@ -349,6 +497,7 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
 #pragma omp parallel
   {
     double* khat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
     double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
     double* pj = (double*)malloc(sizeof(double) * (size_t)(2 * m));
     double* dp = (double*)malloc(sizeof(double) * (size_t)(2 * m));
@@ -382,7 +531,7 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
           }
           const double dlse = w * g;
           /* the round's window, as in the forward */
-          const int64_t n = window(c, qk_bh, pm, s, khat, logit, key);
+          const int64_t n = window(c, qk_bh, pm, NULL, s, khat, qhat, logit, key);
           const double* q = qk_bh + i * d;
           const double scale = 1.0 / sqrt((double)d);
           if (n == 0) {
@@ -425,6 +574,7 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
       }
     }
     free(khat);
+    free(qhat);
     free(logit);
     free(pj);
     free(dp);
@@ -440,25 +590,23 @@ done:
 }
 
 int lsh_oracle_attend_rows(const lsh_oracle_config* c, const double* qk, const double* v,
-                           const int32_t* perm, int64_t n_rows, const int64_t* rows,
-                           double* out_rows, double* lse_rows) {
+                           const int32_t* perm, const int32_t* buckets, int64_t n_rows,
+                           const int64_t* rows, double* out_rows, double* lse_rows) {
   int rc = lsh_oracle_check(c);
   if (rc) return rc;
+  if ((c->variant & LSH_ORACLE_SAME_BUCKET) && !buckets) return -12;
   const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
   const int64_t nbh = (int64_t)c->batch * c->heads;
-  const int64_t nseg = nbh * R;
   for (int64_t k = 0; k < n_rows; ++k)
     if (rows[k] < 0 || rows[k] >= nbh * L) return -9;
-  int32_t* inv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nseg * L));
+  int32_t* inv = inverse_perm(c, perm);
   if (!inv) return -8;
-#pragma omp parallel for schedule(static)
-  for (int64_t seg = 0; seg < nseg; ++seg)
-    for (int64_t s = 0; s < L; ++s) inv[seg * L + perm[seg * L + s]] = (int32_t)s;
 #pragma omp parallel
   {
     double* khat = (double*)malloc(sizeof(double) * (size_t)d);
-    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
-    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+    double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(3 * m));
     double* o = (double*)malloc(sizeof(double) * (size_t)(R * d));
     double* l = (double*)malloc(sizeof(double) * (size_t)R);
 #pragma omp for schedule(dynamic, 16)
@@ -467,18 +615,22 @@ int lsh_oracle_attend_rows(const lsh_oracle_config* c, const double* qk, const d
       for (int64_t r = 0; r < R; ++r) {
         const int64_t seg = bh * R + r;
         const int64_t s = inv[seg * L + i];
-        l[r] = attend_one(c, qk + bh * L * d, v + bh * L * d, perm + seg * L, s, o + r * d,
-                          khat, logit, key);
+        l[r] = attend_one(c, qk + bh * L * d, v + bh * L * d, perm + bh * R * L,
+                          inv + bh * R * L, buckets ? buckets + bh * R * L : NULL, r, s,
+                          o + r * d, khat, qhat, logit, key);
         if (lse_rows) lse_rows[k * R + r] = l[r];
       }
-      combine_one(R, d, o, d, l, 1, out_rows + k * d);
+      if (!(c->variant & LSH_ORACLE_DEDUP)) combine_one(R, d, o, d, l, 1, out_rows + k * d);
     }
     free(khat);
+    free(qhat);
     free(logit);
     free(key);
     free(o);
     free(l);
   }
+  if (c->variant & LSH_ORACLE_DEDUP)
+    rc = union_rows(c, qk, v, perm, inv, buckets, n_rows, rows, out_rows);
   free(inv);
-  return 0;
+  return rc;
 }

@@ -49,7 +49,28 @@ typedef struct {
   int32_t n_rounds;   /* >= 1 */
   int32_t chunk_len;  /* >= 1, divides seq_len */
   int32_t causal;     /* 0 or 1 */
+  int32_t variant;    /* 0, or LSH_ORACLE_* bits below */
 } lsh_oracle_config;
+
+/* Variant readings (bits of variant; 0 is the default reading). Each is a
+ * reading the pages also support:
+ *   LOOK_AHEAD   the window also holds the next chunk ([DT] section 2.1: a
+ *                query looks at the neighbouring groups, one before and one
+ *                after);
+ *   SAME_BUCKET  inside the window only keys of the query's own bucket in that
+ *                round are attendable ([DT] math paragraph: the mask M keeps
+ *                positions of the same bucket);
+ *   NORM_QUERIES queries are unit-normalised as well as keys ([DT] section
+ *                2.1: keys and queries are normalised to unit vectors);
+ *   DEDUP        a key that several rounds give a query counts once: the
+ *                query attends to the union of its rounds' key sets ([2K]
+ *                www.2kiu.com/news/5253576/ section 2.2: the final candidate
+ *                set is the de-duplicated union over rounds).
+ * The backward supports the default reading only. */
+#define LSH_ORACLE_LOOK_AHEAD 1
+#define LSH_ORACLE_SAME_BUCKET 2
+#define LSH_ORACLE_NORM_QUERIES 4
+#define LSH_ORACLE_DEDUP 8
 
 /* Logit given to a query's own key; also the logsumexp of a round in which the
  * query can attend to nothing but itself. */
@@ -63,29 +84,37 @@ int lsh_oracle_hash(const lsh_oracle_config* cfg, const double* qk, const double
 int lsh_oracle_sort(const lsh_oracle_config* cfg, const int32_t* buckets, int32_t* perm,
                     int32_t* inv);
 
+/* buckets [B, H, R, L] (original positions) is read only with SAME_BUCKET and
+ * may be NULL otherwise. With DEDUP, o and lse are the rounds' outputs with
+ * each logit lowered by log N_ij (N_ij = the number of rounds that give key j
+ * to query i), whose combination is the union's attention. */
 int lsh_oracle_attend(const lsh_oracle_config* cfg, const double* qk, const double* v,
-                      const int32_t* perm, double* o, double* lse);
+                      const int32_t* perm, const int32_t* buckets, double* o, double* lse);
 
 int lsh_oracle_combine(const lsh_oracle_config* cfg, const double* o, const double* lse,
                        double* out);
 
 /* Whole forward. buckets_override (nullable) replaces the hash step's buckets;
- * margin is still computed from the projections when rotations are given. */
+ * margin is still computed from the projections when rotations are given.
+ * With DEDUP, out is computed from the union of the rounds' key sets directly,
+ * and lse is that of lsh_oracle_attend. */
 int lsh_oracle_forward(const lsh_oracle_config* cfg, const double* qk, const double* v,
                        const double* rotations, const int32_t* buckets_override,
                        double* out, double* lse, int32_t* buckets, int32_t* perm,
                        double* margin);
 
 /* Backward at fixed permutations: dqk, dv [B, H, L, d] from dout [B, H, L, d]
- * (gradient of a loss with respect to out); perm [B, H, R, L] as from forward. */
+ * (gradient of a loss with respect to out); perm [B, H, R, L] as from forward.
+ * Default reading only (variant 0; otherwise -10). */
 int lsh_oracle_backward(const lsh_oracle_config* cfg, const double* qk, const double* v,
                         const int32_t* perm, const double* dout, double* dqk, double* dv);
 
-/* Output rows for a sample of (b, h, i), given every round's perm:
- * rows[k] = (b * H + h) * L + i; out_rows [n_rows, d]; lse_rows [n_rows, n_rounds]. */
+/* Output rows for a sample of (b, h, i), given every round's perm (and buckets,
+ * as for lsh_oracle_attend): rows[k] = (b * H + h) * L + i; out_rows [n_rows, d];
+ * lse_rows [n_rows, n_rounds]. */
 int lsh_oracle_attend_rows(const lsh_oracle_config* cfg, const double* qk, const double* v,
-                           const int32_t* perm, int64_t n_rows, const int64_t* rows,
-                           double* out_rows, double* lse_rows);
+                           const int32_t* perm, const int32_t* buckets, int64_t n_rows,
+                           const int64_t* rows, double* out_rows, double* lse_rows);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@ import oracle
 
 import test_oracle_backward as bpins
 import test_oracle_pins as pins
+import test_oracle_variants as vpins
 
 # (name, original text, planted mistake); a list replaces several places at once.
 # Every planted mistake keeps all memory accesses in bounds.
@@ -22,9 +23,9 @@ MUTATIONS = [
     ("no look-back", "const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;",
      "const int64_t first = chunk * m;"),
     ("look-ahead instead of look-back",
-     "const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;\n  const int64_t last = (chunk + 1) * m;",
+     "const int64_t first = (chunk > 0 ? chunk - 1 : chunk) * m;\n  int64_t last = (chunk + 1) * m;",
      "const int64_t first = chunk * m;\n"
-     "  const int64_t last = (chunk + 2) * m < c->seq_len ? (chunk + 2) * m : c->seq_len;"),
+     "  int64_t last = (chunk + 2) * m < c->seq_len ? (chunk + 2) * m : c->seq_len;"),
     ("keys not normalised", "khat[t] = (nrm > 0.0) ? k[t] / nrm : 0.0;", "khat[t] = k[t];"),
     ("causal reversed", "if (c->causal && j > i) continue;", "if (c->causal && j < i) continue;"),
     ("self not masked", "if (j == i) continue;", "if (0) continue;"),
@@ -52,6 +53,15 @@ MUTATIONS = [
     ("bwd: key gradient from the key instead of the query",
      "dkhat[(bh * L + j) * d + u] += ds * q[u] * scale;",
      "dkhat[(bh * L + j) * d + u] += ds * khat[u] * scale;"),
+    # variants
+    ("look-ahead chunk missing", "&& last < L) last += m;", "&& last < L) last += 0;"),
+    ("same-bucket mask against itself", "bk[j] != bk[i]) continue;", "bk[j] != bk[j]) continue;"),
+    ("queries not normalised", "unit_key(q, d, qhat);\n    q = qhat;", "unit_key(q, d, qhat);"),
+    ("dedup count ignored",
+     "logit[a] -= log((double)rounds_sharing(c, inv_bh, bk_bh, i, key[a]));",
+     "logit[a] -= 0.0 * log((double)rounds_sharing(c, inv_bh, bk_bh, i, key[a]));"),
+    ("union not de-duplicated", "if (stamp[key[a]] == mark) continue;", "if (0) continue;"),
+    ("shared rounds without the look-ahead chunk", "in = in || cj == ci + 1;", "in = in;"),
 ]
 
 
@@ -74,6 +84,13 @@ def _pin_calls():
         lambda: bpins.test_backward_matches_finite_differences(o, False),
         lambda: bpins.test_backward_matches_finite_differences(o, True),
         lambda: bpins.test_backward_single_chunk_equals_dense_autograd(o, 3, True),
+        lambda: vpins.test_variant_equals_dense_definition(o, vpins.LA, True),
+        lambda: vpins.test_variant_equals_dense_definition(o, vpins.SB, False),
+        lambda: vpins.test_variant_equals_dense_definition(o, vpins.NQ, False),
+        lambda: vpins.test_variant_equals_dense_definition(o, vpins.DD, True),
+        lambda: vpins.test_variant_equals_dense_definition(o, vpins.LA | vpins.DD, False),
+        lambda: vpins.test_look_ahead_over_two_chunks_is_full_attention(o),
+        lambda: vpins.test_dedup_with_identical_rounds_is_one_round(o),
     ]
 
 
