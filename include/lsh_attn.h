@@ -66,8 +66,27 @@ enum {
   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
   /* Also allocate the workspace of lsh_attn_backward: per position and round,
    * 2 fp32 rows of head_dim on the matrix-core path (bf16, chunk_len 64, head_dim
-   * 64 or 128) or 4 on the other shapes, plus 12 bytes; 4 bytes per position. */
-  LSH_ATTN_FLAG_BACKWARD = 4
+   * 64 or 128) or 4 on the other shapes, plus 12 bytes; 4 bytes per position.
+   * Not with the variant flags below (UNSUPPORTED). */
+  LSH_ATTN_FLAG_BACKWARD = 4,
+  /* Variant readings of the window and the combination, each one the pages
+   * also describe (the default, all off, is the previous chunk and the chunk
+   * itself, no bucket mask, raw queries, rounds combined as a multiset):
+   * the window also holds the next chunk (Reformer overview at
+   * www.dtcms.com/a/488796.html, section 2.1: one neighbouring group before
+   * and one after); the last chunk has none. */
+  LSH_ATTN_FLAG_LOOK_AHEAD = 8,
+  /* inside the window only keys in the query's own bucket of that round are
+   * attendable (the same page's mask M of same-bucket positions) */
+  LSH_ATTN_FLAG_SAME_BUCKET = 16,
+  /* queries are unit-normalised as well as keys (same page, section 2.1) */
+  LSH_ATTN_FLAG_NORM_QUERIES = 32,
+  /* a key given to a query by several rounds counts once: the query attends
+   * to the union of its rounds' key sets (www.2kiu.com/news/5253576/, section
+   * 2.2: the de-duplicated union over rounds). Computed per round with each
+   * logit lowered by log N (N = the number of rounds that give the pair);
+   * the lse output holds those per-round values. */
+  LSH_ATTN_FLAG_DEDUP = 64
 };
 
 typedef struct {

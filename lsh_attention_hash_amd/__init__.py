@@ -25,6 +25,10 @@ FP32, BF16 = 0, 1
 FLAG_SEPARATE_GATHER = 1
 FLAG_FP32_ROUND_OUTPUTS = 2
 FLAG_BACKWARD = 4
+FLAG_LOOK_AHEAD = 8
+FLAG_SAME_BUCKET = 16
+FLAG_NORM_QUERIES = 32
+FLAG_DEDUP = 64
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP"}
 
 # Every function declared in include/lsh_attn.h.
@@ -122,11 +126,14 @@ class LSHAttention:
 
     def __init__(self, batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len=64,
                  causal=False, dtype=torch.bfloat16, out_dtype=None, separate_gather=False,
-                 fp32_round_outputs=False, backward=False, device=None):
+                 fp32_round_outputs=False, backward=False, device=None, look_ahead=False,
+                 same_bucket=False, norm_queries=False, dedup=False):
         self.lib = load_library()
         flags = (FLAG_SEPARATE_GATHER if separate_gather else 0) | (
             FLAG_FP32_ROUND_OUTPUTS if fp32_round_outputs else 0) | (
-            FLAG_BACKWARD if backward else 0)
+            FLAG_BACKWARD if backward else 0) | (FLAG_LOOK_AHEAD if look_ahead else 0) | (
+            FLAG_SAME_BUCKET if same_bucket else 0) | (
+            FLAG_NORM_QUERIES if norm_queries else 0) | (FLAG_DEDUP if dedup else 0)
         self.cfg = make_config(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len,
                                causal, dtype, out_dtype, flags)
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None

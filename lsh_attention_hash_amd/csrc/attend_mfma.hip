@@ -520,7 +520,8 @@ void launch_d(const Problem& p, const void* qk, const void* v, const void* qk_s,
 }  // namespace
 
 bool attend_mfma_supported(const Problem& p) {
-  return p.dtype == LSH_ATTN_BF16 && p.m == kChunk && (p.d == 64 || p.d == 128);
+  return p.dtype == LSH_ATTN_BF16 && p.m == kChunk && (p.d == 64 || p.d == 128) &&
+         !(p.flags & kVariantFlags);
 }
 
 template <typename OT>

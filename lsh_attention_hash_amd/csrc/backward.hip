@@ -432,7 +432,8 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
     if (e == hipSuccess)
       e = launch_attend_mfma_dot(p, qk, v, perm, knorm, dout, b.od, b.lse, s);
   } else {
-    e = launch_attend(p, qk, v, nullptr, nullptr, perm, nullptr, b.o32, b.lse, s);
+    e = launch_attend(p, qk, v, nullptr, nullptr, perm, nullptr, nullptr, nullptr, b.o32, b.lse,
+                      s);
   }
   if (e != hipSuccess) return e;
   if (ev) (void)hipEventRecord(ev[1], s);

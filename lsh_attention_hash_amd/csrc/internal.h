@@ -51,6 +51,7 @@ struct HashScratch {
 struct Workspace {
   uint16_t* buckets = nullptr;     // [seg, L]
   int32_t* perm = nullptr;         // [seg, L] sorted slot -> position
+  int32_t* inv = nullptr;          // [seg, L] position -> sorted slot (de-duplicated union only)
   void* o = nullptr;               // [seg, L + kORowPad, d] per-round outputs at original positions
                                    // (fp16, or fp32 with the fp32 flag / plain kernel)
   float* lse = nullptr;            // [seg, L]
@@ -98,9 +99,14 @@ hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* coun
                        int32_t* perm, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                          void* qk_sorted, void* v_sorted, hipStream_t s);
+// buckets [seg, L] at original positions (read by the same-bucket variant),
+// inv [seg, L] (read by the de-duplicated union; may be null otherwise)
 hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const void* qk_sorted,
-                         const void* v_sorted, const int32_t* perm, const float* knorm, float* o,
-                         float* lse, hipStream_t s);
+                         const void* v_sorted, const int32_t* perm, const float* knorm,
+                         const uint16_t* buckets, const int32_t* inv, float* o, float* lse,
+                         hipStream_t s);
+// inv[seg, perm[seg, s]] = s
+hipError_t launch_inverse_perm(const Problem& p, const int32_t* perm, int32_t* inv, hipStream_t s);
 bool attend_mfma_supported(const Problem& p);
 template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
@@ -128,6 +134,10 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
                                 BwdWorkspace& b, hipStream_t s);
+
+// The variant readings (flags); the matrix-core attention takes none of them.
+constexpr int kVariantFlags = LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_SAME_BUCKET |
+                              LSH_ATTN_FLAG_NORM_QUERIES | LSH_ATTN_FLAG_DEDUP;
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.

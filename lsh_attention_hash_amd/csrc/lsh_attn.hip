@@ -46,8 +46,10 @@ int validate(const lsh_attn_config_t* c) {
     return LSH_ATTN_ERR_INVALID_ARG;
   if (c->causal != 0 && c->causal != 1) return LSH_ATTN_ERR_INVALID_ARG;
   if ((c->flags & ~(LSH_ATTN_FLAG_SEPARATE_GATHER | LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS |
-                    LSH_ATTN_FLAG_BACKWARD)) != 0)
+                    LSH_ATTN_FLAG_BACKWARD | lsh::kVariantFlags)) != 0)
     return LSH_ATTN_ERR_INVALID_ARG;
+  if ((c->flags & LSH_ATTN_FLAG_BACKWARD) && (c->flags & lsh::kVariantFlags))
+    return LSH_ATTN_ERR_UNSUPPORTED;
   if (c->dtype != LSH_ATTN_FP32 && c->dtype != LSH_ATTN_BF16) return LSH_ATTN_ERR_UNSUPPORTED;
   if (c->out_dtype != LSH_ATTN_FP32 && c->out_dtype != LSH_ATTN_BF16)
     return LSH_ATTN_ERR_UNSUPPORTED;
@@ -59,6 +61,7 @@ int validate(const lsh_attn_config_t* c) {
 void free_ws(lsh::Workspace& w) {
   hipFree(w.buckets);
   hipFree(w.perm);
+  hipFree(w.inv);
   hipFree(w.o);
   hipFree(w.lse);
   hipFree(w.sort_counts);
@@ -148,6 +151,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
          alloc(&w.hash.x16, p.n_token_heads() * p.d * 2, t) &&
          alloc(&w.hash.xnorm, p.n_token_heads() * 8, t);
   }
+  if (ok && (p.flags & LSH_ATTN_FLAG_DEDUP)) ok = alloc(&w.inv, rows * 4, t);
   if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
     ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
   if (ok && (p.flags & LSH_ATTN_FLAG_BACKWARD)) {
@@ -216,9 +220,11 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   if (e == hipSuccess && separate)
     e = lsh::launch_gather(p, qk, v, pm, w.qk_sorted, w.v_sorted, s);
   mark(5);
+  if (e == hipSuccess && (p.flags & LSH_ATTN_FLAG_DEDUP)) e = lsh::launch_inverse_perm(p, pm, w.inv, s);
   if (e == hipSuccess)
     e = lsh::launch_attend(p, qk, v, separate ? w.qk_sorted : nullptr,
-                           separate ? w.v_sorted : nullptr, pm, w.knorm, (float*)w.o, ls, s);
+                           separate ? w.v_sorted : nullptr, pm, w.knorm, w.buckets, w.inv,
+                           (float*)w.o, ls, s);
   mark(6);
   if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, s);
   mark(7);

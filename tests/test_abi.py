@@ -60,7 +60,8 @@ def _create(**kw):
     (dict(n_rounds=0), 1),
     (dict(chunk_len=0), 1),
     (dict(causal=2), 1),
-    (dict(flags=8), 1),              # unknown flag
+    (dict(flags=128), 1),            # unknown flag
+    (dict(flags=4 | 64), 2),         # backward with a variant reading
     (dict(seq_len=1 << 25, chunk_len=64), 1),
     (dict(head_dim=96), 2),          # valid but not implemented
     (dict(head_dim=256), 2),
