@@ -44,7 +44,7 @@ def esize(dt: str) -> int:
     return 2 if dt == "bf16" else 4
 
 
-def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None):
+def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, window_chunks=2):
     """Per-launch algorithmic work of each stage (what the method must compute
     or move, not what an implementation happens to move).
     N = B*H*L token-heads, R rounds, d head dim, nb buckets, m chunk length;
@@ -73,7 +73,7 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None):
         "gather": {"bytes": N * R * (4 * d * e + 4)},
         # QK^T and PV over the 2m-key window of every query-round; rows read
         # through the permutation, per-round output row and lse written
-        "attend": {"flops": N * R * 4 * d * 2 * m,
+        "attend": {"flops": N * R * 4 * d * window_chunks * m,
                    "bytes": N * R * (2 * d * e + 4 + d * ro + 4)},
         # R per-round rows and lse read, one output row written
         "combine": {"bytes": N * R * (d * ro + 4) + N * d * eo},
@@ -306,6 +306,8 @@ def main_backward(args, w, inp, op_kw):
         except (OSError, ValueError):
             traffic = None
     rl = roofline(dominant, units, stage_avg[dominant], traffic)
+    if variants and dominant == "attend":
+        rl["kernel"] = "k_attend_var"  # the variant readings' own kernel
     per_stage = {}
     for k, t in stage_avg.items():
         per_stage[k] = {"ms": round(t, 5)}
@@ -355,6 +357,9 @@ def main():
     ap.add_argument("--fp32-round-outputs", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward instead of the forward (its own JSON line)")
+    ap.add_argument("--variants", default="",
+                    help="comma list of variant readings for the forward: look_ahead, "
+                         "same_bucket, norm_queries, dedup (default: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: as many as rounds fit the cores)")
@@ -386,6 +391,10 @@ def main():
 
     w = workloads.get(args.workload)
     out_dtype = args.out_dtype or w.dtype
+    variants = [x for x in args.variants.split(",") if x]
+    for x in variants:
+        if x not in ("look_ahead", "same_bucket", "norm_queries", "dedup"):
+            raise SystemExit(f"unknown variant {x!r}")
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -404,7 +413,8 @@ def main():
     op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
                           w.chunk_len, w.causal, dtype=tdt[w.dtype], out_dtype=tdt[out_dtype],
                           separate_gather=args.separate_gather,
-                          fp32_round_outputs=args.fp32_round_outputs)
+                          fp32_round_outputs=args.fp32_round_outputs,
+                          **{x: True for x in variants})
     out = torch.empty((w.batch, w.heads, w.seq_len, w.head_dim), dtype=tdt[out_dtype],
                       device=dev)
     stream = torch.cuda.current_stream()
@@ -432,14 +442,15 @@ def main():
     calibration_copy(args.calib_copy_mib, dev)
 
     fp16_rounds = w.dtype == "bf16" and w.chunk_len == 64 and not args.fp32_round_outputs
-    units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4, stats)
+    units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4, stats,
+                              3 if "look_ahead" in variants else 2)
     if not args.separate_gather:
         stage_avg.pop("gather")   # rows are read through the permutation inside attend
     # the dominant kernel: the slowest stage that is one kernel launch
     single = {k: v_ for k, v_ in stage_avg.items() if k in STAGE_KERNEL}
     dominant = max(single, key=single.get)
     traffic = None
-    if os.path.exists(args.traffic_json):
+    if os.path.exists(args.traffic_json) and not variants:
         try:
             with open(args.traffic_json) as f:
                 tj = json.load(f)
@@ -449,6 +460,8 @@ def main():
         except (OSError, ValueError):
             traffic = None
     rl = roofline(dominant, units, stage_avg[dominant], traffic)
+    if variants and dominant == "attend":
+        rl["kernel"] = "k_attend_var"  # the variant readings' own kernel
     per_stage = {k: {"ms": round(stage_avg[k], 5)} for k in stage_avg}
     for k in per_stage:
         if stage_avg[k] > 0:
@@ -477,6 +490,7 @@ def main():
                    "inputs": f"{w.kind} seeded (qk {1000 + w.seed_base}, v {2000 + w.seed_base},"
                              f" R {3000 + w.seed_base})",
                    "separate_gather": bool(args.separate_gather),
+                   "variants": variants,
                    "round_outputs": "fp16" if fp16_rounds else "fp32"},
         "roofline": rl,
         "stages": per_stage,

@@ -36,6 +36,7 @@ CFLAGS = [
 EXTRA_FLAGS = {
     "hash_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "backward_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attend_variants.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -148,6 +148,8 @@ hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const 
                                           (_Float16*)o, lse, s);
     return launch_attend_mfma<float>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
   }
+  if (attend_variant_mfma_supported(p))
+    return launch_attend_variant_mfma(p, qk, v, perm, knorm, buckets, inv, o, lse, s);
   const bool bf = p.dtype == LSH_ATTN_BF16;
   if (p.d == 64) {
     if (bf) launch_simple<64, bf16_t>(p, qk, v, qk_sorted, v_sorted, perm, buckets, inv, o, lse, s);

@@ -1,0 +1,435 @@
+// attend_variants.hip -- the chunk attention of the variant readings on gfx950
+// matrix cores (bf16 inputs, chunk_len 64, d in {64, 128}).
+//
+// The readings (flags; the definition is the plain kernel's in attend.hip):
+//   LOOK_AHEAD   the window is the previous, the current and the next chunk
+//                (Reformer overview, www.dtcms.com/a/488796.html, section 2.1:
+//                one neighbouring group before and one after);
+//   SAME_BUCKET  only keys in the query's bucket of the round (same page, the
+//                mask M of its attention formula);
+//   NORM_QUERIES queries unit-normalised too (same page, section 2.1);
+//   DEDUP        a key that several rounds give a query counts once
+//                (www.2kiu.com/news/5253576/, section 2.2): each logit is
+//                lowered by log N_ij, N_ij the number of rounds whose window
+//                (and bucket, with SAME_BUCKET) gives key j to query i, so the
+//                usual combination of the rounds is one softmax over the union.
+//
+// The work split and operand layouts follow k_attend_mfma: one workgroup of 4
+// waves x 16 queries walks a range of chunks of one segment; the window's
+// chunks sit in a ring of NS slots in LDS (NS = 3 with the look-ahead), qk rows
+// row-major (keys, and the queries of the current chunk), v rows by pairs of
+// 4-row groups (the A operand of P V); S^T = K Q^T per 16-key block, softmax
+// in log2 units against the Cauchy-Schwarz bound, O^T = V^T P^T per 32-key
+// step, row sums from a ones MFMA. Per key the slot also holds its bucket in
+// this round and, for DEDUP, its chunk (and bucket) in every round, which the
+// count N_ij compares with the query's. The next chunk's rows are loaded while
+// the current one is computed. Per-round outputs are rows at original
+// positions, fp16 (as the default kernel's) or fp32 with the fp32 flag.
+#include <type_traits>
+
+#include "dtype.h"
+#include "internal.h"
+#include "rows_lds.h"
+
+namespace lsh {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+using rows::BLay;
+using rows::load_group;
+using rows::store_pair;
+using rows::store_rm;
+using rows::zero_lds;
+
+constexpr int kChunk = 64;
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kBoundLimit = 60.0f;
+constexpr int kMaxDedupRounds = 8;
+
+template <int D, int NS, bool DD>
+struct VLds {
+  using L = BLay<D>;
+  static constexpr int kKt = 0;                               // [NS][64] qk rows
+  static constexpr int kVp = kKt + NS * L::kRM;               // [NS] v rows by group pairs
+  static constexpr int kScale = kVp + NS * L::kPM;            // [NS][64] log2(e)/(sqrt(d)|k|)
+  static constexpr int kPos = kScale + NS * kChunk * 4;       // [NS][64] original positions
+  static constexpr int kBound = kPos + NS * kChunk * 4;       // [NS][64] log2(e)|k|/sqrt(d)
+  static constexpr int kBkt = kBound + NS * kChunk * 4;       // [NS][64] bucket in the round
+  static constexpr int kRounds = DD ? kMaxDedupRounds : 0;
+  static constexpr int kCid = kBkt + NS * kChunk * 4;         // [NS][64][8] chunk per round
+  static constexpr int kCbk = kCid + NS * kChunk * kRounds * 4;  // [NS][64][8] bucket per round
+  static constexpr int kPn = kCbk + NS * kChunk * kRounds * 4;   // [64] next positions
+  static constexpr int kBytes = kPn + kChunk * 4;
+};
+
+// one chunk's rows and per-row data between their loads and the staging
+struct VRegs {
+  uint4 k[4], v[4];
+  int pos, bk;
+  float n2;
+  int cid[kMaxDedupRounds], cbk[kMaxDedupRounds];
+};
+
+__device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
+
+// Without the de-duplication counts, two workgroups fit a CU at d = 128 when
+// the window is two chunks: let each wave take half the register file.
+template <int D, bool CAUSAL, int NS, bool DD, typename OT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 1))) void k_attend_var(
+    const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
+    const int32_t* __restrict__ perm, const float* __restrict__ knorm,
+    const uint16_t* __restrict__ bkt, const int32_t* __restrict__ inv, OT* __restrict__ o,
+    float* __restrict__ lse, int L, int R, int nseg, int chunks_per_wg, int ranges,
+    int group_segs, int64_t o_seg_rows, int flags) {
+  using Lay = BLay<D>;
+  using M = VLds<D, NS, DD>;
+  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int NB = 4 * NS;  // 16-key blocks of the window
+  constexpr int NE = 2 * NS;  // 32-key steps of P V
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int nchunks = L / kChunk;
+  const int group = blockIdx.x / (unsigned)(group_segs * ranges);
+  const int first = group * group_segs;
+  const int gn = min(group_segs, nseg - first);
+  const int inner = blockIdx.x - group * group_segs * ranges;
+  const int64_t seg = first + inner % gn;
+  const int range = inner / gn;
+  const int c0 = range * chunks_per_wg;
+  const int c1 = min(nchunks, c0 + chunks_per_wg);
+  if (c0 >= c1) return;
+  // chunks the range stages: c0 - 1 .. c1 - 1 (+ c1 when looking ahead)
+  const int fend = min(nchunks, c1 + NS - 2);
+  const int64_t bh = seg / R;
+  const int64_t row0 = bh * L;
+  const int32_t* pm = perm + seg * L;
+  const unsigned char* qkb = qk + row0 * D * 2;
+  const unsigned char* vb = v + row0 * D * 2;
+  const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  const bool nq = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
+  constexpr bool dd = DD;
+  float* kscale = (float*)(lds + M::kScale);
+  int* kpos = (int*)(lds + M::kPos);
+  float* kbound = (float*)(lds + M::kBound);
+  int* kbk = (int*)(lds + M::kBkt);
+  int* kcid = (int*)(lds + M::kCid);
+  int* kcbk = (int*)(lds + M::kCbk);
+  int* pn = (int*)(lds + M::kPn);
+  const int t = threadIdx.x;
+  const float sc = kLog2e / sqrtf((float)D);
+  auto slot_of = [](int x) { return (x + NS) % NS; };
+
+  auto fetch = [&](VRegs& r) {  // the chunk whose positions are in pn
+    load_group<D>(r.k, qkb, pn);
+    load_group<D>(r.v, vb, pn);
+    if (t < kChunk) {
+      r.pos = pn[t];
+      r.n2 = knorm[row0 + r.pos];
+      if (sb) r.bk = bkt[seg * L + r.pos];
+      if (dd) {
+#pragma unroll
+        for (int u = 0; u < kMaxDedupRounds; ++u)
+          if (u < R) {
+            const int64_t base = (bh * R + u) * L + r.pos;
+            r.cid[u] = inv[base] / kChunk;
+            r.cbk[u] = sb ? (int)bkt[base] : 0;
+          }
+      }
+    }
+  };
+  auto stage = [&](const VRegs& r, int sl) {
+    store_rm<D>(lds + M::kKt + sl * Lay::kRM, r.k);
+    store_pair<D>(lds + M::kVp + sl * Lay::kPM, r.v);
+    if (t < kChunk) {
+      const float nrm = sqrtf(r.n2);
+      kscale[sl * kChunk + t] = r.n2 > 0.f ? sc / nrm : 0.f;
+      kpos[sl * kChunk + t] = r.pos;
+      kbound[sl * kChunk + t] = sc * nrm;
+      if (sb) kbk[sl * kChunk + t] = r.bk;
+      if (dd) {
+#pragma unroll
+        for (int u = 0; u < kMaxDedupRounds; ++u)
+          if (u < R) {
+            kcid[(sl * kChunk + t) * kMaxDedupRounds + u] = r.cid[u];
+            kcbk[(sl * kChunk + t) * kMaxDedupRounds + u] = r.cbk[u];
+          }
+      }
+    }
+  };
+
+  // absent chunks (before the first, after the last) stay zero: finite
+  // operands that every mask excludes
+  zero_lds(lds, M::kPn);
+  __syncthreads();
+  VRegs r;
+  for (int x = max(c0 - 1, 0); x < min(fend, c0 + NS - 1); ++x) {
+    if (t < kChunk) pn[t] = pm[x * kChunk + t];
+    __syncthreads();
+    fetch(r);
+    stage(r, slot_of(x));
+    __syncthreads();
+  }
+  if (c0 + NS - 1 < fend && t < kChunk) pn[t] = pm[(c0 + NS - 1) * kChunk + t];
+  __syncthreads();
+
+  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
+  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
+  const uint32_t ones_u[4] = {one2, one2, one2, one2};
+  const bf16x8_t ones = *(const bf16x8_t*)ones_u;
+  const bool la = NS == 3;
+  int pnext = 0;
+
+  for (int c = c0; c < c1; ++c) {
+    const int f = c + NS - 1;  // the chunk loaded during this step
+    const bool more = f < fend;
+    if (more) {
+      fetch(r);
+      if (f + 1 < fend && t < kChunk) pnext = pm[(f + 1) * kChunk + t];
+    }
+    const int cur = slot_of(c);
+    const int q = 16 * w + lq;
+    const int posq = kpos[cur * kChunk + q];
+    float mq = kbound[cur * kChunk + q];
+    float rq = 1.0f;
+    if (nq) {  // |q| = bound / sc; unit queries have bound sc
+      rq = mq > 0.f ? sc / mq : 0.f;
+      mq = mq > 0.f ? sc : 0.f;
+    }
+    const int bq = sb ? kbk[cur * kChunk + q] : 0;
+    int qcid[kMaxDedupRounds], qcbk[kMaxDedupRounds];
+    if (dd) {
+#pragma unroll
+      for (int u = 0; u < kMaxDedupRounds; ++u) {
+        qcid[u] = kcid[(cur * kChunk + q) * kMaxDedupRounds + u];
+        qcbk[u] = kcbk[(cur * kChunk + q) * kMaxDedupRounds + u];
+      }
+    }
+    bf16x8_t qf[KS];
+    {
+      const unsigned char* row = lds + M::kKt + cur * Lay::kRM + q * Lay::kRow;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *(const bf16x8_t*)(row + (32 * ks + 8 * g) * 2);
+    }
+    auto block_slot = [&](int kb) { return slot_of(c - 1 + kb / 4); };
+    auto block_absent = [&](int kb) {
+      const int x = c - 1 + kb / 4;
+      return x < 0 || x >= nchunks;
+    };
+    auto qk_block = [&](int kb) -> floatx4_t {
+      const unsigned char* row =
+          lds + M::kKt + block_slot(kb) * Lay::kRM + ((kb & 3) * 16 + lq) * Lay::kRow;
+      floatx4_t acc;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8_t*)(row + (32 * ks + 8 * g) * 2), qf[ks],
+            ks == 0 ? floatx4_t{} : acc, 0, 0, 0);
+      return acc;
+    };
+    // masks of the 4 keys 4g + 0..3 of block kb for this lane's query
+    auto masks = [&](int kb, const int* kpv, bool* mk) {
+      const int sl = block_slot(kb);
+      const int key = (kb & 3) * 16 + 4 * g;
+      const bool absent = block_absent(kb);
+      int4 kb4 = {0, 0, 0, 0};
+      if (sb) kb4 = *(const int4*)(kbk + sl * kChunk + key);
+      const int kbv[4] = {kb4.x, kb4.y, kb4.z, kb4.w};
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        mk[b] = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq) | (sb && kbv[b] != bq);
+    };
+    // log2 N for key kk of slot sl: the rounds whose window (and bucket) give
+    // it to this query
+    auto log2_shared = [&](int sl, int kk) -> float {
+      const int* kc = kcid + (sl * kChunk + kk) * kMaxDedupRounds;
+      const int* kq = kcbk + (sl * kChunk + kk) * kMaxDedupRounds;
+      int n = 0;
+#pragma unroll
+      for (int u = 0; u < kMaxDedupRounds; ++u) {
+        const int dc = kc[u] - qcid[u];
+        bool in = dc == 0 || dc == -1 || (la && dc == 1);
+        if (sb) in = in && kq[u] == qcbk[u];
+        n += (u < R && in) ? 1 : 0;
+      }
+      return __log2f((float)max(n, 1));
+    };
+    if (__ballot(mq > kBoundLimit) != 0ull) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb) {
+        const floatx4_t sv = qk_block(kb);
+        const int sl = block_slot(kb);
+        const int key = (kb & 3) * 16 + 4 * g;
+        const float4 scv = *(const float4*)(kscale + sl * kChunk + key);
+        const int4 kp = *(const int4*)(kpos + sl * kChunk + key);
+        const float s4[4] = {scv.x, scv.y, scv.z, scv.w};
+        const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
+        bool mk[4];
+        masks(kb, kpv, mk);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) mx = fmaxf(mx, mk[b] ? -INFINITY : sv[b] * s4[b] * rq);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mq = mx == -INFINITY ? 0.f : mx;
+    }
+    float rowsum = 0.f;
+    floatx4_t oacc[DT];
+    floatx4_t lacc = floatx4_t{};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = floatx4_t{};
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      bf16x8_t pf;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kb = 2 * e + half;
+        const floatx4_t sv = qk_block(kb);
+        const int sl = block_slot(kb);
+        const int key = (kb & 3) * 16 + 4 * g;
+        const float4 scv = *(const float4*)(kscale + sl * kChunk + key);
+        const int4 kp = *(const int4*)(kpos + sl * kChunk + key);
+        const float s4[4] = {scv.x, scv.y, scv.z, scv.w};
+        const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
+        bool mk[4];
+        masks(kb, kpv, mk);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float x = fmaf(sv[b], s4[b] * rq, -mq);
+          if (dd) x -= log2_shared(sl, key + b);
+          const float pv = __builtin_amdgcn_exp2f(mk[b] ? -INFINITY : x);
+          rowsum += pv;
+          pf[4 * half + b] = (__bf16)pv;
+        }
+      }
+      const int sl = slot_of(c - 1 + e / 2);
+      // key pair g + 4 (e % 2) of the 32-key step's chunk
+      const unsigned char* vp = lds + M::kVp + sl * Lay::kPM + (g + 4 * (e & 1)) * Lay::kPair +
+                                (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8_t*)(vp + dt * 2 * Lay::kBlk8), pf, oacc[dt], 0, 0, 0);
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc, 0, 0, 0);
+    }
+    rowsum += __shfl_xor(rowsum, 16);
+    rowsum += __shfl_xor(rowsum, 32);
+    {
+      const float l = lacc[0];
+      const bool seen = l > 0.f;
+      const float invl = seen ? 1.0f / l : 0.f;
+      OT* orow = o + (seg * o_seg_rows + posq) * D;
+      if constexpr (sizeof(OT) == 2) {
+        // fp16: tiles t, t + 1 packed, odd and even 16-lane rows swapped, so
+        // lane group g stores dims 16(t + g%2) + 8(g/2) + 0..7 (16 bytes)
+        uint32_t pk[DT][2];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+          const f16x2_t lo = {(_Float16)sat16(oacc[dt][0] * invl), (_Float16)sat16(oacc[dt][1] * invl)};
+          const f16x2_t hi = {(_Float16)sat16(oacc[dt][2] * invl), (_Float16)sat16(oacc[dt][3] * invl)};
+          pk[dt][0] = __builtin_bit_cast(uint32_t, lo);
+          pk[dt][1] = __builtin_bit_cast(uint32_t, hi);
+        }
+#pragma unroll
+        for (int j = 0; j < DT / 2; ++j) {
+          const auto r0 = __builtin_amdgcn_permlane16_swap(pk[2 * j][0], pk[2 * j + 1][0], false, false);
+          const auto r1 = __builtin_amdgcn_permlane16_swap(pk[2 * j][1], pk[2 * j + 1][1], false, false);
+          *(uint4*)(orow + 32 * j + 16 * (g & 1) + 8 * (g >> 1)) = make_uint4(r0[0], r1[0], r0[1], r1[1]);
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          *(float4*)(orow + 16 * dt + 4 * g) = make_float4(oacc[dt][0] * invl, oacc[dt][1] * invl,
+                                                           oacc[dt][2] * invl, oacc[dt][3] * invl);
+      }
+      if (g == 0) lse[seg * L + posq] = seen ? (mq + __log2f(rowsum)) * kLn2 : kSelfLogit;
+    }
+    __syncthreads();  // every wave is done with the slot of chunk c - 1
+    if (more) {
+      stage(r, slot_of(f));
+      if (f + 1 < fend && t < kChunk) pn[t] = pnext;
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kRangeChunks = 16;
+constexpr int kResidentBlocks = 256;
+
+template <int D, bool CAUSAL, int NS, bool DD, typename OT>
+void launch_one(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+                const float* knorm, const uint16_t* bkt, const int32_t* inv, OT* o, float* lse,
+                hipStream_t s) {
+  constexpr int shmem = VLds<D, NS, DD>::kBytes;
+  static bool configured = false;
+  if (!configured) {
+    (void)hipFuncSetAttribute((const void*)k_attend_var<D, CAUSAL, NS, DD, OT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+    configured = true;
+  }
+  const int nchunks = p.L / kChunk;
+  const int64_t nseg = p.nseg();
+  const int per = nchunks < kRangeChunks ? nchunks : kRangeChunks;
+  const int ranges = (nchunks + per - 1) / per;
+  int64_t heads = (kResidentBlocks + (int64_t)ranges * p.R - 1) / ((int64_t)ranges * p.R);
+  if (heads < 1) heads = 1;
+  int64_t group_segs = heads * p.R;
+  if (group_segs > nseg) group_segs = nseg;
+  hipLaunchKernelGGL((k_attend_var<D, CAUSAL, NS, DD, OT>), dim3((unsigned)(nseg * ranges)),
+                     dim3(kThreads), shmem, s, (const unsigned char*)qk,
+                     (const unsigned char*)v, perm, knorm, bkt, inv, o, lse, p.L, p.R,
+                     (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows(),
+                     p.flags & kVariantFlags);
+}
+
+template <int D, typename OT>
+void launch_d(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+              const float* knorm, const uint16_t* bkt, const int32_t* inv, OT* o, float* lse,
+              hipStream_t s) {
+  const bool ahead = (p.flags & LSH_ATTN_FLAG_LOOK_AHEAD) != 0;
+  const bool dd = (p.flags & LSH_ATTN_FLAG_DEDUP) != 0;
+  auto go = [&](auto causal, auto ns, auto ddv) {
+    launch_one<D, decltype(causal)::value, decltype(ns)::value, decltype(ddv)::value, OT>(
+        p, qk, v, perm, knorm, bkt, inv, o, lse, s);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using N2 = std::integral_constant<int, 2>;
+  using N3 = std::integral_constant<int, 3>;
+  if (p.causal) {
+    if (ahead) dd ? go(T{}, N3{}, T{}) : go(T{}, N3{}, F{});
+    else dd ? go(T{}, N2{}, T{}) : go(T{}, N2{}, F{});
+  } else {
+    if (ahead) dd ? go(F{}, N3{}, T{}) : go(F{}, N3{}, F{});
+    else dd ? go(F{}, N2{}, T{}) : go(F{}, N2{}, F{});
+  }
+}
+
+}  // namespace
+
+bool attend_variant_mfma_supported(const Problem& p) {
+  return p.dtype == LSH_ATTN_BF16 && p.m == kChunk && (p.d == 64 || p.d == 128) &&
+         (p.flags & kVariantFlags) &&
+         (!(p.flags & LSH_ATTN_FLAG_DEDUP) || p.R <= kMaxDedupRounds);
+}
+
+hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const void* v,
+                                      const int32_t* perm, const float* knorm,
+                                      const uint16_t* buckets, const int32_t* inv, void* o,
+                                      float* lse, hipStream_t s) {
+  if (round_outputs_half(p)) {
+    if (p.d == 64) launch_d<64>(p, qk, v, perm, knorm, buckets, inv, (_Float16*)o, lse, s);
+    else launch_d<128>(p, qk, v, perm, knorm, buckets, inv, (_Float16*)o, lse, s);
+  } else {
+    if (p.d == 64) launch_d<64>(p, qk, v, perm, knorm, buckets, inv, (float*)o, lse, s);
+    else launch_d<128>(p, qk, v, perm, knorm, buckets, inv, (float*)o, lse, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lsh

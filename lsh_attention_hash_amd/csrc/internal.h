@@ -105,6 +105,13 @@ hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const 
                          const void* v_sorted, const int32_t* perm, const float* knorm,
                          const uint16_t* buckets, const int32_t* inv, float* o, float* lse,
                          hipStream_t s);
+// the variant readings on matrix cores (bf16, chunk_len 64, d in {64, 128};
+// with DEDUP at most 8 rounds): fp32 per-round rows
+bool attend_variant_mfma_supported(const Problem& p);
+hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const void* v,
+                                      const int32_t* perm, const float* knorm,
+                                      const uint16_t* buckets, const int32_t* inv, void* o,
+                                      float* lse, hipStream_t s);
 // inv[seg, perm[seg, s]] = s
 hipError_t launch_inverse_perm(const Problem& p, const int32_t* perm, int32_t* inv, hipStream_t s);
 bool attend_mfma_supported(const Problem& p);
@@ -135,14 +142,16 @@ hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
                                 BwdWorkspace& b, hipStream_t s);
 
-// The variant readings (flags); the matrix-core attention takes none of them.
+// The variant readings (flags); the default matrix-core attention takes none
+// of them (attend_variants.hip does).
 constexpr int kVariantFlags = LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_SAME_BUCKET |
                               LSH_ATTN_FLAG_NORM_QUERIES | LSH_ATTN_FLAG_DEDUP;
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.
 inline bool round_outputs_half(const Problem& p) {
-  return attend_mfma_supported(p) && !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
+  return (attend_mfma_supported(p) || attend_variant_mfma_supported(p)) &&
+         !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
 }
 
 }  // namespace lsh

@@ -135,7 +135,8 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
             alloc(&w.lse, rows * 4, t) &&
             alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
             alloc(&w.stats, 2 * 8, t);
-  if (ok && lsh::attend_mfma_supported(p)) ok = alloc(&w.knorm, p.n_token_heads() * 4, t);
+  if (ok && (lsh::attend_mfma_supported(p) || lsh::attend_variant_mfma_supported(p)))
+    ok = alloc(&w.knorm, p.n_token_heads() * 4, t);
   if (ok && lsh::hash_mfma_supported(p)) {
     const int64_t hp = lsh::hash_half_pad(p);
     if (hipDeviceGetAttribute(&w.hash.n_cu, hipDeviceAttributeMultiprocessorCount, h->device) !=
