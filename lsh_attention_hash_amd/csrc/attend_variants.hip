@@ -59,10 +59,12 @@ struct VLds {
   static constexpr int kPos = kScale + NS * kChunk * 4;       // [NS][64] original positions
   static constexpr int kBound = kPos + NS * kChunk * 4;       // [NS][64] log2(e)|k|/sqrt(d)
   static constexpr int kBkt = kBound + NS * kChunk * 4;       // [NS][64] bucket in the round
-  static constexpr int kRounds = DD ? kMaxDedupRounds : 0;
-  static constexpr int kCid = kBkt + NS * kChunk * 4;         // [NS][64][8] chunk per round
-  static constexpr int kCbk = kCid + NS * kChunk * kRounds * 4;  // [NS][64][8] bucket per round
-  static constexpr int kPn = kCbk + NS * kChunk * kRounds * 4;   // [64] next positions
+  // DEDUP: per key, its chunk (mod 2^16) and bucket in each of up to 8 rounds,
+  // as 8 u16 lanes of 16 bytes
+  static constexpr int kPack = DD ? 16 : 0;
+  static constexpr int kCid = kBkt + NS * kChunk * 4;         // [NS][64] uint4
+  static constexpr int kCbk = kCid + NS * kChunk * kPack;     // [NS][64] uint4
+  static constexpr int kPn = kCbk + NS * kChunk * kPack;      // [64] next positions
   static constexpr int kBytes = kPn + kChunk * 4;
 };
 
@@ -71,8 +73,10 @@ struct VRegs {
   uint4 k[4], v[4];
   int pos, bk;
   float n2;
-  int cid[kMaxDedupRounds], cbk[kMaxDedupRounds];
+  uint32_t cid[kMaxDedupRounds / 2], cbk[kMaxDedupRounds / 2];  // u16 lanes
 };
+
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
 
@@ -116,8 +120,8 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 
   int* kpos = (int*)(lds + M::kPos);
   float* kbound = (float*)(lds + M::kBound);
   int* kbk = (int*)(lds + M::kBkt);
-  int* kcid = (int*)(lds + M::kCid);
-  int* kcbk = (int*)(lds + M::kCbk);
+  uint4* kcid = (uint4*)(lds + M::kCid);
+  uint4* kcbk = (uint4*)(lds + M::kCbk);
   int* pn = (int*)(lds + M::kPn);
   const int t = threadIdx.x;
   const float sc = kLog2e / sqrtf((float)D);
@@ -131,13 +135,21 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 
       r.n2 = knorm[row0 + r.pos];
       if (sb) r.bk = bkt[seg * L + r.pos];
       if (dd) {
+        // lanes past R hold 0x8000, which no query lane (0 there) is near
 #pragma unroll
-        for (int u = 0; u < kMaxDedupRounds; ++u)
-          if (u < R) {
-            const int64_t base = (bh * R + u) * L + r.pos;
-            r.cid[u] = inv[base] / kChunk;
-            r.cbk[u] = sb ? (int)bkt[base] : 0;
-          }
+        for (int u = 0; u < kMaxDedupRounds; u += 2) {
+          uint32_t cw = 0x80008000u, bw = 0u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (u + h < R) {
+              const int64_t base = (bh * R + u + h) * L + r.pos;
+              const uint32_t cc = (uint32_t)(inv[base] / kChunk) & 0xFFFFu;
+              cw = (cw & ~(0xFFFFu << (16 * h))) | (cc << (16 * h));
+              if (sb) bw |= (uint32_t)bkt[base] << (16 * h);
+            }
+          r.cid[u / 2] = cw;
+          r.cbk[u / 2] = bw;
+        }
       }
     }
   };
@@ -151,12 +163,8 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 
       kbound[sl * kChunk + t] = sc * nrm;
       if (sb) kbk[sl * kChunk + t] = r.bk;
       if (dd) {
-#pragma unroll
-        for (int u = 0; u < kMaxDedupRounds; ++u)
-          if (u < R) {
-            kcid[(sl * kChunk + t) * kMaxDedupRounds + u] = r.cid[u];
-            kcbk[(sl * kChunk + t) * kMaxDedupRounds + u] = r.cbk[u];
-          }
+        kcid[sl * kChunk + t] = make_uint4(r.cid[0], r.cid[1], r.cid[2], r.cid[3]);
+        kcbk[sl * kChunk + t] = make_uint4(r.cbk[0], r.cbk[1], r.cbk[2], r.cbk[3]);
       }
     }
   };
@@ -200,12 +208,16 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 
       mq = mq > 0.f ? sc : 0.f;
     }
     const int bq = sb ? kbk[cur * kChunk + q] : 0;
-    int qcid[kMaxDedupRounds], qcbk[kMaxDedupRounds];
+    // the query's chunks and buckets over the rounds (lanes past R: 0)
+    uint32_t qc[kMaxDedupRounds / 2] = {0u, 0u, 0u, 0u}, qb[kMaxDedupRounds / 2] = {0u, 0u, 0u, 0u};
     if (dd) {
+      const uint4 c4 = kcid[cur * kChunk + q], b4 = kcbk[cur * kChunk + q];
+      const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w}, bw[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-      for (int u = 0; u < kMaxDedupRounds; ++u) {
-        qcid[u] = kcid[(cur * kChunk + q) * kMaxDedupRounds + u];
-        qcbk[u] = kcbk[(cur * kChunk + q) * kMaxDedupRounds + u];
+      for (int k = 0; k < kMaxDedupRounds / 2; ++k) {
+        const uint32_t keep = 2 * k + 1 < R ? 0xFFFFFFFFu : (2 * k < R ? 0xFFFFu : 0u);
+        qc[k] = cw[k] & keep;
+        qb[k] = bw[k];
       }
     }
     bf16x8_t qf[KS];
@@ -243,19 +255,32 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 
         mk[b] = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq) | (sb && kbv[b] != bq);
     };
     // log2 N for key kk of slot sl: the rounds whose window (and bucket) give
-    // it to this query
+    // it to this query. Two rounds per 32-bit word (u16 lanes): the chunk
+    // difference d is in the window when d + 1 <= 1 (2 looking ahead), taken
+    // as a saturating subtraction that is 0 exactly then; a bucket mismatch
+    // makes the lane nonzero too; the nonzero lanes are the rounds that do
+    // not give the pair.
     auto log2_shared = [&](int sl, int kk) -> float {
-      const int* kc = kcid + (sl * kChunk + kk) * kMaxDedupRounds;
-      const int* kq = kcbk + (sl * kChunk + kk) * kMaxDedupRounds;
-      int n = 0;
+      const uint4 c4 = kcid[sl * kChunk + kk];
+      const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
+      uint4 b4 = {0u, 0u, 0u, 0u};
+      if (sb) b4 = kcbk[sl * kChunk + kk];
+      const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+      const unsigned short lim = la ? 2 : 1;
+      const u16x2_t one2 = {1, 1}, lim2 = {lim, lim};
+      uint32_t out = 0u;
+      int lanes = 0;
 #pragma unroll
-      for (int u = 0; u < kMaxDedupRounds; ++u) {
-        const int dc = kc[u] - qcid[u];
-        bool in = dc == 0 || dc == -1 || (la && dc == 1);
-        if (sb) in = in && kq[u] == qcbk[u];
-        n += (u < R && in) ? 1 : 0;
+      for (int k = 0; k < kMaxDedupRounds / 2; ++k) {
+        if (2 * k >= R) break;
+        const u16x2_t d = __builtin_bit_cast(u16x2_t, cw[k]) - __builtin_bit_cast(u16x2_t, qc[k]);
+        u16x2_t y = __builtin_elementwise_sub_sat(d + one2, lim2);
+        if (sb) y |= __builtin_bit_cast(u16x2_t, bw[k] ^ qb[k]);
+        y = __builtin_elementwise_min(y, one2);
+        out = __builtin_amdgcn_udot2(y, one2, out, false);
+        lanes += 2;
       }
-      return __log2f((float)max(n, 1));
+      return __log2f((float)max(lanes - (int)out, 1));
     };
     if (__ballot(mq > kBoundLimit) != 0ull) {
       float mx = -INFINITY;
@@ -413,9 +438,10 @@ void launch_d(const Problem& p, const void* qk, const void* v, const int32_t* pe
 }  // namespace
 
 bool attend_variant_mfma_supported(const Problem& p) {
+  // (the de-duplication compares chunks mod 2^16: at most 32768 chunks)
   return p.dtype == LSH_ATTN_BF16 && p.m == kChunk && (p.d == 64 || p.d == 128) &&
          (p.flags & kVariantFlags) &&
-         (!(p.flags & LSH_ATTN_FLAG_DEDUP) || p.R <= kMaxDedupRounds);
+         (!(p.flags & LSH_ATTN_FLAG_DEDUP) || (p.R <= kMaxDedupRounds && p.L / kChunk <= 32768));
 }
 
 hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const void* v,
