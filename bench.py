@@ -157,7 +157,7 @@ STAGE_SOURCES = {
     "hash_rescore": ["hash_mfma.hip"], "sort": ["sort.hip"], "gather": ["gather.hip"],
     "attend": ["attend_mfma.hip", "attend.hip"], "combine": ["combine.hip"],
     "recompute": ["attend_mfma.hip", "backward.hip"], "rows": ["backward.hip"],
-    "products": ["backward_mfma.hip"], "reduce": ["backward.hip"],
+    "products": ["backward_mfma.hip", "rows_lds.h"], "reduce": ["backward.hip"],
 }
 
 
@@ -306,8 +306,6 @@ def main_backward(args, w, inp, op_kw):
         except (OSError, ValueError):
             traffic = None
     rl = roofline(dominant, units, stage_avg[dominant], traffic)
-    if variants and dominant == "attend":
-        rl["kernel"] = "k_attend_var"  # the variant readings' own kernel
     per_stage = {}
     for k, t in stage_avg.items():
         per_stage[k] = {"ms": round(t, 5)}
