@@ -96,6 +96,7 @@ def _load():
             "lsh_oracle_forward": [C, P, P, P, P, P, P, P, P, P],
             "lsh_oracle_attend_rows": [C, P, P, P, P, ctypes.c_int64, P, P, P],
             "lsh_oracle_backward": [C, P, P, P, P, P, P],
+            "lsh_oracle_project": [C, ctypes.c_int64, P, P, P, P, P],
         }.items():
             f = getattr(lib, name)
             f.argtypes = argt
@@ -209,3 +210,14 @@ def backward(c: Config, qk, v, perm, dout):
     _chk(_load().lsh_oracle_backward(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do), _p(dqk),
                                      _p(dv)), "backward")
     return dqk, dv
+
+
+def project(c: Config, x, w_qk, w_v):
+    """qk, v [B, H, L, d] from x [B, L, model_dim] and the weights [H*d, model_dim]."""
+    x, wq, wv = _f64(x), _f64(w_qk), _f64(w_v)
+    model_dim = x.shape[-1]
+    qk = np.empty((c.batch, c.heads, c.seq_len, c.head_dim), np.float64)
+    v = np.empty_like(qk)
+    _chk(_load().lsh_oracle_project(ctypes.byref(c), ctypes.c_int64(model_dim), _p(x), _p(wq),
+                                    _p(wv), _p(qk), _p(v)), "project")
+    return qk, v

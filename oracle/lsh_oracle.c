@@ -634,3 +634,33 @@ int lsh_oracle_attend_rows(const lsh_oracle_config* c, const double* qk, const d
   free(inv);
   return rc;
 }
+
+/* ---------------------------------------------------------------------------
+ * Projections ([TT] shared-QK section): qk and v of every head from the layer
+ * input, one dot product per output element, summed over k in order.
+ * ------------------------------------------------------------------------- */
+int lsh_oracle_project(const lsh_oracle_config* c, int64_t model_dim, const double* x,
+                       const double* w_qk, const double* w_v, double* qk, double* v) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  if (model_dim < 1) return -13;
+  const int64_t B = c->batch, H = c->heads, L = c->seq_len, d = c->head_dim;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t i = 0; i < L; ++i) {
+        const double* xr = x + (b * L + i) * model_dim;
+        for (int64_t e = 0; e < d; ++e) {
+          const double* wq = w_qk + (h * d + e) * model_dim;
+          const double* wv = w_v + (h * d + e) * model_dim;
+          double sq = 0.0, sv = 0.0;
+          for (int64_t k = 0; k < model_dim; ++k) {
+            sq += xr[k] * wq[k];
+            sv += xr[k] * wv[k];
+          }
+          qk[((b * H + h) * L + i) * d + e] = sq;
+          v[((b * H + h) * L + i) * d + e] = sv;
+        }
+      }
+  return 0;
+}

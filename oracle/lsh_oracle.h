@@ -109,6 +109,14 @@ int lsh_oracle_forward(const lsh_oracle_config* cfg, const double* qk, const dou
 int lsh_oracle_backward(const lsh_oracle_config* cfg, const double* qk, const double* v,
                         const int32_t* perm, const double* dout, double* dqk, double* dv);
 
+/* The shared-QK and value projections of a layer input ([TT] shared-QK section:
+ * one linear map gives queries and keys, a second one the values):
+ *   qk[b, h, i, e] = sum_k x[b, i, k] w_qk[h * d + e, k],  v likewise with w_v.
+ * x [B, L, model_dim]; w_qk, w_v [H * d, model_dim] (the weight of a linear
+ * layer from model_dim to H * d features); qk, v [B, H, L, d]. */
+int lsh_oracle_project(const lsh_oracle_config* cfg, int64_t model_dim, const double* x,
+                       const double* w_qk, const double* w_v, double* qk, double* v);
+
 /* Output rows for a sample of (b, h, i), given every round's perm (and buckets,
  * as for lsh_oracle_attend): rows[k] = (b * H + h) * L + i; out_rows [n_rows, d];
  * lse_rows [n_rows, n_rounds]. */

@@ -62,6 +62,11 @@ MUTATIONS = [
      "logit[a] -= 0.0 * log((double)rounds_sharing(c, inv_bh, bk_bh, i, key[a]));"),
     ("union not de-duplicated", "if (stamp[key[a]] == mark) continue;", "if (0) continue;"),
     ("shared rounds without the look-ahead chunk", "in = in || cj == ci + 1;", "in = in;"),
+    # projections
+    ("value weights for the keys", "sq += xr[k] * wq[k];", "sq += xr[k] * wv[k];"),
+    ("head offset of the weights dropped",
+     "const double* wq = w_qk + (h * d + e) * model_dim;",
+     "const double* wq = w_qk + e * model_dim;"),
 ]
 
 
@@ -91,6 +96,8 @@ def _pin_calls():
         lambda: vpins.test_variant_equals_dense_definition(o, vpins.LA | vpins.DD, False),
         lambda: vpins.test_look_ahead_over_two_chunks_is_full_attention(o),
         lambda: vpins.test_dedup_with_identical_rounds_is_one_round(o),
+        lambda: pins.test_projection_equals_library_matmul(o),
+        lambda: pins.test_projection_with_selection_weights_copies_the_input(o),
     ]
 
 

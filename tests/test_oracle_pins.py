@@ -376,3 +376,37 @@ def test_bad_configs_are_rejected(oracle_lib):
         with pytest.raises(ValueError):
             oracle.hash(oracle.config(**base), np.zeros((1, 1, base["seq_len"], 8)),
                         np.zeros((1, 8, 2)))
+
+
+# ---------------------------------------------------------------------------
+# Projections (shared-QK section of the p2.ttnews.xyz summary): one linear map
+# for queries/keys, one for values
+# ---------------------------------------------------------------------------
+def test_projection_equals_library_matmul(oracle_lib):
+    rng = np.random.default_rng(51)
+    B, H, L, d, dm = 2, 3, 16, 8, 40
+    c = _cfg(B, H, L, d, 4, 1, 4, False)
+    x = rng.standard_normal((B, L, dm))
+    wq = rng.standard_normal((H * d, dm))
+    wv = rng.standard_normal((H * d, dm))
+    qk, v = oracle.project(c, x, wq, wv)
+    # numpy's matmul, then split the features into heads
+    want_q = (x @ wq.T).reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    want_v = (x @ wv.T).reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(qk, want_q, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(v, want_v, rtol=0, atol=1e-12)
+
+
+def test_projection_with_selection_weights_copies_the_input(oracle_lib):
+    """Weights that pick input feature h*d + e for output (h, e) give x itself,
+    split into heads, exactly; swapping the two weights swaps the outputs."""
+    rng = np.random.default_rng(52)
+    B, H, L, d = 1, 2, 8, 4
+    dm = H * d
+    c = _cfg(B, H, L, d, 4, 1, 4, False)
+    x = rng.standard_normal((B, L, dm))
+    eye = np.eye(dm)
+    qk, v = oracle.project(c, x, eye, 2.0 * eye)
+    want = x.reshape(B, L, H, d).transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(qk, want)
+    np.testing.assert_array_equal(v, 2.0 * want)
