@@ -138,6 +138,31 @@ int lsh_attn_forward(lsh_attn_t handle, const void* qk, const void* v, const flo
                      void* out, float* lse, int32_t* buckets, int32_t* perm, void* stream);
 
 /*
+ * The forward from a layer input: qk and v are first computed from x by the
+ * shared-QK and the value projections (Reformer summary at p2.ttnews.xyz,
+ * shared-QK section: one linear map gives both queries and keys, another the
+ * values), then the forward runs on them exactly as lsh_attn_forward:
+ *   qk[b, h, i, e] = sum_k x[b, i, k] w_qk[h * head_dim + e, k]   (v: w_v)
+ *   x        [B, L, model_dim]            dtype (read only)
+ *   w_qk, w_v [H * head_dim, model_dim]   dtype (read only): the weights of
+ *            linear layers from model_dim to H * head_dim features
+ *   qk, v    [B, H, L, head_dim]          dtype (written; caller-owned, for
+ *            a later backward), rounded from fp32 sums
+ *   rotations, out, lse, buckets, perm    as for lsh_attn_forward
+ * On the matrix-core path (bf16, head_dim 64 or 128, model_dim a multiple of
+ * 64, and the hash on matrix cores) the projection kernel also writes the
+ * hash's fp16 copy of qk and its norms, which the hash then does not recompute.
+ * Device pointers, all 16-byte aligned. No allocation, no host
+ * synchronisation; timing stage 7 is the projection.
+ * Errors: INVALID_ARG for a null handle or pointer, model_dim < 1 (or
+ * model_dim * H * head_dim > 2^31), a misaligned pointer or a current device
+ * other than the handle's; HIP when a launch fails.
+ */
+int lsh_attn_forward_x(lsh_attn_t handle, const void* x, int32_t model_dim, const void* w_qk,
+                       const void* w_v, const float* rotations, void* qk, void* v, void* out,
+                       float* lse, int32_t* buckets, int32_t* perm, void* stream);
+
+/*
  * Enqueue the backward of a forward on `stream`: the gradients of a loss with
  * respect to qk and v, given dout = dL/dout, at that forward's buckets (the
  * hash is an argmax and the sort a permutation, both piecewise constant, so
@@ -182,11 +207,12 @@ int lsh_attn_get_stats(lsh_attn_t handle, lsh_attn_stats_t* stats);
  * Stages: 0 hash preparation (rotation copies, fp16 copy of qk; 0 ms on the
  * exact fp64 path), 1 hash projection (the matrix-core kernel, or the exact
  * kernel), 2 exact re-scoring of unsettled rows (0 ms on the exact path),
- * 3 sort, 4 gather (0 ms unless separate), 5 chunk attention, 6 combine.
+ * 3 sort, 4 gather (0 ms unless separate), 5 chunk attention, 6 combine,
+ * 7 the qk/v projections of lsh_attn_forward_x (0 ms for lsh_attn_forward).
  * Errors: INVALID_ARG for a null handle or capacity < 0 (0 disables);
  * HIP if events cannot be created.
  */
-#define LSH_ATTN_N_STAGES 7
+#define LSH_ATTN_N_STAGES 8
 int lsh_attn_set_timing(lsh_attn_t handle, int capacity);
 
 /*

@@ -32,12 +32,13 @@ FLAG_DEDUP = 64
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP"}
 
 # Every function declared in include/lsh_attn.h.
-EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward",
+EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x",
+                    "lsh_attn_backward",
                     "lsh_attn_get_stats",
                     "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
                     "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror")
-N_STAGES = 7
-STAGES = ("hash_prep", "hash", "hash_rescore", "sort", "gather", "attend", "combine")
+N_STAGES = 8
+STAGES = ("hash_prep", "hash", "hash_rescore", "sort", "gather", "attend", "combine", "project")
 N_BWD_STAGES = 4
 BWD_STAGES = ("recompute", "rows", "products", "reduce")
 
@@ -77,6 +78,7 @@ def load_library():
     P, I = ctypes.c_void_p, ctypes.c_int
     lib.lsh_attn_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(P)]
     lib.lsh_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P]
+    lib.lsh_attn_forward_x.argtypes = [P, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_backward.argtypes = [P, P, P, P, P, P, P, P]
     lib.lsh_attn_get_stats.argtypes = [P, ctypes.POINTER(Stats)]
     lib.lsh_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
@@ -88,7 +90,8 @@ def load_library():
     lib.lsh_attn_destroy.argtypes = [P]
     lib.lsh_attn_strerror.argtypes = [I]
     lib.lsh_attn_strerror.restype = ctypes.c_char_p
-    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_backward", "lsh_attn_get_stats",
+    for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x", "lsh_attn_backward",
+              "lsh_attn_get_stats",
               "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
               "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
         getattr(lib, n).restype = I
@@ -194,6 +197,50 @@ class LSHAttention:
         if return_lse or return_buckets or return_perm:
             return out, {"lse": lse, "buckets": bk, "perm": pm}
         return out
+
+    def forward_x(self, x, w_qk, w_v, rotations, qk=None, v=None, out=None, return_lse=False,
+                  return_buckets=False, return_perm=False, stream=None):
+        """The forward from a layer input: x [B, L, model_dim] (dtype) and the
+        weights w_qk, w_v [H * d, model_dim] (dtype) give qk and v [B, H, L, d],
+        then the forward runs on them. Returns (out, qk, v), with the extras
+        dict appended when any return_* flag is set."""
+        c = self.cfg
+        if x.dim() != 3 or x.shape[0] != c.batch or x.shape[1] != c.seq_len:
+            raise ValueError(f"x: expected [B={c.batch}, L={c.seq_len}, model_dim], got {tuple(x.shape)}")
+        model_dim = x.shape[2]
+        self._check("x", x, (c.batch, c.seq_len, model_dim), self.dtype)
+        self._check("w_qk", w_qk, (c.heads * c.head_dim, model_dim), self.dtype)
+        self._check("w_v", w_v, (c.heads * c.head_dim, model_dim), self.dtype)
+        shp = (c.batch, c.heads, c.seq_len, c.head_dim)
+        if c.n_buckets > 1:
+            self._check("rotations", rotations, (c.n_rounds, c.head_dim, c.n_buckets // 2),
+                        torch.float32)
+        elif rotations is not None:
+            raise ValueError("rotations must be None when n_buckets == 1")
+        qk = torch.empty(shp, dtype=self.dtype, device=self.device) if qk is None else qk
+        v = torch.empty(shp, dtype=self.dtype, device=self.device) if v is None else v
+        self._check("qk", qk, shp, self.dtype)
+        self._check("v", v, shp, self.dtype)
+        if out is None:
+            out = torch.empty(shp, dtype=self.out_dtype, device=self.device)
+        else:
+            self._check("out", out, shp, self.out_dtype)
+        per_round = (c.batch, c.heads, c.n_rounds, c.seq_len)
+        lse = torch.empty(per_round, dtype=torch.float32, device=self.device) if return_lse else None
+        bk = torch.empty(per_round, dtype=torch.int32, device=self.device) if return_buckets else None
+        pm = torch.empty(per_round, dtype=torch.int32, device=self.device) if return_perm else None
+        s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+        ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        with torch.cuda.device(self.device):
+            rc = self.lib.lsh_attn_forward_x(self.handle, ptr(x), ctypes.c_int32(model_dim),
+                                             ptr(w_qk), ptr(w_v), ptr(rotations), ptr(qk), ptr(v),
+                                             ptr(out), ptr(lse), ptr(bk), ptr(pm),
+                                             ctypes.c_void_p(s))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_attn_forward_x", self.lib)
+        if return_lse or return_buckets or return_perm:
+            return out, qk, v, {"lse": lse, "buckets": bk, "perm": pm}
+        return out, qk, v
 
     def backward(self, qk, v, perm, dout, dqk=None, dv=None, stream=None):
         """Gradients (dqk, dv) [B, H, L, d] (dtype) given dout = dL/dout, at the

@@ -36,6 +36,7 @@
 #include <limits.h>
 
 #include "dtype.h"
+#include "hash_x16.h"
 #include "internal.h"
 
 namespace lsh {
@@ -49,13 +50,9 @@ constexpr int kThreads = 256;     // 4 waves, one per SIMD; each wave pipelines 
 constexpr int kTokWave = 64;      // 2 sets of 32 tokens per wave
 constexpr int kTokWG = kThreads / 64 * kTokWave;
 constexpr int kRotLoads = 32;     // rotation loads per thread in flight (32 x 16 B x 256 = 128 KB)
-constexpr float kF16Max = 65504.0f;
-constexpr float kF16MinNormal = 6.103515625e-05f;  // 2^-14
-
-__device__ __forceinline__ float f16_round(float x) {
-  const float c = fminf(fmaxf(x, -kF16Max), kF16Max);
-  return fabsf(c) < kF16MinNormal ? 0.f : (float)(_Float16)c;
-}
+using hx::f16_round;
+using hx::kF16Max;
+using hx::kF16MinNormal;
 
 // upper bound of a non-negative double as float
 __device__ __forceinline__ float up_f32(double x) { return (float)(x * (1.0 + 1e-6)) + 1e-30f; }
@@ -173,23 +170,17 @@ __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
   for (int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr; row < N;
        row += stride) {
     const uint4 raw = qk[row * kLpr + sub];
-    const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t out[4];
     float a = 0.f, b = 0.f, c = 0.f;
+    if (kX16) {
+      x16[row * kLpr + sub] = hx::x16_piece(raw, a, b, c);
+    } else {
+      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
-      c = fmaf(x0, x0, fmaf(x1, x1, c));
-      if (kX16) {
-        const float h0 = f16_round(x0), h1 = f16_round(x1);
-        const _Float16 e0 = (_Float16)h0, e1 = (_Float16)h1;
-        out[q] = (uint32_t)__builtin_bit_cast(uint16_t, e0) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
-        a = fmaf(h0, h0, fmaf(h1, h1, a));
-        b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
+      for (int q = 0; q < 4; ++q) {
+        const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
+        c = fmaf(x0, x0, fmaf(x1, x1, c));
       }
     }
-    if (kX16) x16[row * kLpr + sub] = make_uint4(out[0], out[1], out[2], out[3]);
 #pragma unroll
     for (int off = 1; off < kLpr; off <<= 1) {
       c += __shfl_xor(c, off);
@@ -200,9 +191,13 @@ __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
     }
     if (sub == 0) {
       if (knorm) knorm[row] = c;
-      if (kX16) xnorm[row] = make_float2(sqrtf(a) * (1.0f + 1e-5f), sqrtf(b) * (1.0f + 1e-5f));
+      if (kX16) xnorm[row] = hx::norm_bounds(a, b);
     }
   }
+}
+
+__global__ void k_clear_u32(unsigned* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
 struct QA {  // two-candidate re-score
@@ -680,7 +675,7 @@ bool hash_mfma_supported(const Problem& p) {
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
                             float* knorm, hipStream_t s, hipEvent_t after_prep,
-                            hipEvent_t after_main) {
+                            hipEvent_t after_main, bool x16_ready) {
   const int half = p.half();
   const int hp = hash_half_pad(p);
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
@@ -703,7 +698,11 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   if (grid < unit) grid = unit;
   const int64_t max_grid = (int64_t)unit * ((n_tok_tiles + 7) / 8);
   if (grid > max_grid) grid = max_grid;
-  {
+  if (x16_ready) {
+    // the projection wrote the fp16 copy and the norms; clear what the
+    // pre-pass would have cleared
+    hipLaunchKernelGGL(k_clear_u32, dim3(1), dim3(256), 0, s, hs.bounds, 4 * p.R + 2);
+  } else {
     const int64_t rpb = 256 / (p.d / 8);
     const int64_t want = (N + rpb - 1) / rpb;
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);

@@ -92,7 +92,15 @@ bool hash_mfma_supported(const Problem& p);
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
                             float* knorm, hipStream_t s, hipEvent_t after_prep,
-                            hipEvent_t after_main);
+                            hipEvent_t after_main, bool x16_ready = false);
+// x16_ready: the projection already wrote hs.x16, hs.xnorm and knorm for qk
+// the shared-QK and value projections of x (project.hip); on the matrix-core
+// path also the hash's fp16 copy of qk, its norm bounds and knorm
+// (*x16_ready = true)
+bool project_mfma_supported(const Problem& p, int model_dim);
+hipError_t launch_project(const Problem& p, int model_dim, const void* x, const void* w_qk,
+                          const void* w_v, void* qk, void* v, HashScratch& hs, float* knorm,
+                          bool* x16_ready, hipStream_t s);
 // squared norms of the qk rows alone (when the matrix-core hash does not run)
 hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipStream_t s);
 hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,

@@ -19,9 +19,12 @@ struct lsh_attn_s {
   int device = 0;
   int64_t bytes = 0;
   hipStream_t last_stream = nullptr;
-  // stage timing: events[k * (N_STAGES + 1) + j] marks the start of stage j of
-  // timed forward k (j = N_STAGES marks the end of the last stage)
+  // stage timing: events[k * kEvPerCall + j] marks the start of stage j of
+  // timed forward k for j < 7 (j = 7: the end of stage 6); j = 8, 9 bracket
+  // the projection (stage 7) of a forward from x, projected[k] says whether
+  // it ran
   std::vector<hipEvent_t> events;
+  std::vector<char> projected;
   int timing_capacity = 0;
   int timed = 0;
   // the same for backwards: bevents[k * (N_BWD_STAGES + 1) + j]
@@ -30,6 +33,8 @@ struct lsh_attn_s {
 };
 
 namespace {
+
+constexpr int kEvPerCall = LSH_ATTN_N_STAGES + 2;
 
 __global__ void k_zero_u64(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
@@ -176,22 +181,14 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   return LSH_ATTN_OK;
 }
 
-int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* rotations,
-                     void* out, float* lse, int32_t* buckets, int32_t* perm, void* stream) {
-  if (!h || !qk || !v || !out) return LSH_ATTN_ERR_INVALID_ARG;
+namespace {
+
+// The forward after the inputs are checked; ev: the timed call's events or
+// null; x16_ready: the projection already prepared the hash's fp16 copy.
+int forward_body(lsh_attn_s* h, const void* qk, const void* v, const float* rotations, void* out,
+                 float* lse, int32_t* buckets, int32_t* perm, hipStream_t s, hipEvent_t* ev,
+                 bool x16_ready) {
   const lsh::Problem& p = h->p;
-  if (p.nb > 1 && !rotations) return LSH_ATTN_ERR_INVALID_ARG;
-  if (!aligned16(qk) || !aligned16(v) || !aligned16(out)) return LSH_ATTN_ERR_INVALID_ARG;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
-    (void)hipGetLastError();
-    return LSH_ATTN_ERR_INVALID_ARG;
-  }
-  hipStream_t s = (hipStream_t)stream;
-  h->last_stream = s;
-  const bool timing = h->timed < h->timing_capacity;
-  hipEvent_t* ev = timing ? &h->events[(size_t)h->timed * (LSH_ATTN_N_STAGES + 1)] : nullptr;
-  if (timing) ++h->timed;
   auto mark = [&](int j) {
     if (ev) hipEventRecord(ev[j], s);
   };
@@ -206,7 +203,7 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   if (e == hipSuccess) {
     if (mfma_hash) {
       e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, w.knorm, s,
-                                ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
+                                ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, x16_ready);
     } else {
       if (w.knorm) e = lsh::launch_key_norms(p, qk, w.knorm, s);
       mark(1);
@@ -233,6 +230,61 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
 }
 
+// the next timed call's events (null when not timing)
+hipEvent_t* next_events(lsh_attn_s* h, bool projected) {
+  if (h->timed >= h->timing_capacity) return nullptr;
+  hipEvent_t* ev = &h->events[(size_t)h->timed * kEvPerCall];
+  h->projected[h->timed] = projected ? 1 : 0;
+  ++h->timed;
+  return ev;
+}
+
+bool on_device(const lsh_attn_s* h) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* rotations,
+                     void* out, float* lse, int32_t* buckets, int32_t* perm, void* stream) {
+  if (!h || !qk || !v || !out) return LSH_ATTN_ERR_INVALID_ARG;
+  if (h->p.nb > 1 && !rotations) return LSH_ATTN_ERR_INVALID_ARG;
+  if (!aligned16(qk) || !aligned16(v) || !aligned16(out)) return LSH_ATTN_ERR_INVALID_ARG;
+  if (!on_device(h)) return LSH_ATTN_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  return forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, next_events(h, false),
+                      false);
+}
+
+int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const void* w_qk,
+                       const void* w_v, const float* rotations, void* qk, void* v, void* out,
+                       float* lse, int32_t* buckets, int32_t* perm, void* stream) {
+  if (!h || !x || !w_qk || !w_v || !qk || !v || !out) return LSH_ATTN_ERR_INVALID_ARG;
+  if (model_dim < 1 || (int64_t)model_dim * h->p.d * h->p.H > ((int64_t)1 << 31))
+    return LSH_ATTN_ERR_INVALID_ARG;
+  if (h->p.nb > 1 && !rotations) return LSH_ATTN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_qk) || !aligned16(w_v) || !aligned16(qk) || !aligned16(v) ||
+      !aligned16(out))
+    return LSH_ATTN_ERR_INVALID_ARG;
+  if (!on_device(h)) return LSH_ATTN_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  h->last_stream = s;
+  hipEvent_t* ev = next_events(h, true);
+  if (ev) hipEventRecord(ev[8], s);
+  bool x16_ready = false;
+  const hipError_t e = lsh::launch_project(h->p, model_dim, x, w_qk, w_v, qk, v, h->ws.hash,
+                                           h->ws.knorm, &x16_ready, s);
+  if (ev) hipEventRecord(ev[9], s);
+  if (e != hipSuccess) return LSH_ATTN_ERR_HIP;
+  return forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, ev, x16_ready);
+}
+
 int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
                       const void* dout, void* dqk, void* dv, void* stream) {
   if (!h || !qk || !v || !perm || !dout || !dqk || !dv) return LSH_ATTN_ERR_INVALID_ARG;
@@ -240,11 +292,7 @@ int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t
   if (!(p.flags & LSH_ATTN_FLAG_BACKWARD)) return LSH_ATTN_ERR_UNSUPPORTED;
   if (!aligned16(qk) || !aligned16(v) || !aligned16(dout) || !aligned16(dqk) || !aligned16(dv))
     return LSH_ATTN_ERR_INVALID_ARG;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) {
-    (void)hipGetLastError();
-    return LSH_ATTN_ERR_INVALID_ARG;
-  }
+  if (!on_device(h)) return LSH_ATTN_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
   const bool timing = h->btimed < h->timing_capacity;
@@ -274,6 +322,7 @@ static void destroy_events(lsh_attn_s* h) {
   for (hipEvent_t e : h->bevents) hipEventDestroy(e);
   h->events.clear();
   h->bevents.clear();
+  h->projected.clear();
   h->timing_capacity = 0;
   h->timed = 0;
   h->btimed = 0;
@@ -322,7 +371,8 @@ int lsh_attn_set_timing(lsh_attn_t h, int capacity) {
     return LSH_ATTN_ERR_HIP;
   }
   destroy_events(h);
-  if (!create_events(h->events, (size_t)capacity * (LSH_ATTN_N_STAGES + 1)) ||
+  h->projected.assign((size_t)capacity, 0);
+  if (!create_events(h->events, (size_t)capacity * kEvPerCall) ||
       ((h->p.flags & LSH_ATTN_FLAG_BACKWARD) &&
        !create_events(h->bevents, (size_t)capacity * (LSH_ATTN_N_BWD_STAGES + 1)))) {
     destroy_events(h);
@@ -334,8 +384,25 @@ int lsh_attn_set_timing(lsh_attn_t h, int capacity) {
 
 int lsh_attn_get_timing(lsh_attn_t h, double* ms, int64_t* n_forwards) {
   if (!h || !ms || !n_forwards || h->timing_capacity == 0) return LSH_ATTN_ERR_INVALID_ARG;
-  const int rc = sum_stage_times(h->events, h->timed, LSH_ATTN_N_STAGES, ms);
-  if (rc != LSH_ATTN_OK) return rc;
+  for (int j = 0; j < LSH_ATTN_N_STAGES; ++j) ms[j] = 0.0;
+  for (int k = 0; k < h->timed; ++k) {
+    const hipEvent_t* ev = &h->events[(size_t)k * kEvPerCall];
+    if (hipEventSynchronize(ev[7]) != hipSuccess) {
+      (void)hipGetLastError();
+      return LSH_ATTN_ERR_HIP;
+    }
+    for (int j = 0; j < 8; ++j) {
+      if (j == 7 && !h->projected[k]) break;
+      float t = 0.f;
+      const hipError_t e = j < 7 ? hipEventElapsedTime(&t, ev[j], ev[j + 1])
+                                 : hipEventElapsedTime(&t, ev[8], ev[9]);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return LSH_ATTN_ERR_HIP;
+      }
+      ms[j] += t;
+    }
+  }
   *n_forwards = h->timed;
   h->timed = 0;
   return LSH_ATTN_OK;

@@ -1,0 +1,242 @@
+// project.hip -- the shared-QK and value projections of a layer input, feeding
+// the hash.
+//
+// Reformer summary (p2.ttnews.xyz), shared-QK section: one linear map gives
+// the queries and the keys, a second one the values:
+//   qk[b, h, i, e] = sum_k x[b, i, k] w_qk[h d + e, k],   v likewise with w_v,
+// x [B, L, model_dim] and the weights [H d, model_dim] (a linear layer's
+// weight, model_dim -> H d features), qk and v written as [B, H, L, d] in the
+// input dtype.
+//
+// Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 64): one
+// workgroup of 4 waves computes a 128-row x d-column tile of one head's qk or
+// v (the grid walks the 2H heads of a row tile next to each other, so the x
+// tile is read from HBM once and from L2 by the others) with
+// v_mfma_f32_16x16x32_bf16: wave w owns rows 32w .. 32w + 31 and every column,
+// so a row's sums stay inside one wave. K goes in slabs of 64, double-buffered
+// in LDS (rows of x and of the weight, K contiguous, +16-byte pad); the next
+// slab is loaded into registers while the current one is multiplied. The
+// epilogue rounds the tile to bf16 and passes it through LDS so that each lane
+// writes 16 contiguous bytes of a row. For qk tiles the same pass produces
+// what the hash's pre-pass would compute from these rows (the fp16 copy of
+// qk, the norm bounds of the copy and of its rounding error, and the squared
+// norm), with the same per-row arithmetic, so the hash can skip that pass.
+#include "dtype.h"
+#include "hash_x16.h"
+#include "internal.h"
+
+namespace lsh {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kRows = 128;          // rows of x per tile
+constexpr int kSlab = 64;           // K per LDS slab
+constexpr int kStride = kSlab * 2 + 16;  // bytes per staged row (+16 pad)
+
+template <int D>
+struct PLds {
+  static constexpr int kA = 0;                         // [2][kRows] x rows
+  static constexpr int kB = kA + 2 * kRows * kStride;  // [2][D] weight rows
+  static constexpr int kBytes = kB + 2 * D * kStride;
+  static constexpr int kOutStride = D * 2 + 16;        // epilogue tile row (bf16, +pad)
+  static_assert(kRows * kOutStride <= kBytes, "epilogue tile fits");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
+    const uint4* __restrict__ x, const uint4* __restrict__ w_qk, const uint4* __restrict__ w_v,
+    uint4* __restrict__ qk, uint4* __restrict__ v, uint4* __restrict__ x16,
+    float2* __restrict__ xnorm, float* __restrict__ knorm, int64_t M, int L, int H,
+    int model_dim) {
+  using Lay = PLds<D>;
+  constexpr int DT = D / 16;                 // 16-column tiles
+  constexpr int kAPer = kRows * 8 / kThreads;  // 16-byte pieces of the x slab per thread
+  constexpr int kBPer = D * 8 / kThreads;      // of the weight slab
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int nt = blockIdx.x % (unsigned)(2 * H);
+  const int64_t row0 = (int64_t)(blockIdx.x / (unsigned)(2 * H)) * kRows;
+  const bool is_v = nt >= H;
+  const int h = is_v ? nt - H : nt;
+  const uint4* wrows = (is_v ? w_v : w_qk) + (int64_t)h * D * (model_dim / 8);
+  const int t = threadIdx.x;
+  const int kseg = model_dim / 8;  // 16-byte pieces per row of x or of the weight
+  const int nslab = model_dim / kSlab;
+
+  uint4 ra[kAPer], rb[kBPer];
+  auto load = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+      const int r = t / 8 + (kThreads / 8) * j, pc = t % 8;
+      const int64_t row = row0 + r;
+      ra[j] = row < M ? x[row * kseg + s * 8 + pc] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+      const int c = t / 8 + (kThreads / 8) * j, pc = t % 8;
+      rb[j] = wrows[(int64_t)c * kseg + s * 8 + pc];
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+      const int r = t / 8 + (kThreads / 8) * j, pc = t % 8;
+      *(uint4*)(lds + Lay::kA + (buf * kRows + r) * kStride + pc * 16) = ra[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) {
+      const int c = t / 8 + (kThreads / 8) * j, pc = t % 8;
+      *(uint4*)(lds + Lay::kB + (buf * D + c) * kStride + pc * 16) = rb[j];
+    }
+  };
+
+  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
+  floatx4_t acc[2][DT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ct = 0; ct < DT; ++ct) acc[i][ct] = floatx4_t{};
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int s = 0; s < nslab; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nslab) load(s + 1);
+#pragma unroll
+    for (int ks = 0; ks < kSlab / 32; ++ks) {
+      bf16x8_t a[2], b[DT];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *(const bf16x8_t*)(lds + Lay::kA + (buf * kRows + 32 * w + 16 * i + lq) * kStride +
+                                  (32 * ks + 8 * g) * 2);
+#pragma unroll
+      for (int ct = 0; ct < DT; ++ct)
+        b[ct] = *(const bf16x8_t*)(lds + Lay::kB + (buf * D + 16 * ct + lq) * kStride +
+                                   (32 * ks + 8 * g) * 2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ct = 0; ct < DT; ++ct)
+          acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[ct], acc[i][ct], 0, 0, 0);
+    }
+    if (s + 1 < nslab) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 32w + 16i + 4g + 0..3 of column 16ct + lq; the
+  // tile goes to LDS as bf16 rows, then out with 16 bytes per lane
+  unsigned char* ot = lds;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ct = 0; ct < DT; ++ct)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *(uint16_t*)(ot + (32 * w + 16 * i + 4 * g + u) * Lay::kOutStride + (16 * ct + lq) * 2) =
+            f32_to_bf16(acc[i][ct][u]).bits;
+  __syncthreads();
+  constexpr int kLpr = D / 8;                  // lanes per row (16 bytes each)
+  constexpr int kRowsPerPass = kThreads / kLpr;
+  const int sub = t % kLpr;
+#pragma unroll
+  for (int r0 = 0; r0 < kRows; r0 += kRowsPerPass) {
+    const int r = r0 + t / kLpr;
+    const int64_t row = row0 + r;  // a row of x: (b, i)
+    const bool live = row < M;
+    const int64_t b = row / L, i = row - b * L;
+    const int64_t th = (b * H + h) * L + i;  // its token-head row
+    const uint4 raw = *(const uint4*)(ot + r * Lay::kOutStride + sub * 16);
+    if (live) (is_v ? v : qk)[th * kLpr + sub] = raw;
+    if (!is_v) {  // the hash pre-pass of this row (all lanes of a row are live together)
+      float a = 0.f, bb = 0.f, c = 0.f;
+      const uint4 h16 = hx::x16_piece(raw, a, bb, c);
+      if (live) x16[th * kLpr + sub] = h16;
+#pragma unroll
+      for (int off = 1; off < kLpr; off <<= 1) {
+        c += __shfl_xor(c, off);
+        a += __shfl_xor(a, off);
+        bb += __shfl_xor(bb, off);
+      }
+      if (live && sub == 0) {
+        knorm[th] = c;
+        xnorm[th] = hx::norm_bounds(a, bb);
+      }
+    }
+  }
+}
+
+// fp32 or other shapes: one thread per output element, fp32 sums in k order
+template <typename T>
+__global__ __launch_bounds__(256) void k_proj_simple(const T* __restrict__ x,
+                                                     const T* __restrict__ w_qk,
+                                                     const T* __restrict__ w_v,
+                                                     T* __restrict__ qk, T* __restrict__ v,
+                                                     int64_t n, int L, int H, int D,
+                                                     int model_dim) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= 2 * n) return;
+  const bool is_v = idx >= n;
+  const int64_t o = is_v ? idx - n : idx;  // [B, H, L, D] element
+  const int e = (int)(o % D);
+  const int64_t th = o / D;
+  const int64_t i = th % L, bh = th / L;
+  const int hh = (int)(bh % H);
+  const int64_t b = bh / H;
+  const T* xr = x + (b * L + i) * model_dim;
+  const T* wr = (is_v ? w_v : w_qk) + ((int64_t)hh * D + e) * model_dim;
+  float s = 0.f;
+  for (int k = 0; k < model_dim; ++k) s = fmaf(to_f32(xr[k]), to_f32(wr[k]), s);
+  (is_v ? v : qk)[o] = from_f32<T>(s);
+}
+
+}  // namespace
+
+bool project_mfma_supported(const Problem& p, int model_dim) {
+  return p.dtype == LSH_ATTN_BF16 && (p.d == 64 || p.d == 128) && model_dim % kSlab == 0 &&
+         hash_mfma_supported(p);
+}
+
+hipError_t launch_project(const Problem& p, int model_dim, const void* x, const void* w_qk,
+                          const void* w_v, void* qk, void* v, HashScratch& hs, float* knorm,
+                          bool* x16_ready, hipStream_t s) {
+  const int64_t M = (int64_t)p.B * p.L;
+  *x16_ready = false;
+  if (project_mfma_supported(p, model_dim) && knorm) {
+    const unsigned grid = (unsigned)(((M + kRows - 1) / kRows) * 2 * p.H);
+    if (p.d == 128) {
+      constexpr int shmem = PLds<128>::kBytes;
+      (void)hipFuncSetAttribute((const void*)k_proj_mfma<128>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+      hipLaunchKernelGGL(k_proj_mfma<128>, dim3(grid), dim3(kThreads), shmem, s,
+                         (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
+                         (uint4*)v, (uint4*)hs.x16, (float2*)hs.xnorm, knorm, M, p.L, p.H,
+                         model_dim);
+    } else {
+      constexpr int shmem = PLds<64>::kBytes;
+      (void)hipFuncSetAttribute((const void*)k_proj_mfma<64>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+      hipLaunchKernelGGL(k_proj_mfma<64>, dim3(grid), dim3(kThreads), shmem, s,
+                         (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
+                         (uint4*)v, (uint4*)hs.x16, (float2*)hs.xnorm, knorm, M, p.L, p.H,
+                         model_dim);
+    }
+    *x16_ready = true;
+    return hipGetLastError();
+  }
+  const int64_t n = p.n_token_heads() * p.d;
+  const dim3 grid((unsigned)((2 * n + 255) / 256));
+  if (p.dtype == LSH_ATTN_BF16)
+    hipLaunchKernelGGL(k_proj_simple<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x,
+                       (const bf16_t*)w_qk, (const bf16_t*)w_v, (bf16_t*)qk, (bf16_t*)v, n, p.L,
+                       p.H, p.d, model_dim);
+  else
+    hipLaunchKernelGGL(k_proj_simple<float>, grid, dim3(256), 0, s, (const float*)x,
+                       (const float*)w_qk, (const float*)w_v, (float*)qk, (float*)v, n, p.L,
+                       p.H, p.d, model_dim);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

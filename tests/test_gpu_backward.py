@@ -4,10 +4,11 @@ from its own seed and rounded to the input dtype, and the oracle takes the
 exact values the GPU sees. Each case prints what it is before it runs.
 
 Tolerance: the gradients come back in the input dtype. For bf16 that
-rounding alone is up to 2^-9 of each value; the rest (fp32 sums, the
-recomputed attention's bf16 products) is bounded by a small fraction of the
-largest gradient. So |g - g_ref| <= 2^-8 |g_ref| + 1e-2 max|g_ref| per element
-for bf16, and 1e-4 max|g_ref| for fp32.
+rounding alone is up to 2^-8 of each value (the unit roundoff of an 8-bit
+significand); the rest (fp32 sums, the recomputed attention's bf16 products)
+is bounded by a small fraction of the largest gradient. So
+|g - g_ref| <= 2^-8 |g_ref| + 1e-2 max|g_ref| per element for bf16, and
+1e-4 max|g_ref| for fp32.
 """
 import sys
 

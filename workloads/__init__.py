@@ -18,6 +18,10 @@ Recipe (all streams are numpy ``Generator(PCG64(seed))``):
   * v   ~ N(0, 1) float32, seed ``seed_base + 2000``.
   * rotations R ~ N(0, 1) float32 of shape [n_rounds, head_dim, n_buckets/2],
     seed ``seed_base + 3000``.
+  * layer inputs (the projections' case): x ~ N(0, 1) [B, L, model_dim], seed
+    ``seed_base + 5000``; the weights w_qk, w_v ~ N(0, 1/model_dim)
+    [H * head_dim, model_dim], seeds ``seed_base + 6000`` and ``+ 7000`` (so
+    qk and v come out with unit variance, as the direct inputs above).
   * bf16 storage: float32 rounded to bfloat16 with round-to-nearest-even.
 The oracle receives exactly the stored values, widened to float64.
 """
@@ -30,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "make_inputs", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "Inputs",
+    "bf16_bits_to_f32", "Inputs", "LayerInputs", "make_layer_inputs",
 ]
 
 
@@ -139,3 +143,39 @@ def make_inputs(w: Workload, sigma: float = 0.1, n_centres: int = 8) -> Inputs:
     v_s, v_bits = _store(v, w.dtype)
     del v
     return Inputs(w, qk_s, v_s, rot, qk_bits, v_bits)
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """A layer input and the two projection weights, stored as for Inputs."""
+    workload: Workload
+    model_dim: int
+    x: np.ndarray
+    w_qk: np.ndarray
+    w_v: np.ndarray
+    rotations: Optional[np.ndarray]
+    x_bits: Optional[np.ndarray] = None
+    w_qk_bits: Optional[np.ndarray] = None
+    w_v_bits: Optional[np.ndarray] = None
+
+
+def make_layer_inputs(w: Workload, model_dim: int) -> LayerInputs:
+    """Draw x [B, L, model_dim] and the weights [H * d, model_dim] of workload ``w``
+    (the rotations are those of make_inputs)."""
+    k = w.seed_base
+    B, L, F = w.batch, w.seq_len, w.heads * w.head_dim
+    x = np.random.Generator(np.random.PCG64(5000 + k)).standard_normal(
+        (B, L, model_dim), dtype=np.float32)
+    scale = np.float32(1.0 / np.sqrt(model_dim))
+    wq = np.random.Generator(np.random.PCG64(6000 + k)).standard_normal(
+        (F, model_dim), dtype=np.float32) * scale
+    wv = np.random.Generator(np.random.PCG64(7000 + k)).standard_normal(
+        (F, model_dim), dtype=np.float32) * scale
+    rot = None
+    if w.n_buckets >= 2:
+        rot = np.random.Generator(np.random.PCG64(3000 + k)).standard_normal(
+            (w.n_rounds, w.head_dim, w.n_buckets // 2), dtype=np.float32)
+    x_s, x_bits = _store(x, w.dtype)
+    wq_s, wq_bits = _store(wq, w.dtype)
+    wv_s, wv_bits = _store(wv, w.dtype)
+    return LayerInputs(w, model_dim, x_s, wq_s, wv_s, rot, x_bits, wq_bits, wv_bits)
