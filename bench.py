@@ -44,7 +44,8 @@ def esize(dt: str) -> int:
     return 2 if dt == "bf16" else 4
 
 
-def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, window_chunks=2):
+def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, window_chunks=2,
+                      model_dim=None):
     """Per-launch algorithmic work of each stage (what the method must compute
     or move, not what an implementation happens to move).
     N = B*H*L token-heads, R rounds, d head dim, nb buckets, m chunk length;
@@ -77,6 +78,13 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, windo
                    "bytes": N * R * (2 * d * e + 4 + d * ro + 4)},
         # R per-round rows and lse read, one output row written
         "combine": {"bytes": N * R * (d * ro + 4) + N * d * eo},
+        # forward from x: x [B*L, K] times the two weights [H*d, K]; x and the
+        # weights read once, qk and v written, and the hash's fp16 copy of qk
+        # with its norms (K = model_dim)
+        "project": {"flops": 2 * w.batch * w.seq_len * (model_dim or 0) * 2 * w.heads * d,
+                    "bytes": w.batch * w.seq_len * (model_dim or 0) * e
+                    + 2 * w.heads * d * (model_dim or 0) * e + 2 * N * d * e + N * d * 2
+                    + N * 12},
     }
 
 
@@ -109,7 +117,7 @@ def backward_units(w, out_dtype: str):
 
 # The matrix-core peak each stage's contraction runs at (fp16 projection,
 # bf16 attention); HBM for the rest; fp64 vector for the exact re-scoring.
-MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs",
+MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs", "project": "mfma_bf16_TFLOPs",
              "recompute": "mfma_bf16_TFLOPs", "products": "mfma_bf16_TFLOPs"}
 
 
@@ -149,13 +157,15 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
 
 # Stages that are exactly one kernel launch (name as rocprofv3 reports it),
 # and the source files each stage's kernels are built from.
-STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine"}
+STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine",
+                "project": "k_proj_mfma"}
 BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "products": "k_bwd_fused_mfma",
                     "reduce": "k_bwd_reduce_sum"}
 STAGE_SOURCES = {
-    "hash_prep": ["hash_mfma.hip"], "hash": ["hash_mfma.hip", "hash.hip"],
+    "hash_prep": ["hash_mfma.hip", "hash_x16.h"], "hash": ["hash_mfma.hip", "hash.hip", "hash_x16.h"],
     "hash_rescore": ["hash_mfma.hip"], "sort": ["sort.hip"], "gather": ["gather.hip"],
     "attend": ["attend_mfma.hip", "attend.hip"], "combine": ["combine.hip"],
+    "project": ["project.hip", "hash_x16.h"],
     "recompute": ["attend_mfma.hip", "backward.hip"], "rows": ["backward.hip"],
     "products": ["backward_mfma.hip", "rows_lds.h"], "reduce": ["backward.hip"],
 }
@@ -355,6 +365,9 @@ def main():
     ap.add_argument("--fp32-round-outputs", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward instead of the forward (its own JSON line)")
+    ap.add_argument("--from-x", action="store_true",
+                    help="time the forward from a layer input x [B, L, H*d] with the shared-QK "
+                         "and value projections (lsh_attn_forward_x); model_dim = H * d")
     ap.add_argument("--variants", default="",
                     help="comma list of variant readings for the forward: look_ahead, "
                          "same_bucket, norm_queries, dedup (default: none)")
@@ -416,9 +429,21 @@ def main():
     out = torch.empty((w.batch, w.heads, w.seq_len, w.head_dim), dtype=tdt[out_dtype],
                       device=dev)
     stream = torch.cuda.current_stream()
+    model_dim = w.heads * w.head_dim
+    if args.from_x:
+        li = workloads.make_layer_inputs(w, model_dim)
+        if w.dtype == "bf16":
+            tens = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            x, wq, wv = tens(li.x_bits), tens(li.w_qk_bits), tens(li.w_v_bits)
+        else:
+            x, wq, wv = (torch.from_numpy(a).to(dev) for a in (li.x, li.w_qk, li.w_v))
+        rot = None if li.rotations is None else torch.from_numpy(li.rotations).to(dev)
+        step = lambda: op.forward_x(x, wq, wv, rot, qk=qk, v=v, out=out)
+    else:
+        step = lambda: op(qk, v, rot, out=out)
 
     for _ in range(args.warmup):
-        op(qk, v, rot, out=out)
+        step()
     torch.cuda.synchronize()
 
     op.set_timing(args.steps)
@@ -428,7 +453,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        op(qk, v, rot, out=out)
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -441,7 +466,9 @@ def main():
 
     fp16_rounds = w.dtype == "bf16" and w.chunk_len == 64 and not args.fp32_round_outputs
     units = algorithmic_units(w, out_dtype, 2 if fp16_rounds else 4, stats,
-                              3 if "look_ahead" in variants else 2)
+                              3 if "look_ahead" in variants else 2, model_dim)
+    if not args.from_x:
+        stage_avg.pop("project")  # no projection in the forward from qk and v
     if not args.separate_gather:
         stage_avg.pop("gather")   # rows are read through the permutation inside attend
     # the dominant kernel: the slowest stage that is one kernel launch
@@ -489,6 +516,8 @@ def main():
                              f" R {3000 + w.seed_base})",
                    "separate_gather": bool(args.separate_gather),
                    "variants": variants,
+                   "from_x": bool(args.from_x),
+                   "model_dim": model_dim if args.from_x else None,
                    "round_outputs": "fp16" if fp16_rounds else "fp32"},
         "roofline": rl,
         "stages": per_stage,

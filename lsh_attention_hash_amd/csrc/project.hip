@@ -10,14 +10,14 @@
 //
 // Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 64): one
 // workgroup of 4 waves computes a 128-row x d-column tile of one head's qk or
-// v (the grid walks the 2H heads of a row tile next to each other, so the x
-// tile is read from HBM once and from L2 by the others) with
+// v (the 2H tiles of a row tile run on one XCD, one after the other, so the x
+// tile is read from HBM once and from that XCD's L2 by the others) with
 // v_mfma_f32_16x16x32_bf16: wave w owns rows 32w .. 32w + 31 and every column,
 // so a row's sums stay inside one wave. K goes in slabs of 64, double-buffered
-// in LDS (rows of x and of the weight, K contiguous, +16-byte pad); the next
-// slab is loaded into registers while the current one is multiplied. The
-// epilogue rounds the tile to bf16 and passes it through LDS so that each lane
-// writes 16 contiguous bytes of a row. For qk tiles the same pass produces
+// in LDS (rows of x and of the weight, K contiguous, +16-byte pad), with the
+// next two slabs in flight in registers while the current one is multiplied.
+// The epilogue rounds the tile to bf16 and passes it through LDS so that each
+// lane writes 16 contiguous bytes of a row. For qk tiles the same pass produces
 // what the hash's pre-pass would compute from these rows (the fp16 copy of
 // qk, the norm bounds of the copy and of its rounding error, and the squared
 // norm), with the same per-row arithmetic, so the hash can skip that pass.
@@ -56,8 +56,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
   constexpr int kAPer = kRows * 8 / kThreads;  // 16-byte pieces of the x slab per thread
   constexpr int kBPer = D * 8 / kThreads;      // of the weight slab
   extern __shared__ __align__(16) unsigned char lds[];
-  const int nt = blockIdx.x % (unsigned)(2 * H);
-  const int64_t row0 = (int64_t)(blockIdx.x / (unsigned)(2 * H)) * kRows;
+  // Workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8): the
+  // 2H tiles of a row tile get ids of one residue, consecutive within their
+  // XCD, so the row tile of x is fetched into that XCD's L2 once.
+  const unsigned nts = 2 * H;
+  const unsigned xcd = blockIdx.x % 8u, k = blockIdx.x / 8u;
+  const int nt = (int)(k % nts);
+  const int64_t mt = (int64_t)(k / nts) * 8 + xcd;
+  const int64_t row0 = mt * kRows;
+  if (row0 >= M) return;
   const bool is_v = nt >= H;
   const int h = is_v ? nt - H : nt;
   const uint4* wrows = (is_v ? w_v : w_qk) + (int64_t)h * D * (model_dim / 8);
@@ -65,30 +72,38 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
   const int kseg = model_dim / 8;  // 16-byte pieces per row of x or of the weight
   const int nslab = model_dim / kSlab;
 
-  uint4 ra[kAPer], rb[kBPer];
-  auto load = [&](int s) {
+  // two slabs in flight in registers (slab j in set j % 2); rows past M
+  // read row M - 1 (their results are not stored), so no load is conditional
+  uint4 ra0[kAPer], rb0[kBPer], ra1[kAPer], rb1[kBPer];
+  int64_t arow[kAPer];
 #pragma unroll
-    for (int j = 0; j < kAPer; ++j) {
-      const int r = t / 8 + (kThreads / 8) * j, pc = t % 8;
-      const int64_t row = row0 + r;
-      ra[j] = row < M ? x[row * kseg + s * 8 + pc] : uint4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < kAPer; ++j) {
+    const int64_t row = row0 + t / 8 + (kThreads / 8) * j;
+    arow[j] = (row < M ? row : M - 1) * kseg + t % 8;
+  }
+  const uint4* wbase = wrows + (int64_t)(t / 8) * kseg + t % 8;
+  auto load = [&](uint4 (&ra)[kAPer], uint4 (&rb)[kBPer], int s) {
 #pragma unroll
-    for (int j = 0; j < kBPer; ++j) {
-      const int c = t / 8 + (kThreads / 8) * j, pc = t % 8;
-      rb[j] = wrows[(int64_t)c * kseg + s * 8 + pc];
-    }
+    for (int j = 0; j < kAPer; ++j) ra[j] = x[arow[j] + s * 8];
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) rb[j] = wbase[(int64_t)(kThreads / 8) * j * kseg + s * 8];
   };
-  auto store = [&](int buf) {
+  // (each piece passes through a register-only asm statement, so the copy
+  // cannot become a memcpy from a stack copy of the registers)
+  auto store = [&](const uint4 (&ra)[kAPer], const uint4 (&rb)[kBPer], int buf) {
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
       const int r = t / 8 + (kThreads / 8) * j, pc = t % 8;
-      *(uint4*)(lds + Lay::kA + (buf * kRows + r) * kStride + pc * 16) = ra[j];
+      uint4 q = ra[j];
+      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+      *(uint4*)(lds + Lay::kA + (buf * kRows + r) * kStride + pc * 16) = q;
     }
 #pragma unroll
     for (int j = 0; j < kBPer; ++j) {
       const int c = t / 8 + (kThreads / 8) * j, pc = t % 8;
-      *(uint4*)(lds + Lay::kB + (buf * D + c) * kStride + pc * 16) = rb[j];
+      uint4 q = rb[j];
+      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+      *(uint4*)(lds + Lay::kB + (buf * D + c) * kStride + pc * 16) = q;
     }
   };
 
@@ -99,12 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
 #pragma unroll
     for (int ct = 0; ct < DT; ++ct) acc[i][ct] = floatx4_t{};
 
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int s = 0; s < nslab; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nslab) load(s + 1);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kSlab / 32; ++ks) {
       bf16x8_t a[2], b[DT];
@@ -122,8 +132,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
         for (int ct = 0; ct < DT; ++ct)
           acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[ct], acc[i][ct], 0, 0, 0);
     }
-    if (s + 1 < nslab) store(buf ^ 1);
+  };
+
+  load(ra0, rb0, 0);
+  store(ra0, rb0, 0);
+  if (1 < nslab) load(ra1, rb1, 1);
+  if (2 < nslab) load(ra0, rb0, 2);
+  __syncthreads();
+  // step s: multiply slab s (LDS buffer s % 2), stage slab s + 1 from its
+  // registers, then reuse them for slab s + 3
+  for (int s = 0; s < nslab; s += 2) {
+    compute(0);
+    if (s + 1 < nslab) store(ra1, rb1, 1);
     __syncthreads();
+    if (s + 3 < nslab) load(ra1, rb1, s + 3);
+    if (s + 1 < nslab) {
+      compute(1);
+      if (s + 2 < nslab) store(ra0, rb0, 0);
+      __syncthreads();
+      if (s + 4 < nslab) load(ra0, rb0, s + 4);
+    }
   }
 
   // epilogue: lane holds rows 32w + 16i + 4g + 0..3 of column 16ct + lq; the
@@ -205,7 +233,10 @@ hipError_t launch_project(const Problem& p, int model_dim, const void* x, const 
   const int64_t M = (int64_t)p.B * p.L;
   *x16_ready = false;
   if (project_mfma_supported(p, model_dim) && knorm) {
-    const unsigned grid = (unsigned)(((M + kRows - 1) / kRows) * 2 * p.H);
+    // row tiles rounded up to a multiple of 8 (one per XCD); the extra
+    // workgroups return at once
+    const int64_t mts = (M + kRows - 1) / kRows;
+    const unsigned grid = (unsigned)(((mts + 7) / 8) * 8 * 2 * p.H);
     if (p.d == 128) {
       constexpr int shmem = PLds<128>::kBytes;
       (void)hipFuncSetAttribute((const void*)k_proj_mfma<128>,
