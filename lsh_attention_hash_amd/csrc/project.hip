@@ -12,8 +12,8 @@
 // workgroup of 4 waves computes a 128-row x d-column tile of one head's qk or
 // v (the 2H tiles of a row tile run on one XCD, one after the other, so the x
 // tile is read from HBM once and from that XCD's L2 by the others) with
-// v_mfma_f32_16x16x32_bf16: wave w owns rows 32w .. 32w + 31 and every column,
-// so a row's sums stay inside one wave. K goes in slabs of 64, double-buffered
+// v_mfma_f32_16x16x32_bf16, the 4 waves as 2 x 2 blocks of 64 rows x d/2
+// columns. K goes in slabs of 64, double-buffered
 // in LDS (rows of x and of the weight, K contiguous, +16-byte pad), with the
 // next two slabs in flight in registers while the current one is multiplied.
 // The epilogue rounds the tile to bf16 and passes it through LDS so that each
@@ -52,7 +52,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     float2* __restrict__ xnorm, float* __restrict__ knorm, int64_t M, int L, int H,
     int model_dim) {
   using Lay = PLds<D>;
-  constexpr int DT = D / 16;                 // 16-column tiles
   constexpr int kAPer = kRows * 8 / kThreads;  // 16-byte pieces of the x slab per thread
   constexpr int kBPer = D * 8 / kThreads;      // of the weight slab
   extern __shared__ __align__(16) unsigned char lds[];
@@ -107,29 +106,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     }
   };
 
+  // waves as 2 x 2: wave w owns rows 64 (w / 2) .. + 63 and columns
+  // (D / 2)(w % 2) .. + D / 2 - 1 of the tile
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  floatx4_t acc[2][DT];
+  constexpr int RT = 4, CT = D / 32;  // 16-row and 16-column tiles per wave
+  const int wr = 64 * (w >> 1), wc = (D / 2) * (w & 1);
+  floatx4_t acc[RT][CT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int ct = 0; ct < DT; ++ct) acc[i][ct] = floatx4_t{};
+    for (int ct = 0; ct < CT; ++ct) acc[i][ct] = floatx4_t{};
 
   auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kSlab / 32; ++ks) {
-      bf16x8_t a[2], b[DT];
+      bf16x8_t a[RT], b[CT];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *(const bf16x8_t*)(lds + Lay::kA + (buf * kRows + 32 * w + 16 * i + lq) * kStride +
+      for (int i = 0; i < RT; ++i)
+        a[i] = *(const bf16x8_t*)(lds + Lay::kA + (buf * kRows + wr + 16 * i + lq) * kStride +
                                   (32 * ks + 8 * g) * 2);
 #pragma unroll
-      for (int ct = 0; ct < DT; ++ct)
-        b[ct] = *(const bf16x8_t*)(lds + Lay::kB + (buf * D + 16 * ct + lq) * kStride +
+      for (int ct = 0; ct < CT; ++ct)
+        b[ct] = *(const bf16x8_t*)(lds + Lay::kB + (buf * D + wc + 16 * ct + lq) * kStride +
                                    (32 * ks + 8 * g) * 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int ct = 0; ct < DT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
           acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[ct], acc[i][ct], 0, 0, 0);
     }
   };
@@ -154,16 +157,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     }
   }
 
-  // epilogue: lane holds rows 32w + 16i + 4g + 0..3 of column 16ct + lq; the
-  // tile goes to LDS as bf16 rows, then out with 16 bytes per lane
+  // epilogue: lane holds rows wr + 16i + 4g + 0..3 of column wc + 16ct + lq;
+  // the tile goes to LDS as bf16 rows, then out with 16 bytes per lane
   unsigned char* ot = lds;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int ct = 0; ct < DT; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        *(uint16_t*)(ot + (32 * w + 16 * i + 4 * g + u) * Lay::kOutStride + (16 * ct + lq) * 2) =
+        *(uint16_t*)(ot + (wr + 16 * i + 4 * g + u) * Lay::kOutStride + (wc + 16 * ct + lq) * 2) =
             f32_to_bf16(acc[i][ct][u]).bits;
   __syncthreads();
   constexpr int kLpr = D / 8;                  // lanes per row (16 bytes each)
