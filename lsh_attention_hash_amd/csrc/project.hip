@@ -9,39 +9,32 @@
 // input dtype.
 //
 // Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 64): one
-// workgroup of 4 waves computes a 128-row x d-column tile of one head's qk or
-// v (the 2H tiles of a row tile run on one XCD, one after the other, so the x
-// tile is read from HBM once and from that XCD's L2 by the others) with
-// v_mfma_f32_16x16x32_bf16, the 4 waves as 2 x 2 blocks of 64 rows x d/2
-// columns. K goes in slabs of 64, double-buffered
-// in LDS (rows of x and of the weight, K contiguous, +16-byte pad), with the
-// next two slabs in flight in registers while the current one is multiplied.
-// The epilogue rounds the tile to bf16 and passes it through LDS so that each
+// workgroup computes a 128-row x d-column tile of one head's qk or v with the
+// tile of gemm_core.h (the 2H tiles of a row tile run on one XCD, one after
+// the other, so the x tile is read from HBM once and from that XCD's L2 by
+// the others). The epilogue rounds the tile to bf16 and passes it through LDS so that each
 // lane writes 16 contiguous bytes of a row. For qk tiles the same pass produces
 // what the hash's pre-pass would compute from these rows (the fp16 copy of
 // qk, the norm bounds of the copy and of its rounding error, and the squared
 // norm), with the same per-row arithmetic, so the hash can skip that pass.
 #include "dtype.h"
+#include "gemm_core.h"
 #include "hash_x16.h"
 #include "internal.h"
 
 namespace lsh {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
+using gemm::floatx4_t;
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;          // rows of x per tile
-constexpr int kSlab = 64;           // K per LDS slab
-constexpr int kStride = kSlab * 2 + 16;  // bytes per staged row (+16 pad)
+using gemm::kRows;
+using gemm::kSlab;
+using gemm::kThreads;
 
 template <int D>
 struct PLds {
-  static constexpr int kA = 0;                         // [2][kRows] x rows
-  static constexpr int kB = kA + 2 * kRows * kStride;  // [2][D] weight rows
-  static constexpr int kBytes = kB + 2 * D * kStride;
-  static constexpr int kOutStride = D * 2 + 16;        // epilogue tile row (bf16, +pad)
+  static constexpr int kBytes = gemm::Lay<D>::kBytes;
+  static constexpr int kOutStride = D * 2 + 16;  // epilogue tile row (bf16, +pad)
   static_assert(kRows * kOutStride <= kBytes, "epilogue tile fits");
 };
 
@@ -52,8 +45,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     float2* __restrict__ xnorm, float* __restrict__ knorm, int64_t M, int L, int H,
     int model_dim) {
   using Lay = PLds<D>;
-  constexpr int kAPer = kRows * 8 / kThreads;  // 16-byte pieces of the x slab per thread
-  constexpr int kBPer = D * 8 / kThreads;      // of the weight slab
   extern __shared__ __align__(16) unsigned char lds[];
   // Workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8): the
   // 2H tiles of a row tile get ids of one residue, consecutive within their
@@ -68,94 +59,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
   const int h = is_v ? nt - H : nt;
   const uint4* wrows = (is_v ? w_v : w_qk) + (int64_t)h * D * (model_dim / 8);
   const int t = threadIdx.x;
-  const int kseg = model_dim / 8;  // 16-byte pieces per row of x or of the weight
-  const int nslab = model_dim / kSlab;
 
-  // two slabs in flight in registers (slab j in set j % 2); rows past M
-  // read row M - 1 (their results are not stored), so no load is conditional
-  uint4 ra0[kAPer], rb0[kBPer], ra1[kAPer], rb1[kBPer];
-  int64_t arow[kAPer];
-#pragma unroll
-  for (int j = 0; j < kAPer; ++j) {
-    const int64_t row = row0 + t / 8 + (kThreads / 8) * j;
-    arow[j] = (row < M ? row : M - 1) * kseg + t % 8;
-  }
-  const uint4* wbase = wrows + (int64_t)(t / 8) * kseg + t % 8;
-  auto load = [&](uint4 (&ra)[kAPer], uint4 (&rb)[kBPer], int s) {
-#pragma unroll
-    for (int j = 0; j < kAPer; ++j) ra[j] = x[arow[j] + s * 8];
-#pragma unroll
-    for (int j = 0; j < kBPer; ++j) rb[j] = wbase[(int64_t)(kThreads / 8) * j * kseg + s * 8];
-  };
-  // (each piece passes through a register-only asm statement, so the copy
-  // cannot become a memcpy from a stack copy of the registers)
-  auto store = [&](const uint4 (&ra)[kAPer], const uint4 (&rb)[kBPer], int buf) {
-#pragma unroll
-    for (int j = 0; j < kAPer; ++j) {
-      const int r = t / 8 + (kThreads / 8) * j, pc = t % 8;
-      uint4 q = ra[j];
-      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-      *(uint4*)(lds + Lay::kA + (buf * kRows + r) * kStride + pc * 16) = q;
-    }
-#pragma unroll
-    for (int j = 0; j < kBPer; ++j) {
-      const int c = t / 8 + (kThreads / 8) * j, pc = t % 8;
-      uint4 q = rb[j];
-      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-      *(uint4*)(lds + Lay::kB + (buf * D + c) * kStride + pc * 16) = q;
-    }
-  };
-
-  // waves as 2 x 2: wave w owns rows 64 (w / 2) .. + 63 and columns
-  // (D / 2)(w % 2) .. + D / 2 - 1 of the tile
-  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  constexpr int RT = 4, CT = D / 32;  // 16-row and 16-column tiles per wave
-  const int wr = 64 * (w >> 1), wc = (D / 2) * (w & 1);
+  constexpr int RT = gemm::Lay<D>::RT, CT = gemm::Lay<D>::CT;
   floatx4_t acc[RT][CT];
-#pragma unroll
-  for (int i = 0; i < RT; ++i)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[i][ct] = floatx4_t{};
-
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int ks = 0; ks < kSlab / 32; ++ks) {
-      bf16x8_t a[RT], b[CT];
-#pragma unroll
-      for (int i = 0; i < RT; ++i)
-        a[i] = *(const bf16x8_t*)(lds + Lay::kA + (buf * kRows + wr + 16 * i + lq) * kStride +
-                                  (32 * ks + 8 * g) * 2);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        b[ct] = *(const bf16x8_t*)(lds + Lay::kB + (buf * D + wc + 16 * ct + lq) * kStride +
-                                   (32 * ks + 8 * g) * 2);
-#pragma unroll
-      for (int i = 0; i < RT; ++i)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-          acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[ct], acc[i][ct], 0, 0, 0);
-    }
-  };
-
-  load(ra0, rb0, 0);
-  store(ra0, rb0, 0);
-  if (1 < nslab) load(ra1, rb1, 1);
-  if (2 < nslab) load(ra0, rb0, 2);
-  __syncthreads();
-  // step s: multiply slab s (LDS buffer s % 2), stage slab s + 1 from its
-  // registers, then reuse them for slab s + 3
-  for (int s = 0; s < nslab; s += 2) {
-    compute(0);
-    if (s + 1 < nslab) store(ra1, rb1, 1);
-    __syncthreads();
-    if (s + 3 < nslab) load(ra1, rb1, s + 3);
-    if (s + 1 < nslab) {
-      compute(1);
-      if (s + 2 < nslab) store(ra0, rb0, 0);
-      __syncthreads();
-      if (s + 4 < nslab) load(ra0, rb0, s + 4);
-    }
-  }
+  gemm::tile<D>(lds, x, row0, M, wrows, model_dim, acc);
+  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
+  const int wr = gemm::wave_row(w), wc = gemm::wave_col<D>(w);
 
   // epilogue: lane holds rows wr + 16i + 4g + 0..3 of column wc + 16ct + lq;
   // the tile goes to LDS as bf16 rows, then out with 16 bytes per lane
