@@ -97,6 +97,7 @@ def _load():
             "lsh_oracle_attend_rows": [C, P, P, P, P, ctypes.c_int64, P, P, P],
             "lsh_oracle_backward": [C, P, P, P, P, P, P],
             "lsh_oracle_project": [C, ctypes.c_int64, P, P, P, P, P],
+            "lsh_oracle_ffn": [ctypes.c_int64] * 4 + [P] * 8,
         }.items():
             f = getattr(lib, name)
             f.argtypes = argt
@@ -210,6 +211,32 @@ def backward(c: Config, qk, v, perm, dout):
     _chk(_load().lsh_oracle_backward(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do), _p(dqk),
                                      _p(dv)), "backward")
     return dqk, dv
+
+
+def ffn(y1, w1, b1, w2, b2, x2=None, chunk_rows=None, return_hidden=False):
+    """Chunked feed-forward: y2 [rows, d_model] from y1 [rows, d_model], w1
+    [d_ff, d_model], b1 [d_ff], w2 [d_model, d_ff], b2 [d_model] and the
+    optional residual x2 [rows, d_model]; chunk_rows defaults to all rows.
+    With return_hidden, also the ReLU activations [rows, d_ff]."""
+    y1, w1, b1, w2, b2 = (_f64(a) for a in (y1, w1, b1, w2, b2))
+    rows, d_model = y1.shape
+    d_ff = w1.shape[0]
+    if w1.shape != (d_ff, d_model) or w2.shape != (d_model, d_ff) or b1.shape != (d_ff,) \
+            or b2.shape != (d_model,):
+        raise ValueError("ffn: inconsistent shapes")
+    x2p = None
+    if x2 is not None:
+        x2 = _f64(x2)
+        if x2.shape != y1.shape:
+            raise ValueError("ffn: x2 must match y1")
+        x2p = _p(x2)
+    y2 = np.empty((rows, d_model), np.float64)
+    hid = np.empty((rows, d_ff), np.float64) if return_hidden else None
+    _chk(_load().lsh_oracle_ffn(ctypes.c_int64(rows), ctypes.c_int64(d_model),
+                                ctypes.c_int64(d_ff), ctypes.c_int64(chunk_rows or max(rows, 1)),
+                                _p(y1), _p(w1), _p(b1), _p(w2), _p(b2), x2p, _p(y2),
+                                None if hid is None else _p(hid)), "ffn")
+    return (y2, hid) if return_hidden else y2
 
 
 def project(c: Config, x, w_qk, w_v):

@@ -664,3 +664,55 @@ int lsh_oracle_project(const lsh_oracle_config* c, int64_t model_dim, const doub
       }
   return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Chunked feed-forward, [DT] section 2.3: the feed-forward is applied to one
+ * chunk of rows at a time and the chunk outputs are concatenated; d_ff is
+ * usually four times the model dimension. [TT] "FF layer chunking" splits
+ * the second half of the reversible block, y2 = x2 + FF(y1), the same way.
+ * Readings where the pages are silent: FF is the plain two-layer feed-forward
+ * with biases and a ReLU between the layers (no normalisation inside), and
+ * the residual x2 is added to its output when given.
+ * Each chunk holds its own hidden activations [chunk_rows, d_ff] (the memory
+ * the chunking bounds); every row is computed the same way in any chunk.
+ */
+int lsh_oracle_ffn(int64_t rows, int64_t d_model, int64_t d_ff, int64_t chunk_rows,
+                   const double* y1, const double* w1, const double* b1, const double* w2,
+                   const double* b2, const double* x2, double* y2, double* hidden) {
+  if (rows < 0 || d_model < 1 || d_ff < 1 || chunk_rows < 1) return -13;
+  if (rows == 0) return 0;
+  const int64_t cr = chunk_rows < rows ? chunk_rows : rows;
+  double* h = (double*)malloc(sizeof(double) * (size_t)(cr * d_ff));
+  if (!h) return -12;
+  for (int64_t c0 = 0; c0 < rows; c0 += cr) {
+    const int64_t n = (rows - c0 < cr) ? rows - c0 : cr;  /* rows in this chunk */
+    /* first layer and ReLU */
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      const double* yr = y1 + (c0 + r) * d_model;
+      for (int64_t j = 0; j < d_ff; ++j) {
+        const double* wj = w1 + j * d_model;
+        double s = 0.0;
+        for (int64_t k = 0; k < d_model; ++k) s += yr[k] * wj[k];
+        s += b1[j];
+        h[r * d_ff + j] = s > 0.0 ? s : 0.0;
+      }
+    }
+    /* second layer, bias, residual */
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      const double* hr = h + r * d_ff;
+      for (int64_t e = 0; e < d_model; ++e) {
+        const double* we = w2 + e * d_ff;
+        double s = 0.0;
+        for (int64_t j = 0; j < d_ff; ++j) s += hr[j] * we[j];
+        s += b2[e];
+        if (x2) s += x2[(c0 + r) * d_model + e];
+        y2[(c0 + r) * d_model + e] = s;
+      }
+    }
+    if (hidden) memcpy(hidden + c0 * d_ff, h, sizeof(double) * (size_t)(n * d_ff));
+  }
+  free(h);
+  return 0;
+}

@@ -19,7 +19,8 @@
  *   [DT] Reformer overview, www.dtcms.com/a/488796.html, section 2.1
  *        "key steps": unit-normalised keys, multiple projection rounds, each
  *        query also looks at the neighbouring group; "math" paragraph: the
- *        scaled softmax with 1/sqrt(d_k) and a mask.
+ *        scaled softmax with 1/sqrt(d_k) and a mask; section 2.3: the
+ *        reversible block and the chunked feed-forward layer.
  * Where the pages leave a step open, the reading taken is stated at the step
  * in lsh_oracle.c.
  *
@@ -116,6 +117,21 @@ int lsh_oracle_backward(const lsh_oracle_config* cfg, const double* qk, const do
  * layer from model_dim to H * d features); qk, v [B, H, L, d]. */
 int lsh_oracle_project(const lsh_oracle_config* cfg, int64_t model_dim, const double* x,
                        const double* w_qk, const double* w_v, double* qk, double* v);
+
+/* The chunked feed-forward layer of the reversible block ([DT] section 2.3,
+ * chunked feed-forward; [TT] reversible Transformer and "FF layer chunking"
+ * sections): the rows (positions) are cut into chunks of chunk_rows (the last
+ * one shorter when rows is not a multiple), each chunk goes through the
+ * feed-forward on its own, and the outputs are concatenated:
+ *   hidden[i, j] = max(0, sum_k y1[i, k] w1[j, k] + b1[j])
+ *   y2[i, e]     = x2[i, e] + sum_j hidden[i, j] w2[e, j] + b2[e]
+ * y1, x2, y2 [rows, d_model]; w1 [d_ff, d_model] and w2 [d_model, d_ff] (the
+ * weights of linear layers d_model -> d_ff and back); b1 [d_ff], b2 [d_model].
+ * x2 may be NULL (no residual; y2 is then the feed-forward alone). hidden, if
+ * not NULL, receives [rows, d_ff]. Returns -13 on bad sizes. */
+int lsh_oracle_ffn(int64_t rows, int64_t d_model, int64_t d_ff, int64_t chunk_rows,
+                   const double* y1, const double* w1, const double* b1, const double* w2,
+                   const double* b2, const double* x2, double* y2, double* hidden);
 
 /* Output rows for a sample of (b, h, i), given every round's perm (and buckets,
  * as for lsh_oracle_attend): rows[k] = (b * H + h) * L + i; out_rows [n_rows, d];

@@ -8,6 +8,7 @@ import pytest
 import oracle
 
 import test_oracle_backward as bpins
+import test_oracle_ffn as fpins
 import test_oracle_pins as pins
 import test_oracle_variants as vpins
 
@@ -67,6 +68,18 @@ MUTATIONS = [
     ("head offset of the weights dropped",
      "const double* wq = w_qk + (h * d + e) * model_dim;",
      "const double* wq = w_qk + e * model_dim;"),
+    # chunked feed-forward
+    ("ffn: ReLU dropped", "h[r * d_ff + j] = s > 0.0 ? s : 0.0;", "h[r * d_ff + j] = s;"),
+    ("ffn: ReLU as absolute value", "h[r * d_ff + j] = s > 0.0 ? s : 0.0;",
+     "h[r * d_ff + j] = s > 0.0 ? s : -s;"),
+    ("ffn: first bias dropped", "s += b1[j];", "s += 0.0 * b1[j];"),
+    ("ffn: second bias dropped", "s += b2[e];", "s += 0.0 * b2[e];"),
+    ("ffn: second weight transposed", "for (int64_t j = 0; j < d_ff; ++j) s += hr[j] * we[j];",
+     "for (int64_t j = 0; j < d_ff; ++j) s += hr[j] * w2[j * d_model + e];"),
+    ("ffn: chunk offset dropped from the input", "const double* yr = y1 + (c0 + r) * d_model;",
+     "const double* yr = y1 + r * d_model;"),
+    ("ffn: residual dropped", "if (x2) s += x2[(c0 + r) * d_model + e];",
+     "if (0) s += x2[(c0 + r) * d_model + e];"),
 ]
 
 
@@ -98,6 +111,11 @@ def _pin_calls():
         lambda: vpins.test_dedup_with_identical_rounds_is_one_round(o),
         lambda: pins.test_projection_equals_library_matmul(o),
         lambda: pins.test_projection_with_selection_weights_copies_the_input(o),
+        lambda: fpins.test_ffn_split_identity_returns_the_input(o),
+        lambda: fpins.test_ffn_half_of_the_split_is_the_positive_part(o),
+        lambda: fpins.test_ffn_biases_through_selection_weights(o),
+        lambda: fpins.test_ffn_residual_is_added(o),
+        lambda: fpins.test_ffn_chunking_changes_nothing(o, 3),
     ]
 
 
