@@ -14,6 +14,10 @@ With --backward, one step is one backward (gradients of qk and v for a seeded
 dout, at the permutation of one forward of the same inputs), with the same
 line layout: tokens/s of backwards, the dominant backward kernel's roofline,
 and the oracle's backward on a bounded sample.
+
+With --ffn, one step is the chunked feed-forward half of the reversible block
+over the workload's B * L rows (d_model = H * d, d_ff = 4 d_model, chunks of
+--ffn-chunk rows), with its two matrix-core layers' roofline.
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "LSH-attn fwd tokens/sec at L=64K, 4 rounds; % MFMA / HBM roofline"
 METRIC_BWD = "LSH-attn bwd tokens/sec at L=64K, 4 rounds; % MFMA / HBM roofline"
+METRIC_FFN = "chunked feed-forward tokens/sec at L=64K; % MFMA roofline"
 
 # MI355X published peaks
 PEAK = {
@@ -118,7 +123,8 @@ def backward_units(w, out_dtype: str):
 # The matrix-core peak each stage's contraction runs at (fp16 projection,
 # bf16 attention); HBM for the rest; fp64 vector for the exact re-scoring.
 MFMA_PEAK = {"hash": "mfma_fp16_TFLOPs", "attend": "mfma_bf16_TFLOPs", "project": "mfma_bf16_TFLOPs",
-             "recompute": "mfma_bf16_TFLOPs", "products": "mfma_bf16_TFLOPs"}
+             "recompute": "mfma_bf16_TFLOPs", "products": "mfma_bf16_TFLOPs",
+             "ffn_up": "mfma_bf16_TFLOPs", "ffn_down": "mfma_bf16_TFLOPs"}
 
 
 def stage_bound(stage: str, u: dict):
@@ -147,7 +153,8 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
         achieved = u["flops"] / (ms * 1e-3) / 1e12
         unit = "TFLOP/s"
     peak = PEAK[peak_key]
-    return {"kernel": STAGE_KERNEL.get(stage, BWD_STAGE_KERNEL.get(stage, stage)),
+    kernels = {**STAGE_KERNEL, **BWD_STAGE_KERNEL, **FFN_STAGE_KERNEL}
+    return {"kernel": kernels.get(stage, stage),
             "stage": stage, "bound": bound,
             "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 5), "traffic": traffic,
@@ -159,6 +166,7 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
 # and the source files each stage's kernels are built from.
 STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine",
                 "project": "k_proj_mfma"}
+FFN_STAGE_KERNEL = {"ffn_up": "k_ffn_mfma<true>", "ffn_down": "k_ffn_mfma<false>"}
 BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "products": "k_bwd_fused_mfma",
                     "reduce": "k_bwd_reduce_sum"}
 STAGE_SOURCES = {
@@ -168,6 +176,7 @@ STAGE_SOURCES = {
     "project": ["project.hip", "hash_x16.h"],
     "recompute": ["attend_mfma.hip", "backward.hip"], "rows": ["backward.hip"],
     "products": ["backward_mfma.hip", "rows_lds.h"], "reduce": ["backward.hip"],
+    "ffn_up": ["ffn.hip", "gemm_core.h"], "ffn_down": ["ffn.hip", "gemm_core.h"],
 }
 
 
@@ -354,6 +363,128 @@ def main_backward(args, w, inp, op_kw):
     print(json.dumps(res), flush=True)
 
 
+def ffn_units(rows: int, d_model: int, d_ff: int, es: int):
+    """Algorithmic work of each feed-forward layer over `rows` rows: 2 rows
+    d_model d_ff flops, and the bytes each reads and writes once (its input
+    rows, weight, bias, output rows; the second layer also the residual)."""
+    flops = 2.0 * rows * d_model * d_ff
+    return {"ffn_up": {"flops": flops,
+                       "bytes": es * (rows * d_model + d_ff * d_model + d_ff + rows * d_ff)},
+            "ffn_down": {"flops": flops,
+                         "bytes": es * (rows * d_ff + d_model * d_ff + d_model
+                                        + 2 * rows * d_model)}}
+
+
+def cpu_baseline_ffn(fi, n_rows: int):
+    """The fp64 oracle's feed-forward as it stands on the first n_rows rows
+    (one chunk), scaled to rows/s."""
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    env_threads = os.environ.get("OMP_NUM_THREADS")
+    if env_threads:
+        threads = min(threads, int(env_threads))
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.ffn(fi.y1[:n_rows], fi.w1, fi.b1, fi.w2, fi.b2, x2=fi.x2[:n_rows])
+    t = time.perf_counter() - t0
+    return {"value": round(n_rows / t, 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the first {n_rows} of {fi.rows} rows (d_model {fi.d_model}, d_ff "
+                      f"{fi.d_ff}, with the residual) through the fp64 oracle's feed-forward "
+                      f"in {t:.2f} s; OpenMP over rows",
+            "seconds": round(t, 3), "threads_available": threads}
+
+
+def main_ffn(args, w):
+    """The --ffn line (see the module docstring)."""
+    import numpy as np
+    import torch
+
+    import lsh_attention_hash_amd as lat
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    rows, d_model = w.batch * w.seq_len, w.heads * w.head_dim
+    d_ff = 4 * d_model
+    fi = workloads.make_ffn_inputs(rows, d_model, d_ff, w.dtype)
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[w.dtype]
+    if w.dtype == "bf16":
+        t = {k: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+             for k, b in fi.bits.items()}
+    else:
+        t = {k: torch.from_numpy(getattr(fi, k)).to(dev) for k in fi.bits}
+    op = lat.ChunkedFeedForward(rows, d_model, d_ff, args.ffn_chunk, dtype=tdt)
+    y2 = torch.empty((rows, d_model), dtype=tdt, device=dev)
+    call = lambda: op(t["y1"], t["w1"], t["b1"], t["w2"], t["b2"], x2=t["x2"], out=y2)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    op.set_timing(args.steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    stage_ms, n_timed, n_chunks = op.get_timing()
+    ws_bytes = op.workspace_bytes()
+    op.close()
+    calibration_copy(args.calib_copy_mib, dev)
+
+    chunk = min(args.ffn_chunk or rows, rows)
+    per_call = n_chunks / max(n_timed, 1)
+    # per launch: one chunk's rows (the last chunk may be shorter: averaged)
+    units = ffn_units(rows / per_call, d_model, d_ff, esize(w.dtype))
+    stage_avg = {k: v_ / max(n_chunks, 1) for k, v_ in stage_ms.items()}  # ms per launch
+    dominant = max(stage_avg, key=stage_avg.get)
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            with open(args.traffic_json) as f:
+                entry = json.load(f).get(args.workload + ":ffn", {}).get(dominant)
+            if entry and entry.get("source_hash") == kernel_source_hash(dominant):
+                traffic = entry.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    rl = roofline(dominant, units, stage_avg[dominant], traffic)
+    per_stage = {}
+    for k, t_ in stage_avg.items():
+        r = roofline(k, units, t_)
+        per_stage[k] = {"ms_per_launch": round(t_, 5), "launches_per_step": per_call,
+                        "achieved": r["achieved"], "unit": r["unit"], "frac": r["frac"]}
+    res = {
+        "metric": METRIC_FFN,
+        "value": round(rows / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "chunked feed-forward", "rows": rows,
+                   "d_model": d_model, "d_ff": d_ff, "chunk_rows": chunk,
+                   "hidden_buffer_bytes": ws_bytes, "residual": True,
+                   "inputs": "seeded normal y1, x2; weights N(0, 1/fan_in); biases N(0, 0.01)"},
+        "roofline": rl,
+        "stages": per_stage,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_ffn(fi, args.ffn_cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,6 +502,13 @@ def main():
     ap.add_argument("--variants", default="",
                     help="comma list of variant readings for the forward: look_ahead, "
                          "same_bucket, norm_queries, dedup (default: none)")
+    ap.add_argument("--ffn", action="store_true",
+                    help="time the chunked feed-forward (d_model = H * d, d_ff = 4 d_model) "
+                         "over the workload's B * L rows instead of the attention")
+    ap.add_argument("--ffn-chunk", type=int, default=16384,
+                    help="rows per feed-forward chunk (0: all rows at once)")
+    ap.add_argument("--ffn-cpu-rows", type=int, default=32768,
+                    help="rows in the oracle's feed-forward sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: as many as rounds fit the cores)")
@@ -401,6 +539,10 @@ def main():
     import workloads
 
     w = workloads.get(args.workload)
+    if args.ffn:
+        torch.cuda.set_device(torch.device("cuda", 0))
+        main_ffn(args, w)
+        return
     out_dtype = args.out_dtype or w.dtype
     variants = [x for x in args.variants.split(",") if x]
     for x in variants:
@@ -589,9 +731,10 @@ def write_traffic(args):
     if os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             out = json.load(f)
-    key = args.workload + (":backward" if args.backward else "")
+    key = args.workload + (":backward" if args.backward else ":ffn" if args.ffn else "")
     entry = out.setdefault(key, {})
-    for stage, kname in (BWD_STAGE_KERNEL if args.backward else STAGE_KERNEL).items():
+    kernels = BWD_STAGE_KERNEL if args.backward else FFN_STAGE_KERNEL if args.ffn else STAGE_KERNEL
+    for stage, kname in kernels.items():
         f_kib, w_kib = mean_of(fetch, kname), mean_of(write, kname)
         if f_kib is None or w_kib is None:
             continue

@@ -247,6 +247,74 @@ int lsh_attn_destroy(lsh_attn_t handle);
 /* Static, never-NULL description of a status code. */
 const char* lsh_attn_strerror(int status);
 
+/* ---------------------------------------------------------------------------
+ * Chunked feed-forward: the other half of the reversible block that holds the
+ * attention (Reformer overview at www.dtcms.com/a/488796.html, section 2.3:
+ * y2 = x2 + FeedForward(y1), and the chunked feed-forward applied to one
+ * chunk of rows at a time with the chunk outputs concatenated; the Reformer
+ * summary at p2.ttnews.xyz, "FF layer chunking"). Per row i:
+ *   hidden[i, :] = max(0, W1 y1[i, :] + b1)         (d_ff values)
+ *   y2[i, :]     = x2[i, :] + W2 hidden[i, :] + b2   (x2 optional)
+ * Rows go in chunks of chunk_rows; only one chunk's hidden rows are held
+ * (chunk_rows x d_ff in the layer dtype, in the handle's workspace). A row's
+ * output is bit-identical whatever the chunking.
+ * Statuses and pointer conventions are those of the attention entry points.
+ */
+typedef struct lsh_ffn_s* lsh_ffn_t;
+
+typedef struct {
+  int64_t max_rows;   /* most rows a forward may take (>= 1) */
+  int64_t chunk_rows; /* rows per chunk; 0 = all rows in one chunk */
+  int32_t d_model;    /* features of y1, x2, y2 (a multiple of 8) */
+  int32_t d_ff;       /* hidden features (a multiple of 8) */
+  int32_t dtype;      /* lsh_attn_dtype_t of every tensor; fp32 accumulation */
+} lsh_ffn_config_t;
+
+/*
+ * Create a handle and allocate the chunk's hidden buffer (hipMalloc,
+ * min(chunk_rows, max_rows) x d_ff elements) on the current device.
+ * Errors: INVALID_ARG for null pointers or sizes below the limits above;
+ * UNSUPPORTED for a dtype outside the enum or d_model / d_ff not multiples of
+ * 8 (and for shapes off the matrix-core path whose chunk exceeds 2^31
+ * elements); OUT_OF_MEMORY if the buffer cannot be allocated.
+ */
+int lsh_ffn_create(const lsh_ffn_config_t* cfg, lsh_ffn_t* handle);
+
+/*
+ * y2 [rows, d_model] from y1 [rows, d_model], w1 [d_ff, d_model], b1 [d_ff],
+ * w2 [d_model, d_ff], b2 [d_model] and x2 [rows, d_model] (NULL: no
+ * residual). Device pointers; y1, w1, w2, x2 and y2 16-byte aligned. y2 may
+ * alias x2 (each element is read before it is written, by the same thread);
+ * it must not overlap y1. rows = 0 does nothing. The matrix-core path takes
+ * bf16 with d_model and d_ff multiples of 128; the hidden rows are rounded
+ * to the layer dtype between the two layers.
+ * Errors: INVALID_ARG for a null handle or required pointer, misalignment,
+ * rows < 0 or rows > max_rows, or a device other than the handle's;
+ * HIP on a launch error.
+ */
+int lsh_ffn_forward(lsh_ffn_t handle, int64_t rows, const void* y1, const void* w1,
+                    const void* b1, const void* w2, const void* b2, const void* x2, void* y2,
+                    void* stream);
+
+/*
+ * Device timing as for the attention: with capacity > 0, each of the next
+ * `capacity` forwards records an event before its first launch and after
+ * every launch. lsh_ffn_get_timing sums, over the timed forwards since the
+ * last call, stage 0 (the first layer, every chunk) and stage 1 (the second
+ * layer) into ms[LSH_FFN_N_STAGES], stores the number of forwards and (if
+ * n_chunks is not NULL) of chunks, and restarts the accumulation.
+ * Errors: INVALID_ARG for null pointers or timing not enabled; HIP on event errors.
+ */
+#define LSH_FFN_N_STAGES 2
+int lsh_ffn_set_timing(lsh_ffn_t handle, int capacity);
+int lsh_ffn_get_timing(lsh_ffn_t handle, double* ms, int64_t* n_forwards, int64_t* n_chunks);
+
+/* Bytes of device workspace (the hidden buffer). INVALID_ARG for null pointers. */
+int lsh_ffn_workspace_bytes(lsh_ffn_t handle, int64_t* bytes);
+
+/* Free the handle (synchronises the device first). NULL is accepted. */
+int lsh_ffn_destroy(lsh_ffn_t handle);
+
 #ifdef __cplusplus
 }
 #endif

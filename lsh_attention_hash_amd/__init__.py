@@ -15,8 +15,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["LSHAttention", "load_library", "library_path", "LSHAttnError", "EXPORTED_SYMBOLS",
-           "FLAG_SEPARATE_GATHER"]
+__all__ = ["LSHAttention", "ChunkedFeedForward", "load_library", "library_path", "LSHAttnError",
+           "EXPORTED_SYMBOLS", "FLAG_SEPARATE_GATHER"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "liblsh_attn.so")
@@ -36,11 +36,15 @@ EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x",
                     "lsh_attn_backward",
                     "lsh_attn_get_stats",
                     "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
-                    "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror")
+                    "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror",
+                    "lsh_ffn_create", "lsh_ffn_forward", "lsh_ffn_set_timing",
+                    "lsh_ffn_get_timing", "lsh_ffn_workspace_bytes", "lsh_ffn_destroy")
 N_STAGES = 8
 STAGES = ("hash_prep", "hash", "hash_rescore", "sort", "gather", "attend", "combine", "project")
 N_BWD_STAGES = 4
 BWD_STAGES = ("recompute", "rows", "products", "reduce")
+N_FFN_STAGES = 2
+FFN_STAGES = ("ffn_up", "ffn_down")
 
 
 class LSHAttnError(RuntimeError):
@@ -54,6 +58,11 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "heads", "seq_len", "head_dim", "n_buckets", "n_rounds", "chunk_len", "causal",
         "dtype", "out_dtype", "flags")]
+
+
+class FFNConfig(ctypes.Structure):
+    _fields_ = [("max_rows", ctypes.c_int64), ("chunk_rows", ctypes.c_int64),
+                ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("dtype", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -90,10 +99,20 @@ def load_library():
     lib.lsh_attn_destroy.argtypes = [P]
     lib.lsh_attn_strerror.argtypes = [I]
     lib.lsh_attn_strerror.restype = ctypes.c_char_p
+    lib.lsh_ffn_create.argtypes = [ctypes.POINTER(FFNConfig), ctypes.POINTER(P)]
+    lib.lsh_ffn_forward.argtypes = [P, ctypes.c_int64, P, P, P, P, P, P, P, P]
+    lib.lsh_ffn_set_timing.argtypes = [P, I]
+    lib.lsh_ffn_get_timing.argtypes = [P, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64)]
+    lib.lsh_ffn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.lsh_ffn_destroy.argtypes = [P]
     for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x", "lsh_attn_backward",
               "lsh_attn_get_stats",
               "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
-              "lsh_attn_workspace_bytes", "lsh_attn_destroy"):
+              "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_ffn_create",
+              "lsh_ffn_forward", "lsh_ffn_set_timing", "lsh_ffn_get_timing",
+              "lsh_ffn_workspace_bytes", "lsh_ffn_destroy"):
         getattr(lib, n).restype = I
     _lib = lib
     return lib
@@ -319,6 +338,98 @@ class LSHAttention:
         try:
             if getattr(self, "handle", None):
                 self.lib.lsh_attn_destroy(self.handle)
+                self.handle = ctypes.c_void_p()
+        except Exception:
+            pass
+
+
+class ChunkedFeedForward:
+    """The chunked feed-forward half of the reversible block, bound to a
+    library handle (which holds one chunk's hidden rows on the device).
+
+    Call with y1 [rows, d_model], w1 [d_ff, d_model], b1 [d_ff], w2
+    [d_model, d_ff], b2 [d_model] and optionally the residual x2
+    [rows, d_model], all contiguous in dtype on the handle's device, rows at
+    most max_rows. Returns y2 = x2 + relu(y1 w1^T + b1) w2^T + b2 [rows, d_model],
+    computed chunk_rows rows at a time (0: all rows at once).
+    """
+
+    def __init__(self, max_rows, d_model, d_ff, chunk_rows=0, dtype=torch.bfloat16, device=None):
+        self.lib = load_library()
+        self.cfg = FFNConfig(int(max_rows), int(chunk_rows), int(d_model), int(d_ff),
+                             _dtype_code(dtype))
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None
+                                   else torch.device(device).index or 0)
+        self.handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            rc = self.lib.lsh_ffn_create(ctypes.byref(self.cfg), ctypes.byref(self.handle))
+        if rc != 0:
+            self.handle = ctypes.c_void_p()
+            raise LSHAttnError(rc, "lsh_ffn_create", self.lib)
+
+    @property
+    def dtype(self):
+        return _TORCH[self.cfg.dtype]
+
+    _check = LSHAttention._check
+
+    def __call__(self, y1, w1, b1, w2, b2, x2=None, out=None, stream=None):
+        c, dt = self.cfg, self.dtype
+        if not isinstance(y1, torch.Tensor) or y1.dim() != 2:
+            raise ValueError("y1 must be a 2-D tensor [rows, d_model]")
+        rows = y1.shape[0]
+        self._check("y1", y1, (rows, c.d_model), dt)
+        self._check("w1", w1, (c.d_ff, c.d_model), dt)
+        self._check("b1", b1, (c.d_ff,), dt)
+        self._check("w2", w2, (c.d_model, c.d_ff), dt)
+        self._check("b2", b2, (c.d_model,), dt)
+        if x2 is not None:
+            self._check("x2", x2, (rows, c.d_model), dt)
+        if out is None:
+            out = torch.empty((rows, c.d_model), dtype=dt, device=self.device)
+        else:
+            self._check("out", out, (rows, c.d_model), dt)
+        s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
+        rc = self.lib.lsh_ffn_forward(self.handle, ctypes.c_int64(rows), y1.data_ptr(),
+                                      w1.data_ptr(), b1.data_ptr(), w2.data_ptr(), b2.data_ptr(),
+                                      None if x2 is None else x2.data_ptr(), out.data_ptr(), s)
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_ffn_forward", self.lib)
+        return out
+
+    def set_timing(self, capacity: int) -> None:
+        """Record HIP events around every launch of the next `capacity` forwards."""
+        rc = self.lib.lsh_ffn_set_timing(self.handle, int(capacity))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_ffn_set_timing", self.lib)
+
+    def get_timing(self):
+        """(dict stage -> summed ms, timed forwards, chunks in them); resets the sums."""
+        ms = (ctypes.c_double * N_FFN_STAGES)()
+        n, nc = ctypes.c_int64(), ctypes.c_int64()
+        rc = self.lib.lsh_ffn_get_timing(self.handle, ms, ctypes.byref(n), ctypes.byref(nc))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_ffn_get_timing", self.lib)
+        return {k: float(ms[j]) for j, k in enumerate(FFN_STAGES)}, int(n.value), int(nc.value)
+
+    def workspace_bytes(self) -> int:
+        b = ctypes.c_int64()
+        rc = self.lib.lsh_ffn_workspace_bytes(self.handle, ctypes.byref(b))
+        if rc != 0:
+            raise LSHAttnError(rc, "lsh_ffn_workspace_bytes", self.lib)
+        return int(b.value)
+
+    def close(self):
+        if self.handle:
+            rc = self.lib.lsh_ffn_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+            if rc != 0:
+                raise LSHAttnError(rc, "lsh_ffn_destroy", self.lib)
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                self.lib.lsh_ffn_destroy(self.handle)
                 self.handle = ctypes.c_void_p()
         except Exception:
             pass

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "lsh_attn.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lsh_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lsh_(?:attn|ffn)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_expected_entry_points():
@@ -92,3 +92,33 @@ def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(lat, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         lat.load_library()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(max_rows=0), 1),
+    (dict(d_model=0), 1),
+    (dict(d_ff=-8), 1),
+    (dict(chunk_rows=-1), 1),
+    (dict(dtype=5), 2),
+    (dict(d_model=100), 2),           # not a multiple of 8
+    (dict(d_ff=1020), 2),
+    # off the matrix-core path (fp32) with a chunk above 2^31 elements
+    (dict(dtype=0, max_rows=1 << 22, d_ff=1024), 2),
+])
+def test_ffn_create_rejects_bad_configs_on_the_host(kw, code):
+    lib = lat.load_library()
+    base = dict(max_rows=1024, chunk_rows=0, d_model=128, d_ff=512, dtype=lat.BF16)
+    base.update(kw)
+    cfg = lat.FFNConfig(**base)
+    h = ctypes.c_void_p(123)
+    assert lib.lsh_ffn_create(ctypes.byref(cfg), ctypes.byref(h)) == code
+    assert h.value is None
+
+
+def test_ffn_null_handle_and_pointers_are_invalid():
+    lib = lat.load_library()
+    assert lib.lsh_ffn_create(None, None) == 1
+    assert lib.lsh_ffn_forward(None, 1, None, None, None, None, None, None, None, None) == 1
+    assert lib.lsh_ffn_set_timing(None, 1) == 1
+    assert lib.lsh_ffn_workspace_bytes(None, None) == 1
+    assert lib.lsh_ffn_destroy(None) == 0

@@ -179,3 +179,43 @@ def make_layer_inputs(w: Workload, model_dim: int) -> LayerInputs:
     wq_s, wq_bits = _store(wq, w.dtype)
     wv_s, wv_bits = _store(wv, w.dtype)
     return LayerInputs(w, model_dim, x_s, wq_s, wv_s, rot, x_bits, wq_bits, wv_bits)
+
+
+@dataclasses.dataclass
+class FFNInputs:
+    """Stored inputs of the chunked feed-forward: float32 arrays holding the
+    stored values (bf16-representable for bf16) and, for bf16, the uint16 bit
+    patterns in ``bits`` (name -> array)."""
+    rows: int
+    d_model: int
+    d_ff: int
+    dtype: str
+    y1: np.ndarray
+    w1: np.ndarray
+    b1: np.ndarray
+    w2: np.ndarray
+    b2: np.ndarray
+    x2: np.ndarray
+    bits: dict
+
+
+def make_ffn_inputs(rows: int, d_model: int, d_ff: int, dtype: str = "bf16",
+                    seed: int = 0) -> FFNInputs:
+    """Draw y1 and x2 [rows, d_model] standard normal (the two halves of the
+    reversible block's input), w1 [d_ff, d_model] and w2 [d_model, d_ff]
+    normal with variance 1 / fan_in, and biases b1 [d_ff], b2 [d_model]
+    normal with standard deviation 0.1; seeds 8000 + 100 j + seed."""
+    def draw(j, shape, scale=1.0):
+        a = np.random.Generator(np.random.PCG64(8000 + 100 * j + seed)).standard_normal(
+            shape, dtype=np.float32)
+        return a * np.float32(scale) if scale != 1.0 else a
+    arrays = {"y1": draw(0, (rows, d_model)),
+              "w1": draw(1, (d_ff, d_model), 1.0 / np.sqrt(d_model)),
+              "b1": draw(2, (d_ff,), 0.1),
+              "w2": draw(3, (d_model, d_ff), 1.0 / np.sqrt(d_ff)),
+              "b2": draw(4, (d_model,), 0.1),
+              "x2": draw(5, (rows, d_model))}
+    stored, bits = {}, {}
+    for k, a in arrays.items():
+        stored[k], bits[k] = _store(a, dtype)
+    return FFNInputs(rows, d_model, d_ff, dtype, bits=bits, **stored)
