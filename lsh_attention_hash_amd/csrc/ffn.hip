@@ -12,8 +12,9 @@
 // Per chunk two launches: the first layer writes the chunk's hidden rows
 // (bias and ReLU in the epilogue, rounded to the layer dtype) into the
 // handle's buffer of chunk_rows x d_ff, and the second layer reads them back
-// (bias and residual in its epilogue). Both are the 128 x 128 tile of
-// gemm_core.h on matrix cores for bf16 with d_model and d_ff multiples of 128;
+// (bias and residual in its epilogue). Both are the 256 x 128 tile of
+// gemm_core.h (K slabs of 32, two workgroups per CU) on matrix cores for bf16
+// with d_model and d_ff multiples of 128;
 // other shapes and fp32 use a plain kernel (one thread per output element).
 // A row's result does not depend on the chunk it falls in: every output
 // element is summed over K in the same order in any tile.
@@ -27,20 +28,22 @@ namespace lsh {
 namespace {
 
 using gemm::floatx4_t;
-using gemm::kRows;
 using gemm::kThreads;
 
-constexpr int kBN = 128;      // output columns per tile
+constexpr int kBM = 256;       // rows per tile
+constexpr int kBN = 128;       // output columns per tile
+constexpr int kKSlab = 32;     // K per LDS slab
 constexpr int kGroupRows = 8;  // row tiles per group in an XCD's tile order
+using Tile = gemm::Lay<kBM, kBN, kKSlab>;
 
 struct FLds {
-  static constexpr int kBytes = gemm::Lay<kBN>::kBytes;
-  static constexpr int kOutStride = kBN * 4 + 16;  // epilogue tile row (fp32, +pad)
-  static_assert(kRows * kOutStride <= kBytes, "epilogue tile fits");
+  static constexpr int kOutStride = kBN * 4 + 16;  // epilogue half-tile row (fp32, +pad)
+  static constexpr int kHalf = kBM / 2 * kOutStride;
+  static constexpr int kBytes = Tile::kBytes > kHalf ? Tile::kBytes : kHalf;
 };
 
 // out[M, N] = epilogue(a[M, K] b[N, K]^T + bias[N]); UP: ReLU, else + resid
-// (resid [M, N] or null). Row-major bf16, N a multiple of 128, K of 64.
+// (resid [M, N] or null). Row-major bf16, N a multiple of 128, K of 32.
 template <bool UP>
 __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(
     const uint4* __restrict__ a, const uint4* __restrict__ b, const bf16_t* __restrict__ bias,
@@ -59,63 +62,70 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(
   const int gm = min(kGroupRows, mtl_n - grp * kGroupRows);  // row tiles in this group
   const int64_t mt = (int64_t)(grp * kGroupRows + rem % gm) * 8 + xcd;
   const int nt = rem / gm;
-  const int64_t row0 = mt * kRows;
+  const int64_t row0 = mt * kBM;
   if (row0 >= M) return;
   const int n0 = nt * kBN;
 
-  constexpr int RT = gemm::Lay<kBN>::RT, CT = gemm::Lay<kBN>::CT;
+  constexpr int RT = Tile::RT, CT = Tile::CT;
   floatx4_t acc[RT][CT];
-  gemm::tile<kBN>(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
+  gemm::tile<kBM, kBN, kKSlab>(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  const int wr = gemm::wave_row(w), wc = gemm::wave_col<kBN>(w);
+  const int wc = gemm::wave_col<kBN>(w);
 
-  // epilogue: bias (and ReLU) on the lane's elements, the tile to LDS in fp32,
-  // then out by rows, 8 elements (16 bytes of output) per lane
+  // epilogue in two halves of kBM / 2 rows (waves 0-1, then 2-3): bias (and
+  // ReLU) on the lane's elements, the half tile to LDS in fp32, then out by
+  // rows, 8 elements (16 bytes of output) per lane
   float* ot = (float*)lds;
   constexpr int kOS = FLds::kOutStride / 4;
+  float bv[CT];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int col = wc + 16 * ct + lq;
-    const float bv = to_f32(bias[n0 + col]);
-#pragma unroll
-    for (int i = 0; i < RT; ++i)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        float y = acc[i][ct][u] + bv;
-        if (UP) y = fmaxf(y, 0.f);
-        ot[(wr + 16 * i + 4 * g + u) * kOS + col] = y;
-      }
-  }
-  __syncthreads();
+  for (int ct = 0; ct < CT; ++ct) bv[ct] = to_f32(bias[n0 + wc + 16 * ct + lq]);
   constexpr int kLpr = kBN / 8;  // lanes per row
   constexpr int kRowsPerPass = kThreads / kLpr;
   const int sub = t % kLpr;
   const int64_t ldo = N / 8;  // 16-byte pieces per output row
-#pragma unroll 2
-  for (int r0 = 0; r0 < kRows; r0 += kRowsPerPass) {
-    const int r = r0 + t / kLpr;
-    const int64_t row = row0 + r;
-    if (row >= M) continue;
-    const float4 lo = *(const float4*)(ot + r * kOS + sub * 8);
-    const float4 hi = *(const float4*)(ot + r * kOS + sub * 8 + 4);
-    float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    const int64_t off = row * ldo + n0 / 8 + sub;
-    if (!UP && resid) {
-      const uint4 rv = resid[off];
-      const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        y[2 * q] += __uint_as_float(rw[q] << 16);
-        y[2 * q + 1] += __uint_as_float(rw[q] & 0xFFFF0000u);
-      }
+  for (int half = 0; half < 2; ++half) {
+    if ((w >> 1) == half) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float y = acc[i][ct][u] + bv[ct];
+            if (UP) y = fmaxf(y, 0.f);
+            ot[(16 * i + 4 * g + u) * kOS + wc + 16 * ct + lq] = y;
+          }
     }
-    uint32_t pw[4];
+    __syncthreads();
+#pragma unroll 2
+    for (int r0 = 0; r0 < kBM / 2; r0 += kRowsPerPass) {
+      const int r = r0 + t / kLpr;
+      const int64_t row = row0 + half * (kBM / 2) + r;
+      if (row >= M) continue;
+      const float4 lo = *(const float4*)(ot + r * kOS + sub * 8);
+      const float4 hi = *(const float4*)(ot + r * kOS + sub * 8 + 4);
+      float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const int64_t off = row * ldo + n0 / 8 + sub;
+      if (!UP && resid) {
+        const uint4 rv = resid[off];
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      pw[q] = (uint32_t)f32_to_bf16(y[2 * q]).bits |
-              ((uint32_t)f32_to_bf16(y[2 * q + 1]).bits << 16);
-    out[off] = uint4{pw[0], pw[1], pw[2], pw[3]};
+        for (int q = 0; q < 4; ++q) {
+          y[2 * q] += __uint_as_float(rw[q] << 16);
+          y[2 * q + 1] += __uint_as_float(rw[q] & 0xFFFF0000u);
+        }
+      }
+      uint32_t pw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        pw[q] = (uint32_t)f32_to_bf16(y[2 * q]).bits |
+                ((uint32_t)f32_to_bf16(y[2 * q + 1]).bits << 16);
+      out[off] = uint4{pw[0], pw[1], pw[2], pw[3]};
+    }
+    __syncthreads();
   }
 }
 
@@ -150,7 +160,7 @@ hipError_t launch_layer(int dtype, const void* a, const void* b, const void* bia
                         const void* resid, void* out, int64_t M, int N, int K, bool mfma,
                         hipStream_t s) {
   if (mfma) {
-    const int64_t mts = (M + kRows - 1) / kRows;
+    const int64_t mts = (M + kBM - 1) / kBM;
     const int mtl_n = (int)((mts + 7) / 8);  // row tiles per XCD
     const unsigned grid = (unsigned)((int64_t)mtl_n * 8 * (N / kBN));
     constexpr int shmem = FLds::kBytes;

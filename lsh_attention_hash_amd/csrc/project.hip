@@ -27,15 +27,15 @@ namespace {
 
 using gemm::floatx4_t;
 
-using gemm::kRows;
-using gemm::kSlab;
 using gemm::kThreads;
+constexpr int kRows = 256;  // rows of x per tile
+constexpr int kSlab = 32;   // K per LDS slab
 
 template <int D>
 struct PLds {
-  static constexpr int kBytes = gemm::Lay<D>::kBytes;
   static constexpr int kOutStride = D * 2 + 16;  // epilogue tile row (bf16, +pad)
-  static_assert(kRows * kOutStride <= kBytes, "epilogue tile fits");
+  static constexpr int kMain = gemm::Lay<kRows, D, kSlab>::kBytes;
+  static constexpr int kBytes = kMain > kRows * kOutStride ? kMain : kRows * kOutStride;
 };
 
 template <int D>
@@ -60,11 +60,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
   const uint4* wrows = (is_v ? w_v : w_qk) + (int64_t)h * D * (model_dim / 8);
   const int t = threadIdx.x;
 
-  constexpr int RT = gemm::Lay<D>::RT, CT = gemm::Lay<D>::CT;
+  constexpr int RT = gemm::Lay<kRows, D, kSlab>::RT, CT = gemm::Lay<kRows, D, kSlab>::CT;
   floatx4_t acc[RT][CT];
-  gemm::tile<D>(lds, x, row0, M, wrows, model_dim, acc);
+  gemm::tile<kRows, D, kSlab>(lds, x, row0, M, wrows, model_dim, acc);
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  const int wr = gemm::wave_row(w), wc = gemm::wave_col<D>(w);
+  const int wr = gemm::wave_row<kRows>(w), wc = gemm::wave_col<D>(w);
 
   // epilogue: lane holds rows wr + 16i + 4g + 0..3 of column wc + 16ct + lq;
   // the tile goes to LDS as bf16 rows, then out with 16 bytes per lane
