@@ -93,30 +93,32 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, windo
     }
 
 
-def backward_units(w, out_dtype: str):
+def backward_units(w, out_dtype: str, grad_row_bytes: int = 2):
     """Per-launch algorithmic work of each backward stage (matrix-core path:
-    bf16 inputs, fp32 per-round gradients). N token-heads, R rounds, d, m as
-    above; a round's window is 2m keys per query. Rows are read through the
-    permutation once per (round, slot); the per-round gradients are fp32 rows
-    at original positions."""
+    bf16 inputs, per-round gradient rows of grad_row_bytes per element: fp16
+    by default, fp32 with --fp32-round-outputs). N token-heads, R rounds, d, m
+    as above; a round's window is 2m keys per query. Rows are read through the
+    permutation once per (round, slot); the per-round gradients are rows at
+    original positions."""
     N = w.batch * w.heads * w.seq_len
     R, d, m = w.n_rounds, w.head_dim, w.chunk_len
-    e, eo = esize(w.dtype), esize(out_dtype)
+    e, eo, g = esize(w.dtype), esize(out_dtype), grad_row_bytes
     return {
         # attention at the permutation (as the forward's) with dout read per
         # query-round; per query-round lse and dout . o_r written; key norms
         "recompute": {"flops": N * R * 4 * d * 2 * m,
                       "bytes": N * R * (3 * d * e + 4 + 4 + 4) + N * (d * e + 4)},
-        # lse and dout . o_r per round, v and dout rows; round weights, dout . out
-        "rows": {"bytes": N * R * (4 + 4 + 4) + N * (2 * d * e + 4)},
+        # lse and dout . o_r read and the round weight written per round; dout . out
+        # and the self-only weight written per token-head
+        "rows": {"bytes": N * R * (4 + 4 + 4) + N * (4 + 4)},
         # per (round, slot), over the 2m-key window of each query: S, dP once,
         # then dQ, dkhat and dv; qk, v, dout rows, perm, lse, weight,
-        # dout . out and key norm read once; fp32 dqk and dv rows written
+        # dout . out and key norm read once; dqk and dv rows written
         "products": {"flops": N * R * 5 * 2 * d * 2 * m,
-                     "bytes": N * R * (3 * d * e + 5 * 4 + 2 * d * 4)},
-        # R rounds of fp32 dqk and dv rows, lse and weight; dout rows; dqk
-        # and dv written
-        "reduce": {"bytes": N * R * (2 * d * 4 + 8) + N * d * e + N * 2 * d * eo},
+                     "bytes": N * R * (3 * d * e + 5 * 4 + 2 * d * g)},
+        # R rounds of dqk and dv rows and the self-only weight read; dqk and dv
+        # written (dout is read only for rows with a self-only round)
+        "reduce": {"bytes": N * R * 2 * d * g + N * 4 + N * 2 * d * eo},
     }
 
 
@@ -312,7 +314,7 @@ def main_backward(args, w, inp, op_kw):
     op.close()
     calibration_copy(args.calib_copy_mib, dev)
 
-    units = backward_units(w, w.dtype)
+    units = backward_units(w, w.dtype, 4 if args.fp32_round_outputs else 2)
     single = {k: v_ for k, v_ in stage_avg.items() if k in BWD_STAGE_KERNEL}
     dominant = max(single, key=single.get)
     traffic = None
@@ -352,7 +354,7 @@ def main_backward(args, w, inp, op_kw):
                    "qk_v_dtype": w.dtype,
                    "inputs": f"{w.kind} seeded (qk {1000 + w.seed_base}, v {2000 + w.seed_base},"
                              f" R {3000 + w.seed_base}); dout torch seed 5, standard normal",
-                   "per_round_gradients": "fp32"},
+                   "per_round_gradients": "fp32" if args.fp32_round_outputs else "fp16"},
         "roofline": rl,
         "stages": per_stage,
         "wall_s_timed": round(wall, 4),

@@ -310,20 +310,21 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
   store8(dv + row * D + sub * 8, gv);
 }
 
-// The same on the matrix-core path, whose per-round rows already hold
-// dq + the normalised key gradient (dqk_r) and dv_r: sums over rounds plus the
-// self-only value term wself dout. kR > 0: R == kR and every load is issued
-// before the sums; kR == 0: any R. Each per-round row is read once
-// (non-temporal); blocks take the rows from the end, which the product kernel
-// wrote last.
-template <int D, typename T, int kR>
+// The same on the matrix-core path, whose per-round rows (GT: fp16 or fp32)
+// already hold dq + the normalised key gradient (dqk_r) and dv_r: sums over
+// rounds in fp32 plus the self-only value term wself dout. kR > 0: R == kR
+// and every load is issued before the sums; kR == 0: any R. Each per-round row
+// is read once (non-temporal); blocks take the rows from the end, which the
+// product kernel wrote last.
+template <int D, typename T, int kR, typename GT>
 __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ dout,
                                                         const float* __restrict__ wself,
-                                                        const float* __restrict__ dqkr,
-                                                        const float* __restrict__ dvr,
+                                                        const GT* __restrict__ dqkr,
+                                                        const GT* __restrict__ dvr,
                                                         T* __restrict__ dqk, T* __restrict__ dv,
                                                         int L, int R_rt, int64_t n_rows) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
   constexpr int kLpr = D / 8;
   constexpr int kG = kR > 0 ? kR : 1;
   const int R = kR > 0 ? kR : R_rt;
@@ -335,26 +336,43 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
   float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float ws = wself[row];
   for (int r0 = 0; r0 < R; r0 += kG) {
-    f32x4_t a[kG][2], c[kG][2];
+    if constexpr (sizeof(GT) == 4) {
+      f32x4_t a[kG][2], c[kG][2];
 #pragma unroll
-    for (int u = 0; u < kG; ++u) {
-      const int64_t sr = (bh * R + r0 + u) * L + j;
-      const f32x4_t* pa = (const f32x4_t*)(dqkr + sr * D + sub * 8);
-      const f32x4_t* pc = (const f32x4_t*)(dvr + sr * D + sub * 8);
-      a[u][0] = __builtin_nontemporal_load(pa);
-      a[u][1] = __builtin_nontemporal_load(pa + 1);
-      c[u][0] = __builtin_nontemporal_load(pc);
-      c[u][1] = __builtin_nontemporal_load(pc + 1);
-    }
-#pragma unroll
-    for (int u = 0; u < kG; ++u)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        gq[k] += a[u][0][k];
-        gq[4 + k] += a[u][1][k];
-        gv[k] += c[u][0][k];
-        gv[4 + k] += c[u][1][k];
+      for (int u = 0; u < kG; ++u) {
+        const int64_t sr = (bh * R + r0 + u) * L + j;
+        const f32x4_t* pa = (const f32x4_t*)(dqkr + sr * D + sub * 8);
+        const f32x4_t* pc = (const f32x4_t*)(dvr + sr * D + sub * 8);
+        a[u][0] = __builtin_nontemporal_load(pa);
+        a[u][1] = __builtin_nontemporal_load(pa + 1);
+        c[u][0] = __builtin_nontemporal_load(pc);
+        c[u][1] = __builtin_nontemporal_load(pc + 1);
       }
+#pragma unroll
+      for (int u = 0; u < kG; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          gq[k] += a[u][0][k];
+          gq[4 + k] += a[u][1][k];
+          gv[k] += c[u][0][k];
+          gv[4 + k] += c[u][1][k];
+        }
+    } else {
+      h8_t a[kG], c[kG];
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const int64_t sr = (bh * R + r0 + u) * L + j;
+        a[u] = __builtin_nontemporal_load((const h8_t*)(dqkr + sr * D + sub * 8));
+        c[u] = __builtin_nontemporal_load((const h8_t*)(dvr + sr * D + sub * 8));
+      }
+#pragma unroll
+      for (int u = 0; u < kG; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          gq[k] += (float)a[u][k];
+          gv[k] += (float)c[u][k];
+        }
+    }
   }
   if (ws > 0.f) {
     float dz[8];
@@ -386,10 +404,19 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
   if (attend_mfma_supported(p)) {
     (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
     mark(3);
+    const bool half = bwd_rows_half(p);
     auto go = [&](auto r) {
       constexpr int kR = decltype(r)::value;
-      hipLaunchKernelGGL((k_bwd_reduce_sum<D, T, kR>), gt, dim3(256), 0, s, (const T*)dout,
-                         b.wself, b.dq, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
+      if (half) {
+        auto kern = k_bwd_reduce_sum<D, T, kR, _Float16>;
+        hipLaunchKernelGGL(kern, gt, dim3(256), 0, s, (const T*)dout, b.wself,
+                           (const _Float16*)b.dq, (const _Float16*)b.dv, (T*)dqk, (T*)dvo, p.L,
+                           p.R, nt);
+      } else {
+        auto kern = k_bwd_reduce_sum<D, T, kR, float>;
+        hipLaunchKernelGGL(kern, gt, dim3(256), 0, s, (const T*)dout, b.wself, b.dq, b.dv,
+                           (T*)dqk, (T*)dvo, p.L, p.R, nt);
+      }
     };
     switch (p.R) {
       case 1: go(std::integral_constant<int, 1>{}); break;

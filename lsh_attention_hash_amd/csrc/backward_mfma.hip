@@ -24,6 +24,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;
+
+// four floats as fp16 (round to nearest even), packed in 8 bytes
+__device__ __forceinline__ uint2 pack_h4(float a, float b, float c, float d) {
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const h2_t lo = {(_Float16)a, (_Float16)b}, hi = {(_Float16)c, (_Float16)d};
+  return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -46,7 +53,9 @@ using rows::zero_lds;
 // dq and dkhat of the same 16 positions (the rows of block w of chunk c - 1),
 // applies the key normalisation's Jacobian per round,
 //   dqk_r = dq_r + (dkhat_r - khat (khat . dkhat_r)) / |k|,
-// and writes dqk_r and dv_r once (fp32, original positions). A range's last
+// and writes dqk_r and dv_r once (at original positions, in GT: fp16 by
+// default, which halves this kernel's largest output and the reduction's
+// reads, or fp32 with LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS). A range's last
 // step takes the queries of the chunk after it for its last keys only; the
 // next range computes their dq. The next chunk's rows are loaded into
 // registers at the start of each step and staged after it.
@@ -79,12 +88,12 @@ struct FRegs {
 constexpr int kFusedRange = 16;
 constexpr int kFusedResident = 256;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename GT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void k_bwd_fused_mfma(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const unsigned char* __restrict__ dout, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
-    const float* __restrict__ cq, float* __restrict__ dqk_r, float* __restrict__ dv_r, int L,
+    const float* __restrict__ cq, GT* __restrict__ dqk_r, GT* __restrict__ dv_r, int L,
     int R, int nseg, int chunks_per_wg, int ranges, int group_segs) {
   using Lay = BLay<D>;
   using M = FLds<D>;
@@ -400,16 +409,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     proj += __shfl_xor(proj, 16);
     proj += __shfl_xor(proj, 32);
     proj *= rn * inv_sqrt_d;  // khat . dkhat
-    float* qo = dqk_r + (seg * L + pos) * D + 4 * g;
-    float* vo = dv_r + (seg * L + pos) * D + 4 * g;
+    GT* qo = dqk_r + (seg * L + pos) * D + 4 * g;
+    GT* vo = dv_r + (seg * L + pos) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       float o[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         o[b] = dqa[dt][b] + (dka[dt][b] * inv_sqrt_d - kv[dt][b] * rn * proj) * rn;
-      *(float4*)(qo + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
-      *(float4*)(vo + 16 * dt) = make_float4(dva[dt][0], dva[dt][1], dva[dt][2], dva[dt][3]);
+      if constexpr (sizeof(GT) == 4) {
+        *(float4*)(qo + 16 * dt) = make_float4(o[0], o[1], o[2], o[3]);
+        *(float4*)(vo + 16 * dt) = make_float4(dva[dt][0], dva[dt][1], dva[dt][2], dva[dt][3]);
+      } else {
+        *(uint2*)(qo + 16 * dt) = pack_h4(o[0], o[1], o[2], o[3]);
+        *(uint2*)(vo + 16 * dt) = pack_h4(dva[dt][0], dva[dt][1], dva[dt][2], dva[dt][3]);
+      }
     }
   };
 
@@ -464,7 +478,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   if (c1 == nchunks) finish((c1 - 1) & 1);  // the last chunk's keys see no later queries
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename GT>
 void launch_fused(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                   const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
   const int nchunks = p.L / kChunk;
@@ -475,18 +489,31 @@ void launch_fused(const Problem& p, const void* qk, const void* v, const int32_t
   if (heads < 1) heads = 1;
   int64_t group_segs = heads * p.R;
   if (group_segs > nseg) group_segs = nseg;
-  hipLaunchKernelGGL((k_bwd_fused_mfma<D, CAUSAL>), dim3((unsigned)(nseg * ranges)),
-                     dim3(kThreads), FLds<D>::kBytes, s, (const unsigned char*)qk,
-                     (const unsigned char*)v, (const unsigned char*)dout, perm, knorm, b.lse,
-                     b.w, b.cq, b.dq, b.dv, p.L, p.R, (int)nseg, per, ranges, (int)group_segs);
+  auto kern = k_bwd_fused_mfma<D, CAUSAL, GT>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(nseg * ranges)), dim3(kThreads), FLds<D>::kBytes, s,
+                     (const unsigned char*)qk, (const unsigned char*)v,
+                     (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, (GT*)b.dq,
+                     (GT*)b.dv, p.L, p.R, (int)nseg, per, ranges, (int)group_segs);
 }
 
-template <int D>
+template <int D, typename GT>
 void configure() {
-  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, true>,
+  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, true, GT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, FLds<D>::kBytes);
-  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, false>,
+  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, false, GT>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, FLds<D>::kBytes);
+}
+
+template <typename GT>
+void launch_gt(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+               const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
+  if (p.d == 64) {
+    if (p.causal) launch_fused<64, true, GT>(p, qk, v, perm, dout, knorm, b, s);
+    else launch_fused<64, false, GT>(p, qk, v, perm, dout, knorm, b, s);
+  } else {
+    if (p.causal) launch_fused<128, true, GT>(p, qk, v, perm, dout, knorm, b, s);
+    else launch_fused<128, false, GT>(p, qk, v, perm, dout, knorm, b, s);
+  }
 }
 
 }  // namespace
@@ -496,17 +523,14 @@ hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 BwdWorkspace& b, hipStream_t s) {
   static bool configured = false;
   if (!configured) {
-    configure<64>();
-    configure<128>();
+    configure<64, float>();
+    configure<128, float>();
+    configure<64, _Float16>();
+    configure<128, _Float16>();
     configured = true;
   }
-  if (p.d == 64) {
-    if (p.causal) launch_fused<64, true>(p, qk, v, perm, dout, knorm, b, s);
-    else launch_fused<64, false>(p, qk, v, perm, dout, knorm, b, s);
-  } else {
-    if (p.causal) launch_fused<128, true>(p, qk, v, perm, dout, knorm, b, s);
-    else launch_fused<128, false>(p, qk, v, perm, dout, knorm, b, s);
-  }
+  if (bwd_rows_half(p)) launch_gt<_Float16>(p, qk, v, perm, dout, knorm, b, s);
+  else launch_gt<float>(p, qk, v, perm, dout, knorm, b, s);
   return hipGetLastError();
 }
 

@@ -72,9 +72,10 @@ struct BwdWorkspace {
   float* cq = nullptr;   // [B*H, L] dout . out
   float* wself = nullptr;  // [B*H, L] summed weight of the self-only rounds (matrix-core path)
   float* dq = nullptr;   // [seg, L, d] per-round dq at original positions (matrix-core
-                         // path: dq plus the normalised key gradient, dqk per round)
+                         // path: dq plus the normalised key gradient, dqk per round;
+                         // fp16 when bwd_rows_half)
   float* dk = nullptr;   // [seg, L, d] per-round d(unit key) (plain path)
-  float* dv = nullptr;   // [seg, L, d] per-round dv
+  float* dv = nullptr;   // [seg, L, d] per-round dv (fp16 when bwd_rows_half)
 };
 
 // Kernel launchers (each defined next to its kernels). All enqueue on `s` and
@@ -160,6 +161,12 @@ constexpr int kVariantFlags = LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_SAME_BUCK
 inline bool round_outputs_half(const Problem& p) {
   return (attend_mfma_supported(p) || attend_variant_mfma_supported(p)) &&
          !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
+}
+
+// The backward's per-round gradient rows (dqk_r, dv_r) on the matrix-core path
+// are kept in fp16 under the same rule; otherwise fp32.
+inline bool bwd_rows_half(const Problem& p) {
+  return attend_mfma_supported(p) && !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
 }
 
 }  // namespace lsh

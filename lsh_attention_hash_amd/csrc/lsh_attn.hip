@@ -167,9 +167,9 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
          alloc(&b.lse, rows * 4, t) &&
          alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
          alloc(&b.wself, p.n_token_heads() * 4, t) &&
-         alloc(&b.dq, rows * p.d * 4, t) &&
+         alloc(&b.dq, rows * p.d * (lsh::bwd_rows_half(p) ? 2 : 4), t) &&
          (lsh::attend_mfma_supported(p) || alloc(&b.dk, rows * p.d * 4, t)) &&
-         alloc(&b.dv, rows * p.d * 4, t);
+         alloc(&b.dv, rows * p.d * (lsh::bwd_rows_half(p) ? 2 : 4), t);
   }
   if (!ok) {
     free_bw(h->bw);

@@ -5,7 +5,9 @@ exact values the GPU sees. Each case prints what it is before it runs.
 
 Tolerance: the gradients come back in the input dtype. For bf16 that
 rounding alone is up to 2^-8 of each value (the unit roundoff of an 8-bit
-significand); the rest (fp32 sums, the recomputed attention's bf16 products)
+significand); the rest (fp32 sums, the recomputed attention's bf16 products,
+and on the matrix-core path the per-round gradient rows held in fp16, 2^-11
+of each row value, unless LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS keeps them in fp32)
 is bounded by a small fraction of the largest gradient. So
 |g - g_ref| <= 2^-8 |g_ref| + 1e-2 max|g_ref| per element for bf16, and
 1e-4 max|g_ref| for fp32.
@@ -80,14 +82,15 @@ BWD = [
 
 @pytest.mark.parametrize("w", BWD, ids=lambda w: f"{w.name}-{w.dtype}-H{w.heads}L{w.seq_len}"
                          f"d{w.head_dim}nb{w.n_buckets}R{w.n_rounds}{'c' if w.causal else 'n'}")
-def test_backward_parity(w):
-    _say(f"[backward] {w}")
+def test_backward_parity(w, fp32_rows=False):
+    _say(f"[backward] {w} fp32 round rows={fp32_rows}")
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda", 0)
     qk, v, rot = to_device(inp, dev)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
-                          w.chunk_len, w.causal, dtype=dt, backward=True)
+                          w.chunk_len, w.causal, dtype=dt, backward=True,
+                          fp32_round_outputs=fp32_rows)
     try:
         _, ex = op(qk, v, rot, return_perm=True)
         dout_t, dout = _dout(w, 9000 + w.seq_len + w.n_rounds)
@@ -168,3 +171,11 @@ def test_backward_full_size_sampled_heads():
                              np.ascontiguousarray(dout[:1, heads]))
     _check("dqk", dqk[:1, heads], rq, True)
     _check("dv", dv[:1, heads], rv, True)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_parity_fp32_round_rows(causal):
+    """The per-round gradient rows kept in fp32 (LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS)
+    instead of the default fp16: the same parity."""
+    test_backward_parity(W("text64k", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=4,
+                           causal=causal), fp32_rows=True)
