@@ -206,7 +206,7 @@ struct lsh_ffn_s {
 namespace {
 
 void ffn_destroy_events(lsh_ffn_s* h) {
-  for (hipEvent_t e : h->events) hipEventDestroy(e);
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
   h->events.clear();
   h->chunks.clear();
   h->timing_capacity = 0;
@@ -284,7 +284,7 @@ int lsh_ffn_forward(lsh_ffn_t h, int64_t rows, const void* y1, const void* w1, c
     h->chunks[h->timed] = nch;
     ++h->timed;
   }
-  if (ev) hipEventRecord(ev[0], s);
+  if (ev) (void)hipEventRecord(ev[0], s);
   hipError_t e = hipSuccess;
   for (int ci = 0; ci < nch && e == hipSuccess; ++ci) {
     const int64_t c0 = ci * h->chunk;
@@ -292,13 +292,13 @@ int lsh_ffn_forward(lsh_ffn_t h, int64_t rows, const void* y1, const void* w1, c
     const char* in = (const char*)y1 + c0 * c.d_model * esize;
     e = lsh::launch_layer<true>(c.dtype, in, w1, b1, nullptr, h->hidden, n, c.d_ff, c.d_model,
                                 mfma, s);
-    if (ev) hipEventRecord(ev[2 * ci + 1], s);
+    if (ev) (void)hipEventRecord(ev[2 * ci + 1], s);
     if (e != hipSuccess) break;
     const char* res = x2 ? (const char*)x2 + c0 * c.d_model * esize : nullptr;
     char* o = (char*)y2 + c0 * c.d_model * esize;
     e = lsh::launch_layer<false>(c.dtype, h->hidden, w2, b2, res, o, n, c.d_model, c.d_ff, mfma,
                                  s);
-    if (ev) hipEventRecord(ev[2 * ci + 2], s);
+    if (ev) (void)hipEventRecord(ev[2 * ci + 2], s);
   }
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -370,8 +370,8 @@ int lsh_ffn_destroy(lsh_ffn_t h) {
                         hipSetDevice(h->device) == hipSuccess;
   const hipError_t e = hipDeviceSynchronize();
   ffn_destroy_events(h);
-  hipFree(h->hidden);
-  if (switched) hipSetDevice(prev);
+  (void)hipFree(h->hidden);
+  if (switched) (void)hipSetDevice(prev);
   delete h;
   if (e != hipSuccess) {
     (void)hipGetLastError();
