@@ -168,7 +168,7 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
 # and the source files each stage's kernels are built from.
 STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine",
                 "project": "k_proj_mfma"}
-FFN_STAGE_KERNEL = {"ffn_up": "k_ffn_mfma<true>", "ffn_down": "k_ffn_mfma<false>"}
+FFN_STAGE_KERNEL = {"ffn_up": "k_ffn_mfma<true, 256>", "ffn_down": "k_ffn_mfma<false, 256>"}
 BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "products": "k_bwd_fused_mfma",
                     "reduce": "k_bwd_reduce_sum"}
 STAGE_SOURCES = {

@@ -12,9 +12,11 @@
 // Per chunk two launches: the first layer writes the chunk's hidden rows
 // (bias and ReLU in the epilogue, rounded to the layer dtype) into the
 // handle's buffer of chunk_rows x d_ff, and the second layer reads them back
-// (bias and residual in its epilogue). Both are the 256 x 128 tile of
-// gemm_core.h (K slabs of 32, two workgroups per CU) on matrix cores for bf16
-// with d_model and d_ff multiples of 128;
+// (bias and residual in its epilogue). Both use the tile of gemm_core.h with K
+// slabs of 32 on matrix cores for bf16 with d_model and d_ff multiples of
+// 128: 256 x 256 tiles of 8 waves (one workgroup per CU) for layers whose
+// output width is a multiple of 256, else 256 x 128 tiles of 4 waves (two
+// workgroups per CU);
 // other shapes and fp32 use a plain kernel (one thread per output element).
 // A row's result does not depend on the chunk it falls in: every output
 // element is summed over K in the same order in any tile.
@@ -28,24 +30,38 @@ namespace lsh {
 namespace {
 
 using gemm::floatx4_t;
-using gemm::kThreads;
 
 constexpr int kBM = 256;       // rows per tile
-constexpr int kBN = 128;       // output columns per tile
 constexpr int kKSlab = 32;     // K per LDS slab
 constexpr int kGroupRows = 8;  // row tiles per group in an XCD's tile order
-using Tile = gemm::Lay<kBM, kBN, kKSlab>;
 
+// Tile shape per output-column width BN: the wave grid (WM x WN waves) and
+// the workgroups per CU the registers and LDS allow.
+template <int BN>
+struct FCfg;
+template <>
+struct FCfg<128> {
+  static constexpr int WM = 2, WN = 2, kPerCU = 2;
+};
+template <>
+struct FCfg<256> {
+  static constexpr int WM = 4, WN = 2, kPerCU = 1;
+};
+
+template <int BN>
 struct FLds {
-  static constexpr int kOutStride = kBN * 4 + 16;  // epilogue half-tile row (fp32, +pad)
-  static constexpr int kHalf = kBM / 2 * kOutStride;
-  static constexpr int kBytes = Tile::kBytes > kHalf ? Tile::kBytes : kHalf;
+  using C = FCfg<BN>;
+  using Tile = gemm::Lay<kBM, BN, kKSlab, C::WM, C::WN>;
+  static constexpr int kThr = Tile::kThr;
+  static constexpr int kOutStride = BN * 4 + 16;  // epilogue slice row (fp32, +pad)
+  static constexpr int kSlice = kBM / C::WM * kOutStride;  // one wave row's slice
+  static constexpr int kBytes = Tile::kBytes > kSlice ? Tile::kBytes : kSlice;
 };
 
 // out[M, N] = epilogue(a[M, K] b[N, K]^T + bias[N]); UP: ReLU, else + resid
-// (resid [M, N] or null). Row-major bf16, N a multiple of 128, K of 32.
-template <bool UP>
-__global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(
+// (resid [M, N] or null). Row-major bf16, N a multiple of BN, K of 32.
+template <bool UP, int BN>
+__global__ __launch_bounds__(FLds<BN>::kThr, FCfg<BN>::kPerCU) void k_ffn_mfma(
     const uint4* __restrict__ a, const uint4* __restrict__ b, const bf16_t* __restrict__ bias,
     const uint4* resid, uint4* out, int64_t M, int N, int K,
     int mtl_n) {
@@ -54,7 +70,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(
   // x owns row tiles x, x + 8, ... Inside an XCD, tiles go in groups of
   // kGroupRows row tiles, row-fastest, so that the workgroups resident at
   // once share a few rows of a and a few column tiles of b in its L2.
-  const int nts = N / kBN;
+  using C = FCfg<BN>;
+  using Tile = typename FLds<BN>::Tile;
+  constexpr int kThr = FLds<BN>::kThr;
+  const int nts = N / BN;
   const int xcd = (int)(blockIdx.x % 8u);
   const int k = (int)(blockIdx.x / 8u);
   const int grp = k / (kGroupRows * nts);
@@ -64,30 +83,30 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(
   const int nt = rem / gm;
   const int64_t row0 = mt * kBM;
   if (row0 >= M) return;
-  const int n0 = nt * kBN;
+  const int n0 = nt * BN;
 
   constexpr int RT = Tile::RT, CT = Tile::CT;
   floatx4_t acc[RT][CT];
-  gemm::tile<kBM, kBN, kKSlab>(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
+  gemm::tile<kBM, BN, kKSlab, C::WM, C::WN>(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  const int wc = gemm::wave_col<kBN>(w);
+  const int wc = gemm::wave_col<BN, C::WN>(w);
 
-  // epilogue in two halves of kBM / 2 rows (waves 0-1, then 2-3): bias (and
-  // ReLU) on the lane's elements, the half tile to LDS in fp32, then out by
+  // epilogue in slices of kBM / WM rows (one row of waves at a time): bias
+  // (and ReLU) on the lane's elements, the slice to LDS in fp32, then out by
   // rows, 8 elements (16 bytes of output) per lane
   float* ot = (float*)lds;
-  constexpr int kOS = FLds::kOutStride / 4;
+  constexpr int kOS = FLds<BN>::kOutStride / 4;
   float bv[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) bv[ct] = to_f32(bias[n0 + wc + 16 * ct + lq]);
-  constexpr int kLpr = kBN / 8;  // lanes per row
-  constexpr int kRowsPerPass = kThreads / kLpr;
+  constexpr int kLpr = BN / 8;  // lanes per row
+  constexpr int kRowsPerPass = kThr / kLpr;
   const int sub = t % kLpr;
   const int64_t ldo = N / 8;  // 16-byte pieces per output row
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if ((w >> 1) == half) {
+  for (int half = 0; half < C::WM; ++half) {
+    if (w / C::WN == half) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -101,9 +120,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(
     }
     __syncthreads();
 #pragma unroll 2
-    for (int r0 = 0; r0 < kBM / 2; r0 += kRowsPerPass) {
+    for (int r0 = 0; r0 < kBM / C::WM; r0 += kRowsPerPass) {
       const int r = r0 + t / kLpr;
-      const int64_t row = row0 + half * (kBM / 2) + r;
+      const int64_t row = row0 + half * (kBM / C::WM) + r;
       if (row >= M) continue;
       const float4 lo = *(const float4*)(ot + r * kOS + sub * 8);
       const float4 hi = *(const float4*)(ot + r * kOS + sub * 8 + 4);
@@ -151,7 +170,22 @@ __global__ __launch_bounds__(256) void k_ffn_simple(const T* __restrict__ a,
 }
 
 bool ffn_mfma_supported(int dtype, int d_model, int d_ff) {
-  return dtype == LSH_ATTN_BF16 && d_model % kBN == 0 && d_ff % kBN == 0;
+  return dtype == LSH_ATTN_BF16 && d_model % 128 == 0 && d_ff % 128 == 0;
+}
+
+template <bool UP, int BN>
+void launch_mfma(const void* a, const void* b, const void* bias, const void* resid, void* out,
+                 int64_t M, int N, int K, hipStream_t s) {
+  const int64_t mts = (M + kBM - 1) / kBM;
+  const int mtl_n = (int)((mts + 7) / 8);  // row tiles per XCD
+  const unsigned grid = (unsigned)((int64_t)mtl_n * 8 * (N / BN));
+  constexpr int shmem = FLds<BN>::kBytes;
+  auto kern = k_ffn_mfma<UP, BN>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            shmem);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(FLds<BN>::kThr), shmem, s, (const uint4*)a,
+                     (const uint4*)b, (const bf16_t*)bias, (const uint4*)resid, (uint4*)out, M,
+                     N, K, mtl_n);
 }
 
 // One layer over M rows: out = epilogue(a b^T + bias).
@@ -160,15 +194,8 @@ hipError_t launch_layer(int dtype, const void* a, const void* b, const void* bia
                         const void* resid, void* out, int64_t M, int N, int K, bool mfma,
                         hipStream_t s) {
   if (mfma) {
-    const int64_t mts = (M + kBM - 1) / kBM;
-    const int mtl_n = (int)((mts + 7) / 8);  // row tiles per XCD
-    const unsigned grid = (unsigned)((int64_t)mtl_n * 8 * (N / kBN));
-    constexpr int shmem = FLds::kBytes;
-    (void)hipFuncSetAttribute((const void*)k_ffn_mfma<UP>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
-    hipLaunchKernelGGL(k_ffn_mfma<UP>, dim3(grid), dim3(kThreads), shmem, s, (const uint4*)a,
-                       (const uint4*)b, (const bf16_t*)bias, (const uint4*)resid, (uint4*)out,
-                       M, N, K, mtl_n);
+    if (N % 256 == 0) launch_mfma<UP, 256>(a, b, bias, resid, out, M, N, K, s);
+    else launch_mfma<UP, 128>(a, b, bias, resid, out, M, N, K, s);
   } else {
     const dim3 grid((unsigned)((M * N + 255) / 256));
     if (dtype == LSH_ATTN_BF16) {

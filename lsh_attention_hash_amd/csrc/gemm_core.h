@@ -2,7 +2,8 @@
 // A [M, K] and B [N, K] bf16 row-major (K contiguous; B is a linear layer's
 // weight), fp32 accumulators, v_mfma_f32_16x16x32_bf16.
 //
-// A workgroup of 4 waves as 2 x 2 blocks of BM/2 rows x BN/2 columns. K goes
+// A workgroup of WM x WN waves (4 by default), each owning a block of BM/WM
+// rows x BN/WN columns. K goes
 // in slabs of SLAB (32 or 64), double-buffered in LDS (rows of A and of B, K
 // contiguous, +16-byte pad: the 16 lanes of a fragment read distinct bank
 // groups), with the next two slabs in flight in two named register sets while
@@ -21,33 +22,35 @@ namespace gemm {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // threads of the default 2 x 2 wave grid
 
-template <int BM, int BN, int SLAB>
+template <int BM, int BN, int SLAB, int WM = 2, int WN = 2>
 struct Lay {
+  static constexpr int kThr = 64 * WM * WN;
   static constexpr int kStride = SLAB * 2 + 16;     // bytes per staged row (+16 pad)
   static constexpr int kA = 0;                      // [2][BM] rows of A
   static constexpr int kB = kA + 2 * BM * kStride;  // [2][BN] rows of B
   static constexpr int kBytes = kB + 2 * BN * kStride;
-  static constexpr int RT = BM / 32;                // 16-row tiles per wave
-  static constexpr int CT = BN / 32;                // 16-column tiles per wave
+  static constexpr int RT = BM / WM / 16;           // 16-row tiles per wave
+  static constexpr int CT = BN / WN / 16;           // 16-column tiles per wave
 };
 
 // The lane's outputs: acc[i][ct][u] is row wave_row<BM>(w) + 16i + 4(lane/16) + u,
 // column wave_col<BN>(w) + 16ct + lane%16 of the tile.
-template <int BM>
-__device__ __forceinline__ int wave_row(int w) { return (BM / 2) * (w >> 1); }
-template <int BN>
-__device__ __forceinline__ int wave_col(int w) { return (BN / 2) * (w & 1); }
+template <int BM, int WM = 2, int WN = 2>
+__device__ __forceinline__ int wave_row(int w) { return (BM / WM) * (w / WN); }
+template <int BN, int WN = 2>
+__device__ __forceinline__ int wave_col(int w) { return (BN / WN) * (w % WN); }
 
 // A B^T for rows row0 .. row0 + BM - 1 of A and the BN rows of B at brows (K a
 // multiple of SLAB). Ends with a barrier: the LDS may be reused at once.
-template <int BM, int BN, int SLAB>
+template <int BM, int BN, int SLAB, int WM = 2, int WN = 2>
 __device__ __forceinline__ void tile(unsigned char* lds, const uint4* __restrict__ a,
                                      int64_t row0, int64_t M, const uint4* __restrict__ brows,
                                      int K,
-                                     floatx4_t (&acc)[Lay<BM, BN, SLAB>::RT][Lay<BM, BN, SLAB>::CT]) {
-  using L = Lay<BM, BN, SLAB>;
+                                     floatx4_t (&acc)[Lay<BM, BN, SLAB, WM, WN>::RT][Lay<BM, BN, SLAB, WM, WN>::CT]) {
+  using L = Lay<BM, BN, SLAB, WM, WN>;
+  constexpr int kThreads = L::kThr;
   constexpr int kP = SLAB / 8;               // 16-byte pieces per staged row
   constexpr int kStride = L::kStride;
   constexpr int kAPer = BM * kP / kThreads;  // 16-byte pieces of the A slab per thread
@@ -93,7 +96,7 @@ __device__ __forceinline__ void tile(unsigned char* lds, const uint4* __restrict
   };
 
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
-  const int wr = wave_row<BM>(w), wc = wave_col<BN>(w);
+  const int wr = wave_row<BM, WM, WN>(w), wc = wave_col<BN, WN>(w);
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
