@@ -105,11 +105,13 @@ def test_ffn_parity(rows, d_model, d_ff, chunk, dtype, residual):
 
 
 def test_ffn_chunking_changes_no_bit():
+    """Chunks of one row up to all rows (one-row chunks: a tile with a single
+    live row; 7: every tile ragged) give the same bits."""
     fi = workloads.make_ffn_inputs(1000, 256, 1024, "bf16", seed=11)
-    _say("[ffn chunks] rows=1000 d_model=256 d_ff=1024, chunks 0, 128, 200, 999")
+    _say("[ffn chunks] rows=1000 d_model=256 d_ff=1024, chunks 0, 1, 7, 128, 200, 999")
     t = _tensors(fi)
     base = _gpu(fi, 0, t=t)
-    for chunk in (128, 200, 999):
+    for chunk in (1, 7, 128, 200, 999):
         np.testing.assert_array_equal(_gpu(fi, chunk, t=t), base)
 
 
