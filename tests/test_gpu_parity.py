@@ -183,3 +183,24 @@ def test_forward_rejects_null_and_misaligned_pointers():
                                 P(rot.data_ptr()), P(out.data_ptr()), None, None, None, s) == 1
     assert op.workspace_bytes() > 0
     op.close()
+
+
+@pytest.mark.parametrize("L", [65536, 131072])
+def test_sort_of_long_segments(L):
+    """Segments of 64 and 128 sort tiles (L above the bench's 65,536 too):
+    buckets against the oracle's hash, the permutation equal to the oracle's
+    stable sort."""
+    w = W("c4k", batch=1, heads=1, seq_len=L, n_buckets=256, n_rounds=1, causal=False)
+    _say(f"[long sort] {w}")
+    inp = workloads.make_inputs(w)
+    qk, v, rot = to_device(inp)
+    op = make_op(w)
+    try:
+        _, ex = op(qk, v, rot, return_buckets=True, return_perm=True)
+        torch.cuda.synchronize()
+        gb = ex["buckets"].cpu().numpy()
+        gp = ex["perm"].cpu().numpy()
+    finally:
+        op.close()
+    check_buckets(w, inp, gb)
+    check_perm(w, gb, gp)
