@@ -91,6 +91,8 @@ CASES = [
     (1000, 384, 1536, 333, "bf16", True),   # several tiles per chunk, odd chunk size
     (200, 96, 200, 64, "bf16", True),       # off the matrix-core path (plain kernel)
     (150, 64, 256, 50, "fp32", True),       # fp32 (plain kernel)
+    (1, 256, 512, 0, "bf16", True),         # a single row
+    (257, 256, 768, 0, "bf16", True),       # one row past a 256-row tile
 ]
 
 
