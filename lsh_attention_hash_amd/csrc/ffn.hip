@@ -181,8 +181,12 @@ void launch_mfma(const void* a, const void* b, const void* bias, const void* res
   const unsigned grid = (unsigned)((int64_t)mtl_n * 8 * (N / BN));
   constexpr int shmem = FLds<BN>::kBytes;
   auto kern = k_ffn_mfma<UP, BN>;
-  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            shmem);
+  static bool configured = false;  // once per kernel (a repeated set is harmless)
+  if (!configured) {
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              shmem);
+    configured = true;
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(FLds<BN>::kThr), shmem, s, (const uint4*)a,
                      (const uint4*)b, (const bf16_t*)bias, (const uint4*)resid, (uint4*)out, M,
                      N, K, mtl_n);
