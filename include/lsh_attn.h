@@ -150,7 +150,7 @@ int lsh_attn_forward(lsh_attn_t handle, const void* qk, const void* v, const flo
  *            a later backward), rounded from fp32 sums
  *   rotations, out, lse, buckets, perm    as for lsh_attn_forward
  * On the matrix-core path (bf16, head_dim 64 or 128, model_dim a multiple of
- * 64, and the hash on matrix cores) the projection kernel also writes the
+ * 32, and the hash on matrix cores) the projection kernel also writes the
  * hash's fp16 copy of qk and its norms, which the hash then does not recompute.
  * Device pointers, all 16-byte aligned. No allocation, no host
  * synchronisation; timing stage 7 is the projection.

@@ -8,7 +8,7 @@
 // weight, model_dim -> H d features), qk and v written as [B, H, L, d] in the
 // input dtype.
 //
-// Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 64): one
+// Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 32): one
 // workgroup computes a 128-row x d-column tile of one head's qk or v with the
 // tile of gemm_core.h (the 2H tiles of a row tile run on one XCD, one after
 // the other, so the x tile is read from HBM once and from that XCD's L2 by

@@ -100,6 +100,7 @@ CASES = [
     (W("c4k", batch=2, heads=2, seq_len=192, n_buckets=8, n_rounds=2), 64),
     (W("c4k", batch=1, heads=2, seq_len=256, n_buckets=8, n_rounds=2), 80),   # plain kernel
     (W("tiny", n_rounds=2), 96),                                            # fp32
+    (W("c4k", batch=1, heads=2, seq_len=256, n_buckets=8, n_rounds=2), 96),   # 3 K slabs of 32
 ]
 
 
