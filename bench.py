@@ -33,6 +33,15 @@ if ROOT not in sys.path:
 
 METRIC = "LSH-attn fwd tokens/sec at L=64K, 4 rounds; % MFMA / HBM roofline"
 METRIC_BWD = "LSH-attn bwd tokens/sec at L=64K, 4 rounds; % MFMA / HBM roofline"
+
+
+def metric_name(w, direction: str) -> str:
+    """The headline metric for the 64K-token, 4-round workload; the same
+    metric at the other workloads' length and round count."""
+    if w.seq_len == 65536 and w.n_rounds == 4:
+        return METRIC if direction == "fwd" else METRIC_BWD
+    L = f"{w.seq_len // 1024}K" if w.seq_len % 1024 == 0 else str(w.seq_len)
+    return f"LSH-attn {direction} tokens/sec at L={L}, {w.n_rounds} rounds; % MFMA / HBM roofline"
 METRIC_FFN = "chunked feed-forward tokens/sec at L=64K; % MFMA roofline"
 
 # MI355X published peaks
@@ -164,6 +173,18 @@ def roofline(stage: str, units: dict, ms: float, traffic=None):
             "algorithmic_flops": u.get("flops", u.get("flops64"))}
 
 
+def both_fractions(stage: str, units: dict, ms: float):
+    """A stage's algorithmic bytes against the HBM peak and, where it has a
+    matrix-core contraction, its flops against that matrix peak."""
+    u = units[stage]
+    out = {}
+    if u.get("bytes"):
+        out["hbm_frac"] = round(u["bytes"] / (ms * 1e-3) / 1e9 / PEAK["hbm_GBps"], 5)
+    if u.get("flops") and stage in MFMA_PEAK:
+        out["mfma_frac"] = round(u["flops"] / (ms * 1e-3) / 1e12 / PEAK[MFMA_PEAK[stage]], 5)
+    return out
+
+
 # Stages that are exactly one kernel launch (name as rocprofv3 reports it),
 # and the source files each stage's kernels are built from.
 STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine",
@@ -200,7 +221,7 @@ def cpu_baseline(w, inp, heads: int):
     rot = None if inp.rotations is None else inp.rotations.astype(np.float64)
     oracle.build(force=False)
     t0 = time.perf_counter()
-    oracle.forward(c, qk, v, rot)
+    ref = oracle.forward(c, qk, v, rot)
     t = time.perf_counter() - t0
     frac = heads / (w.batch * w.heads)
     value = w.batch * w.seq_len * frac / t
@@ -218,7 +239,59 @@ def cpu_baseline(w, inp, heads: int):
             "sample": f"batch 0, heads 0..{heads - 1} of {w.heads}, full L={w.seq_len}, "
                       f"all {w.n_rounds} rounds ({frac:.4f} of the workload), fp64 oracle "
                       f"forward in {t:.2f} s; OpenMP over (head, round) segments",
-            "seconds": round(t, 3), "cpu_model": model, "threads_available": threads}
+            "seconds": round(t, 3), "cpu_model": model, "threads_available": threads}, ref
+
+
+def parity_summary(w, inp, gpu, ref, heads: int):
+    """What the timed configuration's results are, against the oracle: bucket
+    ids of every head and round against the oracle's hash (mismatches and
+    near-ties, oracle top-two margin < 1e-5), and the outputs and logsumexps
+    of the cpu_baseline sample (batch 0, heads 0..heads-1) against the oracle's
+    forward on them. gpu: out [B,H,L,d], lse [B,H,R,L], buckets [B,H,R,L]
+    (numpy)."""
+    import numpy as np
+
+    import oracle
+
+    res = {}
+    if w.n_buckets > 1:
+        t0 = time.perf_counter()
+        bk, mg = oracle.hash(oracle.config(w), inp.qk, inp.rotations)
+        res["bucket_ids_compared"] = int(bk.size)
+        res["bucket_mismatches"] = int(np.sum(bk != gpu["buckets"]))
+        res["near_ties"] = int(np.sum(mg < 1e-5))
+        res["near_tie_mismatches"] = int(np.sum((bk != gpu["buckets"]) & (mg < 1e-5)))
+        res["oracle_hash_s"] = round(time.perf_counter() - t0, 2)
+    out = gpu["out"][:1, :heads].astype(np.float64)
+    res["out_rows_compared"] = int(heads * w.seq_len)
+    res["out_max_abs_err"] = float(np.abs(out - ref["out"]).max())
+    lg = gpu["lse"][:1, :heads].astype(np.float64)
+    keep = ref["lse"] != oracle.SELF_LOGIT
+    res["lse_max_abs_err"] = float(np.abs(lg - ref["lse"])[keep].max()) if keep.any() else 0.0
+    res["self_only_flags_equal"] = bool(np.array_equal(lg == oracle.SELF_LOGIT, ~keep))
+    res["perm_equal_sample"] = bool(np.array_equal(gpu["perm"][:1, :heads], ref["perm"]))
+    res["out_tolerance"] = 2e-2 if w.dtype == "bf16" else 1e-5
+    return res
+
+
+def settle(step, ms: float):
+    """Run forwards for at least `ms` milliseconds of wall time before the
+    warm-up steps: the first tens of milliseconds of sustained work run at
+    lower clocks (measured: 20 timed forwards after 5 warm-ups take ~7% longer
+    than after ~100 ms of work). Returns the record the JSON line declares."""
+    import torch
+    if ms <= 0:
+        return {"forwards": 0, "ms": 0.0}
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    return {"forwards": n, "ms": round((time.perf_counter() - t0) * 1e3, 1),
+            "why": "untimed forwards before the warm-up steps so that the timed ones run at "
+                   "the clocks of sustained work, not the ramp at the start of the process"}
 
 
 def calibration_copy(mib: int, dev):
@@ -294,6 +367,7 @@ def main_backward(args, w, inp, op_kw):
     dqk = torch.empty_like(qk)
     dv = torch.empty_like(v)
     stream = torch.cuda.current_stream()
+    settled = settle(lambda: op.backward(qk, v, perm, dout, dqk, dv), args.settle_ms)
     for _ in range(args.warmup):
         op.backward(qk, v, perm, dout, dqk, dv)
     torch.cuda.synchronize()
@@ -334,9 +408,10 @@ def main_backward(args, w, inp, op_kw):
             r = roofline(k, units, t)
             per_stage[k].update({"achieved": r["achieved"], "unit": r["unit"],
                                  "frac": r["frac"], "bound": r["bound"]})
+            per_stage[k].update(both_fractions(k, units, t))
     tokens = w.batch * w.seq_len
     res = {
-        "metric": METRIC_BWD,
+        "metric": metric_name(w, "bwd"),
         "value": round(tokens / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -357,6 +432,7 @@ def main_backward(args, w, inp, op_kw):
                    "per_round_gradients": "fp32" if args.fp32_round_outputs else "fp16"},
         "roofline": rl,
         "stages": per_stage,
+        "settle": settled,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
@@ -420,6 +496,7 @@ def main_ffn(args, w):
     y2 = torch.empty((rows, d_model), dtype=tdt, device=dev)
     call = lambda: op(t["y1"], t["w1"], t["b1"], t["w2"], t["b2"], x2=t["x2"], out=y2)
     stream = torch.cuda.current_stream()
+    settled = settle(call, args.settle_ms)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -480,6 +557,7 @@ def main_ffn(args, w):
                    "inputs": "seeded normal y1, x2; weights N(0, 1/fan_in); biases N(0, 0.01)"},
         "roofline": rl,
         "stages": per_stage,
+        "settle": settled,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
@@ -511,7 +589,11 @@ def main():
                     help="rows per feed-forward chunk (0: all rows at once)")
     ap.add_argument("--ffn-cpu-rows", type=int, default=32768,
                     help="rows in the oracle's feed-forward sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle's timing and the parity summary")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed forwards for this many milliseconds before the warm-up "
+                         "steps (declared in the JSON line as 'settle')")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the oracle sample (0: as many as rounds fit the cores)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -586,6 +668,7 @@ def main():
     else:
         step = lambda: op(qk, v, rot, out=out)
 
+    settled = settle(step, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -637,10 +720,11 @@ def main():
             r = roofline(k, units, stage_avg[k])
             per_stage[k].update({"achieved": r["achieved"], "unit": r["unit"],
                                  "frac": r["frac"], "bound": r["bound"]})
+            per_stage[k].update(both_fractions(k, units, stage_avg[k]))
 
     tokens = w.batch * w.seq_len
     res = {
-        "metric": METRIC,
+        "metric": metric_name(w, "fwd"),
         "value": round(tokens / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -667,11 +751,20 @@ def main():
         "stages": per_stage,
         "token_heads_per_s": round(w.batch * w.heads * w.seq_len / (ms * 1e-3), 1),
         "hash_stats": stats,
+        "settle": settled,
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
         heads = args.cpu_heads or max(1, min(w.heads, len(os.sched_getaffinity(0)) // w.n_rounds))
-        res["cpu_baseline"] = cpu_baseline(w, inp, heads)
+        res["cpu_baseline"], ref = cpu_baseline(w, inp, heads)
+        if not args.from_x and not variants:
+            # the results of the timed configuration: one more forward, untimed
+            out, ex = op(qk, v, rot, out=out, return_lse=True, return_buckets=True,
+                         return_perm=True)
+            torch.cuda.synchronize()
+            gpu = {"out": out.float().cpu().numpy(), "lse": ex["lse"].cpu().numpy(),
+                   "buckets": ex["buckets"].cpu().numpy(), "perm": ex["perm"].cpu().numpy()}
+            res["parity"] = parity_summary(w, inp, gpu, ref, heads)
     op.close()
     print(json.dumps(res), flush=True)
 

@@ -59,10 +59,13 @@ enum {
    * (workspace grows by 2 * n_rounds * |qk|). By default the chunk-attention
    * kernel reads rows through the permutation itself. Results are identical. */
   LSH_ATTN_FLAG_SEPARATE_GATHER = 1,
-  /* Keep the per-round outputs in fp32 between the attention and the combine
-   * step. By default the matrix-core path (bf16 inputs) keeps them in fp16,
-   * which halves that traffic; fp16 saturates at +-65504, so inputs whose v
-   * exceeds that magnitude need this flag. */
+  /* Keep the per-round outputs (and the backward's per-round gradient rows)
+   * in fp32 between the attention and the combine step. By default the
+   * matrix-core path (bf16 inputs) keeps them in fp16, which halves that
+   * traffic; fp16 holds at most +-65504 and larger values are clamped there,
+   * so inputs whose |v| (or, in the backward, |dout| |v| or |dout| |qk|)
+   * reaches that magnitude need this flag. lsh_attn_get_stats counts the
+   * values that reached the limit. */
   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
   /* Also allocate the workspace of lsh_attn_backward: per position and round,
    * 2 fp32 rows of head_dim on the matrix-core path (bf16, chunk_len 64, head_dim
@@ -188,14 +191,28 @@ int lsh_attn_backward(lsh_attn_t handle, const void* qk, const void* v, const in
                       const void* dout, void* dqk, void* dv, void* stream);
 
 /*
- * Counters of the last forward (waits for the handle's last stream):
- *   n_exact_rescored: hash decisions the bulk projection could not certify and
- *   that were settled by recomputing the candidates in fp64.
- * Errors: INVALID_ARG for null pointers; HIP if the copy fails.
+ * Counters (waits for the handle's last stream):
+ *   n_exact_rescored, n_full_fallback (of the last forward): hash decisions the
+ *   bulk projection could not certify, settled by recomputing in fp64 the two
+ *   candidate columns or every column;
+ *   n_round_rows_at_fp16_limit (forwards since the previous call of this
+ *   function): (position, 8 dims) pieces whose fp16 per-round output rows
+ *   reached +-65504, the fp16 limit, where values are clamped. The per-round
+ *   rows are kept in fp16 on the matrix-core path unless
+ *   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS is set; they are convex combinations of
+ *   v rows, so this stays 0 while every |v| < 65504; a nonzero count means the
+ *   affected outputs are inaccurate and the handle should use the flag;
+ *   n_grad_rows_at_fp16_limit (backwards since the previous call): the same
+ *   for the backward's fp16 per-round gradient rows (dqk_r, dv_r), whose
+ *   magnitudes grow with |dout| |v| and |dout| |qk|.
+ * The two limit counters restart at 0 after each call.
+ * Errors: INVALID_ARG for null pointers; HIP if a copy fails.
  */
 typedef struct {
   int64_t n_exact_rescored;
   int64_t n_full_fallback;
+  int64_t n_round_rows_at_fp16_limit;
+  int64_t n_grad_rows_at_fp16_limit;
 } lsh_attn_stats_t;
 int lsh_attn_get_stats(lsh_attn_t handle, lsh_attn_stats_t* stats);
 

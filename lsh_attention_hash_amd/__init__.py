@@ -66,7 +66,9 @@ class FFNConfig(ctypes.Structure):
 
 
 class Stats(ctypes.Structure):
-    _fields_ = [("n_exact_rescored", ctypes.c_int64), ("n_full_fallback", ctypes.c_int64)]
+    _fields_ = [("n_exact_rescored", ctypes.c_int64), ("n_full_fallback", ctypes.c_int64),
+                ("n_round_rows_at_fp16_limit", ctypes.c_int64),
+                ("n_grad_rows_at_fp16_limit", ctypes.c_int64)]
 
 
 _lib = None
@@ -293,7 +295,7 @@ class LSHAttention:
         rc = self.lib.lsh_attn_get_stats(self.handle, ctypes.byref(st))
         if rc != 0:
             raise LSHAttnError(rc, "lsh_attn_get_stats", self.lib)
-        return {"n_exact_rescored": st.n_exact_rescored, "n_full_fallback": st.n_full_fallback}
+        return {k: getattr(st, k) for k, _ in Stats._fields_}
 
     def set_timing(self, capacity: int) -> None:
         """Record per-stage HIP events for the next `capacity` forwards (0 disables)."""

@@ -322,7 +322,8 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
                                                         const GT* __restrict__ dqkr,
                                                         const GT* __restrict__ dvr,
                                                         T* __restrict__ dqk, T* __restrict__ dv,
-                                                        int L, int R_rt, int64_t n_rows) {
+                                                        int L, int R_rt, int64_t n_rows,
+                                                        unsigned long long* __restrict__ at_limit) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
   constexpr int kLpr = D / 8;
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
   const int64_t bh = row / L, j = row - bh * L;
   float gq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  uint32_t lim = 0;
   const float ws = wself[row];
   for (int r0 = 0; r0 < R; r0 += kG) {
     if constexpr (sizeof(GT) == 4) {
@@ -365,6 +367,17 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
         a[u] = __builtin_nontemporal_load((const h8_t*)(dqkr + sr * D + sub * 8));
         c[u] = __builtin_nontemporal_load((const h8_t*)(dvr + sr * D + sub * 8));
       }
+      // fp16 rows clamped at +-65504 by the product kernel: a half-word whose
+      // magnitude bits reach 0x7BFF carries into its sign bit here
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int u = 0; u < kG; ++u) {
+        const u32x4_t ba = __builtin_bit_cast(u32x4_t, a[u]);
+        const u32x4_t bc = __builtin_bit_cast(u32x4_t, c[u]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          lim |= ((ba[k] & 0x7FFF7FFFu) + 0x04010401u) | ((bc[k] & 0x7FFF7FFFu) + 0x04010401u);
+      }
 #pragma unroll
       for (int u = 0; u < kG; ++u)
 #pragma unroll
@@ -374,6 +387,7 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
         }
     }
   }
+  if (lim & 0x80008000u) atomicAdd(at_limit, 1ull);
   if (ws > 0.f) {
     float dz[8];
     load8<T>(dout + row * D + sub * 8, dz);
@@ -387,7 +401,7 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
 template <int D, typename T>
 void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* perm,
               const void* dout, void* dqk, void* dvo, const float* knorm, BwdWorkspace& b,
-              hipStream_t s, const hipEvent_t* ev) {
+              unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev) {
   auto mark = [&](int j) {
     if (ev) (void)hipEventRecord(ev[j], s);
   };
@@ -411,11 +425,11 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
         auto kern = k_bwd_reduce_sum<D, T, kR, _Float16>;
         hipLaunchKernelGGL(kern, gt, dim3(256), 0, s, (const T*)dout, b.wself,
                            (const _Float16*)b.dq, (const _Float16*)b.dv, (T*)dqk, (T*)dvo, p.L,
-                           p.R, nt);
+                           p.R, nt, at_limit);
       } else {
         auto kern = k_bwd_reduce_sum<D, T, kR, float>;
         hipLaunchKernelGGL(kern, gt, dim3(256), 0, s, (const T*)dout, b.wself, b.dq, b.dv,
-                           (T*)dqk, (T*)dvo, p.L, p.R, nt);
+                           (T*)dqk, (T*)dvo, p.L, p.R, nt, at_limit);
       }
     };
     switch (p.R) {
@@ -450,7 +464,7 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
 
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                            const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
-                           hipStream_t s, const hipEvent_t* ev) {
+                           unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev) {
   // the per-round attention, recomputed from the permutation in fp32
   hipError_t e;
   if (ev) (void)hipEventRecord(ev[0], s);
@@ -466,11 +480,11 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
   if (ev) (void)hipEventRecord(ev[1], s);
   const bool bf = p.dtype == LSH_ATTN_BF16;
   if (p.d == 64) {
-    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
-    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
+    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
+    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
   } else {
-    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
-    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, s, ev);
+    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
+    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
   }
   return hipGetLastError();
 }

@@ -25,10 +25,14 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;
 
-// four floats as fp16 (round to nearest even), packed in 8 bytes
+// four floats as fp16 (round to nearest even), packed in 8 bytes; values past
+// the fp16 range are clamped to +-65504 (the sum over rounds counts such
+// values, so the caller can tell the gradients are inaccurate)
+__device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
 __device__ __forceinline__ uint2 pack_h4(float a, float b, float c, float d) {
   typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-  const h2_t lo = {(_Float16)a, (_Float16)b}, hi = {(_Float16)c, (_Float16)d};
+  const h2_t lo = {(_Float16)sat16(a), (_Float16)sat16(b)};
+  const h2_t hi = {(_Float16)sat16(c), (_Float16)sat16(d)};
   return uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 constexpr int kThreads = 256;

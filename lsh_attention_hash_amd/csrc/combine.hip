@@ -11,6 +11,10 @@
 // logsumexp is the self-only value -1e5 has output v_i by definition; that row
 // is taken from v, the round's own row (finite, zeros on the matrix-core path)
 // entering with weight 0.
+// fp16 per-round rows hold at most +-65504 (the attention clamps them there);
+// every (position, 8 dims) piece whose rounds reached that limit is counted
+// in *at_limit, so the caller can tell the result is inaccurate (and keep the
+// rows in fp32).
 #include <type_traits>
 
 #include "dtype.h"
@@ -21,7 +25,7 @@ namespace {
 
 // 8 consecutive per-round outputs as floats. Each row is read exactly once,
 // so the loads are non-temporal (streamed past the caches).
-__device__ __forceinline__ void load8(const float* p, float* x) {
+__device__ __forceinline__ void load8(const float* p, float* x, uint32_t&) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   const f32x4_t a = __builtin_nontemporal_load((const f32x4_t*)p);
   const f32x4_t b = __builtin_nontemporal_load((const f32x4_t*)(p + 4));
@@ -31,13 +35,25 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
     x[4 + j] = b[j];
   }
 }
-__device__ __forceinline__ void load8(const _Float16* p, float* x) {
+// lim: bit 15 or 31 is set when a half-word's magnitude bits reach 0x7BFF
+// (65504, the largest finite fp16) or beyond (x + 0x0401 carries into the
+// sign position; no carry crosses into the other half-word)
+__device__ __forceinline__ void load8(const _Float16* p, float* x, uint32_t& lim) {
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const f16x8_t a = __builtin_nontemporal_load((const f16x8_t*)p);
+  const u32x4_t b = __builtin_bit_cast(u32x4_t, a);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lim |= (b[j] & 0x7FFF7FFFu) + 0x04010401u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
 }
 // 8 consecutive inputs (v) as floats
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
 __device__ __forceinline__ void load8(const bf16_t* p, float* x) {
   const uint4 a = *(const uint4*)p;
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -68,7 +84,8 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
                                                  const float* __restrict__ lse,
                                                  const VT* __restrict__ v,
                                                  OutT* __restrict__ out, int L, int R_rt,
-                                                 int64_t n_rows, int64_t o_seg_rows) {
+                                                 int64_t n_rows, int64_t o_seg_rows,
+                                                 unsigned long long* __restrict__ at_limit) {
   constexpr int kLpr = D / 8;             // lanes per row
   constexpr int kRpb = 256 / kLpr;        // rows per block
   constexpr int kG = kR > 0 ? kR : 4;     // rounds per group
@@ -87,6 +104,7 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
     float mx = -INFINITY;
     float sum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float wself = 0.f;  // weight of the self-only rounds
+    uint32_t lim = 0;
     // rounds r0 .. r0 + kG - 1 given their logsumexps and rows, mx final
     auto accumulate = [&](int r0, const float* lv, float (*x)[8]) {
 #pragma unroll
@@ -105,7 +123,7 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
 #pragma unroll
       for (int u = 0; u < kR; ++u) lv[u] = lr[(int64_t)u * L];
 #pragma unroll
-      for (int u = 0; u < kR; ++u) load8(orow + u * o_seg_rows * D, x[u]);
+      for (int u = 0; u < kR; ++u) load8(orow + u * o_seg_rows * D, x[u], lim);
 #pragma unroll
       for (int u = 0; u < kR; ++u) mx = fmaxf(mx, lv[u]);
       accumulate(0, lv, x);
@@ -123,7 +141,7 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
         for (int u = 0; u < kG; ++u) {
           const bool in = r0 + u < R;
           lv[u] = in ? lr[(int64_t)(r0 + u) * L] : -INFINITY;  // weight 0 past R
-          if (in) load8(orow + (r0 + u) * o_seg_rows * D, x[u]);
+          if (in) load8(orow + (r0 + u) * o_seg_rows * D, x[u], lim);
         }
         accumulate(r0, lv, x);
       }
@@ -138,12 +156,13 @@ __global__ __launch_bounds__(256) void k_combine(const OT* __restrict__ o,
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= inv_sum;
     store8(out + row * D + sub * 8, acc);
+    if (lim & 0x80008000u) atomicAdd(at_limit, 1ull);
   }
 }
 
 template <int D, typename OT, typename VT>
 void launch_t(const Problem& p, const OT* o, const float* lse, const VT* v, void* out,
-              hipStream_t s) {
+              unsigned long long* at_limit, hipStream_t s) {
   const int64_t n = p.n_token_heads();
   const int64_t rpb = 256 / (D / 8);
   const int64_t want = (n + rpb - 1) / rpb;
@@ -152,10 +171,10 @@ void launch_t(const Problem& p, const OT* o, const float* lse, const VT* v, void
     constexpr int G = decltype(g)::value;
     if (p.out_dtype == LSH_ATTN_BF16)
       hipLaunchKernelGGL((k_combine<D, bf16_t, OT, VT, G>), dim3(blocks), dim3(256), 0, s, o, lse,
-                         v, (bf16_t*)out, p.L, p.R, n, p.o_seg_rows());
+                         v, (bf16_t*)out, p.L, p.R, n, p.o_seg_rows(), at_limit);
     else
       hipLaunchKernelGGL((k_combine<D, float, OT, VT, G>), dim3(blocks), dim3(256), 0, s, o, lse,
-                         v, (float*)out, p.L, p.R, n, p.o_seg_rows());
+                         v, (float*)out, p.L, p.R, n, p.o_seg_rows(), at_limit);
   };
   switch (p.R) {
     case 1: go(std::integral_constant<int, 1>{}); break;
@@ -169,21 +188,24 @@ void launch_t(const Problem& p, const OT* o, const float* lse, const VT* v, void
 
 template <int D, typename OT>
 void launch_v(const Problem& p, const OT* o, const float* lse, const void* v, void* out,
-              hipStream_t s) {
-  if (p.dtype == LSH_ATTN_BF16) launch_t<D, OT, bf16_t>(p, o, lse, (const bf16_t*)v, out, s);
-  else launch_t<D, OT, float>(p, o, lse, (const float*)v, out, s);
+              unsigned long long* at_limit, hipStream_t s) {
+  if (p.dtype == LSH_ATTN_BF16)
+    launch_t<D, OT, bf16_t>(p, o, lse, (const bf16_t*)v, out, at_limit, s);
+  else
+    launch_t<D, OT, float>(p, o, lse, (const float*)v, out, at_limit, s);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
-                          const void* v, void* out, hipStream_t s) {
+                          const void* v, void* out, unsigned long long* at_limit,
+                          hipStream_t s) {
   if (p.d == 64) {
-    if (o_half) launch_v<64, _Float16>(p, (const _Float16*)o, lse, v, out, s);
-    else launch_v<64, float>(p, (const float*)o, lse, v, out, s);
+    if (o_half) launch_v<64, _Float16>(p, (const _Float16*)o, lse, v, out, at_limit, s);
+    else launch_v<64, float>(p, (const float*)o, lse, v, out, at_limit, s);
   } else {
-    if (o_half) launch_v<128, _Float16>(p, (const _Float16*)o, lse, v, out, s);
-    else launch_v<128, float>(p, (const float*)o, lse, v, out, s);
+    if (o_half) launch_v<128, _Float16>(p, (const _Float16*)o, lse, v, out, at_limit, s);
+    else launch_v<128, float>(p, (const float*)o, lse, v, out, at_limit, s);
   }
   return hipGetLastError();
 }

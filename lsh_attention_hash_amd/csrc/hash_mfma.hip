@@ -685,13 +685,16 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   // persistent grid: as many resident workgroups as fit, a multiple of 8 R
   const int lds = p.d == 128 ? lds_bytes<128>(hp) : lds_bytes<64>(hp);
   const void* fn = p.d == 128 ? (const void*)k_hash_mfma<128> : (const void*)k_hash_mfma<64>;
-  (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
-  int per_cu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess ||
-      per_cu < 1) {
-    (void)hipGetLastError();
-    per_cu = 1;
+  if (hs.per_cu == 0) {  // once per handle (on its device)
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&hs.per_cu, fn, kThreads, lds) !=
+            hipSuccess ||
+        hs.per_cu < 1) {
+      (void)hipGetLastError();
+      hs.per_cu = 1;
+    }
   }
+  const int per_cu = hs.per_cu;
   const int unit = 8 * p.R;
   int64_t grid = (int64_t)hs.n_cu * per_cu;
   grid = (grid / unit) * unit;

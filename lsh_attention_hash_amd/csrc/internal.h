@@ -44,6 +44,8 @@ struct HashScratch {
   void* x16 = nullptr;        // [N, d] fp16 copy of qk
   void* xnorm = nullptr;      // [N] float2 bounds of |x16| and |x - x16|
   int n_cu = 0;               // compute units of the handle's device
+  int per_cu = 0;             // resident hash workgroups per CU (0: not yet queried)
+  bool proj_attr = false;     // the projection kernel's LDS attribute is set
 };
 
 // Device workspace owned by a handle. Per-round arrays are [seg, L(, d)] with
@@ -58,7 +60,9 @@ struct Workspace {
   uint32_t* sort_counts = nullptr; // [seg, tiles, nb] counts, then first output slots
   void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
   void* v_sorted = nullptr;        // [seg, L, d]
-  unsigned long long* stats = nullptr;  // [2] exact rescored, full fallback
+  unsigned long long* stats = nullptr;  // [4] exact rescored, full fallback (last forward);
+                                        // fp16 limit hits of forward / backward rows (since
+                                        // the last lsh_attn_get_stats)
   float* knorm = nullptr;          // [B*H*L] squared qk row norms (matrix-core attention)
   HashScratch hash;                     // matrix-core hash only
 };
@@ -135,15 +139,19 @@ hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* 
                                   float* od, float* lse, hipStream_t s);
 // o is fp16 when o_half, else fp32; v (the input values) supplies the rows of
 // rounds in which a query saw only itself
+// at_limit: incremented once per (position, 8 dims) piece whose fp16
+// per-round rows reached the fp16 limit (+-65504)
 hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const float* lse,
-                          const void* v, void* out, hipStream_t s);
+                          const void* v, void* out, unsigned long long* at_limit,
+                          hipStream_t s);
 
 // gradients of qk and v given dout, at the permutations perm of a forward
 // ev (may be null): 5 events, recorded before the recomputation and after
-// each of its 4 stages (recomputation, rows, gradient products, reduction)
+// each of its 4 stages (recomputation, rows, gradient products, reduction);
+// at_limit: as for launch_combine, for the fp16 per-round gradient rows
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                            const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
-                           hipStream_t s, const hipEvent_t* ev);
+                           unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev);
 
 // the per-round gradient products on matrix cores (attend_mfma_supported
 // shapes): b.dq receives dqk per round (dq and the normalised dkhat), b.dv dv

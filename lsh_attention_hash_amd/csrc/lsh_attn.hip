@@ -139,7 +139,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
             alloc(&w.o, p.nseg() * p.o_seg_rows() * p.d * (lsh::round_outputs_half(p) ? 2 : 4), t) &&
             alloc(&w.lse, rows * 4, t) &&
             alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
-            alloc(&w.stats, 2 * 8, t);
+            alloc(&w.stats, 4 * 8, t) && hipMemset(w.stats, 0, 4 * 8) == hipSuccess;
   if (ok && (lsh::attend_mfma_supported(p) || lsh::attend_variant_mfma_supported(p)))
     ok = alloc(&w.knorm, p.n_token_heads() * 4, t);
   if (ok && lsh::hash_mfma_supported(p)) {
@@ -207,7 +207,7 @@ int forward_body(lsh_attn_s* h, const void* qk, const void* v, const float* rota
     } else {
       if (w.knorm) e = lsh::launch_key_norms(p, qk, w.knorm, s);
       mark(1);
-      e = lsh::launch_hash_exact(p, qk, rotations, w.buckets, buckets, s);
+      if (e == hipSuccess) e = lsh::launch_hash_exact(p, qk, rotations, w.buckets, buckets, s);
       mark(2);
     }
   }
@@ -224,7 +224,8 @@ int forward_body(lsh_attn_s* h, const void* qk, const void* v, const float* rota
                            separate ? w.v_sorted : nullptr, pm, w.knorm, w.buckets, w.inv,
                            (float*)w.o, ls, s);
   mark(6);
-  if (e == hipSuccess) e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, s);
+  if (e == hipSuccess)
+    e = lsh::launch_combine(p, w.o, lsh::round_outputs_half(p), ls, v, out, w.stats + 2, s);
   mark(7);
   if (e == hipSuccess) e = hipGetLastError();
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
@@ -237,6 +238,13 @@ hipEvent_t* next_events(lsh_attn_s* h, bool projected) {
   h->projected[h->timed] = projected ? 1 : 0;
   ++h->timed;
   return ev;
+}
+
+// A call that failed before recording all of its events gives its timing slot
+// back, so the accumulation only holds calls whose events were all recorded.
+int release_on_error(lsh_attn_s* h, const hipEvent_t* ev, int rc) {
+  if (rc != LSH_ATTN_OK && ev && h->timed > 0) --h->timed;
+  return rc;
 }
 
 bool on_device(const lsh_attn_s* h) {
@@ -258,8 +266,9 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   if (!on_device(h)) return LSH_ATTN_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
-  return forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, next_events(h, false),
-                      false);
+  hipEvent_t* ev = next_events(h, false);
+  return release_on_error(h, ev,
+                          forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, ev, false));
 }
 
 int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const void* w_qk,
@@ -281,8 +290,9 @@ int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const voi
   const hipError_t e = lsh::launch_project(h->p, model_dim, x, w_qk, w_v, qk, v, h->ws.hash,
                                            h->ws.knorm, &x16_ready, s);
   if (ev) hipEventRecord(ev[9], s);
-  if (e != hipSuccess) return LSH_ATTN_ERR_HIP;
-  return forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, ev, x16_ready);
+  if (e != hipSuccess) return release_on_error(h, ev, LSH_ATTN_ERR_HIP);
+  return release_on_error(
+      h, ev, forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, ev, x16_ready));
 }
 
 int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
@@ -299,21 +309,27 @@ int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t
   const hipEvent_t* ev =
       timing ? &h->bevents[(size_t)h->btimed * (LSH_ATTN_N_BWD_STAGES + 1)] : nullptr;
   if (timing) ++h->btimed;
-  hipError_t e = lsh::launch_backward(p, qk, v, perm, dout, dqk, dv, h->ws.knorm, h->bw, s, ev);
+  hipError_t e = lsh::launch_backward(p, qk, v, perm, dout, dqk, dv, h->ws.knorm, h->bw,
+                                      h->ws.stats + 3, s, ev);
   if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess && timing) --h->btimed;  // its events were not all recorded
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
 }
 
 int lsh_attn_get_stats(lsh_attn_t h, lsh_attn_stats_t* stats) {
   if (!h || !stats) return LSH_ATTN_ERR_INVALID_ARG;
-  unsigned long long host[2] = {0, 0};
+  unsigned long long host[4] = {0, 0, 0, 0};
+  const unsigned long long zero[2] = {0, 0};
   if (hipStreamSynchronize(h->last_stream) != hipSuccess ||
-      hipMemcpy(host, h->ws.stats, sizeof(host), hipMemcpyDeviceToHost) != hipSuccess) {
+      hipMemcpy(host, h->ws.stats, sizeof(host), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(h->ws.stats + 2, zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipGetLastError();
     return LSH_ATTN_ERR_HIP;
   }
   stats->n_exact_rescored = (int64_t)host[0];
   stats->n_full_fallback = (int64_t)host[1];
+  stats->n_round_rows_at_fp16_limit = (int64_t)host[2];
+  stats->n_grad_rows_at_fp16_limit = (int64_t)host[3];
   return LSH_ATTN_OK;
 }
 

@@ -151,21 +151,24 @@ hipError_t launch_project(const Problem& p, int model_dim, const void* x, const 
     const unsigned grid = (unsigned)(((mts + 7) / 8) * 8 * 2 * p.H);
     if (p.d == 128) {
       constexpr int shmem = PLds<128>::kBytes;
-      (void)hipFuncSetAttribute((const void*)k_proj_mfma<128>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+      if (!hs.proj_attr)
+        (void)hipFuncSetAttribute((const void*)k_proj_mfma<128>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
       hipLaunchKernelGGL(k_proj_mfma<128>, dim3(grid), dim3(kThreads), shmem, s,
                          (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
                          (uint4*)v, (uint4*)hs.x16, (float2*)hs.xnorm, knorm, M, p.L, p.H,
                          model_dim);
     } else {
       constexpr int shmem = PLds<64>::kBytes;
-      (void)hipFuncSetAttribute((const void*)k_proj_mfma<64>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+      if (!hs.proj_attr)
+        (void)hipFuncSetAttribute((const void*)k_proj_mfma<64>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
       hipLaunchKernelGGL(k_proj_mfma<64>, dim3(grid), dim3(kThreads), shmem, s,
                          (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
                          (uint4*)v, (uint4*)hs.x16, (float2*)hs.xnorm, knorm, M, p.L, p.H,
                          model_dim);
     }
+    hs.proj_attr = true;
     *x16_ready = true;
     return hipGetLastError();
   }

@@ -179,3 +179,37 @@ def test_backward_parity_fp32_round_rows(causal):
     instead of the default fp16: the same parity."""
     test_backward_parity(W("text64k", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=4,
                            causal=causal), fp32_rows=True)
+
+
+def test_backward_gradient_rows_at_the_fp16_limit():
+    """The per-round gradient rows are fp16 by default: with dout x 2^16 some
+    pass +-65504, which the library counts (the rows are clamped there); with
+    fp32 rows the same backward matches the oracle and counts nothing."""
+    w = W("c4k", batch=1, heads=2, seq_len=1024, n_buckets=16, n_rounds=2, causal=True)
+    _say(f"[backward fp16 limit] {w}")
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    qk, v, rot = to_device(inp, dev)
+    dout_t, dout = _dout(w, 31)
+    dout_t = dout_t * 2.0 ** 16
+    dout = dout * 2.0 ** 16
+    res = {}
+    for fp32_rows in (False, True):
+        op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
+                              w.chunk_len, w.causal, backward=True, fp32_round_outputs=fp32_rows)
+        try:
+            _, ex = op(qk, v, rot, return_perm=True)
+            op.stats()  # restart the limit counters
+            dqk, dv = op.backward(qk, v, ex["perm"], dout_t.to(dev))
+            torch.cuda.synchronize()
+            res[fp32_rows] = (ex["perm"].cpu().numpy(), dqk.to(torch.float64).cpu().numpy(),
+                              dv.to(torch.float64).cpu().numpy(),
+                              op.stats()["n_grad_rows_at_fp16_limit"])
+        finally:
+            op.close()
+    _say(f"  fp16 rows: {res[False][3]} pieces at the limit; fp32 rows: {res[True][3]}")
+    assert res[False][3] > 0 and res[True][3] == 0
+    perm, dqk, dv, _ = res[True]
+    rq, rv = oracle.backward(oracle.config(w), inp.qk, inp.v, perm, dout)
+    _check("dqk", dqk, rq, True)
+    _check("dv", dv, rv, True)

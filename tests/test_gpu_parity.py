@@ -1,9 +1,11 @@
 """HIP path vs the fp64 oracle, through the C ABI, on seeded inputs.
 
-Small cases are compared element by element over every output; the full-size
-workloads are compared on every bucket of a few heads, on the whole
-permutation (the oracle's stable sort of the GPU's bucket ids), and on a few
-thousand sampled output rows. Each case prints what it is before it runs.
+Every case is compared with the oracle's own forward element by element:
+bucket ids and permutations bit-exact everywhere (near-ties included and
+counted), every output and logsumexp within its tolerance. That holds for the
+full-size workloads too (every head, every round, every position), in the
+launch configuration the bench times. Each case prints what it is before it
+runs.
 """
 import ctypes
 import sys
@@ -15,8 +17,8 @@ import torch
 import oracle
 import workloads
 import lsh_attention_hash_amd as lat
-from parity import (check_buckets, check_outputs_full, check_outputs_rows, check_perm,
-                    make_op, run_gpu, to_device)
+from parity import (OUT_TOL, check_buckets, check_forward, check_outputs_full, check_perm,
+                    make_op, run_gpu, scaled_inputs, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,10 +65,9 @@ def test_small_full_parity(w):
     _say(f"[small] {w}")
     inp = workloads.make_inputs(w)
     gpu = run_gpu(w, inp)
-    n, ties, tie_mis = check_buckets(w, inp, gpu["buckets"])
-    check_perm(w, gpu["buckets"], gpu["perm"])
-    err, lerr = check_outputs_full(w, inp, gpu)
-    _say(f"  buckets {n} ties {ties} tie-mismatch {tie_mis} out err {err:.3g} lse err {lerr:.3g}")
+    r = check_forward(w, inp, gpu)
+    _say(f"  buckets {r['buckets']} ties {r['ties']} out err {r['out_err']:.3g} "
+         f"lse err {r['lse_err']:.3g}")
 
 
 def test_tiny_fp32_full_parity():
@@ -74,11 +75,9 @@ def test_tiny_fp32_full_parity():
     _say(f"[tiny] {w}")
     inp = workloads.make_inputs(w)
     gpu = run_gpu(w, inp)
-    check_buckets(w, inp, gpu["buckets"])
-    check_perm(w, gpu["buckets"], gpu["perm"])
-    err, lerr = check_outputs_full(w, inp, gpu)
-    assert err <= 1e-5
-    _say(f"  out err {err:.3g} lse err {lerr:.3g}")
+    r = check_forward(w, inp, gpu)
+    assert r["out_err"] <= 1e-5
+    _say(f"  out err {r['out_err']:.3g} lse err {r['lse_err']:.3g}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -153,17 +152,16 @@ FULL = ["c4k", "text64k", "image12k", "skewed"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_parity(name):
+def test_full_size_parity(name):
+    """The workload at full size, compared over every element with the
+    oracle's whole forward (tens of seconds of fp64 on the host threads)."""
     w = workloads.get(name)
     _say(f"[full] {w}")
     inp = workloads.make_inputs(w)
     gpu = run_gpu(w, inp)
-    check_perm(w, gpu["buckets"], gpu["perm"])
-    sel = [(0, 0), (w.batch - 1, w.heads - 1)]
-    n, ties, tie_mis = check_buckets(w, inp, gpu["buckets"], bh_sel=sel)
-    err, lerr = check_outputs_rows(w, inp, gpu, n_rows=1024)
-    _say(f"  buckets checked {n} ties {ties} tie-mismatch {tie_mis} out err {err:.3g} "
-         f"lse err {lerr:.3g} stats {gpu['stats']}")
+    r = check_forward(w, inp, gpu)
+    _say(f"  buckets {r['buckets']} ties {r['ties']} out err {r['out_err']:.3g} "
+         f"lse err {r['lse_err']:.3g} stats {gpu['stats']}")
 
 
 def test_forward_rejects_null_and_misaligned_pointers():
@@ -204,3 +202,60 @@ def test_sort_of_long_segments(L):
         op.close()
     check_buckets(w, inp, gb)
     check_perm(w, gb, gp)
+
+
+LARGE = [
+    # d = 128: |q| ~ 1,450, Cauchy-Schwarz shift ~185 > 60: the true-max softmax
+    (W("text64k", batch=1, heads=2, seq_len=2048, n_buckets=64, n_rounds=2, causal=True), 7, 0),
+    (W("text64k", batch=1, heads=1, seq_len=1024, n_buckets=16, n_rounds=3, causal=False), 7, 0),
+    # d = 64, qk and v both scaled
+    (W("c4k", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=3, causal=True), 7, 7),
+    (W("image12k", batch=2, heads=1, seq_len=768, n_buckets=12, n_rounds=4, causal=False), 7, 0),
+    # fp32 inputs (plain kernels)
+    (W("tiny", n_rounds=2, causal=True), 7, 0),
+]
+
+
+@pytest.mark.parametrize("w,qk_exp,v_exp", LARGE,
+                         ids=[f"{w.name}-{w.dtype}-L{w.seq_len}d{w.head_dim}R{w.n_rounds}"
+                              f"{'c' if w.causal else 'n'}-qk2^{a}-v2^{b}" for w, a, b in LARGE])
+def test_large_magnitudes(w, qk_exp, v_exp):
+    """qk (and v) multiplied by a power of two, exact in the storage type: the
+    hash certificate and the re-scoring at large norms (buckets equal to the
+    oracle's and to those of the unscaled rows, since the definition is
+    invariant to positive scaling), and the softmax branch that takes the true
+    row maximum when the Cauchy-Schwarz shift is too large for exp2."""
+    inp = workloads.make_inputs(w)
+    big = scaled_inputs(inp, qk_exp, v_exp)
+    _say(f"[large] {w} qk x 2^{qk_exp} v x 2^{v_exp}")
+    gpu = run_gpu(w, big)
+    r = check_forward(w, big, gpu, v_scale=2.0 ** v_exp, scaled_qk=qk_exp > 0)
+    assert gpu["stats"]["n_round_rows_at_fp16_limit"] == 0
+    base = run_gpu(w, inp)
+    np.testing.assert_array_equal(gpu["buckets"], base["buckets"])
+    _say(f"  buckets {r['buckets']} ties {r['ties']} out err {r['out_err']:.3g} "
+         f"lse err {r['lse_err']:.3g}")
+
+
+def test_round_rows_at_the_fp16_limit():
+    """Per-round rows are fp16 by default: v x 2^13 (|v| < 65504) stays exact
+    to the tolerance and reaches no limit; v x 2^16 takes some rows past
+    +-65504, which the library counts, and with fp32 per-round rows the same
+    inputs match the oracle again."""
+    w = W("c4k", batch=1, heads=2, seq_len=1024, n_buckets=16, n_rounds=2, causal=True)
+    inp = workloads.make_inputs(w)
+    _say(f"[fp16 limit] {w}")
+    mid = scaled_inputs(inp, 0, 13)
+    assert np.abs(mid.v).max() < 65504
+    g = run_gpu(w, mid)
+    assert g["stats"]["n_round_rows_at_fp16_limit"] == 0
+    check_forward(w, mid, g, v_scale=2.0 ** 13)
+    big = scaled_inputs(inp, 0, 16)
+    g = run_gpu(w, big)
+    hits = g["stats"]["n_round_rows_at_fp16_limit"]
+    _say(f"  v x 2^16: {hits} pieces at the fp16 limit")
+    assert hits > 0
+    g = run_gpu(w, big, fp32_round_outputs=True)
+    assert g["stats"]["n_round_rows_at_fp16_limit"] == 0
+    r = check_forward(w, big, g, v_scale=2.0 ** 16)
+    _say(f"  fp32 round rows: out err {r['out_err']:.3g}")

@@ -141,7 +141,7 @@ def test_forward_from_layer_input_full_size():
     _check_projection(w, li, gpu["qk"], gpu["v"], rows=rows)
     inp = workloads.Inputs(w, gpu["qk"].astype(np.float32), gpu["v"].astype(np.float32),
                            li.rotations)
-    check_buckets(w, inp, gpu["buckets"], bh_sel=[(0, 0), (0, w.heads - 1)])
+    check_buckets(w, inp, gpu["buckets"])
     np.testing.assert_array_equal(gpu["out"], gpu["out_direct"])
 
 

@@ -13,7 +13,8 @@ import torch
 import oracle
 import workloads
 import lsh_attention_hash_amd as lat
-from parity import OUT_TOL, _cmp_lse, check_buckets, to_device
+from parity import (OUT_TOL, _cmp_lse, check_buckets, lse_tol, out_tol, sample_rows,
+                    scaled_inputs, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,9 +48,10 @@ def _name(variant):
     return "+".join(parts) or "default"
 
 
-def _run(w, variant):
+def _run(w, variant, inp=None):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    inp = workloads.make_inputs(w)
+    if inp is None:
+        inp = workloads.make_inputs(w)
     qk, v, rot = to_device(inp)
     op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
                           w.chunk_len, w.causal, dtype=dt, **_kw(variant))
@@ -91,26 +93,55 @@ def test_variant_parity(w, variant):
     err = np.abs(gpu["out"] - ref["out"])
     _say(f"  out max err {err.max():.3g}")
     assert err.max() <= OUT_TOL[w.dtype], f"out max err {err.max()}"
-    _cmp_lse(w, gpu["lse"], ref["lse"])
+    _cmp_lse(w, gpu["lse"], ref["lse"], lse_tol(w, inp.qk))
+
+
+SCALED = [
+    # qk x 2^7: the Cauchy-Schwarz shift exceeds the kernel's limit, so the
+    # variant kernel takes the true row maximum (unit queries keep it small)
+    (W("text64k", batch=1, heads=1, seq_len=2048, n_buckets=32, n_rounds=4), LA | SB | DD),
+    (W("c4k", batch=1, heads=2, seq_len=1024, n_buckets=16, n_rounds=3, causal=False), LA | DD),
+    (W("c4k", batch=1, heads=2, seq_len=1024, n_buckets=16, n_rounds=2), NQ),
+]
+
+
+@pytest.mark.parametrize("w,variant", SCALED,
+                         ids=[f"{w.name}-L{w.seq_len}d{w.head_dim}R{w.n_rounds}"
+                              f"{'c' if w.causal else 'n'}-{_name(v)}-qk2^7" for w, v in SCALED])
+def test_variant_parity_large_qk(w, variant):
+    inp = scaled_inputs(workloads.make_inputs(w), 7, 0)
+    _say(f"[variant {_name(variant)}, qk x 2^7] {w}")
+    inp, gpu = _run(w, variant, inp)
+    check_buckets(w, inp, gpu["buckets"])
+    c = oracle.config(w, variant=variant)
+    ref = oracle.forward(c, inp.qk, inp.v, inp.rotations, buckets_override=gpu["buckets"])
+    np.testing.assert_array_equal(ref["perm"], gpu["perm"])
+    err = np.abs(gpu["out"] - ref["out"])
+    tol = out_tol(w, inp, scaled_qk=True)
+    _say(f"  out max err {err.max():.3g} (bound {tol:.3g})")
+    assert err.max() <= tol
+    _cmp_lse(w, gpu["lse"], ref["lse"], lse_tol(w, inp.qk))
 
 
 def test_variants_full_size_sampled_rows():
-    """Text-64K at full size with every variant on, ~2,000 sampled rows."""
+    """Text-64K at full size with every variant on: every bucket id against
+    the oracle's hash, and 256 sampled rows of every head (the chunk ends
+    among them) against the oracle's variant attention."""
     w = workloads.get("text64k")
     _say(f"[variant all, full size] {w}")
     inp, gpu = _run(w, ALL)
-    check_buckets(w, inp, gpu["buckets"], bh_sel=[(0, 0), (0, w.heads - 1)])
-    rng = np.random.default_rng(7)
+    n, ties, _ = check_buckets(w, inp, gpu["buckets"])
+    rows = sample_rows(w, per_head=256, seed=7)
     N = w.batch * w.heads * w.seq_len
-    rows = np.unique(np.concatenate([rng.choice(N, size=2000, replace=False),
-                                     np.array([0, w.seq_len - 1, N - 1])]))
     c = oracle.config(w, variant=ALL)
     out_r, lse_r = oracle.attend_rows(c, inp.qk, inp.v, gpu["perm"], rows, gpu["buckets"])
     err = np.abs(gpu["out"].reshape(N, w.head_dim)[rows] - out_r)
-    _say(f"  out max err {err.max():.3g}")
+    _say(f"  buckets {n} ties {ties} rows {rows.size} out max err {err.max():.3g}")
     assert err.max() <= OUT_TOL[w.dtype]
     bh, i = rows // w.seq_len, rows % w.seq_len
-    _cmp_lse(w, gpu["lse"].reshape(w.batch * w.heads, w.n_rounds, w.seq_len)[bh, :, i], lse_r)
+    tol = lse_tol(w, inp.qk).reshape(w.batch * w.heads, w.seq_len)[bh, i][:, None]
+    _cmp_lse(w, gpu["lse"].reshape(w.batch * w.heads, w.n_rounds, w.seq_len)[bh, :, i], lse_r,
+             tol)
 
 
 def test_backward_with_a_variant_is_unsupported():
