@@ -138,7 +138,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   bool ok = alloc(&w.buckets, rows * 2, t) && alloc(&w.perm, rows * 4, t) &&
             alloc(&w.o, p.nseg() * p.o_seg_rows() * p.d * (lsh::round_outputs_half(p) ? 2 : 4), t) &&
             alloc(&w.lse, rows * 4, t) &&
-            alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * (p.sort_tiles() + 1) * 4, t) &&
+            alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
             alloc(&w.stats, 4 * 8, t) && hipMemset(w.stats, 0, 4 * 8) == hipSuccess;
   if (ok && (lsh::attend_mfma_supported(p) || lsh::attend_variant_mfma_supported(p)))
     ok = alloc(&w.knorm, p.n_token_heads() * 4, t);

@@ -10,14 +10,11 @@
 // tile; wave w owns the tile's positions 256w .. 256w + 255):
 //   count:   counts[seg][tile][b] = how many positions of the tile are in b
 //            (LDS atomic adds; the order of the adds does not matter);
-//   scan:    per (segment, bucket), in parallel over both: counts[seg][tile][b]
-//            becomes the sum of the counts of bucket b in earlier tiles, and
-//            totals[seg][b] the bucket's size;
-//   scatter: the tile's first output slot in bucket b is the sum of the
-//            totals of buckets < b (a block scan of the totals in LDS) plus
-//            counts[seg][tile][b]; each wave first counts its own positions
-//            per bucket; a prefix over the waves turns the tile offset into
-//            per-wave offsets; then
+//   scan:    offsets[seg][tile][b] = sum of all counts of buckets < b plus the
+//            counts of bucket b in earlier tiles: the first output slot of the
+//            tile's positions in bucket b;
+//   scatter: each wave first counts its own positions per bucket; a prefix
+//            over the waves turns the tile offset into per-wave offsets; then
 //            every position gets slot = its wave's offset + (number of earlier
 //            positions of the same wave in b), found with wave ballots over
 //            the bucket bits (lanes holding equal ids find each other), 64
@@ -103,73 +100,60 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint16_t* __r
   }
 }
 
-// Per (segment, 256 buckets), one thread per bucket: the counts of the bucket
-// in the segment's tiles are replaced by their exclusive running sum over the
-// tiles (the tile's first slot relative to the bucket's first slot), and the
-// bucket's total goes to totals[seg][b]. Counts are read 16 tiles at a time,
-// all loads of a batch issued before any use. The buckets' own first slots
-// (an exclusive scan of the totals over buckets) are formed by the scatter.
-__global__ __launch_bounds__(kSortThreads) void k_sort_scan(uint32_t* __restrict__ counts,
-                                                            uint32_t* __restrict__ totals, int nb,
-                                                            int tiles, int groups) {
+// One block per segment. Buckets are taken 1024 at a time, one per thread:
+// first the bucket's total over the tiles, then a block-wide exclusive scan
+// of the totals gives the bucket's first slot, and a second pass over the
+// tiles replaces every count with the running slot. Counts are read 16 tiles
+// at a time, all loads of a batch issued before any use.
+__global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ counts, int nb,
+                                                    int tiles) {
   constexpr int kBatch = 16;
-  const int64_t seg = blockIdx.x / (unsigned)groups;
-  const int b = (int)(blockIdx.x % (unsigned)groups) * kSortThreads + threadIdx.x;
-  if (b >= nb) return;
-  uint32_t* c = counts + seg * nb * (int64_t)tiles + b;
-  uint32_t run = 0;
-  for (int t0 = 0; t0 < tiles; t0 += kBatch) {
-    uint32_t x[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb] : 0u;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (t0 + u < tiles) c[(int64_t)(t0 + u) * nb] = run;
-      run += x[u];
-    }
-  }
-  totals[seg * nb + b] = run;
-}
-
-// Exclusive scan of n <= kLdsBins values v[0..n) in LDS, in place, plus carry;
-// returns the sum of the n values. All threads of the block call it.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t* v, int n, uint32_t carry,
-                                                         uint32_t* part) {
-  constexpr int kPer = kLdsBins / kSortThreads;  // values per thread
+  __shared__ uint32_t part[1024];
   const int tid = threadIdx.x;
-  uint32_t x[kPer], sum = 0;
+  uint32_t* c = counts + (int64_t)blockIdx.x * nb * tiles;
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < nb; b0 += 1024) {
+    const int b = b0 + tid;
+    uint32_t total = 0;
+    if (b < nb) {
+      for (int t0 = 0; t0 < tiles; t0 += kBatch) {
+        uint32_t x[kBatch];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int j = tid * kPer + u;
-    x[u] = j < n ? v[j] : 0u;
-    sum += x[u];
-  }
-  part[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kSortThreads; off <<= 1) {
-    const uint32_t add = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  uint32_t run = carry + part[tid] - sum;
-  const uint32_t total = part[kSortThreads - 1];
+        for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb + b] : 0u;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int j = tid * kPer + u;
-    if (j < n) v[j] = run;
-    run += x[u];
+        for (int u = 0; u < kBatch; ++u) total += x[u];
+      }
+    }
+    part[tid] = total;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const uint32_t add = tid >= off ? part[tid - off] : 0u;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    uint32_t run = carry + part[tid] - total;  // exclusive
+    if (b < nb) {
+      for (int t0 = 0; t0 < tiles; t0 += kBatch) {
+        uint32_t x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb + b] : 0u;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (t0 + u < tiles) c[(int64_t)(t0 + u) * nb + b] = run;
+          run += x[u];
+        }
+      }
+    }
+    carry += part[1023];
+    __syncthreads();
   }
-  __syncthreads();
-  return total;
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const uint16_t* __restrict__ buckets, const uint32_t* __restrict__ offsets,
-    const uint32_t* __restrict__ totals, int32_t* __restrict__ perm, int L, int nb, int tiles,
-    int nbits, int64_t nseg) {
-  extern __shared__ uint32_t next[];  // [wave][window], then the window's first slots
-  __shared__ uint32_t part[kSortThreads];
+    int32_t* __restrict__ perm, int L, int nb, int tiles, int nbits, int64_t nseg) {
+  extern __shared__ uint32_t next[];  // [wave][window]
   int64_t seg;
   int tile;
   block_tile(tiles, nseg, seg, tile);
@@ -184,22 +168,18 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
   int e[kPerThread];
   load_tile(buckets + seg * L, begin, end, b, e);
   const int window = min(nb, kLdsBins);
-  uint32_t* first = next + kSortWaves * window;  // first slot of each bucket of the window
-  uint32_t carry = 0;
   for (int base = 0; base < nb; base += window) {
     const int span = min(window, nb - base);
     uint32_t* mine = next + w * span;
     for (int j = tid; j < kSortWaves * span; j += kSortThreads) next[j] = 0;
-    for (int j = tid; j < span; j += kSortThreads) first[j] = totals[seg * nb + base + j];
     __syncthreads();
-    carry += block_exclusive_scan(first, span, carry, part);
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k)
       if (e[k] < end && (int)b[k] >= base && (int)b[k] < base + span)
         atomicAdd(&mine[b[k] - base], 1u);
     __syncthreads();
     for (int j = tid; j < span; j += kSortThreads) {
-      uint32_t run = first[j] + os[base + j];
+      uint32_t run = os[base + j];
 #pragma unroll
       for (int ww = 0; ww < kSortWaves; ++ww) {
         const uint32_t n = next[ww * span + j];
@@ -233,15 +213,12 @@ hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* coun
   while ((1 << nbits) < p.nb) ++nbits;
   const dim3 grid((unsigned)(tiles * p.nseg()));
   const size_t window = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins);
-  // the buckets' totals follow the per-tile counts in the same buffer
-  uint32_t* totals = counts + p.nseg() * (int64_t)p.nb * tiles;
-  const int groups = (p.nb + kSortThreads - 1) / kSortThreads;
   hipLaunchKernelGGL(k_sort_count, grid, dim3(kSortThreads), window * 4, s, buckets, counts, p.L,
                      p.nb, tiles, p.nseg());
-  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)(p.nseg() * groups)), dim3(kSortThreads), 0, s,
-                     counts, totals, p.nb, tiles, groups);
-  hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kSortThreads), (kSortWaves + 1) * window * 4, s,
-                     buckets, counts, totals, perm, p.L, p.nb, tiles, nbits, p.nseg());
+  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)p.nseg()), dim3(1024), 0, s, counts, p.nb,
+                     tiles);
+  hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kSortThreads), kSortWaves * window * 4, s,
+                     buckets, counts, perm, p.L, p.nb, tiles, nbits, p.nseg());
   return hipGetLastError();
 }
 
