@@ -50,7 +50,9 @@ typedef enum {
   LSH_ATTN_ERR_INVALID_ARG = 1,   /* null required pointer, bad sizes, bad flag */
   LSH_ATTN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim, dtype) */
   LSH_ATTN_ERR_OUT_OF_MEMORY = 3, /* workspace allocation failed in create */
-  LSH_ATTN_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+  LSH_ATTN_ERR_HIP = 4,           /* a HIP runtime call or kernel launch failed */
+  LSH_ATTN_ERR_WORKSPACE_TOO_LARGE = 5  /* lsh_attn_forward_static: the problem's workspace
+                                           exceeds LSH_ATTN_STATIC_SCRATCH_BYTES */
 } lsh_attn_status_t;
 
 /* Flags (bit set in lsh_attn_config_t.flags). */
@@ -254,6 +256,31 @@ int lsh_attn_get_timing(lsh_attn_t handle, double* ms, int64_t* n_forwards);
  */
 #define LSH_ATTN_N_BWD_STAGES 4
 int lsh_attn_get_backward_timing(lsh_attn_t handle, double* ms, int64_t* n_backwards);
+
+/*
+ * The forward of lsh_attn_forward without a handle and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, results and conventions as lsh_attn_forward, with the config
+ * passed directly (host pointer); LSH_ATTN_FLAG_BACKWARD is not accepted
+ * (UNSUPPORTED). The workspace comes from a static device array of
+ * LSH_ATTN_STATIC_SCRATCH_BYTES that every GPU the library runs on holds
+ * until the process ends; its address is looked up once per device, on the
+ * first call there. Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads) race and give
+ * undefined results: order them on the device. No stage timing, and no
+ * counters (lsh_attn_get_stats needs a handle). The workspace is that of a
+ * handle for the same config (per-round rows, permutations, hash buffers):
+ * about 61 MB for batch 4, 8 heads, L 4096, head_dim 64, 64 buckets, 2
+ * rounds; larger problems need a handle.
+ * Errors: those of lsh_attn_create's validation and of lsh_attn_forward,
+ * UNSUPPORTED with LSH_ATTN_FLAG_BACKWARD, WORKSPACE_TOO_LARGE when the
+ * problem's workspace exceeds the static array (nothing is launched).
+ */
+#define LSH_ATTN_STATIC_SCRATCH_BYTES ((int64_t)64 << 20)
+int lsh_attn_forward_static(const lsh_attn_config_t* cfg, const void* qk, const void* v,
+                            const float* rotations, void* out, float* lse, int32_t* buckets,
+                            int32_t* perm, void* stream);
 
 /* Bytes of device workspace the handle holds. INVALID_ARG for null pointers. */
 int lsh_attn_workspace_bytes(lsh_attn_t handle, int64_t* bytes);

@@ -15,8 +15,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["LSHAttention", "ChunkedFeedForward", "load_library", "library_path", "LSHAttnError",
-           "EXPORTED_SYMBOLS", "FLAG_SEPARATE_GATHER"]
+__all__ = ["LSHAttention", "ChunkedFeedForward", "forward_static", "load_library",
+           "library_path", "LSHAttnError", "EXPORTED_SYMBOLS", "FLAG_SEPARATE_GATHER"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "_lib", "liblsh_attn.so")
@@ -29,11 +29,13 @@ FLAG_LOOK_AHEAD = 8
 FLAG_SAME_BUCKET = 16
 FLAG_NORM_QUERIES = 32
 FLAG_DEDUP = 64
-STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP"}
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "OUT_OF_MEMORY", 4: "HIP",
+          5: "WORKSPACE_TOO_LARGE"}
+STATIC_SCRATCH_BYTES = 64 << 20
 
 # Every function declared in include/lsh_attn.h.
 EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x",
-                    "lsh_attn_backward",
+                    "lsh_attn_backward", "lsh_attn_forward_static",
                     "lsh_attn_get_stats",
                     "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
                     "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror",
@@ -91,6 +93,7 @@ def load_library():
     lib.lsh_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_forward_x.argtypes = [P, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_backward.argtypes = [P, P, P, P, P, P, P, P]
+    lib.lsh_attn_forward_static.argtypes = [ctypes.POINTER(Config), P, P, P, P, P, P, P, P]
     lib.lsh_attn_get_stats.argtypes = [P, ctypes.POINTER(Stats)]
     lib.lsh_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.lsh_attn_set_timing.argtypes = [P, I]
@@ -110,6 +113,7 @@ def load_library():
     lib.lsh_ffn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.lsh_ffn_destroy.argtypes = [P]
     for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x", "lsh_attn_backward",
+              "lsh_attn_forward_static",
               "lsh_attn_get_stats",
               "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
               "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_ffn_create",
@@ -137,6 +141,55 @@ def make_config(batch, heads, seq_len, head_dim, n_buckets, n_rounds, chunk_len=
     oc = dc if out_dtype is None else _dtype_code(out_dtype)
     return Config(int(batch), int(heads), int(seq_len), int(head_dim), int(n_buckets),
                   int(n_rounds), int(chunk_len), int(causal), dc, oc, int(flags))
+
+
+def forward_static(qk, v, rotations, n_buckets, n_rounds, chunk_len=64, causal=False,
+                   out=None, lse=None, buckets=None, perm=None, out_dtype=None,
+                   separate_gather=False, fp32_round_outputs=False, look_ahead=False,
+                   same_bucket=False, norm_queries=False, dedup=False, stream=None):
+    """The forward through lsh_attn_forward_static: no handle, and no device
+    allocation in the library (its workspace is a static device array of
+    STATIC_SCRATCH_BYTES per GPU; calls that overlap on one GPU race). qk, v
+    [B, H, L, d] and rotations as for LSHAttention; out [B, H, L, d] and the
+    optional lse, buckets, perm [B, H, R, L] are written when given (out is
+    allocated with torch if None, on the caller's side of the boundary).
+    Returns out."""
+    lib = load_library()
+    B, H, L, d = qk.shape
+    flags = (FLAG_SEPARATE_GATHER if separate_gather else 0) | (
+        FLAG_FP32_ROUND_OUTPUTS if fp32_round_outputs else 0) | (
+        FLAG_LOOK_AHEAD if look_ahead else 0) | (FLAG_SAME_BUCKET if same_bucket else 0) | (
+        FLAG_NORM_QUERIES if norm_queries else 0) | (FLAG_DEDUP if dedup else 0)
+    cfg = make_config(B, H, L, d, n_buckets, n_rounds, chunk_len, causal, qk.dtype,
+                      out_dtype, flags)
+    dev = qk.device
+    for name, t in (("qk", qk), ("v", v)):
+        if t.device != dev or t.dtype != qk.dtype or tuple(t.shape) != (B, H, L, d) or \
+                not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {qk.dtype} tensor {(B, H, L, d)} "
+                             f"on {dev}")
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=_TORCH[cfg.out_dtype], device=dev)
+    per_round = (B, H, n_rounds, L)
+    for name, t, dt, shp in (("out", out, _TORCH[cfg.out_dtype], (B, H, L, d)),
+                             ("rotations", rotations, torch.float32,
+                              (n_rounds, d, n_buckets // 2)),
+                             ("lse", lse, torch.float32, per_round),
+                             ("buckets", buckets, torch.int32, per_round),
+                             ("perm", perm, torch.int32, per_round)):
+        if t is None:
+            continue
+        if t.device != dev or t.dtype != dt or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous {dt} tensor {shp} on {dev}")
+    s = (stream if stream is not None else torch.cuda.current_stream(dev)).cuda_stream
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    with torch.cuda.device(dev):
+        rc = lib.lsh_attn_forward_static(ctypes.byref(cfg), ptr(qk), ptr(v), ptr(rotations),
+                                         ptr(out), ptr(lse), ptr(buckets), ptr(perm),
+                                         ctypes.c_void_p(s))
+    if rc != 0:
+        raise LSHAttnError(rc, "lsh_attn_forward_static", lib)
+    return out
 
 
 class LSHAttention:

@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -38,6 +39,12 @@ constexpr int kEvPerCall = LSH_ATTN_N_STAGES + 2;
 
 __global__ void k_zero_u64(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+lsh::Problem problem_of(const lsh_attn_config_t* c) {
+  return lsh::Problem{c->batch,     c->heads,    c->seq_len,   c->head_dim,
+                      c->n_buckets, c->n_rounds, c->chunk_len, c->causal,
+                      c->dtype,     c->out_dtype, c->flags};
 }
 
 int validate(const lsh_attn_config_t* c) {
@@ -111,6 +118,57 @@ bool alloc(T** ptr, int64_t bytes, int64_t& total) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The forward's workspace buffers for a problem, in one order: where each
+// pointer goes and how many bytes it takes. create allocates each one; the
+// allocation-free forward carves them out of its static scratch.
+struct Part {
+  void** ptr;
+  int64_t bytes;
+};
+constexpr int kMaxParts = 20;
+int forward_parts(const lsh::Problem& p, lsh::Workspace& w, Part* parts) {
+  const int64_t rows = p.n_rows();
+  const int esize = p.dtype == LSH_ATTN_BF16 ? 2 : 4;
+  int n = 0;
+  auto add = [&](auto** ptr, int64_t bytes) { parts[n++] = Part{(void**)ptr, bytes}; };
+  add(&w.buckets, rows * 2);
+  add(&w.perm, rows * 4);
+  add(&w.o, p.nseg() * p.o_seg_rows() * p.d * (lsh::round_outputs_half(p) ? 2 : 4));
+  add(&w.lse, rows * 4);
+  add(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4);
+  add(&w.stats, 4 * 8);
+  if (lsh::attend_mfma_supported(p) || lsh::attend_variant_mfma_supported(p))
+    add(&w.knorm, p.n_token_heads() * 4);
+  if (lsh::hash_mfma_supported(p)) {
+    const int64_t hp = lsh::hash_half_pad(p);
+    add(&w.hash.rh, (int64_t)p.R * hp * p.d * 2);
+    add(&w.hash.rt, (int64_t)p.R * p.half() * p.d * 4);
+    add(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4);
+    add(&w.hash.queue_a, rows * 16);
+    add(&w.hash.queue_b, rows * 8);
+    add(&w.hash.x16, p.n_token_heads() * p.d * 2);
+    add(&w.hash.xnorm, p.n_token_heads() * 8);
+  }
+  if (p.flags & LSH_ATTN_FLAG_DEDUP) add(&w.inv, rows * 4);
+  if (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER) {
+    add(&w.qk_sorted, rows * p.d * esize);
+    add(&w.v_sorted, rows * p.d * esize);
+  }
+  return n;
+}
+
+// compute units of the current device (1 if the query fails)
+int device_cus(int device) {
+  int n_cu = 1;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device) !=
+          hipSuccess ||
+      n_cu < 1) {
+    (void)hipGetLastError();
+    n_cu = 1;
+  }
+  return n_cu;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,9 +180,7 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   if (rc != LSH_ATTN_OK) return rc;
   lsh_attn_s* h = new (std::nothrow) lsh_attn_s();
   if (!h) return LSH_ATTN_ERR_OUT_OF_MEMORY;
-  h->p = lsh::Problem{cfg->batch,  cfg->heads,   cfg->seq_len, cfg->head_dim,
-                      cfg->n_buckets, cfg->n_rounds, cfg->chunk_len, cfg->causal,
-                      cfg->dtype,  cfg->out_dtype, cfg->flags};
+  h->p = problem_of(cfg);
   if (hipGetDevice(&h->device) != hipSuccess) {
     (void)hipGetLastError();
     delete h;
@@ -132,34 +188,14 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   }
   const lsh::Problem& p = h->p;
   const int64_t rows = p.n_rows();
-  const int esize = p.dtype == LSH_ATTN_BF16 ? 2 : 4;
   lsh::Workspace& w = h->ws;
   int64_t& t = h->bytes;
-  bool ok = alloc(&w.buckets, rows * 2, t) && alloc(&w.perm, rows * 4, t) &&
-            alloc(&w.o, p.nseg() * p.o_seg_rows() * p.d * (lsh::round_outputs_half(p) ? 2 : 4), t) &&
-            alloc(&w.lse, rows * 4, t) &&
-            alloc(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4, t) &&
-            alloc(&w.stats, 4 * 8, t) && hipMemset(w.stats, 0, 4 * 8) == hipSuccess;
-  if (ok && (lsh::attend_mfma_supported(p) || lsh::attend_variant_mfma_supported(p)))
-    ok = alloc(&w.knorm, p.n_token_heads() * 4, t);
-  if (ok && lsh::hash_mfma_supported(p)) {
-    const int64_t hp = lsh::hash_half_pad(p);
-    if (hipDeviceGetAttribute(&w.hash.n_cu, hipDeviceAttributeMultiprocessorCount, h->device) !=
-            hipSuccess ||
-        w.hash.n_cu < 1) {
-      (void)hipGetLastError();
-      w.hash.n_cu = 1;
-    }
-    ok = alloc(&w.hash.rh, (int64_t)p.R * hp * p.d * 2, t) &&
-         alloc(&w.hash.rt, (int64_t)p.R * p.half() * p.d * 4, t) &&
-         alloc(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4, t) &&
-         alloc(&w.hash.queue_a, rows * 16, t) && alloc(&w.hash.queue_b, rows * 8, t) &&
-         alloc(&w.hash.x16, p.n_token_heads() * p.d * 2, t) &&
-         alloc(&w.hash.xnorm, p.n_token_heads() * 8, t);
-  }
-  if (ok && (p.flags & LSH_ATTN_FLAG_DEDUP)) ok = alloc(&w.inv, rows * 4, t);
-  if (ok && (p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER))
-    ok = alloc(&w.qk_sorted, rows * p.d * esize, t) && alloc(&w.v_sorted, rows * p.d * esize, t);
+  Part parts[kMaxParts];
+  const int np = forward_parts(p, w, parts);
+  bool ok = true;
+  for (int i = 0; ok && i < np; ++i) ok = alloc(parts[i].ptr, parts[i].bytes, t);
+  ok = ok && hipMemset(w.stats, 0, 4 * 8) == hipSuccess;
+  if (ok && lsh::hash_mfma_supported(p)) w.hash.n_cu = device_cus(h->device);
   if (ok && (p.flags & LSH_ATTN_FLAG_BACKWARD)) {
     lsh::BwdWorkspace& b = h->bw;
     ok = (lsh::attend_mfma_supported(p) ? alloc(&b.od, rows * 4, t)
@@ -185,14 +221,12 @@ namespace {
 
 // The forward after the inputs are checked; ev: the timed call's events or
 // null; x16_ready: the projection already prepared the hash's fp16 copy.
-int forward_body(lsh_attn_s* h, const void* qk, const void* v, const float* rotations, void* out,
-                 float* lse, int32_t* buckets, int32_t* perm, hipStream_t s, hipEvent_t* ev,
-                 bool x16_ready) {
-  const lsh::Problem& p = h->p;
+int forward_body(const lsh::Problem& p, lsh::Workspace& w, const void* qk, const void* v,
+                 const float* rotations, void* out, float* lse, int32_t* buckets, int32_t* perm,
+                 hipStream_t s, hipEvent_t* ev, bool x16_ready) {
   auto mark = [&](int j) {
     if (ev) hipEventRecord(ev[j], s);
   };
-  lsh::Workspace& w = h->ws;
   int32_t* pm = perm ? perm : w.perm;
   float* ls = lse ? lse : w.lse;
   hipError_t e = hipSuccess;
@@ -268,7 +302,8 @@ int lsh_attn_forward(lsh_attn_t h, const void* qk, const void* v, const float* r
   h->last_stream = s;
   hipEvent_t* ev = next_events(h, false);
   return release_on_error(h, ev,
-                          forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, ev, false));
+                          forward_body(h->p, h->ws, qk, v, rotations, out, lse, buckets, perm, s,
+                                       ev, false));
 }
 
 int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const void* w_qk,
@@ -292,7 +327,8 @@ int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const voi
   if (ev) hipEventRecord(ev[9], s);
   if (e != hipSuccess) return release_on_error(h, ev, LSH_ATTN_ERR_HIP);
   return release_on_error(
-      h, ev, forward_body(h, qk, v, rotations, out, lse, buckets, perm, s, ev, x16_ready));
+      h, ev,
+      forward_body(h->p, h->ws, qk, v, rotations, out, lse, buckets, perm, s, ev, x16_ready));
 }
 
 int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
@@ -457,6 +493,99 @@ int lsh_attn_destroy(lsh_attn_t h) {
   return LSH_ATTN_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free forward. Its workspace is carved from `scratch`, a
+// static device array of kStaticScratchBytes that every GPU the library runs
+// on holds for the life of the process. In host code the array's name is only
+// a stand-in: its device address comes from hipGetSymbolAddress, once per
+// device (with that device current), and only that address is used.
+namespace {
+
+constexpr int64_t kStaticScratchBytes = (int64_t)64 << 20;  // LSH_ATTN_STATIC_SCRATCH_BYTES
+static_assert(kStaticScratchBytes == LSH_ATTN_STATIC_SCRATCH_BYTES, "header and source agree");
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+  void* ptr = nullptr;  // device address of this device's scratch
+  int n_cu = 0;
+  int hash_per_cu = 0;  // the hash kernel's resident workgroups per CU (0: not yet queried)
+  bool proj_attr = false;
+};
+StaticDevice g_static[kMaxDevices];
+std::mutex g_static_mutex;
+
+// Set-up on the current device (first call there): the scratch's address.
+int static_device(int device, StaticDevice** out) {
+  if (device < 0 || device >= kMaxDevices) return LSH_ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_static_mutex);
+  StaticDevice& sd = g_static[device];
+  if (!sd.ptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return LSH_ATTN_ERR_HIP;
+    }
+    sd.n_cu = device_cus(device);
+    sd.ptr = ptr;
+  }
+  *out = &sd;
+  return LSH_ATTN_OK;
+}
+
+// bytes of the forward's workspace parts, each rounded up to 256
+int64_t static_bytes(const lsh::Problem& p) {
+  lsh::Workspace w;
+  Part parts[kMaxParts];
+  const int np = forward_parts(p, w, parts);
+  int64_t total = 0;
+  for (int i = 0; i < np; ++i) total += (parts[i].bytes + 255) / 256 * 256;
+  return total;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lsh_attn_forward_static(const lsh_attn_config_t* cfg, const void* qk, const void* v,
+                            const float* rotations, void* out, float* lse, int32_t* buckets,
+                            int32_t* perm, void* stream) {
+  int rc = validate(cfg);
+  if (rc != LSH_ATTN_OK) return rc;
+  if (cfg->flags & LSH_ATTN_FLAG_BACKWARD) return LSH_ATTN_ERR_UNSUPPORTED;
+  if (!qk || !v || !out) return LSH_ATTN_ERR_INVALID_ARG;
+  if (cfg->n_buckets > 1 && !rotations) return LSH_ATTN_ERR_INVALID_ARG;
+  if (!aligned16(qk) || !aligned16(v) || !aligned16(out)) return LSH_ATTN_ERR_INVALID_ARG;
+  const lsh::Problem p = problem_of(cfg);
+  if (static_bytes(p) > kStaticScratchBytes) return LSH_ATTN_ERR_WORKSPACE_TOO_LARGE;
+  int device = -1;
+  if (hipGetDevice(&device) != hipSuccess) {
+    (void)hipGetLastError();
+    return LSH_ATTN_ERR_HIP;
+  }
+  StaticDevice* sd = nullptr;
+  rc = static_device(device, &sd);
+  if (rc != LSH_ATTN_OK) return rc;
+  lsh::Workspace w;
+  Part parts[kMaxParts];
+  const int np = forward_parts(p, w, parts);
+  unsigned char* base = (unsigned char*)sd->ptr;
+  int64_t off = 0;
+  for (int i = 0; i < np; ++i) {
+    *parts[i].ptr = base + off;
+    off += (parts[i].bytes + 255) / 256 * 256;
+  }
+  w.hash.n_cu = sd->n_cu;
+  w.hash.per_cu = sd->hash_per_cu;
+  w.hash.proj_attr = sd->proj_attr;
+  hipStream_t s = (hipStream_t)stream;
+  rc = forward_body(p, w, qk, v, rotations, out, lse, buckets, perm, s, nullptr, false);
+  sd->hash_per_cu = w.hash.per_cu;
+  return rc;
+}
+
 const char* lsh_attn_strerror(int status) {
   switch (status) {
     case LSH_ATTN_OK: return "ok";
@@ -464,6 +593,8 @@ const char* lsh_attn_strerror(int status) {
     case LSH_ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case LSH_ATTN_ERR_OUT_OF_MEMORY: return "out of device memory";
     case LSH_ATTN_ERR_HIP: return "HIP runtime or launch error";
+    case LSH_ATTN_ERR_WORKSPACE_TOO_LARGE:
+      return "workspace larger than the static scratch of lsh_attn_forward_static (64 MiB)";
     default: return "unknown status";
   }
 }

@@ -122,3 +122,30 @@ def test_ffn_null_handle_and_pointers_are_invalid():
     assert lib.lsh_ffn_set_timing(None, 1) == 1
     assert lib.lsh_ffn_workspace_bytes(None, None) == 1
     assert lib.lsh_ffn_destroy(None) == 0
+
+
+def test_static_forward_rejects_on_the_host():
+    """lsh_attn_forward_static checks the config and the size of its workspace
+    against the static scratch before any HIP call (fake, aligned pointers:
+    nothing is launched)."""
+    lib = lat.load_library()
+    P = ctypes.c_void_p
+    fake = P(4096)
+
+    def call(**kw):
+        base = dict(batch=1, heads=2, seq_len=256, head_dim=64, n_buckets=8, n_rounds=2,
+                    chunk_len=64, causal=0, dtype=lat.BF16, out_dtype=lat.BF16, flags=0)
+        base.update(kw)
+        cfg = lat.Config(**base)
+        return lib.lsh_attn_forward_static(ctypes.byref(cfg), fake, fake, fake, fake, None,
+                                           None, None, None)
+
+    assert call(seq_len=100) == 1                    # invalid config
+    assert call(head_dim=96) == 2                    # unsupported shape
+    assert call(flags=lat.FLAG_BACKWARD) == 2        # no backward without a handle
+    # Text-64K needs ~1.6 GB of workspace: beyond the 64 MiB scratch
+    assert call(batch=1, heads=8, seq_len=65536, head_dim=128, n_buckets=1024,
+                n_rounds=4, causal=1) == 5
+    assert lib.lsh_attn_forward_static(None, fake, fake, fake, fake, None, None, None,
+                                       None) == 1
+    assert b"static scratch" in lib.lsh_attn_strerror(5)
