@@ -144,9 +144,10 @@ hipError_t launch_attend(const Problem& p, const void* qk, const void* v, const 
                          hipStream_t s) {
   if (attend_mfma_supported(p)) {
     if (round_outputs_half(p))
-      return launch_attend_mfma<_Float16>(p, qk, v, qk_sorted, v_sorted, perm, knorm,
+      return launch_attend_mfma<_Float16>(p, qk, v, qk_sorted, v_sorted, perm, knorm, buckets,
                                           (_Float16*)o, lse, s);
-    return launch_attend_mfma<float>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
+    return launch_attend_mfma<float>(p, qk, v, qk_sorted, v_sorted, perm, knorm, buckets, o, lse,
+                                     s);
   }
   if (attend_variant_mfma_supported(p))
     return launch_attend_variant_mfma(p, qk, v, perm, knorm, buckets, inv, o, lse, s);

@@ -47,6 +47,13 @@
 // or 16 (fp32) contiguous bytes. An MFMA against a block of ones gives the row
 // sums of the bf16-rounded P, so numerator and denominator use the same
 // weights; the logsumexp takes the fp32 sum of the unrounded p.
+//
+// Two variant readings run in this kernel as template flags (same overview
+// page, section 2.1): NQ, queries unit-normalised too (logits scaled by 1/|q|,
+// so the shift becomes log2(e)/sqrt(d); a zero query has logits 0); SB, only
+// keys in the query's own bucket of the round are attendable (bucket ids
+// staged per key, read through the permutation like the rows). The
+// look-ahead window and the de-duplicated union have their own kernel.
 #include <type_traits>
 
 #include "dtype.h"
@@ -75,7 +82,8 @@ struct Lds {
   static constexpr int kPos = kScale + 2 * kChunk * 4;
   static constexpr int kBound = kPos + 2 * kChunk * 4;
   static constexpr int kPermNext = kBound + 2 * kChunk * 4;  // positions of the next chunk
-  static constexpr int kBytes = kPermNext + kChunk * 4;
+  static constexpr int kBkt = kPermNext + kChunk * 4;         // bucket id per key (SB)
+  static constexpr int kBytes = kBkt + 2 * kChunk * 4;
 };
 
 __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
@@ -96,6 +104,7 @@ struct ChunkRegs {
   uint4 v[4];
   int pos;   // original position of row t % 64
   float n2;  // squared norm of qk row t (t < 64)
+  int bkt;   // bucket id of row t in the round (t < 64; same-bucket reading)
 };
 
 // permutation entries (original positions) a chunk's loads need
@@ -125,11 +134,11 @@ __device__ __forceinline__ void read_perm(PermRegs<D>& pr, const int* pn) {
 // Rows are addressed as a wave-uniform base (the segment's first row) plus a
 // 32-bit byte offset per lane, every offset computed before the first load,
 // so no load waits for an earlier one to release its address registers.
-template <int D, bool SORTED>
+template <int D, bool SORTED, bool SB = false>
 __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& pr, int c,
                                            const uint4* qk_rows, const uint4* v_rows,
                                            const float* knorm, int64_t row0,
-                                           int64_t sorted_row0) {
+                                           int64_t sorted_row0, const uint16_t* bk_seg = nullptr) {
   using CR = ChunkRegs<D>;
   constexpr uint32_t kRowBytes = D * 2;
   const int t = threadIdx.x;
@@ -147,6 +156,9 @@ __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& 
   cr.pos = pr.pos;
   __builtin_amdgcn_sched_barrier(0);
   if (t < kChunk) cr.n2 = knorm[row0 + pr.pos];
+  if constexpr (SB) {
+    if (t < kChunk) cr.bkt = bk_seg[pr.pos];
+  }
 #pragma unroll
   for (int k = 0; k < CR::kQ; ++k) cr.qk[k] = *(const uint4*)(qb + qoff[k]);
   if (t < CR::kVUsers) {
@@ -155,7 +167,7 @@ __device__ __forceinline__ void fetch_rows(ChunkRegs<D>& cr, const PermRegs<D>& 
   }
 }
 
-template <int D>
+template <int D, bool SB = false>
 __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const ChunkRegs<D>& cr) {
   using Lay = Lds<D>;
   using CR = ChunkRegs<D>;
@@ -177,6 +189,7 @@ __device__ __forceinline__ void stage_chunk(unsigned char* lds, int sl, const Ch
       ((float*)(lds + Lay::kScale))[sl * kChunk + t] = nn > 0.f ? sc / nrm : 0.f;
       ((int*)(lds + Lay::kPos))[sl * kChunk + t] = cr.pos;
       ((float*)(lds + Lay::kBound))[sl * kChunk + t] = sc * nrm;
+      if constexpr (SB) ((int*)(lds + Lay::kBkt))[sl * kChunk + t] = cr.bkt;
     }
   }
   // v rows, 4 keys x 8 dims per piece: group qd is half (qd / 4) % 2 of key
@@ -211,13 +224,14 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
 // per query the scalar dout(i) . o_r(i) ([seg, L] fp32; dout(i) . v_i for a
 // query that saw only itself, whose output is v_i), dout being bf16 rows
 // [B*H, L, D].
-template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false>
+template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false, bool NQ = false,
+          bool SB = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attend_mfma(
     const uint4* __restrict__ qk, const uint4* __restrict__ v, const uint4* __restrict__ qk_s,
     const uint4* __restrict__ v_s, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, OT* __restrict__ o, float* __restrict__ lse, int L, int R,
     int nseg, int chunks_per_wg, int ranges, int group_segs, int64_t o_seg_rows,
-    const unsigned char* __restrict__ dout) {
+    const unsigned char* __restrict__ dout, const uint16_t* __restrict__ buckets) {
   using Lay = Lds<D>;
   constexpr int KS = D / 32;  // 32-dim K-steps of QK^T
   constexpr int DT = D / 16;  // 16-dim tiles of the output
@@ -242,6 +256,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int64_t srow0 = seg * L;
   const uint4* qk_rows = SORTED ? qk_s : qk;
   const uint4* v_rows = SORTED ? v_s : v;
+  const uint16_t* bk_seg = SB ? buckets + seg * L : nullptr;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -258,8 +273,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     perm_to_lds(c0 - 1);
     __syncthreads();
     read_perm<D>(pr, pn);
-    fetch_rows<D, SORTED>(cr, pr, c0 - 1, qk_rows, v_rows, knorm, row0, srow0);
-    stage_chunk<D>(lds, (c0 - 1) & 1, cr);
+    fetch_rows<D, SORTED, SB>(cr, pr, c0 - 1, qk_rows, v_rows, knorm, row0, srow0, bk_seg);
+    stage_chunk<D, SB>(lds, (c0 - 1) & 1, cr);
     __syncthreads();
   } else {
     // chunk 0 has no previous chunk: zero keys and values in its slot
@@ -272,8 +287,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   perm_to_lds(c0);
   __syncthreads();
   read_perm<D>(pr, pn);
-  fetch_rows<D, SORTED>(cr, pr, c0, qk_rows, v_rows, knorm, row0, srow0);
-  stage_chunk<D>(lds, c0 & 1, cr);
+  fetch_rows<D, SORTED, SB>(cr, pr, c0, qk_rows, v_rows, knorm, row0, srow0, bk_seg);
+  stage_chunk<D, SB>(lds, c0 & 1, cr);
   __syncthreads();
   if (c0 + 1 < c1) perm_to_lds(c0 + 1);
   __syncthreads();
@@ -282,6 +297,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float* kscale = (const float*)(lds + Lay::kScale);
   const int* kpos = (const int*)(lds + Lay::kPos);
   const float* kbound = (const float*)(lds + Lay::kBound);
+  const int* kbkt = (const int*)(lds + Lay::kBkt);
   const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
   const uint32_t ones_u[4] = {one2, one2, one2, one2};
   const bf16x8_t ones = *(const bf16x8_t*)ones_u;
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int c = c0; c < c1; ++c) {
     if (c + 1 < c1) {
       read_perm<D>(pr, pn);
-      fetch_rows<D, SORTED>(cr, pr, c + 1, qk_rows, v_rows, knorm, row0, srow0);
+      fetch_rows<D, SORTED, SB>(cr, pr, c + 1, qk_rows, v_rows, knorm, row0, srow0, bk_seg);
       if (c + 2 < c1 && threadIdx.x < kChunk) pnext = pm[(c + 2) * kChunk + threadIdx.x];
     }
     const int cur = c & 1, prv = cur ^ 1;
@@ -297,6 +313,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int q = 16 * w + lq;
     float mq = kbound[cur * kChunk + q];
     const int posq = kpos[cur * kChunk + q];
+    // NQ: logits times 1/|q| (mq = log2(e)|q|/sqrt(d), so |q| = mq / that
+    // factor); the Cauchy-Schwarz shift is then log2(e)/sqrt(d), or 0 for a
+    // zero query (whose logits are 0)
+    float qs = 1.0f;
+    if constexpr (NQ) {
+      const float sc = kLog2e / sqrtf((float)D);
+      qs = mq > 0.f ? sc / mq : 0.f;
+      mq = mq > 0.f ? sc : 0.f;
+    }
+    const int bq = SB ? kbkt[cur * kChunk + q] : 0;
     // DOT: the query's dout, dims 16 dt + 4g + 0..3 (as the output tiles)
     uint2 dz[DOT ? DT : 1];
     if constexpr (DOT) {
@@ -324,8 +350,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     // (absent is uniform; a bitwise or keeps it from becoming a branch that
     // splits the key reads)
-    auto masked = [&](bool absent, int kp) -> bool {
-      return absent | (CAUSAL ? kp >= posq : kp == posq);
+    auto masked = [&](bool absent, int kp, int kbk) -> bool {
+      return absent | (CAUSAL ? kp >= posq : kp == posq) | (SB && kbk != bq);
     };
     if (__ballot(mq > kBoundLimit) != 0ull) {
       float mx = -INFINITY;
@@ -336,11 +362,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int key = (kb & 3) * 16 + 4 * g;
         const float4 sc = *(const float4*)(kscale + sl * kChunk + key);
         const int4 kp = *(const int4*)(kpos + sl * kChunk + key);
-        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+        const int4 kk = SB ? *(const int4*)(kbkt + sl * kChunk + key) : int4{};
+        const float scv[4] = {sc.x * qs, sc.y * qs, sc.z * qs, sc.w * qs};
         const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
+        const int kbv[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          mx = fmaxf(mx, masked(kb < kb0, kpv[b]) ? -INFINITY : sb[b] * scv[b]);
+          mx = fmaxf(mx, masked(kb < kb0, kpv[b], kbv[b]) ? -INFINITY : sb[b] * scv[b]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -358,13 +386,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int key = (kb & 3) * 16 + 4 * g;
         const float4 sc = *(const float4*)(kscale + sl * kChunk + key);
         const int4 kp = *(const int4*)(kpos + sl * kChunk + key);
-        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+        const int4 kk = SB ? *(const int4*)(kbkt + sl * kChunk + key) : int4{};
+        const float scv[4] = {sc.x * qs, sc.y * qs, sc.z * qs, sc.w * qs};
         const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
+        const int kbv[4] = {kk.x, kk.y, kk.z, kk.w};
         const bool absent = kb < kb0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const float x = fmaf(s[b], scv[b], -mq);
-          const float pv = __builtin_amdgcn_exp2f(masked(absent, kpv[b]) ? -INFINITY : x);
+          const float pv = __builtin_amdgcn_exp2f(masked(absent, kpv[b], kbv[b]) ? -INFINITY : x);
           rowsum += pv;
           pf[4 * half + b] = (__bf16)pv;
         }
@@ -406,7 +436,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     rowsum += __shfl_xor(rowsum, 32);
     __syncthreads();  // every wave is done with slot prv
     if (c + 1 < c1) {
-      stage_chunk<D>(lds, prv, cr);
+      stage_chunk<D, SB>(lds, prv, cr);
       if (c + 2 < c1 && threadIdx.x < kChunk) pn[threadIdx.x] = pnext;
     }
     // normalise and scatter to the query's original position: lane holds dims
@@ -483,10 +513,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 constexpr int kRangeChunks = 16;
 constexpr int kResidentBlocks = 512;
 
-template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false>
+template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false, bool NQ = false,
+          bool SB = false>
 void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_s,
                 const void* v_s, const int32_t* perm, const float* knorm, OT* o, float* lse,
-                hipStream_t s, const void* dout = nullptr) {
+                hipStream_t s, const void* dout = nullptr, const uint16_t* buckets = nullptr) {
   const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
   const int per = nchunks < kRangeChunks ? nchunks : kRangeChunks;
@@ -497,16 +528,39 @@ void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_
   int64_t group_segs = heads * p.R;
   if (group_segs > nseg) group_segs = nseg;
   const size_t shmem = Lds<D>::kBytes;
-  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED, DOT>), dim3((unsigned)(nseg * ranges)),
-                     dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
-                     (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse, p.L,
-                     p.R, (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows(),
-                     (const unsigned char*)dout);
+  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED, DOT, NQ, SB>),
+                     dim3((unsigned)(nseg * ranges)), dim3(kThreads), shmem, s, (const uint4*)qk,
+                     (const uint4*)v, (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse,
+                     p.L, p.R, (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows(),
+                     (const unsigned char*)dout, buckets);
+}
+
+// the unit-query and same-bucket readings (fused gather only)
+template <int D, typename OT, bool CAUSAL>
+void launch_nq_sb(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+                  const float* knorm, const uint16_t* buckets, OT* o, float* lse, hipStream_t s) {
+  const bool nq = (p.flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
+  const bool sb = (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  if (nq && sb)
+    launch_one<D, OT, CAUSAL, false, false, true, true>(p, qk, v, nullptr, nullptr, perm, knorm,
+                                                        o, lse, s, nullptr, buckets);
+  else if (nq)
+    launch_one<D, OT, CAUSAL, false, false, true, false>(p, qk, v, nullptr, nullptr, perm, knorm,
+                                                         o, lse, s, nullptr, buckets);
+  else
+    launch_one<D, OT, CAUSAL, false, false, false, true>(p, qk, v, nullptr, nullptr, perm, knorm,
+                                                         o, lse, s, nullptr, buckets);
 }
 
 template <int D, typename OT>
 void launch_d(const Problem& p, const void* qk, const void* v, const void* qk_s, const void* v_s,
-              const int32_t* perm, const float* knorm, OT* o, float* lse, hipStream_t s) {
+              const int32_t* perm, const float* knorm, const uint16_t* buckets, OT* o,
+              float* lse, hipStream_t s) {
+  if (p.flags & (LSH_ATTN_FLAG_NORM_QUERIES | LSH_ATTN_FLAG_SAME_BUCKET)) {
+    if (p.causal) launch_nq_sb<D, OT, true>(p, qk, v, perm, knorm, buckets, o, lse, s);
+    else launch_nq_sb<D, OT, false>(p, qk, v, perm, knorm, buckets, o, lse, s);
+    return;
+  }
   const bool sorted = qk_s != nullptr;
   if (p.causal) {
     if (sorted) launch_one<D, OT, true, true>(p, qk, v, qk_s, v_s, perm, knorm, o, lse, s);
@@ -520,14 +574,20 @@ void launch_d(const Problem& p, const void* qk, const void* v, const void* qk_s,
 }  // namespace
 
 bool attend_mfma_supported(const Problem& p) {
+  // unit queries and the same-bucket mask run here too (with the gather fused);
+  // the look-ahead window and the de-duplicated union have their own kernel
+  const int own = LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_DEDUP;
+  const int here = LSH_ATTN_FLAG_NORM_QUERIES | LSH_ATTN_FLAG_SAME_BUCKET;
   return p.dtype == LSH_ATTN_BF16 && p.m == kChunk && (p.d == 64 || p.d == 128) &&
-         !(p.flags & kVariantFlags);
+         !(p.flags & own) &&
+         (!(p.flags & here) || !(p.flags & LSH_ATTN_FLAG_SEPARATE_GATHER));
 }
 
 template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
-                              const float* knorm, OT* o, float* lse, hipStream_t s) {
+                              const float* knorm, const uint16_t* buckets, OT* o, float* lse,
+                              hipStream_t s) {
   static bool configured = false;
   if (!configured) {
     // allow the dynamic LDS size above the 64 KiB default
@@ -539,10 +599,19 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
     (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, false, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    const void* variants[] = {
+        (const void*)k_attend_mfma<128, OT, true, false, false, true, false>,
+        (const void*)k_attend_mfma<128, OT, true, false, false, false, true>,
+        (const void*)k_attend_mfma<128, OT, true, false, false, true, true>,
+        (const void*)k_attend_mfma<128, OT, false, false, false, true, false>,
+        (const void*)k_attend_mfma<128, OT, false, false, false, false, true>,
+        (const void*)k_attend_mfma<128, OT, false, false, false, true, true>};
+    for (const void* f : variants)
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
     configured = true;
   }
-  if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
-  else launch_d<128, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, o, lse, s);
+  if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, buckets, o, lse, s);
+  else launch_d<128, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, buckets, o, lse, s);
   return hipGetLastError();
 }
 
@@ -572,10 +641,11 @@ hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* 
 }
 
 template hipError_t launch_attend_mfma<float>(const Problem&, const void*, const void*, const void*,
-                                              const void*, const int32_t*, const float*, float*,
-                                              float*, hipStream_t);
+                                              const void*, const int32_t*, const float*,
+                                              const uint16_t*, float*, float*, hipStream_t);
 template hipError_t launch_attend_mfma<_Float16>(const Problem&, const void*, const void*,
                                                  const void*, const void*, const int32_t*,
-                                                 const float*, _Float16*, float*, hipStream_t);
+                                                 const float*, const uint16_t*, _Float16*, float*,
+                                                 hipStream_t);
 
 }  // namespace lsh

@@ -127,11 +127,15 @@ hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const vo
                                       float* lse, hipStream_t s);
 // inv[seg, perm[seg, s]] = s
 hipError_t launch_inverse_perm(const Problem& p, const int32_t* perm, int32_t* inv, hipStream_t s);
+// bf16, chunk_len 64, d in {64, 128}: the default reading, and the unit-query
+// and same-bucket readings with the gather fused
 bool attend_mfma_supported(const Problem& p);
+// buckets [seg, L]: read with LSH_ATTN_FLAG_SAME_BUCKET (may be null otherwise)
 template <typename OT>
 hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
-                              const float* knorm, OT* o, float* lse, hipStream_t s);
+                              const float* knorm, const uint16_t* buckets, OT* o, float* lse,
+                              hipStream_t s);
 // the per-round attention of the backward: lse as above, and per query the
 // scalar dout . o_r in od [seg, L] instead of the rows
 hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* v,

@@ -96,6 +96,7 @@ def _load():
             "lsh_oracle_forward": [C, P, P, P, P, P, P, P, P, P],
             "lsh_oracle_attend_rows": [C, P, P, P, P, ctypes.c_int64, P, P, P],
             "lsh_oracle_backward": [C, P, P, P, P, P, P],
+            "lsh_oracle_backward_magnitudes": [C, P, P, P, P, P, P],
             "lsh_oracle_project": [C, ctypes.c_int64, P, P, P, P, P],
             "lsh_oracle_ffn": [ctypes.c_int64] * 4 + [P] * 8,
         }.items():
@@ -211,6 +212,18 @@ def backward(c: Config, qk, v, perm, dout):
     _chk(_load().lsh_oracle_backward(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do), _p(dqk),
                                      _p(dv)), "backward")
     return dqk, dv
+
+
+def backward_magnitudes(c: Config, qk, v, perm, dout):
+    """(mdqk, mdv) [B, H, L, d]: sums of upper bounds of the absolute values of
+    the terms of dqk and dv (|dqk| <= mdqk, |dv| <= mdv), for error bounds of
+    a finite-precision backward."""
+    qk, v, pm, do = _f64(qk), _f64(v), _i32(perm), _f64(dout)
+    mq = np.empty((c.batch, c.heads, c.seq_len, c.head_dim), np.float64)
+    mv = np.empty_like(mq)
+    _chk(_load().lsh_oracle_backward_magnitudes(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do),
+                                                _p(mq), _p(mv)), "backward_magnitudes")
+    return mq, mv
 
 
 def ffn(y1, w1, b1, w2, b2, x2=None, chunk_rows=None, return_hidden=False):

@@ -589,6 +589,128 @@ done:
   return rc;
 }
 
+/* ---------------------------------------------------------------------------
+ * Magnitudes of the backward's terms, for error bounds on a finite-precision
+ * backward (test infrastructure: the tolerance of a GPU backward is a unit
+ * roundoff times these sums). Same traversal as lsh_oracle_backward, with
+ * every term replaced by an upper bound of its absolute value:
+ *   A_ij   = w_r(i) P_ij (|dout_i . v_j| + |dout_i . out_i| + 2 E_i),
+ *            E_i = sum over rounds r' of w_r'(i) sum_j' P_ij' |dout_i . v_j'|,
+ *            which bounds |dS_ij| and also scales the error of dS_ij that
+ *            comes from an inexact dout_i . out_i;
+ *   mdv[j] += w_r(i) P_ij |dout_i|            (elementwise; self-only rounds:
+ *                                              w_r(i) |dout_i| at i);
+ *   mdq[i] += A_ij |khat_j| / sqrt(d),  mdk[j] += A_ij |q_i| / sqrt(d);
+ *   mdqk   = mdq + (|mdk| + |khat| (|khat| . mdk)) / |k|   (the normalisation's
+ *            Jacobian with every term taken in absolute value).
+ * So |dv| <= mdv and |dqk| <= mdqk elementwise (triangle inequality), with
+ * equality for dv when every dout and v entry is non-negative.
+ * Default reading only (variant 0; otherwise -10). */
+int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
+                                   const double* v, const int32_t* perm, const double* dout,
+                                   double* mdqk, double* mdv) {
+  int rc = lsh_oracle_check(c);
+  if (rc) return rc;
+  if (c->variant != 0) return -10;
+  const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
+  const int64_t nbh = (int64_t)c->batch * c->heads;
+  const size_t nsl = seg_count(c) * (size_t)L;
+  double* o = (double*)malloc(sizeof(double) * nsl * (size_t)d);
+  double* lse = (double*)malloc(sizeof(double) * nsl);
+  double* out = (double*)malloc(sizeof(double) * (size_t)(nbh * L * d));
+  double* mdk = (double*)calloc((size_t)(nbh * L * d), sizeof(double));
+  double* eq = (double*)calloc((size_t)(nbh * L), sizeof(double));
+  if (!o || !lse || !out || !mdk || !eq) { rc = -8; goto done; }
+  rc = lsh_oracle_attend(c, qk, v, perm, NULL, o, lse);
+  if (rc) goto done;
+  rc = lsh_oracle_combine(c, o, lse, out);
+  if (rc) goto done;
+  for (int64_t x = 0; x < nbh * L * d; ++x) { mdqk[x] = 0.0; mdv[x] = 0.0; }
+#pragma omp parallel
+  {
+    double* khat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < nbh; ++bh) {
+      const double* qk_bh = qk + bh * L * d;
+      const double* v_bh = v + bh * L * d;
+      /* two passes over the rounds: E_i first, then the sums */
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int64_t r = 0; r < R; ++r) {
+          const int64_t seg = bh * R + r;
+          const int32_t* pm = perm + seg * L;
+          for (int64_t s = 0; s < L; ++s) {
+            const int64_t i = pm[s];
+            double mx = -INFINITY;
+            for (int64_t rr = 0; rr < R; ++rr) {
+              const double l = lse[(bh * R + rr) * L + i];
+              mx = l > mx ? l : mx;
+            }
+            double sum = 0.0;
+            for (int64_t rr = 0; rr < R; ++rr) sum += exp(lse[(bh * R + rr) * L + i] - mx);
+            const double w = exp(lse[seg * L + i] - mx) / sum;
+            const double* drow = dout + (bh * L + i) * d;
+            const int64_t n = window(c, qk_bh, pm, NULL, s, khat, qhat, logit, key);
+            if (n == 0) {
+              if (pass == 1)
+                for (int64_t u = 0; u < d; ++u) mdv[(bh * L + i) * d + u] += w * fabs(drow[u]);
+              continue;
+            }
+            const double l = lse[seg * L + i];
+            const double* outrow = out + (bh * L + i) * d;
+            double dq_out = 0.0;
+            for (int64_t u = 0; u < d; ++u) dq_out += drow[u] * outrow[u];
+            const double* q = qk_bh + i * d;
+            const double scale = 1.0 / sqrt((double)d);
+            for (int64_t a = 0; a < n; ++a) {
+              const int64_t j = key[a];
+              const double wp = w * exp(logit[a] - l);
+              double dpv = 0.0;
+              for (int64_t u = 0; u < d; ++u) dpv += drow[u] * v_bh[j * d + u];
+              if (pass == 0) {
+                eq[bh * L + i] += wp * fabs(dpv);
+                continue;
+              }
+              const double A = wp * (fabs(dpv) + fabs(dq_out) + 2.0 * eq[bh * L + i]);
+              unit_key(qk_bh + j * d, d, khat);
+              for (int64_t u = 0; u < d; ++u) {
+                mdv[(bh * L + j) * d + u] += wp * fabs(drow[u]);
+                mdqk[(bh * L + i) * d + u] += A * fabs(khat[u]) * scale;
+                mdk[(bh * L + j) * d + u] += A * fabs(q[u]) * scale;
+              }
+            }
+          }
+        }
+      }
+      for (int64_t j = 0; j < L; ++j) {
+        const double* k = qk_bh + j * d;
+        double ss = 0.0;
+        for (int64_t u = 0; u < d; ++u) ss += k[u] * k[u];
+        const double nrm = sqrt(ss);
+        if (nrm == 0.0) continue;
+        const double* mk = mdk + (bh * L + j) * d;
+        double proj = 0.0;
+        for (int64_t u = 0; u < d; ++u) proj += fabs(k[u] / nrm) * mk[u];
+        for (int64_t u = 0; u < d; ++u)
+          mdqk[(bh * L + j) * d + u] += (mk[u] + fabs(k[u] / nrm) * proj) / nrm;
+      }
+    }
+    free(khat);
+    free(qhat);
+    free(logit);
+    free(key);
+  }
+done:
+  free(o);
+  free(lse);
+  free(out);
+  free(mdk);
+  free(eq);
+  return rc;
+}
+
 int lsh_oracle_attend_rows(const lsh_oracle_config* c, const double* qk, const double* v,
                            const int32_t* perm, const int32_t* buckets, int64_t n_rows,
                            const int64_t* rows, double* out_rows, double* lse_rows) {

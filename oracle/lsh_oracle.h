@@ -110,6 +110,13 @@ int lsh_oracle_forward(const lsh_oracle_config* cfg, const double* qk, const dou
 int lsh_oracle_backward(const lsh_oracle_config* cfg, const double* qk, const double* v,
                         const int32_t* perm, const double* dout, double* dqk, double* dv);
 
+/* Upper bounds of the absolute values of the backward's terms, summed as the
+ * backward sums them (test infrastructure for error bounds): |dv| <= mdv and
+ * |dqk| <= mdqk elementwise; see lsh_oracle.c. Default reading only. */
+int lsh_oracle_backward_magnitudes(const lsh_oracle_config* cfg, const double* qk,
+                                   const double* v, const int32_t* perm, const double* dout,
+                                   double* mdqk, double* mdv);
+
 /* The shared-QK and value projections of a layer input ([TT] shared-QK section:
  * one linear map gives queries and keys, a second one the values):
  *   qk[b, h, i, e] = sum_k x[b, i, k] w_qk[h * d + e, k],  v likewise with w_v.

@@ -104,3 +104,66 @@ def test_backward_zero_key_stays_finite(oracle_lib):
     pm, _ = oracle.sort(c, bk)
     dqk, dv = oracle.backward(c, qk, v, pm, rng.standard_normal((B, H, L, d)))
     assert np.isfinite(dqk).all() and np.isfinite(dv).all()
+
+
+def _mag_case(seed, causal, R=3, m=4, L=24, d=6, nb=6):
+    rng = np.random.default_rng(seed)
+    c = _cfg(1, 2, L, d, nb, R, m, causal)
+    qk = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, d))
+    rot = rng.standard_normal((R, d, nb // 2))
+    bk, _ = oracle.hash(c, qk, rot)
+    pm, _ = oracle.sort(c, bk)
+    dout = rng.standard_normal((1, 2, L, d))
+    return c, qk, v, pm, dout
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_magnitudes_bound_the_gradients(oracle_lib, causal):
+    """Each magnitude is a sum of upper bounds of the absolute values of the
+    gradient's terms, so it bounds the gradient elementwise; for dv, whose
+    terms are w P dout, it equals |dv| exactly when dout and v are
+    non-negative (every term then has the same sign)."""
+    c, qk, v, pm, dout = _mag_case(3 + int(causal), causal)
+    dqk, dv = oracle.backward(c, qk, v, pm, dout)
+    mq, mv = oracle.backward_magnitudes(c, qk, v, pm, dout)
+    assert np.all(np.abs(dqk) <= mq * (1 + 1e-12) + 1e-300)
+    assert np.all(np.abs(dv) <= mv * (1 + 1e-12) + 1e-300)
+    # strictly larger somewhere: the bound is not the gradient itself
+    assert np.any(mq > np.abs(dqk) * 1.5)
+    _, dvp = oracle.backward(c, qk, np.abs(v), pm, np.abs(dout))
+    _, mvp = oracle.backward_magnitudes(c, qk, np.abs(v), pm, np.abs(dout))
+    np.testing.assert_allclose(mvp, dvp, rtol=1e-12, atol=0)
+
+
+def test_backward_magnitudes_scale_with_dout(oracle_lib):
+    """Positive homogeneity in dout: every term is linear in dout."""
+    c, qk, v, pm, dout = _mag_case(11, True)
+    mq, mv = oracle.backward_magnitudes(c, qk, v, pm, dout)
+    mq2, mv2 = oracle.backward_magnitudes(c, qk, v, pm, -4.0 * dout)
+    np.testing.assert_allclose(mq2, 4.0 * mq, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(mv2, 4.0 * mv, rtol=1e-12, atol=0)
+
+
+def test_backward_magnitudes_of_one_key_window(oracle_lib):
+    """A hand case: L = 2, one chunk of 2, causal. Position 0 sees only itself
+    (dv_0 gets w dout_0 = dout_0: one round), position 1 attends only to key 0
+    with P = 1, so dS = dout_1.v_0 - dout_1.out_1 = 0 (out_1 = v_0) and the
+    magnitude of that term is |dout_1.v_0| + |dout_1.v_0| + 2 |dout_1.v_0|."""
+    c = _cfg(1, 1, 2, 2, 1, 1, 2, True)
+    qk = np.array([[[[3.0, 4.0], [1.0, 0.0]]]])
+    v = np.array([[[[1.0, -2.0], [5.0, 7.0]]]])
+    dout = np.array([[[[0.5, -1.0], [2.0, 3.0]]]])
+    pm = np.array([[[[0, 1]]]], dtype=np.int32)
+    mq, mv = oracle.backward_magnitudes(c, qk, v, pm, dout)
+    dv1 = abs(2.0 * 1.0 + 3.0 * -2.0)        # |dout_1 . v_0| = 4
+    A = 4.0 * dv1                             # 16
+    khat0 = np.array([0.6, 0.8])
+    # dv: key 0 gets |dout_1| (P = 1, w = 1) plus its own self-only |dout_0|
+    np.testing.assert_allclose(mv[0, 0, 0], np.abs(dout[0, 0, 1]) + np.abs(dout[0, 0, 0]))
+    np.testing.assert_allclose(mv[0, 0, 1], [0.0, 0.0])
+    # dq of query 1: A |khat_0| / sqrt(2)
+    np.testing.assert_allclose(mq[0, 0, 1], A * khat0 / math.sqrt(2), rtol=1e-14)
+    # dkhat of key 0: A |q_1| / sqrt(2), then the Jacobian in absolute value
+    mk = A * np.array([1.0, 0.0]) / math.sqrt(2)
+    np.testing.assert_allclose(mq[0, 0, 0], (mk + khat0 * (khat0 @ mk)) / 5.0, rtol=1e-14)
