@@ -9,6 +9,7 @@ runs without a GPU.
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import subprocess
 import sys
@@ -24,10 +25,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
-    # no packed-fp32 instructions in device code
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Device pass only: no packed-fp32 instructions in device code. Each source is
+# compiled in two passes (device code object, then the host object that
+# embeds it) so this target feature never reaches the x86 host compiler; both
+# passes get the same compilation-unit id, so the host registers exactly the
+# device symbols (kernels, static device arrays) of its own device pass.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 # Per-source extra flags. The hash kernel folds every MFMA result with vector
@@ -44,12 +49,26 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def _run(cmd, src):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    return r.stderr
+
+
+def _compile(src: str, csrc: str = CSRC, obj_dir: str = OBJ_DIR) -> str:
+    base = os.path.basename(src)[:-4]
+    obj = os.path.join(obj_dir, base + ".o")
+    fatbin = os.path.join(obj_dir, base + ".hipfb")
+    cuid = "cuid=" + hashlib.sha1(os.path.relpath(src, ROOT).encode()).hexdigest()[:16]
+    flags = [f if f != CSRC else csrc for f in CFLAGS]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    warnings = _run([HIPCC, "-x", "hip", *flags, f"-{cuid}", "--cuda-device-only", *DEVICE_FLAGS,
+                     *extra, "-c", src, "-o", fatbin], src)
+    warnings += _run([HIPCC, "-x", "hip", *flags, f"-{cuid}", "--cuda-host-only", "-Xclang",
+                      "-fcuda-include-gpubinary", "-Xclang", fatbin, "-c", src, "-o", obj], src)
+    if warnings.strip():
+        print(f"{os.path.basename(src)}:\n{warnings}", file=sys.stderr)
     return obj
 
 

@@ -58,6 +58,7 @@
 
 #include "dtype.h"
 #include "internal.h"
+#include "walks.h"
 
 namespace lsh {
 namespace {
@@ -241,12 +242,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // the segments of a group interleaved, so the workgroups in flight read
   // the rows of few heads, which then stay in the memory-side cache for the
   // other rounds.
-  const int group = blockIdx.x / (unsigned)(group_segs * ranges);
-  const int first = group * group_segs;
-  const int gn = min(group_segs, nseg - first);
-  const int inner = blockIdx.x - group * group_segs * ranges;
-  const int64_t seg = first + inner % gn;
-  const int range = inner / gn;
+  int64_t seg;
+  int range;
+  walks::range_block(blockIdx.x, group_segs, ranges, nseg, seg, range);
   const int c0 = range * chunks_per_wg;
   const int c1 = min(nchunks, c0 + chunks_per_wg);
   if (c0 >= c1) return;
@@ -518,20 +516,15 @@ template <int D, typename OT, bool CAUSAL, bool SORTED, bool DOT = false, bool N
 void launch_one(const Problem& p, const void* qk, const void* v, const void* qk_s,
                 const void* v_s, const int32_t* perm, const float* knorm, OT* o, float* lse,
                 hipStream_t s, const void* dout = nullptr, const uint16_t* buckets = nullptr) {
-  const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
-  const int per = nchunks < kRangeChunks ? nchunks : kRangeChunks;
-  const int ranges = (nchunks + per - 1) / per;
   // whole heads (all their rounds) per group, enough to fill the resident set
-  int64_t heads = (kResidentBlocks + (int64_t)ranges * p.R - 1) / ((int64_t)ranges * p.R);
-  if (heads < 1) heads = 1;
-  int64_t group_segs = heads * p.R;
-  if (group_segs > nseg) group_segs = nseg;
+  const walks::RangeShape sh =
+      walks::range_shape(p.L / kChunk, nseg, p.R, kRangeChunks, kResidentBlocks);
   const size_t shmem = Lds<D>::kBytes;
-  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED, DOT, NQ, SB>),
-                     dim3((unsigned)(nseg * ranges)), dim3(kThreads), shmem, s, (const uint4*)qk,
-                     (const uint4*)v, (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse,
-                     p.L, p.R, (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows(),
+  hipLaunchKernelGGL((k_attend_mfma<D, OT, CAUSAL, SORTED, DOT, NQ, SB>), dim3((unsigned)sh.blocks),
+                     dim3(kThreads), shmem, s, (const uint4*)qk, (const uint4*)v,
+                     (const uint4*)qk_s, (const uint4*)v_s, perm, knorm, o, lse, p.L, p.R,
+                     (int)nseg, sh.per, sh.ranges, sh.group_segs, p.o_seg_rows(),
                      (const unsigned char*)dout, buckets);
 }
 

@@ -30,6 +30,7 @@
 #include "dtype.h"
 #include "internal.h"
 #include "rows_lds.h"
+#include "walks.h"
 
 namespace lsh {
 namespace {
@@ -97,12 +98,9 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 
   constexpr int NE = 2 * NS;  // 32-key steps of P V
   extern __shared__ __align__(16) unsigned char lds[];
   const int nchunks = L / kChunk;
-  const int group = blockIdx.x / (unsigned)(group_segs * ranges);
-  const int first = group * group_segs;
-  const int gn = min(group_segs, nseg - first);
-  const int inner = blockIdx.x - group * group_segs * ranges;
-  const int64_t seg = first + inner % gn;
-  const int range = inner / gn;
+  int64_t seg;
+  int range;
+  walks::range_block(blockIdx.x, group_segs, ranges, nseg, seg, range);
   const int c0 = range * chunks_per_wg;
   const int c1 = min(nchunks, c0 + chunks_per_wg);
   if (c0 >= c1) return;
@@ -397,18 +395,13 @@ void launch_one(const Problem& p, const void* qk, const void* v, const int32_t* 
                               hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
     configured = true;
   }
-  const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
-  const int per = nchunks < kRangeChunks ? nchunks : kRangeChunks;
-  const int ranges = (nchunks + per - 1) / per;
-  int64_t heads = (kResidentBlocks + (int64_t)ranges * p.R - 1) / ((int64_t)ranges * p.R);
-  if (heads < 1) heads = 1;
-  int64_t group_segs = heads * p.R;
-  if (group_segs > nseg) group_segs = nseg;
-  hipLaunchKernelGGL((k_attend_var<D, CAUSAL, NS, DD, OT>), dim3((unsigned)(nseg * ranges)),
+  const walks::RangeShape sh =
+      walks::range_shape(p.L / kChunk, nseg, p.R, kRangeChunks, kResidentBlocks);
+  hipLaunchKernelGGL((k_attend_var<D, CAUSAL, NS, DD, OT>), dim3((unsigned)sh.blocks),
                      dim3(kThreads), shmem, s, (const unsigned char*)qk,
                      (const unsigned char*)v, perm, knorm, bkt, inv, o, lse, p.L, p.R,
-                     (int)nseg, per, ranges, (int)group_segs, p.o_seg_rows(),
+                     (int)nseg, sh.per, sh.ranges, sh.group_segs, p.o_seg_rows(),
                      p.flags & kVariantFlags);
 }
 

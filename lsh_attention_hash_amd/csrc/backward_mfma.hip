@@ -16,6 +16,7 @@
 #include "dtype.h"
 #include "internal.h"
 #include "rows_lds.h"
+#include "walks.h"
 
 namespace lsh {
 namespace {
@@ -105,12 +106,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   extern __shared__ __align__(16) unsigned char lds[];
   const int nchunks = L / kChunk;
   // groups of group_segs segments (all rounds of a few heads), interleaved
-  const int group = blockIdx.x / (unsigned)(group_segs * ranges);
-  const int first = group * group_segs;
-  const int gn = min(group_segs, nseg - first);
-  const int inner = blockIdx.x - group * group_segs * ranges;
-  const int64_t seg = first + inner % gn;
-  const int range = inner / gn;
+  int64_t seg;
+  int range;
+  walks::range_block(blockIdx.x, group_segs, ranges, nseg, seg, range);
   const int c0 = range * chunks_per_wg;
   const int c1 = min(nchunks, c0 + chunks_per_wg);
   if (c0 >= c1) return;
@@ -485,19 +483,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 template <int D, bool CAUSAL, typename GT>
 void launch_fused(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                   const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
-  const int nchunks = p.L / kChunk;
   const int64_t nseg = p.nseg();
-  const int per = nchunks < kFusedRange ? nchunks : kFusedRange;
-  const int ranges = (nchunks + per - 1) / per;
-  int64_t heads = (kFusedResident + (int64_t)ranges * p.R - 1) / ((int64_t)ranges * p.R);
-  if (heads < 1) heads = 1;
-  int64_t group_segs = heads * p.R;
-  if (group_segs > nseg) group_segs = nseg;
+  const walks::RangeShape sh =
+      walks::range_shape(p.L / kChunk, nseg, p.R, kFusedRange, kFusedResident);
   auto kern = k_bwd_fused_mfma<D, CAUSAL, GT>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(nseg * ranges)), dim3(kThreads), FLds<D>::kBytes, s,
+  hipLaunchKernelGGL(kern, dim3((unsigned)sh.blocks), dim3(kThreads), FLds<D>::kBytes, s,
                      (const unsigned char*)qk, (const unsigned char*)v,
                      (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, (GT*)b.dq,
-                     (GT*)b.dv, p.L, p.R, (int)nseg, per, ranges, (int)group_segs);
+                     (GT*)b.dv, p.L, p.R, (int)nseg, sh.per, sh.ranges, sh.group_segs);
 }
 
 template <int D, typename GT>

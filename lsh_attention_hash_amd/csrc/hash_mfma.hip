@@ -38,6 +38,7 @@
 #include "dtype.h"
 #include "hash_x16.h"
 #include "internal.h"
+#include "walks.h"
 
 namespace lsh {
 namespace {
@@ -242,10 +243,8 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   uint2* qb_l = (uint2*)(lds + half_pad * ROWB + kQaLds * 16);
   unsigned* qn_l = (unsigned*)(lds + half_pad * ROWB + kQaLds * 16 + kQbLds * 8);
   if (threadIdx.x < 2) qn_l[threadIdx.x] = 0u;
-  const int xcd = blockIdx.x & 7;
-  const int kk = blockIdx.x >> 3;
-  const int r = kk % R;
-  const int grp = xcd + 8 * (kk / R);
+  int r, grp;
+  walks::hash_block(blockIdx.x, R, r, grp);
   const int ngrp = gridDim.x / R;      // gridDim.x is a multiple of 8 R
 
   // x in fp16 as the B operand: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
@@ -299,9 +298,8 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   // head and position of the wave's first token (wave-uniform), advanced by
   // the walk's stride at the end of every token tile: one division per walk
   const int64_t tfirst = (int64_t)grp * kTokWG + __builtin_amdgcn_readfirstlane(w) * kTokWave;
-  const int64_t tstep = (int64_t)ngrp * kTokWG;
-  int64_t bh0 = tfirst / L, i0 = tfirst - (tfirst / L) * L;
-  const int64_t step_q = tstep / L, step_r = tstep - (tstep / L) * L;
+  walks::TokenWalk tw;
+  tw.init(tfirst, (int64_t)ngrp * kTokWG, L);
   for (int j = grp; j < n_tok_tiles; j += ngrp) {
     const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
     f16x8_t bx[2][KS];
@@ -445,11 +443,8 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       const float ex = (gamma * rh_max + lo_max) * (hf ? nx[1] : nx[0]) +
                        r_max * (hf ? nres[1] : nres[0]);
       const float thr = 2.0f * (ex + ldexpf(d1, ib - 22));
-      int64_t bh = bh0, i = i0 + hf * 32 + tl;
-      while (i >= L) {  // at most once when L >= 64
-        i -= L;
-        ++bh;
-      }
+      int64_t bh, i;
+      tw.at(hf * 32 + tl, bh, i);
       const int64_t row = (bh * R + r) * L + i;
       const uint32_t k1 = a1 & imask;
       if (d1 - d2 > thr && k1 < (uint32_t)half) {
@@ -468,12 +463,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         else qb[atomicAdd(qcount + 1, 1u)] = entry;
       }
     }
-    bh0 += step_q;
-    i0 += step_r;
-    if (i0 >= L) {
-      i0 -= L;
-      ++bh0;
-    }
+    tw.advance();
   }
   // move the workgroup's queued entries to the global queues
   __syncthreads();
@@ -695,12 +685,7 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
     }
   }
   const int per_cu = hs.per_cu;
-  const int unit = 8 * p.R;
-  int64_t grid = (int64_t)hs.n_cu * per_cu;
-  grid = (grid / unit) * unit;
-  if (grid < unit) grid = unit;
-  const int64_t max_grid = (int64_t)unit * ((n_tok_tiles + 7) / 8);
-  if (grid > max_grid) grid = max_grid;
+  const int64_t grid = walks::hash_grid(hs.n_cu, per_cu, p.R, n_tok_tiles);
   if (x16_ready) {
     // the projection wrote the fp16 copy and the norms; clear what the
     // pre-pass would have cleared

@@ -71,36 +71,36 @@ int validate(const lsh_attn_config_t* c) {
 }
 
 void free_ws(lsh::Workspace& w) {
-  hipFree(w.buckets);
-  hipFree(w.perm);
-  hipFree(w.inv);
-  hipFree(w.o);
-  hipFree(w.lse);
-  hipFree(w.sort_counts);
-  hipFree(w.qk_sorted);
-  hipFree(w.v_sorted);
-  hipFree(w.stats);
-  hipFree(w.knorm);
-  hipFree(w.hash.rh);
-  hipFree(w.hash.rt);
-  hipFree(w.hash.bounds);
-  hipFree(w.hash.queue_a);
-  hipFree(w.hash.queue_b);
-  hipFree(w.hash.x16);
-  hipFree(w.hash.xnorm);
+  (void)hipFree(w.buckets);
+  (void)hipFree(w.perm);
+  (void)hipFree(w.inv);
+  (void)hipFree(w.o);
+  (void)hipFree(w.lse);
+  (void)hipFree(w.sort_counts);
+  (void)hipFree(w.qk_sorted);
+  (void)hipFree(w.v_sorted);
+  (void)hipFree(w.stats);
+  (void)hipFree(w.knorm);
+  (void)hipFree(w.hash.rh);
+  (void)hipFree(w.hash.rt);
+  (void)hipFree(w.hash.bounds);
+  (void)hipFree(w.hash.queue_a);
+  (void)hipFree(w.hash.queue_b);
+  (void)hipFree(w.hash.x16);
+  (void)hipFree(w.hash.xnorm);
   w = lsh::Workspace{};
 }
 
 void free_bw(lsh::BwdWorkspace& b) {
-  hipFree(b.o32);
-  hipFree(b.od);
-  hipFree(b.lse);
-  hipFree(b.w);
-  hipFree(b.cq);
-  hipFree(b.wself);
-  hipFree(b.dq);
-  hipFree(b.dk);
-  hipFree(b.dv);
+  (void)hipFree(b.o32);
+  (void)hipFree(b.od);
+  (void)hipFree(b.lse);
+  (void)hipFree(b.w);
+  (void)hipFree(b.cq);
+  (void)hipFree(b.wself);
+  (void)hipFree(b.dq);
+  (void)hipFree(b.dk);
+  (void)hipFree(b.dv);
   b = lsh::BwdWorkspace{};
 }
 
@@ -225,7 +225,7 @@ int forward_body(const lsh::Problem& p, lsh::Workspace& w, const void* qk, const
                  const float* rotations, void* out, float* lse, int32_t* buckets, int32_t* perm,
                  hipStream_t s, hipEvent_t* ev, bool x16_ready) {
   auto mark = [&](int j) {
-    if (ev) hipEventRecord(ev[j], s);
+    if (ev) (void)hipEventRecord(ev[j], s);
   };
   int32_t* pm = perm ? perm : w.perm;
   float* ls = lse ? lse : w.lse;
@@ -320,11 +320,11 @@ int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const voi
   hipStream_t s = (hipStream_t)stream;
   h->last_stream = s;
   hipEvent_t* ev = next_events(h, true);
-  if (ev) hipEventRecord(ev[8], s);
+  if (ev) (void)hipEventRecord(ev[8], s);
   bool x16_ready = false;
   const hipError_t e = lsh::launch_project(h->p, model_dim, x, w_qk, w_v, qk, v, h->ws.hash,
                                            h->ws.knorm, &x16_ready, s);
-  if (ev) hipEventRecord(ev[9], s);
+  if (ev) (void)hipEventRecord(ev[9], s);
   if (e != hipSuccess) return release_on_error(h, ev, LSH_ATTN_ERR_HIP);
   return release_on_error(
       h, ev,
@@ -370,8 +370,8 @@ int lsh_attn_get_stats(lsh_attn_t h, lsh_attn_stats_t* stats) {
 }
 
 static void destroy_events(lsh_attn_s* h) {
-  for (hipEvent_t e : h->events) hipEventDestroy(e);
-  for (hipEvent_t e : h->bevents) hipEventDestroy(e);
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  for (hipEvent_t e : h->bevents) (void)hipEventDestroy(e);
   h->events.clear();
   h->bevents.clear();
   h->projected.clear();
@@ -484,7 +484,7 @@ int lsh_attn_destroy(lsh_attn_t h) {
   destroy_events(h);
   free_bw(h->bw);
   free_ws(h->ws);
-  if (switched) hipSetDevice(prev);
+  if (switched) (void)hipSetDevice(prev);
   delete h;
   if (e != hipSuccess) {
     (void)hipGetLastError();

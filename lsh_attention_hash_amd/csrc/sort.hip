@@ -22,6 +22,7 @@
 // Buckets are handled in LDS windows of at most kLdsBins ids, so any
 // n_buckets up to 65536 works with a bounded LDS footprint.
 #include "internal.h"
+#include "walks.h"
 
 namespace lsh {
 namespace {
@@ -43,21 +44,10 @@ __device__ __forceinline__ uint64_t match_peers(uint32_t key, bool active, int n
   return peers;
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin. When the segments split
-// evenly, block b takes a tile of a segment s with s % 8 == b % 8, so all
-// tiles of a segment run on one XCD and the partial-line permutation writes
-// of neighbouring tiles meet in that XCD's L2 before they reach HBM.
-constexpr int kXcds = 8;
+// Workgroups are dealt to the 8 XCDs round-robin (walks.h: block b takes a
+// tile of a segment on b's XCD when the segments split evenly).
 __device__ __forceinline__ void block_tile(int tiles, int64_t nseg, int64_t& seg, int& tile) {
-  const unsigned b = blockIdx.x;
-  if (nseg % kXcds == 0) {
-    const unsigned k = b / kXcds;
-    seg = (int64_t)(b % kXcds) + (int64_t)kXcds * (k / (unsigned)tiles);
-    tile = (int)(k % (unsigned)tiles);
-  } else {
-    seg = b / (unsigned)tiles;
-    tile = (int)(b % (unsigned)tiles);
-  }
+  walks::sort_block_tile(blockIdx.x, tiles, nseg, seg, tile);
 }
 
 // Thread (w, lane) takes positions begin + 256w + 64k + lane, k = 0..3: in
