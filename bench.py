@@ -203,52 +203,102 @@ STAGE_SOURCES = {
 }
 
 
-def cpu_baseline(w, inp, heads: int):
-    """The fp64 oracle as it stands, on batch 0 and the first `heads` heads at
-    full sequence length, all rounds; scaled to tokens/s of the whole workload."""
-    import numpy as np
-
-    import oracle
-
+def _oracle_threads():
     threads = len(os.sched_getaffinity(0))
     env_threads = os.environ.get("OMP_NUM_THREADS")
     if env_threads:
         threads = min(threads, int(env_threads))
-    sub = w.with_(batch=1, heads=heads)
-    c = oracle.config(sub)
-    qk = np.ascontiguousarray(inp.qk[:1, :heads], dtype=np.float64)
-    v = np.ascontiguousarray(inp.v[:1, :heads], dtype=np.float64)
-    rot = None if inp.rotations is None else inp.rotations.astype(np.float64)
-    oracle.build(force=False)
-    t0 = time.perf_counter()
-    ref = oracle.forward(c, qk, v, rot)
-    t = time.perf_counter() - t0
-    frac = heads / (w.batch * w.heads)
-    value = w.batch * w.seq_len * frac / t
-    used = min(threads, heads * w.n_rounds)
-    model = ""
+    return threads
+
+
+def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
+    return ""
+
+
+def cpu_sample(w, pairs: int):
+    """The first `pairs` (batch, head) pairs in batch-major order, as whole
+    batches when pairs >= heads (pairs rounded down to a multiple of heads),
+    else the first heads of batch 0: (batches, heads) of the sample."""
+    if pairs >= w.heads:
+        return min(w.batch, pairs // w.heads), w.heads
+    return 1, max(1, pairs)
+
+
+def cpu_baseline(w, inp, target_s: float = 10.0, pairs: int = 0):
+    """The fp64 oracle as it stands, timed on a bounded sample of the workload
+    (whole (batch, head) pairs at full sequence length, all rounds): a pilot
+    on one pair sizes the sample to about target_s seconds (or `pairs` pairs),
+    repeated when even the whole workload takes less; scaled to tokens/s.
+    Returns (the record, the oracle's result on the sample, (batches, heads))."""
+    import numpy as np
+
+    import oracle
+
+    threads = _oracle_threads()
+    rot = None if inp.rotations is None else inp.rotations.astype(np.float64)
+    oracle.build(force=False)
+
+    def run(nb, nh):
+        c = oracle.config(w.with_(batch=nb, heads=nh))
+        qk = np.ascontiguousarray(inp.qk[:nb, :nh], dtype=np.float64)
+        v = np.ascontiguousarray(inp.v[:nb, :nh], dtype=np.float64)
+        t0 = time.perf_counter()
+        ref = oracle.forward(c, qk, v, rot)
+        return time.perf_counter() - t0, ref
+
+    all_pairs = w.batch * w.heads
+    if pairs:
+        nb, nh = cpu_sample(w, pairs)
+        t, ref = run(nb, nh)
+    else:
+        # grow the sample (the oracle runs its segments in parallel, so the
+        # time is not proportional to the pairs) until it takes a third of
+        # the target or is the whole workload
+        pairs, t1 = 1, 0.0
+        while True:
+            nb, nh = cpu_sample(w, pairs)
+            t, ref = run(nb, nh)
+            t1 = t1 or t
+            if t >= target_s / 3 or nb * nh == all_pairs:
+                break
+            pairs = min(all_pairs, max(pairs + 1, int(pairs * target_s / max(t, 1e-3))))
+    n_pairs = nb * nh
+    repeats = 1
+    if n_pairs == all_pairs and t < target_s / 3:
+        repeats = max(1, min(100, int(target_s / max(t, 1e-6))))
+        t = 0.0
+        for _ in range(repeats):
+            dt, ref = run(nb, nh)
+            t += dt
+    frac = n_pairs / all_pairs
+    value = w.batch * w.seq_len * frac * repeats / t
+    used = min(threads, n_pairs * w.n_rounds)
     return {"value": round(value, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"batch 0, heads 0..{heads - 1} of {w.heads}, full L={w.seq_len}, "
-                      f"all {w.n_rounds} rounds ({frac:.4f} of the workload), fp64 oracle "
-                      f"forward in {t:.2f} s; OpenMP over (head, round) segments",
-            "seconds": round(t, 3), "cpu_model": model, "threads_available": threads}, ref
+            "sample": f"{nb} batch(es) x {nh} head(s) of {w.batch} x {w.heads}, full "
+                      f"L={w.seq_len}, all {w.n_rounds} rounds ({frac:.4f} of the workload)"
+                      + (f", {repeats} times" if repeats > 1 else "")
+                      + f": fp64 oracle forward in {t:.2f} s (sample grown from one (batch, "
+                      f"head) pair towards {target_s:.0f} s); OpenMP over (batch, head, round) "
+                      f"segments",
+            "seconds": round(t, 3), "cpu_model": _cpu_model(), "threads_available": threads}, \
+        ref, (nb, nh)
 
 
-def parity_summary(w, inp, gpu, ref, heads: int):
+def parity_summary(w, inp, gpu, ref, sample):
     """What the timed configuration's results are, against the oracle: bucket
     ids of every head and round against the oracle's hash (mismatches and
     near-ties, oracle top-two margin < 1e-5), and the outputs and logsumexps
-    of the cpu_baseline sample (batch 0, heads 0..heads-1) against the oracle's
-    forward on them. gpu: out [B,H,L,d], lse [B,H,R,L], buckets [B,H,R,L]
-    (numpy)."""
+    of the cpu_baseline sample (its first `sample` = (batches, heads)) against
+    the oracle's forward on them. gpu: out [B,H,L,d], lse [B,H,R,L], buckets
+    [B,H,R,L] (numpy)."""
+    nb, heads = sample
     import numpy as np
 
     import oracle
@@ -262,14 +312,14 @@ def parity_summary(w, inp, gpu, ref, heads: int):
         res["near_ties"] = int(np.sum(mg < 1e-5))
         res["near_tie_mismatches"] = int(np.sum((bk != gpu["buckets"]) & (mg < 1e-5)))
         res["oracle_hash_s"] = round(time.perf_counter() - t0, 2)
-    out = gpu["out"][:1, :heads].astype(np.float64)
-    res["out_rows_compared"] = int(heads * w.seq_len)
+    out = gpu["out"][:nb, :heads].astype(np.float64)
+    res["out_rows_compared"] = int(nb * heads * w.seq_len)
     res["out_max_abs_err"] = float(np.abs(out - ref["out"]).max())
-    lg = gpu["lse"][:1, :heads].astype(np.float64)
+    lg = gpu["lse"][:nb, :heads].astype(np.float64)
     keep = ref["lse"] != oracle.SELF_LOGIT
     res["lse_max_abs_err"] = float(np.abs(lg - ref["lse"])[keep].max()) if keep.any() else 0.0
     res["self_only_flags_equal"] = bool(np.array_equal(lg == oracle.SELF_LOGIT, ~keep))
-    res["perm_equal_sample"] = bool(np.array_equal(gpu["perm"][:1, :heads], ref["perm"]))
+    res["perm_equal_sample"] = bool(np.array_equal(gpu["perm"][:nb, :heads], ref["perm"]))
     res["out_tolerance"] = 2e-2 if w.dtype == "bf16" else 1e-5
     return res
 
@@ -595,7 +645,9 @@ def main():
                     help="untimed forwards for this many milliseconds before the warm-up "
                          "steps (declared in the JSON line as 'settle')")
     ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="heads in the oracle sample (0: as many as rounds fit the cores)")
+                    help="(batch, head) pairs in the oracle sample (0: sized to --cpu-seconds)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time the sample is sized to (a one-pair pilot estimates it)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -755,8 +807,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     if not args.no_cpu_baseline:
-        heads = args.cpu_heads or max(1, min(w.heads, len(os.sched_getaffinity(0)) // w.n_rounds))
-        res["cpu_baseline"], ref = cpu_baseline(w, inp, heads)
+        res["cpu_baseline"], ref, sample = cpu_baseline(w, inp, args.cpu_seconds, args.cpu_heads)
         if not args.from_x and not variants:
             # the results of the timed configuration: one more forward, untimed
             out, ex = op(qk, v, rot, out=out, return_lse=True, return_buckets=True,
@@ -764,7 +815,7 @@ def main():
             torch.cuda.synchronize()
             gpu = {"out": out.float().cpu().numpy(), "lse": ex["lse"].cpu().numpy(),
                    "buckets": ex["buckets"].cpu().numpy(), "perm": ex["perm"].cpu().numpy()}
-            res["parity"] = parity_summary(w, inp, gpu, ref, heads)
+            res["parity"] = parity_summary(w, inp, gpu, ref, sample)
     op.close()
     print(json.dumps(res), flush=True)
 
