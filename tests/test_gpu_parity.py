@@ -96,6 +96,20 @@ def test_one_bucket_one_chunk_is_full_attention(causal, d):
     check_outputs_full(w, inp, gpu)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_odd_chunk_length(causal, d):
+    """A chunk length of 40 (the plain kernel): query blocks of 16, 16 and 8,
+    and key blocks that end inside the window."""
+    w = W("c4k", batch=1, heads=2, seq_len=1200, head_dim=d, n_buckets=16, n_rounds=2,
+          chunk_len=40, causal=causal)
+    _say(f"[chunk 40] {w}")
+    inp = workloads.make_inputs(w)
+    gpu = run_gpu(w, inp)
+    r = check_forward(w, inp, gpu)
+    _say(f"  out err {r['out_err']:.3g} lse err {r['lse_err']:.3g}")
+
+
 def test_out_dtype_fp32_and_separate_gather():
     w = W("c4k", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=2, causal=True)
     _say(f"[out fp32 / separate gather] {w}")

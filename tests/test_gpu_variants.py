@@ -77,6 +77,10 @@ CASES = [
     (W("text64k", batch=1, heads=1, seq_len=2048, n_buckets=32, n_rounds=4, causal=False),
      LA | DD),
     (W("skewed", batch=1, heads=2, seq_len=2048, n_buckets=32, n_rounds=3), SB | DD),
+    # plain kernel at its limits: the largest window (3 chunks of 256) and a
+    # chunk length that leaves partial query and key blocks
+    (W("tiny", chunk_len=256, n_rounds=2), LA),
+    (W("tiny", seq_len=1200, head_dim=128, chunk_len=40, n_rounds=2, causal=True), ALL),
 ]
 
 
