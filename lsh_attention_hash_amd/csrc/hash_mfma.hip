@@ -18,15 +18,17 @@
 //     v_mfma_f32_32x32x16_f16
 //     gives p~ = x16 . Rh_k with exact products and fp32 sums. For every
 //     column the kernel forms a key (bits of |p~| with the low ib mantissa bits
-//     replaced by k) and keeps the three largest keys per row (max / med3).
+//     replaced by k) and keeps the two largest keys per row (max3 / med3).
 //     With E = (gamma |Rh|max + |lo|max) |x16| + |R|max |x - x16| bounding
 //     | |p~_k| - |p_k| | for every k (Cauchy-Schwarz on each correction term,
 //     gamma = (d + 2) 2^-23 for the fp32 accumulation in any order) and S the
 //     key truncation (2^(ib-22) of the top value):
 //       top1 - top2 > 2 (E + S): the winner is certain; its sign comes from an
 //         fp32 recomputation of p~_k1 (|p| > E, so the sign is right);
-//       else top1 - top3 > 2 (E + S): only k1, k2 can win -> queue A;
-//       else -> queue B (all columns).
+//       else the row is queued for a rescan, which recomputes the same
+//         projections keeping the three largest keys:
+//         top1 - top3 > 2 (E + S): only k1, k2 can win -> queue A;
+//         else -> queue B (all columns).
 //  3. fallback: queue A entries re-score the two candidates, queue B entries
 //     every column, in fp64 with t = 0..d-1 in order: the products of a bf16
 //     input and an fp32 rotation are exact in fp64, so these sums are the
@@ -34,6 +36,8 @@
 //     the definition (largest entry, lowest index on ties).
 #include <float.h>
 #include <limits.h>
+
+#include <type_traits>
 
 #include "dtype.h"
 #include "hash_x16.h"
@@ -207,15 +211,40 @@ struct QA {  // two-candidate re-score
 // Re-score entries are first appended to a workgroup queue in LDS (LDS atomics
 // answer in tens of cycles) and moved to the global queues, one global atomic
 // per queue, when the workgroup ends; only a full LDS queue appends globally.
-constexpr int kQaLds = 256, kQbLds = 64;
-constexpr int kQueueLdsBytes = kQaLds * 16 + kQbLds * 8 + 16;
+// Each wave also keeps in LDS the tokens whose winner its main pass left
+// open (kWq slots; rescanned 64 at a time).
+constexpr int kQaLds = 256, kQbLds = 64, kWq = 128;
+constexpr int kQueueLdsBytes = kQaLds * 16 + kQbLds * 8 + 16 + (kThreads / 64) * kWq * 4;
+
+// Keep the two largest of (t1 >= t2) and keys a, b: max3 for the first; the
+// second is the larger of t2 and the middle of (t1, a, b). (Keys order as
+// floats like their bit patterns, see top3.)
+__device__ __forceinline__ void top2_pair(uint32_t& t1, uint32_t& t2, uint32_t a, uint32_t b) {
+  const uint32_t m = __float_as_uint(
+      __builtin_amdgcn_fmed3f(__uint_as_float(t1), __uint_as_float(a), __uint_as_float(b)));
+  const uint32_t n1 = t1 > a ? t1 : a;
+  t1 = n1 > b ? n1 : b;
+  t2 = t2 > m ? t2 : m;
+}
+
+template <bool B>
+using Mode = std::integral_constant<bool, B>;
 
 // Persistent: workgroup w serves round r and token tiles j = grp, grp + G/R, ...
-// (tiles of kTokWG consecutive token-heads). Its rotation R_r stays in LDS for
-// the whole walk. w -> (xcd = w % 8, k = w / 8, r = k % R, grp = xcd + 8 (k / R)):
-// the R workgroups that read the same token tile differ only in r and run on
-// the same XCD, so the tile is fetched from HBM once and the other rounds find
-// it in that XCD's L2.
+// (tiles of kTokWG tokens). Its rotation R_r stays in LDS for the whole walk.
+// w -> (xcd = w % 8, k = w / 8, r = k % R, grp = xcd + 8 (k / R)): the R
+// workgroups that read the same token tile differ only in r and run on the
+// same XCD, so the tile is fetched from HBM once and the other rounds find it
+// in that XCD's L2.
+//
+// Every wave works on its own 64 tokens of a tile, in two modes. The main
+// mode keeps the two largest keys per row (2.5 vector instructions per key):
+// a row whose winner is certain gets its bucket, any other row's token goes
+// to the wave's rescan queue in LDS. Whenever that queue holds 64 tokens, and
+// once at the end of the walk, the wave runs the rescan mode on them: the
+// same projections (bit for bit) keeping three keys per row, which decide
+// between the certain winner, queue A (two candidates) and queue B (all
+// columns).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const uint16_t* __restrict__ x16, const float2* __restrict__ xnorm,
@@ -242,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   QA* qa_l = (QA*)(lds + half_pad * ROWB);
   uint2* qb_l = (uint2*)(lds + half_pad * ROWB + kQaLds * 16);
   unsigned* qn_l = (unsigned*)(lds + half_pad * ROWB + kQaLds * 16 + kQbLds * 8);
+  uint32_t* wq = (uint32_t*)(lds + half_pad * ROWB + kQaLds * 16 + kQbLds * 8 + 16) + w * kWq;
   if (threadIdx.x < 2) qn_l[threadIdx.x] = 0u;
   int r, grp;
   walks::hash_block(blockIdx.x, R, r, grp);
@@ -254,19 +284,26 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   // first one while the rotation is copied into LDS.
   f16x8_t bn[2][KS];
   float2 nn[2];
-  auto fetch = [&](int j) {
+  auto load_rows = [&](f16x8_t (&b)[2][KS], float2 (&nrm)[2], const int64_t (&tok)[2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int64_t n = (int64_t)j * kTokWG + w * kTokWave + s * 32 + tl;
-      const int64_t nc = n < N ? n : 0;
-      const uint4* src = (const uint4*)(x16 + nc * D) + hf * KS;
+      const uint4* src = (const uint4*)(x16 + tok[s] * D) + hf * KS;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 u = src[ks];
-        bn[s][ks] = __builtin_bit_cast(f16x8_t, u);
+        b[s][ks] = __builtin_bit_cast(f16x8_t, u);
       }
-      nn[s] = xnorm[nc];
+      nrm[s] = xnorm[tok[s]];
     }
+  };
+  auto fetch = [&](int j) {
+    int64_t tok[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t n = (int64_t)j * kTokWG + w * kTokWave + s * 32 + tl;
+      tok[s] = n < N ? n : 0;
+    }
+    load_rows(bn, nn, tok);
   };
   if (grp < n_tok_tiles) fetch(grp);
 
@@ -295,25 +332,13 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
   const int ntiles = half_pad / 32;
 
-  // head and position of the wave's first token (wave-uniform), advanced by
-  // the walk's stride at the end of every token tile: one division per walk
-  const int64_t tfirst = (int64_t)grp * kTokWG + __builtin_amdgcn_readfirstlane(w) * kTokWave;
-  walks::TokenWalk tw;
-  tw.init(tfirst, (int64_t)ngrp * kTokWG, L);
-  for (int j = grp; j < n_tok_tiles; j += ngrp) {
-    const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
-    f16x8_t bx[2][KS];
-    float nx[2], nres[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bx[s][ks] = bn[s][ks];
-      nx[s] = nn[s].x;
-      nres[s] = nn[s].y;
-    }
-    if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
-
-    // two independent top-3 lists per set (even and odd accumulator
+  // One wave's 64 tokens (2 sets of 32) against every column of the round.
+  // Returns whether this lane's row (token tl of set hf) is left open (main
+  // mode only). bh, i: the row's head and position.
+  auto run = [&](auto mode, const f16x8_t (&bx)[2][KS], const float (&nx)[2],
+                 const float (&nres)[2], bool valid, int64_t bh, int64_t i) -> bool {
+    constexpr bool kT3 = decltype(mode)::value;
+    // two independent key lists per set (even and odd accumulator
     // registers), merged once per token tile: half the dependency chain
     uint32_t t1[2] = {0u, 0u}, t2[2] = {0u, 0u}, t3[2] = {0u, 0u};
     uint32_t u1[2] = {0u, 0u}, u2[2] = {0u, 0u}, u3[2] = {0u, 0u};
@@ -337,14 +362,34 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     // The index field gets kt*32 + 8(v/4) + v%4 (uniform across the wave); bit
     // 2 (the lane half) is added when the halves merge. Within one lane the
     // order of keys is the same with or without that bit.
+    auto key = [&](int kt, const floatx16_t& c, int v) {
+      // the tile's base index is opaque to the compiler, so the key's index
+      // stays one scalar add and the key one v_and_or_b32 (not and + or3)
+      uint32_t kb = (uint32_t)(kt * 32);
+      asm("" : "+s"(kb));
+      const uint32_t k = kb + (uint32_t)(8 * (v >> 2) + (v & 3));
+      return (__float_as_uint(c[v]) & vmask_v) | k;
+    };
     auto fold = [&](int kt, const floatx16_t& c, int s) {
+      if constexpr (kT3) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t k = (uint32_t)(kt * 32 + 8 * (v >> 2) + (v & 3));
-        if (v & 1) top3(u1[s], u2[s], u3[s], (__float_as_uint(c[v]) & vmask_v) | k);
-        else top3(t1[s], t2[s], t3[s], (__float_as_uint(c[v]) & vmask_v) | k);
+        for (int v = 0; v < 16; ++v) {
+          if (v & 1) top3(u1[s], u2[s], u3[s], key(kt, c, v));
+          else top3(t1[s], t2[s], t3[s], key(kt, c, v));
+        }
+      } else {
+        // pairs (v, v + 2): v = 0, 4, 8, 12 to the even list, 1, 5, 9, 13
+        // to the odd one
+#pragma unroll
+        for (int v = 0; v < 16; v += 4) {
+          top2_pair(t1[s], t2[s], key(kt, c, v), key(kt, c, v + 2));
+          top2_pair(u1[s], u2[s], key(kt, c, v + 1), key(kt, c, v + 3));
+        }
       }
     };
+    // vector instructions per set, tile and MFMA: 4 per key for three keys,
+    // about 2.5 for two
+    constexpr int kFoldPerMfma = kT3 ? 8 : 5;
     // Tiles alternate between two accumulator pairs: each set's keys of tile
     // kt are folded from one pair while the MFMAs of tile kt + 1 fill the
     // other, so the fold reads the MFMA results in place (no copies); the
@@ -360,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kFoldPerMfma, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       set_mfma(nxt[1], 1, use);
@@ -369,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kFoldPerMfma, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -395,17 +440,25 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     // tokens, other columns)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      top3(t1[s], t2[s], t3[s], u1[s]);
-      top3(t1[s], t2[s], t3[s], u2[s]);
-      top3(t1[s], t2[s], t3[s], u3[s]);
-      t1[s] |= (uint32_t)(hf << 2);
-      t2[s] |= (uint32_t)(hf << 2);
-      t3[s] |= (uint32_t)(hf << 2);
-      const uint32_t o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32),
-                  o3 = __shfl_xor(t3[s], 32);
-      top3(t1[s], t2[s], t3[s], o1);
-      top3(t1[s], t2[s], t3[s], o2);
-      top3(t1[s], t2[s], t3[s], o3);
+      if constexpr (kT3) {
+        top3(t1[s], t2[s], t3[s], u1[s]);
+        top3(t1[s], t2[s], t3[s], u2[s]);
+        top3(t1[s], t2[s], t3[s], u3[s]);
+        t1[s] |= (uint32_t)(hf << 2);
+        t2[s] |= (uint32_t)(hf << 2);
+        t3[s] |= (uint32_t)(hf << 2);
+        const uint32_t o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32),
+                       o3 = __shfl_xor(t3[s], 32);
+        top3(t1[s], t2[s], t3[s], o1);
+        top3(t1[s], t2[s], t3[s], o2);
+        top3(t1[s], t2[s], t3[s], o3);
+      } else {
+        top2_pair(t1[s], t2[s], u1[s], u2[s]);
+        t1[s] |= (uint32_t)(hf << 2);
+        t2[s] |= (uint32_t)(hf << 2);
+        const uint32_t o1 = __shfl_xor(t1[s], 32), o2 = __shfl_xor(t2[s], 32);
+        top2_pair(t1[s], t2[s], o1, o2);
+      }
     }
     // sign of p~ at each set's best column, partial over this lane's dims
     // (four partial sums: any fp32 order is within the certificate's bound)
@@ -432,39 +485,97 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const float recv = __shfl_xor(send, 32);
     const float pk1 = (hf ? part[1] : part[0]) + recv;
 
-    const int64_t n = tok0 + hf * 32 + tl;
-    if (n < N) {
-      const uint32_t a1 = hf ? t1[1] : t1[0];
-      const uint32_t a2 = hf ? t2[1] : t2[0];
+    if (!valid) return false;
+    const uint32_t a1 = hf ? t1[1] : t1[0];
+    const uint32_t a2 = hf ? t2[1] : t2[0];
+    const float d1 = __uint_as_float(a1 & vmask);
+    const float d2 = __uint_as_float(a2 & vmask);
+    const float ex = (gamma * rh_max + lo_max) * (hf ? nx[1] : nx[0]) +
+                     r_max * (hf ? nres[1] : nres[0]);
+    const float thr = 2.0f * (ex + ldexpf(d1, ib - 22));
+    const int64_t row = (bh * R + r) * L + i;
+    const uint32_t k1 = a1 & imask;
+    if (d1 - d2 > thr && k1 < (uint32_t)half) {
+      const int bk = (int)k1 + (pk1 < 0.f ? half : 0);
+      buckets[row] = (uint16_t)bk;
+      if (buckets_out) buckets_out[row] = bk;
+      return false;
+    }
+    if constexpr (!kT3) {
+      return true;
+    } else {
       const uint32_t a3 = hf ? t3[1] : t3[0];
-      const float d1 = __uint_as_float(a1 & vmask);
-      const float d2 = __uint_as_float(a2 & vmask);
       const float d3 = __uint_as_float(a3 & vmask);
-      const float ex = (gamma * rh_max + lo_max) * (hf ? nx[1] : nx[0]) +
-                       r_max * (hf ? nres[1] : nres[0]);
-      const float thr = 2.0f * (ex + ldexpf(d1, ib - 22));
-      int64_t bh, i;
-      tw.at(hf * 32 + tl, bh, i);
-      const int64_t row = (bh * R + r) * L + i;
-      const uint32_t k1 = a1 & imask;
-      if (d1 - d2 > thr && k1 < (uint32_t)half) {
-        const int bk = (int)k1 + (pk1 < 0.f ? half : 0);
-        buckets[row] = (uint16_t)bk;
-        if (buckets_out) buckets_out[row] = bk;
-      } else if (d1 - d3 > thr && k1 < (uint32_t)half && (a2 & imask) < (uint32_t)half) {
+      if (d1 - d3 > thr && k1 < (uint32_t)half && (a2 & imask) < (uint32_t)half) {
         const QA entry{(uint32_t)row, (uint32_t)(row >> 32), k1, a2 & imask};
-        const unsigned e = atomicAdd(qn_l + 0, 1u);
-        if (e < (unsigned)kQaLds) qa_l[e] = entry;
+        const unsigned q = atomicAdd(qn_l + 0, 1u);
+        if (q < (unsigned)kQaLds) qa_l[q] = entry;
         else qa[atomicAdd(qcount + 0, 1u)] = entry;
       } else {
         const uint2 entry = make_uint2((uint32_t)row, (uint32_t)(row >> 32));
-        const unsigned e = atomicAdd(qn_l + 1, 1u);
-        if (e < (unsigned)kQbLds) qb_l[e] = entry;
+        const unsigned q = atomicAdd(qn_l + 1, 1u);
+        if (q < (unsigned)kQbLds) qb_l[q] = entry;
         else qb[atomicAdd(qcount + 1, 1u)] = entry;
       }
+      return false;
+    }
+  };
+
+  // rescan of the first c (<= 64) tokens of the wave's queue: token e of the
+  // queue is token tl = e % 32 of set e / 32
+  auto rescan = [&](unsigned c) {
+    int64_t tok[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const unsigned e = (unsigned)(s * 32 + tl);
+      tok[s] = e < c ? (int64_t)wq[e] : 0;
+    }
+    f16x8_t b[2][KS];
+    float2 nrm[2];
+    load_rows(b, nrm, tok);
+    const float nx[2] = {nrm[0].x, nrm[1].x}, nres[2] = {nrm[0].y, nrm[1].y};
+    const int64_t n = hf ? tok[1] : tok[0];
+    const int64_t bh = n / L;
+    (void)run(Mode<true>(), b, nx, nres, (unsigned)(hf * 32 + tl) < c, bh, n - bh * L);
+  };
+
+  // head and position of the wave's first token (wave-uniform), advanced by
+  // the walk's stride at the end of every token tile: one division per walk
+  const int64_t tfirst = (int64_t)grp * kTokWG + __builtin_amdgcn_readfirstlane(w) * kTokWave;
+  walks::TokenWalk tw;
+  tw.init(tfirst, (int64_t)ngrp * kTokWG, L);
+  const uint64_t below = (1ull << lane) - 1ull;
+  unsigned nq = 0;  // tokens in the wave's rescan queue (wave-uniform)
+  for (int j = grp; j < n_tok_tiles; j += ngrp) {
+    const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
+    f16x8_t bx[2][KS];
+    float nx[2], nres[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bx[s][ks] = bn[s][ks];
+      nx[s] = nn[s].x;
+      nres[s] = nn[s].y;
+    }
+    if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
+    const int64_t n = tok0 + hf * 32 + tl;
+    int64_t bh, i;
+    tw.at(hf * 32 + tl, bh, i);
+    const bool open = run(Mode<false>(), bx, nx, nres, n < N, bh, i);
+    // append the open rows' tokens to the wave's queue, in lane order
+    const uint64_t m = __ballot(open);
+    if (open) wq[nq + (unsigned)__popcll(m & below)] = (uint32_t)n;
+    nq += (unsigned)__popcll(m);
+    if (nq >= 64) {
+      rescan(64);
+      // the rest (fewer than 64) moves to the front
+      const uint32_t rest = lane + 64 < (int)nq ? wq[64 + lane] : 0u;
+      if (lane + 64 < (int)nq) wq[lane] = rest;
+      nq -= 64;
     }
     tw.advance();
   }
+  if (nq > 0) rescan(nq);
   // move the workgroup's queued entries to the global queues
   __syncthreads();
   unsigned* base_l = qn_l + 2;
@@ -657,6 +768,7 @@ hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipS
 
 bool hash_mfma_supported(const Problem& p) {
   if (p.dtype != LSH_ATTN_BF16 || p.nb < 2 || (p.d != 64 && p.d != 128)) return false;
+  if (p.n_token_heads() >= ((int64_t)1 << 32)) return false;  // rescan queues hold u32 tokens
   const int hp = hash_half_pad(p);
   const int bytes = p.d == 64 ? lds_bytes<64>(hp) : lds_bytes<128>(hp);
   return bytes <= 150 * 1024;
