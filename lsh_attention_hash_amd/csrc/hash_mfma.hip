@@ -51,10 +51,10 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;     // 4 waves, one per SIMD; each wave pipelines its own work
+constexpr int kThreads = 512;     // 8 waves, two per SIMD: one's MFMAs cover the other's waits
 constexpr int kTokWave = 64;      // 2 sets of 32 tokens per wave
 constexpr int kTokWG = kThreads / 64 * kTokWave;
-constexpr int kRotLoads = 32;     // rotation loads per thread in flight (32 x 16 B x 256 = 128 KB)
+constexpr int kRotLoads = 8;      // rotation loads per thread in flight (8 x 16 B x 512 = 64 KB)
 using hx::f16_round;
 using hx::kF16Max;
 using hx::kF16MinNormal;
@@ -280,8 +280,9 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   // x in fp16 as the B operand: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
   // of token tl of each set, K-step ks covering dims hf*D/2 + 8ks + 0..7 (the
   // K order of both operands is permuted the same way, which leaves the
-  // product as is). The next token tile is loaded while this one runs; the
-  // first one while the rotation is copied into LDS.
+  // product as is). A wave loads its token rows when it starts a tile (the
+  // other wave of its SIMD computes meanwhile); the first tile's rows while
+  // the rotation is copied into LDS.
   f16x8_t bn[2][KS];
   float2 nn[2];
   auto load_rows = [&](f16x8_t (&b)[2][KS], float2 (&nrm)[2], const int64_t (&tok)[2]) {
@@ -343,9 +344,8 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     uint32_t t1[2] = {0u, 0u}, t2[2] = {0u, 0u}, t3[2] = {0u, 0u};
     uint32_t u1[2] = {0u, 0u}, u2[2] = {0u, 0u}, u3[2] = {0u, 0u};
     // Rotation tiles (the A operand, shared by both sets) are read from LDS
-    // one step ahead: even tiles into at0, odd tiles into at1. A read past the
-    // last tile re-reads the last one (never used).
-    f16x8_t at0[KS], at1[KS];
+    // at the start of the step that multiplies them. A read past the last
+    // tile re-reads the last one (never used).
     auto load_tile = [&](int kt, f16x8_t (&at)[KS]) {
       const int kc = kt < ntiles ? kt : ntiles - 1;
       const unsigned char* arow = lds + (kc * 32 + tl) * ROWB + hf * D;
@@ -392,13 +392,14 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     constexpr int kFoldPerMfma = kT3 ? 8 : 5;
     // Tiles alternate between two accumulator pairs: each set's keys of tile
     // kt are folded from one pair while the MFMAs of tile kt + 1 fill the
-    // other, so the fold reads the MFMA results in place (no copies); the
-    // rotation tile kt + 2 is read meanwhile. The group barriers interleave
-    // one MFMA with the vector work around it.
-    auto step = [&](int kt, floatx16_t (&cur)[2], floatx16_t (&nxt)[2], const f16x8_t (&use)[KS],
-                    f16x8_t (&pre)[KS]) {
-      load_tile(kt + 2, pre);
-      set_mfma(nxt[0], 0, use);
+    // other, so the fold reads the MFMA results in place (no copies). The
+    // group barriers interleave one MFMA with the vector work around it.
+    // one rotation tile buffer: tile kt + 1 is read at the start of step kt,
+    // the fold of tile kt covering the read's latency
+    f16x8_t at[KS];
+    auto step = [&](int kt, floatx16_t (&cur)[2], floatx16_t (&nxt)[2]) {
+      load_tile(kt + 1, at);
+      set_mfma(nxt[0], 0, at);
       fold(kt, cur[0], 0);
       __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // rotation tile reads
       __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
         __builtin_amdgcn_sched_group_barrier(0x002, kFoldPerMfma, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      set_mfma(nxt[1], 1, use);
+      set_mfma(nxt[1], 1, at);
       fold(kt, cur[1], 1);
       __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
 #pragma unroll
@@ -419,17 +420,16 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       __builtin_amdgcn_sched_barrier(0);
     };
     floatx16_t even[2], odd[2];
-    load_tile(0, at0);
-    load_tile(1, at1);
-    set_mfma(even[0], 0, at0);
-    set_mfma(even[1], 1, at0);
+    load_tile(0, at);
+    set_mfma(even[0], 0, at);
+    set_mfma(even[1], 1, at);
     int kt = 0;
     for (; kt + 2 < ntiles; kt += 2) {
-      step(kt, even, odd, at1, at0);
-      step(kt + 1, odd, even, at0, at1);
+      step(kt, even, odd);
+      step(kt + 1, odd, even);
     }
     if (kt + 1 < ntiles) {
-      step(kt, even, odd, at1, at0);
+      step(kt, even, odd);
       fold(kt + 1, odd[0], 0);
       fold(kt + 1, odd[1], 1);
     } else {
@@ -548,6 +548,7 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   unsigned nq = 0;  // tokens in the wave's rescan queue (wave-uniform)
   for (int j = grp; j < n_tok_tiles; j += ngrp) {
     const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
+    if (j != grp) fetch(j);
     f16x8_t bx[2][KS];
     float nx[2], nres[2];
 #pragma unroll
@@ -557,7 +558,6 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       nx[s] = nn[s].x;
       nres[s] = nn[s].y;
     }
-    if (j + ngrp < n_tok_tiles) fetch(j + ngrp);
     const int64_t n = tok0 + hf * 32 + tl;
     int64_t bh, i;
     tw.at(hf * 32 + tl, bh, i);

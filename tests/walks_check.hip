@@ -57,10 +57,10 @@ static int check_sort(int tiles, int64_t nseg) {
 }
 
 // hash: every (round, token-head) once; the incremental (head, position)
-// equals the division; every row index in range. 4 waves of 64 tokens per
-// workgroup (the kernel's token tile), lanes as offsets 0..63 of a wave.
-static int check_hash(int64_t BH, int64_t L, int R, int n_cu, int per_cu) {
-  const int kTokWave = 64, kTokWG = 4 * kTokWave;
+// equals the division; every row index in range. `waves` waves of 64 tokens
+// per workgroup (the kernel's token tile: 8), lanes as offsets 0..63 of a wave.
+static int check_hash(int64_t BH, int64_t L, int R, int n_cu, int per_cu, int waves) {
+  const int kTokWave = 64, kTokWG = waves * kTokWave;
   const int64_t N = BH * L;
   const int n_tok_tiles = (int)((N + kTokWG - 1) / kTokWG);
   const int64_t grid = hash_grid(n_cu, per_cu, R, n_tok_tiles);
@@ -73,7 +73,7 @@ static int check_hash(int64_t BH, int64_t L, int R, int n_cu, int per_cu) {
     hash_block((unsigned)b, R, r, grp);
     if (r < 0 || r >= R || grp < 0 || grp >= ngrp) return fail("hash block", b, r, grp);
     if (block_rg[(size_t)(r * ngrp + grp)]++) return fail("hash (round, group) twice", b, r, grp);
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < waves; ++w) {
       TokenWalk tw;
       tw.init((int64_t)grp * kTokWG + w * kTokWave, (int64_t)ngrp * kTokWG, L);
       for (int j = grp; j < n_tok_tiles; j += ngrp) {
@@ -114,11 +114,13 @@ int main() {
       for (int R : {1, 2, 3, 4, 5, 8})
         for (int n_cu : {1, 8, 80, 256})
           for (int per_cu : {1, 2})
-            if (check_hash(bh, L, R, n_cu, per_cu)) return 1;
+            for (int waves : {8, 4})
+              if (check_hash(bh, L, R, n_cu, per_cu, waves)) return 1;
   // the bench's largest walks, in full
-  if (check_hash(8, 65536, 4, 256, 1) || check_hash(64, 12288, 8, 256, 2) ||
-      check_hash(16, 32768, 8, 256, 1))
-    return 1;
+  for (int waves : {8, 4})
+    if (check_hash(8, 65536, 4, 256, 1, waves) || check_hash(64, 12288, 8, 256, 2, waves) ||
+        check_hash(16, 32768, 8, 256, 1, waves) || check_hash(3, 1000, 3, 80, 1, waves))
+      return 1;
   if (check_ranges(1024, 32, 4, 16, 512) || check_ranges(192, 512, 8, 16, 512) ||
       check_ranges(512, 128, 8, 16, 256))
     return 1;
