@@ -581,8 +581,8 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const void* qk_sorted, const void* v_sorted, const int32_t* perm,
                               const float* knorm, const uint16_t* buckets, OT* o, float* lse,
                               hipStream_t s) {
-  static bool configured = false;
-  if (!configured) {
+  static bool configured[kMaxDevices] = {};
+  if (first_on_device(configured)) {
     // allow the dynamic LDS size above the 64 KiB default
     (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, OT, true, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
@@ -601,7 +601,6 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
         (const void*)k_attend_mfma<128, OT, false, false, false, true, true>};
     for (const void* f : variants)
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
-    configured = true;
   }
   if (p.d == 64) launch_d<64, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, buckets, o, lse, s);
   else launch_d<128, OT>(p, qk, v, qk_sorted, v_sorted, perm, knorm, buckets, o, lse, s);
@@ -611,13 +610,12 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
 hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* v,
                                   const int32_t* perm, const float* knorm, const void* dout,
                                   float* od, float* lse, hipStream_t s) {
-  static bool configured = false;
-  if (!configured) {
+  static bool configured[kMaxDevices] = {};
+  if (first_on_device(configured)) {
     (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, float, true, false, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
     (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, float, false, false, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
-    configured = true;
   }
   auto go = [&](auto d) {
     constexpr int D = decltype(d)::value;

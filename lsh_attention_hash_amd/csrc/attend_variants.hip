@@ -389,11 +389,10 @@ void launch_one(const Problem& p, const void* qk, const void* v, const int32_t* 
                 const float* knorm, const uint16_t* bkt, const int32_t* inv, OT* o, float* lse,
                 hipStream_t s) {
   constexpr int shmem = VLds<D, NS, DD>::kBytes;
-  static bool configured = false;
-  if (!configured) {
+  static bool configured[kMaxDevices] = {};
+  if (first_on_device(configured)) {
     (void)hipFuncSetAttribute((const void*)k_attend_var<D, CAUSAL, NS, DD, OT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
-    configured = true;
   }
   const int64_t nseg = p.nseg();
   const walks::RangeShape sh =

@@ -518,13 +518,12 @@ void launch_gt(const Problem& p, const void* qk, const void* v, const int32_t* p
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
                                 BwdWorkspace& b, hipStream_t s) {
-  static bool configured = false;
-  if (!configured) {
+  static bool configured[kMaxDevices] = {};
+  if (first_on_device(configured)) {
     configure<64, float>();
     configure<128, float>();
     configure<64, _Float16>();
     configure<128, _Float16>();
-    configured = true;
   }
   if (bwd_rows_half(p)) launch_gt<_Float16>(p, qk, v, perm, dout, knorm, b, s);
   else launch_gt<float>(p, qk, v, perm, dout, knorm, b, s);

@@ -170,6 +170,22 @@ constexpr int kVariantFlags = LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_SAME_BUCK
 
 // Per-round outputs are kept in fp16 on the matrix-core path unless the
 // caller asks for fp32.
+// Kernel attributes (the LDS size above 64 KiB) are set once per device:
+// `done` holds one flag per device index; past kMaxDevices the attribute is
+// set on every call (setting it again is harmless).
+constexpr int kMaxDevices = 64;
+inline bool first_on_device(bool (&done)[kMaxDevices]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return true;
+  if (done[dev]) return false;
+  done[dev] = true;
+  return true;
+}
+
 inline bool round_outputs_half(const Problem& p) {
   return (attend_mfma_supported(p) || attend_variant_mfma_supported(p)) &&
          !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
