@@ -154,16 +154,15 @@ __device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, u
   t3 = __float_as_uint(n3);
 }
 
-// x -> fp16 (clamped to +-65504, |x| < 2^-14 flushed to 0), once per forward
-// for every round; with the upper bounds of |x16| and |x - x16| per row that
-// the certificate needs, and the squared norm of the bf16 row (fp32), which
-// the attention turns into its key scale. D/8 consecutive lanes share a row.
-// Block 0 also clears the norm bounds and queue counters of this forward
-// (the rotation preparation, launched next, accumulates into them).
-// With kX16 = false only the squared norms are produced.
+// Per row, once per forward for every round: the upper bounds of |x16| and
+// |x - x16| that the certificate needs (x16: the fp16 row the projection
+// converts in registers, hx::x16_pair), and the squared norm of the bf16 row
+// (fp32), which the attention turns into its key scale. D/8 consecutive
+// lanes share a row. Block 0 also clears the norm bounds and queue counters
+// of this forward (the rotation preparation, launched next, accumulates into
+// them). With kX16 = false only the squared norms are produced.
 template <int D, bool kX16>
 __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
-                                                  uint4* __restrict__ x16,
                                                   float2* __restrict__ xnorm,
                                                   float* __restrict__ knorm, int64_t N,
                                                   unsigned* __restrict__ clear, int n_clear) {
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
     const uint4 raw = qk[row * kLpr + sub];
     float a = 0.f, b = 0.f, c = 0.f;
     if (kX16) {
-      x16[row * kLpr + sub] = hx::x16_piece(raw, a, b, c);
+      (void)hx::x16_piece(raw, a, b, c);
     } else {
       const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -247,7 +246,7 @@ using Mode = std::integral_constant<bool, B>;
 // columns).
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_hash_mfma(
-    const uint16_t* __restrict__ x16, const float2* __restrict__ xnorm,
+    const uint16_t* __restrict__ qkb, const float2* __restrict__ xnorm,
     const _Float16* __restrict__ rh,
     const unsigned* __restrict__ bounds_u, uint16_t* __restrict__ buckets,
     int32_t* __restrict__ buckets_out, QA* __restrict__ qa, uint2* __restrict__ qb,
@@ -280,22 +279,35 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
   // x in fp16 as the B operand: lane half hf holds dims [hf*D/2, hf*D/2 + D/2)
   // of token tl of each set, K-step ks covering dims hf*D/2 + 8ks + 0..7 (the
   // K order of both operands is permuted the same way, which leaves the
-  // product as is). A wave loads its token rows when it starts a tile (the
-  // other wave of its SIMD computes meanwhile); the first tile's rows while
-  // the rotation is copied into LDS.
-  f16x8_t bn[2][KS];
+  // product as is). A wave loads its token rows (bf16) when it starts a tile
+  // (the other wave of its SIMD computes meanwhile) and converts them to
+  // fp16 in registers (hx::x16_pair, 1.5 instructions per value); the first
+  // tile's rows are loaded while the rotation is copied into LDS.
+  uint4 bn[2][KS];
   float2 nn[2];
-  auto load_rows = [&](f16x8_t (&b)[2][KS], float2 (&nrm)[2], const int64_t (&tok)[2]) {
+  auto load_rows = [&](uint4 (&b)[2][KS], float2 (&nrm)[2], const int64_t (&tok)[2]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const uint4* src = (const uint4*)(x16 + tok[s] * D) + hf * KS;
+      const uint4* src = (const uint4*)(qkb + tok[s] * D) + hf * KS;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 u = src[ks];
-        b[s][ks] = __builtin_bit_cast(f16x8_t, u);
-      }
+      for (int ks = 0; ks < KS; ++ks) b[s][ks] = src[ks];
       nrm[s] = xnorm[tok[s]];
     }
+  };
+  auto to_f16 = [&](f16x8_t (&bx)[2][KS], const uint4 (&b)[2][KS]) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t w[4] = {b[s][ks].x, b[s][ks].y, b[s][ks].z, b[s][ks].w};
+        uint32_t h[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float x0, x1;
+          h[q] = hx::x16_pair(w[q], x0, x1);
+        }
+        bx[s][ks] = __builtin_bit_cast(f16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+      }
   };
   auto fetch = [&](int j) {
     int64_t tok[2];
@@ -530,9 +542,11 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
       const unsigned e = (unsigned)(s * 32 + tl);
       tok[s] = e < c ? (int64_t)wq[e] : 0;
     }
-    f16x8_t b[2][KS];
+    uint4 raw[2][KS];
     float2 nrm[2];
-    load_rows(b, nrm, tok);
+    load_rows(raw, nrm, tok);
+    f16x8_t b[2][KS];
+    to_f16(b, raw);
     const float nx[2] = {nrm[0].x, nrm[1].x}, nres[2] = {nrm[0].y, nrm[1].y};
     const int64_t n = hf ? tok[1] : tok[0];
     const int64_t bh = n / L;
@@ -550,11 +564,10 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const int64_t tok0 = (int64_t)j * kTokWG + w * kTokWave;
     if (j != grp) fetch(j);
     f16x8_t bx[2][KS];
+    to_f16(bx, bn);
     float nx[2], nres[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bx[s][ks] = bn[s][ks];
       nx[s] = nn[s].x;
       nres[s] = nn[s].y;
     }
@@ -759,10 +772,10 @@ hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipS
   const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
   if (p.d == 128)
     hipLaunchKernelGGL((k_hash_x16<128, false>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                       nullptr, nullptr, knorm, N, nullptr, 0);
+                       nullptr, knorm, N, nullptr, 0);
   else
     hipLaunchKernelGGL((k_hash_x16<64, false>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                       nullptr, nullptr, knorm, N, nullptr, 0);
+                       nullptr, knorm, N, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -777,7 +790,7 @@ bool hash_mfma_supported(const Problem& p) {
 hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, HashScratch& hs,
                             uint16_t* buckets, int32_t* buckets_out, unsigned long long* stats,
                             float* knorm, hipStream_t s, hipEvent_t after_prep,
-                            hipEvent_t after_main, bool x16_ready) {
+                            hipEvent_t after_main, bool norms_ready) {
   const int half = p.half();
   const int hp = hash_half_pad(p);
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
@@ -798,8 +811,8 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   }
   const int per_cu = hs.per_cu;
   const int64_t grid = walks::hash_grid(hs.n_cu, per_cu, p.R, n_tok_tiles);
-  if (x16_ready) {
-    // the projection wrote the fp16 copy and the norms; clear what the
+  if (norms_ready) {
+    // the projection wrote the row norms and their bounds; clear what the
     // pre-pass would have cleared
     hipLaunchKernelGGL(k_clear_u32, dim3(1), dim3(256), 0, s, hs.bounds, 4 * p.R + 2);
   } else {
@@ -808,23 +821,23 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
     if (p.d == 128)
       hipLaunchKernelGGL((k_hash_x16<128, true>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (uint4*)hs.x16, (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
+                         (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
     else
       hipLaunchKernelGGL((k_hash_x16<64, true>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (uint4*)hs.x16, (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
+                         (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
   }
   hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * (hp / 32))), dim3(256), 0, s, rot, hs.rh,
                      hs.rt, hs.bounds, p.d, half, hp);
   if (after_prep) (void)hipEventRecord(after_prep, s);
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_mfma<128>, dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       (const uint16_t*)hs.x16, (const float2*)hs.xnorm, hs.rh, hs.bounds,
+                       (const uint16_t*)qk, (const float2*)hs.xnorm, hs.rh, hs.bounds,
                        buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);
   else
     hipLaunchKernelGGL(k_hash_mfma<64>, dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       (const uint16_t*)hs.x16, (const float2*)hs.xnorm, hs.rh, hs.bounds,
+                       (const uint16_t*)qk, (const float2*)hs.xnorm, hs.rh, hs.bounds,
                        buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);

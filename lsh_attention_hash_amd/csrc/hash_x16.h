@@ -1,7 +1,7 @@
-// hash_x16.h -- the per-row preparation of the matrix-core hash: the fp16
-// copy of a bf16 qk row and the bounds the hash's certificate needs. Shared
-// by the hash's own pre-pass and by the projection kernel, which produces the
-// same values for the rows it writes.
+// hash_x16.h -- the fp16 form of a bf16 qk row in the matrix-core hash and
+// the bounds its certificate needs. Shared by the hash kernel (which converts
+// the rows it loads), the hash's norm pre-pass and the projection kernel,
+// which produces the same bounds for the rows it writes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,26 +13,37 @@ namespace hx {
 constexpr float kF16Max = 65504.0f;
 constexpr float kF16MinNormal = 6.103515625e-05f;  // 2^-14
 
-// fp16 value of x as the projection uses it: clamped to the fp16 range and
-// flushed to 0 below the smallest normal
+// fp16 value of a rotation entry: clamped to the fp16 range and flushed to 0
+// below the smallest normal
 __device__ __forceinline__ float f16_round(float x) {
   const float c = fminf(fmaxf(x, -kF16Max), kF16Max);
   return fabsf(c) < kF16MinNormal ? 0.f : (float)(_Float16)c;
 }
 
+// fp16 values of the bf16 pair in w (low half first) as the projection uses
+// them: converted toward zero by v_cvt_pkrtz_f16_f32, exactly for every bf16
+// value in the fp16 range, within 2^-24 below it (fp16 subnormals, which the
+// matrix cores and v_dot2 take as they are), to the largest finite fp16
+// value above it. Every kernel that makes or bounds the fp16 row uses this.
+__device__ __forceinline__ uint32_t x16_pair(uint32_t w, float& x0, float& x1) {
+  x0 = __uint_as_float(w << 16);
+  x1 = __uint_as_float(w & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+}
+
 // One 16-byte piece of a bf16 row (8 values): returns its fp16 copy and adds
-// to a, b, c the squares of the copy, of the rounding error and of the values.
+// to a, b, c the squares of the copy, of the conversion error and of the
+// values.
 __device__ __forceinline__ uint4 x16_piece(uint4 raw, float& a, float& b, float& c) {
   const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
   uint32_t out[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
+    float x0, x1;
+    out[q] = x16_pair(wv[q], x0, x1);
     c = fmaf(x0, x0, fmaf(x1, x1, c));
-    const float h0 = f16_round(x0), h1 = f16_round(x1);
-    const _Float16 e0 = (_Float16)h0, e1 = (_Float16)h1;
-    out[q] = (uint32_t)__builtin_bit_cast(uint16_t, e0) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+    const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(out[q] & 0xFFFFu));
+    const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(out[q] >> 16));
     a = fmaf(h0, h0, fmaf(h1, h1, a));
     b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
   }

@@ -86,7 +86,6 @@ void free_ws(lsh::Workspace& w) {
   (void)hipFree(w.hash.bounds);
   (void)hipFree(w.hash.queue_a);
   (void)hipFree(w.hash.queue_b);
-  (void)hipFree(w.hash.x16);
   (void)hipFree(w.hash.xnorm);
   w = lsh::Workspace{};
 }
@@ -146,7 +145,6 @@ int forward_parts(const lsh::Problem& p, lsh::Workspace& w, Part* parts) {
     add(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4);
     add(&w.hash.queue_a, rows * 16);
     add(&w.hash.queue_b, rows * 8);
-    add(&w.hash.x16, p.n_token_heads() * p.d * 2);
     add(&w.hash.xnorm, p.n_token_heads() * 8);
   }
   if (p.flags & LSH_ATTN_FLAG_DEDUP) add(&w.inv, rows * 4);
@@ -220,10 +218,10 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
 namespace {
 
 // The forward after the inputs are checked; ev: the timed call's events or
-// null; x16_ready: the projection already prepared the hash's fp16 copy.
+// null; norms_ready: the projection already wrote the hash's row norm bounds.
 int forward_body(const lsh::Problem& p, lsh::Workspace& w, const void* qk, const void* v,
                  const float* rotations, void* out, float* lse, int32_t* buckets, int32_t* perm,
-                 hipStream_t s, hipEvent_t* ev, bool x16_ready) {
+                 hipStream_t s, hipEvent_t* ev, bool norms_ready) {
   auto mark = [&](int j) {
     if (ev) (void)hipEventRecord(ev[j], s);
   };
@@ -237,7 +235,7 @@ int forward_body(const lsh::Problem& p, lsh::Workspace& w, const void* qk, const
   if (e == hipSuccess) {
     if (mfma_hash) {
       e = lsh::launch_hash_mfma(p, qk, rotations, w.hash, w.buckets, buckets, w.stats, w.knorm, s,
-                                ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, x16_ready);
+                                ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, norms_ready);
     } else {
       if (w.knorm) e = lsh::launch_key_norms(p, qk, w.knorm, s);
       mark(1);
@@ -321,14 +319,14 @@ int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const voi
   h->last_stream = s;
   hipEvent_t* ev = next_events(h, true);
   if (ev) (void)hipEventRecord(ev[8], s);
-  bool x16_ready = false;
+  bool norms_ready = false;
   const hipError_t e = lsh::launch_project(h->p, model_dim, x, w_qk, w_v, qk, v, h->ws.hash,
-                                           h->ws.knorm, &x16_ready, s);
+                                           h->ws.knorm, &norms_ready, s);
   if (ev) (void)hipEventRecord(ev[9], s);
   if (e != hipSuccess) return release_on_error(h, ev, LSH_ATTN_ERR_HIP);
   return release_on_error(
       h, ev,
-      forward_body(h->p, h->ws, qk, v, rotations, out, lse, buckets, perm, s, ev, x16_ready));
+      forward_body(h->p, h->ws, qk, v, rotations, out, lse, buckets, perm, s, ev, norms_ready));
 }
 
 int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,

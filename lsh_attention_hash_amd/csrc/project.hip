@@ -14,9 +14,9 @@
 // the other, so the x tile is read from HBM once and from that XCD's L2 by
 // the others). The epilogue rounds the tile to bf16 and passes it through LDS so that each
 // lane writes 16 contiguous bytes of a row. For qk tiles the same pass produces
-// what the hash's pre-pass would compute from these rows (the fp16 copy of
-// qk, the norm bounds of the copy and of its rounding error, and the squared
-// norm), with the same per-row arithmetic, so the hash can skip that pass.
+// what the hash's pre-pass would compute from these rows (the norm bounds of
+// the rows' fp16 form and of its conversion error, and the squared norm),
+// with the same per-row arithmetic, so the hash can skip that pass.
 #include "dtype.h"
 #include "gemm_core.h"
 #include "hash_x16.h"
@@ -41,7 +41,7 @@ struct PLds {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     const uint4* __restrict__ x, const uint4* __restrict__ w_qk, const uint4* __restrict__ w_v,
-    uint4* __restrict__ qk, uint4* __restrict__ v, uint4* __restrict__ x16,
+    uint4* __restrict__ qk, uint4* __restrict__ v,
     float2* __restrict__ xnorm, float* __restrict__ knorm, int64_t M, int L, int H,
     int model_dim) {
   using Lay = PLds<D>;
@@ -92,8 +92,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     if (live) (is_v ? v : qk)[th * kLpr + sub] = raw;
     if (!is_v) {  // the hash pre-pass of this row (all lanes of a row are live together)
       float a = 0.f, bb = 0.f, c = 0.f;
-      const uint4 h16 = hx::x16_piece(raw, a, bb, c);
-      if (live) x16[th * kLpr + sub] = h16;
+      (void)hx::x16_piece(raw, a, bb, c);
 #pragma unroll
       for (int off = 1; off < kLpr; off <<= 1) {
         c += __shfl_xor(c, off);
@@ -141,9 +140,9 @@ bool project_mfma_supported(const Problem& p, int model_dim) {
 
 hipError_t launch_project(const Problem& p, int model_dim, const void* x, const void* w_qk,
                           const void* w_v, void* qk, void* v, HashScratch& hs, float* knorm,
-                          bool* x16_ready, hipStream_t s) {
+                          bool* norms_ready, hipStream_t s) {
   const int64_t M = (int64_t)p.B * p.L;
-  *x16_ready = false;
+  *norms_ready = false;
   if (project_mfma_supported(p, model_dim) && knorm) {
     // row tiles rounded up to a multiple of 8 (one per XCD); the extra
     // workgroups return at once
@@ -156,7 +155,7 @@ hipError_t launch_project(const Problem& p, int model_dim, const void* x, const 
                                   hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
       hipLaunchKernelGGL(k_proj_mfma<128>, dim3(grid), dim3(kThreads), shmem, s,
                          (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
-                         (uint4*)v, (uint4*)hs.x16, (float2*)hs.xnorm, knorm, M, p.L, p.H,
+                         (uint4*)v, (float2*)hs.xnorm, knorm, M, p.L, p.H,
                          model_dim);
     } else {
       constexpr int shmem = PLds<64>::kBytes;
@@ -165,11 +164,11 @@ hipError_t launch_project(const Problem& p, int model_dim, const void* x, const 
                                   hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
       hipLaunchKernelGGL(k_proj_mfma<64>, dim3(grid), dim3(kThreads), shmem, s,
                          (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
-                         (uint4*)v, (uint4*)hs.x16, (float2*)hs.xnorm, knorm, M, p.L, p.H,
+                         (uint4*)v, (float2*)hs.xnorm, knorm, M, p.L, p.H,
                          model_dim);
     }
     hs.proj_attr = true;
-    *x16_ready = true;
+    *norms_ready = true;
     return hipGetLastError();
   }
   const int64_t n = p.n_token_heads() * p.d;
