@@ -74,11 +74,13 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, windo
     n_a = (stats or {}).get("n_exact_rescored", 0)
     n_b = (stats or {}).get("n_full_fallback", 0)
     return {
-        # fp16 copy of qk and its two norm bounds; rotation copies (fp16, fp32)
-        "hash_prep": {"bytes": N * d * e + N * d * 2 + N * 8 + R * d * half * (4 + 2 + 4)},
+        # qk read for the two norm bounds of its fp16 form and the key norms;
+        # rotation copies (fp16, fp32)
+        "hash_prep": {"bytes": N * d * e + N * 12 + R * d * half * (4 + 2 + 4)},
         # projection x.R for every token-head and round: nb/2 MACs of length d;
-        # reads the fp16 rows and norm bounds once, writes the bucket ids
-        "hash": {"flops": N * R * d * nb, "bytes": N * d * 2 + N * 8 + N * R * 2},
+        # reads the rows (converted to fp16 in registers) and norm bounds once,
+        # writes the bucket ids
+        "hash": {"flops": N * R * d * nb, "bytes": N * d * e + N * 8 + N * R * 2},
         # exact fp64 dot products of the re-scored rows
         "hash_rescore": {"flops64": 2 * d * (2 * n_a + half * n_b),
                          "bytes": (n_a + n_b) * d * e + 2 * n_a * d * 4},
@@ -93,12 +95,11 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, windo
         # R per-round rows and lse read, one output row written
         "combine": {"bytes": N * R * (d * ro + 4) + N * d * eo},
         # forward from x: x [B*L, K] times the two weights [H*d, K]; x and the
-        # weights read once, qk and v written, and the hash's fp16 copy of qk
-        # with its norms (K = model_dim)
+        # weights read once, qk and v written, with the hash's norm bounds
+        # and the key norms of qk (K = model_dim)
         "project": {"flops": 2 * w.batch * w.seq_len * (model_dim or 0) * 2 * w.heads * d,
                     "bytes": w.batch * w.seq_len * (model_dim or 0) * e
-                    + 2 * w.heads * d * (model_dim or 0) * e + 2 * N * d * e + N * d * 2
-                    + N * 12},
+                    + 2 * w.heads * d * (model_dim or 0) * e + 2 * N * d * e + N * 12},
     }
 
 
