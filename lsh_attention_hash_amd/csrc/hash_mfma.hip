@@ -157,45 +157,73 @@ __device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, u
 // Per row, once per forward for every round: the upper bounds of |x16| and
 // |x - x16| that the certificate needs (x16: the fp16 row the projection
 // converts in registers, hx::x16_pair), and the squared norm of the bf16 row
-// (fp32), which the attention turns into its key scale. D/8 consecutive
-// lanes share a row. Block 0 also clears the norm bounds and queue counters
-// of this forward (the rotation preparation, launched next, accumulates into
-// them). With kX16 = false only the squared norms are produced.
+// (fp32), which the attention turns into its key scale. 4 consecutive lanes
+// share a row (D/32 16-byte pieces each), two rows per lane group in flight.
+// Block 0 also clears the norm bounds and queue counters of this forward
+// (the rotation preparation, launched next, accumulates into them). With
+// kX16 = false only the squared norms are produced.
+constexpr int kNormLanes = 4;
 template <int D, bool kX16>
 __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
                                                   float2* __restrict__ xnorm,
                                                   float* __restrict__ knorm, int64_t N,
                                                   unsigned* __restrict__ clear, int n_clear) {
-  constexpr int kLpr = D / 8;
+  constexpr int kPieces = D / 8 / kNormLanes;      // 16-byte pieces per lane and row
+  constexpr int kRowsPerBlock = 256 / kNormLanes;
   if (kX16 && blockIdx.x == 0)
     for (int i = threadIdx.x; i < n_clear; i += 256) clear[i] = 0u;
-  const int sub = threadIdx.x % kLpr;
-  const int64_t stride = (int64_t)gridDim.x * (256 / kLpr);
-  for (int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr; row < N;
-       row += stride) {
-    const uint4 raw = qk[row * kLpr + sub];
-    float a = 0.f, b = 0.f, c = 0.f;
-    if (kX16) {
-      (void)hx::x16_piece(raw, a, b, c);
-    } else {
-      const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
+  const int sub = threadIdx.x % kNormLanes;
+  const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+  for (int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kNormLanes; row0 < N;
+       row0 += 2 * stride) {
+    uint4 raw[2][kPieces];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float x0 = __uint_as_float(wv[q] << 16), x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
-        c = fmaf(x0, x0, fmaf(x1, x1, c));
-      }
-    }
+    for (int u = 0; u < 2; ++u) {
+      const int64_t row = row0 + u * stride;
+      const int64_t rc = row < N ? row : row0;
 #pragma unroll
-    for (int off = 1; off < kLpr; off <<= 1) {
-      c += __shfl_xor(c, off);
-      if (kX16) {
-        a += __shfl_xor(a, off);
-        b += __shfl_xor(b, off);
-      }
+      for (int k = 0; k < kPieces; ++k) raw[u][k] = qk[rc * (D / 8) + k * kNormLanes + sub];
     }
-    if (sub == 0) {
-      if (knorm) knorm[row] = c;
-      if (kX16) xnorm[row] = hx::norm_bounds(a, b);
+    // The sums follow the projection epilogue's order (one piece per lane,
+    // pairs combined by xor shuffles over 1, 2, 4, ...): per piece from 0,
+    // then across the 4 lanes (pieces k*4 + 0..3), then the lane's pieces
+    // pairwise, so both give the same bits.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t row = row0 + u * stride;
+      float bk[kPieces], ck[kPieces];
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) {
+        bk[k] = 0.f;
+        ck[k] = 0.f;
+        if (kX16) {
+          hx::x16_piece(raw[u][k], bk[k], ck[k]);
+        } else {
+          const uint32_t wv[4] = {raw[u][k].x, raw[u][k].y, raw[u][k].z, raw[u][k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float x0 = __uint_as_float(wv[q] << 16);
+            const float x1 = __uint_as_float(wv[q] & 0xFFFF0000u);
+            ck[k] = fmaf(x0, x0, fmaf(x1, x1, ck[k]));
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < kNormLanes; off <<= 1) {
+          ck[k] += __shfl_xor(ck[k], off);
+          if (kX16) bk[k] += __shfl_xor(bk[k], off);
+        }
+      }
+#pragma unroll
+      for (int span = 1; span < kPieces; span <<= 1)
+#pragma unroll
+        for (int k = 0; k < kPieces; k += 2 * span) {
+          ck[k] += ck[k + span];
+          bk[k] += bk[k + span];
+        }
+      if (sub == 0 && row < N) {
+        if (knorm) knorm[row] = ck[0];
+        if (kX16) xnorm[row] = hx::norm_bounds(ck[0], bk[0]);
+      }
     }
   }
 }
@@ -767,7 +795,7 @@ int hash_half_pad(const Problem& p) { return ((p.half() + 31) / 32) * 32; }
 
 hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipStream_t s) {
   const int64_t N = p.n_token_heads();
-  const int64_t rpb = 256 / (p.d / 8);
+  const int64_t rpb = 2 * (256 / kNormLanes);
   const int64_t want = (N + rpb - 1) / rpb;
   const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
   if (p.d == 128)
@@ -816,7 +844,7 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
     // pre-pass would have cleared
     hipLaunchKernelGGL(k_clear_u32, dim3(1), dim3(256), 0, s, hs.bounds, 4 * p.R + 2);
   } else {
-    const int64_t rpb = 256 / (p.d / 8);
+    const int64_t rpb = 2 * (256 / kNormLanes);
     const int64_t want = (N + rpb - 1) / rpb;
     const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
     if (p.d == 128)

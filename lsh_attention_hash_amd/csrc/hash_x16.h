@@ -31,29 +31,27 @@ __device__ __forceinline__ uint32_t x16_pair(uint32_t w, float& x0, float& x1) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
 }
 
-// One 16-byte piece of a bf16 row (8 values): returns its fp16 copy and adds
-// to a, b, c the squares of the copy, of the conversion error and of the
-// values.
-__device__ __forceinline__ uint4 x16_piece(uint4 raw, float& a, float& b, float& c) {
+// One 16-byte piece of a bf16 row (8 values): adds to b the squares of the
+// conversion error of its fp16 form and to c the squares of the values.
+// (|x16| <= |x| for every value, the conversion being toward zero, so the
+// row's |x| bounds |x16|.)
+__device__ __forceinline__ void x16_piece(uint4 raw, float& b, float& c) {
   const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
-  uint32_t out[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float x0, x1;
-    out[q] = x16_pair(wv[q], x0, x1);
+    const uint32_t h = x16_pair(wv[q], x0, x1);
     c = fmaf(x0, x0, fmaf(x1, x1, c));
-    const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(out[q] & 0xFFFFu));
-    const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(out[q] >> 16));
-    a = fmaf(h0, h0, fmaf(h1, h1, a));
+    const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+    const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(h >> 16));
     b = fmaf(x0 - h0, x0 - h0, fmaf(x1 - h1, x1 - h1, b));
   }
-  return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-// upper bounds of |x16| and |x - x16| from the row's sums (covering their
-// fp32 rounding)
-__device__ __forceinline__ float2 norm_bounds(float a, float b) {
-  return make_float2(sqrtf(a) * (1.0f + 1e-5f), sqrtf(b) * (1.0f + 1e-5f));
+// upper bounds of |x16| and |x - x16| from the row's sums of x^2 (c) and of
+// (x - x16)^2 (b), covering their fp32 rounding
+__device__ __forceinline__ float2 norm_bounds(float c, float b) {
+  return make_float2(sqrtf(c) * (1.0f + 1e-5f), sqrtf(b) * (1.0f + 1e-5f));
 }
 
 }  // namespace hx

@@ -91,17 +91,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
     const uint4 raw = *(const uint4*)(ot + r * Lay::kOutStride + sub * 16);
     if (live) (is_v ? v : qk)[th * kLpr + sub] = raw;
     if (!is_v) {  // the hash pre-pass of this row (all lanes of a row are live together)
-      float a = 0.f, bb = 0.f, c = 0.f;
-      (void)hx::x16_piece(raw, a, bb, c);
+      float bb = 0.f, c = 0.f;
+      hx::x16_piece(raw, bb, c);
 #pragma unroll
       for (int off = 1; off < kLpr; off <<= 1) {
         c += __shfl_xor(c, off);
-        a += __shfl_xor(a, off);
         bb += __shfl_xor(bb, off);
       }
       if (live && sub == 0) {
         knorm[th] = c;
-        xnorm[th] = hx::norm_bounds(a, bb);
+        xnorm[th] = hx::norm_bounds(c, bb);
       }
     }
   }
