@@ -62,21 +62,22 @@ using hx::kF16MinNormal;
 // upper bound of a non-negative double as float
 __device__ __forceinline__ float up_f32(double x) { return (float)(x * (1.0 + 1e-6)) + 1e-30f; }
 
-// One block of 256 threads per (round, 32-column tile): 8 groups of 32
-// threads read R row by row (coalesced over columns), the tile is transposed
-// in LDS and written out as rows of d.
+// Rotation preparation, one block of 256 threads per (round, 32-column
+// tile) `tb`: 8 groups of 32 threads read R row by row (coalesced over
+// columns), the tile is transposed in LDS and written out as rows of d; the
+// tile's maxima of |Rh_k|, |R_k - Rh_k| and |R_k| go to part[r][kt] (the
+// projection takes the maximum over the round's tiles).
 constexpr int kPrepMaxD = 128;
-__global__ __launch_bounds__(256) void k_hash_prep(const float* __restrict__ rot,
-                                                   _Float16* __restrict__ rh,
-                                                   float* __restrict__ rt,
-                                                   unsigned* __restrict__ bounds, int d, int half,
-                                                   int half_pad) {
+__device__ __forceinline__ void prep_tile(int tb, const float* __restrict__ rot,
+                                          _Float16* __restrict__ rh, float* __restrict__ rt,
+                                          float4* __restrict__ part, int d, int half,
+                                          int half_pad) {
   __shared__ __align__(16) _Float16 th[32][kPrepMaxD + 8];
   __shared__ __align__(16) float tx[32][kPrepMaxD + 4];
   __shared__ double red[3][8][33];
   const int ntiles = half_pad / 32;
-  const int kt = blockIdx.x % (unsigned)ntiles;
-  const int r = blockIdx.x / (unsigned)ntiles;
+  const int kt = tb % ntiles;
+  const int r = tb / ntiles;
   const int col = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int k = kt * 32 + col;
   // every load issued before the first use
@@ -128,12 +129,7 @@ __global__ __launch_bounds__(256) void k_hash_prep(const float* __restrict__ rot
       fb = fmaxf(fb, __shfl_xor(fb, off));
       fc = fmaxf(fc, __shfl_xor(fc, off));
     }
-    if (col == 0) {
-      // non-negative floats order like their bit patterns
-      atomicMax(bounds + r * 4 + 0, __float_as_uint(fa));
-      atomicMax(bounds + r * 4 + 1, __float_as_uint(fb));
-      atomicMax(bounds + r * 4 + 2, __float_as_uint(fc));
-    }
+    if (col == 0) part[r * ntiles + kt] = make_float4(fa, fb, fc, 0.f);
   }
 }
 
@@ -157,24 +153,21 @@ __device__ __forceinline__ void top3(uint32_t& t1, uint32_t& t2, uint32_t& t3, u
 // Per row, once per forward for every round: the upper bounds of |x16| and
 // |x - x16| that the certificate needs (x16: the fp16 row the projection
 // converts in registers, hx::x16_pair), and the squared norm of the bf16 row
-// (fp32), which the attention turns into its key scale. 4 consecutive lanes
-// share a row (D/32 16-byte pieces each), two rows per lane group in flight.
-// Block 0 also clears the norm bounds and queue counters of this forward
-// (the rotation preparation, launched next, accumulates into them). With
-// kX16 = false only the squared norms are produced.
+// (fp32), which the attention turns into its key scale; block `blk` of
+// `nblk`. 4 consecutive lanes share a row (D/32 16-byte pieces each), two
+// rows per lane group in flight. With kX16 = false only the squared norms
+// are produced.
 constexpr int kNormLanes = 4;
+constexpr int kNormRowsPerBlock = 2 * (256 / kNormLanes);  // per block and step
 template <int D, bool kX16>
-__global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
-                                                  float2* __restrict__ xnorm,
-                                                  float* __restrict__ knorm, int64_t N,
-                                                  unsigned* __restrict__ clear, int n_clear) {
+__device__ __forceinline__ void row_norms(int64_t blk, int64_t nblk, const uint4* __restrict__ qk,
+                                          float2* __restrict__ xnorm, float* __restrict__ knorm,
+                                          int64_t N) {
   constexpr int kPieces = D / 8 / kNormLanes;      // 16-byte pieces per lane and row
   constexpr int kRowsPerBlock = 256 / kNormLanes;
-  if (kX16 && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < n_clear; i += 256) clear[i] = 0u;
   const int sub = threadIdx.x % kNormLanes;
-  const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
-  for (int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kNormLanes; row0 < N;
+  const int64_t stride = nblk * kRowsPerBlock;
+  for (int64_t row0 = blk * kRowsPerBlock + threadIdx.x / kNormLanes; row0 < N;
        row0 += 2 * stride) {
     uint4 raw[2][kPieces];
 #pragma unroll
@@ -228,8 +221,28 @@ __global__ __launch_bounds__(256) void k_hash_x16(const uint4* __restrict__ qk,
   }
 }
 
-__global__ void k_clear_u32(unsigned* __restrict__ p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+template <int D>
+__global__ __launch_bounds__(256) void k_key_norms(const uint4* __restrict__ qk,
+                                                   float* __restrict__ knorm, int64_t N) {
+  row_norms<D, false>(blockIdx.x, gridDim.x, qk, nullptr, knorm, N);
+}
+
+// The hash's preparation in one launch: blocks 0 .. n_prep-1 prepare the
+// rotation tiles, the others the row norms (none when the projection wrote
+// them); the first of those clears the queue counters of this forward.
+template <int D>
+__global__ __launch_bounds__(256) void k_hash_prepare(
+    const float* __restrict__ rot, _Float16* __restrict__ rh, float* __restrict__ rt,
+    float4* __restrict__ part, const uint4* __restrict__ qk, float2* __restrict__ xnorm,
+    float* __restrict__ knorm, int64_t N, unsigned* __restrict__ qcount, int d, int half,
+    int half_pad, int n_prep) {
+  if ((int)blockIdx.x < n_prep) {
+    prep_tile(blockIdx.x, rot, rh, rt, part, d, half, half_pad);
+    return;
+  }
+  if ((int)blockIdx.x == n_prep && threadIdx.x < 2) qcount[threadIdx.x] = 0u;
+  row_norms<D, true>((int64_t)blockIdx.x - n_prep, (int64_t)gridDim.x - n_prep, qk, xnorm, knorm,
+                     N);
 }
 
 struct QA {  // two-candidate re-score
@@ -276,7 +289,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     const uint16_t* __restrict__ qkb, const float2* __restrict__ xnorm,
     const _Float16* __restrict__ rh,
-    const unsigned* __restrict__ bounds_u, uint16_t* __restrict__ buckets,
+    const float4* __restrict__ part, uint16_t* __restrict__ buckets,
     int32_t* __restrict__ buckets_out, QA* __restrict__ qa, uint2* __restrict__ qb,
     unsigned* __restrict__ qcount, int64_t N, int L, int R, int half, int half_pad, int ib,
     int n_tok_tiles) {
@@ -368,10 +381,14 @@ __global__ __launch_bounds__(kThreads) void k_hash_mfma(
     }
   }
   __syncthreads();
-  const float rh_max = __uint_as_float(bounds_u[r * 4 + 0]);
-  const float lo_max = __uint_as_float(bounds_u[r * 4 + 1]);
-  const float r_max = __uint_as_float(bounds_u[r * 4 + 2]);
   const int ntiles = half_pad / 32;
+  float rh_max = 0.f, lo_max = 0.f, r_max = 0.f;  // over the round's column tiles
+  for (int t = 0; t < ntiles; ++t) {
+    const float4 b = part[r * ntiles + t];
+    rh_max = fmaxf(rh_max, b.x);
+    lo_max = fmaxf(lo_max, b.y);
+    r_max = fmaxf(r_max, b.z);
+  }
 
   // One wave's 64 tokens (2 sets of 32) against every column of the round.
   // Returns whether this lane's row (token tl of set hf) is left open (main
@@ -795,15 +812,13 @@ int hash_half_pad(const Problem& p) { return ((p.half() + 31) / 32) * 32; }
 
 hipError_t launch_key_norms(const Problem& p, const void* qk, float* knorm, hipStream_t s) {
   const int64_t N = p.n_token_heads();
-  const int64_t rpb = 2 * (256 / kNormLanes);
-  const int64_t want = (N + rpb - 1) / rpb;
+  const int64_t want = (N + kNormRowsPerBlock - 1) / kNormRowsPerBlock;
   const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
   if (p.d == 128)
-    hipLaunchKernelGGL((k_hash_x16<128, false>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                       nullptr, knorm, N, nullptr, 0);
+    hipLaunchKernelGGL(k_key_norms<128>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk, knorm,
+                       N);
   else
-    hipLaunchKernelGGL((k_hash_x16<64, false>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                       nullptr, knorm, N, nullptr, 0);
+    hipLaunchKernelGGL(k_key_norms<64>, dim3(blocks), dim3(256), 0, s, (const uint4*)qk, knorm, N);
   return hipGetLastError();
 }
 
@@ -822,7 +837,11 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   const int half = p.half();
   const int hp = hash_half_pad(p);
   const int ib = ceil_log2(hp) > 5 ? ceil_log2(hp) : 5;
-  unsigned* qcount = hs.bounds + 4 * p.R;
+  // hs.bounds: per (round, column tile) the rotation's partial maxima
+  // (float4), then the counts of queues A and B
+  const int n_prep = p.R * (hp / 32);
+  float4* part = (float4*)hs.bounds;
+  unsigned* qcount = hs.bounds + 4 * n_prep;
   const int64_t N = p.n_token_heads();
   const int n_tok_tiles = (int)((N + kTokWG - 1) / kTokWG);
   // persistent grid: as many resident workgroups as fit, a multiple of 8 R
@@ -839,33 +858,28 @@ hipError_t launch_hash_mfma(const Problem& p, const void* qk, const float* rot, 
   }
   const int per_cu = hs.per_cu;
   const int64_t grid = walks::hash_grid(hs.n_cu, per_cu, p.R, n_tok_tiles);
-  if (norms_ready) {
-    // the projection wrote the row norms and their bounds; clear what the
-    // pre-pass would have cleared
-    hipLaunchKernelGGL(k_clear_u32, dim3(1), dim3(256), 0, s, hs.bounds, 4 * p.R + 2);
-  } else {
-    const int64_t rpb = 2 * (256 / kNormLanes);
-    const int64_t want = (N + rpb - 1) / rpb;
-    const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
-    if (p.d == 128)
-      hipLaunchKernelGGL((k_hash_x16<128, true>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
-    else
-      hipLaunchKernelGGL((k_hash_x16<64, true>), dim3(blocks), dim3(256), 0, s, (const uint4*)qk,
-                         (float2*)hs.xnorm, knorm, N, hs.bounds, 4 * p.R + 2);
-  }
-  hipLaunchKernelGGL(k_hash_prep, dim3((unsigned)(p.R * (hp / 32))), dim3(256), 0, s, rot, hs.rh,
-                     hs.rt, hs.bounds, p.d, half, hp);
+  // rotation tiles and row norms (none when the projection wrote them) in one launch
+  const int64_t n_rows = norms_ready ? 0 : N;
+  const int64_t want = (n_rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock;
+  const unsigned blocks = (unsigned)(n_prep + (want < 1 ? 1 : want < 65536 ? want : 65536));
+  if (p.d == 128)
+    hipLaunchKernelGGL(k_hash_prepare<128>, dim3(blocks), dim3(256), 0, s, rot, hs.rh, hs.rt, part,
+                       (const uint4*)qk, (float2*)hs.xnorm, knorm, n_rows, qcount, p.d, half, hp,
+                       n_prep);
+  else
+    hipLaunchKernelGGL(k_hash_prepare<64>, dim3(blocks), dim3(256), 0, s, rot, hs.rh, hs.rt, part,
+                       (const uint4*)qk, (float2*)hs.xnorm, knorm, n_rows, qcount, p.d, half, hp,
+                       n_prep);
   if (after_prep) (void)hipEventRecord(after_prep, s);
   if (p.d == 128)
     hipLaunchKernelGGL(k_hash_mfma<128>, dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       (const uint16_t*)qk, (const float2*)hs.xnorm, hs.rh, hs.bounds,
+                       (const uint16_t*)qk, (const float2*)hs.xnorm, hs.rh, part,
                        buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);
   else
     hipLaunchKernelGGL(k_hash_mfma<64>, dim3((unsigned)grid), dim3(kThreads), lds, s,
-                       (const uint16_t*)qk, (const float2*)hs.xnorm, hs.rh, hs.bounds,
+                       (const uint16_t*)qk, (const float2*)hs.xnorm, hs.rh, part,
                        buckets, buckets_out,
                        (QA*)hs.queue_a, (uint2*)hs.queue_b, qcount, N, p.L, p.R, half, hp, ib,
                        n_tok_tiles);

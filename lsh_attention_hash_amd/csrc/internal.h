@@ -38,7 +38,8 @@ struct Problem {
 struct HashScratch {
   _Float16* rh = nullptr;     // [R, half_pad, d] fp16 rotations, transposed, zero-padded
   float* rt = nullptr;        // [R, half, d] fp32 rotations, transposed (exact re-scoring)
-  unsigned* bounds = nullptr; // [R][4] norm bounds (float bits), then 2 queue counters
+  unsigned* bounds = nullptr; // [R][column tiles] float4 partial norm maxima of the
+                              // rotation, then the counts of queues A and B
   void* queue_a = nullptr;    // [R * N] two-candidate re-score entries (16 B)
   void* queue_b = nullptr;    // [R * N] all-column re-score entries (8 B)
   void* xnorm = nullptr;      // [N] float2 bounds of |x16| and |x - x16| (x16: qk in fp16)

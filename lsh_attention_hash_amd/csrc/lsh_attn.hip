@@ -142,7 +142,7 @@ int forward_parts(const lsh::Problem& p, lsh::Workspace& w, Part* parts) {
     const int64_t hp = lsh::hash_half_pad(p);
     add(&w.hash.rh, (int64_t)p.R * hp * p.d * 2);
     add(&w.hash.rt, (int64_t)p.R * p.half() * p.d * 4);
-    add(&w.hash.bounds, (4 * (int64_t)p.R + 2) * 4);
+    add(&w.hash.bounds, (4 * (int64_t)p.R * (hp / 32) + 2) * 4);
     add(&w.hash.queue_a, rows * 16);
     add(&w.hash.queue_b, rows * 8);
     add(&w.hash.xnorm, p.n_token_heads() * 8);
