@@ -261,8 +261,9 @@ def cpu_baseline(w, inp, target_s: float = 10.0, pairs: int = 0):
     else:
         # grow the sample (the oracle runs its segments in parallel, so the
         # time is not proportional to the pairs) until it takes a third of
-        # the target or is the whole workload
-        pairs, t1 = 1, 0.0
+        # the target or is the whole workload; it starts with enough pairs
+        # for a segment per thread
+        pairs, t1 = min(all_pairs, max(1, -(-threads // w.n_rounds))), 0.0
         while True:
             nb, nh = cpu_sample(w, pairs)
             t, ref = run(nb, nh)
@@ -286,8 +287,8 @@ def cpu_baseline(w, inp, target_s: float = 10.0, pairs: int = 0):
                       f"L={w.seq_len}, all {w.n_rounds} rounds ({frac:.4f} of the workload)"
                       + (f", {repeats} times" if repeats > 1 else "")
                       + f": fp64 oracle forward in {t:.2f} s (sample grown from one (batch, "
-                      f"head) pair towards {target_s:.0f} s); OpenMP over (batch, head, round) "
-                      f"segments",
+                      f"head) pair per {w.n_rounds} threads, a segment per thread, towards "
+                      f"{target_s:.0f} s); OpenMP over (batch, head, round) segments",
             "seconds": round(t, 3), "cpu_model": _cpu_model(), "threads_available": threads}, \
         ref, (nb, nh)
 
