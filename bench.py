@@ -766,8 +766,13 @@ def main():
         except (OSError, ValueError):
             traffic = None
     rl = roofline(dominant, units, stage_avg[dominant], traffic)
-    if variants and dominant == "attend":
-        rl["kernel"] = "k_attend_var"  # the variant readings' own kernel
+    plain = w.dtype != "bf16" or w.chunk_len != 64 or w.head_dim not in (64, 128)
+    if dominant == "attend" and plain:
+        rl["kernel"] = "k_attend_simple"  # fp32 rows or other chunk lengths
+    elif dominant == "hash" and (w.dtype != "bf16" or w.head_dim not in (64, 128)):
+        rl["kernel"] = "k_hash_exact"
+    elif variants and dominant == "attend" and set(variants) & {"look_ahead", "dedup"}:
+        rl["kernel"] = "k_attend_var"  # the look-ahead and de-duplication readings' own kernel
     per_stage = {k: {"ms": round(stage_avg[k], 5)} for k in stage_avg}
     for k in per_stage:
         if stage_avg[k] > 0:
