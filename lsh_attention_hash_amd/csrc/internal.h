@@ -57,7 +57,8 @@ struct Workspace {
   void* o = nullptr;               // [seg, L + kORowPad, d] per-round outputs at original positions
                                    // (fp16, or fp32 with the fp32 flag / plain kernel)
   float* lse = nullptr;            // [seg, L]
-  uint32_t* sort_counts = nullptr; // [seg, tiles, nb] counts, then first output slots
+  uint32_t* sort_counts = nullptr; // [seg, tiles, nb] counts, then their running sums;
+                                   // [seg, nb] totals; [seg, nb] first slots
   void* qk_sorted = nullptr;       // [seg, L, d] (separate-gather mode only)
   void* v_sorted = nullptr;        // [seg, L, d]
   unsigned long long* stats = nullptr;  // [4] exact rescored, full fallback (last forward);

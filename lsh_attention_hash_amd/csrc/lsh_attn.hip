@@ -134,7 +134,7 @@ int forward_parts(const lsh::Problem& p, lsh::Workspace& w, Part* parts) {
   add(&w.perm, rows * 4);
   add(&w.o, p.nseg() * p.o_seg_rows() * p.d * (lsh::round_outputs_half(p) ? 2 : 4));
   add(&w.lse, rows * 4);
-  add(&w.sort_counts, p.nseg() * (int64_t)p.nb * p.sort_tiles() * 4);
+  add(&w.sort_counts, p.nseg() * (int64_t)p.nb * (p.sort_tiles() + 2) * 4);
   add(&w.stats, 4 * 8);
   if (lsh::attend_mfma_supported(p) || lsh::attend_variant_mfma_supported(p))
     add(&w.knorm, p.n_token_heads() * 4);

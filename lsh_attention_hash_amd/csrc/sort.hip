@@ -6,13 +6,15 @@
 // bucket id alone yields exactly the (bucket, position) order; no pass over
 // the position bits is needed.
 //
-// Three phases over tiles of kSortTile positions (one 4-wave workgroup per
+// Phases over tiles of kSortTile positions (one 4-wave workgroup per
 // tile; wave w owns the tile's positions 256w .. 256w + 255):
 //   count:   counts[seg][tile][b] = how many positions of the tile are in b
 //            (LDS atomic adds; the order of the adds does not matter);
-//   scan:    offsets[seg][tile][b] = sum of all counts of buckets < b plus the
-//            counts of bucket b in earlier tiles: the first output slot of the
-//            tile's positions in bucket b;
+//   scan:    per (segment, 256 buckets): rel[seg][tile][b] = the counts of
+//            bucket b in earlier tiles, and the bucket's total;
+//   starts:  per segment, start[seg][b] = the totals of all buckets < b. The
+//            first output slot of the tile's positions in bucket b is
+//            start + rel;
 //   scatter: each wave first counts its own positions per bucket; a prefix
 //            over the waves turns the tile offset into per-wave offsets; then
 //            every position gets slot = its wave's offset + (number of earlier
@@ -90,59 +92,89 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_count(const uint16_t* __r
   }
 }
 
-// One block per segment. Buckets are taken 1024 at a time, one per thread:
-// first the bucket's total over the tiles, then a block-wide exclusive scan
-// of the totals gives the bucket's first slot, and a second pass over the
-// tiles replaces every count with the running slot. Counts are read 16 tiles
-// at a time, all loads of a batch issued before any use.
-__global__ __launch_bounds__(1024) void k_sort_scan(uint32_t* __restrict__ counts, int nb,
-                                                    int tiles) {
+// Exclusive scan of n <= kLdsBins values of src into dst, plus carry (all
+// threads of a kSortThreads block call it); returns the sum of the n values.
+__device__ uint32_t block_exclusive_scan(const uint32_t* __restrict__ src, uint32_t* dst, int n,
+                                         uint32_t carry, uint32_t* wsum) {
+  constexpr int kPer = kLdsBins / kSortThreads;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  uint32_t x[kPer];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int k = tid * kPer + u;
+    x[u] = k < n ? src[k] : 0u;
+    sum += x[u];
+  }
+  uint32_t inc = sum;  // inclusive scan of the thread sums over the wave
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  uint32_t before = carry, total = carry;
+  for (int ww = 0; ww < kSortWaves; ++ww) {
+    if (ww < w) before += wsum[ww];
+    total += wsum[ww];
+  }
+  uint32_t run = before + inc - sum;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int k = tid * kPer + u;
+    if (k < n) dst[k] = run;
+    run += x[u];
+  }
+  __syncthreads();
+  return total - carry;
+}
+
+// One block per (segment, 256 buckets), a thread per bucket: the running
+// count of the bucket over the tiles replaces each tile's count, all loads of
+// a batch of 16 tiles issued before any use, and the bucket's total goes to
+// totals[seg][b].
+__global__ __launch_bounds__(kSortThreads) void k_sort_scan(uint32_t* __restrict__ counts,
+                                                            uint32_t* __restrict__ totals, int nb,
+                                                            int tiles, int bblocks) {
   constexpr int kBatch = 16;
-  __shared__ uint32_t part[1024];
-  const int tid = threadIdx.x;
-  uint32_t* c = counts + (int64_t)blockIdx.x * nb * tiles;
+  const int64_t seg = blockIdx.x / (unsigned)bblocks;
+  const int b = (int)(blockIdx.x - seg * bblocks) * kSortThreads + threadIdx.x;
+  if (b >= nb) return;
+  uint32_t* c = counts + seg * nb * (int64_t)tiles + b;
+  uint32_t run = 0;
+  for (int t0 = 0; t0 < tiles; t0 += kBatch) {
+    uint32_t x[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb] : 0u;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (t0 + u < tiles) c[(int64_t)(t0 + u) * nb] = run;
+      run += x[u];
+    }
+  }
+  totals[seg * nb + b] = run;
+}
+
+// One block per segment: the exclusive scan of the bucket totals gives every
+// bucket's first slot, start[seg][b].
+__global__ __launch_bounds__(kSortThreads) void k_sort_starts(const uint32_t* __restrict__ totals,
+                                                              uint32_t* __restrict__ start,
+                                                              int nb) {
+  __shared__ uint32_t wsum[kSortWaves];
+  const int64_t seg = blockIdx.x;
   uint32_t carry = 0;
-  for (int b0 = 0; b0 < nb; b0 += 1024) {
-    const int b = b0 + tid;
-    uint32_t total = 0;
-    if (b < nb) {
-      for (int t0 = 0; t0 < tiles; t0 += kBatch) {
-        uint32_t x[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb + b] : 0u;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) total += x[u];
-      }
-    }
-    part[tid] = total;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const uint32_t add = tid >= off ? part[tid - off] : 0u;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
-    }
-    uint32_t run = carry + part[tid] - total;  // exclusive
-    if (b < nb) {
-      for (int t0 = 0; t0 < tiles; t0 += kBatch) {
-        uint32_t x[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) x[u] = t0 + u < tiles ? c[(int64_t)(t0 + u) * nb + b] : 0u;
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (t0 + u < tiles) c[(int64_t)(t0 + u) * nb + b] = run;
-          run += x[u];
-        }
-      }
-    }
-    carry += part[1023];
-    __syncthreads();
+  for (int base = 0; base < nb; base += kLdsBins) {
+    const int span = min(kLdsBins, nb - base);
+    carry += block_exclusive_scan(totals + seg * nb + base, start + seg * nb + base, span, carry,
+                                  wsum);
   }
 }
 
 __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
     const uint16_t* __restrict__ buckets, const uint32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int L, int nb, int tiles, int nbits, int64_t nseg) {
+    const uint32_t* __restrict__ start, int32_t* __restrict__ perm, int L, int nb, int tiles,
+    int nbits, int64_t nseg) {
   extern __shared__ uint32_t next[];  // [wave][window]
   int64_t seg;
   int tile;
@@ -169,7 +201,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
         atomicAdd(&mine[b[k] - base], 1u);
     __syncthreads();
     for (int j = tid; j < span; j += kSortThreads) {
-      uint32_t run = os[base + j];
+      uint32_t run = start[seg * nb + base + j] + os[base + j];
 #pragma unroll
       for (int ww = 0; ww < kSortWaves; ++ww) {
         const uint32_t n = next[ww * span + j];
@@ -198,17 +230,24 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
 
 hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,
                        int32_t* perm, hipStream_t s) {
+  // counts: [seg][tiles][nb] tile counts (then their running sums), then the
+  // totals and the first slots [seg][nb] of every bucket
   const int tiles = p.sort_tiles();
+  uint32_t* totals = counts + p.nseg() * (int64_t)tiles * p.nb;
+  uint32_t* start = totals + p.nseg() * (int64_t)p.nb;
   int nbits = 0;
   while ((1 << nbits) < p.nb) ++nbits;
   const dim3 grid((unsigned)(tiles * p.nseg()));
   const size_t window = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins);
   hipLaunchKernelGGL(k_sort_count, grid, dim3(kSortThreads), window * 4, s, buckets, counts, p.L,
                      p.nb, tiles, p.nseg());
-  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)p.nseg()), dim3(1024), 0, s, counts, p.nb,
-                     tiles);
+  const int bblocks = (p.nb + kSortThreads - 1) / kSortThreads;
+  hipLaunchKernelGGL(k_sort_scan, dim3((unsigned)(p.nseg() * bblocks)), dim3(kSortThreads), 0, s,
+                     counts, totals, p.nb, tiles, bblocks);
+  hipLaunchKernelGGL(k_sort_starts, dim3((unsigned)p.nseg()), dim3(kSortThreads), 0, s, totals,
+                     start, p.nb);
   hipLaunchKernelGGL(k_sort_scatter, grid, dim3(kSortThreads), kSortWaves * window * 4, s,
-                     buckets, counts, perm, p.L, p.nb, tiles, nbits, p.nseg());
+                     buckets, counts, start, perm, p.L, p.nb, tiles, nbits, p.nseg());
   return hipGetLastError();
 }
 
