@@ -12,11 +12,11 @@
 // Per chunk two launches: the first layer writes the chunk's hidden rows
 // (bias and ReLU in the epilogue, rounded to the layer dtype) into the
 // handle's buffer of chunk_rows x d_ff, and the second layer reads them back
-// (bias and residual in its epilogue). Both use the tile of gemm_core.h with K
-// slabs of 32 on matrix cores for bf16 with d_model and d_ff multiples of
-// 128: 256 x 256 tiles of 8 waves (one workgroup per CU) for layers whose
-// output width is a multiple of 256, else 256 x 128 tiles of 4 waves (two
-// workgroups per CU);
+// (bias and residual in its epilogue). Both use the tiles of gemm_core.h with
+// K slabs of 32 on matrix cores for bf16 with d_model and d_ff multiples of
+// 128: 256 x 256 tiles of 8 waves in two alternating groups (tile_pp, one
+// workgroup per CU) for layers whose output width is a multiple of 256, else
+// 256 x 128 tiles of 4 waves (two workgroups per CU);
 // other shapes and fp32 use a plain kernel (one thread per output element).
 // A row's result does not depend on the chunk it falls in: every output
 // element is summed over K in the same order in any tile.
@@ -56,7 +56,8 @@ struct FLds {
   static constexpr int kThr = Tile::kThr;
   static constexpr int kOutStride = BN * 4 + 16;  // epilogue slice row (fp32, +pad)
   static constexpr int kSlice = kBM / C::WM * kOutStride;  // one wave row's slice
-  static constexpr int kBytes = Tile::kBytes > kSlice ? Tile::kBytes : kSlice;
+  static constexpr int kTileBytes = BN == 256 ? gemm::LayPP::kBytes : Tile::kBytes;
+  static constexpr int kBytes = kTileBytes > kSlice ? kTileBytes : kSlice;
 };
 
 // out[M, N] = epilogue(a[M, K] b[N, K]^T + bias[N]); UP: ReLU, else + resid
@@ -88,7 +89,10 @@ __global__ __launch_bounds__(FLds<BN>::kThr, FCfg<BN>::kPerCU) void k_ffn_mfma(
 
   constexpr int RT = Tile::RT, CT = Tile::CT;
   floatx4_t acc[RT][CT];
-  gemm::tile<kBM, BN, kKSlab, C::WM, C::WN>(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
+  if constexpr (BN == 256)
+    gemm::tile_pp(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
+  else
+    gemm::tile<kBM, BN, kKSlab, C::WM, C::WN>(lds, a, row0, M, b + (int64_t)n0 * (K / 8), K, acc);
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
   const int wc = gemm::wave_col<BN, C::WN>(w);
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(256) void k_ffn_simple(const T* __restrict__ a,
 }
 
 bool ffn_mfma_supported(int dtype, int d_model, int d_ff) {
-  return dtype == LSH_ATTN_BF16 && d_model % 128 == 0 && d_ff % 128 == 0;
+  return dtype == LSH_ATTN_BF16 && d_model % 128 == 0 && d_ff % 128 == 0 && d_model <= (1 << 20) &&
+         d_ff <= (1 << 20);
 }
 
 template <bool UP, int BN>

@@ -2,15 +2,20 @@
 // A [M, K] and B [N, K] bf16 row-major (K contiguous; B is a linear layer's
 // weight), fp32 accumulators, v_mfma_f32_16x16x32_bf16.
 //
-// A workgroup of WM x WN waves (4 by default), each owning a block of BM/WM
-// rows x BN/WN columns. K goes
-// in slabs of SLAB (32 or 64), double-buffered in LDS (rows of A and of B, K
-// contiguous, +16-byte pad: the 16 lanes of a fragment read distinct bank
-// groups), with the next two slabs in flight in two named register sets while
-// the current one is multiplied. Loads are branch-free: rows of A past M read
-// row M - 1 (the caller does not store them). Every output element is summed
-// over K in ascending 32-wide steps whatever the tile shape or slab, so the
-// shapes give identical results.
+// tile(): a workgroup of WM x WN waves (4 by default), each owning a block of
+// BM/WM rows x BN/WN columns. K goes in slabs of SLAB (32 or 64),
+// double-buffered in LDS (rows of A and of B, K contiguous, +16-byte pad: the
+// 16 lanes of a fragment read distinct bank groups), with the next two slabs
+// in flight in two named register sets while the current one is multiplied.
+// tile_pp(): 256 x 256 on 8 waves in two groups that take turns at the matrix
+// pipe (below).
+// Loads are buffer loads through resources in scalar registers, each piece at
+// a fixed 32-bit offset (so 256 K * 2 bytes must stay below 2^31), and every
+// load and store is unconditional: rows of A past M read row M - 1 (the caller
+// does not store them), slabs past the end re-read the last one. (A load or
+// store behind a branch makes the compiler drain every load in flight after
+// the branch.) Every output element is summed over K in ascending 32-wide
+// steps whatever the tile shape or slab, so all shapes give identical results.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,38 +65,43 @@ __device__ __forceinline__ void tile(unsigned char* lds, const uint4* __restrict
   const int t = threadIdx.x;
   const int kseg = K / 8;  // 16-byte pieces per row
   const int nslab = K / SLAB;
-  // two slabs in flight in registers (slab j in set j % 2); rows past M
-  // read row M - 1 (their results are not stored), so no load is conditional
-  uint4 ra0[kAPer], rb0[kBPer], ra1[kAPer], rb1[kBPer];
-  int64_t arow[kAPer];
+  // two slabs in flight in registers (slab j in set j % 2). The loads are
+  // buffer loads through two resources held in scalar registers (the tile's
+  // rows of A, the BN rows of B), each piece at a fixed 32-bit offset plus the
+  // slab's; rows of A past M read row M - 1 (their results are not stored),
+  // so no load is conditional.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t arows = (M - row0 < BM ? M - row0 : BM);  // rows of A this tile reads
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a + row0 * kseg), (short)0, (int)(arows * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)brows, (short)0, BN * K * 2, 0x00020000);
+  u32x4 ra0[kAPer], rb0[kBPer], ra1[kAPer], rb1[kBPer];
+  int aoff[kAPer], boff[kBPer];
 #pragma unroll
   for (int j = 0; j < kAPer; ++j) {
-    const int64_t row = row0 + t / kP + (kThreads / kP) * j;
-    arow[j] = (row < M ? row : M - 1) * kseg + t % kP;
+    const int r = t / kP + (kThreads / kP) * j;
+    aoff[j] = ((r < arows ? r : (int)arows - 1) * kseg + t % kP) * 16;
   }
-  const uint4* bbase = brows + (int64_t)(t / kP) * kseg + t % kP;
-  auto load = [&](uint4 (&ra)[kAPer], uint4 (&rb)[kBPer], int s) {
 #pragma unroll
-    for (int j = 0; j < kAPer; ++j) ra[j] = a[arow[j] + s * kP];
+  for (int j = 0; j < kBPer; ++j) boff[j] = ((t / kP + (kThreads / kP) * j) * kseg + t % kP) * 16;
+  auto load = [&](u32x4 (&ra)[kAPer], u32x4 (&rb)[kBPer], int s) {
+    const int so = s * SLAB * 2;
 #pragma unroll
-    for (int j = 0; j < kBPer; ++j) rb[j] = bbase[(int64_t)(kThreads / kP) * j * kseg + s * kP];
+    for (int j = 0; j < kAPer; ++j) ra[j] = __builtin_amdgcn_raw_buffer_load_b128(ares, aoff[j] + so, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kBPer; ++j) rb[j] = __builtin_amdgcn_raw_buffer_load_b128(bres, boff[j] + so, 0, 0);
   };
-  // (each piece passes through a register-only asm statement, so the copy
-  // cannot become a memcpy from a stack copy of the registers)
-  auto store = [&](const uint4 (&ra)[kAPer], const uint4 (&rb)[kBPer], int buf) {
+  auto store = [&](const u32x4 (&ra)[kAPer], const u32x4 (&rb)[kBPer], int buf) {
 #pragma unroll
     for (int j = 0; j < kAPer; ++j) {
       const int r = t / kP + (kThreads / kP) * j, pc = t % kP;
-      uint4 q = ra[j];
-      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-      *(uint4*)(lds + L::kA + (buf * BM + r) * kStride + pc * 16) = q;
+      *(u32x4*)(lds + L::kA + (buf * BM + r) * kStride + pc * 16) = ra[j];
     }
 #pragma unroll
     for (int j = 0; j < kBPer; ++j) {
       const int c = t / kP + (kThreads / kP) * j, pc = t % kP;
-      uint4 q = rb[j];
-      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
-      *(uint4*)(lds + L::kB + (buf * BN + c) * kStride + pc * 16) = q;
+      *(u32x4*)(lds + L::kB + (buf * BN + c) * kStride + pc * 16) = rb[j];
     }
   };
 
@@ -126,25 +136,137 @@ __device__ __forceinline__ void tile(unsigned char* lds, const uint4* __restrict
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // (the stores of the clamped slabs past the end land in a buffer no wave
+  // reads again)
+  const int last = nslab - 1;
   load(ra0, rb0, 0);
   store(ra0, rb0, 0);
-  if (1 < nslab) load(ra1, rb1, 1);
-  if (2 < nslab) load(ra0, rb0, 2);
+  load(ra1, rb1, min(1, last));
+  load(ra0, rb0, min(2, last));
   __syncthreads();
   // step s: multiply slab s (LDS buffer s % 2), stage slab s + 1 from its
   // registers, then reuse them for slab s + 3
   for (int s = 0; s < nslab; s += 2) {
     compute(0);
-    if (s + 1 < nslab) store(ra1, rb1, 1);
+    store(ra1, rb1, 1);
     __syncthreads();
-    if (s + 3 < nslab) load(ra1, rb1, s + 3);
-    if (s + 1 < nslab) {
-      compute(1);
-      if (s + 2 < nslab) store(ra0, rb0, 0);
-      __syncthreads();
-      if (s + 4 < nslab) load(ra0, rb0, s + 4);
-    }
+    load(ra1, rb1, min(s + 3, last));
+    if (s + 1 < nslab) compute(1);
+    store(ra0, rb0, 0);
+    __syncthreads();
+    load(ra0, rb0, min(s + 4, last));
   }
+}
+
+// The same product for BM = BN = 256 on 8 waves (a 4 x 2 wave grid, each wave
+// 64 rows x 128 columns, the accumulator layout of tile<256, 256, 32, 4, 2>),
+// with the waves in two groups that alternate: waves 0-3 (one per SIMD) stage
+// the slabs of A, waves 4-7 those of B, and while one group multiplies the
+// slab whose operands it holds in registers, the other reads its operands of
+// the same slab from LDS, stages its half of the next slab and issues the
+// loads of a later one. Every phase ends with a barrier and group 1 runs one
+// phase behind group 0, so each SIMD always has one wave issuing products.
+// LDS: two stages of 256 rows of A and of B (K slabs of 32, +16-byte pad);
+// each group's half of slab j + 1 is staged during its phase of slab j, and
+// its loads of slab j + 3 go into the register set just staged. K must be a
+// multiple of 64. Sums are taken in the same order as tile(): identical
+// results.
+struct LayPP {
+  static constexpr int kThr = 512;
+  static constexpr int kStride = 32 * 2 + 16;
+  static constexpr int kHalf = 256 * kStride;       // one stage of A (or B)
+  static constexpr int kBytes = 4 * kHalf;          // [stage][A | B]
+  static constexpr int RT = 4, CT = 8;
+};
+
+__device__ __forceinline__ void tile_pp(unsigned char* lds, const uint4* __restrict__ a,
+                                        int64_t row0, int64_t M, const uint4* __restrict__ brows,
+                                        int K, floatx4_t (&acc)[4][8]) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kStride = LayPP::kStride;
+  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const bool gb = w >= 4;  // group 1: stages B
+  const int tt = t & 255;
+  const int kseg = K / 8;
+  const int nslab = K / 32;
+  const int last = nslab - 1;
+  const int64_t arows = (M - row0 < 256 ? M - row0 : 256);
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a + row0 * kseg), (short)0, (int)(arows * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t bres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)brows, (short)0, 256 * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t res = gb ? bres : ares;
+  const int nrows = gb ? 256 : (int)arows;
+  // this thread's 4 pieces of its group's half-slab: rows tt/4 + 64j, piece tt%4
+  int off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = tt / 4 + 64 * j;
+    off[j] = ((r < nrows ? r : nrows - 1) * kseg + tt % 4) * 16;
+  }
+  unsigned char* const sbase = lds + (gb ? LayPP::kHalf : 0) + (tt / 4) * kStride + (tt % 4) * 16;
+  u32x4 r0[4], r1[4];
+  auto load = [&](u32x4 (&r)[4], int s) {
+    const int so = s * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(res, off[j] + so, 0, 0);
+  };
+  auto store = [&](const u32x4 (&r)[4], int stage) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *(u32x4*)(sbase + stage * 2 * LayPP::kHalf + 64 * j * kStride) = r[j];
+  };
+  const int lane = t & 63, g = lane >> 4, lq = lane & 15;
+  const int wr = 64 * (w / 2), wc = 128 * (w % 2);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[i][ct] = floatx4_t{};
+  bf16x8_t fa[4], fb[8];
+  auto read = [&](int stage) {
+    const unsigned char* sa = lds + stage * 2 * LayPP::kHalf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[i] = *(const bf16x8_t*)(sa + (wr + 16 * i + lq) * kStride + 16 * g);
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      fb[ct] = *(const bf16x8_t*)(sa + LayPP::kHalf + (wc + 16 * ct + lq) * kStride + 16 * g);
+  };
+  auto compute = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+        acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[ct], acc[i][ct], 0, 0, 0);
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  load(r0, 0);
+  store(r0, 0);
+  load(r1, min(1, last));
+  load(r0, min(2, last));
+  sync();
+  if (gb) sync();  // group 1 runs one phase behind
+  for (int s = 0; s < nslab; s += 2) {
+    read(0);
+    store(r1, 1);
+    load(r1, min(s + 3, last));
+    sync();
+    compute();
+    sync();
+    read(1);
+    store(r0, 0);
+    load(r0, min(s + 4, last));
+    sync();
+    compute();
+    sync();
+  }
+  if (!gb) sync();
 }
 
 }  // namespace gemm

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void k_proj_simple(const T* __restrict__ x,
 
 bool project_mfma_supported(const Problem& p, int model_dim) {
   return p.dtype == LSH_ATTN_BF16 && (p.d == 64 || p.d == 128) && model_dim % kSlab == 0 &&
-         hash_mfma_supported(p);
+         model_dim <= (1 << 20) && hash_mfma_supported(p);
 }
 
 hipError_t launch_project(const Problem& p, int model_dim, const void* x, const void* w_qk,
