@@ -9,10 +9,11 @@
 // input dtype.
 //
 // Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 32): one
-// workgroup computes a 128-row x d-column tile of one head's qk or v with the
-// tile of gemm_core.h (the 2H tiles of a row tile run on one XCD, one after
-// the other, so the x tile is read from HBM once and from that XCD's L2 by
-// the others). The epilogue rounds the tile to bf16 and passes it through LDS so that each
+// workgroup computes a 256-row x d-column tile of one head's qk or v with the
+// tile of gemm_core.h, or, for d = 128 with an even head count and model_dim
+// a multiple of 64, a 256-row tile of two heads with the two-group tile (the
+// tiles of a row tile run on one XCD, one after the other, so the x tile is
+// read from HBM once and from that XCD's L2 by the others). The epilogue rounds the tile to bf16 and passes it through LDS so that each
 // lane writes 16 contiguous bytes of a row. For qk tiles the same pass produces
 // what the hash's pre-pass would compute from these rows (the norm bounds of
 // the rows' fp16 form and of its conversion error, and the squared norm),
@@ -106,6 +107,87 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
   }
 }
 
+// d = 128 with an even head count and model_dim a multiple of 64: a
+// 256-row x 256-column tile (heads 2p and 2p + 1 of qk or of v) on the
+// two-group tile of gemm_core.h; its wave column w % 2 holds head 2p + w % 2.
+// The epilogue takes one head at a time through LDS, with the same per-row
+// arithmetic as k_proj_mfma.
+constexpr int kPPOutStride = 128 * 2 + 16;
+constexpr int kPPBytes =
+    gemm::LayPP::kBytes > kRows * kPPOutStride ? gemm::LayPP::kBytes : kRows * kPPOutStride;
+
+__global__ __launch_bounds__(gemm::LayPP::kThr, 1) void k_proj_pp(
+    const uint4* __restrict__ x, const uint4* __restrict__ w_qk, const uint4* __restrict__ w_v,
+    uint4* __restrict__ qk, uint4* __restrict__ v,
+    float2* __restrict__ xnorm, float* __restrict__ knorm, int64_t M, int L, int H,
+    int model_dim) {
+  constexpr int D = 128;
+  constexpr int kThr = gemm::LayPP::kThr;
+  extern __shared__ __align__(16) unsigned char lds[];
+  // the H tiles of a row tile (H/2 head pairs of qk, then of v) get ids of
+  // one residue mod 8, consecutive within their XCD
+  const unsigned nts = H;
+  const unsigned xcd = blockIdx.x % 8u, k = blockIdx.x / 8u;
+  const int nt = (int)(k % nts);
+  const int64_t mt = (int64_t)(k / nts) * 8 + xcd;
+  const int64_t row0 = mt * kRows;
+  if (row0 >= M) return;
+  const bool is_v = nt >= H / 2;
+  const int h0 = 2 * (is_v ? nt - H / 2 : nt);
+  const uint4* wrows = (is_v ? w_v : w_qk) + (int64_t)h0 * D * (model_dim / 8);
+  const int t = threadIdx.x;
+
+  floatx4_t acc[4][8];
+  gemm::tile_pp(lds, x, row0, M, wrows, model_dim, acc);
+  const int lane = t & 63, w = t >> 6, g = lane >> 4, lq = lane & 15;
+  const int wr = 64 * (w / 2), hh = w % 2;
+
+  unsigned char* ot = lds;
+  constexpr int kLpr = D / 8;  // lanes per row (16 bytes each)
+  constexpr int kRowsPerPass = kThr / kLpr;
+  const int sub = t % kLpr;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    // head h0 + pass: the waves of that column put it in LDS as bf16 rows
+    if (hh == pass) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            *(uint16_t*)(ot + (wr + 16 * i + 4 * g + u) * kPPOutStride + (16 * ct + lq) * 2) =
+                f32_to_bf16(acc[i][ct][u]).bits;
+    }
+    __syncthreads();
+    const int h = h0 + pass;
+#pragma unroll 2
+    for (int r0 = 0; r0 < kRows; r0 += kRowsPerPass) {
+      const int r = r0 + t / kLpr;
+      const int64_t row = row0 + r;  // a row of x: (b, i)
+      const bool live = row < M;
+      const int64_t b = row / L, i = row - b * L;
+      const int64_t th = (b * H + h) * L + i;  // its token-head row
+      const uint4 raw = *(const uint4*)(ot + r * kPPOutStride + sub * 16);
+      if (live) (is_v ? v : qk)[th * kLpr + sub] = raw;
+      if (!is_v) {  // the hash pre-pass of this row (all lanes of a row are live together)
+        float bb = 0.f, c = 0.f;
+        hx::x16_piece(raw, bb, c);
+#pragma unroll
+        for (int off = 1; off < kLpr; off <<= 1) {
+          c += __shfl_xor(c, off);
+          bb += __shfl_xor(bb, off);
+        }
+        if (live && sub == 0) {
+          knorm[th] = c;
+          xnorm[th] = hx::norm_bounds(c, bb);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // fp32 or other shapes: one thread per output element, fp32 sums in k order
 template <typename T>
 __global__ __launch_bounds__(256) void k_proj_simple(const T* __restrict__ x,
@@ -147,7 +229,15 @@ hipError_t launch_project(const Problem& p, int model_dim, const void* x, const 
     // workgroups return at once
     const int64_t mts = (M + kRows - 1) / kRows;
     const unsigned grid = (unsigned)(((mts + 7) / 8) * 8 * 2 * p.H);
-    if (p.d == 128) {
+    if (p.d == 128 && p.H % 2 == 0 && model_dim % 64 == 0) {
+      const unsigned grid_pp = (unsigned)(((mts + 7) / 8) * 8 * p.H);
+      if (!hs.proj_attr)
+        (void)hipFuncSetAttribute((const void*)k_proj_pp,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, kPPBytes);
+      hipLaunchKernelGGL(k_proj_pp, dim3(grid_pp), dim3(gemm::LayPP::kThr), kPPBytes, s,
+                         (const uint4*)x, (const uint4*)w_qk, (const uint4*)w_v, (uint4*)qk,
+                         (uint4*)v, (float2*)hs.xnorm, knorm, M, p.L, p.H, model_dim);
+    } else if (p.d == 128) {
       constexpr int shmem = PLds<128>::kBytes;
       if (!hs.proj_attr)
         (void)hipFuncSetAttribute((const void*)k_proj_mfma<128>,
