@@ -71,8 +71,8 @@ enum {
   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
   /* Also allocate the workspace of lsh_attn_backward: per position and round,
    * 2 fp32 rows of head_dim on the matrix-core path (bf16, chunk_len 64, head_dim
-   * 64 or 128) or 4 on the other shapes, plus 12 bytes; 4 bytes per position.
-   * Not with the variant flags below (UNSUPPORTED). */
+   * 64 or 128, no variant flag) or 4 on the other shapes and with the variant
+   * flags, plus 12 bytes; 4 bytes per position. */
   LSH_ATTN_FLAG_BACKWARD = 4,
   /* Variant readings of the window and the combination, each one the pages
    * also describe (the default, all off, is the previous chunk and the chunk
@@ -186,11 +186,32 @@ int lsh_attn_forward_x(lsh_attn_t handle, const void* x, int32_t model_dim, cons
  * device (same stream). Performs no allocation and no host/device
  * synchronisation. Deterministic: every output element is written once.
  * Errors: INVALID_ARG for a null handle or pointer, a misaligned pointer or a
- * current device other than the handle's; UNSUPPORTED if the handle was
- * created without LSH_ATTN_FLAG_BACKWARD; HIP when a launch fails.
+ * current device other than the handle's, or LSH_ATTN_FLAG_SAME_BUCKET (which
+ * needs the forward's bucket ids: lsh_attn_backward_buckets); UNSUPPORTED if
+ * the handle was created without LSH_ATTN_FLAG_BACKWARD; HIP when a launch
+ * fails.
  */
 int lsh_attn_backward(lsh_attn_t handle, const void* qk, const void* v, const int32_t* perm,
                       const void* dout, void* dqk, void* dv, void* stream);
+
+/*
+ * The same backward for handles created with the variant flags: the window
+ * and the logits are those of the forward's reading (look-ahead chunk,
+ * same-bucket mask, unit queries, de-duplicated rounds; Reformer overview at
+ * www.dtcms.com/a/488796.html, section 2.1, and www.2kiu.com/news/5253576/,
+ * section 2.2). With LSH_ATTN_FLAG_NORM_QUERIES the unit query q / |q| takes
+ * the same normalisation Jacobian as the unit key of that row. The variant
+ * readings run on the plain kernels (fp32 per-round rows).
+ *   buckets   [B, H, n_rounds, L]   int32  (read only): the forward's buckets
+ *             output; required with LSH_ATTN_FLAG_SAME_BUCKET (INVALID_ARG if
+ *             null then), may be null otherwise
+ * Other arguments, workspace and errors as for lsh_attn_backward, which is
+ * this call with buckets null. Uses the handle's bucket-id buffer and, with
+ * LSH_ATTN_FLAG_DEDUP, its inverse-permutation buffer as scratch.
+ */
+int lsh_attn_backward_buckets(lsh_attn_t handle, const void* qk, const void* v,
+                              const int32_t* perm, const int32_t* buckets, const void* dout,
+                              void* dqk, void* dv, void* stream);
 
 /*
  * Counters (waits for the handle's last stream):

@@ -35,7 +35,7 @@ STATIC_SCRATCH_BYTES = 64 << 20
 
 # Every function declared in include/lsh_attn.h.
 EXPORTED_SYMBOLS = ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x",
-                    "lsh_attn_backward", "lsh_attn_forward_static",
+                    "lsh_attn_backward", "lsh_attn_backward_buckets", "lsh_attn_forward_static",
                     "lsh_attn_get_stats",
                     "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
                     "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_attn_strerror",
@@ -93,6 +93,7 @@ def load_library():
     lib.lsh_attn_forward.argtypes = [P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_forward_x.argtypes = [P, P, ctypes.c_int32, P, P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_backward.argtypes = [P, P, P, P, P, P, P, P]
+    lib.lsh_attn_backward_buckets.argtypes = [P, P, P, P, P, P, P, P, P]
     lib.lsh_attn_forward_static.argtypes = [ctypes.POINTER(Config), P, P, P, P, P, P, P, P]
     lib.lsh_attn_get_stats.argtypes = [P, ctypes.POINTER(Stats)]
     lib.lsh_attn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
@@ -113,7 +114,7 @@ def load_library():
     lib.lsh_ffn_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.lsh_ffn_destroy.argtypes = [P]
     for n in ("lsh_attn_create", "lsh_attn_forward", "lsh_attn_forward_x", "lsh_attn_backward",
-              "lsh_attn_forward_static",
+              "lsh_attn_backward_buckets", "lsh_attn_forward_static",
               "lsh_attn_get_stats",
               "lsh_attn_set_timing", "lsh_attn_get_timing", "lsh_attn_get_backward_timing",
               "lsh_attn_workspace_bytes", "lsh_attn_destroy", "lsh_ffn_create",
@@ -316,15 +317,20 @@ class LSHAttention:
             return out, qk, v, {"lse": lse, "buckets": bk, "perm": pm}
         return out, qk, v
 
-    def backward(self, qk, v, perm, dout, dqk=None, dv=None, stream=None):
+    def backward(self, qk, v, perm, dout, dqk=None, dv=None, stream=None, buckets=None):
         """Gradients (dqk, dv) [B, H, L, d] (dtype) given dout = dL/dout, at the
         permutations perm [B, H, R, L] int32 returned by the forward (call it
-        with return_perm=True). Needs backward=True at construction."""
+        with return_perm=True; with the same-bucket reading also pass its
+        buckets [B, H, R, L] int32, return_buckets=True). Needs backward=True
+        at construction."""
         c = self.cfg
         shp = (c.batch, c.heads, c.seq_len, c.head_dim)
         self._check("qk", qk, shp, self.dtype)
         self._check("v", v, shp, self.dtype)
         self._check("perm", perm, (c.batch, c.heads, c.n_rounds, c.seq_len), torch.int32)
+        if buckets is not None:
+            self._check("buckets", buckets, (c.batch, c.heads, c.n_rounds, c.seq_len),
+                        torch.int32)
         self._check("dout", dout, shp, self.dtype)
         if dqk is None:
             dqk = torch.empty(shp, dtype=self.dtype, device=self.device)
@@ -337,10 +343,17 @@ class LSHAttention:
         s = (stream if stream is not None else torch.cuda.current_stream(self.device)).cuda_stream
         ptr = lambda t: ctypes.c_void_p(t.data_ptr())
         with torch.cuda.device(self.device):
-            rc = self.lib.lsh_attn_backward(self.handle, ptr(qk), ptr(v), ptr(perm), ptr(dout),
-                                            ptr(dqk), ptr(dv), ctypes.c_void_p(s))
+            if buckets is None:
+                rc = self.lib.lsh_attn_backward(self.handle, ptr(qk), ptr(v), ptr(perm),
+                                                ptr(dout), ptr(dqk), ptr(dv), ctypes.c_void_p(s))
+                name = "lsh_attn_backward"
+            else:
+                rc = self.lib.lsh_attn_backward_buckets(self.handle, ptr(qk), ptr(v), ptr(perm),
+                                                        ptr(buckets), ptr(dout), ptr(dqk),
+                                                        ptr(dv), ctypes.c_void_p(s))
+                name = "lsh_attn_backward_buckets"
         if rc != 0:
-            raise LSHAttnError(rc, "lsh_attn_backward", self.lib)
+            raise LSHAttnError(rc, name, self.lib)
         return dqk, dv
 
     def stats(self) -> dict:

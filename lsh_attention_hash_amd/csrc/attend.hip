@@ -287,6 +287,22 @@ __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int32_t* __rest
 
 }  // namespace
 
+hipError_t launch_attend_plain(const Problem& p, const void* qk, const void* v,
+                               const int32_t* perm, const uint16_t* buckets, const int32_t* inv,
+                               float* o, float* lse, hipStream_t s) {
+  const bool bf = p.dtype == LSH_ATTN_BF16;
+  if (p.d == 64) {
+    if (bf) launch_simple<64, bf16_t>(p, qk, v, nullptr, nullptr, perm, buckets, inv, o, lse, s);
+    else launch_simple<64, float>(p, qk, v, nullptr, nullptr, perm, buckets, inv, o, lse, s);
+  } else if (p.d == 128) {
+    if (bf) launch_simple<128, bf16_t>(p, qk, v, nullptr, nullptr, perm, buckets, inv, o, lse, s);
+    else launch_simple<128, float>(p, qk, v, nullptr, nullptr, perm, buckets, inv, o, lse, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_inverse_perm(const Problem& p, const int32_t* perm, int32_t* inv, hipStream_t s) {
   const int64_t n = p.n_rows();
   hipLaunchKernelGGL(k_inverse_perm, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, perm,

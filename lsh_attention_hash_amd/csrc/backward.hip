@@ -18,10 +18,17 @@
 // w_r(i) dout(i) to v_i. Key normalisation khat = k / |k| (0 for k = 0):
 //   dk_j = (dkhat_j - khat_j (khat_j . dkhat_j)) / |k_j|,  dqk = dq + dk.
 //
-// On the matrix-core path (bf16, chunk_len 64, d in {64, 128}) the dq and
-// (dkhat, dv) products run in one kernel of backward_mfma.hip instead of the
-// two below; it also applies the normalisation per round, so its reduction
-// (k_bwd_reduce_sum) only sums.
+// On the matrix-core path (bf16, chunk_len 64, d in {64, 128}, the default
+// reading) the dq and (dkhat, dv) products run in one kernel of
+// backward_mfma.hip instead of the two below; it also applies the
+// normalisation per round, so its reduction (k_bwd_reduce_sum) only sums.
+// The variant readings take the plain kernels below: the window and the
+// logits are those of the forward's reading (the overview, section 2.1:
+// look-ahead chunk, same-bucket mask, unit queries; de-duplicated rounds,
+// www.2kiu.com/news/5253576/, section 2.2: P divided by the number of rounds
+// sharing the pair), and with unit queries q / |q| the query's gradient is
+// taken with respect to the unit query, which goes through the same
+// normalisation Jacobian as the row's unit key.
 // Launches (one stream): the per-round attention is recomputed from the
 // forward's permutation (fp32 rows and logsumexps; on the matrix-core path only
 // the logsumexps and dout . o_r per query); per position, the round weights
@@ -158,8 +165,29 @@ __global__ __launch_bounds__(256) void k_bwd_rows_dot(const float* __restrict__ 
   wself[row] = ws;
 }
 
+// DEDUP: the number of rounds whose window holds key j for query i (the self
+// and causal masks do not depend on the round); inv_bh, bk_bh: [R, L] of one
+// (b, h), bk_bh read with SAME_BUCKET.
+__device__ __forceinline__ int shared_rounds(const int32_t* inv_bh, const uint16_t* bk_bh, int L,
+                                             int m, int R, int i, int j, int flags) {
+  int n = 0;
+  for (int r = 0; r < R; ++r) {
+    const int64_t o = (int64_t)r * L;
+    const int ci = inv_bh[o + i] / m, cj = inv_bh[o + j] / m;
+    bool in = cj == ci || cj == ci - 1 || ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && cj == ci + 1);
+    if ((flags & LSH_ATTN_FLAG_SAME_BUCKET) && bk_bh[o + j] != bk_bh[o + i]) in = false;
+    n += in;
+  }
+  return n;
+}
+
 // dq of the query at slot s of segment seg (one D/8-lane row group per
-// query): the sum over its window of dS_ij khat_j / sqrt(d).
+// query): the sum over its window of dS_ij khat_j / sqrt(d). The variant
+// readings (flags) change the window and the logits as in the forward:
+// LOOK_AHEAD adds the next chunk, SAME_BUCKET drops keys of other buckets (bkt
+// [seg, L]), NORM_QUERIES takes the logit with q / |q| (and this is then the
+// gradient with respect to the unit query), DEDUP divides P by the number of
+// rounds sharing the pair (inv [seg, L]).
 template <int D, typename T, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_bwd_dq(const T* __restrict__ qk, const T* __restrict__ v,
                                                 const T* __restrict__ dout,
@@ -168,7 +196,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(const T* __restrict__ qk, const 
                                                 const float* __restrict__ w,
                                                 const float* __restrict__ cq,
                                                 float* __restrict__ dq, int L, int m, int R,
-                                                int64_t n_rows) {
+                                                int64_t n_rows, int flags,
+                                                const uint16_t* __restrict__ bkt,
+                                                const int32_t* __restrict__ inv) {
   constexpr int kLpr = D / 8;
   const int sub = threadIdx.x % kLpr;
   const int64_t slot_row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
@@ -186,11 +216,21 @@ __global__ __launch_bounds__(256) void k_bwd_dq(const T* __restrict__ qk, const 
     float q[8], dz[8];
     load8<T>(qk + (bh * L + i) * D + sub * 8, q);
     load8<T>(dout + (bh * L + i) * D + sub * 8, dz);
+    float qs = 1.f;
+    if (flags & LSH_ATTN_FLAG_NORM_QUERIES) {
+      const float qn2 = row_sum<kLpr>(dot8(q, q));
+      qs = qn2 > 0.f ? 1.0f / sqrtf(qn2) : 0.f;
+    }
+    const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+    const int bi = sb ? bkt[seg * L + i] : 0;
     const int chunk = s / m;
-    const int first = (chunk > 0 ? chunk - 1 : chunk) * m, last = (chunk + 1) * m;
+    const int first = (chunk > 0 ? chunk - 1 : chunk) * m;
+    int last = (chunk + 1) * m;
+    if ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && last < L) last += m;
     for (int t = first; t < last; ++t) {
       const int j = pm[t];
       if (j == i || (CAUSAL && j > i)) continue;
+      if (sb && bkt[seg * L + j] != bi) continue;
       float k[8], vj[8];
       load8<T>(qk + (bh * L + j) * D + sub * 8, k);
       load8<T>(v + (bh * L + j) * D + sub * 8, vj);
@@ -198,7 +238,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(const T* __restrict__ qk, const 
       const float qkd = row_sum<kLpr>(dot8(q, k));
       const float dv = row_sum<kLpr>(dot8(dz, vj));
       const float rn = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
-      const float p = __expf(qkd * rn * scale - l);
+      float p = __expf(qkd * qs * rn * scale - l);
+      if (flags & LSH_ATTN_FLAG_DEDUP)
+        p /= (float)shared_rounds(inv + bh * R * L, bkt + bh * R * L, L, m, R, i, j, flags);
       const float ds = wi * p * (dv - ci);
 #pragma unroll
       for (int u = 0; u < 8; ++u) g[u] = fmaf(ds * rn * scale, k[u], g[u]);
@@ -208,7 +250,9 @@ __global__ __launch_bounds__(256) void k_bwd_dq(const T* __restrict__ qk, const 
 }
 
 // dkhat and dv of the key at slot t of segment seg: the queries that see it
-// are those of its chunk and of the next one.
+// are those of its chunk and of the next one (and of the previous one with
+// LOOK_AHEAD); variant readings as for k_bwd_dq (with NORM_QUERIES, dkhat
+// takes the unit query).
 template <int D, typename T, bool CAUSAL>
 __global__ __launch_bounds__(256) void k_bwd_dkv(const T* __restrict__ qk, const T* __restrict__ v,
                                                  const T* __restrict__ dout,
@@ -217,7 +261,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(const T* __restrict__ qk, const
                                                  const float* __restrict__ w,
                                                  const float* __restrict__ cq,
                                                  float* __restrict__ dk, float* __restrict__ dv,
-                                                 int L, int m, int R, int64_t n_rows) {
+                                                 int L, int m, int R, int64_t n_rows, int flags,
+                                                 const uint16_t* __restrict__ bkt,
+                                                 const int32_t* __restrict__ inv) {
   constexpr int kLpr = D / 8;
   const int sub = threadIdx.x % kLpr;
   const int64_t slot_row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
@@ -233,31 +279,50 @@ __global__ __launch_bounds__(256) void k_bwd_dkv(const T* __restrict__ qk, const
   load8<T>(v + (bh * L + j) * D + sub * 8, vj);
   const float n2 = row_sum<kLpr>(dot8(k, k));
   const float rn = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
+  const bool nq = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
+  const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  const int bj = sb ? bkt[seg * L + j] : 0;
   float gk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int chunk = t / m;
-  const int first = chunk * m, last = min(L, (chunk + 2) * m);
+  const int first = ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && chunk > 0 ? chunk - 1 : chunk) * m;
+  const int last = min(L, (chunk + 2) * m);
   for (int s = first; s < last; ++s) {
     const int i = pm[s];
     if (i == j || (CAUSAL && j > i)) continue;
+    if (sb && bkt[seg * L + i] != bj) continue;
     const float l = lse[seg * L + i];
     if (l == kSelfLogit) continue;
     const float wi = w[seg * L + i], ci = cq[bh * L + i];
     float q[8], dz[8];
     load8<T>(qk + (bh * L + i) * D + sub * 8, q);
     load8<T>(dout + (bh * L + i) * D + sub * 8, dz);
+    float qs = 1.f;
+    if (nq) {
+      const float qn2 = row_sum<kLpr>(dot8(q, q));
+      qs = qn2 > 0.f ? 1.0f / sqrtf(qn2) : 0.f;
+    }
     const float qkd = row_sum<kLpr>(dot8(q, k));
     const float dvd = row_sum<kLpr>(dot8(dz, vj));
-    const float p = __expf(qkd * rn * scale - l);
+    float p = __expf(qkd * qs * rn * scale - l);
+    if (flags & LSH_ATTN_FLAG_DEDUP)
+      p /= (float)shared_rounds(inv + bh * R * L, bkt + bh * R * L, L, m, R, i, j, flags);
     const float ds = wi * p * (dvd - ci);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      gk[u] = fmaf(ds * scale, q[u], gk[u]);
+      gk[u] = fmaf(ds * scale * qs, q[u], gk[u]);
       gv[u] = fmaf(wi * p, dz[u], gv[u]);
     }
   }
   store8(dk + (seg * L + j) * D + sub * 8, gk);
   store8(dv + (seg * L + j) * D + sub * 8, gv);
+}
+
+// the forward's int32 bucket ids as the kernels' u16 ids
+__global__ void k_bwd_bucket16(const int32_t* __restrict__ b32, uint16_t* __restrict__ b16,
+                               int64_t n) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x < n) b16[x] = (uint16_t)b32[x];
 }
 
 // Sum over rounds, key normalisation, the self-only value terms; dqk and dv
@@ -271,7 +336,7 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
                                                     const float* __restrict__ dk,
                                                     const float* __restrict__ dvr,
                                                     T* __restrict__ dqk, T* __restrict__ dv,
-                                                    int L, int R, int64_t n_rows) {
+                                                    int L, int R, int64_t n_rows, bool nq) {
   constexpr int kLpr = D / 8;
   const int sub = threadIdx.x % kLpr;
   const int64_t row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
@@ -294,6 +359,13 @@ __global__ __launch_bounds__(256) void k_bwd_reduce(const T* __restrict__ qk,
       gv[u] += c[u];
     }
     if (lse[sr] == kSelfLogit) wself += w[sr];
+  }
+  if (nq) {  // dq is then the gradient of the unit query: it shares the key's Jacobian
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      gk[u] += gq[u];
+      gq[u] = 0.f;
+    }
   }
   float k[8], dz[8];
   load8<T>(qk + row * D + sub * 8, k);
@@ -400,22 +472,23 @@ __global__ __launch_bounds__(256) void k_bwd_reduce_sum(const T* __restrict__ do
 
 template <int D, typename T>
 void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-              const void* dout, void* dqk, void* dvo, const float* knorm, BwdWorkspace& b,
-              unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev) {
+              const void* dout, void* dqk, void* dvo, const float* knorm, const uint16_t* bk16,
+              const int32_t* inv, BwdWorkspace& b, unsigned long long* at_limit, hipStream_t s,
+              const hipEvent_t* ev) {
   auto mark = [&](int j) {
     if (ev) (void)hipEventRecord(ev[j], s);
   };
   const int64_t rpb = 256 / (D / 8);
   const int64_t nt = p.n_token_heads(), nr = p.n_rows();
   const dim3 gt((unsigned)((nt + rpb - 1) / rpb)), gr((unsigned)((nr + rpb - 1) / rpb));
-  if (attend_mfma_supported(p))
+  if (bwd_mfma_supported(p))
     hipLaunchKernelGGL(k_bwd_rows_dot, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, b.od,
                        b.lse, b.w, b.cq, b.wself, p.L, p.R, nt);
   else
     hipLaunchKernelGGL((k_bwd_rows<D, T>), gt, dim3(256), 0, s, b.o32, b.lse, (const T*)v,
                        (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
   mark(2);
-  if (attend_mfma_supported(p)) {
+  if (bwd_mfma_supported(p)) {
     (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
     mark(3);
     const bool half = bwd_rows_half(p);
@@ -443,48 +516,61 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
     mark(4);
     return;
   }
+  const int vf = p.flags & kVariantFlags;
   if (p.causal) {
     hipLaunchKernelGGL((k_bwd_dq<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
+                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr, vf, bk16,
+                       inv);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr);
+                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr, vf,
+                       bk16, inv);
   } else {
     hipLaunchKernelGGL((k_bwd_dq<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr);
+                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr, vf, bk16,
+                       inv);
     hipLaunchKernelGGL((k_bwd_dkv<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr);
+                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr, vf,
+                       bk16, inv);
   }
   mark(3);
   hipLaunchKernelGGL((k_bwd_reduce<D, T>), gt, dim3(256), 0, s, (const T*)qk, (const T*)dout,
-                     b.lse, b.w, b.dq, b.dk, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt);
+                     b.lse, b.w, b.dq, b.dk, b.dv, (T*)dqk, (T*)dvo, p.L, p.R, nt,
+                     (p.flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0);
   mark(4);
 }
 
 }  // namespace
 
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-                           const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
+                           const int32_t* buckets, const void* dout, void* dqk, void* dv,
+                           float* knorm, uint16_t* bk16, int32_t* inv, BwdWorkspace& b,
                            unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev) {
-  // the per-round attention, recomputed from the permutation in fp32
-  hipError_t e;
+  // the per-round attention, recomputed from the permutation
+  hipError_t e = hipSuccess;
   if (ev) (void)hipEventRecord(ev[0], s);
-  if (attend_mfma_supported(p)) {
+  if (bwd_mfma_supported(p)) {
     e = launch_key_norms(p, qk, knorm, s);
     if (e == hipSuccess)
       e = launch_attend_mfma_dot(p, qk, v, perm, knorm, dout, b.od, b.lse, s);
   } else {
-    e = launch_attend(p, qk, v, nullptr, nullptr, perm, nullptr, nullptr, nullptr, b.o32, b.lse,
-                      s);
+    // fp32 rows from the plain kernel, which takes every variant reading
+    if (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) {
+      const int64_t n = p.n_rows();
+      hipLaunchKernelGGL(k_bwd_bucket16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                         buckets, bk16, n);
+    }
+    if (p.flags & LSH_ATTN_FLAG_DEDUP) e = launch_inverse_perm(p, perm, inv, s);
+    if (e == hipSuccess) e = launch_attend_plain(p, qk, v, perm, bk16, inv, b.o32, b.lse, s);
   }
   if (e != hipSuccess) return e;
   if (ev) (void)hipEventRecord(ev[1], s);
   const bool bf = p.dtype == LSH_ATTN_BF16;
   if (p.d == 64) {
-    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
-    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
+    if (bf) launch_t<64, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, bk16, inv, b, at_limit, s, ev);
+    else launch_t<64, float>(p, qk, v, perm, dout, dqk, dv, knorm, bk16, inv, b, at_limit, s, ev);
   } else {
-    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
-    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, b, at_limit, s, ev);
+    if (bf) launch_t<128, bf16_t>(p, qk, v, perm, dout, dqk, dv, knorm, bk16, inv, b, at_limit, s, ev);
+    else launch_t<128, float>(p, qk, v, perm, dout, dqk, dv, knorm, bk16, inv, b, at_limit, s, ev);
   }
   return hipGetLastError();
 }

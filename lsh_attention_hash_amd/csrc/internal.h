@@ -128,6 +128,12 @@ hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const vo
                                       float* lse, hipStream_t s);
 // inv[seg, perm[seg, s]] = s
 hipError_t launch_inverse_perm(const Problem& p, const int32_t* perm, int32_t* inv, hipStream_t s);
+// the plain chunk attention (any shape, every variant reading) with fp32
+// per-round rows o [seg, o_seg_rows, d] and lse [seg, L]; buckets [seg, L]
+// read with SAME_BUCKET, inv with DEDUP
+hipError_t launch_attend_plain(const Problem& p, const void* qk, const void* v,
+                               const int32_t* perm, const uint16_t* buckets, const int32_t* inv,
+                               float* o, float* lse, hipStream_t s);
 // bf16, chunk_len 64, d in {64, 128}: the default reading, and the unit-query
 // and same-bucket readings with the gather fused
 bool attend_mfma_supported(const Problem& p);
@@ -153,9 +159,13 @@ hipError_t launch_combine(const Problem& p, const void* o, bool o_half, const fl
 // gradients of qk and v given dout, at the permutations perm of a forward
 // ev (may be null): 5 events, recorded before the recomputation and after
 // each of its 4 stages (recomputation, rows, gradient products, reduction);
-// at_limit: as for launch_combine, for the fp16 per-round gradient rows
+// at_limit: as for launch_combine, for the fp16 per-round gradient rows.
+// Variant readings: buckets [seg, L] int32, the forward's bucket ids (read
+// with SAME_BUCKET, may be null otherwise), copied to bk16 [seg, L]; inv
+// [seg, L] receives the inverse permutations (DEDUP).
 hipError_t launch_backward(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-                           const void* dout, void* dqk, void* dv, float* knorm, BwdWorkspace& b,
+                           const int32_t* buckets, const void* dout, void* dqk, void* dv,
+                           float* knorm, uint16_t* bk16, int32_t* inv, BwdWorkspace& b,
                            unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev);
 
 // the per-round gradient products on matrix cores (attend_mfma_supported
@@ -192,10 +202,17 @@ inline bool round_outputs_half(const Problem& p) {
          !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
 }
 
+// The backward's products run on matrix cores for the default reading on the
+// matrix-core attention's shapes; the variant readings take the plain
+// kernels (fp32 per-round rows).
+inline bool bwd_mfma_supported(const Problem& p) {
+  return attend_mfma_supported(p) && !(p.flags & kVariantFlags);
+}
+
 // The backward's per-round gradient rows (dqk_r, dv_r) on the matrix-core path
 // are kept in fp16 under the same rule; otherwise fp32.
 inline bool bwd_rows_half(const Problem& p) {
-  return attend_mfma_supported(p) && !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
+  return bwd_mfma_supported(p) && !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
 }
 
 }  // namespace lsh

@@ -60,8 +60,6 @@ int validate(const lsh_attn_config_t* c) {
   if ((c->flags & ~(LSH_ATTN_FLAG_SEPARATE_GATHER | LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS |
                     LSH_ATTN_FLAG_BACKWARD | lsh::kVariantFlags)) != 0)
     return LSH_ATTN_ERR_INVALID_ARG;
-  if ((c->flags & LSH_ATTN_FLAG_BACKWARD) && (c->flags & lsh::kVariantFlags))
-    return LSH_ATTN_ERR_UNSUPPORTED;
   if (c->dtype != LSH_ATTN_FP32 && c->dtype != LSH_ATTN_BF16) return LSH_ATTN_ERR_UNSUPPORTED;
   if (c->out_dtype != LSH_ATTN_FP32 && c->out_dtype != LSH_ATTN_BF16)
     return LSH_ATTN_ERR_UNSUPPORTED;
@@ -196,13 +194,13 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   if (ok && lsh::hash_mfma_supported(p)) w.hash.n_cu = device_cus(h->device);
   if (ok && (p.flags & LSH_ATTN_FLAG_BACKWARD)) {
     lsh::BwdWorkspace& b = h->bw;
-    ok = (lsh::attend_mfma_supported(p) ? alloc(&b.od, rows * 4, t)
-                                        : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
+    ok = (lsh::bwd_mfma_supported(p) ? alloc(&b.od, rows * 4, t)
+                                     : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
          alloc(&b.lse, rows * 4, t) &&
          alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
          alloc(&b.wself, p.n_token_heads() * 4, t) &&
          alloc(&b.dq, rows * p.d * (lsh::bwd_rows_half(p) ? 2 : 4), t) &&
-         (lsh::attend_mfma_supported(p) || alloc(&b.dk, rows * p.d * 4, t)) &&
+         (lsh::bwd_mfma_supported(p) || alloc(&b.dk, rows * p.d * 4, t)) &&
          alloc(&b.dv, rows * p.d * (lsh::bwd_rows_half(p) ? 2 : 4), t);
   }
   if (!ok) {
@@ -329,11 +327,13 @@ int lsh_attn_forward_x(lsh_attn_t h, const void* x, int32_t model_dim, const voi
       forward_body(h->p, h->ws, qk, v, rotations, out, lse, buckets, perm, s, ev, norms_ready));
 }
 
-int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
-                      const void* dout, void* dqk, void* dv, void* stream) {
+int lsh_attn_backward_buckets(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
+                              const int32_t* buckets, const void* dout, void* dqk, void* dv,
+                              void* stream) {
   if (!h || !qk || !v || !perm || !dout || !dqk || !dv) return LSH_ATTN_ERR_INVALID_ARG;
   const lsh::Problem& p = h->p;
   if (!(p.flags & LSH_ATTN_FLAG_BACKWARD)) return LSH_ATTN_ERR_UNSUPPORTED;
+  if ((p.flags & LSH_ATTN_FLAG_SAME_BUCKET) && !buckets) return LSH_ATTN_ERR_INVALID_ARG;
   if (!aligned16(qk) || !aligned16(v) || !aligned16(dout) || !aligned16(dqk) || !aligned16(dv))
     return LSH_ATTN_ERR_INVALID_ARG;
   if (!on_device(h)) return LSH_ATTN_ERR_INVALID_ARG;
@@ -343,11 +343,16 @@ int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t
   const hipEvent_t* ev =
       timing ? &h->bevents[(size_t)h->btimed * (LSH_ATTN_N_BWD_STAGES + 1)] : nullptr;
   if (timing) ++h->btimed;
-  hipError_t e = lsh::launch_backward(p, qk, v, perm, dout, dqk, dv, h->ws.knorm, h->bw,
-                                      h->ws.stats + 3, s, ev);
+  hipError_t e = lsh::launch_backward(p, qk, v, perm, buckets, dout, dqk, dv, h->ws.knorm,
+                                      h->ws.buckets, h->ws.inv, h->bw, h->ws.stats + 3, s, ev);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess && timing) --h->btimed;  // its events were not all recorded
   return e == hipSuccess ? LSH_ATTN_OK : LSH_ATTN_ERR_HIP;
+}
+
+int lsh_attn_backward(lsh_attn_t h, const void* qk, const void* v, const int32_t* perm,
+                      const void* dout, void* dqk, void* dv, void* stream) {
+  return lsh_attn_backward_buckets(h, qk, v, perm, nullptr, dout, dqk, dv, stream);
 }
 
 int lsh_attn_get_stats(lsh_attn_t h, lsh_attn_stats_t* stats) {

@@ -95,8 +95,8 @@ def _load():
             "lsh_oracle_combine": [C, P, P, P],
             "lsh_oracle_forward": [C, P, P, P, P, P, P, P, P, P],
             "lsh_oracle_attend_rows": [C, P, P, P, P, ctypes.c_int64, P, P, P],
-            "lsh_oracle_backward": [C, P, P, P, P, P, P],
-            "lsh_oracle_backward_magnitudes": [C, P, P, P, P, P, P],
+            "lsh_oracle_backward": [C, P, P, P, P, P, P, P],
+            "lsh_oracle_backward_magnitudes": [C, P, P, P, P, P, P, P],
             "lsh_oracle_project": [C, ctypes.c_int64, P, P, P, P, P],
             "lsh_oracle_ffn": [ctypes.c_int64] * 4 + [P] * 8,
         }.items():
@@ -203,26 +203,27 @@ def attend_rows(c: Config, qk, v, perm, rows, buckets=None):
     return out, lse
 
 
-def backward(c: Config, qk, v, perm, dout):
+def backward(c: Config, qk, v, perm, dout, buckets=None):
     """Gradients (dqk, dv) [B, H, L, d] of a loss given dout = dL/dout, at the
-    permutations perm [B, H, R, L] of the forward (buckets held fixed)."""
-    qk, v, pm, do = _f64(qk), _f64(v), _i32(perm), _f64(dout)
+    permutations perm [B, H, R, L] of the forward (buckets held fixed; the
+    forward's buckets [B, H, R, L] are needed with SAME_BUCKET)."""
+    qk, v, pm, do, bk = _f64(qk), _f64(v), _i32(perm), _f64(dout), _i32(buckets)
     dqk = np.empty((c.batch, c.heads, c.seq_len, c.head_dim), np.float64)
     dv = np.empty_like(dqk)
-    _chk(_load().lsh_oracle_backward(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do), _p(dqk),
-                                     _p(dv)), "backward")
+    _chk(_load().lsh_oracle_backward(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(bk), _p(do),
+                                     _p(dqk), _p(dv)), "backward")
     return dqk, dv
 
 
-def backward_magnitudes(c: Config, qk, v, perm, dout):
+def backward_magnitudes(c: Config, qk, v, perm, dout, buckets=None):
     """(mdqk, mdv) [B, H, L, d]: sums of upper bounds of the absolute values of
     the terms of dqk and dv (|dqk| <= mdqk, |dv| <= mdv), for error bounds of
-    a finite-precision backward."""
-    qk, v, pm, do = _f64(qk), _f64(v), _i32(perm), _f64(dout)
+    a finite-precision backward (buckets as for backward)."""
+    qk, v, pm, do, bk = _f64(qk), _f64(v), _i32(perm), _f64(dout), _i32(buckets)
     mq = np.empty((c.batch, c.heads, c.seq_len, c.head_dim), np.float64)
     mv = np.empty_like(mq)
-    _chk(_load().lsh_oracle_backward_magnitudes(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(do),
-                                                _p(mq), _p(mv)), "backward_magnitudes")
+    _chk(_load().lsh_oracle_backward_magnitudes(ctypes.byref(c), _p(qk), _p(v), _p(pm), _p(bk),
+                                                _p(do), _p(mq), _p(mv)), "backward_magnitudes")
     return mq, mv
 
 

@@ -473,13 +473,21 @@ done:
  *  key normalisation (khat = k / |k|, khat := 0 for k = 0):
  *    dL/dk_j      = (dkhat_j - khat_j (khat_j . dkhat_j)) / |k_j|
  *  shared QK: dL/dqk_j = dL/dq_j + dL/dk_j.
- * perm: every round's permutation [B, H, R, L]; dout, dqk, dv: [B, H, L, d].
+ * The variant readings change only which keys are attendable and the logits,
+ * exactly as in the forward (window(), and with DEDUP s_ij lowered by the
+ * constant log N_ij), except NORM_QUERIES, where s_ij uses the unit query
+ * qhat_i = q_i / |q_i|: then dL/dqhat_i += dL/ds_ij khat_j / sqrt(d), the key
+ * term uses qhat_i, and qhat_i goes through the same normalisation Jacobian as
+ * khat_i (they are the same unit vector of qk_i).
+ * perm: every round's permutation [B, H, R, L]; buckets [B, H, R, L] (read
+ * with SAME_BUCKET, else may be NULL); dout, dqk, dv: [B, H, L, d].
  * ------------------------------------------------------------------------- */
 int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const double* v,
-                        const int32_t* perm, const double* dout, double* dqk, double* dv) {
+                        const int32_t* perm, const int32_t* buckets, const double* dout,
+                        double* dqk, double* dv) {
   int rc = lsh_oracle_check(c);
   if (rc) return rc;
-  if (c->variant != 0) return -10;
+  if ((c->variant & LSH_ORACLE_SAME_BUCKET) && !buckets) return -12;
   const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
   const int64_t nbh = (int64_t)c->batch * c->heads;
   const size_t nsl = seg_count(c) * (size_t)L;
@@ -487,8 +495,12 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
   double* lse = (double*)malloc(sizeof(double) * nsl);
   double* out = (double*)malloc(sizeof(double) * (size_t)(nbh * L * d));
   double* dkhat = (double*)calloc((size_t)(nbh * L * d), sizeof(double));
-  if (!o || !lse || !out || !dkhat) { rc = -8; goto done; }
-  rc = lsh_oracle_attend(c, qk, v, perm, NULL, o, lse);
+  int32_t* inv = (c->variant & LSH_ORACLE_DEDUP) ? inverse_perm(c, perm) : NULL;
+  if (!o || !lse || !out || !dkhat || ((c->variant & LSH_ORACLE_DEDUP) && !inv)) {
+    rc = -8;
+    goto done;
+  }
+  rc = lsh_oracle_attend(c, qk, v, perm, buckets, o, lse);
   if (rc) goto done;
   rc = lsh_oracle_combine(c, o, lse, out);
   if (rc) goto done;
@@ -498,10 +510,10 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
   {
     double* khat = (double*)malloc(sizeof(double) * (size_t)d);
     double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
-    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
-    double* pj = (double*)malloc(sizeof(double) * (size_t)(2 * m));
-    double* dp = (double*)malloc(sizeof(double) * (size_t)(2 * m));
-    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    double* pj = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(3 * m));
     double* dor = (double*)malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t bh = 0; bh < nbh; ++bh) {
@@ -530,9 +542,17 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
             g += (orow[u] - outrow[u]) * drow[u];
           }
           const double dlse = w * g;
-          /* the round's window, as in the forward */
-          const int64_t n = window(c, qk_bh, pm, NULL, s, khat, qhat, logit, key);
-          const double* q = qk_bh + i * d;
+          /* the round's window and logits, as in the forward (with
+           * NORM_QUERIES, window() leaves the unit query in qhat) */
+          const int64_t n = window(c, qk_bh, pm, buckets ? buckets + seg * L : NULL, s, khat,
+                                   qhat, logit, key);
+          if (c->variant & LSH_ORACLE_DEDUP)
+            for (int64_t a = 0; a < n; ++a)
+              logit[a] -= log((double)rounds_sharing(c, inv + bh * R * L,
+                                                     buckets ? buckets + bh * R * L : NULL, i,
+                                                     key[a]));
+          const int nq = (c->variant & LSH_ORACLE_NORM_QUERIES) != 0;
+          const double* q = nq ? qhat : qk_bh + i * d;
           const double scale = 1.0 / sqrt((double)d);
           if (n == 0) {
             for (int64_t u = 0; u < d; ++u) dv[(bh * L + i) * d + u] += dor[u];
@@ -551,15 +571,19 @@ int lsh_oracle_backward(const lsh_oracle_config* c, const double* qk, const doub
             const int64_t j = key[a];
             const double ds = pj[a] * (dp[a] - dsum) + pj[a] * dlse;
             unit_key(qk_bh + j * d, d, khat);
+            /* the query's own gradient: with NORM_QUERIES it is taken with
+             * respect to the unit query, which shares the key's Jacobian */
+            double* dqi = nq ? dkhat + (bh * L + i) * d : dqk + (bh * L + i) * d;
             for (int64_t u = 0; u < d; ++u) {
               dv[(bh * L + j) * d + u] += pj[a] * dor[u];
-              dqk[(bh * L + i) * d + u] += ds * khat[u] * scale;
+              dqi[u] += ds * khat[u] * scale;
               dkhat[(bh * L + j) * d + u] += ds * q[u] * scale;
             }
           }
         }
       }
-      /* key normalisation */
+      /* normalisation of the keys (and of the queries with NORM_QUERIES):
+       * x / |x| has the Jacobian (I - xhat xhat^T) / |x| */
       for (int64_t j = 0; j < L; ++j) {
         const double* k = qk_bh + j * d;
         double ss = 0.0;
@@ -586,6 +610,7 @@ done:
   free(lse);
   free(out);
   free(dkhat);
+  free(inv);
   return rc;
 }
 
@@ -604,14 +629,15 @@ done:
  *   mdqk   = mdq + (|mdk| + |khat| (|khat| . mdk)) / |k|   (the normalisation's
  *            Jacobian with every term taken in absolute value).
  * So |dv| <= mdv and |dqk| <= mdqk elementwise (triangle inequality), with
- * equality for dv when every dout and v entry is non-negative.
- * Default reading only (variant 0; otherwise -10). */
+ * equality for dv when every dout and v entry is non-negative. The variant
+ * readings change the windows and logits as in the forward; with
+ * NORM_QUERIES q_i is the unit query and its term goes into mdk[i]. */
 int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
-                                   const double* v, const int32_t* perm, const double* dout,
-                                   double* mdqk, double* mdv) {
+                                   const double* v, const int32_t* perm, const int32_t* buckets,
+                                   const double* dout, double* mdqk, double* mdv) {
   int rc = lsh_oracle_check(c);
   if (rc) return rc;
-  if (c->variant != 0) return -10;
+  if ((c->variant & LSH_ORACLE_SAME_BUCKET) && !buckets) return -12;
   const int64_t L = c->seq_len, d = c->head_dim, R = c->n_rounds, m = c->chunk_len;
   const int64_t nbh = (int64_t)c->batch * c->heads;
   const size_t nsl = seg_count(c) * (size_t)L;
@@ -620,8 +646,12 @@ int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
   double* out = (double*)malloc(sizeof(double) * (size_t)(nbh * L * d));
   double* mdk = (double*)calloc((size_t)(nbh * L * d), sizeof(double));
   double* eq = (double*)calloc((size_t)(nbh * L), sizeof(double));
-  if (!o || !lse || !out || !mdk || !eq) { rc = -8; goto done; }
-  rc = lsh_oracle_attend(c, qk, v, perm, NULL, o, lse);
+  int32_t* inv = (c->variant & LSH_ORACLE_DEDUP) ? inverse_perm(c, perm) : NULL;
+  if (!o || !lse || !out || !mdk || !eq || ((c->variant & LSH_ORACLE_DEDUP) && !inv)) {
+    rc = -8;
+    goto done;
+  }
+  rc = lsh_oracle_attend(c, qk, v, perm, buckets, o, lse);
   if (rc) goto done;
   rc = lsh_oracle_combine(c, o, lse, out);
   if (rc) goto done;
@@ -630,8 +660,8 @@ int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
   {
     double* khat = (double*)malloc(sizeof(double) * (size_t)d);
     double* qhat = (double*)malloc(sizeof(double) * (size_t)d);
-    double* logit = (double*)malloc(sizeof(double) * (size_t)(2 * m));
-    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * m));
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(3 * m));
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)(3 * m));
 #pragma omp for schedule(dynamic, 1)
     for (int64_t bh = 0; bh < nbh; ++bh) {
       const double* qk_bh = qk + bh * L * d;
@@ -652,7 +682,13 @@ int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
             for (int64_t rr = 0; rr < R; ++rr) sum += exp(lse[(bh * R + rr) * L + i] - mx);
             const double w = exp(lse[seg * L + i] - mx) / sum;
             const double* drow = dout + (bh * L + i) * d;
-            const int64_t n = window(c, qk_bh, pm, NULL, s, khat, qhat, logit, key);
+            const int64_t n = window(c, qk_bh, pm, buckets ? buckets + seg * L : NULL, s, khat,
+                                     qhat, logit, key);
+            if (c->variant & LSH_ORACLE_DEDUP)
+              for (int64_t a = 0; a < n; ++a)
+                logit[a] -= log((double)rounds_sharing(c, inv + bh * R * L,
+                                                       buckets ? buckets + bh * R * L : NULL, i,
+                                                       key[a]));
             if (n == 0) {
               if (pass == 1)
                 for (int64_t u = 0; u < d; ++u) mdv[(bh * L + i) * d + u] += w * fabs(drow[u]);
@@ -662,7 +698,8 @@ int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
             const double* outrow = out + (bh * L + i) * d;
             double dq_out = 0.0;
             for (int64_t u = 0; u < d; ++u) dq_out += drow[u] * outrow[u];
-            const double* q = qk_bh + i * d;
+            const int nq = (c->variant & LSH_ORACLE_NORM_QUERIES) != 0;
+            const double* q = nq ? qhat : qk_bh + i * d;
             const double scale = 1.0 / sqrt((double)d);
             for (int64_t a = 0; a < n; ++a) {
               const int64_t j = key[a];
@@ -675,9 +712,10 @@ int lsh_oracle_backward_magnitudes(const lsh_oracle_config* c, const double* qk,
               }
               const double A = wp * (fabs(dpv) + fabs(dq_out) + 2.0 * eq[bh * L + i]);
               unit_key(qk_bh + j * d, d, khat);
+              double* mqi = nq ? mdk + (bh * L + i) * d : mdqk + (bh * L + i) * d;
               for (int64_t u = 0; u < d; ++u) {
                 mdv[(bh * L + j) * d + u] += wp * fabs(drow[u]);
-                mdqk[(bh * L + i) * d + u] += A * fabs(khat[u]) * scale;
+                mqi[u] += A * fabs(khat[u]) * scale;
                 mdk[(bh * L + j) * d + u] += A * fabs(q[u]) * scale;
               }
             }
@@ -708,6 +746,7 @@ done:
   free(out);
   free(mdk);
   free(eq);
+  free(inv);
   return rc;
 }
 

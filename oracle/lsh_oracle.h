@@ -105,17 +105,19 @@ int lsh_oracle_forward(const lsh_oracle_config* cfg, const double* qk, const dou
                        double* margin);
 
 /* Backward at fixed permutations: dqk, dv [B, H, L, d] from dout [B, H, L, d]
- * (gradient of a loss with respect to out); perm [B, H, R, L] as from forward.
- * Default reading only (variant 0; otherwise -10). */
+ * (gradient of a loss with respect to out); perm [B, H, R, L] as from forward;
+ * buckets [B, H, R, L] as from forward, needed with SAME_BUCKET (-12 if NULL
+ * then), else may be NULL. Every variant reading. */
 int lsh_oracle_backward(const lsh_oracle_config* cfg, const double* qk, const double* v,
-                        const int32_t* perm, const double* dout, double* dqk, double* dv);
+                        const int32_t* perm, const int32_t* buckets, const double* dout,
+                        double* dqk, double* dv);
 
 /* Upper bounds of the absolute values of the backward's terms, summed as the
  * backward sums them (test infrastructure for error bounds): |dv| <= mdv and
- * |dqk| <= mdqk elementwise; see lsh_oracle.c. Default reading only. */
+ * |dqk| <= mdqk elementwise; see lsh_oracle.c. Arguments as for the backward. */
 int lsh_oracle_backward_magnitudes(const lsh_oracle_config* cfg, const double* qk,
-                                   const double* v, const int32_t* perm, const double* dout,
-                                   double* mdqk, double* mdv);
+                                   const double* v, const int32_t* perm, const int32_t* buckets,
+                                   const double* dout, double* mdqk, double* mdv);
 
 /* The shared-QK and value projections of a layer input ([TT] shared-QK section:
  * one linear map gives queries and keys, a second one the values):

@@ -61,7 +61,14 @@ static int one_case(int B, int H, int L, int d, int nb, int R, int m, int causal
   double* orow = (double*)malloc(sizeof(double) * 4 * d);
   double* lrow = (double*)malloc(sizeof(double) * 4 * R);
   CHECK(lsh_oracle_attend_rows(&c, qk, v, pm, bk, 4, sample, orow, lrow));
-  if (variant == 0) CHECK(lsh_oracle_backward(&c, qk, v, pm, dout, dqk, dv));
+  CHECK(lsh_oracle_backward(&c, qk, v, pm, bk, dout, dqk, dv));
+  {
+    double* mq = (double*)malloc(sizeof(double) * tok * d);
+    double* mv = (double*)malloc(sizeof(double) * tok * d);
+    CHECK(lsh_oracle_backward_magnitudes(&c, qk, v, pm, bk, dout, mq, mv));
+    free(mq);
+    free(mv);
+  }
   const int64_t md = 24;
   double* x = fill((size_t)B * L * md);
   double* wq = fill((size_t)H * d * md);

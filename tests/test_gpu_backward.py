@@ -238,3 +238,93 @@ def test_backward_gradient_rows_at_the_fp16_limit():
     assert res[False][3] > 0 and res[True][3] == 0
     perm, dqk, dv, _ = res[True]
     _check_both(w, oracle.config(w), inp.qk, inp.v, perm, dout, dqk, dv, fp32_rows=True)
+
+
+# ---------------------------------------------------------------------------
+# Variant readings. They run on the plain kernels: every step in fp32 from the
+# inputs' exact values, over windows of up to three chunks, so the fp32 form
+# of the bound holds with (6 chunk_len + 2 head_dim) 2^-24 for the bracket,
+# plus the rounding of the result to the input dtype (u |ref|).
+
+_VFLAGS = {"look_ahead": oracle.LOOK_AHEAD, "same_bucket": oracle.SAME_BUCKET,
+           "norm_queries": oracle.NORM_QUERIES, "dedup": oracle.DEDUP}
+_ALLV = dict(look_ahead=True, same_bucket=True, norm_queries=True, dedup=True)
+
+VAR_BWD = [
+    (W("c4k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=2, causal=True),
+     dict(look_ahead=True)),
+    (W("c4k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=2, causal=False),
+     dict(same_bucket=True)),
+    (W("text64k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=2, causal=True),
+     dict(norm_queries=True)),
+    (W("c4k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=3, causal=True),
+     dict(dedup=True)),
+    (W("c4k", batch=1, heads=1, seq_len=512, n_buckets=8, n_rounds=3, causal=False),
+     dict(look_ahead=True, dedup=True)),
+    (W("text64k", batch=1, heads=2, seq_len=640, n_buckets=8, n_rounds=3, causal=True), _ALLV),
+    (W("tiny", n_rounds=2), _ALLV),  # fp32
+    # chunk length 40, 1200 positions: a ragged window count
+    (W("c4k", batch=1, heads=1, seq_len=1200, chunk_len=40, n_buckets=8, n_rounds=2,
+       causal=False), _ALLV),
+]
+
+
+def _bound_plain(ref, mag, w):
+    u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -24
+    c = (6 * w.chunk_len + 2 * w.head_dim) * 2.0 ** -24
+    return u * np.abs(ref) + c * mag + 1e-30
+
+
+@pytest.mark.parametrize("w,kw", VAR_BWD,
+                         ids=[f"{w.name}-{w.dtype}-H{w.heads}L{w.seq_len}m{w.chunk_len}"
+                              f"R{w.n_rounds}{'c' if w.causal else 'n'}-" + "+".join(kw)
+                              for w, kw in VAR_BWD])
+def test_variant_backward_parity(w, kw):
+    _say(f"[backward variant] {w} {sorted(kw)}")
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    qk, v, rot = to_device(inp, dev)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
+                          w.chunk_len, w.causal, dtype=dt, backward=True, **kw)
+    try:
+        _, ex = op(qk, v, rot, return_perm=True, return_buckets=True)
+        dout_t, dout = _dout(w, 7100 + w.seq_len + w.n_rounds)
+        sb = kw.get("same_bucket", False)
+        dqk, dv = op.backward(qk, v, ex["perm"], dout_t.to(dev),
+                              buckets=ex["buckets"] if sb else None)
+        torch.cuda.synchronize()
+        perm = ex["perm"].cpu().numpy()
+        bk = ex["buckets"].cpu().numpy()
+        dqk = dqk.to(torch.float64).cpu().numpy()
+        dv = dv.to(torch.float64).cpu().numpy()
+    finally:
+        op.close()
+    variant = sum(_VFLAGS[k] for k, on in kw.items() if on)
+    c = oracle.config(w, variant=variant)
+    rq, rv = oracle.backward(c, inp.qk, inp.v, perm, dout, buckets=bk)
+    mq, mv = oracle.backward_magnitudes(c, inp.qk, inp.v, perm, dout, buckets=bk)
+    for name, g, ref, mag in (("dqk", dqk, rq, mq), ("dv", dv, rv, mv)):
+        err = np.abs(g - ref)
+        bound = _bound_plain(ref, mag, w)
+        worst = float((err / bound).max())
+        _say(f"  {name}: max err {err.max():.3g} (max |ref| {np.abs(ref).max():.3g}), "
+             f"worst err/bound {worst:.3g}")
+        assert (err <= bound).all(), f"{name} outside the bound (worst ratio {worst:.3g})"
+
+
+def test_same_bucket_backward_needs_the_buckets():
+    w = W("c4k", batch=1, heads=1, seq_len=256, n_buckets=4, n_rounds=1, causal=True)
+    _say(f"[backward same-bucket without buckets] {w}")
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    qk, v, rot = to_device(inp, dev)
+    op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
+                          w.chunk_len, w.causal, backward=True, same_bucket=True)
+    try:
+        _, ex = op(qk, v, rot, return_perm=True)
+        with pytest.raises(lat.LSHAttnError) as e:
+            op.backward(qk, v, ex["perm"], torch.zeros_like(qk))
+        assert e.value.status == 1  # INVALID_ARG
+    finally:
+        op.close()

@@ -148,7 +148,3 @@ def test_variants_full_size_sampled_rows():
              tol)
 
 
-def test_backward_with_a_variant_is_unsupported():
-    with pytest.raises(lat.LSHAttnError) as e:
-        lat.LSHAttention(1, 1, 256, 64, 4, 1, 64, True, backward=True, dedup=True)
-    assert e.value.status == 2  # UNSUPPORTED

@@ -8,7 +8,12 @@ it against things that do not share its formulas:
     queries that see only themselves;
   * for one bucket and one chunk covering the sequence, PyTorch fp64 autograd
     of dense shared-QK attention with unit keys and the self-mask, a separate
-    formulation (the forward of that case is pinned to SDPA).
+    formulation (the forward of that case is pinned to SDPA); with unit
+    queries too for NORM_QUERIES.
+The variant readings (look-ahead, same-bucket, unit queries, de-duplication
+and their combinations) are pinned the same way, by finite differences of the
+forward of that reading (DEDUP's forward takes the union of the rounds' key
+sets directly), and DEDUP also by identical rounds reducing to one round.
 """
 import math
 
@@ -167,3 +172,126 @@ def test_backward_magnitudes_of_one_key_window(oracle_lib):
     # dkhat of key 0: A |q_1| / sqrt(2), then the Jacobian in absolute value
     mk = A * np.array([1.0, 0.0]) / math.sqrt(2)
     np.testing.assert_allclose(mq[0, 0, 0], (mk + khat0 * (khat0 @ mk)) / 5.0, rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Variant readings: the same pins (finite differences of the oracle's own
+# forward of that reading, which for DEDUP takes the union of the rounds' key
+# sets directly, a separate formulation from the backward's per-round terms)
+
+LA, SB, NQ, DD = oracle.LOOK_AHEAD, oracle.SAME_BUCKET, oracle.NORM_QUERIES, oracle.DEDUP
+VARIANTS = [LA, SB, NQ, DD, LA | DD, SB | DD, LA | SB | NQ | DD]
+
+
+def _vcfg(L, d, nb, R, m, causal, variant, H=2):
+    return oracle.config(batch=1, heads=H, seq_len=L, head_dim=d, n_buckets=nb, n_rounds=R,
+                         chunk_len=m, causal=int(causal), variant=variant)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_variant_backward_matches_finite_differences(oracle_lib, variant, causal):
+    rng = np.random.default_rng(100 + variant + 17 * int(causal))
+    L, d, nb, R, m = 16, 4, 4, 2, 4
+    c = _vcfg(L, d, nb, R, m, causal, variant)
+    qk = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, d))
+    bk, _ = oracle.hash(c, qk, rng.standard_normal((R, d, nb // 2)))
+    pm, _ = oracle.sort(c, bk)
+    dout = rng.standard_normal((1, 2, L, d))
+    dqk, dv = oracle.backward(c, qk, v, pm, dout, buckets=bk)
+    h = 1e-6
+    for x, g in ((qk, dqk), (v, dv)):
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + h
+            up = _loss(c, qk, v, bk, dout)
+            x[idx] = keep - h
+            dn = _loss(c, qk, v, bk, dout)
+            x[idx] = keep
+            fd[idx] = (up - dn) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=2e-7)
+
+
+def _dense_grads_unit_queries(qk, v, dout, causal):
+    """Dense shared-QK attention with unit queries and unit keys and the
+    self-mask, differentiated by torch autograd in float64."""
+    L, d = qk.shape
+    q = torch.tensor(qk, requires_grad=True)
+    vv = torch.tensor(v, requires_grad=True)
+    k = q / q.norm(dim=-1, keepdim=True)
+    allowed = ~torch.eye(L, dtype=torch.bool)
+    if causal:
+        allowed &= torch.ones(L, L, dtype=torch.bool).tril()
+    empty = ~allowed.any(dim=1)
+    logits = (k @ k.T) / math.sqrt(d)
+    p = torch.softmax(logits.masked_fill(~allowed, -math.inf).masked_fill(empty[:, None], 0.0),
+                      dim=1)
+    out = torch.where(empty[:, None], vv, p @ vv)
+    (out * torch.tensor(dout)).sum().backward()
+    return q.grad.numpy(), vv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_unit_query_backward_single_chunk_equals_dense_autograd(oracle_lib, causal):
+    rng = np.random.default_rng(40 + int(causal))
+    L, d = 20, 6
+    c = _vcfg(L, d, 1, 2, L, causal, NQ)
+    qk = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, d))
+    dout = rng.standard_normal((1, 2, L, d))
+    pm = oracle.forward(c, qk, v, None)["perm"]
+    dqk, dv = oracle.backward(c, qk, v, pm, dout)
+    for h in range(2):
+        gq, gv = _dense_grads_unit_queries(qk[0, h], v[0, h], dout[0, h], causal)
+        np.testing.assert_allclose(dqk[0, h], gq, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv[0, h], gv, rtol=0, atol=1e-12)
+
+
+def test_dedup_backward_of_identical_rounds_equals_one_round(oracle_lib):
+    """With R rounds of the same buckets every pair is shared by all R rounds,
+    so DEDUP's union is one round's key set and its gradients equal those of
+    a single round of the default reading."""
+    rng = np.random.default_rng(8)
+    L, d, nb, m = 24, 5, 6, 4
+    c1 = _vcfg(L, d, nb, 1, m, True, 0)
+    c3 = _vcfg(L, d, nb, 3, m, True, DD)
+    qk = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, d))
+    dout = rng.standard_normal((1, 2, L, d))
+    bk1, _ = oracle.hash(c1, qk, rng.standard_normal((1, d, nb // 2)))
+    bk3 = np.repeat(bk1, 3, axis=2)
+    pm1, _ = oracle.sort(c1, bk1)
+    pm3, _ = oracle.sort(c3, bk3)
+    g1 = oracle.backward(c1, qk, v, pm1, dout)
+    g3 = oracle.backward(c3, qk, v, pm3, dout, buckets=bk3)
+    for a, b in zip(g1, g3):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_variant_backward_magnitudes_bound_the_gradients(oracle_lib, variant):
+    rng = np.random.default_rng(60 + variant)
+    L, d, nb, R, m = 24, 6, 6, 3, 4
+    c = _vcfg(L, d, nb, R, m, True, variant)
+    qk = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, d))
+    bk, _ = oracle.hash(c, qk, rng.standard_normal((R, d, nb // 2)))
+    pm, _ = oracle.sort(c, bk)
+    dout = rng.standard_normal((1, 2, L, d))
+    dqk, dv = oracle.backward(c, qk, v, pm, dout, buckets=bk)
+    mq, mv = oracle.backward_magnitudes(c, qk, v, pm, dout, buckets=bk)
+    assert np.all(np.abs(dqk) <= mq * (1 + 1e-12) + 1e-300)
+    assert np.all(np.abs(dv) <= mv * (1 + 1e-12) + 1e-300)
+    _, dvp = oracle.backward(c, qk, np.abs(v), pm, np.abs(dout), buckets=bk)
+    _, mvp = oracle.backward_magnitudes(c, qk, np.abs(v), pm, np.abs(dout), buckets=bk)
+    np.testing.assert_allclose(mvp, dvp, rtol=1e-12, atol=0)
+
+
+def test_same_bucket_backward_needs_buckets(oracle_lib):
+    c = _vcfg(8, 2, 2, 1, 4, False, SB, H=1)
+    z = np.zeros((1, 1, 8, 2))
+    pm = np.tile(np.arange(8, dtype=np.int32), (1, 1, 1, 1))
+    with pytest.raises(ValueError):
+        oracle.backward(c, z, z, pm, z)

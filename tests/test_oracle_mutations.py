@@ -54,6 +54,17 @@ MUTATIONS = [
     ("bwd: key gradient from the key instead of the query",
      "dkhat[(bh * L + j) * d + u] += ds * q[u] * scale;",
      "dkhat[(bh * L + j) * d + u] += ds * khat[u] * scale;"),
+    ("bwd: unit-query gradient outside the normalisation Jacobian",
+     "double* dqi = nq ? dkhat + (bh * L + i) * d : dqk + (bh * L + i) * d;",
+     "double* dqi = dqk + (bh * L + i) * d;"),
+    ("bwd: key gradient from the raw query with unit queries",
+     "          const double* q = nq ? qhat : qk_bh + i * d;\n          const double scale",
+     "          const double* q = qk_bh + i * d;\n          const double scale"),
+    ("bwd: dedup count ignored",
+     "              logit[a] -= log((double)rounds_sharing(c, inv + bh * R * L,\n"
+     "                                                     buckets",
+     "              logit[a] -= 0.0 * log((double)rounds_sharing(c, inv + bh * R * L,\n"
+     "                                                     buckets"),
     # variants
     ("look-ahead chunk missing", "&& last < L) last += m;", "&& last < L) last += 0;"),
     ("same-bucket mask against itself", "bk[j] != bk[i]) continue;", "bk[j] != bk[j]) continue;"),
@@ -102,6 +113,12 @@ def _pin_calls():
         lambda: bpins.test_backward_matches_finite_differences(o, False),
         lambda: bpins.test_backward_matches_finite_differences(o, True),
         lambda: bpins.test_backward_single_chunk_equals_dense_autograd(o, 3, True),
+        lambda: bpins.test_variant_backward_matches_finite_differences(o, bpins.NQ, False),
+        lambda: bpins.test_variant_backward_matches_finite_differences(o, bpins.DD, True),
+        lambda: bpins.test_variant_backward_matches_finite_differences(
+            o, bpins.LA | bpins.SB | bpins.NQ | bpins.DD, True),
+        lambda: bpins.test_unit_query_backward_single_chunk_equals_dense_autograd(o, True),
+        lambda: bpins.test_dedup_backward_of_identical_rounds_equals_one_round(o),
         lambda: vpins.test_variant_equals_dense_definition(o, vpins.LA, True),
         lambda: vpins.test_variant_equals_dense_definition(o, vpins.SB, False),
         lambda: vpins.test_variant_equals_dense_definition(o, vpins.NQ, False),

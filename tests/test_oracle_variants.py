@@ -190,8 +190,11 @@ def test_variant_rows_match_full_forward(oracle_lib):
                                atol=1e-14)
 
 
-def test_backward_rejects_variants(oracle_lib):
-    c = _cfg(1, 1, 16, 4, 4, 1, 4, False, LA)
+def test_same_bucket_backward_rejects_missing_buckets(oracle_lib):
+    """The variant backward is pinned in test_oracle_backward.py; here only
+    that the same-bucket reading refuses to run without the bucket ids."""
+    c = _cfg(1, 1, 16, 4, 4, 1, 4, False, SB)
     z = np.zeros((1, 1, 16, 4))
+    pm = np.tile(np.arange(16, dtype=np.int32), (1, 1, 1, 1))
     with pytest.raises(ValueError):
-        oracle.backward(c, z, z, np.zeros((1, 1, 1, 16), np.int32), z)
+        oracle.backward(c, z, z, pm, z)
