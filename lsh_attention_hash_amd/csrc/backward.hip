@@ -181,141 +181,383 @@ __device__ __forceinline__ int shared_rounds(const int32_t* inv_bh, const uint16
   return n;
 }
 
-// dq of the query at slot s of segment seg (one D/8-lane row group per
-// query): the sum over its window of dS_ij khat_j / sqrt(d). The variant
-// readings (flags) change the window and the logits as in the forward:
-// LOOK_AHEAD adds the next chunk, SAME_BUCKET drops keys of other buckets (bkt
-// [seg, L]), NORM_QUERIES takes the logit with q / |q| (and this is then the
-// gradient with respect to the unit query), DEDUP divides P by the number of
-// rounds sharing the pair (inv [seg, L]).
-template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void k_bwd_dq(const T* __restrict__ qk, const T* __restrict__ v,
-                                                const T* __restrict__ dout,
-                                                const int32_t* __restrict__ perm,
-                                                const float* __restrict__ lse,
-                                                const float* __restrict__ w,
-                                                const float* __restrict__ cq,
-                                                float* __restrict__ dq, int L, int m, int R,
-                                                int64_t n_rows, int flags,
-                                                const uint16_t* __restrict__ bkt,
-                                                const int32_t* __restrict__ inv) {
-  constexpr int kLpr = D / 8;
-  const int sub = threadIdx.x % kLpr;
-  const int64_t slot_row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
-  if (slot_row >= n_rows) return;
-  const int64_t seg = slot_row / L;
-  const int s = (int)(slot_row - seg * L);
-  const int64_t bh = seg / R;
-  const int32_t* pm = perm + seg * L;
-  const int i = pm[s];
-  const float l = lse[seg * L + i];
-  float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (l != kSelfLogit) {
-    const float scale = 1.0f / sqrtf((float)D);
-    const float wi = w[seg * L + i], ci = cq[bh * L + i];
-    float q[8], dz[8];
-    load8<T>(qk + (bh * L + i) * D + sub * 8, q);
-    load8<T>(dout + (bh * L + i) * D + sub * 8, dz);
-    float qs = 1.f;
-    if (flags & LSH_ATTN_FLAG_NORM_QUERIES) {
-      const float qn2 = row_sum<kLpr>(dot8(q, q));
-      qs = qn2 > 0.f ? 1.0f / sqrtf(qn2) : 0.f;
-    }
-    const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
-    const int bi = sb ? bkt[seg * L + i] : 0;
-    const int chunk = s / m;
-    const int first = (chunk > 0 ? chunk - 1 : chunk) * m;
-    int last = (chunk + 1) * m;
-    if ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && last < L) last += m;
-    for (int t = first; t < last; ++t) {
-      const int j = pm[t];
-      if (j == i || (CAUSAL && j > i)) continue;
-      if (sb && bkt[seg * L + j] != bi) continue;
-      float k[8], vj[8];
-      load8<T>(qk + (bh * L + j) * D + sub * 8, k);
-      load8<T>(v + (bh * L + j) * D + sub * 8, vj);
-      const float n2 = row_sum<kLpr>(dot8(k, k));
-      const float qkd = row_sum<kLpr>(dot8(q, k));
-      const float dv = row_sum<kLpr>(dot8(dz, vj));
-      const float rn = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
-      float p = __expf(qkd * qs * rn * scale - l);
-      if (flags & LSH_ATTN_FLAG_DEDUP)
-        p /= (float)shared_rounds(inv + bh * R * L, bkt + bh * R * L, L, m, R, i, j, flags);
-      const float ds = wi * p * (dv - ci);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) g[u] = fmaf(ds * rn * scale, k[u], g[u]);
-    }
-  }
-  store8(dq + (seg * L + i) * D + sub * 8, g);
+// The plain gradient products (any shape, every variant reading), in the
+// plain attention kernel's layout: a workgroup of 256 threads takes kQB
+// queries (k_bwd_dq_tiled: dq = sum over the window of dS_ij khat_j / sqrt(d))
+// or kQB keys (k_bwd_dkv_tiled: dkhat_j = sum_i dS_ij q_i / sqrt(d) and
+// dv_j = sum_i w_r(i) P_ij dout_i over the queries that see the key: those of
+// its chunk and of the next one, and of the previous one with LOOK_AHEAD) of
+// one chunk, 16 threads per row. The other side's rows are staged in LDS as
+// fp32, kKB at a time, the next block loaded into registers while the current
+// one is used. A thread computes the pairs of its row with the staged rows
+// g + 16 u (full dot products from LDS), writes the pair coefficients to LDS,
+// and then accumulates its kDPT output dims over the block. The variant
+// readings change the window and the logits as in the forward: LOOK_AHEAD adds
+// the next chunk, SAME_BUCKET drops keys of other buckets (bkt [seg, L]),
+// NORM_QUERIES takes the unit query (and dq is then the gradient with respect
+// to it), DEDUP lowers each logit by log of the number of rounds sharing the
+// pair (inv [seg, L]).
+template <int D>
+struct BT {
+  static constexpr int kQB = 16;                     // rows per workgroup
+  static constexpr int kKB = D == 64 ? 64 : 32;      // staged rows per block
+  static constexpr int kPPT = kKB / 16;              // pairs per thread per block
+  static constexpr int kDPT = D / 16;                // output dims per thread
+  static constexpr int kS = D + 4;                   // LDS row stride (fp32 words)
+  static constexpr int kPieces = kKB * D / 4 / 256;  // 4-element loads per thread per array
+  static constexpr int kTPR = 256 / kKB;             // threads per staged row in norm passes
+  static constexpr int kMaxWin = 3 * 256;            // window slots (chunk_len <= 256)
+};
+
+__device__ __forceinline__ float4 load4f(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4f(const bf16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
 }
 
-// dkhat and dv of the key at slot t of segment seg: the queries that see it
-// are those of its chunk and of the next one (and of the previous one with
-// LOOK_AHEAD); variant readings as for k_bwd_dq (with NORM_QUERIES, dkhat
-// takes the unit query).
+template <int D>
+__device__ __forceinline__ float lds_dot(const float* a, const float* b) {
+  float s = 0.f;
+#pragma unroll
+  for (int col = 0; col < D; col += 4) {
+    const float4 x = *(const float4*)(a + col);
+    const float4 y = *(const float4*)(b + col);
+    s = fmaf(x.x, y.x, s);
+    s = fmaf(x.y, y.y, s);
+    s = fmaf(x.z, y.z, s);
+    s = fmaf(x.w, y.w, s);
+  }
+  return s;
+}
+
 template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void k_bwd_dkv(const T* __restrict__ qk, const T* __restrict__ v,
-                                                 const T* __restrict__ dout,
-                                                 const int32_t* __restrict__ perm,
-                                                 const float* __restrict__ lse,
-                                                 const float* __restrict__ w,
-                                                 const float* __restrict__ cq,
-                                                 float* __restrict__ dk, float* __restrict__ dv,
-                                                 int L, int m, int R, int64_t n_rows, int flags,
-                                                 const uint16_t* __restrict__ bkt,
-                                                 const int32_t* __restrict__ inv) {
-  constexpr int kLpr = D / 8;
-  const int sub = threadIdx.x % kLpr;
-  const int64_t slot_row = (int64_t)blockIdx.x * (256 / kLpr) + threadIdx.x / kLpr;
-  if (slot_row >= n_rows) return;
-  const int64_t seg = slot_row / L;
-  const int t = (int)(slot_row - seg * L);
+__global__ __launch_bounds__(256) void k_bwd_dq_tiled(
+    const T* __restrict__ qk, const T* __restrict__ v, const T* __restrict__ dout,
+    const int32_t* __restrict__ perm, const float* __restrict__ lse, const float* __restrict__ w,
+    const float* __restrict__ cq, float* __restrict__ dq, int L, int m, int R, int flags,
+    const uint16_t* __restrict__ bkt, const int32_t* __restrict__ inv) {
+  using S = BT<D>;
+  __shared__ __align__(16) float ks[S::kKB * S::kS];
+  __shared__ __align__(16) float vs[S::kKB * S::kS];
+  __shared__ __align__(16) float qs[S::kQB * S::kS];
+  __shared__ __align__(16) float zs[S::kQB * S::kS];
+  __shared__ float cs[S::kQB * S::kKB];
+  __shared__ float nrm[S::kKB];
+  __shared__ int pw[S::kMaxWin];
+  __shared__ uint16_t bw[S::kMaxWin];
+  const int tid = threadIdx.x;
+  const int qblocks = (m + S::kQB - 1) / S::kQB;
+  const int nchunks = L / m;
+  const int64_t seg = blockIdx.x / (unsigned)(nchunks * qblocks);
+  const int rest = (int)(blockIdx.x - seg * (nchunks * qblocks));
+  const int c = rest / qblocks, qb = rest % qblocks;
   const int64_t bh = seg / R;
   const int32_t* pm = perm + seg * L;
-  const int j = pm[t];
-  const float scale = 1.0f / sqrtf((float)D);
-  float k[8], vj[8];
-  load8<T>(qk + (bh * L + j) * D + sub * 8, k);
-  load8<T>(v + (bh * L + j) * D + sub * 8, vj);
-  const float n2 = row_sum<kLpr>(dot8(k, k));
-  const float rn = n2 > 0.f ? 1.0f / sqrtf(n2) : 0.f;
-  const bool nq = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
   const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
-  const int bj = sb ? bkt[seg * L + j] : 0;
-  float gk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float gv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int chunk = t / m;
-  const int first = ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && chunk > 0 ? chunk - 1 : chunk) * m;
-  const int last = min(L, (chunk + 2) * m);
-  for (int s = first; s < last; ++s) {
-    const int i = pm[s];
-    if (i == j || (CAUSAL && j > i)) continue;
-    if (sb && bkt[seg * L + i] != bj) continue;
-    const float l = lse[seg * L + i];
-    if (l == kSelfLogit) continue;
-    const float wi = w[seg * L + i], ci = cq[bh * L + i];
-    float q[8], dz[8];
-    load8<T>(qk + (bh * L + i) * D + sub * 8, q);
-    load8<T>(dout + (bh * L + i) * D + sub * 8, dz);
-    float qs = 1.f;
-    if (nq) {
-      const float qn2 = row_sum<kLpr>(dot8(q, q));
-      qs = qn2 > 0.f ? 1.0f / sqrtf(qn2) : 0.f;
-    }
-    const float qkd = row_sum<kLpr>(dot8(q, k));
-    const float dvd = row_sum<kLpr>(dot8(dz, vj));
-    float p = __expf(qkd * qs * rn * scale - l);
-    if (flags & LSH_ATTN_FLAG_DEDUP)
-      p /= (float)shared_rounds(inv + bh * R * L, bkt + bh * R * L, L, m, R, i, j, flags);
-    const float ds = wi * p * (dvd - ci);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      gk[u] = fmaf(ds * scale * qs, q[u], gk[u]);
-      gv[u] = fmaf(wi * p, dz[u], gv[u]);
-    }
+  const bool dedup = (flags & LSH_ATTN_FLAG_DEDUP) != 0;
+  const int first = (c > 0 ? c - 1 : c) * m;
+  int last = (c + 1) * m;
+  if ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && last < L) last += m;
+  const int nwin = last - first;
+  for (int x = tid; x < nwin; x += 256) {
+    const int j = pm[first + x];
+    pw[x] = j;
+    if (sb) bw[x] = bkt[seg * L + j];
   }
-  store8(dk + (seg * L + j) * D + sub * 8, gk);
-  store8(dv + (seg * L + j) * D + sub * 8, gv);
+  __syncthreads();
+  const int q = tid / 16, g = tid % 16;
+  const int qslot0 = c * m + qb * S::kQB;
+  const int nq = min(S::kQB, (c + 1) * m - qslot0);
+  for (int p = tid; p < S::kQB * D / 4; p += 256) {
+    const int ql = p / (D / 4), col = (p % (D / 4)) * 4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), z = a;
+    if (ql < nq) {
+      const int64_t row = (bh * L + pw[qslot0 + ql - first]) * D + col;
+      a = load4f(qk + row);
+      z = load4f(dout + row);
+    }
+    *(float4*)&qs[ql * S::kS + col] = a;
+    *(float4*)&zs[ql * S::kS + col] = z;
+  }
+  const bool active = q < nq;
+  const int i = active ? pw[qslot0 + q - first] : 0;
+  const int bi = sb && active ? bw[qslot0 + q - first] : 0;
+  const float l = active ? lse[seg * L + i] : kSelfLogit;
+  const bool live = active && l != kSelfLogit;  // a self-only query has dq = 0
+  const float wi = live ? w[seg * L + i] : 0.f, ci = live ? cq[bh * L + i] : 0.f;
+  __syncthreads();
+  if (flags & LSH_ATTN_FLAG_NORM_QUERIES) {  // the unit query, as the forward takes it
+    float qq = 0.f;
+#pragma unroll
+    for (int u = 0; u < S::kDPT; ++u) {
+      const float x = qs[q * S::kS + g * S::kDPT + u];
+      qq += x * x;
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) qq += __shfl_xor(qq, off);
+    const float rq = qq > 0.f ? 1.0f / sqrtf(qq) : 0.f;
+#pragma unroll
+    for (int u = 0; u < S::kDPT; ++u) qs[q * S::kS + g * S::kDPT + u] *= rq;
+    __syncthreads();
+  }
+  float4 kr[S::kPieces], vr[S::kPieces];
+  auto fetch = [&](int kb) {
+    const int t0 = kb * S::kKB;
+#pragma unroll
+    for (int u = 0; u < S::kPieces; ++u) {
+      const int p = tid + 256 * u;
+      const int kk = p / (D / 4), col = (p % (D / 4)) * 4;
+      const int x = t0 + kk;
+      if (x < nwin) {
+        const int64_t row = (bh * L + pw[x]) * D + col;
+        kr[u] = load4f(qk + row);
+        vr[u] = load4f(v + row);
+      } else {
+        kr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        vr[u] = kr[u];
+      }
+    }
+  };
+  const float scale = 1.0f / sqrtf((float)D);
+  float acc[S::kDPT];
+#pragma unroll
+  for (int u = 0; u < S::kDPT; ++u) acc[u] = 0.f;
+  const int nblk = (nwin + S::kKB - 1) / S::kKB;
+  fetch(0);
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int t0 = kb * S::kKB;
+    const int nk = min(S::kKB, nwin - t0);
+#pragma unroll
+    for (int u = 0; u < S::kPieces; ++u) {
+      const int p = tid + 256 * u;
+      const int kk = p / (D / 4), col = (p % (D / 4)) * 4;
+      *(float4*)&ks[kk * S::kS + col] = kr[u];
+      *(float4*)&vs[kk * S::kS + col] = vr[u];
+    }
+    if (kb + 1 < nblk) fetch(kb + 1);
+    __syncthreads();
+    {  // squared key norms, as the forward sums them
+      const int kk = tid / S::kTPR, part = tid % S::kTPR;
+      float nn = 0.f;
+#pragma unroll
+      for (int u = 0; u < D / S::kTPR; ++u) {
+        const float x = ks[kk * S::kS + part * (D / S::kTPR) + u];
+        nn += x * x;
+      }
+#pragma unroll
+      for (int off = 1; off < S::kTPR; off <<= 1) nn += __shfl_xor(nn, off);
+      if (part == 0) nrm[kk] = nn;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < S::kPPT; ++u) {
+      const int kk = g + 16 * u;
+      float cv = 0.f;
+      if (live && kk < nk) {
+        const int j = pw[t0 + kk];
+        const bool keep = j != i && !(CAUSAL && j > i) && !(sb && bw[t0 + kk] != bi);
+        if (keep) {
+          const float nn = nrm[kk];
+          const float rn = nn > 0.f ? 1.0f / sqrtf(nn) : 0.f;
+          float logit = nn > 0.f ? lds_dot<D>(qs + q * S::kS, ks + kk * S::kS) / sqrtf(nn) * scale
+                                 : 0.f;
+          if (dedup) logit -= __logf((float)shared_rounds(inv + bh * R * L, bkt + bh * R * L, L,
+                                                          m, R, i, j, flags));
+          const float p = __expf(logit - l);
+          const float dvd = lds_dot<D>(zs + q * S::kS, vs + kk * S::kS);
+          cv = wi * p * (dvd - ci) * rn * scale;
+        }
+      }
+      cs[q * S::kKB + kk] = cv;
+    }
+    // the 16 threads of a query (one wave) wrote its coefficients; each reads them all
+    for (int kk = 0; kk < nk; ++kk) {
+      const float cv = cs[q * S::kKB + kk];
+#pragma unroll
+      for (int u = 0; u < S::kDPT; u += 4) {
+        const float4 b = *(const float4*)&ks[kk * S::kS + g * S::kDPT + u];
+        acc[u] = fmaf(cv, b.x, acc[u]);
+        acc[u + 1] = fmaf(cv, b.y, acc[u + 1]);
+        acc[u + 2] = fmaf(cv, b.z, acc[u + 2]);
+        acc[u + 3] = fmaf(cv, b.w, acc[u + 3]);
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  float* drow = dq + (seg * L + i) * D + g * S::kDPT;
+#pragma unroll
+  for (int u = 0; u < S::kDPT; u += 4)
+    *(float4*)(drow + u) = make_float4(acc[u], acc[u + 1], acc[u + 2], acc[u + 3]);
+}
+
+template <int D, typename T, bool CAUSAL>
+__global__ __launch_bounds__(256) void k_bwd_dkv_tiled(
+    const T* __restrict__ qk, const T* __restrict__ v, const T* __restrict__ dout,
+    const int32_t* __restrict__ perm, const float* __restrict__ lse, const float* __restrict__ w,
+    const float* __restrict__ cq, float* __restrict__ dk, float* __restrict__ dv, int L, int m,
+    int R, int flags, const uint16_t* __restrict__ bkt, const int32_t* __restrict__ inv) {
+  using S = BT<D>;
+  __shared__ __align__(16) float ks[S::kQB * S::kS];
+  __shared__ __align__(16) float vs[S::kQB * S::kS];
+  __shared__ __align__(16) float qs[S::kKB * S::kS];
+  __shared__ __align__(16) float zs[S::kKB * S::kS];
+  __shared__ float ca[S::kQB * S::kKB];
+  __shared__ float cb[S::kQB * S::kKB];
+  __shared__ float qsc[S::kKB];
+  __shared__ int pw[S::kMaxWin];
+  __shared__ uint16_t bw[S::kMaxWin];
+  const int tid = threadIdx.x;
+  const int kblocks = (m + S::kQB - 1) / S::kQB;
+  const int nchunks = L / m;
+  const int64_t seg = blockIdx.x / (unsigned)(nchunks * kblocks);
+  const int rest = (int)(blockIdx.x - seg * (nchunks * kblocks));
+  const int c = rest / kblocks, kbk = rest % kblocks;
+  const int64_t bh = seg / R;
+  const int32_t* pm = perm + seg * L;
+  const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  const bool dedup = (flags & LSH_ATTN_FLAG_DEDUP) != 0;
+  const bool nqf = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
+  // the queries that see the keys of chunk c: chunks c and c + 1, and c - 1
+  // with the look-ahead window
+  const int first = ((flags & LSH_ATTN_FLAG_LOOK_AHEAD) && c > 0 ? c - 1 : c) * m;
+  const int last = min(L, (c + 2) * m);
+  const int nwin = last - first;
+  for (int x = tid; x < nwin; x += 256) {
+    const int i = pm[first + x];
+    pw[x] = i;
+    if (sb) bw[x] = bkt[seg * L + i];
+  }
+  const int key = tid / 16, g = tid % 16;
+  const int kslot0 = c * m + kbk * S::kQB;
+  const int nk = min(S::kQB, (c + 1) * m - kslot0);
+  for (int p = tid; p < S::kQB * D / 4; p += 256) {
+    const int kl = p / (D / 4), col = (p % (D / 4)) * 4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (kl < nk) {
+      const int64_t row = (bh * L + pm[kslot0 + kl]) * D + col;
+      a = load4f(qk + row);
+      b = load4f(v + row);
+    }
+    *(float4*)&ks[kl * S::kS + col] = a;
+    *(float4*)&vs[kl * S::kS + col] = b;
+  }
+  const bool active = key < nk;
+  const int j = active ? pm[kslot0 + key] : 0;
+  const int bj = sb && active ? bkt[seg * L + j] : 0;
+  __syncthreads();
+  float kn = 0.f;  // |k_j|^2 over the 16 threads of the key
+#pragma unroll
+  for (int u = 0; u < S::kDPT; ++u) {
+    const float x = ks[key * S::kS + g * S::kDPT + u];
+    kn += x * x;
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) kn += __shfl_xor(kn, off);
+  const float rn = kn > 0.f ? 1.0f / sqrtf(kn) : 0.f;
+  float4 qr[S::kPieces], zr[S::kPieces];
+  auto fetch = [&](int qb) {
+    const int s0 = qb * S::kKB;
+#pragma unroll
+    for (int u = 0; u < S::kPieces; ++u) {
+      const int p = tid + 256 * u;
+      const int qq = p / (D / 4), col = (p % (D / 4)) * 4;
+      const int x = s0 + qq;
+      if (x < nwin) {
+        const int64_t row = (bh * L + pw[x]) * D + col;
+        qr[u] = load4f(qk + row);
+        zr[u] = load4f(dout + row);
+      } else {
+        qr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        zr[u] = qr[u];
+      }
+    }
+  };
+  const float scale = 1.0f / sqrtf((float)D);
+  float gk[S::kDPT], gv[S::kDPT];
+#pragma unroll
+  for (int u = 0; u < S::kDPT; ++u) {
+    gk[u] = 0.f;
+    gv[u] = 0.f;
+  }
+  const int nblk = (nwin + S::kKB - 1) / S::kKB;
+  fetch(0);
+  for (int qb = 0; qb < nblk; ++qb) {
+    const int s0 = qb * S::kKB;
+    const int nqb = min(S::kKB, nwin - s0);
+#pragma unroll
+    for (int u = 0; u < S::kPieces; ++u) {
+      const int p = tid + 256 * u;
+      const int qq = p / (D / 4), col = (p % (D / 4)) * 4;
+      *(float4*)&qs[qq * S::kS + col] = qr[u];
+      *(float4*)&zs[qq * S::kS + col] = zr[u];
+    }
+    if (qb + 1 < nblk) fetch(qb + 1);
+    __syncthreads();
+    if (nqf) {  // unit queries: kTPR threads per staged query
+      const int qq = tid / S::kTPR, part = tid % S::kTPR;
+      float nn = 0.f;
+#pragma unroll
+      for (int u = 0; u < D / S::kTPR; ++u) {
+        const float x = qs[qq * S::kS + part * (D / S::kTPR) + u];
+        nn += x * x;
+      }
+#pragma unroll
+      for (int off = 1; off < S::kTPR; off <<= 1) nn += __shfl_xor(nn, off);
+      if (part == 0) qsc[qq] = nn > 0.f ? 1.0f / sqrtf(nn) : 0.f;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < S::kPPT; ++u) {
+      const int qq = g + 16 * u;
+      float a = 0.f, b = 0.f;
+      if (active && qq < nqb) {
+        const int i = pw[s0 + qq];
+        bool keep = i != j && !(CAUSAL && j > i) && !(sb && bw[s0 + qq] != bj);
+        const float l = keep ? lse[seg * L + i] : kSelfLogit;
+        if (keep && l != kSelfLogit) {
+          const float qs_i = nqf ? qsc[qq] : 1.f;
+          float logit = lds_dot<D>(qs + qq * S::kS, ks + key * S::kS) * qs_i * rn * scale;
+          if (dedup) logit -= __logf((float)shared_rounds(inv + bh * R * L, bkt + bh * R * L, L,
+                                                          m, R, i, j, flags));
+          const float p = __expf(logit - l);
+          const float dvd = lds_dot<D>(zs + qq * S::kS, vs + key * S::kS);
+          const float wi = w[seg * L + i], ci = cq[bh * L + i];
+          a = wi * p * (dvd - ci) * scale * qs_i;
+          b = wi * p;
+        }
+      }
+      ca[key * S::kKB + qq] = a;
+      cb[key * S::kKB + qq] = b;
+    }
+    // the 16 threads of a key (one wave) wrote its coefficients; each reads them all
+    for (int qq = 0; qq < nqb; ++qq) {
+      const float a = ca[key * S::kKB + qq], b = cb[key * S::kKB + qq];
+#pragma unroll
+      for (int u = 0; u < S::kDPT; u += 4) {
+        const float4 x = *(const float4*)&qs[qq * S::kS + g * S::kDPT + u];
+        const float4 z = *(const float4*)&zs[qq * S::kS + g * S::kDPT + u];
+        gk[u] = fmaf(a, x.x, gk[u]);
+        gk[u + 1] = fmaf(a, x.y, gk[u + 1]);
+        gk[u + 2] = fmaf(a, x.z, gk[u + 2]);
+        gk[u + 3] = fmaf(a, x.w, gk[u + 3]);
+        gv[u] = fmaf(b, z.x, gv[u]);
+        gv[u + 1] = fmaf(b, z.y, gv[u + 1]);
+        gv[u + 2] = fmaf(b, z.z, gv[u + 2]);
+        gv[u + 3] = fmaf(b, z.w, gv[u + 3]);
+      }
+    }
+    __syncthreads();
+  }
+  if (!active) return;
+  float* krow = dk + (seg * L + j) * D + g * S::kDPT;
+  float* vrow = dv + (seg * L + j) * D + g * S::kDPT;
+#pragma unroll
+  for (int u = 0; u < S::kDPT; u += 4) {
+    *(float4*)(krow + u) = make_float4(gk[u], gk[u + 1], gk[u + 2], gk[u + 3]);
+    *(float4*)(vrow + u) = make_float4(gv[u], gv[u + 1], gv[u + 2], gv[u + 3]);
+  }
 }
 
 // the forward's int32 bucket ids as the kernels' u16 ids
@@ -517,20 +759,21 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
     return;
   }
   const int vf = p.flags & kVariantFlags;
+  const dim3 gq((unsigned)(p.nseg() * (p.L / p.m) * ((p.m + BT<D>::kQB - 1) / BT<D>::kQB)));
   if (p.causal) {
-    hipLaunchKernelGGL((k_bwd_dq<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr, vf, bk16,
-                       inv);
-    hipLaunchKernelGGL((k_bwd_dkv<D, T, true>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr, vf,
-                       bk16, inv);
+    hipLaunchKernelGGL((k_bwd_dq_tiled<D, T, true>), gq, dim3(256), 0, s, (const T*)qk,
+                       (const T*)v, (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R,
+                       vf, bk16, inv);
+    hipLaunchKernelGGL((k_bwd_dkv_tiled<D, T, true>), gq, dim3(256), 0, s, (const T*)qk,
+                       (const T*)v, (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m,
+                       p.R, vf, bk16, inv);
   } else {
-    hipLaunchKernelGGL((k_bwd_dq<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R, nr, vf, bk16,
-                       inv);
-    hipLaunchKernelGGL((k_bwd_dkv<D, T, false>), gr, dim3(256), 0, s, (const T*)qk, (const T*)v,
-                       (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m, p.R, nr, vf,
-                       bk16, inv);
+    hipLaunchKernelGGL((k_bwd_dq_tiled<D, T, false>), gq, dim3(256), 0, s, (const T*)qk,
+                       (const T*)v, (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R,
+                       vf, bk16, inv);
+    hipLaunchKernelGGL((k_bwd_dkv_tiled<D, T, false>), gq, dim3(256), 0, s, (const T*)qk,
+                       (const T*)v, (const T*)dout, perm, b.lse, b.w, b.cq, b.dk, b.dv, p.L, p.m,
+                       p.R, vf, bk16, inv);
   }
   mark(3);
   hipLaunchKernelGGL((k_bwd_reduce<D, T>), gt, dim3(256), 0, s, (const T*)qk, (const T*)dout,
