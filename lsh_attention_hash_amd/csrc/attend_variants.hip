@@ -81,11 +81,12 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
 
-// Without the de-duplication counts, two workgroups fit a CU at d = 128 when
-// the window is two chunks: let each wave take half the register file.
+// With a window of two chunks, two workgroups fit a CU at d = 128 (76 KB of LDS
+// with the de-duplication counts, 245 VGPRs): let each wave take half the
+// register file.
 template <int D, bool CAUSAL, int NS, bool DD, typename OT>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(NS == 2 && !DD ? 2 : 1, NS == 2 && !DD ? 2 : 1))) void k_attend_var(
+__attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_attend_var(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const int32_t* __restrict__ perm, const float* __restrict__ knorm,
     const uint16_t* __restrict__ bkt, const int32_t* __restrict__ inv, OT* __restrict__ o,
