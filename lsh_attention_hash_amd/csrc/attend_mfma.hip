@@ -609,25 +609,45 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
 
 hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* v,
                                   const int32_t* perm, const float* knorm, const void* dout,
-                                  float* od, float* lse, hipStream_t s) {
+                                  const uint16_t* buckets, float* od, float* lse, hipStream_t s) {
   static bool configured[kMaxDevices] = {};
   if (first_on_device(configured)) {
-    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, float, true, false, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
-    (void)hipFuncSetAttribute((const void*)k_attend_mfma<128, float, false, false, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::kBytes);
+    auto attr = [](const void* k) {
+      (void)hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                Lds<128>::kBytes);
+    };
+    attr((const void*)k_attend_mfma<128, float, true, false, true>);
+    attr((const void*)k_attend_mfma<128, float, false, false, true>);
+    attr((const void*)k_attend_mfma<128, float, true, false, true, true, false>);
+    attr((const void*)k_attend_mfma<128, float, false, false, true, true, false>);
+    attr((const void*)k_attend_mfma<128, float, true, false, true, false, true>);
+    attr((const void*)k_attend_mfma<128, float, false, false, true, false, true>);
+    attr((const void*)k_attend_mfma<128, float, true, false, true, true, true>);
+    attr((const void*)k_attend_mfma<128, float, false, false, true, true, true>);
   }
-  auto go = [&](auto d) {
+  // the unit-query and same-bucket readings as in the forward (template flags)
+  const bool nq = (p.flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
+  const bool sb = (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  auto go = [&](auto d, auto c, auto n, auto b) {
     constexpr int D = decltype(d)::value;
-    if (p.causal)
-      launch_one<D, float, true, false, true>(p, qk, v, nullptr, nullptr, perm, knorm, od, lse, s,
-                                              dout);
-    else
-      launch_one<D, float, false, false, true>(p, qk, v, nullptr, nullptr, perm, knorm, od, lse,
-                                               s, dout);
+    constexpr bool C = decltype(c)::value, NQ = decltype(n)::value, SB = decltype(b)::value;
+    launch_one<D, float, C, false, true, NQ, SB>(p, qk, v, nullptr, nullptr, perm, knorm, od, lse,
+                                                 s, dout, buckets);
   };
-  if (p.d == 64) go(std::integral_constant<int, 64>{});
-  else go(std::integral_constant<int, 128>{});
+  auto flags = [&](auto d, auto c) {
+    using T = std::true_type;
+    using F = std::false_type;
+    if (nq && sb) go(d, c, T{}, T{});
+    else if (nq) go(d, c, T{}, F{});
+    else if (sb) go(d, c, F{}, T{});
+    else go(d, c, F{}, F{});
+  };
+  auto causal = [&](auto d) {
+    if (p.causal) flags(d, std::true_type{});
+    else flags(d, std::false_type{});
+  };
+  if (p.d == 64) causal(std::integral_constant<int, 64>{});
+  else causal(std::integral_constant<int, 128>{});
   return hipGetLastError();
 }
 

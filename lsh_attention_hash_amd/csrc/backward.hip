@@ -731,7 +731,7 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
                        (const T*)dout, b.w, b.cq, p.L, p.R, p.o_seg_rows(), nt);
   mark(2);
   if (bwd_mfma_supported(p)) {
-    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, b, s);
+    (void)launch_backward_mfma(p, qk, v, perm, dout, knorm, bk16, b, s);
     mark(3);
     const bool half = bwd_rows_half(p);
     auto go = [&](auto r) {
@@ -791,17 +791,17 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
   // the per-round attention, recomputed from the permutation
   hipError_t e = hipSuccess;
   if (ev) (void)hipEventRecord(ev[0], s);
+  if (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) {
+    const int64_t n = p.n_rows();
+    hipLaunchKernelGGL(k_bwd_bucket16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       buckets, bk16, n);
+  }
   if (bwd_mfma_supported(p)) {
     e = launch_key_norms(p, qk, knorm, s);
     if (e == hipSuccess)
-      e = launch_attend_mfma_dot(p, qk, v, perm, knorm, dout, b.od, b.lse, s);
+      e = launch_attend_mfma_dot(p, qk, v, perm, knorm, dout, bk16, b.od, b.lse, s);
   } else {
     // fp32 rows from the plain kernel, which takes every variant reading
-    if (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) {
-      const int64_t n = p.n_rows();
-      hipLaunchKernelGGL(k_bwd_bucket16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                         buckets, bk16, n);
-    }
     if (p.flags & LSH_ATTN_FLAG_DEDUP) e = launch_inverse_perm(p, perm, inv, s);
     if (e == hipSuccess) e = launch_attend_plain(p, qk, v, perm, bk16, inv, b.o32, b.lse, s);
   }

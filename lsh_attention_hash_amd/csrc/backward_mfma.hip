@@ -13,6 +13,11 @@
 //   S    = Q K^T,  dP   = dO V^T                 (a key block, the chunk's queries)
 //   wP = w_q P, dS = wP (dP - dout.out)          -> dV^T += dO^T wP, dkhat^T += Q^T dS
 // Rows are written at original positions, once: no atomics, deterministic.
+// Two variant readings as template flags, as in the forward's kernel: NQ, unit
+// queries (the logits of query i times 1/|q_i|, dkhat taking the unit query,
+// and the query's own gradient, then taken with respect to the unit query,
+// going through the same normalisation Jacobian as the row's unit key); SB,
+// only keys in the query's bucket of the round (bucket ids staged per row).
 #include "dtype.h"
 #include "internal.h"
 #include "rows_lds.h"
@@ -79,13 +84,14 @@ struct FLds {
   static constexpr int kQLse = kKPos + 2 * kChunk * 4;
   static constexpr int kQC = kQLse + kChunk * 4;          // [64] dout . out
   static constexpr int kPn = kQC + kChunk * 4;            // [64] positions of the next chunk
-  static constexpr int kBytes = kPn + kChunk * 4;
+  static constexpr int kBkt = kPn + kChunk * 4;           // [2][64] bucket ids (SB)
+  static constexpr int kBytes = kBkt + 2 * kChunk * 4;
 };
 
 // one chunk's rows and scalars between their loads and the staging
 struct FRegs {
   uint4 k[4], v[4], d[4];
-  int pos;
+  int pos, bk;
   float n2, lse, w, c;
 };
 
@@ -93,13 +99,14 @@ struct FRegs {
 constexpr int kFusedRange = 16;
 constexpr int kFusedResident = 256;
 
-template <int D, bool CAUSAL, typename GT>
+template <int D, bool CAUSAL, typename GT, bool NQ = false, bool SB = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void k_bwd_fused_mfma(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const unsigned char* __restrict__ dout, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
     const float* __restrict__ cq, GT* __restrict__ dqk_r, GT* __restrict__ dv_r, int L,
-    int R, int nseg, int chunks_per_wg, int ranges, int group_segs) {
+    int R, int nseg, int chunks_per_wg, int ranges, int group_segs,
+    const uint16_t* __restrict__ buckets) {
   using Lay = BLay<D>;
   using M = FLds<D>;
   constexpr int KS = D / 32, DT = D / 16;
@@ -125,9 +132,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   float* qlse = (float*)(lds + M::kQLse);
   float* qc = (float*)(lds + M::kQC);
   int* pn = (int*)(lds + M::kPn);
+  int* kbkt = (int*)(lds + M::kBkt);
   const int t = threadIdx.x;
   const float sc = kLog2e / sqrtf((float)D);
   const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+  const float sqrt_d = sqrtf((float)D);
 
   auto fetch = [&](FRegs& r, bool queries) {
     load_group<D>(r.k, qkb, pn);
@@ -136,6 +145,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     if (t < kChunk) {
       r.pos = pn[t];
       r.n2 = knorm[row0 + r.pos];
+      if (SB) r.bk = buckets[seg * L + r.pos];
       if (queries) {
         r.lse = lse[seg * L + r.pos];
         r.w = wr[seg * L + r.pos];
@@ -156,6 +166,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       kscale[sl * kChunk + t] = sc * rn;
       kscale_ds[sl * kChunk + t] = rn * inv_sqrt_d;
       kpos[sl * kChunk + t] = r.pos;
+      if (SB) kbkt[sl * kChunk + t] = r.bk;
       if (queries) {
         // a zero weight gives +inf here and P = 0 below
         qlse[t] = r.lse * kLog2e - __log2f(r.w);
@@ -179,6 +190,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       kscale[kChunk + t] = 0.f;
       kscale_ds[kChunk + t] = 0.f;
       kpos[kChunk + t] = 0;
+      kbkt[kChunk + t] = 0;
     }
   }
   if (t < kChunk) pn[t] = pm[c0 * kChunk + t];
@@ -199,6 +211,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   auto keys_step = [&](int sl, int cur) {
     const float ksc = kscale[sl * kChunk + blk];
     const int kp = kpos[sl * kChunk + blk];
+    const int kbk = SB ? kbkt[sl * kChunk + blk] : 0;
     bf16x8_t kf[KS], vf[KS];
     {
       const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + blk * Lay::kRow;
@@ -233,12 +246,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
         const int qpv[4] = {qp.x, qp.y, qp.z, qp.w};
         const float qlv[4] = {ql.x, ql.y, ql.z, ql.w};
         const float qcc[4] = {qcv.x, qcv.y, qcv.z, qcv.w};
+        float rq[4] = {1.f, 1.f, 1.f, 1.f};  // 1 / |q| (unit queries)
+        int qbk[4] = {0, 0, 0, 0};
+        if (NQ) {
+          const float4 r4 = *(const float4*)(kscale_ds + cur * kChunk + q0);
+          rq[0] = r4.x * sqrt_d, rq[1] = r4.y * sqrt_d, rq[2] = r4.z * sqrt_d, rq[3] = r4.w * sqrt_d;
+        }
+        if (SB) {
+          const int4 b4 = *(const int4*)(kbkt + cur * kChunk + q0);
+          qbk[0] = b4.x, qbk[1] = b4.y, qbk[2] = b4.z, qbk[3] = b4.w;
+        }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const bool masked = CAUSAL ? kp >= qpv[b] : kp == qpv[b];
-          const float wp = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], ksc, -qlv[b]));
+          const bool masked = (CAUSAL ? kp >= qpv[b] : kp == qpv[b]) | (SB && kbk != qbk[b]);
+          const float wp =
+              masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(NQ ? s[b] * rq[b] : s[b], ksc, -qlv[b]));
           wpf[4 * half + b] = (__bf16)wp;
-          dsf[4 * half + b] = (__bf16)(wp * (dp[b] - qcc[b]));
+          dsf[4 * half + b] = (__bf16)(wp * (dp[b] - qcc[b]) * (NQ ? rq[b] : 1.f));
         }
       }
       const int off = (g + 4 * e) * Lay::kPair + (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
@@ -261,12 +285,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     const int prv = cur ^ 1;
     const int sls[2] = {prv, cur};
     float ksc[2];
-    int kp[2];
+    int kp[2], kbk[2];
     bf16x8_t kf[2][KS], vf[2][KS];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       ksc[j] = kscale[sls[j] * kChunk + blk];
       kp[j] = kpos[sls[j] * kChunk + blk];
+      kbk[j] = SB ? kbkt[sls[j] * kChunk + blk] : 0;
       const unsigned char* krow = lds + M::kKt + sls[j] * Lay::kRM + blk * Lay::kRow;
       const unsigned char* vrow = lds + M::kVt + sls[j] * Lay::kRM + blk * Lay::kRow;
 #pragma unroll
@@ -307,14 +332,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
         const int qpv[4] = {qp.x, qp.y, qp.z, qp.w};
         const float qlv[4] = {ql.x, ql.y, ql.z, ql.w};
         const float qcc[4] = {qcv.x, qcv.y, qcv.z, qcv.w};
+        float rq[4] = {1.f, 1.f, 1.f, 1.f};  // 1 / |q| (unit queries)
+        int qbk[4] = {0, 0, 0, 0};
+        if (NQ) {
+          const float4 r4 = *(const float4*)(kscale_ds + cur * kChunk + q0);
+          rq[0] = r4.x * sqrt_d, rq[1] = r4.y * sqrt_d, rq[2] = r4.z * sqrt_d, rq[3] = r4.w * sqrt_d;
+        }
+        if (SB) {
+          const int4 b4 = *(const int4*)(kbkt + cur * kChunk + q0);
+          qbk[0] = b4.x, qbk[1] = b4.y, qbk[2] = b4.z, qbk[3] = b4.w;
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const bool masked = CAUSAL ? kp[j] >= qpv[b] : kp[j] == qpv[b];
-            const float wp = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(sv[j][b], ksc[j], -qlv[b]));
+            const bool masked =
+                (CAUSAL ? kp[j] >= qpv[b] : kp[j] == qpv[b]) | (SB && kbk[j] != qbk[b]);
+            const float wp = masked ? 0.f
+                                    : __builtin_amdgcn_exp2f(fmaf(NQ ? sv[j][b] * rq[b] : sv[j][b],
+                                                                  ksc[j], -qlv[b]));
             wpf[j][4 * half + b] = (__bf16)wp;
-            dsf[j][4 * half + b] = (__bf16)(wp * (dp[j][b] - qcc[b]));
+            dsf[j][4 * half + b] = (__bf16)(wp * (dp[j][b] - qcc[b]) * (NQ ? rq[b] : 1.f));
           }
       }
       const int off = (g + 4 * e) * Lay::kPair + (lq >> 3) * Lay::kBlk8 + (lq & 7) * 16;
@@ -336,6 +374,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   auto query_step = [&](int c, int cur, int prv, floatx4_t* dq) {
     const int posq = kpos[cur * kChunk + blk];
     const float lse2 = qlse[blk], cqv = qc[blk];
+    const float rq = NQ ? kscale_ds[cur * kChunk + blk] * sqrt_d : 1.f;  // 1 / |q|
+    const int bq = SB ? kbkt[cur * kChunk + blk] : 0;
     const int kb0 = c > 0 ? 0 : 4;  // chunk 0: the first four 16-key blocks are absent
     bf16x8_t qf[KS], df[KS];
     {
@@ -373,11 +413,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
         const float scv[4] = {scv4.x, scv4.y, scv4.z, scv4.w};
         const float sdv[4] = {sdv4.x, sdv4.y, sdv4.z, sdv4.w};
         const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
+        int kbv[4] = {0, 0, 0, 0};
+        if (SB) {
+          const int4 b4 = *(const int4*)(kbkt + sl * kChunk + key);
+          kbv[0] = b4.x, kbv[1] = b4.y, kbv[2] = b4.z, kbv[3] = b4.w;
+        }
         const bool absent = kb < kb0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const bool masked = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq);
-          const float wp = masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(s[b], scv[b], -lse2));
+          const bool masked =
+              absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq) | (SB && kbv[b] != bq);
+          const float wp =
+              masked ? 0.f : __builtin_amdgcn_exp2f(fmaf(NQ ? s[b] * rq : s[b], scv[b], -lse2));
           dsf[4 * half + b] = (__bf16)(wp * (dp[b] - cqv) * sdv[b]);
         }
       }
@@ -398,6 +445,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     const unsigned char* krow = lds + M::kKt + sl * Lay::kRM + blk * Lay::kRow + 8 * g;
     float kv[DT][4];
     float proj = 0.f;
+    if (NQ) {  // the unit query's gradient joins the unit key's: both take the Jacobian
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          dka[dt][b] = fmaf(dka[dt][b], inv_sqrt_d, dqa[dt][b]) * sqrt_d;
+          dqa[dt][b] = 0.f;
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const uint2 x = *(const uint2*)(krow + 32 * dt);
@@ -480,53 +536,77 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   if (c1 == nchunks) finish((c1 - 1) & 1);  // the last chunk's keys see no later queries
 }
 
-template <int D, bool CAUSAL, typename GT>
+template <int D, bool CAUSAL, typename GT, bool NQ, bool SB>
 void launch_fused(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-                  const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
+                  const void* dout, const float* knorm, const uint16_t* buckets, BwdWorkspace& b,
+                  hipStream_t s) {
   const int64_t nseg = p.nseg();
   const walks::RangeShape sh =
       walks::range_shape(p.L / kChunk, nseg, p.R, kFusedRange, kFusedResident);
-  auto kern = k_bwd_fused_mfma<D, CAUSAL, GT>;
+  auto kern = k_bwd_fused_mfma<D, CAUSAL, GT, NQ, SB>;
   hipLaunchKernelGGL(kern, dim3((unsigned)sh.blocks), dim3(kThreads), FLds<D>::kBytes, s,
                      (const unsigned char*)qk, (const unsigned char*)v,
                      (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, (GT*)b.dq,
-                     (GT*)b.dv, p.L, p.R, (int)nseg, sh.per, sh.ranges, sh.group_segs);
+                     (GT*)b.dv, p.L, p.R, (int)nseg, sh.per, sh.ranges, sh.group_segs, buckets);
 }
 
-template <int D, typename GT>
+template <int D, typename GT, bool NQ, bool SB>
 void configure() {
-  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, true, GT>,
+  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, true, GT, NQ, SB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, FLds<D>::kBytes);
-  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, false, GT>,
+  (void)hipFuncSetAttribute((const void*)k_bwd_fused_mfma<D, false, GT, NQ, SB>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, FLds<D>::kBytes);
+}
+
+template <typename GT, bool NQ, bool SB>
+void configure_all() {
+  configure<64, GT, NQ, SB>();
+  configure<128, GT, NQ, SB>();
+}
+
+template <typename GT, bool NQ, bool SB>
+void launch_gt(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+               const void* dout, const float* knorm, const uint16_t* buckets, BwdWorkspace& b,
+               hipStream_t s) {
+  if (p.d == 64) {
+    if (p.causal) launch_fused<64, true, GT, NQ, SB>(p, qk, v, perm, dout, knorm, buckets, b, s);
+    else launch_fused<64, false, GT, NQ, SB>(p, qk, v, perm, dout, knorm, buckets, b, s);
+  } else {
+    if (p.causal) launch_fused<128, true, GT, NQ, SB>(p, qk, v, perm, dout, knorm, buckets, b, s);
+    else launch_fused<128, false, GT, NQ, SB>(p, qk, v, perm, dout, knorm, buckets, b, s);
+  }
 }
 
 template <typename GT>
-void launch_gt(const Problem& p, const void* qk, const void* v, const int32_t* perm,
-               const void* dout, const float* knorm, BwdWorkspace& b, hipStream_t s) {
-  if (p.d == 64) {
-    if (p.causal) launch_fused<64, true, GT>(p, qk, v, perm, dout, knorm, b, s);
-    else launch_fused<64, false, GT>(p, qk, v, perm, dout, knorm, b, s);
-  } else {
-    if (p.causal) launch_fused<128, true, GT>(p, qk, v, perm, dout, knorm, b, s);
-    else launch_fused<128, false, GT>(p, qk, v, perm, dout, knorm, b, s);
-  }
+void launch_flags(const Problem& p, const void* qk, const void* v, const int32_t* perm,
+                  const void* dout, const float* knorm, const uint16_t* buckets,
+                  BwdWorkspace& b, hipStream_t s) {
+  const bool nq = (p.flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
+  const bool sb = (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  if (nq && sb) launch_gt<GT, true, true>(p, qk, v, perm, dout, knorm, buckets, b, s);
+  else if (nq) launch_gt<GT, true, false>(p, qk, v, perm, dout, knorm, buckets, b, s);
+  else if (sb) launch_gt<GT, false, true>(p, qk, v, perm, dout, knorm, buckets, b, s);
+  else launch_gt<GT, false, false>(p, qk, v, perm, dout, knorm, buckets, b, s);
 }
 
 }  // namespace
 
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
-                                BwdWorkspace& b, hipStream_t s) {
+                                const uint16_t* buckets, BwdWorkspace& b, hipStream_t s) {
   static bool configured[kMaxDevices] = {};
   if (first_on_device(configured)) {
-    configure<64, float>();
-    configure<128, float>();
-    configure<64, _Float16>();
-    configure<128, _Float16>();
+    configure_all<float, false, false>();
+    configure_all<float, true, false>();
+    configure_all<float, false, true>();
+    configure_all<float, true, true>();
+    configure_all<_Float16, false, false>();
+    configure_all<_Float16, true, false>();
+    configure_all<_Float16, false, true>();
+    configure_all<_Float16, true, true>();
   }
-  if (bwd_rows_half(p)) launch_gt<_Float16>(p, qk, v, perm, dout, knorm, b, s);
-  else launch_gt<float>(p, qk, v, perm, dout, knorm, b, s);
+  if (bwd_rows_half(p)) launch_flags<_Float16>(p, qk, v, perm, dout, knorm, buckets, b, s);
+  else launch_flags<float>(p, qk, v, perm, dout, knorm, buckets, b, s);
   return hipGetLastError();
 }
 

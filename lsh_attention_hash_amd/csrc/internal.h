@@ -144,10 +144,12 @@ hipError_t launch_attend_mfma(const Problem& p, const void* qk, const void* v,
                               const float* knorm, const uint16_t* buckets, OT* o, float* lse,
                               hipStream_t s);
 // the per-round attention of the backward: lse as above, and per query the
-// scalar dout . o_r in od [seg, L] instead of the rows
+// scalar dout . o_r in od [seg, L] instead of the rows; the unit-query and
+// same-bucket readings as in the forward (buckets [seg, L], read with
+// SAME_BUCKET)
 hipError_t launch_attend_mfma_dot(const Problem& p, const void* qk, const void* v,
                                   const int32_t* perm, const float* knorm, const void* dout,
-                                  float* od, float* lse, hipStream_t s);
+                                  const uint16_t* buckets, float* od, float* lse, hipStream_t s);
 // o is fp16 when o_half, else fp32; v (the input values) supplies the rows of
 // rounds in which a query saw only itself
 // at_limit: incremented once per (position, 8 dims) piece whose fp16
@@ -168,11 +170,12 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
                            float* knorm, uint16_t* bk16, int32_t* inv, BwdWorkspace& b,
                            unsigned long long* at_limit, hipStream_t s, const hipEvent_t* ev);
 
-// the per-round gradient products on matrix cores (attend_mfma_supported
-// shapes): b.dq receives dqk per round (dq and the normalised dkhat), b.dv dv
+// the per-round gradient products on matrix cores (bwd_mfma_supported
+// shapes): b.dq receives dqk per round (dq and the normalised dkhat), b.dv dv;
+// buckets [seg, L] read with SAME_BUCKET
 hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
-                                BwdWorkspace& b, hipStream_t s);
+                                const uint16_t* buckets, BwdWorkspace& b, hipStream_t s);
 
 // The variant readings (flags); the default matrix-core attention takes none
 // of them (attend_variants.hip does).
@@ -202,11 +205,13 @@ inline bool round_outputs_half(const Problem& p) {
          !(p.flags & LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS);
 }
 
-// The backward's products run on matrix cores for the default reading on the
-// matrix-core attention's shapes; the variant readings take the plain
-// kernels (fp32 per-round rows).
+// The backward's products run on matrix cores on the matrix-core attention's
+// shapes for the default reading and the unit-query and same-bucket readings;
+// the look-ahead and de-duplicated readings take the plain kernels (fp32
+// per-round rows).
 inline bool bwd_mfma_supported(const Problem& p) {
-  return attend_mfma_supported(p) && !(p.flags & kVariantFlags);
+  return attend_mfma_supported(p) &&
+         !(p.flags & (LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_DEDUP));
 }
 
 // The backward's per-round gradient rows (dqk_r, dv_r) on the matrix-core path

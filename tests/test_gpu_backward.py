@@ -241,10 +241,16 @@ def test_backward_gradient_rows_at_the_fp16_limit():
 
 
 # ---------------------------------------------------------------------------
-# Variant readings. They run on the plain kernels: every step in fp32 from the
-# inputs' exact values, over windows of up to three chunks, so the fp32 form
-# of the bound holds with (6 chunk_len + 2 head_dim) 2^-24 for the bracket,
-# plus the rounding of the result to the input dtype (u |ref|).
+# Variant readings. Unit queries and the same-bucket mask run on the matrix
+# cores for bf16 and chunk length 64, as the default reading does, and take its
+# bound (the extra 1/|q| factor is one fp32 rounding, next to the bf16
+# roundings the bound counts; the query's term of the magnitudes goes through
+# the normalisation as its gradient does). The look-ahead and de-duplicated
+# readings, and every fp32 or other-chunk shape, run on the plain kernels:
+# every step in fp32 from the inputs' exact values, over windows of up to
+# three chunks, so the fp32 form of the bound holds with
+# (6 chunk_len + 2 head_dim) 2^-24 for the bracket, plus the rounding of the
+# result to the input dtype (u |ref|).
 
 _VFLAGS = {"look_ahead": oracle.LOOK_AHEAD, "same_bucket": oracle.SAME_BUCKET,
            "norm_queries": oracle.NORM_QUERIES, "dedup": oracle.DEDUP}
@@ -257,6 +263,12 @@ VAR_BWD = [
      dict(same_bucket=True)),
     (W("text64k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=2, causal=True),
      dict(norm_queries=True)),
+    (W("c4k", batch=1, heads=2, seq_len=1024, n_buckets=8, n_rounds=2, causal=True),
+     dict(norm_queries=True)),
+    (W("text64k", batch=1, heads=2, seq_len=2048, n_buckets=16, n_rounds=4, causal=True),
+     dict(norm_queries=True, same_bucket=True)),
+    (W("c4k", batch=1, heads=2, seq_len=1280, n_buckets=8, n_rounds=3, causal=False),
+     dict(norm_queries=True, same_bucket=True)),
     (W("c4k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=3, causal=True),
      dict(dedup=True)),
     (W("c4k", batch=1, heads=1, seq_len=512, n_buckets=8, n_rounds=3, causal=False),
@@ -304,9 +316,11 @@ def test_variant_backward_parity(w, kw):
     c = oracle.config(w, variant=variant)
     rq, rv = oracle.backward(c, inp.qk, inp.v, perm, dout, buckets=bk)
     mq, mv = oracle.backward_magnitudes(c, inp.qk, inp.v, perm, dout, buckets=bk)
+    mfma = (w.dtype == "bf16" and w.chunk_len == 64 and not kw.get("look_ahead")
+            and not kw.get("dedup"))
     for name, g, ref, mag in (("dqk", dqk, rq, mq), ("dv", dv, rv, mv)):
         err = np.abs(g - ref)
-        bound = _bound_plain(ref, mag, w)
+        bound = _bound(name, ref, mag, w) if mfma else _bound_plain(ref, mag, w)
         worst = float((err / bound).max())
         _say(f"  {name}: max err {err.max():.3g} (max |ref| {np.abs(ref).max():.3g}), "
              f"worst err/bound {worst:.3g}")
