@@ -71,8 +71,8 @@ enum {
   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
   /* Also allocate the workspace of lsh_attn_backward: per position and round,
    * 2 fp32 rows of head_dim on the matrix-core path (bf16, chunk_len 64, head_dim
-   * 64 or 128, no variant flag) or 4 on the other shapes and with the variant
-   * flags, plus 12 bytes; 4 bytes per position. */
+   * 64 or 128, neither LOOK_AHEAD nor DEDUP) or 4 on the other shapes and with
+   * those flags, plus 12 bytes; 4 bytes per position. */
   LSH_ATTN_FLAG_BACKWARD = 4,
   /* Variant readings of the window and the combination, each one the pages
    * also describe (the default, all off, is the previous chunk and the chunk
@@ -200,8 +200,10 @@ int lsh_attn_backward(lsh_attn_t handle, const void* qk, const void* v, const in
  * same-bucket mask, unit queries, de-duplicated rounds; Reformer overview at
  * www.dtcms.com/a/488796.html, section 2.1, and www.2kiu.com/news/5253576/,
  * section 2.2). With LSH_ATTN_FLAG_NORM_QUERIES the unit query q / |q| takes
- * the same normalisation Jacobian as the unit key of that row. The variant
- * readings run on the plain kernels (fp32 per-round rows).
+ * the same normalisation Jacobian as the unit key of that row. Unit queries and
+ * the same-bucket mask run on the matrix-core path of the default reading; the
+ * look-ahead and de-duplicated readings on the plain kernels (fp32 per-round
+ * rows).
  *   buckets   [B, H, n_rounds, L]   int32  (read only): the forward's buckets
  *             output; required with LSH_ATTN_FLAG_SAME_BUCKET (INVALID_ARG if
  *             null then), may be null otherwise
