@@ -293,7 +293,24 @@ def _bound_plain(ref, mag, w):
                               for w, kw in VAR_BWD])
 def test_variant_backward_parity(w, kw):
     _say(f"[backward variant] {w} {sorted(kw)}")
+    _variant_backward_check(w, kw, workloads.make_inputs(w))
+
+
+@pytest.mark.parametrize("kw", [dict(norm_queries=True, same_bucket=True),
+                                dict(norm_queries=True, look_ahead=True)],
+                         ids=["nq+sb-matrix-cores", "nq+la-plain"])
+def test_variant_backward_zero_rows(kw):
+    """Zero qk rows: a zero key or unit query is 0, every logit with it is 0,
+    and the normalisation passes no gradient to the row."""
+    w = W("c4k", batch=1, heads=2, seq_len=512, n_buckets=8, n_rounds=2, causal=True)
+    _say(f"[backward variant zero rows] {w} {sorted(kw)}")
     inp = workloads.make_inputs(w)
+    inp.qk[:, :, ::7] = 0.0
+    inp.qk_bits[:, :, ::7] = 0
+    _variant_backward_check(w, kw, inp)
+
+
+def _variant_backward_check(w, kw, inp):
     dev = torch.device("cuda", 0)
     qk, v, rot = to_device(inp, dev)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
