@@ -160,34 +160,47 @@ __device__ __forceinline__ void tile(unsigned char* lds, const uint4* __restrict
 
 // The same product for BM = BN = 256 on 8 waves (a 4 x 2 wave grid, each wave
 // 64 rows x 128 columns, the accumulator layout of tile<256, 256, 32, 4, 2>),
-// with the waves in two groups that alternate: waves 0-3 (one per SIMD) stage
+// with the waves in two groups that alternate: waves 0-3 (one per SIMD) load
 // the slabs of A, waves 4-7 those of B, and while one group multiplies the
-// slab whose operands it holds in registers, the other reads its operands of
-// the same slab from LDS, stages its half of the next slab and issues the
-// loads of a later one. Every phase ends with a barrier and group 1 runs one
-// phase behind group 0, so each SIMD always has one wave issuing products.
-// LDS: two stages of 256 rows of A and of B (K slabs of 32, +16-byte pad);
-// each group's half of slab j + 1 is staged during its phase of slab j, and
-// its loads of slab j + 3 go into the register set just staged. K must be a
-// multiple of 64. Sums are taken in the same order as tile(): identical
+// slab whose operands it holds in registers, the other issues the loads of a
+// later slab and reads its operands of the same slab from LDS. Every phase
+// ends with a barrier and group 1 runs one phase behind group 0, so each SIMD
+// always has one wave issuing products. The slabs go from memory straight
+// into LDS (buffer loads with the LDS as destination: no staging registers or
+// stores) through a ring of four stages of 256 rows of A then of B, 64 bytes
+// per row, loaded three slabs ahead; within each 16-row block the 16-byte
+// piece p of row r sits in slot p ^ ((r / 4) % 4), so the 16 lanes of a
+// fragment read distinct banks. One load instruction fills a 16-row block
+// (1 KB): lane l writes row l / 4, slot l % 4, and so loads piece
+// (l % 4) ^ ((l / 16) % 4) of its row. The barriers carry no memory fence (a
+// fence would wait for every load in flight): each wave waits for its own part
+// of the next slab by vmcnt and for its fragment reads by lgkmcnt before the
+// barrier, which the compiler does not do for loads into LDS. K must be a
+// multiple of 32. Sums are taken in the same order as tile(): identical
 // results.
 struct LayPP {
   static constexpr int kThr = 512;
-  static constexpr int kStride = 32 * 2 + 16;
-  static constexpr int kHalf = 256 * kStride;       // one stage of A (or B)
-  static constexpr int kBytes = 4 * kHalf;          // [stage][A | B]
+  static constexpr int kHalf = 256 * 64;            // 256 rows of A (or B), one K slab
+  static constexpr int kStage = 2 * kHalf;          // [A | B]
+  static constexpr int kStages = 4;
+  static constexpr int kBytes = kStages * kStage;
   static constexpr int RT = 4, CT = 8;
 };
+
+template <int N>
+__device__ __forceinline__ void pp_wait_vm() {
+  // s_waitcnt vmcnt(N), no wait on the other counters
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
 
 __device__ __forceinline__ void tile_pp(unsigned char* lds, const uint4* __restrict__ a,
                                         int64_t row0, int64_t M, const uint4* __restrict__ brows,
                                         int K, floatx4_t (&acc)[4][8]) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  constexpr int kStride = LayPP::kStride;
+  typedef __attribute__((address_space(3))) void* lptr_t;
   const int t = threadIdx.x;
+  const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool gb = w >= 4;  // group 1: stages B
-  const int tt = t & 255;
+  const bool gb = w >= 4;  // group 1 stages B
   const int kseg = K / 8;
   const int nslab = K / 32;
   const int last = nslab - 1;
@@ -198,40 +211,42 @@ __device__ __forceinline__ void tile_pp(unsigned char* lds, const uint4* __restr
       __builtin_amdgcn_make_buffer_rsrc((void*)brows, (short)0, 256 * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t res = gb ? bres : ares;
   const int nrows = gb ? 256 : (int)arows;
-  // this thread's 4 pieces of its group's half-slab: rows tt/4 + 64j, piece tt%4
+  // wave w % 4 of the group loads the 16-row blocks 4 (w % 4) + j of its half
+  // (one 1 KB block per load: lane l writes row l / 4 of the block, slot l % 4,
+  // and so fetches piece (l % 4) ^ ((l / 16) % 4) of that row)
+  const int wg = w & 3;
+  const int lpiece = (lane & 3) ^ ((lane >> 4) & 3);
   int off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = tt / 4 + 64 * j;
-    off[j] = ((r < nrows ? r : nrows - 1) * kseg + tt % 4) * 16;
+    const int r = 16 * (4 * wg + j) + (lane >> 2);
+    off[j] = ((r < nrows ? r : nrows - 1) * kseg + lpiece) * 16;
   }
-  unsigned char* const sbase = lds + (gb ? LayPP::kHalf : 0) + (tt / 4) * kStride + (tt % 4) * 16;
-  u32x4 r0[4], r1[4];
-  auto load = [&](u32x4 (&r)[4], int s) {
-    const int so = s * 64;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_raw_buffer_load_b128(res, off[j] + so, 0, 0);
-  };
-  auto store = [&](const u32x4 (&r)[4], int stage) {
+  unsigned char* const hbase = lds + (gb ? LayPP::kHalf : 0) + 4 * wg * 1024;
+  auto dma = [&](int s) {
+    unsigned char* dst = hbase + (s & 3) * LayPP::kStage;
+    const int so = (s < last ? s : last) * 64;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *(u32x4*)(sbase + stage * 2 * LayPP::kHalf + 64 * j * kStride) = r[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lptr_t)(dst + j * 1024), 16, off[j], so, 0,
+                                               0);
   };
-  const int lane = t & 63, g = lane >> 4, lq = lane & 15;
+  const int g = lane >> 4, lq = lane & 15;
   const int wr = 64 * (w / 2), wc = 128 * (w % 2);
+  const int slot = 16 * (g ^ (lq >> 2));
+  const int arel = (wr + lq) * 64 + slot;
+  const int brel = LayPP::kHalf + (wc + lq) * 64 + slot;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) acc[i][ct] = floatx4_t{};
   bf16x8_t fa[4], fb[8];
-  auto read = [&](int stage) {
-    const unsigned char* sa = lds + stage * 2 * LayPP::kHalf;
+  auto read = [&](int s) {
+    const unsigned char* st = lds + (s & 3) * LayPP::kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[i] = *(const bf16x8_t*)(sa + (wr + 16 * i + lq) * kStride + 16 * g);
+    for (int i = 0; i < 4; ++i) fa[i] = *(const bf16x8_t*)(st + arel + i * 1024);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      fb[ct] = *(const bf16x8_t*)(sa + LayPP::kHalf + (wc + 16 * ct + lq) * kStride + 16 * g);
+    for (int ct = 0; ct < 8; ++ct) fb[ct] = *(const bf16x8_t*)(st + brel + ct * 1024);
   };
   auto compute = [&]() {
 #pragma unroll
@@ -240,33 +255,49 @@ __device__ __forceinline__ void tile_pp(unsigned char* lds, const uint4* __restr
       for (int ct = 0; ct < 8; ++ct)
         acc[i][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[ct], acc[i][ct], 0, 0, 0);
   };
-  auto sync = [&]() {
+  // barriers without a memory fence: the waits are explicit (the loads into
+  // LDS by vmcnt, the fragment reads by lgkmcnt), so the slab loads stay in
+  // flight across them
+  auto bar = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto lgkm0 = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto vm8 = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    pp_wait_vm<8>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  load(r0, 0);
-  store(r0, 0);
-  load(r1, min(1, last));
-  load(r0, min(2, last));
-  sync();
-  if (gb) sync();  // group 1 runs one phase behind
-  for (int s = 0; s < nslab; s += 2) {
-    read(0);
-    store(r1, 1);
-    load(r1, min(s + 3, last));
-    sync();
+  dma(0);
+  dma(1);
+  dma(2);
+  vm8();  // slab 0 of this wave is in LDS
+  bar();
+  if (gb) bar();  // group 1 runs one phase behind
+  for (int s = 0; s < nslab; ++s) {
+    // memory phase: slab s + 3 on its way, slab s + 1 (this wave's part) in
+    // LDS, then this wave's operands of slab s
+    dma(s + 3);
+    vm8();
+    read(s);
+    lgkm0();
+    bar();
     compute();
-    sync();
-    read(1);
-    store(r0, 0);
-    load(r0, min(s + 4, last));
-    sync();
-    compute();
-    sync();
+    bar();
   }
-  if (!gb) sync();
+  if (!gb) bar();
+  // the loads of the clamped slabs past the end: drain them before the
+  // caller reuses the LDS
+  __builtin_amdgcn_sched_barrier(0);
+  pp_wait_vm<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
 }
 
 }  // namespace gemm

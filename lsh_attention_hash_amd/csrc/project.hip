@@ -10,8 +10,8 @@
 //
 // Matrix-core path (bf16, d in {64, 128}, model_dim a multiple of 32): one
 // workgroup computes a 256-row x d-column tile of one head's qk or v with the
-// tile of gemm_core.h, or, for d = 128 with an even head count and model_dim
-// a multiple of 64, a 256-row tile of two heads with the two-group tile (the
+// tile of gemm_core.h, or, for d = 128 with an even head count, a 256-row
+// tile of two heads with the two-group tile (the
 // tiles of a row tile run on one XCD, one after the other, so the x tile is
 // read from HBM once and from that XCD's L2 by the others). The epilogue rounds the tile to bf16 and passes it through LDS so that each
 // lane writes 16 contiguous bytes of a row. For qk tiles the same pass produces
@@ -107,9 +107,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_proj_mfma(
   }
 }
 
-// d = 128 with an even head count and model_dim a multiple of 64: a
-// 256-row x 256-column tile (heads 2p and 2p + 1 of qk or of v) on the
-// two-group tile of gemm_core.h; its wave column w % 2 holds head 2p + w % 2.
+// d = 128 with an even head count: a 256-row x 256-column tile (heads 2p and
+// 2p + 1 of qk or of v) on the two-group tile of gemm_core.h; its wave column
+// w % 2 holds head 2p + w % 2.
 // The epilogue takes one head at a time through LDS, with the same per-row
 // arithmetic as k_proj_mfma.
 constexpr int kPPOutStride = 128 * 2 + 16;
@@ -229,7 +229,7 @@ hipError_t launch_project(const Problem& p, int model_dim, const void* x, const 
     // workgroups return at once
     const int64_t mts = (M + kRows - 1) / kRows;
     const unsigned grid = (unsigned)(((mts + 7) / 8) * 8 * 2 * p.H);
-    if (p.d == 128 && p.H % 2 == 0 && model_dim % 64 == 0) {
+    if (p.d == 128 && p.H % 2 == 0) {
       const unsigned grid_pp = (unsigned)(((mts + 7) / 8) * 8 * p.H);
       if (!hs.proj_attr)
         (void)hipFuncSetAttribute((const void*)k_proj_pp,

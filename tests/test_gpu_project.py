@@ -103,7 +103,7 @@ CASES = [
     (W("c4k", batch=1, heads=2, seq_len=256, n_buckets=8, n_rounds=2), 96),   # 3 K slabs of 32
     # d = 128: two-head tiles (even H, model_dim of 64s), ragged rows
     (W("text64k", batch=1, heads=2, seq_len=320, n_buckets=16, n_rounds=2), 128),
-    # d = 128 on one-head tiles: odd H, and model_dim not a multiple of 64
+    # d = 128: one-head tiles (odd H); two-head tiles over 3 K slabs
     (W("text64k", batch=1, heads=3, seq_len=320, n_buckets=16, n_rounds=2), 192),
     (W("text64k", batch=2, heads=2, seq_len=256, n_buckets=16, n_rounds=2), 96),
 ]
