@@ -189,7 +189,7 @@ def both_fractions(stage: str, units: dict, ms: float):
 # Stages that are exactly one kernel launch (name as rocprofv3 reports it),
 # and the source files each stage's kernels are built from.
 STAGE_KERNEL = {"hash": "k_hash_mfma", "attend": "k_attend_mfma", "combine": "k_combine",
-                "project": "k_proj_mfma"}
+                "project": "k_proj"}  # k_proj_pp (d = 128, even heads) or k_proj_mfma
 FFN_STAGE_KERNEL = {"ffn_up": "k_ffn_mfma<true, 256>", "ffn_down": "k_ffn_mfma<false, 256>"}
 BWD_STAGE_KERNEL = {"rows": "k_bwd_rows_dot", "products": "k_bwd_fused_mfma",
                     "reduce": "k_bwd_reduce_sum"}
@@ -197,7 +197,7 @@ STAGE_SOURCES = {
     "hash_prep": ["hash_mfma.hip", "hash_x16.h"], "hash": ["hash_mfma.hip", "hash.hip", "hash_x16.h"],
     "hash_rescore": ["hash_mfma.hip"], "sort": ["sort.hip"], "gather": ["gather.hip"],
     "attend": ["attend_mfma.hip", "attend.hip"], "combine": ["combine.hip"],
-    "project": ["project.hip", "hash_x16.h"],
+    "project": ["project.hip", "hash_x16.h", "gemm_core.h"],
     "recompute": ["attend_mfma.hip", "backward.hip"], "rows": ["backward.hip"],
     "products": ["backward_mfma.hip", "rows_lds.h"], "reduce": ["backward.hip"],
     "ffn_up": ["ffn.hip", "gemm_core.h"], "ffn_down": ["ffn.hip", "gemm_core.h"],
@@ -773,6 +773,9 @@ def main():
         rl["kernel"] = "k_hash_exact"
     elif variants and dominant == "attend" and set(variants) & {"look_ahead", "dedup"}:
         rl["kernel"] = "k_attend_var"  # the look-ahead and de-duplication readings' own kernel
+    elif dominant == "project":
+        rl["kernel"] = ("k_proj_pp" if w.head_dim == 128 and w.heads % 2 == 0 else
+                        "k_proj_mfma")
     per_stage = {k: {"ms": round(stage_avg[k], 5)} for k in stage_avg}
     for k in per_stage:
         if stage_avg[k] > 0:
