@@ -24,7 +24,9 @@
 // this round and, for DEDUP, its chunk (and bucket) in every round, which the
 // count N_ij compares with the query's. The next chunk's rows are loaded while
 // the current one is computed. Per-round outputs are rows at original
-// positions, fp16 (as the default kernel's) or fp32 with the fp32 flag.
+// positions, fp16 (as the default kernel's) or fp32 with the fp32 flag; in the
+// DOT form (the backward's recomputation) each query's row is reduced to
+// dout(i) . o_r(i) instead, as in the default kernel's DOT form.
 #include <type_traits>
 
 #include "dtype.h"
@@ -84,14 +86,18 @@ __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0
 // With a window of two chunks, two workgroups fit a CU at d = 128 (76 KB of LDS
 // with the de-duplication counts, 245 VGPRs): let each wave take half the
 // register file.
-template <int D, bool CAUSAL, int NS, bool DD, typename OT>
+// DOT: o receives per query the scalar dout(i) . o_r(i) ([seg, L] fp32;
+// dout(i) . v_i for a query that saw only itself, whose output is v_i), dout
+// being bf16 rows [B*H, L, D].
+template <int D, bool CAUSAL, int NS, bool DD, typename OT, bool DOT>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_attend_var(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const int32_t* __restrict__ perm, const float* __restrict__ knorm,
     const uint16_t* __restrict__ bkt, const int32_t* __restrict__ inv, OT* __restrict__ o,
     float* __restrict__ lse, int L, int R, int nseg, int chunks_per_wg, int ranges,
-    int group_segs, int64_t o_seg_rows, int flags) {
+    int group_segs, int64_t o_seg_rows, int flags, const unsigned char* __restrict__ dout) {
+  static_assert(!DOT || std::is_same<OT, float>::value, "the DOT form writes fp32 scalars");
   using Lay = BLay<D>;
   using M = VLds<D, NS, DD>;
   constexpr int KS = D / 32, DT = D / 16;
@@ -347,7 +353,38 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_at
       const bool seen = l > 0.f;
       const float invl = seen ? 1.0f / l : 0.f;
       OT* orow = o + (seg * o_seg_rows + posq) * D;
-      if constexpr (sizeof(OT) == 2) {
+      if constexpr (DOT) {
+        // lane group g holds dims 16 dt + 4g + 0..3 of the row, as dout's
+        // 8-byte pieces; the four groups' partial sums are added across lanes
+        const unsigned char* drow = dout + ((row0 + posq) * D + 4 * g) * 2;
+        auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+        auto hi = [](uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); };
+        float dsum = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint2 z = *(const uint2*)(drow + 32 * dt);
+          dsum = fmaf(oacc[dt][0], lo(z.x), dsum);
+          dsum = fmaf(oacc[dt][1], hi(z.x), dsum);
+          dsum = fmaf(oacc[dt][2], lo(z.y), dsum);
+          dsum = fmaf(oacc[dt][3], hi(z.y), dsum);
+        }
+        dsum *= invl;
+        if (!seen) {  // the round's output is v_i itself
+          const unsigned char* vrow = vb + (posq * D + 4 * g) * 2;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint2 x = *(const uint2*)(vrow + 32 * dt);
+            const uint2 z = *(const uint2*)(drow + 32 * dt);
+            dsum = fmaf(lo(x.x), lo(z.x), dsum);
+            dsum = fmaf(hi(x.x), hi(z.x), dsum);
+            dsum = fmaf(lo(x.y), lo(z.y), dsum);
+            dsum = fmaf(hi(x.y), hi(z.y), dsum);
+          }
+        }
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
+        if (g == 0) o[seg * L + posq] = dsum;
+      } else if constexpr (sizeof(OT) == 2) {
         // fp16: tiles t, t + 1 packed, odd and even 16-lane rows swapped, so
         // lane group g stores dims 16(t + g%2) + 8(g/2) + 0..7 (16 bytes)
         uint32_t pk[DT][2];
@@ -385,35 +422,35 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_at
 constexpr int kRangeChunks = 16;
 constexpr int kResidentBlocks = 256;
 
-template <int D, bool CAUSAL, int NS, bool DD, typename OT>
+template <int D, bool CAUSAL, int NS, bool DD, typename OT, bool DOT>
 void launch_one(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                 const float* knorm, const uint16_t* bkt, const int32_t* inv, OT* o, float* lse,
-                hipStream_t s) {
+                const void* dout, hipStream_t s) {
   constexpr int shmem = VLds<D, NS, DD>::kBytes;
   static bool configured[kMaxDevices] = {};
   if (first_on_device(configured)) {
-    (void)hipFuncSetAttribute((const void*)k_attend_var<D, CAUSAL, NS, DD, OT>,
+    (void)hipFuncSetAttribute((const void*)k_attend_var<D, CAUSAL, NS, DD, OT, DOT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   }
   const int64_t nseg = p.nseg();
   const walks::RangeShape sh =
       walks::range_shape(p.L / kChunk, nseg, p.R, kRangeChunks, kResidentBlocks);
-  hipLaunchKernelGGL((k_attend_var<D, CAUSAL, NS, DD, OT>), dim3((unsigned)sh.blocks),
+  hipLaunchKernelGGL((k_attend_var<D, CAUSAL, NS, DD, OT, DOT>), dim3((unsigned)sh.blocks),
                      dim3(kThreads), shmem, s, (const unsigned char*)qk,
                      (const unsigned char*)v, perm, knorm, bkt, inv, o, lse, p.L, p.R,
                      (int)nseg, sh.per, sh.ranges, sh.group_segs, p.o_seg_rows(),
-                     p.flags & kVariantFlags);
+                     p.flags & kVariantFlags, (const unsigned char*)dout);
 }
 
-template <int D, typename OT>
+template <int D, typename OT, bool DOT = false>
 void launch_d(const Problem& p, const void* qk, const void* v, const int32_t* perm,
               const float* knorm, const uint16_t* bkt, const int32_t* inv, OT* o, float* lse,
-              hipStream_t s) {
+              hipStream_t s, const void* dout = nullptr) {
   const bool ahead = (p.flags & LSH_ATTN_FLAG_LOOK_AHEAD) != 0;
   const bool dd = (p.flags & LSH_ATTN_FLAG_DEDUP) != 0;
   auto go = [&](auto causal, auto ns, auto ddv) {
-    launch_one<D, decltype(causal)::value, decltype(ns)::value, decltype(ddv)::value, OT>(
-        p, qk, v, perm, knorm, bkt, inv, o, lse, s);
+    launch_one<D, decltype(causal)::value, decltype(ns)::value, decltype(ddv)::value, OT, DOT>(
+        p, qk, v, perm, knorm, bkt, inv, o, lse, dout, s);
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -448,6 +485,15 @@ hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const vo
     if (p.d == 64) launch_d<64>(p, qk, v, perm, knorm, buckets, inv, (float*)o, lse, s);
     else launch_d<128>(p, qk, v, perm, knorm, buckets, inv, (float*)o, lse, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_variant_dot(const Problem& p, const void* qk, const void* v,
+                                     const int32_t* perm, const float* knorm, const void* dout,
+                                     const uint16_t* buckets, const int32_t* inv, float* od,
+                                     float* lse, hipStream_t s) {
+  if (p.d == 64) launch_d<64, float, true>(p, qk, v, perm, knorm, buckets, inv, od, lse, s, dout);
+  else launch_d<128, float, true>(p, qk, v, perm, knorm, buckets, inv, od, lse, s, dout);
   return hipGetLastError();
 }
 

@@ -723,7 +723,7 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
   const int64_t rpb = 256 / (D / 8);
   const int64_t nt = p.n_token_heads(), nr = p.n_rows();
   const dim3 gt((unsigned)((nt + rpb - 1) / rpb)), gr((unsigned)((nr + rpb - 1) / rpb));
-  if (bwd_mfma_supported(p))
+  if (bwd_recompute_dot(p))
     hipLaunchKernelGGL(k_bwd_rows_dot, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, b.od,
                        b.lse, b.w, b.cq, b.wself, p.L, p.R, nt);
   else
@@ -796,14 +796,20 @@ hipError_t launch_backward(const Problem& p, const void* qk, const void* v, cons
     hipLaunchKernelGGL(k_bwd_bucket16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        buckets, bk16, n);
   }
+  if (p.flags & LSH_ATTN_FLAG_DEDUP) e = launch_inverse_perm(p, perm, inv, s);
+  if (e != hipSuccess) return e;
   if (bwd_mfma_supported(p)) {
     e = launch_key_norms(p, qk, knorm, s);
     if (e == hipSuccess)
       e = launch_attend_mfma_dot(p, qk, v, perm, knorm, dout, bk16, b.od, b.lse, s);
+  } else if (bwd_recompute_dot(p)) {
+    // look-ahead, de-duplication: the variant kernel reduced to dout . o_r
+    e = launch_key_norms(p, qk, knorm, s);
+    if (e == hipSuccess)
+      e = launch_attend_variant_dot(p, qk, v, perm, knorm, dout, bk16, inv, b.od, b.lse, s);
   } else {
     // fp32 rows from the plain kernel, which takes every variant reading
-    if (p.flags & LSH_ATTN_FLAG_DEDUP) e = launch_inverse_perm(p, perm, inv, s);
-    if (e == hipSuccess) e = launch_attend_plain(p, qk, v, perm, bk16, inv, b.o32, b.lse, s);
+    e = launch_attend_plain(p, qk, v, perm, bk16, inv, b.o32, b.lse, s);
   }
   if (e != hipSuccess) return e;
   if (ev) (void)hipEventRecord(ev[1], s);

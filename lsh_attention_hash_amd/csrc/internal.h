@@ -126,6 +126,13 @@ hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const vo
                                       const int32_t* perm, const float* knorm,
                                       const uint16_t* buckets, const int32_t* inv, void* o,
                                       float* lse, hipStream_t s);
+// the same kernels in the backward's recomputation form: od [seg, L] receives
+// dout . o_r per query (dout . v_i for a query that saw only itself), lse the
+// per-round logsumexps
+hipError_t launch_attend_variant_dot(const Problem& p, const void* qk, const void* v,
+                                     const int32_t* perm, const float* knorm, const void* dout,
+                                     const uint16_t* buckets, const int32_t* inv, float* od,
+                                     float* lse, hipStream_t s);
 // inv[seg, perm[seg, s]] = s
 hipError_t launch_inverse_perm(const Problem& p, const int32_t* perm, int32_t* inv, hipStream_t s);
 // the plain chunk attention (any shape, every variant reading) with fp32
@@ -207,11 +214,17 @@ inline bool round_outputs_half(const Problem& p) {
 
 // The backward's products run on matrix cores on the matrix-core attention's
 // shapes for the default reading and the unit-query and same-bucket readings;
-// the look-ahead and de-duplicated readings take the plain kernels (fp32
-// per-round rows).
+// the look-ahead and de-duplicated readings take the plain kernels.
 inline bool bwd_mfma_supported(const Problem& p) {
   return attend_mfma_supported(p) &&
          !(p.flags & (LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_DEDUP));
+}
+// The backward's recomputation runs on matrix cores, reduced to dout . o_r per
+// query (no per-round rows), wherever a matrix-core forward kernel takes the
+// reading: the default kernel with the matrix-core products, the variant
+// kernel before the plain products (look-ahead, de-duplication).
+inline bool bwd_recompute_dot(const Problem& p) {
+  return bwd_mfma_supported(p) || attend_variant_mfma_supported(p);
 }
 
 // The backward's per-round gradient rows (dqk_r, dv_r) on the matrix-core path

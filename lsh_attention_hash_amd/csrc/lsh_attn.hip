@@ -194,8 +194,8 @@ int lsh_attn_create(const lsh_attn_config_t* cfg, lsh_attn_t* handle) {
   if (ok && lsh::hash_mfma_supported(p)) w.hash.n_cu = device_cus(h->device);
   if (ok && (p.flags & LSH_ATTN_FLAG_BACKWARD)) {
     lsh::BwdWorkspace& b = h->bw;
-    ok = (lsh::bwd_mfma_supported(p) ? alloc(&b.od, rows * 4, t)
-                                     : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
+    ok = (lsh::bwd_recompute_dot(p) ? alloc(&b.od, rows * 4, t)
+                                    : alloc(&b.o32, p.nseg() * p.o_seg_rows() * p.d * 4, t)) &&
          alloc(&b.lse, rows * 4, t) &&
          alloc(&b.w, rows * 4, t) && alloc(&b.cq, p.n_token_heads() * 4, t) &&
          alloc(&b.wself, p.n_token_heads() * 4, t) &&
