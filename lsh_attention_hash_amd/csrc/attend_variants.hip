@@ -29,6 +29,7 @@
 // dout(i) . o_r(i) instead, as in the default kernel's DOT form.
 #include <type_traits>
 
+#include "dedup_lanes.h"
 #include "dtype.h"
 #include "internal.h"
 #include "rows_lds.h"
@@ -51,7 +52,6 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kBoundLimit = 60.0f;
-constexpr int kMaxDedupRounds = 8;
 
 template <int D, int NS, bool DD>
 struct VLds {
@@ -76,10 +76,8 @@ struct VRegs {
   uint4 k[4], v[4];
   int pos, bk;
   float n2;
-  uint32_t cid[kMaxDedupRounds / 2], cbk[kMaxDedupRounds / 2];  // u16 lanes
+  uint32_t cid[dedup::kMaxRounds / 2], cbk[dedup::kMaxRounds / 2];  // u16 lanes
 };
-
-typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float sat16(float x) { return fminf(fmaxf(x, -65504.0f), 65504.0f); }
 
@@ -139,23 +137,9 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_at
       r.pos = pn[t];
       r.n2 = knorm[row0 + r.pos];
       if (sb) r.bk = bkt[seg * L + r.pos];
-      if (dd) {
-        // lanes past R hold 0x8000, which no query lane (0 there) is near
-#pragma unroll
-        for (int u = 0; u < kMaxDedupRounds; u += 2) {
-          uint32_t cw = 0x80008000u, bw = 0u;
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            if (u + h < R) {
-              const int64_t base = (bh * R + u + h) * L + r.pos;
-              const uint32_t cc = (uint32_t)(inv[base] / kChunk) & 0xFFFFu;
-              cw = (cw & ~(0xFFFFu << (16 * h))) | (cc << (16 * h));
-              if (sb) bw |= (uint32_t)bkt[base] << (16 * h);
-            }
-          r.cid[u / 2] = cw;
-          r.cbk[u / 2] = bw;
-        }
-      }
+      if (dd)
+        dedup::row_lanes(inv + bh * R * L, bkt + bh * R * L, R, L, kChunk, r.pos, sb, r.cid,
+                         r.cbk);
     }
   };
   auto stage = [&](const VRegs& r, int sl) {
@@ -214,16 +198,12 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_at
     }
     const int bq = sb ? kbk[cur * kChunk + q] : 0;
     // the query's chunks and buckets over the rounds (lanes past R: 0)
-    uint32_t qc[kMaxDedupRounds / 2] = {0u, 0u, 0u, 0u}, qb[kMaxDedupRounds / 2] = {0u, 0u, 0u, 0u};
+    uint32_t qc[dedup::kMaxRounds / 2] = {0u, 0u, 0u, 0u}, qb[dedup::kMaxRounds / 2] = {0u, 0u, 0u, 0u};
     if (dd) {
       const uint4 c4 = kcid[cur * kChunk + q], b4 = kcbk[cur * kChunk + q];
-      const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w}, bw[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int k = 0; k < kMaxDedupRounds / 2; ++k) {
-        const uint32_t keep = 2 * k + 1 < R ? 0xFFFFFFFFu : (2 * k < R ? 0xFFFFu : 0u);
-        qc[k] = cw[k] & keep;
-        qb[k] = bw[k];
-      }
+      const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
+      dedup::query_lanes(cw, R, qc);
+      qb[0] = b4.x, qb[1] = b4.y, qb[2] = b4.z, qb[3] = b4.w;
     }
     bf16x8_t qf[KS];
     {
@@ -260,32 +240,14 @@ __attribute__((amdgpu_waves_per_eu(NS == 2 ? 2 : 1, NS == 2 ? 2 : 1))) void k_at
         mk[b] = absent | (CAUSAL ? kpv[b] >= posq : kpv[b] == posq) | (sb && kbv[b] != bq);
     };
     // log2 N for key kk of slot sl: the rounds whose window (and bucket) give
-    // it to this query. Two rounds per 32-bit word (u16 lanes): the chunk
-    // difference d is in the window when d + 1 <= 1 (2 looking ahead), taken
-    // as a saturating subtraction that is 0 exactly then; a bucket mismatch
-    // makes the lane nonzero too; the nonzero lanes are the rounds that do
-    // not give the pair.
+    // it to this query
     auto log2_shared = [&](int sl, int kk) -> float {
       const uint4 c4 = kcid[sl * kChunk + kk];
       const uint32_t cw[4] = {c4.x, c4.y, c4.z, c4.w};
       uint4 b4 = {0u, 0u, 0u, 0u};
       if (sb) b4 = kcbk[sl * kChunk + kk];
       const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
-      const unsigned short lim = la ? 2 : 1;
-      const u16x2_t one2 = {1, 1}, lim2 = {lim, lim};
-      uint32_t out = 0u;
-      int lanes = 0;
-#pragma unroll
-      for (int k = 0; k < kMaxDedupRounds / 2; ++k) {
-        if (2 * k >= R) break;
-        const u16x2_t d = __builtin_bit_cast(u16x2_t, cw[k]) - __builtin_bit_cast(u16x2_t, qc[k]);
-        u16x2_t y = __builtin_elementwise_sub_sat(d + one2, lim2);
-        if (sb) y |= __builtin_bit_cast(u16x2_t, bw[k] ^ qb[k]);
-        y = __builtin_elementwise_min(y, one2);
-        out = __builtin_amdgcn_udot2(y, one2, out, false);
-        lanes += 2;
-      }
-      return __log2f((float)max(lanes - (int)out, 1));
+      return dedup::log2_rounds(qc, qb, cw, bw, R, la, sb);
     };
     if (__ballot(mq > kBoundLimit) != 0ull) {
       float mx = -INFINITY;
@@ -471,7 +433,7 @@ bool attend_variant_mfma_supported(const Problem& p) {
   // (the de-duplication compares chunks mod 2^16: at most 32768 chunks)
   return p.dtype == LSH_ATTN_BF16 && p.m == kChunk && (p.d == 64 || p.d == 128) &&
          (p.flags & kVariantFlags) &&
-         (!(p.flags & LSH_ATTN_FLAG_DEDUP) || (p.R <= kMaxDedupRounds && p.L / kChunk <= 32768));
+         (!(p.flags & LSH_ATTN_FLAG_DEDUP) || (p.R <= dedup::kMaxRounds && p.L / kChunk <= 32768));
 }
 
 hipError_t launch_attend_variant_mfma(const Problem& p, const void* qk, const void* v,

@@ -760,7 +760,9 @@ void launch_t(const Problem& p, const void* qk, const void* v, const int32_t* pe
   }
   const int vf = p.flags & kVariantFlags;
   const dim3 gq((unsigned)(p.nseg() * (p.L / p.m) * ((p.m + BT<D>::kQB - 1) / BT<D>::kQB)));
-  if (p.causal) {
+  if (bwd_recompute_dot(p)) {  // look-ahead, de-duplication: products on matrix cores
+    (void)launch_backward_var_mfma(p, qk, v, perm, dout, knorm, bk16, inv, b, s);
+  } else if (p.causal) {
     hipLaunchKernelGGL((k_bwd_dq_tiled<D, T, true>), gq, dim3(256), 0, s, (const T*)qk,
                        (const T*)v, (const T*)dout, perm, b.lse, b.w, b.cq, b.dq, p.L, p.m, p.R,
                        vf, bk16, inv);

@@ -184,6 +184,16 @@ hipError_t launch_backward_mfma(const Problem& p, const void* qk, const void* v,
                                 const int32_t* perm, const void* dout, const float* knorm,
                                 const uint16_t* buckets, BwdWorkspace& b, hipStream_t s);
 
+// the per-round gradient products of the look-ahead and de-duplicated
+// readings on matrix cores (attend_variant_mfma_supported shapes): fp32 rows
+// b.dq (dq, or the unit query's with NORM_QUERIES), b.dk (dkhat), b.dv, as the
+// plain products write them; buckets [seg, L] read with SAME_BUCKET, inv
+// [seg, L] with DEDUP
+hipError_t launch_backward_var_mfma(const Problem& p, const void* qk, const void* v,
+                                    const int32_t* perm, const void* dout, const float* knorm,
+                                    const uint16_t* buckets, const int32_t* inv,
+                                    BwdWorkspace& b, hipStream_t s);
+
 // The variant readings (flags); the default matrix-core attention takes none
 // of them (attend_variants.hip does).
 constexpr int kVariantFlags = LSH_ATTN_FLAG_LOOK_AHEAD | LSH_ATTN_FLAG_SAME_BUCKET |

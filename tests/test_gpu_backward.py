@@ -274,6 +274,10 @@ VAR_BWD = [
     (W("c4k", batch=1, heads=1, seq_len=512, n_buckets=8, n_rounds=3, causal=False),
      dict(look_ahead=True, dedup=True)),
     (W("text64k", batch=1, heads=2, seq_len=640, n_buckets=8, n_rounds=3, causal=True), _ALLV),
+    (W("text64k", batch=1, heads=2, seq_len=1280, n_buckets=16, n_rounds=2, causal=True),
+     dict(look_ahead=True)),
+    (W("text64k", batch=1, heads=1, seq_len=1024, n_buckets=8, n_rounds=4, causal=False),
+     dict(dedup=True, same_bucket=True)),
     (W("tiny", n_rounds=2), _ALLV),  # fp32
     # 9 rounds: de-duplication past the matrix-core kernel's 8, plain kernels at bf16
     (W("c4k", batch=1, heads=1, seq_len=256, n_buckets=4, n_rounds=9, causal=True),
@@ -290,20 +294,22 @@ def _bound_plain(ref, mag, w):
     return u * np.abs(ref) + c * mag + 1e-30
 
 
-def _bound_variant_dot(name, ref, mag, w):
+def _bound_variant_mfma(name, ref, mag, w):
     """Look-ahead and de-duplication at bf16, chunk 64: the recomputation
     runs on the variant matrix-core kernel, reduced to dout . o_r per query,
-    and the products on the plain fp32 kernels. The recomputed lse is an fp32
-    sum of unrounded exponentials (fp32-level error, as on the plain path),
-    but o_r weights the values by bf16(p_j) normalised by their own sum: each
-    normalised weight is within 2u/(1-u) of P_ij, so |od_r' - od_r| <=
-    2u/(1-u) sum_j P_ij |dout . v_j| and |cq' - cq| <= 2u/(1-u) E_i; in dS
-    that is at most wP 2u/(1-u) E_i <= u/(1-u) A_ij. dv does not use cq:
-        |dv - dv_ref|   <= u |dv_ref|  + c_plain m_dv,
-        |dqk - dqk_ref| <= u |dqk_ref| + (u/(1-u) + c_plain) m_dqk,
-    with c_plain = (6 chunk_len + 2 head_dim) 2^-24 the plain path's."""
+    and the products on their own matrix-core kernels with fp32 per-round
+    rows. The recomputed lse is an fp32 sum of unrounded exponentials
+    (fp32-level error), but o_r weights the values by bf16(p_j) normalised by
+    their own sum: each normalised weight is within 2u/(1-u) of P_ij, so
+    |od_r' - od_r| <= 2u/(1-u) sum_j P_ij |dout . v_j| and |cq' - cq| <=
+    2u/(1-u) E_i; in dS that is at most wP 2u/(1-u) E_i <= u/(1-u) A_ij. The
+    products round wP and dS to bf16 (u of each term), and sum in fp32:
+        |dv - dv_ref|   <= u |dv_ref|  + (u + c_fp32) m_dv,
+        |dqk - dqk_ref| <= u |dqk_ref| + (u + u/(1-u) + c_fp32) m_dqk,
+    with c_fp32 = (6 chunk_len + 2 head_dim) 2^-24, the plain path's constant
+    for its fp32 logits, exponentials and sums."""
     u = 2.0 ** -8
-    c = (6 * w.chunk_len + 2 * w.head_dim) * 2.0 ** -24
+    c = u + (6 * w.chunk_len + 2 * w.head_dim) * 2.0 ** -24
     if name == "dqk":
         c += u / (1 - u)
     return u * np.abs(ref) + c * mag + 1e-30
@@ -355,9 +361,9 @@ def _variant_backward_check(w, kw, inp):
     c = oracle.config(w, variant=variant)
     rq, rv = oracle.backward(c, inp.qk, inp.v, perm, dout, buckets=bk)
     mq, mv = oracle.backward_magnitudes(c, inp.qk, inp.v, perm, dout, buckets=bk)
-    # which kernels ran: matrix-core recomputation and products (default
-    # kernel's readings), matrix-core recomputation and plain products
-    # (look-ahead, de-duplication), or plain kernels throughout
+    # which kernels ran: the default kernel's matrix-core recomputation and
+    # fused products (its readings), the variant kernels' (look-ahead,
+    # de-duplication), or plain kernels throughout
     mfma_shape = w.dtype == "bf16" and w.chunk_len == 64 and w.head_dim in (64, 128)
     la_dd = kw.get("look_ahead", False) or kw.get("dedup", False)
     mfma = mfma_shape and not la_dd
@@ -367,7 +373,7 @@ def _variant_backward_check(w, kw, inp):
         if mfma:
             bound = _bound(name, ref, mag, w)
         elif var_dot:
-            bound = _bound_variant_dot(name, ref, mag, w)
+            bound = _bound_variant_mfma(name, ref, mag, w)
         else:
             bound = _bound_plain(ref, mag, w)
         worst = float((err / bound).max())
