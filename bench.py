@@ -103,32 +103,38 @@ def algorithmic_units(w, out_dtype: str, round_bytes: int = 2, stats=None, windo
     }
 
 
-def backward_units(w, out_dtype: str, grad_row_bytes: int = 2):
+def backward_units(w, out_dtype: str, grad_row_bytes: int = 2, window_chunks: int = 2,
+                   split_rows: bool = False):
     """Per-launch algorithmic work of each backward stage (matrix-core path:
     bf16 inputs, per-round gradient rows of grad_row_bytes per element: fp16
     by default, fp32 with --fp32-round-outputs). N token-heads, R rounds, d, m
-    as above; a round's window is 2m keys per query. Rows are read through the
-    permutation once per (round, slot); the per-round gradients are rows at
-    original positions."""
+    as above; a round's window is window_chunks * m keys per query (3 with the
+    look-ahead reading). Rows are read through the permutation once per
+    (round, slot); the per-round gradients are rows at original positions.
+    split_rows: the look-ahead and de-duplicated readings' products write dq
+    and dkhat as separate fp32 rows (three per round, not two), which the
+    reduction reads back with the round's lse and weight."""
     N = w.batch * w.heads * w.seq_len
     R, d, m = w.n_rounds, w.head_dim, w.chunk_len
     e, eo, g = esize(w.dtype), esize(out_dtype), grad_row_bytes
+    nrows = 3 if split_rows else 2
     return {
         # attention at the permutation (as the forward's) with dout read per
         # query-round; per query-round lse and dout . o_r written; key norms
-        "recompute": {"flops": N * R * 4 * d * 2 * m,
+        "recompute": {"flops": N * R * 4 * d * window_chunks * m,
                       "bytes": N * R * (3 * d * e + 4 + 4 + 4) + N * (d * e + 4)},
         # lse and dout . o_r read and the round weight written per round; dout . out
         # and the self-only weight written per token-head
         "rows": {"bytes": N * R * (4 + 4 + 4) + N * (4 + 4)},
-        # per (round, slot), over the 2m-key window of each query: S, dP once,
-        # then dQ, dkhat and dv; qk, v, dout rows, perm, lse, weight,
-        # dout . out and key norm read once; dqk and dv rows written
-        "products": {"flops": N * R * 5 * 2 * d * 2 * m,
-                     "bytes": N * R * (3 * d * e + 5 * 4 + 2 * d * g)},
-        # R rounds of dqk and dv rows and the self-only weight read; dqk and dv
-        # written (dout is read only for rows with a self-only round)
-        "reduce": {"bytes": N * R * 2 * d * g + N * 4 + N * 2 * d * eo},
+        # per (round, slot), over the window of each query: S, dP once, then
+        # dQ, dkhat and dv; qk, v, dout rows, perm, lse, weight, dout . out and
+        # key norm read once; the per-round gradient rows written
+        "products": {"flops": N * R * 5 * 2 * d * window_chunks * m,
+                     "bytes": N * R * (3 * d * e + 5 * 4 + nrows * d * g)},
+        # R rounds of gradient rows (and, split, lse and weight) read; dqk and
+        # dv written (dout is read only for rows with a self-only round)
+        "reduce": {"bytes": N * R * (nrows * d * g + (8 if split_rows else 0)) + N * 4
+                   + N * 2 * d * eo},
     }
 
 
@@ -393,8 +399,10 @@ def cpu_baseline_backward(w, inp, heads: int):
             "seconds": round(t, 3), "threads_available": threads}
 
 
-def main_backward(args, w, inp, op_kw):
-    """The --backward line (see the module docstring)."""
+def main_backward(args, w, inp, op_kw, variants=()):
+    """The --backward line (see the module docstring); with --variants, the
+    backward of those readings (the same-bucket mask takes the forward's
+    bucket ids)."""
     import numpy as np
     import torch
 
@@ -410,18 +418,21 @@ def main_backward(args, w, inp, op_kw):
         v = torch.from_numpy(inp.v).to(dev)
     rot = None if inp.rotations is None else torch.from_numpy(inp.rotations).to(dev)
     op = lat.LSHAttention(w.batch, w.heads, w.seq_len, w.head_dim, w.n_buckets, w.n_rounds,
-                          w.chunk_len, w.causal, dtype=tdt[w.dtype], backward=True, **op_kw)
-    _, ex = op(qk, v, rot, return_perm=True)
+                          w.chunk_len, w.causal, dtype=tdt[w.dtype], backward=True, **op_kw,
+                          **{x: True for x in variants})
+    sb = "same_bucket" in variants
+    _, ex = op(qk, v, rot, return_perm=True, return_buckets=sb)
     perm = ex["perm"]
+    bk = ex["buckets"] if sb else None
     g = torch.Generator(device="cpu").manual_seed(5)
     dout = torch.randn((w.batch, w.heads, w.seq_len, w.head_dim), generator=g).to(
         tdt[w.dtype]).to(dev)
     dqk = torch.empty_like(qk)
     dv = torch.empty_like(v)
     stream = torch.cuda.current_stream()
-    settled = settle(lambda: op.backward(qk, v, perm, dout, dqk, dv), args.settle_ms)
+    settled = settle(lambda: op.backward(qk, v, perm, dout, dqk, dv, buckets=bk), args.settle_ms)
     for _ in range(args.warmup):
-        op.backward(qk, v, perm, dout, dqk, dv)
+        op.backward(qk, v, perm, dout, dqk, dv, buckets=bk)
     torch.cuda.synchronize()
     op.set_timing(args.steps)
     start = torch.cuda.Event(enable_timing=True)
@@ -430,7 +441,7 @@ def main_backward(args, w, inp, op_kw):
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        op.backward(qk, v, perm, dout, dqk, dv)
+        op.backward(qk, v, perm, dout, dqk, dv, buckets=bk)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -440,11 +451,15 @@ def main_backward(args, w, inp, op_kw):
     op.close()
     calibration_copy(args.calib_copy_mib, dev)
 
-    units = backward_units(w, w.dtype, 4 if args.fp32_round_outputs else 2)
+    # the look-ahead and de-duplicated readings: their own recomputation form
+    # and product kernels, fp32 per-round rows of dq, dkhat and dv
+    split = bool(set(variants) & {"look_ahead", "dedup"})
+    units = backward_units(w, w.dtype, 4 if (args.fp32_round_outputs or split) else 2,
+                           3 if "look_ahead" in variants else 2, split)
     single = {k: v_ for k, v_ in stage_avg.items() if k in BWD_STAGE_KERNEL}
     dominant = max(single, key=single.get)
     traffic = None
-    if os.path.exists(args.traffic_json):
+    if os.path.exists(args.traffic_json) and not variants:
         try:
             with open(args.traffic_json) as f:
                 entry = json.load(f).get(args.workload + ":backward", {}).get(dominant)
@@ -453,6 +468,10 @@ def main_backward(args, w, inp, op_kw):
         except (OSError, ValueError):
             traffic = None
     rl = roofline(dominant, units, stage_avg[dominant], traffic)
+    if split and dominant == "products":
+        rl["kernel"] = "k_bwd_var_dq + k_bwd_var_dkv"
+    elif split and dominant == "reduce":
+        rl["kernel"] = "k_bwd_reduce"
     per_stage = {}
     for k, t in stage_avg.items():
         per_stage[k] = {"ms": round(t, 5)}
@@ -481,13 +500,14 @@ def main_backward(args, w, inp, op_kw):
                    "qk_v_dtype": w.dtype,
                    "inputs": f"{w.kind} seeded (qk {1000 + w.seed_base}, v {2000 + w.seed_base},"
                              f" R {3000 + w.seed_base}); dout torch seed 5, standard normal",
-                   "per_round_gradients": "fp32" if args.fp32_round_outputs else "fp16"},
+                   "per_round_gradients": "fp32" if (args.fp32_round_outputs or split) else "fp16",
+                   "variants": list(variants)},
         "roofline": rl,
         "stages": per_stage,
         "settle": settled,
         "wall_s_timed": round(wall, 4),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not variants:
         heads = args.cpu_heads or max(1, min(w.heads, len(os.sched_getaffinity(0)) // 4))
         res["cpu_baseline"] = cpu_baseline_backward(w, inp, heads)
     print(json.dumps(res), flush=True)
@@ -632,8 +652,9 @@ def main():
                     help="time the forward from a layer input x [B, L, H*d] with the shared-QK "
                          "and value projections (lsh_attn_forward_x); model_dim = H * d")
     ap.add_argument("--variants", default="",
-                    help="comma list of variant readings for the forward: look_ahead, "
-                         "same_bucket, norm_queries, dedup (default: none)")
+                    help="comma list of variant readings for the forward (or, with "
+                         "--backward, the backward): look_ahead, same_bucket, norm_queries, "
+                         "dedup (default: none)")
     ap.add_argument("--ffn", action="store_true",
                     help="time the chunked feed-forward (d_model = H * d, d_ff = 4 d_model) "
                          "over the workload's B * L rows instead of the attention")
@@ -691,7 +712,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.backward:
         main_backward(args, w, inp, {"separate_gather": args.separate_gather,
-                                     "fp32_round_outputs": args.fp32_round_outputs})
+                                     "fp32_round_outputs": args.fp32_round_outputs}, variants)
         return
     if w.dtype == "bf16":
         qk = torch.from_numpy(inp.qk_bits.view(np.int16)).to(dev).view(torch.bfloat16)

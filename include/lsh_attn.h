@@ -202,8 +202,10 @@ int lsh_attn_backward(lsh_attn_t handle, const void* qk, const void* v, const in
  * section 2.2). With LSH_ATTN_FLAG_NORM_QUERIES the unit query q / |q| takes
  * the same normalisation Jacobian as the unit key of that row. Unit queries and
  * the same-bucket mask run on the matrix-core path of the default reading; the
- * look-ahead and de-duplicated readings on the plain kernels (fp32 per-round
- * rows).
+ * look-ahead and de-duplicated readings on matrix-core kernels of their own
+ * (fp32 per-round gradient rows) where the forward's variant kernel takes the
+ * shape (bf16, chunk_len 64, d in {64, 128}, with DEDUP at most 8 rounds), on
+ * the plain kernels otherwise.
  *   buckets   [B, H, n_rounds, L]   int32  (read only): the forward's buckets
  *             output; required with LSH_ATTN_FLAG_SAME_BUCKET (INVALID_ARG if
  *             null then), may be null otherwise
