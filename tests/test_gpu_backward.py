@@ -278,6 +278,14 @@ VAR_BWD = [
      dict(look_ahead=True)),
     (W("text64k", batch=1, heads=1, seq_len=1024, n_buckets=8, n_rounds=4, causal=False),
      dict(dedup=True, same_bucket=True)),
+    # one chunk: the look-ahead window is the chunk itself
+    (W("c4k", batch=1, heads=2, seq_len=64, n_buckets=4, n_rounds=2, causal=True),
+     dict(look_ahead=True)),
+    # two chunks, 8 rounds: the most the matrix-core de-duplication takes
+    (W("text64k", batch=1, heads=1, seq_len=128, n_buckets=4, n_rounds=8, causal=False),
+     dict(look_ahead=True, dedup=True)),
+    (W("image12k", batch=2, heads=1, seq_len=768, n_buckets=8, n_rounds=2, causal=True),
+     dict(look_ahead=True, same_bucket=True, norm_queries=True)),
     (W("tiny", n_rounds=2), _ALLV),  # fp32
     # 9 rounds: de-duplication past the matrix-core kernel's 8, plain kernels at bf16
     (W("c4k", batch=1, heads=1, seq_len=256, n_buckets=4, n_rounds=9, causal=True),
