@@ -23,6 +23,19 @@
 //            positions at a time in position order.
 // Buckets are handled in LDS windows of at most kLdsBins ids, so any
 // n_buckets up to 65536 works with a bounded LDS footprint.
+//
+// Segment form (L <= 16384, n_buckets <= 1024): one workgroup of 16 waves
+// takes a whole segment in one launch, wave w owning the positions
+// [w S, (w + 1) S), S = L / 16 rounded up to 64-position steps. The wave
+// holds its bucket ids in registers, counts them into its own row of a
+// [16][n_buckets] LDS table, the table becomes per-wave first slots (an
+// exclusive scan of the bucket totals, then a prefix over the waves), and the
+// wave assigns slots 64 positions at a time in position order as the scatter
+// above does. Longer segments keep the tiled form: with one workgroup per
+// segment, the scattered 4-byte stores of a 65,536-position segment all issue
+// from one CU (Text-64K: 118 us against 34 us tiled).
+#include <type_traits>
+
 #include "internal.h"
 #include "walks.h"
 
@@ -226,17 +239,102 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scatter(
   }
 }
 
+constexpr int kSegThreads = 1024;
+constexpr int kSegWaves = kSegThreads / kWave;
+constexpr int kSegMaxBins = 1024;
+constexpr int kSegMaxL = 16384;
+
+// K: the most 64-position steps a wave takes (steps <= K)
+template <int K>
+__global__ __launch_bounds__(kSegThreads) void k_sort_segment(const uint16_t* __restrict__ buckets,
+                                                              int32_t* __restrict__ perm, int L,
+                                                              int nb, int nbits, int steps) {
+  extern __shared__ uint32_t off[];  // [kSegWaves][nb], then the wave sums
+  uint32_t* wsum = off + kSegWaves * nb;
+  const int64_t seg = blockIdx.x;
+  const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
+  const uint16_t* bk = buckets + seg * L;
+  int32_t* pm = perm + seg * L;
+  const int begin = w * steps * kWave;
+  for (int j = t; j < kSegWaves * nb; j += kSegThreads) off[j] = 0;
+  constexpr uint32_t kNone = 0xFFFFFFFFu;  // no position (past L)
+  uint32_t ids[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int e = begin + kWave * k + lane;
+    ids[k] = k < steps && e < L ? (uint32_t)bk[e] : kNone;
+  }
+  __syncthreads();
+  uint32_t* mine = off + w * nb;
+#pragma unroll
+  for (int k = 0; k < K; ++k)
+    if (ids[k] != kNone) atomicAdd(&mine[ids[k]], 1u);
+  __syncthreads();
+  // thread b: the bucket's total over the waves, its first slot (exclusive
+  // scan over the buckets), then each wave's first slot in it
+  uint32_t total = 0;
+  if (t < nb)
+    for (int ww = 0; ww < kSegWaves; ++ww) total += off[ww * nb + t];
+  uint32_t inc = total;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == kWave - 1) wsum[w] = inc;
+  __syncthreads();
+  uint32_t run = inc - total;
+  for (int ww = 0; ww < w; ++ww) run += wsum[ww];
+  if (t < nb)
+    for (int ww = 0; ww < kSegWaves; ++ww) {
+      const uint32_t n = off[ww * nb + t];
+      off[ww * nb + t] = run;
+      run += n;
+    }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (k >= steps) break;  // the same for every wave
+    const bool in = ids[k] != kNone;
+    const uint64_t peers = match_peers(ids[k], in, nbits);
+    if (in) {
+      const uint32_t slot = mine[ids[k]] + (uint32_t)__popcll(peers & below);
+      pm[slot] = begin + kWave * k + lane;
+    }
+    // all lanes have read the wave's slot above; the group's first lane
+    // advances it
+    if (in && lane == __builtin_ctzll(peers)) mine[ids[k]] += (uint32_t)__popcll(peers);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* counts,
                        int32_t* perm, hipStream_t s) {
+  int nbits = 0;
+  while ((1 << nbits) < p.nb) ++nbits;
+  if (p.L <= kSegMaxL && p.nb <= kSegMaxBins) {
+    const int steps = (p.L + kSegThreads - 1) / kSegThreads;  // per wave
+    const size_t shmem = ((size_t)kSegWaves * p.nb + kSegWaves) * 4;
+    auto go = [&](auto kk) {
+      constexpr int K = decltype(kk)::value;
+      static bool configured[kMaxDevices] = {};
+      if (first_on_device(configured))
+        (void)hipFuncSetAttribute((const void*)k_sort_segment<K>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (kSegWaves * kSegMaxBins + kSegWaves) * 4);
+      hipLaunchKernelGGL(k_sort_segment<K>, dim3((unsigned)p.nseg()), dim3(kSegThreads), shmem,
+                         s, buckets, perm, p.L, p.nb, nbits, steps);
+    };
+    go(std::integral_constant<int, kSegMaxL / kSegThreads>{});
+    return hipGetLastError();
+  }
   // counts: [seg][tiles][nb] tile counts (then their running sums), then the
   // totals and the first slots [seg][nb] of every bucket
   const int tiles = p.sort_tiles();
   uint32_t* totals = counts + p.nseg() * (int64_t)tiles * p.nb;
   uint32_t* start = totals + p.nseg() * (int64_t)p.nb;
-  int nbits = 0;
-  while ((1 << nbits) < p.nb) ++nbits;
   const dim3 grid((unsigned)(tiles * p.nseg()));
   const size_t window = (size_t)(p.nb < kLdsBins ? p.nb : kLdsBins);
   hipLaunchKernelGGL(k_sort_count, grid, dim3(kSortThreads), window * 4, s, buckets, counts, p.L,

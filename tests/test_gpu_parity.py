@@ -218,6 +218,28 @@ def test_sort_of_long_segments(L):
     check_perm(w, gb, gp)
 
 
+@pytest.mark.parametrize("L,nb", [(16384, 1024), (16320, 1000), (4096, 2), (1024, 1026)])
+def test_sort_segment_form(L, nb):
+    """Segments short enough for the one-launch sort (L <= 16384 with at most
+    1024 buckets: its longest segment and most buckets, a ragged last wave,
+    two buckets), and just past its bucket limit (the tiled form): the
+    permutation equal to the oracle's stable sort of the GPU's buckets."""
+    w = W("c4k", batch=1, heads=2, seq_len=L, n_buckets=nb, n_rounds=2, causal=False)
+    _say(f"[segment sort] {w}")
+    inp = workloads.make_inputs(w)
+    qk, v, rot = to_device(inp)
+    op = make_op(w)
+    try:
+        _, ex = op(qk, v, rot, return_buckets=True, return_perm=True)
+        torch.cuda.synchronize()
+        gb = ex["buckets"].cpu().numpy()
+        gp = ex["perm"].cpu().numpy()
+    finally:
+        op.close()
+    check_buckets(w, inp, gb)
+    check_perm(w, gb, gp)
+
+
 LARGE = [
     # d = 128: |q| ~ 1,450, Cauchy-Schwarz shift ~185 > 60: the true-max softmax
     (W("text64k", batch=1, heads=2, seq_len=2048, n_buckets=64, n_rounds=2, causal=True), 7, 0),
