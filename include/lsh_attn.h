@@ -69,10 +69,11 @@ enum {
    * reaches that magnitude need this flag. lsh_attn_get_stats counts the
    * values that reached the limit. */
   LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS = 2,
-  /* Also allocate the workspace of lsh_attn_backward: per position and round,
-   * 2 fp32 rows of head_dim on the matrix-core path (bf16, chunk_len 64, head_dim
-   * 64 or 128, neither LOOK_AHEAD nor DEDUP) or 4 on the other shapes and with
-   * those flags, plus 12 bytes; 4 bytes per position. */
+  /* Also allocate the workspace of lsh_attn_backward, per position and round:
+   * on the matrix-core shapes (bf16, chunk_len 64, head_dim 64 or 128) 2 rows
+   * of head_dim (fp16, or fp32 with LSH_ATTN_FLAG_FP32_ROUND_OUTPUTS), or 3
+   * fp32 rows with LOOK_AHEAD or DEDUP, plus 12 bytes; on the other shapes 4
+   * fp32 rows plus 8 bytes. Plus 8 bytes per position. */
   LSH_ATTN_FLAG_BACKWARD = 4,
   /* Variant readings of the window and the combination, each one the pages
    * also describe (the default, all off, is the previous chunk and the chunk
