@@ -279,9 +279,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_var_dq(
 }
 
 // -------------------------------------------------------------------------
-// dkhat and dv of the keys of chunk c (wave w: keys 16 w + lq)
+// dkhat and dv of the keys of chunk c (wave w: keys 16 w + lq). Two
+// workgroups per CU (75 KB of LDS each at d = 128) where the registers allow
+// it without spills: all but the de-duplicated form at d = 128.
 template <int D, bool DD>
-__global__ __launch_bounds__(kThreads) void k_bwd_var_dkv(
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DD && D == 128 ? 1 : 2, DD && D == 128 ? 1 : 2))) void k_bwd_var_dkv(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const unsigned char* __restrict__ dout, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
