@@ -25,6 +25,8 @@
 // of rows_lds.h), while the next chunk's rows are loaded into registers. The
 // masks are the forward's: self (and causal), the same-bucket mask, and for
 // DEDUP the logit lowered by log N_ij (dedup_lanes.h).
+#include <type_traits>
+
 #include "dedup_lanes.h"
 #include "dtype.h"
 #include "internal.h"
@@ -279,12 +281,15 @@ __global__ __launch_bounds__(kThreads) void k_bwd_var_dq(
 }
 
 // -------------------------------------------------------------------------
-// dkhat and dv of the keys of chunk c (wave w: keys 16 w + lq). Two
-// workgroups per CU (75 KB of LDS each at d = 128) where the registers allow
-// it without spills: all but the de-duplicated form at d = 128.
-template <int D, bool DD>
+// dkhat and dv of the keys of chunk c (wave w: keys 16 w + lq); SB: the
+// same-bucket mask (a template flag here: its per-query bucket lanes are what
+// the de-duplicated form at d = 128 cannot fit). Two workgroups per CU (75 KB
+// of LDS each at d = 128) where the registers allow it without spills: all
+// but the de-duplicated form with the same-bucket mask at d = 128.
+template <int D, bool DD, bool SB>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(DD && D == 128 ? 1 : 2, DD && D == 128 ? 1 : 2))) void k_bwd_var_dkv(
+__attribute__((amdgpu_waves_per_eu(DD && SB && D == 128 ? 1 : 2,
+                                   DD && SB && D == 128 ? 1 : 2))) void k_bwd_var_dkv(
     const unsigned char* __restrict__ qk, const unsigned char* __restrict__ v,
     const unsigned char* __restrict__ dout, const int32_t* __restrict__ perm,
     const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
@@ -304,7 +309,7 @@ __attribute__((amdgpu_waves_per_eu(DD && D == 128 ? 1 : 2, DD && D == 128 ? 1 : 
   const unsigned char* zb = dout + row0 * D * 2;
   const bool causal = (flags & kCausalFlag) != 0;
   const bool la = (flags & LSH_ATTN_FLAG_LOOK_AHEAD) != 0;
-  const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  constexpr bool sb = SB;
   const bool nq = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
   const int32_t* inv_bh = inv + bh * R * L;
   const uint16_t* bk_bh = bkt + bh * R * L;
@@ -438,7 +443,7 @@ __attribute__((amdgpu_waves_per_eu(DD && D == 128 ? 1 : 2, DD && D == 128 ? 1 : 
   }
 }
 
-template <int D, bool DD>
+template <int D, bool DD, bool SB>
 void launch_dd(const Problem& p, const void* qk, const void* v, const int32_t* perm,
                const void* dout, const float* knorm, const uint16_t* bkt, const int32_t* inv,
                BwdWorkspace& b, hipStream_t s) {
@@ -447,7 +452,7 @@ void launch_dd(const Problem& p, const void* qk, const void* v, const int32_t* p
   if (first_on_device(configured)) {
     (void)hipFuncSetAttribute((const void*)k_bwd_var_dq<D, DD>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, qbytes);
-    (void)hipFuncSetAttribute((const void*)k_bwd_var_dkv<D, DD>,
+    (void)hipFuncSetAttribute((const void*)k_bwd_var_dkv<D, DD, SB>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kbytes);
   }
   const dim3 grid((unsigned)(p.nseg() * (p.L / kChunk)));
@@ -456,7 +461,7 @@ void launch_dd(const Problem& p, const void* qk, const void* v, const int32_t* p
                      (const unsigned char*)qk, (const unsigned char*)v,
                      (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, bkt, inv, b.dq,
                      p.L, p.R, flags);
-  hipLaunchKernelGGL((k_bwd_var_dkv<D, DD>), grid, dim3(kThreads), kbytes, s,
+  hipLaunchKernelGGL((k_bwd_var_dkv<D, DD, SB>), grid, dim3(kThreads), kbytes, s,
                      (const unsigned char*)qk, (const unsigned char*)v,
                      (const unsigned char*)dout, perm, knorm, b.lse, b.w, b.cq, bkt, inv, b.dk,
                      b.dv, p.L, p.R, flags);
@@ -469,12 +474,21 @@ hipError_t launch_backward_var_mfma(const Problem& p, const void* qk, const void
                                     const uint16_t* buckets, const int32_t* inv,
                                     BwdWorkspace& b, hipStream_t s) {
   const bool dd = (p.flags & LSH_ATTN_FLAG_DEDUP) != 0;
+  const bool sb = (p.flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
+  auto go = [&](auto dv_, auto ddv, auto sbv) {
+    launch_dd<decltype(dv_)::value, decltype(ddv)::value, decltype(sbv)::value>(
+        p, qk, v, perm, dout, knorm, buckets, inv, b, s);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (p.d == 64) {
-    if (dd) launch_dd<64, true>(p, qk, v, perm, dout, knorm, buckets, inv, b, s);
-    else launch_dd<64, false>(p, qk, v, perm, dout, knorm, buckets, inv, b, s);
+    if (dd) sb ? go(D64{}, T{}, T{}) : go(D64{}, T{}, F{});
+    else sb ? go(D64{}, F{}, T{}) : go(D64{}, F{}, F{});
   } else {
-    if (dd) launch_dd<128, true>(p, qk, v, perm, dout, knorm, buckets, inv, b, s);
-    else launch_dd<128, false>(p, qk, v, perm, dout, knorm, buckets, inv, b, s);
+    if (dd) sb ? go(D128{}, T{}, T{}) : go(D128{}, T{}, F{});
+    else sb ? go(D128{}, F{}, T{}) : go(D128{}, F{}, F{});
   }
   return hipGetLastError();
 }
