@@ -24,18 +24,17 @@
 // Buckets are handled in LDS windows of at most kLdsBins ids, so any
 // n_buckets up to 65536 works with a bounded LDS footprint.
 //
-// Segment form (L <= 16384, n_buckets <= 1024): one workgroup of 16 waves
-// takes a whole segment in one launch, wave w owning the positions
-// [w S, (w + 1) S), S = L / 16 rounded up to 64-position steps. The wave
-// holds its bucket ids in registers, counts them into its own row of a
-// [16][n_buckets] LDS table, the table becomes per-wave first slots (an
-// exclusive scan of the bucket totals, then a prefix over the waves), and the
-// wave assigns slots 64 positions at a time in position order as the scatter
-// above does. Longer segments keep the tiled form: with one workgroup per
-// segment, the scattered 4-byte stores of a 65,536-position segment all issue
-// from one CU (Text-64K: 118 us against 34 us tiled).
-#include <type_traits>
-
+// Segment form (L <= 16384, n_buckets <= 1024): one launch, one workgroup
+// of 16 waves per segment. Wave w owns the positions [w S, (w + 1) S),
+// S = L / 16 rounded up to 64-position steps, holds their bucket ids in
+// registers, counts them into its own row of a [16][n_buckets] LDS table; the
+// table becomes per-wave first slots (an exclusive scan of the bucket totals,
+// then a prefix over the waves), and the wave assigns slots 64 positions at a
+// time in position order as the scatter above does, into an LDS copy of the
+// segment's permutation, which is then stored with coalesced writes
+// (scattered 4-byte global stores cost ~2.7 cycles each per CU). Longer
+// segments keep the tiled form: ranking costs ~100 vector instructions per
+// 64 positions, which the tiled form spreads over every CU.
 #include "internal.h"
 #include "walks.h"
 
@@ -243,31 +242,30 @@ constexpr int kSegThreads = 1024;
 constexpr int kSegWaves = kSegThreads / kWave;
 constexpr int kSegMaxBins = 1024;
 constexpr int kSegMaxL = 16384;
+constexpr int kSegMaxSteps = kSegMaxL / kSegThreads;  // 64-position steps per wave
 
-// K: the most 64-position steps a wave takes (steps <= K)
-template <int K>
 __global__ __launch_bounds__(kSegThreads) void k_sort_segment(const uint16_t* __restrict__ buckets,
                                                               int32_t* __restrict__ perm, int L,
                                                               int nb, int nbits, int steps) {
-  extern __shared__ uint32_t off[];  // [kSegWaves][nb], then the wave sums
+  extern __shared__ uint32_t off[];  // [kSegWaves][nb], the wave sums, the permutation
   uint32_t* wsum = off + kSegWaves * nb;
+  int32_t* slots = (int32_t*)(wsum + kSegWaves);
   const int64_t seg = blockIdx.x;
   const int t = threadIdx.x, w = t / kWave, lane = t % kWave;
   const uint16_t* bk = buckets + seg * L;
-  int32_t* pm = perm + seg * L;
   const int begin = w * steps * kWave;
   for (int j = t; j < kSegWaves * nb; j += kSegThreads) off[j] = 0;
   constexpr uint32_t kNone = 0xFFFFFFFFu;  // no position (past L)
-  uint32_t ids[K];
+  uint32_t ids[kSegMaxSteps];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
+  for (int k = 0; k < kSegMaxSteps; ++k) {
     const int e = begin + kWave * k + lane;
     ids[k] = k < steps && e < L ? (uint32_t)bk[e] : kNone;
   }
   __syncthreads();
   uint32_t* mine = off + w * nb;
 #pragma unroll
-  for (int k = 0; k < K; ++k)
+  for (int k = 0; k < kSegMaxSteps; ++k)
     if (ids[k] != kNone) atomicAdd(&mine[ids[k]], 1u);
   __syncthreads();
   // thread b: the bucket's total over the waves, its first slot (exclusive
@@ -294,18 +292,18 @@ __global__ __launch_bounds__(kSegThreads) void k_sort_segment(const uint16_t* __
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
+  for (int k = 0; k < kSegMaxSteps; ++k) {
     if (k >= steps) break;  // the same for every wave
     const bool in = ids[k] != kNone;
     const uint64_t peers = match_peers(ids[k], in, nbits);
-    if (in) {
-      const uint32_t slot = mine[ids[k]] + (uint32_t)__popcll(peers & below);
-      pm[slot] = begin + kWave * k + lane;
-    }
+    if (in) slots[mine[ids[k]] + (uint32_t)__popcll(peers & below)] = begin + kWave * k + lane;
     // all lanes have read the wave's slot above; the group's first lane
     // advances it
     if (in && lane == __builtin_ctzll(peers)) mine[ids[k]] += (uint32_t)__popcll(peers);
   }
+  __syncthreads();  // every slot holds its position
+  int32_t* pm = perm + seg * L;
+  for (int j = t; j < L; j += kSegThreads) pm[j] = slots[j];
 }
 
 }  // namespace
@@ -316,18 +314,14 @@ hipError_t launch_sort(const Problem& p, const uint16_t* buckets, uint32_t* coun
   while ((1 << nbits) < p.nb) ++nbits;
   if (p.L <= kSegMaxL && p.nb <= kSegMaxBins) {
     const int steps = (p.L + kSegThreads - 1) / kSegThreads;  // per wave
-    const size_t shmem = ((size_t)kSegWaves * p.nb + kSegWaves) * 4;
-    auto go = [&](auto kk) {
-      constexpr int K = decltype(kk)::value;
-      static bool configured[kMaxDevices] = {};
-      if (first_on_device(configured))
-        (void)hipFuncSetAttribute((const void*)k_sort_segment<K>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (kSegWaves * kSegMaxBins + kSegWaves) * 4);
-      hipLaunchKernelGGL(k_sort_segment<K>, dim3((unsigned)p.nseg()), dim3(kSegThreads), shmem,
-                         s, buckets, perm, p.L, p.nb, nbits, steps);
-    };
-    go(std::integral_constant<int, kSegMaxL / kSegThreads>{});
+    const size_t shmem = ((size_t)kSegWaves * p.nb + kSegWaves + p.L) * 4;
+    static bool configured[kMaxDevices] = {};
+    if (first_on_device(configured))
+      (void)hipFuncSetAttribute((const void*)k_sort_segment,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (kSegWaves * kSegMaxBins + kSegWaves + kSegMaxL) * 4);
+    hipLaunchKernelGGL(k_sort_segment, dim3((unsigned)p.nseg()), dim3(kSegThreads), shmem, s,
+                       buckets, perm, p.L, p.nb, nbits, steps);
     return hipGetLastError();
   }
   // counts: [seg][tiles][nb] tile counts (then their running sums), then the
