@@ -143,7 +143,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_var_dq(
     const float* __restrict__ knorm, const float* __restrict__ lse, const float* __restrict__ wr,
     const float* __restrict__ cq, const uint16_t* __restrict__ bkt,
     const int32_t* __restrict__ inv, float* __restrict__ dq, int L, int R, int flags) {
-  using Lay = BLay<D>;
   using M = QLds<D, DD>;
   constexpr int KS = D / 32, DT = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -158,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_var_dq(
   const bool la = (flags & LSH_ATTN_FLAG_LOOK_AHEAD) != 0;
   const bool sb = (flags & LSH_ATTN_FLAG_SAME_BUCKET) != 0;
   const bool nq = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
-  const int32_t* inv_bh = inv + bh * R * L;
+  const int32_t* inv_bh = DD ? inv + bh * R * L : nullptr;  // inv is read only with DEDUP
   const uint16_t* bk_bh = bkt + bh * R * L;
   float* kinv = (float*)(lds + M::kKinv);
   int* kpos = (int*)(lds + M::kPos);
@@ -296,7 +295,6 @@ __attribute__((amdgpu_waves_per_eu(DD && SB && D == 128 ? 1 : 2,
     const float* __restrict__ cq, const uint16_t* __restrict__ bkt,
     const int32_t* __restrict__ inv, float* __restrict__ dk, float* __restrict__ dv, int L,
     int R, int flags) {
-  using Lay = BLay<D>;
   using M = KLds<D, DD>;
   constexpr int KS = D / 32, DT = D / 16;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -311,7 +309,7 @@ __attribute__((amdgpu_waves_per_eu(DD && SB && D == 128 ? 1 : 2,
   const bool la = (flags & LSH_ATTN_FLAG_LOOK_AHEAD) != 0;
   constexpr bool sb = SB;
   const bool nq = (flags & LSH_ATTN_FLAG_NORM_QUERIES) != 0;
-  const int32_t* inv_bh = inv + bh * R * L;
+  const int32_t* inv_bh = DD ? inv + bh * R * L : nullptr;  // inv is read only with DEDUP
   const uint16_t* bk_bh = bkt + bh * R * L;
   int* qpos = (int*)(lds + M::kPos);
   float* ql2 = (float*)(lds + M::kL2);

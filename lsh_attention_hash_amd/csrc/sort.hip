@@ -293,13 +293,14 @@ __global__ __launch_bounds__(kSegThreads) void k_sort_segment(const uint16_t* __
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int k = 0; k < kSegMaxSteps; ++k) {
-    if (k >= steps) break;  // the same for every wave
-    const bool in = ids[k] != kNone;
-    const uint64_t peers = match_peers(ids[k], in, nbits);
-    if (in) slots[mine[ids[k]] + (uint32_t)__popcll(peers & below)] = begin + kWave * k + lane;
-    // all lanes have read the wave's slot above; the group's first lane
-    // advances it
-    if (in && lane == __builtin_ctzll(peers)) mine[ids[k]] += (uint32_t)__popcll(peers);
+    if (k < steps) {  // the same for every wave
+      const bool in = ids[k] != kNone;
+      const uint64_t peers = match_peers(ids[k], in, nbits);
+      if (in) slots[mine[ids[k]] + (uint32_t)__popcll(peers & below)] = begin + kWave * k + lane;
+      // all lanes have read the wave's slot above; the group's first lane
+      // advances it
+      if (in && lane == __builtin_ctzll(peers)) mine[ids[k]] += (uint32_t)__popcll(peers);
+    }
   }
   __syncthreads();  // every slot holds its position
   int32_t* pm = perm + seg * L;
